@@ -1,0 +1,333 @@
+"""CPU oracle for the Q4 expert gate/up + SwiGLU path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports, loads or calls
+this module; only the tests, the smoke check and the benchmark's CPU-baseline
+leg do.  It shares no code with the HIP kernels.
+
+What it computes, and where the pages define it (pages of the diff of
+@mlx-bun/inference 1.0.0 on my.diffend.io; "page 52" is
+.../0.0.0-stage/1.0.0/page/52):
+
+* Slot layout and validation -- page 51, kernels/glm52/layout.ts
+  (``Glm52CanonicalMetalLayout``, ``validateRange``) and page 52,
+  kernels/glm52/streamed-experts.ts (``validateCall``): byte offsets from the
+  slot base, each field must lie inside the slot.
+* Weight decode -- page 52, streamed-experts.ts, ``GATE_UP_SOURCE``: row ``i``
+  of a projection is ``H/8`` uint32 words; nibble ``p`` of word ``w`` (bits
+  ``4p..4p+3``) is input position ``k = 8w + p``; its weight is ``q - 8``
+  (zero point 8, the "affine zero-point 8" Q4 family of the same file).
+* Gate/up -- same kernel: ``gate = (sum_k (q_k - 8) x_k) * scale_row`` in F32.
+  The kernel's F32 FMA order is one of many valid orders; the oracle takes the
+  plain definition: the exact sum, times the F32 scale, rounded once to F32
+  (round to nearest, ties to even).
+* SwiGLU tail -- same kernel, lane-0 tail: gate and up rounded to bf16, then
+  ``s = bf16(1 / (1 + exp(-g)))`` evaluated in F32, ``silu = bf16(g * s)``,
+  ``out = bf16(silu * u)``.  F32 -> bf16 rounding is round to nearest even,
+  the rule of the ``trellis_bf16`` helper on page 54, kernels/trellis/codebook.ts.
+* Grouped call -- row independence stated on page 52 (one launch geometry for
+  every batch width; each sample and row is computed on its own): output
+  ``[t, j, :]`` is the single-expert result for token ``t`` on slot
+  ``ids[t, j]``.  Ids outside ``[0, num_slots)`` give zero outputs and are
+  counted (a reading: the pages have no grouped Q4 call).
+
+Readings where the pages are silent (listed with reasons in the design notes):
+``exp`` is evaluated in double and rounded once to F32 (the pages ask for a
+precise F32 exp); non-finite activations are outside the contract.
+
+Every function here is a plain, slow transcription of those definitions.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+OFFSET_ABSENT = (1 << 64) - 1
+
+
+# ---------------------------------------------------------------------------
+# bf16 / f32 helpers
+# ---------------------------------------------------------------------------
+
+def bf16_to_f32(bits) -> np.ndarray:
+    """bf16 bit patterns -> float32 values (exact: bf16 is the top half of f32)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32)
+
+
+def f32_to_bf16(v) -> np.ndarray:
+    """Round float32 values to bf16, nearest, ties to even; returns bit patterns.
+
+    Definition-level implementation: for each finite value take the two bf16
+    neighbours that bracket it (truncation toward zero and the next bf16 away
+    from zero), compare the exact distances in float64, and on a tie keep the
+    one with an even last significand bit.  Values beyond the largest bf16 by
+    half an ulp or more round to infinity (IEEE).  NaN maps to the quiet NaN
+    0x7FC0 with the input's sign.
+    """
+    u = np.ascontiguousarray(np.asarray(v, dtype=np.float32)).view(np.uint32).reshape(-1)
+    sign = (u >> np.uint32(16)) & np.uint32(0x8000)
+    mag = u & np.uint32(0x7FFFFFFF)
+    is_nan = mag > np.uint32(0x7F800000)
+    is_inf = mag == np.uint32(0x7F800000)
+    lo_bits = (mag >> np.uint32(16)).astype(np.uint32)          # toward zero
+    hi_bits = lo_bits + np.uint32(1)                             # away from zero
+    a = mag.view(np.float32).astype(np.float64)
+    lo_val = (lo_bits << np.uint32(16)).view(np.float32).astype(np.float64)
+    # one bf16 ulp at lo, in an unbounded exponent range (so the neighbour
+    # above the largest finite bf16 is 2**128, whose pattern is infinity)
+    efield = ((lo_bits >> np.uint32(7)) & np.uint32(0xFF)).astype(np.int64)
+    ulp = np.exp2(np.maximum(efield, 1) - 127 - 7).astype(np.float64)
+    hi_val = lo_val + ulp
+    d_lo = a - lo_val
+    d_hi = hi_val - a
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & ((lo_bits & np.uint32(1)) == np.uint32(1)))
+    take_hi &= d_lo != 0.0
+    res = np.where(take_hi, hi_bits, lo_bits)
+    res = np.where(is_inf, np.uint32(0x7F80), res)
+    res = np.where(is_nan, np.uint32(0x7FC0), res)
+    res = (res | sign).astype(np.uint16)
+    return res.reshape(np.shape(v))
+
+
+def f32_round_dyadic(n: int, e: int, zero_sign: float = 1.0) -> float:
+    """Round the exact value ``n * 2**e`` (integers) to float32, ties to even.
+
+    Returns a Python float holding the float32 value.  Handles subnormals and
+    overflow to infinity.  ``zero_sign`` gives the sign of an exact zero.
+    """
+    if n == 0:
+        return math.copysign(0.0, zero_sign)
+    neg = n < 0
+    a = -n if neg else n
+    top = a.bit_length() - 1 + e                # floor(log2 |value|)
+    q_exp = max(top - 23, -149)                 # exponent of one f32 ulp here
+    shift = q_exp - e
+    if shift <= 0:
+        m = a << (-shift)
+    else:
+        m = a >> shift
+        r = a - (m << shift)
+        half = 1 << (shift - 1)
+        if r > half or (r == half and (m & 1)):
+            m += 1
+    if m.bit_length() + q_exp > 128:
+        val = math.inf
+    else:
+        val = math.ldexp(m, q_exp)
+    return -val if neg else val
+
+
+def f32_parts(v: float) -> Tuple[int, int]:
+    """Exact integer decomposition of a finite float: ``v == n * 2**e``."""
+    if v == 0.0:
+        return 0, 0
+    m, ex = math.frexp(v)                        # v = m * 2**ex, 0.5 <= |m| < 1
+    n = int(m * (1 << 53))
+    return n, ex - 53
+
+
+# ---------------------------------------------------------------------------
+# Slot decode
+# ---------------------------------------------------------------------------
+
+def _check_range(offset: int, length: int, slot_bytes: int, label: str) -> None:
+    if offset < 0:
+        raise ValueError(f"{label} offset must be a non-negative safe integer")
+    if length < 0:
+        raise ValueError(f"{label} length must be a non-negative safe integer")
+    if offset + length > slot_bytes:
+        raise ValueError(f"{label} exceeds the canonical expert slot")
+
+
+def check_layout(layout, H: int, I: int) -> None:
+    """Range rules of validateRange / validateCall for the gate/up fields."""
+    if H <= 0 or I <= 0 or layout.slot_bytes <= 0:
+        raise ValueError("hidden size, intermediate size and slot bytes must be positive")
+    if H % 8:
+        raise ValueError("Q4 expert dimensions must be divisible by 8")
+    wb = I * H // 2
+    _check_range(layout.gate_weight_offset, wb, layout.slot_bytes, "gate weights")
+    _check_range(layout.up_weight_offset, wb, layout.slot_bytes, "up weights")
+    _check_range(layout.gate_scale_offset, 4 * I, layout.slot_bytes, "gate scales")
+    _check_range(layout.up_scale_offset, 4 * I, layout.slot_bytes, "up scales")
+    if layout.down_weight_offset != OFFSET_ABSENT:
+        _check_range(layout.down_weight_offset, wb, layout.slot_bytes, "down weights")
+    if layout.down_scale_offset != OFFSET_ABSENT:
+        _check_range(layout.down_scale_offset, 4 * H, layout.slot_bytes, "down scales")
+
+
+def q4_weights(slot: np.ndarray, offset: int, I: int, H: int) -> np.ndarray:
+    """Decode a ``[I, H]`` matrix of weights ``q - 8`` (int8) from the slot.
+
+    Word ``w`` of row ``i`` is the little-endian uint32 at
+    ``offset + 4 * (i * H/8 + w)``; its nibble ``p`` is position ``8w + p``.
+    """
+    words = np.frombuffer(slot, dtype="<u4", count=I * H // 8, offset=offset).reshape(I, H // 8)
+    w = np.empty((I, H), dtype=np.int8)
+    for p in range(8):
+        q = (words >> np.uint32(4 * p)) & np.uint32(0xF)
+        w[:, p::8] = q.astype(np.int8) - np.int8(8)
+    return w
+
+
+def row_scales(slot: np.ndarray, offset: int, I: int) -> np.ndarray:
+    return np.frombuffer(slot, dtype="<f4", count=I, offset=offset).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Exact dot products
+# ---------------------------------------------------------------------------
+
+def bf16_integer_parts(xbits: np.ndarray):
+    """Write each finite bf16 as ``sign * mag * 2**exp``, integer ``mag`` < 256."""
+    b = np.asarray(xbits, dtype=np.uint16).astype(np.int64)
+    ef = (b >> 7) & 0xFF
+    if np.any(ef == 0xFF):
+        raise ValueError("non-finite activations are outside the oracle's contract")
+    frac = b & 0x7F
+    mag = np.where(ef == 0, frac, frac | 0x80)
+    exp = np.where(ef == 0, 1, ef) - 127 - 7
+    sign = np.where(b & 0x8000, -1, 1)
+    return sign, mag, exp
+
+
+_LIMB_BITS = 24
+
+
+def exact_dots(w: np.ndarray, xbits: np.ndarray) -> Tuple[List[List[int]], List[int]]:
+    """Exact ``S[i][m] = sum_k w[i, k] * x[m, k]`` as ``num[i][m] * 2**e[m]``.
+
+    Each token's x is scaled by a power of two to integers ``X`` (exact: the
+    scale is that token's smallest exponent).  ``|X|`` may be wider than 64
+    bits, so it is cut into signed 24-bit limbs.  Each limb product is a
+    float64 matrix product in which every product ``w * limb`` (|w| <= 8) and
+    every partial sum of at most H <= 2**16 of them is an integer of magnitude
+    below 2**43, hence exactly representable: the product is exact whatever
+    order the library sums in.  Limbs are recombined in Python integers.
+    """
+    I, H = w.shape
+    if H > (1 << 16):
+        raise ValueError("oracle supports H <= 65536")
+    sign, mag, exp = bf16_integer_parts(xbits)
+    M = xbits.shape[0]
+    nz = mag != 0
+    exps = [int(exp[m][nz[m]].min()) if np.any(nz[m]) else 0 for m in range(M)]
+    shifts = np.where(nz, exp - np.array(exps, dtype=np.int64)[:, None], 0)
+    nlimbs = max(1, (int(shifts.max()) + 8 + _LIMB_BITS - 1) // _LIMB_BITS)
+    mask = (1 << _LIMB_BITS) - 1
+    wf = np.asarray(w, dtype=np.float64)
+    acc = None
+    for l in range(nlimbs):
+        # bits [24 l, 24 l + 24) of |X| = mag * 2**shift, with X's sign
+        d = shifts - l * _LIMB_BITS
+        left = (mag << np.clip(d, 0, _LIMB_BITS - 1)) & mask
+        right = np.where(d > -64, mag >> np.clip(-d, 0, 63), 0)
+        limb = np.where(d >= _LIMB_BITS, 0, np.where(d >= 0, left, right)) * sign
+        r = wf @ np.ascontiguousarray(limb.T, dtype=np.float64)     # [I, M], exact
+        part = r.astype(np.int64).astype(object) * (1 << (l * _LIMB_BITS))
+        acc = part if acc is None else acc + part
+    return acc.tolist(), exps
+
+
+def scaled_f32(nums: List[List[int]], exps: List[int], scales: np.ndarray) -> np.ndarray:
+    """``RN_f32(S[i][m] * scale[i])`` for every row and token -> ``[M, I]``."""
+    I = len(nums)
+    M = len(exps)
+    out = np.empty((M, I), dtype=np.float32)
+    for i in range(I):
+        s = float(scales[i])
+        sn, se = f32_parts(s)
+        for m in range(M):
+            out[m, i] = f32_round_dyadic(nums[i][m] * sn, exps[m] + se, zero_sign=s)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# SwiGLU tail
+# ---------------------------------------------------------------------------
+
+def _exp_f32(v: float) -> np.float32:
+    """exp(v) evaluated in double, rounded once to float32 (inf on overflow)."""
+    try:
+        e = math.exp(v)
+    except OverflowError:
+        return np.float32(np.inf)
+    with np.errstate(over="ignore"):
+        return np.float32(e)
+
+
+def swiglu_tail(gate: np.ndarray, up: np.ndarray) -> np.ndarray:
+    """bf16 output bits of the lane-0 tail for F32 gate and up values."""
+    gate = np.asarray(gate, dtype=np.float32)
+    up = np.asarray(up, dtype=np.float32)
+    gT = bf16_to_f32(f32_to_bf16(gate))
+    uT = bf16_to_f32(f32_to_bf16(up))
+    flat = gT.reshape(-1)
+    e = np.array([_exp_f32(-float(g)) for g in flat], dtype=np.float32).reshape(gT.shape)
+    one = np.float32(1.0)
+    with np.errstate(over="ignore", under="ignore", divide="ignore"):
+        d = one + e                       # F32 add
+        sig = one / d                     # F32 divide
+    sT = bf16_to_f32(f32_to_bf16(sig))
+    siluT = bf16_to_f32(f32_to_bf16(gT * sT))   # F32 product, exact for bf16*bf16
+    return f32_to_bf16(siluT * uT)
+
+
+# ---------------------------------------------------------------------------
+# The two calls
+# ---------------------------------------------------------------------------
+
+def expert_gate_up(slot: np.ndarray, layout, xbits: np.ndarray, H: int, I: int):
+    """Single expert: returns ``(gate f32 [M,I], up f32 [M,I], out bf16 bits [M,I])``."""
+    slot = np.ascontiguousarray(slot, dtype=np.uint8).reshape(-1)
+    xbits = np.ascontiguousarray(xbits, dtype=np.uint16).reshape(-1, H)
+    check_layout(layout, H, I)
+    if slot.size < layout.slot_bytes:
+        raise ValueError("canonical expert slot array is shorter than its layout")
+    if xbits.shape[0] < 1:
+        raise ValueError("Q4 expert gate/up requires input [M,H] with M >= 1")
+    wg = q4_weights(slot, layout.gate_weight_offset, I, H)
+    wu = q4_weights(slot, layout.up_weight_offset, I, H)
+    sg = row_scales(slot, layout.gate_scale_offset, I)
+    su = row_scales(slot, layout.up_scale_offset, I)
+    gate = scaled_f32(*exact_dots(wg, xbits), sg)
+    up = scaled_f32(*exact_dots(wu, xbits), su)
+    return gate, up, swiglu_tail(gate, up)
+
+
+def expert_gate_up_grouped(slots: np.ndarray, slot_stride: int, num_slots: int, layout,
+                           xbits: np.ndarray, ids: np.ndarray, H: int, I: int):
+    """Grouped call over routed slots.
+
+    Returns ``(gate [M,K,I], up [M,K,I], out bits [M,K,I], invalid_count)``.
+    Pair ``(t, j)`` uses slot ``ids[t, j]`` and token ``t``; invalid ids give
+    zero gate, up and output.
+    """
+    flat = np.ascontiguousarray(slots, dtype=np.uint8).reshape(-1)
+    xbits = np.ascontiguousarray(xbits, dtype=np.uint16).reshape(-1, H)
+    ids = np.asarray(ids, dtype=np.int64)
+    M, K = ids.shape
+    gate = np.zeros((M, K, I), dtype=np.float32)
+    up = np.zeros((M, K, I), dtype=np.float32)
+    out = np.zeros((M, K, I), dtype=np.uint16)
+    invalid = 0
+    by_slot: Dict[int, List[Tuple[int, int]]] = {}
+    for t in range(M):
+        for j in range(K):
+            e = int(ids[t, j])
+            if 0 <= e < num_slots:
+                by_slot.setdefault(e, []).append((t, j))
+            else:
+                invalid += 1
+    for e, pairs in sorted(by_slot.items()):
+        slot = flat[e * slot_stride:e * slot_stride + layout.slot_bytes]
+        toks = [t for t, _ in pairs]
+        g, u, o = expert_gate_up(slot, layout, xbits[toks], H, I)
+        for r, (t, j) in enumerate(pairs):
+            gate[t, j] = g[r]
+            up[t, j] = u[r]
+            out[t, j] = o[r]
+    return gate, up, out, invalid

@@ -1,0 +1,242 @@
+"""Seeded generators for expert slots, activations and routing ids.
+
+Every generator takes a ``numpy.random.Generator`` and draws in a fixed,
+documented order, so a seed fixes every byte.  Workload shapes follow the
+five benchmark configurations of the Q4 expert gate/up path:
+
+1. one expert, H=256, I=128, M=1, scales U[0.005, 0.02];
+2. one expert, H=4096, I=1536, M=1, one 4 KiB-aligned contiguous slot;
+3. as 2 with M=8;
+4. 64 expert slots (H=6144, I=2048) in one buffer, M=32 tokens, top-8 ids
+   drawn without replacement per token;
+5. one expert, H=7168, I=4096, M in {1, 4, 16, 32}; 1% of gate rows and 1% of
+   up rows forced to the all-8 nibble pattern (zero weights), 1% of x entries
+   set to +-9984 (the bf16 value nearest 1e4), scales U[0.001, 0.05].
+
+Slot byte layout (an expert slot as described on diff page 52/51 of
+@mlx-bun/inference 1.0.0, kernels/glm52/layout.ts: byte offsets of each field
+from the slot base): ``[gate words | up words | gate scales | up scales]``
+back to back, padded to a multiple of 4096 bytes.  Gate and up words are
+little-endian uint32 ``[I][H/8]``; scales are little-endian float32 ``[I]``.
+
+x values are standard normal float32 samples truncated toward zero to bf16
+(the upper 16 bits), which keeps the generator free of the rounding rule under
+test while giving the same N(0,1) distribution at bf16 resolution.
+"""
+
+from __future__ import annotations
+
+import hashlib
+from dataclasses import dataclass, field, replace
+from typing import Dict, List, Optional
+
+import numpy as np
+
+OFFSET_ABSENT = (1 << 64) - 1
+
+# bf16 bit patterns of +9984 and -9984 (9984 = 156 * 64 is the bf16 value
+# nearest to 1e4).
+BF16_POS_9984 = 0x461C
+BF16_NEG_9984 = 0xC61C
+ALL_EIGHT_WORD = 0x88888888
+
+
+@dataclass(frozen=True)
+class SlotLayout:
+    """Byte offsets of each field from the slot base (down fields optional)."""
+
+    slot_bytes: int
+    gate_weight_offset: int
+    up_weight_offset: int
+    gate_scale_offset: int
+    up_scale_offset: int
+    down_weight_offset: int = OFFSET_ABSENT
+    down_scale_offset: int = OFFSET_ABSENT
+
+
+def contiguous_layout(H: int, I: int, align: int = 4096) -> SlotLayout:
+    """Gate words, up words, gate scales, up scales back to back."""
+    wbytes = I * H // 2
+    gate_w = 0
+    up_w = wbytes
+    gate_s = 2 * wbytes
+    up_s = gate_s + 4 * I
+    end = up_s + 4 * I
+    slot = (end + align - 1) // align * align
+    return SlotLayout(slot, gate_w, up_w, gate_s, up_s)
+
+
+def pack_nibbles(nibbles: np.ndarray) -> np.ndarray:
+    """Pack a ``[R, H]`` array of values 0..15 into ``[R, H/8]`` uint32 words.
+
+    Nibble ``k`` of a row sits in word ``k // 8`` at bits ``4*(k % 8)``.
+    Used by tests that want to choose weights nibble by nibble.
+    """
+    nib = np.asarray(nibbles, dtype=np.uint32)
+    R, H = nib.shape
+    assert H % 8 == 0
+    words = np.zeros((R, H // 8), dtype=np.uint32)
+    for p in range(8):
+        words |= (nib[:, p::8] & 0xF) << np.uint32(4 * p)
+    return words
+
+
+def write_slot(layout: SlotLayout, H: int, I: int, gate_words, up_words, gate_scales, up_scales,
+               out: Optional[np.ndarray] = None) -> np.ndarray:
+    """Lay given gate/up words ``[I, H/8]`` and scales ``[I]`` into a slot."""
+    if out is None:
+        out = np.zeros(layout.slot_bytes, dtype=np.uint8)
+    wb = I * H // 2
+    gw = np.asarray(gate_words, dtype="<u4").reshape(I, H // 8)
+    uw = np.asarray(up_words, dtype="<u4").reshape(I, H // 8)
+    out[layout.gate_weight_offset:layout.gate_weight_offset + wb] = gw.view(np.uint8).ravel()
+    out[layout.up_weight_offset:layout.up_weight_offset + wb] = uw.view(np.uint8).ravel()
+    out[layout.gate_scale_offset:layout.gate_scale_offset + 4 * I] = \
+        np.asarray(gate_scales, dtype="<f4").view(np.uint8)
+    out[layout.up_scale_offset:layout.up_scale_offset + 4 * I] = \
+        np.asarray(up_scales, dtype="<f4").view(np.uint8)
+    return out
+
+
+def _uniform_words(rng: np.random.Generator, I: int, H: int) -> np.ndarray:
+    return rng.integers(0, 1 << 32, size=(I, H // 8), dtype=np.uint64).astype(np.uint32)
+
+
+def fill_slot(
+    rng: np.random.Generator,
+    H: int,
+    I: int,
+    layout: SlotLayout,
+    scale_range=(0.005, 0.02),
+    zero_row_fraction: float = 0.0,
+    out: Optional[np.ndarray] = None,
+) -> np.ndarray:
+    """Draw one expert slot into a uint8 array of ``layout.slot_bytes``.
+
+    Draw order: gate words, up words, gate scales, up scales, then (if
+    ``zero_row_fraction``) the gate rows and the up rows forced to all-8.
+    Padding bytes are zero.
+    """
+    if out is None:
+        out = np.zeros(layout.slot_bytes, dtype=np.uint8)
+    else:
+        out[:] = 0
+    gw = _uniform_words(rng, I, H)
+    uw = _uniform_words(rng, I, H)
+    lo, hi = scale_range
+    gs = rng.uniform(lo, hi, size=I).astype(np.float32)
+    us = rng.uniform(lo, hi, size=I).astype(np.float32)
+    if zero_row_fraction:
+        n = int(round(zero_row_fraction * I))
+        gw[rng.choice(I, n, replace=False)] = ALL_EIGHT_WORD
+        uw[rng.choice(I, n, replace=False)] = ALL_EIGHT_WORD
+    wb = I * H // 2
+    out[layout.gate_weight_offset:layout.gate_weight_offset + wb] = gw.astype("<u4").view(np.uint8).ravel()
+    out[layout.up_weight_offset:layout.up_weight_offset + wb] = uw.astype("<u4").view(np.uint8).ravel()
+    out[layout.gate_scale_offset:layout.gate_scale_offset + 4 * I] = gs.astype("<f4").view(np.uint8)
+    out[layout.up_scale_offset:layout.up_scale_offset + 4 * I] = us.astype("<f4").view(np.uint8)
+    return out
+
+
+def bf16_normal(rng: np.random.Generator, shape) -> np.ndarray:
+    """N(0,1) float32 samples truncated to bf16; returns uint16 bit patterns."""
+    f = rng.standard_normal(size=shape, dtype=np.float32)
+    return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def add_outliers(rng: np.random.Generator, xbits: np.ndarray, fraction: float) -> np.ndarray:
+    """Set ``round(fraction * x.size)`` distinct entries to +-9984 (equal odds)."""
+    x = xbits.copy()
+    flat = x.reshape(-1)
+    n = int(round(fraction * flat.size))
+    pos = rng.choice(flat.size, n, replace=False)
+    signs = rng.integers(0, 2, size=n)
+    flat[pos] = np.where(signs == 1, BF16_NEG_9984, BF16_POS_9984).astype(np.uint16)
+    return x
+
+
+def top_k_routing(rng: np.random.Generator, M: int, K: int, num_slots: int) -> np.ndarray:
+    """Per token, K distinct slot ids drawn uniformly without replacement."""
+    ids = np.empty((M, K), dtype=np.int32)
+    for t in range(M):
+        ids[t] = rng.choice(num_slots, K, replace=False)
+    return ids
+
+
+def sha256_hex(a: np.ndarray) -> str:
+    return hashlib.sha256(np.ascontiguousarray(a).view(np.uint8)).hexdigest()
+
+
+@dataclass
+class Config:
+    """One workload: slots (uint8 [num_slots, slot_stride]), x bits, ids."""
+
+    name: str
+    seed: int
+    H: int
+    I: int
+    M: int
+    layout: SlotLayout
+    slots: np.ndarray            # uint8 [num_slots, slot_stride]
+    x: np.ndarray                # uint16 [M, H] bf16 bits
+    ids: Optional[np.ndarray] = None   # int32 [M, K] for the grouped call
+    K: int = 0
+    notes: Dict[str, str] = field(default_factory=dict)
+
+    @property
+    def num_slots(self) -> int:
+        return self.slots.shape[0]
+
+    @property
+    def slot_stride(self) -> int:
+        return self.slots.shape[1]
+
+
+CONFIGS: Dict[str, dict] = {
+    "cfg1": dict(seed=101, H=256, I=128, M=1, scale=(0.005, 0.02)),
+    "cfg2": dict(seed=102, H=4096, I=1536, M=1, scale=(0.005, 0.02)),
+    "cfg3": dict(seed=103, H=4096, I=1536, M=8, scale=(0.005, 0.02)),
+    "cfg4": dict(seed=104, H=6144, I=2048, M=32, K=8, num_slots=64, scale=(0.005, 0.02)),
+    "cfg5": dict(seed=105, H=7168, I=4096, M=None, scale=(0.001, 0.05), zero_rows=0.01, outliers=0.01),
+}
+
+
+def make_config(name: str, M: Optional[int] = None, num_slots: Optional[int] = None,
+                H: Optional[int] = None, I: Optional[int] = None, seed: Optional[int] = None) -> Config:
+    """Build one of the five workloads (or a resized variant of it).
+
+    ``cfg5`` needs ``M`` in {1, 4, 16, 32}; its x is drawn from seed 105+M.
+    ``num_slots``/``H``/``I``/``seed`` override the defaults for scaled-down
+    or scaled-up variants with the same distributions.
+    """
+    spec = dict(CONFIGS[name])
+    H = H or spec["H"]
+    I = I or spec["I"]
+    seed = spec["seed"] if seed is None else seed
+    layout = contiguous_layout(H, I)
+    rng = np.random.default_rng(seed)
+    if name == "cfg4":
+        E = num_slots or spec["num_slots"]
+        M = M or spec["M"]
+        K = spec["K"] if E >= spec["K"] else E
+        slots = np.zeros((E, layout.slot_bytes), dtype=np.uint8)
+        for e in range(E):
+            fill_slot(rng, H, I, layout, spec["scale"], out=slots[e])
+        x = bf16_normal(rng, (M, H))
+        ids = top_k_routing(rng, M, K, E)
+        return Config(name, seed, H, I, M, layout, slots, x, ids, K)
+    if name == "cfg5":
+        if M is None:
+            raise ValueError("cfg5 needs M")
+        slots = fill_slot(rng, H, I, layout, spec["scale"], spec["zero_rows"])[None, :]
+        xrng = np.random.default_rng(seed + M)
+        x = bf16_normal(xrng, (M, H))
+        x = add_outliers(xrng, x, spec["outliers"])
+        return Config(name, seed, H, I, M, layout, slots, x)
+    M = M or spec["M"]
+    E = num_slots or 1
+    slots = np.zeros((E, layout.slot_bytes), dtype=np.uint8)
+    for e in range(E):
+        fill_slot(rng, H, I, layout, spec["scale"], out=slots[e])
+    x = bf16_normal(rng, (M, H))
+    return Config(name, seed, H, I, M, layout, slots, x)
