@@ -1,0 +1,168 @@
+/*
+ * q4moe.h -- C ABI of the MI355X (gfx950) Q4 expert gate/up + SwiGLU library.
+ *
+ * What is computed (diff of @mlx-bun/inference 1.0.0, page 52,
+ * kernels/glm52/streamed-experts.ts, GATE_UP_SOURCE and its launch in
+ * Glm52CanonicalMetalExecutor.execute):
+ *
+ *   for every token m and intermediate row i of one expert slot
+ *     gate[m,i] = (sum_k (qg[i,k] - 8) * x[m,k]) * gate_scale[i]      (F32)
+ *     up[m,i]   = (sum_k (qu[i,k] - 8) * x[m,k]) * up_scale[i]        (F32)
+ *     gT = bf16(gate), uT = bf16(up)
+ *     sT = bf16(1 / (1 + exp(-gT)))          (evaluated in F32)
+ *     out[m,i] = bf16(bf16(gT * sT) * uT)
+ *
+ *   q[i,k] is nibble (k % 8) -- bits 4*(k%8) .. 4*(k%8)+3 -- of the
+ *   little-endian uint32 word (i*H/8 + k/8) of the projection's packed rows.
+ *   Every bf16 rounding is round-to-nearest-even.
+ *
+ * Accumulation.  The library computes each sum exactly (integer matrix-core
+ * arithmetic on a fixed-point split of each bf16 x into six signed 8-bit
+ * digits) and rounds (sum * scale) once to F32.  The pages accumulate in F32 FMA order,
+ * which is one rounding-order approximation of the same value.  Activations
+ * whose magnitudes span more than 2^38 within one token have their smallest
+ * entries rounded to the token's 2^-38-relative grid (error below
+ * 2^-37 * max|x| per entry).  Results are identical for every batch width,
+ * kernel shape and routing (batch-invariant).
+ *
+ * Slot layout (page 51, kernels/glm52/layout.ts, Glm52CanonicalMetalLayout
+ * and validateRange): every field is a byte offset from the slot base.
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are borrowed.  The caller owns the slots, x, out, ids,
+ *     probes and workspace and keeps them alive until the stream has completed
+ *     the call (the lease rule of glm52CanonicalQ4SlotView, page 52).
+ *   - Calls are asynchronous on `stream`; the library never synchronises and
+ *     allocates no device memory.
+ *   - Arguments are validated on the host before anything is enqueued; on an
+ *     invalid argument nothing is enqueued and a negative status is returned.
+ *     q4_last_error() then describes the failure.
+ *   - Non-finite activations are outside the contract: a token whose x holds
+ *     an Inf or NaN gets NaN gate/up and a NaN output row.
+ */
+#ifndef Q4MOE_H
+#define Q4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* HIP stream handle (hipStream_t); NULL is the default stream. */
+typedef struct ihipStream_t *q4_stream_t;
+
+#define Q4_OFFSET_ABSENT UINT64_MAX
+
+/* Status codes. */
+enum {
+  Q4_OK = 0,
+  Q4_ERR_INVALID_ARGUMENT = -1, /* null pointer, non-positive size, H % 8 != 0 */
+  Q4_ERR_ALIGNMENT = -2,        /* slot/stride not 4096-aligned, offsets/x/out misaligned */
+  Q4_ERR_RANGE = -3,            /* a slot field does not fit inside slot_bytes */
+  Q4_ERR_UNSUPPORTED = -4,      /* sizes beyond the library's limits (below) */
+  Q4_ERR_HIP = -5,              /* the kernel launch failed */
+  Q4_ERR_WORKSPACE = -6         /* workspace missing or smaller than required */
+};
+
+/* Limits: 8 <= H <= 65536 with H % 8 == 0; 1 <= I; I*H/2 <= 2^31 - 16;
+ * 1 <= M <= 65535; grouped: 1 <= K, M*K <= 65536, 1 <= num_slots <= 65535. */
+
+/*
+ * Byte offsets of an expert slot's fields from the slot base (page 51,
+ * Glm52CanonicalMetalLayout).  gate/up weights: uint32 [I][H/8] little-endian,
+ * 16-byte aligned offsets.  gate/up scales: float32 [I], 4-byte aligned.
+ * The down fields belong to the down projection, which this library does not
+ * compute; they may be Q4_OFFSET_ABSENT, otherwise they are range-checked
+ * (down weights I*H/2 bytes, down scales 4*H bytes) as on page 52
+ * (validateCall).
+ */
+typedef struct {
+  uint64_t slot_bytes;
+  uint64_t gate_weight_offset;
+  uint64_t up_weight_offset;
+  uint64_t gate_scale_offset;
+  uint64_t up_scale_offset;
+  uint64_t down_weight_offset;
+  uint64_t down_scale_offset;
+} q4_slot_layout;
+
+/*
+ * Single expert: out[M][I] (bf16) for x[M][H] (bf16) against one slot.
+ *   slot      device pointer to the slot base, 4096-byte aligned
+ *             (our reading of the page-aligned slot rule of
+ *             glm52CanonicalQ4SlotView; the pages use 16 KiB pages).
+ *   layout    host pointer to the field offsets.
+ *   x_bf16    device, row-major [M][H], 16-byte aligned.
+ *   out_bf16  device, row-major [M][I], 2-byte aligned.
+ * Returns Q4_OK or a negative status.
+ */
+int q4_expert_gate_up(const void *slot, const q4_slot_layout *layout,
+                      const void *x_bf16, int64_t M, int64_t H, int64_t I,
+                      void *out_bf16, q4_stream_t stream);
+
+/* As q4_expert_gate_up, and also writes the F32 gate and up values before
+ * their bf16 rounding to gate_f32/up_f32 ([M][I] each, 4-byte aligned);
+ * either may be NULL.  Same kernels; used by parity tests. */
+int q4_expert_gate_up_probe(const void *slot, const q4_slot_layout *layout,
+                            const void *x_bf16, int64_t M, int64_t H, int64_t I,
+                            void *out_bf16, float *gate_f32, float *up_f32,
+                            q4_stream_t stream);
+
+/* Bytes of device workspace the grouped call needs (256-byte aligned). */
+size_t q4_grouped_workspace_bytes(int64_t M, int64_t K, int64_t num_slots);
+
+/*
+ * Grouped call over routed expert slots.  Pair (t, j) runs token t against
+ * slot slot_ids[t*K + j] and writes out[t][j][:] (bf16 [M][K][I]); each pair
+ * is independent of the others (row independence, page 52).  Slots are
+ * num_slots slots of one layout spaced slot_stride bytes apart from
+ * slots_base (both 4096-aligned, slot_stride >= slot_bytes).
+ *   slot_ids  device int32 [M][K]; duplicates are allowed.  An id outside
+ *             [0, num_slots) yields zero gate/up/out for that pair, and the
+ *             number of such ids is stored as int32 at workspace[0].
+ *   workspace device, >= q4_grouped_workspace_bytes(M, K, num_slots) bytes,
+ *             256-byte aligned; contents on entry are ignored.
+ */
+int q4_expert_gate_up_grouped(const void *slots_base, uint64_t slot_stride,
+                              int64_t num_slots, const q4_slot_layout *layout,
+                              const void *x_bf16, int64_t M,
+                              const int32_t *slot_ids, int64_t K,
+                              int64_t H, int64_t I, void *out_bf16,
+                              void *workspace, size_t workspace_bytes,
+                              q4_stream_t stream);
+
+/* As q4_expert_gate_up_grouped with optional F32 gate/up probes [M][K][I]. */
+int q4_expert_gate_up_grouped_probe(const void *slots_base, uint64_t slot_stride,
+                                    int64_t num_slots, const q4_slot_layout *layout,
+                                    const void *x_bf16, int64_t M,
+                                    const int32_t *slot_ids, int64_t K,
+                                    int64_t H, int64_t I, void *out_bf16,
+                                    float *gate_f32, float *up_f32,
+                                    void *workspace, size_t workspace_bytes,
+                                    q4_stream_t stream);
+
+/* Host-only argument checks of the two calls (no device access, nothing
+ * enqueued): the same validation the entry points run first.  Pointers are
+ * only tested for NULL and alignment. */
+int q4_validate_gate_up(const void *slot, const q4_slot_layout *layout,
+                        const void *x_bf16, int64_t M, int64_t H, int64_t I,
+                        const void *out_bf16);
+int q4_validate_grouped(const void *slots_base, uint64_t slot_stride,
+                        int64_t num_slots, const q4_slot_layout *layout,
+                        const void *x_bf16, int64_t M, const int32_t *slot_ids,
+                        int64_t K, int64_t H, int64_t I, const void *out_bf16,
+                        const void *workspace, size_t workspace_bytes);
+
+/* Message for the last failing call on this thread ("" after success). */
+const char *q4_last_error(void);
+
+/* ABI version: 1. */
+int q4_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4MOE_H */

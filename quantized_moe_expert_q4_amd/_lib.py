@@ -1,0 +1,187 @@
+"""ctypes binding of libq4moe.so: argument marshalling only.
+
+Every step of the computation runs in the HIP kernels behind the C ABI
+declared in include/q4moe.h.  This module turns tensors into device pointers,
+passes the current HIP stream, and raises on a non-zero status.  It never
+computes a result itself and has no fallback: without the built library every
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libq4moe.so")
+
+OFFSET_ABSENT = (1 << 64) - 1
+
+Q4_OK = 0
+Q4_ERR_INVALID_ARGUMENT = -1
+Q4_ERR_ALIGNMENT = -2
+Q4_ERR_RANGE = -3
+Q4_ERR_UNSUPPORTED = -4
+Q4_ERR_HIP = -5
+Q4_ERR_WORKSPACE = -6
+
+STATUS_NAMES = {
+    Q4_OK: "OK",
+    Q4_ERR_INVALID_ARGUMENT: "INVALID_ARGUMENT",
+    Q4_ERR_ALIGNMENT: "ALIGNMENT",
+    Q4_ERR_RANGE: "RANGE",
+    Q4_ERR_UNSUPPORTED: "UNSUPPORTED",
+    Q4_ERR_HIP: "HIP_ERROR",
+    Q4_ERR_WORKSPACE: "WORKSPACE",
+}
+
+
+class Q4Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+class SlotLayoutC(ctypes.Structure):
+    _fields_ = [
+        ("slot_bytes", ctypes.c_uint64),
+        ("gate_weight_offset", ctypes.c_uint64),
+        ("up_weight_offset", ctypes.c_uint64),
+        ("gate_scale_offset", ctypes.c_uint64),
+        ("up_scale_offset", ctypes.c_uint64),
+        ("down_weight_offset", ctypes.c_uint64),
+        ("down_scale_offset", ctypes.c_uint64),
+    ]
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_U64 = ctypes.c_uint64
+_SZ = ctypes.c_size_t
+_LAYOUT = ctypes.POINTER(SlotLayoutC)
+
+_SIGNATURES = {
+    "q4_expert_gate_up": (ctypes.c_int, [_P, _LAYOUT, _P, _I64, _I64, _I64, _P, _P]),
+    "q4_expert_gate_up_probe": (ctypes.c_int, [_P, _LAYOUT, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
+    "q4_grouped_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "q4_expert_gate_up_grouped": (ctypes.c_int, [_P, _U64, _I64, _LAYOUT, _P, _I64, _P, _I64, _I64, _I64,
+                                                 _P, _P, _SZ, _P]),
+    "q4_expert_gate_up_grouped_probe": (ctypes.c_int, [_P, _U64, _I64, _LAYOUT, _P, _I64, _P, _I64, _I64,
+                                                       _I64, _P, _P, _P, _P, _SZ, _P]),
+    "q4_validate_gate_up": (ctypes.c_int, [_P, _LAYOUT, _P, _I64, _I64, _I64, _P]),
+    "q4_validate_grouped": (ctypes.c_int, [_P, _U64, _I64, _LAYOUT, _P, _I64, _P, _I64, _I64, _I64, _P, _P,
+                                           _SZ]),
+    "q4_last_error": (ctypes.c_char_p, []),
+    "q4_abi_version": (ctypes.c_int, []),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libq4moe.so from the package directory (raises if it is missing)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m quantized_moe_expert_q4_amd.build` "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().q4_last_error().decode()
+
+
+def abi_version() -> int:
+    return load().q4_abi_version()
+
+
+def layout_c(layout) -> SlotLayoutC:
+    """Marshal any object with the seven offset attributes into the C struct."""
+    return SlotLayoutC(
+        int(layout.slot_bytes), int(layout.gate_weight_offset), int(layout.up_weight_offset),
+        int(layout.gate_scale_offset), int(layout.up_scale_offset),
+        int(getattr(layout, "down_weight_offset", OFFSET_ABSENT)),
+        int(getattr(layout, "down_scale_offset", OFFSET_ABSENT)))
+
+
+def _check(status: int) -> int:
+    if status != Q4_OK:
+        raise Q4Error(status, last_error())
+    return status
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def grouped_workspace_bytes(M: int, K: int, num_slots: int) -> int:
+    return int(load().q4_grouped_workspace_bytes(M, K, num_slots))
+
+
+def expert_gate_up(slot, layout, x, M: int, H: int, I: int, out, gate_probe=None, up_probe=None,
+                   stream=None) -> None:
+    """Enqueue the single-expert kernel (see q4_expert_gate_up in include/q4moe.h)."""
+    lib = load()
+    lay = layout_c(layout)
+    if gate_probe is None and up_probe is None:
+        st = lib.q4_expert_gate_up(_ptr(slot), ctypes.byref(lay), _ptr(x), M, H, I, _ptr(out), _stream(stream))
+    else:
+        st = lib.q4_expert_gate_up_probe(_ptr(slot), ctypes.byref(lay), _ptr(x), M, H, I, _ptr(out),
+                                         _ptr(gate_probe), _ptr(up_probe), _stream(stream))
+    _check(st)
+
+
+def expert_gate_up_grouped(slots_base, slot_stride: int, num_slots: int, layout, x, M: int, slot_ids, K: int,
+                           H: int, I: int, out, workspace, workspace_bytes: int, gate_probe=None,
+                           up_probe=None, stream=None) -> None:
+    """Enqueue the grouped kernel (see q4_expert_gate_up_grouped in include/q4moe.h)."""
+    lib = load()
+    lay = layout_c(layout)
+    if gate_probe is None and up_probe is None:
+        st = lib.q4_expert_gate_up_grouped(_ptr(slots_base), slot_stride, num_slots, ctypes.byref(lay), _ptr(x),
+                                           M, _ptr(slot_ids), K, H, I, _ptr(out), _ptr(workspace),
+                                           workspace_bytes, _stream(stream))
+    else:
+        st = lib.q4_expert_gate_up_grouped_probe(_ptr(slots_base), slot_stride, num_slots, ctypes.byref(lay),
+                                                 _ptr(x), M, _ptr(slot_ids), K, H, I, _ptr(out),
+                                                 _ptr(gate_probe), _ptr(up_probe), _ptr(workspace),
+                                                 workspace_bytes, _stream(stream))
+    _check(st)
+
+
+def validate_gate_up(slot, layout, x, M: int, H: int, I: int, out) -> int:
+    """Host-only argument check; returns the status (0 or negative)."""
+    lay = None if layout is None else layout_c(layout)
+    return load().q4_validate_gate_up(_ptr(slot), None if lay is None else ctypes.byref(lay), _ptr(x), M, H, I,
+                                      _ptr(out))
+
+
+def validate_grouped(slots_base, slot_stride, num_slots, layout, x, M, slot_ids, K, H, I, out, workspace,
+                     workspace_bytes) -> int:
+    lay = None if layout is None else layout_c(layout)
+    return load().q4_validate_grouped(_ptr(slots_base), slot_stride, num_slots,
+                                      None if lay is None else ctypes.byref(lay), _ptr(x), M, _ptr(slot_ids), K,
+                                      H, I, _ptr(out), _ptr(workspace), workspace_bytes)

@@ -1,0 +1,245 @@
+// C ABI of the Q4 expert gate/up library: argument validation and dispatch.
+//
+// Validation mirrors validateCall (page 52 of the @mlx-bun/inference 1.0.0
+// diff, kernels/glm52/streamed-experts.ts) and validateRange (page 51,
+// kernels/glm52/layout.ts): positive sizes, H divisible by the 8 weights of a
+// packed word, input [M, H] with M >= 1, every slot field inside the slot, a
+// page-aligned slot pointer.  The pages' "divisible by 4" rule comes from their
+// 4-rows-per-threadgroup grid and does not apply to these kernels, and the
+// pages' 16 KiB page alignment is read as 4096 bytes (device allocations).
+#include <stdint.h>
+#include <string.h>
+
+#include <string>
+
+#include "q4moe.h"
+#include "q4moe_launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return Q4_OK;
+}
+
+constexpr uint64_t kSlotAlign = 4096;
+constexpr int64_t kMaxH = 65536;
+constexpr int64_t kMaxM = 65535;
+constexpr int64_t kMaxPairs = 65536;
+constexpr int64_t kMaxSlots = 65535;
+constexpr uint64_t kMaxWeightBytes = (1ull << 31) - 16;
+constexpr size_t kWorkspaceBytes = 256;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_range(uint64_t offset, uint64_t length, uint64_t slot_bytes, const char* label) {
+  if (offset > slot_bytes || length > slot_bytes - offset)
+    return fail(Q4_ERR_RANGE, std::string(label) + " exceeds the canonical expert slot");
+  return Q4_OK;
+}
+
+int check_dims(int64_t M, int64_t H, int64_t I) {
+  if (H <= 0) return fail(Q4_ERR_INVALID_ARGUMENT, "hidden size must be a positive integer");
+  if (I <= 0) return fail(Q4_ERR_INVALID_ARGUMENT, "intermediate size must be a positive integer");
+  if (H % 8 != 0) return fail(Q4_ERR_INVALID_ARGUMENT, "Q4 expert dimensions must be divisible by 8");
+  if (M < 1) return fail(Q4_ERR_INVALID_ARGUMENT, "Q4 expert gate/up requires input [M,H] with M >= 1");
+  if (H > kMaxH) return fail(Q4_ERR_UNSUPPORTED, "hidden size above 65536 is not supported");
+  if (M > kMaxM) return fail(Q4_ERR_UNSUPPORTED, "more than 65535 tokens per call is not supported");
+  if ((uint64_t)I * (uint64_t)(H / 2) > kMaxWeightBytes)
+    return fail(Q4_ERR_UNSUPPORTED, "a projection above 2^31 - 16 bytes is not supported");
+  return Q4_OK;
+}
+
+int check_layout(const q4_slot_layout* L, int64_t H, int64_t I) {
+  if (!L) return fail(Q4_ERR_INVALID_ARGUMENT, "slot layout must not be null");
+  if (L->slot_bytes == 0) return fail(Q4_ERR_INVALID_ARGUMENT, "expert slot bytes must be a positive integer");
+  const uint64_t wb = (uint64_t)I * (uint64_t)(H / 2);
+  int rc;
+  if (L->down_weight_offset != Q4_OFFSET_ABSENT &&
+      (rc = check_range(L->down_weight_offset, wb, L->slot_bytes, "down weights")))
+    return rc;
+  if ((rc = check_range(L->gate_weight_offset, wb, L->slot_bytes, "gate weights"))) return rc;
+  if ((rc = check_range(L->up_weight_offset, wb, L->slot_bytes, "up weights"))) return rc;
+  if (L->down_scale_offset != Q4_OFFSET_ABSENT &&
+      (rc = check_range(L->down_scale_offset, 4 * (uint64_t)H, L->slot_bytes, "down scales")))
+    return rc;
+  if ((rc = check_range(L->gate_scale_offset, 4 * (uint64_t)I, L->slot_bytes, "gate scales"))) return rc;
+  if ((rc = check_range(L->up_scale_offset, 4 * (uint64_t)I, L->slot_bytes, "up scales"))) return rc;
+  if (L->gate_weight_offset % 16 || L->up_weight_offset % 16)
+    return fail(Q4_ERR_ALIGNMENT, "gate and up weight offsets must be multiples of 16 bytes");
+  if (L->gate_scale_offset % 4 || L->up_scale_offset % 4)
+    return fail(Q4_ERR_ALIGNMENT, "gate and up scale offsets must be multiples of 4 bytes");
+  return Q4_OK;
+}
+
+int check_io(const void* x, const void* out, const void* gate_probe, const void* up_probe) {
+  if (!x) return fail(Q4_ERR_INVALID_ARGUMENT, "input x must be a non-null device pointer");
+  if (!out) return fail(Q4_ERR_INVALID_ARGUMENT, "output must be a non-null device pointer");
+  if (!aligned(x, 16)) return fail(Q4_ERR_ALIGNMENT, "input x must be 16-byte aligned");
+  if (!aligned(out, 2)) return fail(Q4_ERR_ALIGNMENT, "output must be 2-byte aligned");
+  if ((gate_probe && !aligned(gate_probe, 4)) || (up_probe && !aligned(up_probe, 4)))
+    return fail(Q4_ERR_ALIGNMENT, "gate/up probes must be 4-byte aligned");
+  return Q4_OK;
+}
+
+int check_single(const void* slot, const q4_slot_layout* layout, const void* x, int64_t M, int64_t H,
+                 int64_t I, const void* out, const void* gp, const void* up) {
+  int rc;
+  if ((rc = check_dims(M, H, I))) return rc;
+  if (!slot) return fail(Q4_ERR_INVALID_ARGUMENT, "expert slot pointer must be a non-null device pointer");
+  if (!aligned(slot, kSlotAlign))
+    return fail(Q4_ERR_ALIGNMENT, "expert slot pointer must be page-aligned (4096 bytes) for direct device access");
+  if ((rc = check_layout(layout, H, I))) return rc;
+  if ((rc = check_io(x, out, gp, up))) return rc;
+  return ok();
+}
+
+int check_grouped(const void* base, uint64_t stride, int64_t num_slots, const q4_slot_layout* layout,
+                  const void* x, int64_t M, const int32_t* ids, int64_t K, int64_t H, int64_t I,
+                  const void* out, const void* gp, const void* up, const void* ws, size_t ws_bytes) {
+  int rc;
+  if ((rc = check_dims(M, H, I))) return rc;
+  if (K < 1) return fail(Q4_ERR_INVALID_ARGUMENT, "top-k must be a positive integer");
+  if (num_slots < 1) return fail(Q4_ERR_INVALID_ARGUMENT, "number of slots must be a positive integer");
+  if (num_slots > kMaxSlots) return fail(Q4_ERR_UNSUPPORTED, "more than 65535 slots is not supported");
+  if (M * K > kMaxPairs) return fail(Q4_ERR_UNSUPPORTED, "more than 65536 routed pairs per call is not supported");
+  if (!base) return fail(Q4_ERR_INVALID_ARGUMENT, "expert slot pointer must be a non-null device pointer");
+  if (!aligned(base, kSlotAlign))
+    return fail(Q4_ERR_ALIGNMENT, "expert slot pointer must be page-aligned (4096 bytes) for direct device access");
+  if (stride % kSlotAlign) return fail(Q4_ERR_ALIGNMENT, "slot stride must be a multiple of 4096 bytes");
+  if ((rc = check_layout(layout, H, I))) return rc;
+  if (stride < layout->slot_bytes) return fail(Q4_ERR_RANGE, "slot stride is shorter than the slot");
+  if ((uint64_t)(num_slots - 1) > (UINT64_MAX - layout->slot_bytes) / stride)
+    return fail(Q4_ERR_RANGE, "slot array exceeds the address space");
+  if (!ids) return fail(Q4_ERR_INVALID_ARGUMENT, "slot ids must be a non-null device pointer");
+  if (!aligned(ids, 4)) return fail(Q4_ERR_ALIGNMENT, "slot ids must be 4-byte aligned");
+  if ((rc = check_io(x, out, gp, up))) return rc;
+  if (!ws) return fail(Q4_ERR_WORKSPACE, "workspace must be a non-null device pointer");
+  if (!aligned(ws, 256)) return fail(Q4_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+  if (ws_bytes < q4_grouped_workspace_bytes(M, K, num_slots))
+    return fail(Q4_ERR_WORKSPACE, "workspace is smaller than q4_grouped_workspace_bytes()");
+  return ok();
+}
+
+int launch(const q4::GateUpParams& p, int num_slots, int tokens_per_slot, hipStream_t stream) {
+  const q4::LaunchPlan lp = q4::plan_launch(tokens_per_slot, p.I, num_slots, p.H);
+  const hipError_t e = q4::launch_gate_up(p, num_slots, lp, stream);
+  if (e != hipSuccess) return fail(Q4_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  return ok();
+}
+
+int run_single(const void* slot, const q4_slot_layout* layout, const void* x, int64_t M, int64_t H, int64_t I,
+               void* out, float* gp, float* up, q4_stream_t stream) {
+  int rc = check_single(slot, layout, x, M, H, I, out, gp, up);
+  if (rc) return rc;
+  q4::GateUpParams p{};
+  p.slots = static_cast<const uint8_t*>(slot);
+  p.slot_stride = layout->slot_bytes;
+  p.gate_w_off = layout->gate_weight_offset;
+  p.up_w_off = layout->up_weight_offset;
+  p.gate_s_off = layout->gate_scale_offset;
+  p.up_s_off = layout->up_scale_offset;
+  p.x = static_cast<const uint16_t*>(x);
+  p.ids = nullptr;
+  p.out = static_cast<uint16_t*>(out);
+  p.gate_probe = gp;
+  p.up_probe = up;
+  p.invalid_count = nullptr;
+  p.M = (int)M;
+  p.K = 1;
+  p.H = (int)H;
+  p.I = (int)I;
+  p.num_slots = 1;
+  return launch(p, 1, (int)M, reinterpret_cast<hipStream_t>(stream));
+}
+
+int run_grouped(const void* base, uint64_t stride, int64_t num_slots, const q4_slot_layout* layout,
+                const void* x, int64_t M, const int32_t* ids, int64_t K, int64_t H, int64_t I, void* out,
+                float* gp, float* up, void* ws, size_t ws_bytes, q4_stream_t stream) {
+  int rc = check_grouped(base, stride, num_slots, layout, x, M, ids, K, H, I, out, gp, up, ws, ws_bytes);
+  if (rc) return rc;
+  q4::GateUpParams p{};
+  p.slots = static_cast<const uint8_t*>(base);
+  p.slot_stride = stride;
+  p.gate_w_off = layout->gate_weight_offset;
+  p.up_w_off = layout->up_weight_offset;
+  p.gate_s_off = layout->gate_scale_offset;
+  p.up_s_off = layout->up_scale_offset;
+  p.x = static_cast<const uint16_t*>(x);
+  p.ids = ids;
+  p.out = static_cast<uint16_t*>(out);
+  p.gate_probe = gp;
+  p.up_probe = up;
+  p.invalid_count = static_cast<int32_t*>(ws);
+  p.M = (int)M;
+  p.K = (int)K;
+  p.H = (int)H;
+  p.I = (int)I;
+  p.num_slots = (int)num_slots;
+  return launch(p, (int)num_slots, (int)M, reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int q4_expert_gate_up(const void* slot, const q4_slot_layout* layout, const void* x_bf16, int64_t M, int64_t H,
+                      int64_t I, void* out_bf16, q4_stream_t stream) {
+  return run_single(slot, layout, x_bf16, M, H, I, out_bf16, nullptr, nullptr, stream);
+}
+
+int q4_expert_gate_up_probe(const void* slot, const q4_slot_layout* layout, const void* x_bf16, int64_t M,
+                            int64_t H, int64_t I, void* out_bf16, float* gate_f32, float* up_f32,
+                            q4_stream_t stream) {
+  return run_single(slot, layout, x_bf16, M, H, I, out_bf16, gate_f32, up_f32, stream);
+}
+
+size_t q4_grouped_workspace_bytes(int64_t M, int64_t K, int64_t num_slots) {
+  (void)M;
+  (void)K;
+  (void)num_slots;
+  return kWorkspaceBytes;
+}
+
+int q4_expert_gate_up_grouped(const void* slots_base, uint64_t slot_stride, int64_t num_slots,
+                              const q4_slot_layout* layout, const void* x_bf16, int64_t M,
+                              const int32_t* slot_ids, int64_t K, int64_t H, int64_t I, void* out_bf16,
+                              void* workspace, size_t workspace_bytes, q4_stream_t stream) {
+  return run_grouped(slots_base, slot_stride, num_slots, layout, x_bf16, M, slot_ids, K, H, I, out_bf16, nullptr,
+                     nullptr, workspace, workspace_bytes, stream);
+}
+
+int q4_expert_gate_up_grouped_probe(const void* slots_base, uint64_t slot_stride, int64_t num_slots,
+                                    const q4_slot_layout* layout, const void* x_bf16, int64_t M,
+                                    const int32_t* slot_ids, int64_t K, int64_t H, int64_t I, void* out_bf16,
+                                    float* gate_f32, float* up_f32, void* workspace, size_t workspace_bytes,
+                                    q4_stream_t stream) {
+  return run_grouped(slots_base, slot_stride, num_slots, layout, x_bf16, M, slot_ids, K, H, I, out_bf16, gate_f32,
+                     up_f32, workspace, workspace_bytes, stream);
+}
+
+int q4_validate_gate_up(const void* slot, const q4_slot_layout* layout, const void* x_bf16, int64_t M, int64_t H,
+                        int64_t I, const void* out_bf16) {
+  return check_single(slot, layout, x_bf16, M, H, I, out_bf16, nullptr, nullptr);
+}
+
+int q4_validate_grouped(const void* slots_base, uint64_t slot_stride, int64_t num_slots,
+                        const q4_slot_layout* layout, const void* x_bf16, int64_t M, const int32_t* slot_ids,
+                        int64_t K, int64_t H, int64_t I, const void* out_bf16, const void* workspace,
+                        size_t workspace_bytes) {
+  return check_grouped(slots_base, slot_stride, num_slots, layout, x_bf16, M, slot_ids, K, H, I, out_bf16, nullptr,
+                       nullptr, workspace, workspace_bytes);
+}
+
+const char* q4_last_error(void) { return g_err.c_str(); }
+
+int q4_abi_version(void) { return 1; }
+
+}  // extern "C"

@@ -55,12 +55,19 @@ class SlotLayout:
 
 
 def contiguous_layout(H: int, I: int, align: int = 4096) -> SlotLayout:
-    """Gate words, up words, gate scales, up scales back to back."""
+    """Gate words, up words, gate scales, up scales back to back.
+
+    Each field starts on a 16-byte boundary (a no-op for the five workloads,
+    whose fields are all multiples of 16 bytes long).
+    """
+    def up16(n):
+        return (n + 15) // 16 * 16
+
     wbytes = I * H // 2
     gate_w = 0
-    up_w = wbytes
-    gate_s = 2 * wbytes
-    up_s = gate_s + 4 * I
+    up_w = up16(wbytes)
+    gate_s = up16(up_w + wbytes)
+    up_s = up16(gate_s + 4 * I)
     end = up_s + 4 * I
     slot = (end + align - 1) // align * align
     return SlotLayout(slot, gate_w, up_w, gate_s, up_s)

@@ -1,0 +1,99 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI
+and compare it with the oracle under the stated tolerances.
+
+T1 (F32 gate/up before their bf16 rounding): |g - g_ref| <= 1e-5 |g_ref| + 1e-6.
+T2 (bf16 output): distance in ordered bf16 keys (+0 and -0 equal, two values
+both below 2^-100 in magnitude equal) between the GPU output and the oracle's
+tail evaluated on the GPU's own F32 gate/up is at most 1.
+"""
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import quantized_moe_expert_q4_amd as q4
+from quantized_moe_expert_q4_amd.device import aligned_empty, bf16_bits, upload_bf16_bits, upload_slots
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run_single(slot_np, layout, xbits, H, I, probes=True):
+    M = xbits.shape[0]
+    slot = upload_slots(slot_np.reshape(1, -1))
+    x = upload_bf16_bits(xbits)
+    out = torch.empty((M, I), dtype=torch.bfloat16, device="cuda")
+    g = torch.empty((M, I), dtype=torch.float32, device="cuda") if probes else None
+    u = torch.empty((M, I), dtype=torch.float32, device="cuda") if probes else None
+    q4.expert_gate_up(slot, layout, x, M, H, I, out, g, u)
+    torch.cuda.synchronize()
+    res = [bf16_bits(out)]
+    if probes:
+        res += [g.cpu().numpy(), u.cpu().numpy()]
+    return res
+
+
+def run_grouped(slots_np, layout, xbits, ids, H, I, probes=True, ws_fill=None):
+    M, K = ids.shape
+    E = slots_np.shape[0]
+    slots = upload_slots(slots_np)
+    x = upload_bf16_bits(xbits)
+    idt = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda()
+    out = torch.empty((M, K, I), dtype=torch.bfloat16, device="cuda")
+    g = torch.empty((M, K, I), dtype=torch.float32, device="cuda") if probes else None
+    u = torch.empty((M, K, I), dtype=torch.float32, device="cuda") if probes else None
+    wsb = q4.grouped_workspace_bytes(M, K, E)
+    ws = aligned_empty(wsb, 256)
+    ws.fill_(0xAB if ws_fill is None else ws_fill)
+    q4.expert_gate_up_grouped(slots, slots_np.shape[1], E, layout, x, M, idt, K, H, I, out, ws, wsb, g, u)
+    torch.cuda.synchronize()
+    invalid = int(ws[:4].cpu().numpy().view(np.int32)[0])
+    res = [bf16_bits(out)]
+    if probes:
+        res += [g.cpu().numpy(), u.cpu().numpy()]
+    return res, invalid
+
+
+def t1_violations(g, g_ref):
+    g = np.asarray(g, np.float64)
+    r = np.asarray(g_ref, np.float64)
+    bad = ~(np.abs(g - r) <= 1e-5 * np.abs(r) + 1e-6)
+    return int(bad.sum())
+
+
+def bf16_key(bits):
+    b = np.asarray(bits, dtype=np.int64)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def bf16_dist(a, b):
+    d = np.abs(bf16_key(a) - bf16_key(b))
+    va = np.abs(oracle.bf16_to_f32(a).astype(np.float64))
+    vb = np.abs(oracle.bf16_to_f32(b).astype(np.float64))
+    tiny = (va < 2.0 ** -100) & (vb < 2.0 ** -100)
+    return np.where(tiny, 0, d)
+
+
+def check_parity(out, g, u, g_ref, u_ref, out_ref, label, require_exact_gate_up=True):
+    """Assert T1 and T2; report (and by default require) bit-exact gate/up."""
+    n = out.size
+    t1g, t1u = t1_violations(g, g_ref), t1_violations(u, u_ref)
+    tail = oracle.swiglu_tail(g, u)
+    t2 = bf16_dist(out, tail)
+    e2e = bf16_dist(out, out_ref)
+    exact_g = int(np.sum(g.view(np.uint32) == np.asarray(g_ref, np.float32).view(np.uint32)))
+    exact_u = int(np.sum(u.view(np.uint32) == np.asarray(u_ref, np.float32).view(np.uint32)))
+    exact_o = int(np.sum(out == out_ref))
+    say(f"[{label}] n={n} T1 fail gate={t1g} up={t1u}; T2 max={int(t2.max())}; end-to-end max={int(e2e.max())}; "
+        f"bit-exact gate={exact_g}/{n} up={exact_u}/{n} out={exact_o}/{n}")
+    assert t1g == 0 and t1u == 0, label
+    assert int(t2.max()) <= 1, label
+    assert int(e2e.max()) <= 1, label
+    if require_exact_gate_up:
+        assert exact_g == n and exact_u == n, label
+    return dict(n=n, exact_gate=exact_g, exact_up=exact_u, exact_out=exact_o, t2_max=int(t2.max()),
+                e2e_max=int(e2e.max()))
