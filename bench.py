@@ -1,0 +1,269 @@
+"""Weight-stream benchmark of the Q4 expert gate/up + SwiGLU path on one MI355X.
+
+Workload (the decode-matvec expert shape H=4096, I=1536 with M=1 token):
+a pool of 171 distinct expert slots of that shape (171 * 6,303,744 B =
+1.08 GB, larger than the 256 MB Infinity Cache, so every step streams its
+weights from HBM).  One step is one grouped call that routes the token(s) to
+every slot of the pool: the routing scan, activation split, weight stream,
+exact accumulation, scale and SwiGLU tail of every slot, in one launch.
+
+The headline ``value`` is algorithmic weight bytes (packed gate and up
+nibbles plus their F32 row scales) per second at M=1; the same pool at M=8
+(eight tokens on every slot, the verify width) is reported in ``m8``.
+
+``roofline`` prices the gate/up kernel against MI355X's 8 TB/s HBM peak;
+``achieved`` is the algorithmic bytes of one launch divided by the mean
+launch duration from HIP events on the launch stream.  ``traffic`` comes from
+the committed rocprofv3 counter summary (profiles/traffic_gate_up_pool.json)
+when that summary was taken on the current kernel source, else null.
+
+``cpu_baseline`` times the CPU oracle (test infrastructure, exact arithmetic)
+on the host cores on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+POOL_SLOTS = 171
+DISTINCT_CONTENTS = 8
+H, I = 4096, 1536
+SEED = 102
+KERNEL_SRC = os.path.join(ROOT, "quantized_moe_expert_q4_amd", "csrc", "q4moe_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_pool.json")
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def make_pool_host():
+    import synth
+    lay = synth.contiguous_layout(H, I)
+    rng = np.random.default_rng(SEED)
+    contents = np.zeros((DISTINCT_CONTENTS, lay.slot_bytes), np.uint8)
+    for d in range(DISTINCT_CONTENTS):
+        synth.fill_slot(rng, H, I, lay, out=contents[d])
+    x = synth.bf16_normal(rng, (8, H))
+    return lay, contents, x
+
+
+def weight_bytes_per_slot() -> int:
+    return 2 * (I * H // 2) + 2 * 4 * I
+
+
+class Pool:
+    def __init__(self, lay, contents, x8):
+        import torch
+        from quantized_moe_expert_q4_amd.device import aligned_empty, upload_bf16_bits
+        self.torch = torch
+        self.lay = lay
+        self.stride = lay.slot_bytes
+        self.slots = aligned_empty(POOL_SLOTS * self.stride)
+        dev_contents = torch.from_numpy(contents).cuda()
+        for s in range(POOL_SLOTS):
+            self.slots[s * self.stride:(s + 1) * self.stride].copy_(dev_contents[s % DISTINCT_CONTENTS])
+        del dev_contents
+        self.x8 = upload_bf16_bits(x8)
+        torch.cuda.synchronize()
+
+    def step_fn(self, M: int):
+        import quantized_moe_expert_q4_amd as q4
+        torch = self.torch
+        from quantized_moe_expert_q4_amd.device import aligned_empty
+        x = self.x8[:M].contiguous()
+        ids = torch.arange(POOL_SLOTS, dtype=torch.int32, device="cuda").repeat(M, 1).contiguous()
+        out = torch.empty((M, POOL_SLOTS, I), dtype=torch.bfloat16, device="cuda")
+        wsb = q4.grouped_workspace_bytes(M, POOL_SLOTS, POOL_SLOTS)
+        ws = aligned_empty(wsb, 256)
+        stream = torch.cuda.current_stream()
+
+        def step():
+            q4.expert_gate_up_grouped(self.slots, self.stride, POOL_SLOTS, self.lay, x, M, ids, POOL_SLOTS, H, I,
+                                      out, ws, wsb, stream=stream)
+        return step, stream
+
+    def single_fn(self):
+        """Back-to-back single-expert launches, one per pool slot (context)."""
+        import quantized_moe_expert_q4_amd as q4
+        torch = self.torch
+        x = self.x8[:1].contiguous()
+        out = torch.empty((1, I), dtype=torch.bfloat16, device="cuda")
+        stream = torch.cuda.current_stream()
+        ptr0 = self.slots.data_ptr()
+
+        def step():
+            for s in range(POOL_SLOTS):
+                q4.expert_gate_up(ptr0 + s * self.stride, self.lay, x, 1, H, I, out, stream=stream)
+        return step, stream
+
+
+def time_steps(step, stream, steps: int, warmup: int):
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / 1000.0, wall
+
+
+def cpu_baseline(lay, contents, x8, budget_s: float = 12.0):
+    """Time the oracle on whole pool slots at M=1 until ~budget_s of CPU work."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    n = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget_s:
+            oracle.expert_gate_up(contents[n % DISTINCT_CONTENTS], lay, x8[:1], H, I)
+            n += 1
+        dt = time.perf_counter() - t0
+    gbs = n * weight_bytes_per_slot() / dt / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} pool-slot gate/up passes at M=1 (H={H}, I={I}; exact oracle, one thread), {dt:.1f} s",
+            "cpu": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def load_traffic(bytes_per_launch: float):
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_sha256") != kernel_sha():
+        return None
+    return {"fetch_bytes": t["fetch_bytes_per_launch"], "write_bytes": t["write_bytes_per_launch"],
+            "fetch_over_algorithmic": round(t["fetch_bytes_per_launch"] / bytes_per_launch, 4),
+            "source": os.path.relpath(TRAFFIC_FILE, ROOT)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--only", choices=["m1", "m8", "single", "copy"], default=None,
+                    help="run one leg only (for profiling); 'copy' times a plain 1 GiB device copy, "
+                         "the reference for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE to bytes")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this path runs on a single MI355X (no multi-GPU leg)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import quantized_moe_expert_q4_amd as q4
+    q4.load()
+
+    if args.only == "copy":
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        stream = torch.cuda.current_stream()
+        t, _ = time_steps(lambda: dst.copy_(src), stream, args.steps, args.warmup)
+        print(json.dumps({"copy_bytes": 1 << 30, "steps": args.steps,
+                          "GBps_read_plus_write": round(2 * (1 << 30) * args.steps / t / 1e9, 1)}), flush=True)
+        return
+
+    lay, contents, x8 = make_pool_host()
+    pool = Pool(lay, contents, x8)
+    bytes_step = POOL_SLOTS * weight_bytes_per_slot()
+
+    res = {}
+    legs = [args.only] if args.only else ["m1", "m8", "single"]
+    for leg in legs:
+        if leg == "single":
+            step, stream = pool.single_fn()
+            steps = max(1, args.steps // 5)
+        else:
+            step, stream = pool.step_fn(1 if leg == "m1" else 8)
+            steps = args.steps
+        t, wall = time_steps(step, stream, steps, args.warmup)
+        res[leg] = dict(seconds=t, wall=wall, steps=steps)
+
+    out = {}
+    primary = "m1" if "m1" in res else legs[0]
+    r = res[primary]
+    sec_per_step = r["seconds"] / r["steps"]
+    value = bytes_step / sec_per_step / 1e9
+    M = 8 if primary == "m8" else 1
+    out.update({
+        "metric": "achieved weight GB/s (% of HBM peak) for Q4 gate/up SwiGLU at M=1 and M=8",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": r["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": round(sec_per_step * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "q4 weights x bf16 activations, exact int32 matrix-core accumulation, f32 scale, bf16 out",
+        "data": "synthetic (seeded uniform nibbles, U[0.005,0.02] f32 scales, N(0,1) bf16 x)",
+        "config": {"workload": f"expert gate/up+SwiGLU, H={H} I={I}, M={M}, {POOL_SLOTS}-slot cold pool "
+                               f"({bytes_step / 1e9:.3f} GB of weights+scales per step), one grouped launch per step",
+                   "H": H, "I": I, "M": M, "slots": POOL_SLOTS, "bytes_per_step": bytes_step},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "rows_per_s": round(M * POOL_SLOTS * I / sec_per_step, 1),
+    })
+    if "m8" in res and primary != "m8":
+        s8 = res["m8"]["seconds"] / res["m8"]["steps"]
+        v8 = bytes_step / s8 / 1e9
+        out["m8"] = {"value": round(v8, 2), "unit": "GB/s", "pct_hbm_peak": round(100 * v8 / HBM_PEAK_GBS, 2),
+                     "ms_per_step": round(s8 * 1e3, 4), "rows_per_s": round(8 * POOL_SLOTS * I / s8, 1)}
+    if "single" in res:
+        ss = res["single"]["seconds"] / res["single"]["steps"]
+        vs = bytes_step / ss / 1e9
+        out["single_launches_m1"] = {
+            "value": round(vs, 2), "unit": "GB/s", "pct_hbm_peak": round(100 * vs / HBM_PEAK_GBS, 2),
+            "us_per_launch": round(ss / POOL_SLOTS * 1e6, 3),
+            "note": f"{POOL_SLOTS} back-to-back single-expert launches (one per slot, {weight_bytes_per_slot()} B each)"}
+    # One step is one launch of the gate/up kernel; the HIP events bracket the
+    # launches on their own stream, so the per-launch mean is seconds/steps.
+    achieved = bytes_step / sec_per_step / 1e9
+    out["roofline"] = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(bytes_step),
+                       "kernel": "q4::gate_up_kernel (grouped, M=%d)" % M,
+                       "algorithmic_bytes_per_launch": bytes_step}
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(lay, contents, x8, args.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
