@@ -85,7 +85,7 @@ class Pool:
         x = self.x8[:M].contiguous()
         ids = torch.arange(POOL_SLOTS, dtype=torch.int32, device="cuda").repeat(M, 1).contiguous()
         out = torch.empty((M, POOL_SLOTS, I), dtype=torch.bfloat16, device="cuda")
-        wsb = q4.grouped_workspace_bytes(M, POOL_SLOTS, POOL_SLOTS)
+        wsb = q4.grouped_workspace_bytes(M, POOL_SLOTS, H, I, POOL_SLOTS)
         ws = aligned_empty(wsb, 256)
         stream = torch.cuda.current_stream()
 

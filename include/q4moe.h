@@ -110,8 +110,11 @@ int q4_expert_gate_up_probe(const void *slot, const q4_slot_layout *layout,
                             void *out_bf16, float *gate_f32, float *up_f32,
                             q4_stream_t stream);
 
-/* Bytes of device workspace the grouped call needs (256-byte aligned). */
-size_t q4_grouped_workspace_bytes(int64_t M, int64_t K, int64_t num_slots);
+/* Bytes of device workspace the grouped call needs for these sizes on the
+ * current device (a multiple of 256), or 0 for sizes outside the limits.
+ * The workspace holds the digit-split activations, the routing plan and the
+ * partial sums of tiles shared by two waves; it is reused by every call. */
+size_t q4_grouped_workspace_bytes(int64_t M, int64_t K, int64_t H, int64_t I, int64_t num_slots);
 
 /*
  * Grouped call over routed expert slots.  Pair (t, j) runs token t against
@@ -122,8 +125,9 @@ size_t q4_grouped_workspace_bytes(int64_t M, int64_t K, int64_t num_slots);
  *   slot_ids  device int32 [M][K]; duplicates are allowed.  An id outside
  *             [0, num_slots) yields zero gate/up/out for that pair, and the
  *             number of such ids is stored as int32 at workspace[0].
- *   workspace device, >= q4_grouped_workspace_bytes(M, K, num_slots) bytes,
- *             256-byte aligned; contents on entry are ignored.
+ *   workspace device, >= q4_grouped_workspace_bytes(M, K, H, I, num_slots)
+ *             bytes, 256-byte aligned; contents on entry are ignored.  Calls
+ *             that share one workspace must not overlap in time.
  */
 int q4_expert_gate_up_grouped(const void *slots_base, uint64_t slot_stride,
                               int64_t num_slots, const q4_slot_layout *layout,

@@ -64,7 +64,7 @@ _LAYOUT = ctypes.POINTER(SlotLayoutC)
 _SIGNATURES = {
     "q4_expert_gate_up": (ctypes.c_int, [_P, _LAYOUT, _P, _I64, _I64, _I64, _P, _P]),
     "q4_expert_gate_up_probe": (ctypes.c_int, [_P, _LAYOUT, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
-    "q4_grouped_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "q4_grouped_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I64]),
     "q4_expert_gate_up_grouped": (ctypes.c_int, [_P, _U64, _I64, _LAYOUT, _P, _I64, _P, _I64, _I64, _I64,
                                                  _P, _P, _SZ, _P]),
     "q4_expert_gate_up_grouped_probe": (ctypes.c_int, [_P, _U64, _I64, _LAYOUT, _P, _I64, _P, _I64, _I64,
@@ -137,8 +137,8 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
-def grouped_workspace_bytes(M: int, K: int, num_slots: int) -> int:
-    return int(load().q4_grouped_workspace_bytes(M, K, num_slots))
+def grouped_workspace_bytes(M: int, K: int, H: int, I: int, num_slots: int) -> int:
+    return int(load().q4_grouped_workspace_bytes(M, K, H, I, num_slots))
 
 
 def expert_gate_up(slot, layout, x, M: int, H: int, I: int, out, gate_probe=None, up_probe=None,

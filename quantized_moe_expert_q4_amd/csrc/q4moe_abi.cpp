@@ -35,7 +35,6 @@ constexpr int64_t kMaxM = 65535;
 constexpr int64_t kMaxPairs = 65536;
 constexpr int64_t kMaxSlots = 65535;
 constexpr uint64_t kMaxWeightBytes = (1ull << 31) - 16;
-constexpr size_t kWorkspaceBytes = 256;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -123,7 +122,7 @@ int check_grouped(const void* base, uint64_t stride, int64_t num_slots, const q4
   if ((rc = check_io(x, out, gp, up))) return rc;
   if (!ws) return fail(Q4_ERR_WORKSPACE, "workspace must be a non-null device pointer");
   if (!aligned(ws, 256)) return fail(Q4_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
-  if (ws_bytes < q4_grouped_workspace_bytes(M, K, num_slots))
+  if (ws_bytes < q4_grouped_workspace_bytes(M, K, H, I, num_slots))
     return fail(Q4_ERR_WORKSPACE, "workspace is smaller than q4_grouped_workspace_bytes()");
   return ok();
 }
@@ -157,6 +156,11 @@ int run_single(const void* slot, const q4_slot_layout* layout, const void* x, in
   p.H = (int)H;
   p.I = (int)I;
   p.num_slots = 1;
+  if (q4::resident_fits((int)M, (int)H)) {
+    const hipError_t e = q4::launch_resident(p, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(Q4_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+    return ok();
+  }
   return launch(p, 1, (int)M, reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -165,7 +169,31 @@ int run_grouped(const void* base, uint64_t stride, int64_t num_slots, const q4_s
                 float* gp, float* up, void* ws, size_t ws_bytes, q4_stream_t stream) {
   int rc = check_grouped(base, stride, num_slots, layout, x, M, ids, K, H, I, out, gp, up, ws, ws_bytes);
   if (rc) return rc;
-  q4::GateUpParams p{};
+  if (q4::resident_fits((int)M, (int)H)) {
+    q4::ResidentParams r{};
+    r.slots = static_cast<const uint8_t*>(base);
+    r.slot_stride = stride;
+    r.gate_w_off = layout->gate_weight_offset;
+    r.up_w_off = layout->up_weight_offset;
+    r.gate_s_off = layout->gate_scale_offset;
+    r.up_s_off = layout->up_scale_offset;
+    r.x = static_cast<const uint16_t*>(x);
+    r.ids = ids;
+    r.out = static_cast<uint16_t*>(out);
+    r.gate_probe = gp;
+    r.up_probe = up;
+    r.invalid_count = static_cast<int32_t*>(ws);
+    r.M = (int)M;
+    r.K = (int)K;
+    r.H = (int)H;
+    r.I = (int)I;
+    r.num_slots = (int)num_slots;
+    const hipError_t e = q4::launch_resident(r, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(Q4_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+    return ok();
+  }
+  const q4::StreamPlan sp = q4::plan_stream((int)M, (int)K, (int)H, (int)I, (int)num_slots);
+  q4::StreamParams p{};
   p.slots = static_cast<const uint8_t*>(base);
   p.slot_stride = stride;
   p.gate_w_off = layout->gate_weight_offset;
@@ -177,13 +205,30 @@ int run_grouped(const void* base, uint64_t stride, int64_t num_slots, const q4_s
   p.out = static_cast<uint16_t*>(out);
   p.gate_probe = gp;
   p.up_probe = up;
-  p.invalid_count = static_cast<int32_t*>(ws);
+  p.ws = static_cast<uint8_t*>(ws);
+  p.off_xmax = sp.off_xmax;
+  p.off_count = sp.off_count;
+  p.off_offset = sp.off_offset;
+  p.off_vprefix = sp.off_vprefix;
+  p.off_pairs = sp.off_pairs;
+  p.off_bad = sp.off_bad;
+  p.off_fixcnt = sp.off_fixcnt;
+  p.off_fixrec = sp.off_fixrec;
+  p.off_digits = sp.off_digits;
+  p.tok_stride = sp.tok_stride;
+  p.rec_bytes = sp.rec_bytes;
   p.M = (int)M;
   p.K = (int)K;
   p.H = (int)H;
   p.I = (int)I;
   p.num_slots = (int)num_slots;
-  return launch(p, (int)num_slots, (int)M, reinterpret_cast<hipStream_t>(stream));
+  p.G = sp.g;
+  p.rtc = sp.rtc;
+  p.nsteps = sp.nsteps;
+  p.W = sp.waves;
+  const hipError_t e = q4::launch_stream(p, sp, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(Q4_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  return ok();
 }
 
 }  // namespace
@@ -201,11 +246,11 @@ int q4_expert_gate_up_probe(const void* slot, const q4_slot_layout* layout, cons
   return run_single(slot, layout, x_bf16, M, H, I, out_bf16, gate_f32, up_f32, stream);
 }
 
-size_t q4_grouped_workspace_bytes(int64_t M, int64_t K, int64_t num_slots) {
-  (void)M;
-  (void)K;
-  (void)num_slots;
-  return kWorkspaceBytes;
+size_t q4_grouped_workspace_bytes(int64_t M, int64_t K, int64_t H, int64_t I, int64_t num_slots) {
+  if (M < 1 || K < 1 || H < 8 || I < 1 || num_slots < 1 || M > kMaxM || H > kMaxH || num_slots > kMaxSlots ||
+      M * K > kMaxPairs)
+    return 0;
+  return (size_t)q4::plan_stream((int)M, (int)K, (int)H, (int)I, (int)num_slots).workspace;
 }
 
 int q4_expert_gate_up_grouped(const void* slots_base, uint64_t slot_stride, int64_t num_slots,

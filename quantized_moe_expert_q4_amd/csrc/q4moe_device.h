@@ -1,0 +1,172 @@
+// Device arithmetic shared by the Q4 gate/up kernels (single-expert and
+// grouped paths): activation digit split, weight split, exact recombination
+// with one F32 rounding, and the SwiGLU tail of GATE_UP_SOURCE (diff page 52
+// of @mlx-bun/inference 1.0.0, kernels/glm52/streamed-experts.ts).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4 {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+constexpr int kSlices = 6;       // digits per activation
+constexpr int kFracBits = 38;    // X = x * 2^(38 - e_top): |X| <= 255 * 2^38 < 2^46
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// Six balanced base-256 digits (two's-complement bytes 0..5) of
+// X = round(x * 2^(38 - e_top)); `etop1` is max(exponent field of the token's
+// largest |x|, 1).  Entries more than 38 binades below the largest are rounded
+// to the grid (half away from zero).
+__device__ __forceinline__ uint64_t x_digits(uint32_t b, int etop1) {
+  const uint32_t E = (b >> 7) & 0xFFu;
+  const uint32_t mag = (b & 0x7Fu) | (E ? 0x80u : 0u);
+  const int sh = (int)(E ? E : 1u) - etop1 + kFracBits;
+  int64_t X;
+  if (sh >= 0) {
+    X = (int64_t)mag << sh;
+  } else if (sh >= -8) {
+    X = (int64_t)((mag + (1u << (-sh - 1))) >> (-sh));
+  } else {
+    X = 0;
+  }
+  if (b & 0x8000u) X = -X;
+  const uint64_t C = 0x808080808080ull;  // 128 in every digit: offset to unsigned bytes
+  return ((uint64_t)X + C) ^ C;
+}
+
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)(((u >> 16) & 0x8000u) | 0x7FC0u);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ float bf16_val(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round (hi * 2^24 + lo) * 2^e2 * s to F32 once (nearest, ties to even).
+// (P, c) is a double-double of the exact product with error below 2^-105 of
+// it, while a non-zero distance to an F32 rounding midpoint is at least
+// ~2^-95 of it (the product has at most 95 significant bits), so the sign
+// test below decides every case exactly.
+__device__ float round_scaled(int64_t hi, int64_t lo, int e2, float s) {
+#pragma clang fp contract(off)
+  const double vh = (double)hi * 16777216.0;  // exact: |hi| < 2^47
+  const double vl = (double)lo;               // exact: |lo| < 2^47
+  const double S = vh + vl;
+  const double bb = S - vh;
+  const double eS = (vh - (S - bb)) + (vl - bb);  // S + eS == vh + vl exactly
+  const double sd = (double)s;
+  double P = S * sd;
+  const double eP = __builtin_fma(S, sd, -P);      // S*sd == P + eP exactly
+  double c = eP + eS * sd;
+  P = __builtin_ldexp(P, e2);
+  c = __builtin_ldexp(c, e2);
+  float r = (float)P;
+  if (!__builtin_isfinite(r)) return r;
+  const double rd = (double)r;
+  const double diff = (P - rd) + c;  // true value minus r (P - rd is exact)
+  if (diff != 0.0) {
+    const float n = nextafterf(r, diff > 0.0 ? __builtin_inff() : -__builtin_inff());
+    const double mid = 0.5 * (rd + (double)n);
+    const double dm = (P - mid) + c;  // true value minus the midpoint toward n
+    const bool beyond = diff > 0.0 ? (dm > 0.0) : (dm < 0.0);
+    if (beyond || (dm == 0.0 && (__float_as_uint(r) & 1u))) r = n;
+  }
+  return r;
+}
+
+// The lane-0 tail of GATE_UP_SOURCE: gate and up rounded to bf16, sigmoid in
+// F32 (exp evaluated in double and rounded once to F32), silu and the product
+// each rounded to bf16.
+__device__ uint16_t swiglu_tail(float gate, float up) {
+#pragma clang fp contract(off)
+  const float gT = bf16_val(bf16_rne(gate));
+  const float uT = bf16_val(bf16_rne(up));
+  const float e = (float)exp(-(double)gT);
+  const float d = 1.0f + e;
+  const float sig = 1.0f / d;
+  const float sT = bf16_val(bf16_rne(sig));
+  const float siluT = bf16_val(bf16_rne(gT * sT));
+  return bf16_rne(siluT * uT);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+template <bool VEC>
+__device__ __forceinline__ v4u load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (VEC) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  } else {
+    v4u v;
+    v.x = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+    v.y = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off + 4, 0, 0);
+    v.z = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off + 8, 0, 0);
+    v.w = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off + 12, 0, 0);
+    return v;
+  }
+}
+
+// 16*(q-8) as int8 for the even (p = 0,2,4,6) and odd nibbles of four words.
+__device__ __forceinline__ void split_weights(const v4u w, v4i& ev, v4i& od) {
+  const uint32_t a0 = w.x ^ 0x88888888u, a1 = w.y ^ 0x88888888u;
+  const uint32_t a2 = w.z ^ 0x88888888u, a3 = w.w ^ 0x88888888u;
+  od.x = (int)(a0 & 0xF0F0F0F0u);
+  od.y = (int)(a1 & 0xF0F0F0F0u);
+  od.z = (int)(a2 & 0xF0F0F0F0u);
+  od.w = (int)(a3 & 0xF0F0F0F0u);
+  ev.x = (int)((a0 << 4) & 0xF0F0F0F0u);
+  ev.y = (int)((a1 << 4) & 0xF0F0F0F0u);
+  ev.z = (int)((a2 << 4) & 0xF0F0F0F0u);
+  ev.w = (int)((a3 << 4) & 0xF0F0F0F0u);
+}
+
+
+// Byte transpose of eight digit words: lo[p]/hi[p] hold digits 0..3 / 4..5 of
+// position p (p = 0..7 of one packed word); d[s] receives digit s of the four
+// positions of parity `par` (p = par, par+2, par+4, par+6), one byte each --
+// the byte order of one MFMA B-operand dword.
+__device__ __forceinline__ void digit_words(const uint32_t (&lo)[8], const uint32_t (&hi)[8], int par,
+                                            uint32_t (&d)[6]) {
+  const uint32_t u01 = perm(lo[par + 2], lo[par], 0x05010400u);
+  const uint32_t u23 = perm(lo[par + 2], lo[par], 0x07030602u);
+  const uint32_t v01 = perm(lo[par + 6], lo[par + 4], 0x05010400u);
+  const uint32_t v23 = perm(lo[par + 6], lo[par + 4], 0x07030602u);
+  const uint32_t h01 = perm(hi[par + 2], hi[par], 0x05010400u);
+  const uint32_t h45 = perm(hi[par + 6], hi[par + 4], 0x05010400u);
+  d[0] = perm(v01, u01, 0x05040100u);
+  d[1] = perm(v01, u01, 0x07060302u);
+  d[2] = perm(v23, u23, 0x05040100u);
+  d[3] = perm(v23, u23, 0x07060302u);
+  d[4] = perm(h45, h01, 0x05040100u);
+  d[5] = perm(h45, h01, 0x07060302u);
+}
+
+// Digits of the eight bf16 activations packed in one uint4 (positions 0..7).
+__device__ __forceinline__ void x8_digits(const uint4 v, int etop1, uint32_t (&lo)[8], uint32_t (&hi)[8]) {
+  const uint32_t xb[8] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16,
+                          v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const uint64_t z = x_digits(xb[p], etop1);
+    lo[p] = (uint32_t)z;
+    hi[p] = (uint32_t)(z >> 32);
+  }
+}
+
+// Largest bf16 magnitude bits among eight packed activations.
+__device__ __forceinline__ uint32_t max_mag8(const uint4 v) {
+  uint32_t m = max(max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu), max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu));
+  return max(m, max(max(v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu), max(v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu)));
+}
+
+// Exponent offset of the recombined sum: sum(w*x) = V * 2^(etop1 - 176)
+// (X = x * 2^(172 - etop1) and the 16x weight factor).
+__device__ __forceinline__ int sum_exponent(int xmax_bits) { return max((xmax_bits >> 7) & 0xFF, 1) - 176; }
+
+}  // namespace q4

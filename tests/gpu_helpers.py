@@ -45,7 +45,7 @@ def run_grouped(slots_np, layout, xbits, ids, H, I, probes=True, ws_fill=None):
     out = torch.empty((M, K, I), dtype=torch.bfloat16, device="cuda")
     g = torch.empty((M, K, I), dtype=torch.float32, device="cuda") if probes else None
     u = torch.empty((M, K, I), dtype=torch.float32, device="cuda") if probes else None
-    wsb = q4.grouped_workspace_bytes(M, K, E)
+    wsb = q4.grouped_workspace_bytes(M, K, H, I, E)
     ws = aligned_empty(wsb, 256)
     ws.fill_(0xAB if ws_fill is None else ws_fill)
     q4.expert_gate_up_grouped(slots, slots_np.shape[1], E, layout, x, M, idt, K, H, I, out, ws, wsb, g, u)

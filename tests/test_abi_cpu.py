@@ -31,9 +31,13 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_workspace_size_is_aligned_and_positive():
-    for M, K, E in ((1, 1, 1), (32, 8, 64), (4096, 16, 65535)):
-        b = q4.grouped_workspace_bytes(M, K, E)
-        assert b >= 4 and b % 256 == 0
+    for M, K, H, I, E in ((1, 1, 8, 1, 1), (32, 8, 6144, 2048, 64), (4096, 16, 7168, 4096, 65535)):
+        b = q4.grouped_workspace_bytes(M, K, H, I, E)
+        assert b >= 256 and b % 256 == 0
+    # grows with the activations it holds (six digit bytes per position per token)
+    assert q4.grouped_workspace_bytes(8, 1, 8192, 64, 1) > q4.grouped_workspace_bytes(8, 1, 4096, 64, 1)
+    assert q4.grouped_workspace_bytes(0, 1, 4096, 64, 1) == 0
+    assert q4.grouped_workspace_bytes(1, 1, 4096, 64, 0) == 0
 
 
 SLOT = 1 << 20           # fake, 4096-aligned "device" addresses: validation never dereferences them
@@ -114,7 +118,7 @@ def test_down_fields_in_range_are_accepted():
 def _grouped(**kw):
     lay = _lay(6144, 2048)
     a = dict(base=SLOT, stride=lay.slot_bytes, E=64, layout=lay, x=X, M=32, ids=IDS, K=8, H=6144, I=2048,
-             out=OUT, ws=WS, wsb=q4.grouped_workspace_bytes(32, 8, 64))
+             out=OUT, ws=WS, wsb=q4.grouped_workspace_bytes(32, 8, 6144, 2048, 64))
     a.update(kw)
     st = q4.validate_grouped(a["base"], a["stride"], a["E"], a["layout"], a["x"], a["M"], a["ids"], a["K"], a["H"],
                              a["I"], a["out"], a["ws"], a["wsb"])
