@@ -39,13 +39,18 @@ POOL_SLOTS = 171
 DISTINCT_CONTENTS = 8
 H, I = 4096, 1536
 SEED = 102
-KERNEL_SRC = os.path.join(ROOT, "quantized_moe_expert_q4_amd", "csrc", "q4moe_kernels.hip")
+CSRC = os.path.join(ROOT, "quantized_moe_expert_q4_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_pool.json")
 
 
 def kernel_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """sha256 over every kernel source (a change anywhere invalidates stored counters)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
 
 
 def make_pool_host():
@@ -256,7 +261,7 @@ def main():
     achieved = bytes_step / sec_per_step / 1e9
     out["roofline"] = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(bytes_step),
-                       "kernel": "q4::gate_up_kernel (grouped, M=%d)" % M,
+                       "kernel": ("q4::resident_kernel" if M <= 2 else "q4::batch_kernel") + " (grouped call, M=%d)" % M,
                        "algorithmic_bytes_per_launch": bytes_step}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(lay, contents, x8, args.cpu_budget)

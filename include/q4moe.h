@@ -110,10 +110,10 @@ int q4_expert_gate_up_probe(const void *slot, const q4_slot_layout *layout,
                             void *out_bf16, float *gate_f32, float *up_f32,
                             q4_stream_t stream);
 
-/* Bytes of device workspace the grouped call needs for these sizes on the
- * current device (a multiple of 256), or 0 for sizes outside the limits.
- * The workspace holds the digit-split activations, the routing plan and the
- * partial sums of tiles shared by two waves; it is reused by every call. */
+/* Bytes of device workspace the grouped call needs for these sizes (a
+ * multiple of 256), or 0 for sizes outside the limits.  The workspace
+ * receives the count of out-of-range ids; its size may grow with the sizes
+ * in later versions, so callers should always ask. */
 size_t q4_grouped_workspace_bytes(int64_t M, int64_t K, int64_t H, int64_t I, int64_t num_slots);
 
 /*

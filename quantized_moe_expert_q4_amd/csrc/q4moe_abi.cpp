@@ -35,6 +35,7 @@ constexpr int64_t kMaxM = 65535;
 constexpr int64_t kMaxPairs = 65536;
 constexpr int64_t kMaxSlots = 65535;
 constexpr uint64_t kMaxWeightBytes = (1ull << 31) - 16;
+constexpr size_t kWorkspaceBytes = 256;  // [0]: number of out-of-range ids
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -127,73 +128,10 @@ int check_grouped(const void* base, uint64_t stride, int64_t num_slots, const q4
   return ok();
 }
 
-int launch(const q4::GateUpParams& p, int num_slots, int tokens_per_slot, hipStream_t stream) {
-  const q4::LaunchPlan lp = q4::plan_launch(tokens_per_slot, p.I, num_slots, p.H);
-  const hipError_t e = q4::launch_gate_up(p, num_slots, lp, stream);
-  if (e != hipSuccess) return fail(Q4_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
-  return ok();
-}
-
-int run_single(const void* slot, const q4_slot_layout* layout, const void* x, int64_t M, int64_t H, int64_t I,
-               void* out, float* gp, float* up, q4_stream_t stream) {
-  int rc = check_single(slot, layout, x, M, H, I, out, gp, up);
-  if (rc) return rc;
+q4::GateUpParams make_params(const void* base, uint64_t stride, int64_t num_slots, const q4_slot_layout* layout,
+                             const void* x, int64_t M, const int32_t* ids, int64_t K, int64_t H, int64_t I,
+                             void* out, float* gp, float* up, void* ws) {
   q4::GateUpParams p{};
-  p.slots = static_cast<const uint8_t*>(slot);
-  p.slot_stride = layout->slot_bytes;
-  p.gate_w_off = layout->gate_weight_offset;
-  p.up_w_off = layout->up_weight_offset;
-  p.gate_s_off = layout->gate_scale_offset;
-  p.up_s_off = layout->up_scale_offset;
-  p.x = static_cast<const uint16_t*>(x);
-  p.ids = nullptr;
-  p.out = static_cast<uint16_t*>(out);
-  p.gate_probe = gp;
-  p.up_probe = up;
-  p.invalid_count = nullptr;
-  p.M = (int)M;
-  p.K = 1;
-  p.H = (int)H;
-  p.I = (int)I;
-  p.num_slots = 1;
-  if (q4::resident_fits((int)M, (int)H)) {
-    const hipError_t e = q4::launch_resident(p, reinterpret_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return fail(Q4_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
-    return ok();
-  }
-  return launch(p, 1, (int)M, reinterpret_cast<hipStream_t>(stream));
-}
-
-int run_grouped(const void* base, uint64_t stride, int64_t num_slots, const q4_slot_layout* layout,
-                const void* x, int64_t M, const int32_t* ids, int64_t K, int64_t H, int64_t I, void* out,
-                float* gp, float* up, void* ws, size_t ws_bytes, q4_stream_t stream) {
-  int rc = check_grouped(base, stride, num_slots, layout, x, M, ids, K, H, I, out, gp, up, ws, ws_bytes);
-  if (rc) return rc;
-  if (q4::resident_fits((int)M, (int)H)) {
-    q4::ResidentParams r{};
-    r.slots = static_cast<const uint8_t*>(base);
-    r.slot_stride = stride;
-    r.gate_w_off = layout->gate_weight_offset;
-    r.up_w_off = layout->up_weight_offset;
-    r.gate_s_off = layout->gate_scale_offset;
-    r.up_s_off = layout->up_scale_offset;
-    r.x = static_cast<const uint16_t*>(x);
-    r.ids = ids;
-    r.out = static_cast<uint16_t*>(out);
-    r.gate_probe = gp;
-    r.up_probe = up;
-    r.invalid_count = static_cast<int32_t*>(ws);
-    r.M = (int)M;
-    r.K = (int)K;
-    r.H = (int)H;
-    r.I = (int)I;
-    r.num_slots = (int)num_slots;
-    const hipError_t e = q4::launch_resident(r, reinterpret_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return fail(Q4_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
-    return ok();
-  }
-  const q4::StreamPlan sp = q4::plan_stream((int)M, (int)K, (int)H, (int)I, (int)num_slots);
-  q4::StreamParams p{};
   p.slots = static_cast<const uint8_t*>(base);
   p.slot_stride = stride;
   p.gate_w_off = layout->gate_weight_offset;
@@ -205,30 +143,35 @@ int run_grouped(const void* base, uint64_t stride, int64_t num_slots, const q4_s
   p.out = static_cast<uint16_t*>(out);
   p.gate_probe = gp;
   p.up_probe = up;
-  p.ws = static_cast<uint8_t*>(ws);
-  p.off_xmax = sp.off_xmax;
-  p.off_count = sp.off_count;
-  p.off_offset = sp.off_offset;
-  p.off_vprefix = sp.off_vprefix;
-  p.off_pairs = sp.off_pairs;
-  p.off_bad = sp.off_bad;
-  p.off_fixcnt = sp.off_fixcnt;
-  p.off_fixrec = sp.off_fixrec;
-  p.off_digits = sp.off_digits;
-  p.tok_stride = sp.tok_stride;
-  p.rec_bytes = sp.rec_bytes;
+  p.invalid_count = static_cast<int32_t*>(ws);
   p.M = (int)M;
   p.K = (int)K;
   p.H = (int)H;
   p.I = (int)I;
   p.num_slots = (int)num_slots;
-  p.G = sp.g;
-  p.rtc = sp.rtc;
-  p.nsteps = sp.nsteps;
-  p.W = sp.waves;
-  const hipError_t e = q4::launch_stream(p, sp, reinterpret_cast<hipStream_t>(stream));
+  return p;
+}
+
+int launch(const q4::GateUpParams& p, q4_stream_t stream) {
+  const hipError_t e = q4::launch_gate_up(p, p.M, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(Q4_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
   return ok();
+}
+
+int run_single(const void* slot, const q4_slot_layout* layout, const void* x, int64_t M, int64_t H, int64_t I,
+               void* out, float* gp, float* up, q4_stream_t stream) {
+  const int rc = check_single(slot, layout, x, M, H, I, out, gp, up);
+  if (rc) return rc;
+  return launch(make_params(slot, layout->slot_bytes, 1, layout, x, M, nullptr, 1, H, I, out, gp, up, nullptr),
+                stream);
+}
+
+int run_grouped(const void* base, uint64_t stride, int64_t num_slots, const q4_slot_layout* layout,
+                const void* x, int64_t M, const int32_t* ids, int64_t K, int64_t H, int64_t I, void* out,
+                float* gp, float* up, void* ws, size_t ws_bytes, q4_stream_t stream) {
+  const int rc = check_grouped(base, stride, num_slots, layout, x, M, ids, K, H, I, out, gp, up, ws, ws_bytes);
+  if (rc) return rc;
+  return launch(make_params(base, stride, num_slots, layout, x, M, ids, K, H, I, out, gp, up, ws), stream);
 }
 
 }  // namespace
@@ -250,7 +193,7 @@ size_t q4_grouped_workspace_bytes(int64_t M, int64_t K, int64_t H, int64_t I, in
   if (M < 1 || K < 1 || H < 8 || I < 1 || num_slots < 1 || M > kMaxM || H > kMaxH || num_slots > kMaxSlots ||
       M * K > kMaxPairs)
     return 0;
-  return (size_t)q4::plan_stream((int)M, (int)K, (int)H, (int)I, (int)num_slots).workspace;
+  return kWorkspaceBytes;
 }
 
 int q4_expert_gate_up_grouped(const void* slots_base, uint64_t slot_stride, int64_t num_slots,

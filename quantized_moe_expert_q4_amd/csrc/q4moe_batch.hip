@@ -1,0 +1,352 @@
+// Q4 gate/up + SwiGLU for wide token groups (verify / prefill widths).
+//
+// Arithmetic: GATE_UP_SOURCE of the @mlx-bun/inference 1.0.0 diff, page 52
+// (kernels/glm52/streamed-experts.ts), made exact as in q4moe_device.h.
+//
+// A group of up to G = 16*NT/6 tokens has C = 6*count digit columns; for the
+// whole K they do not fit LDS, so the sixteen waves of a work-group move
+// through K together, one K-chunk at a time:
+//  * One persistent launch, one 1024-thread work-group per CU: work-group b
+//    takes the whole 16-row tiles [bT/NB, (b+1)T/NB); it walks them in
+//    batches of sixteen (one tile per wave), so the per-CU weight bytes
+//    differ by at most one tile.
+//  * Per batch the K-steps are cut into chunks; chunk c+1's digits are split
+//    from x into one half of a double-buffered LDS area while the waves
+//    multiply chunk c out of the other half (one barrier per chunk).  When
+//    one chunk covers K, the digits are staged once per token group.
+//  * Each wave keeps two K-steps of weights in flight in a register ring that
+//    runs on across chunk barriers and into its next batch's tile.
+//  * The epilogue needs no LDS: the owner lane of each (4 rows, token) pulls
+//    the token's six digit columns from the accumulator lanes with cross-lane
+//    shuffles and recombines them exactly.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "q4moe_device.h"
+#include "q4moe_launch.h"
+
+namespace q4 {
+
+namespace {
+
+constexpr int kBatWaves = 16;
+constexpr int kBatThreads = kBatWaves * 64;
+constexpr int kBatBuf = 72 * 1024;        // one of two digit buffers
+
+__host__ __device__ constexpr int bat_block_stride(int C) { return C * 16 + 16; }  // one padded (step, parity, g) block
+
+// K-steps per chunk for C columns and S (even) steps: chunks of equal even length.
+__host__ __device__ inline int bat_chunk_steps(int C, int S) {
+  int mx = kBatBuf / (8 * bat_block_stride(C));
+  mx -= mx & 1;
+  if (mx < 2) mx = 2;
+  const int n = (S + mx - 1) / mx;
+  int spc = (S + n - 1) / n;
+  spc += spc & 1;
+  return spc;
+}
+
+}  // namespace
+
+template <int NT, bool VEC>
+__global__ __launch_bounds__(kBatThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void batch_kernel(const GateUpParams a) {
+  constexpr int G = (16 * NT) / 6;
+  __shared__ __attribute__((aligned(16))) uint8_t s_b[2][kBatBuf];
+  __shared__ int s_pairs[G];
+  __shared__ int s_xmax[G];
+  __shared__ int s_count;
+  __shared__ int s_invalid;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g4 = lane >> 4, cc = lane & 15;
+  const int H = a.H, I = a.I;
+  const int P = a.M * a.K;
+  const bool grouped = a.ids != nullptr;
+  const int S = a.steps;                     // K-steps per tile, even
+  const int tps = (I + 15) / 16;
+  const int T = a.num_slots * tps;
+  const int NB = gridDim.x;
+  const int v0 = (int)((int64_t)blockIdx.x * T / NB), v1 = (int)((int64_t)(blockIdx.x + 1) * T / NB);
+  const uint32_t wbytes = (uint32_t)((uint64_t)I * (uint32_t)(H / 2));
+
+  // ---- invalid routing ids (grouped): zero-filled by work-group 0 ----
+  if (grouped && blockIdx.x == 0) {
+    if (tid == 0) s_invalid = 0;
+    __syncthreads();
+    int cnt = 0;
+    for (int p = tid; p < P; p += kBatThreads) {
+      const int e = a.ids[p];
+      if (e < 0 || e >= a.num_slots) {
+        ++cnt;
+        for (int r = 0; r < I; ++r) {
+          const uint64_t o = (uint64_t)p * I + r;
+          a.out[o] = 0;
+          if (a.gate_probe) a.gate_probe[o] = 0.0f;
+          if (a.up_probe) a.up_probe[o] = 0.0f;
+        }
+      }
+    }
+    if (cnt) atomicAdd(&s_invalid, cnt);
+    __syncthreads();
+    if (tid == 0 && a.invalid_count) *a.invalid_count = s_invalid;
+  }
+
+  int v = v0;
+  while (v < v1) {
+    const int e = v / tps;
+    const int t0 = v - e * tps;
+    const int t1 = min(v1, (e + 1) * tps) - e * tps;
+    v = e * tps + t1;
+    const uint8_t* slot = a.slots + (uint64_t)e * a.slot_stride;
+    const __amdgpu_buffer_rsrc_t gsrc = make_rsrc(slot + a.gate_w_off, wbytes);
+    const __amdgpu_buffer_rsrc_t usrc = make_rsrc(slot + a.up_w_off, wbytes);
+    const float* gscale = (const float*)(slot + a.gate_s_off);
+    const float* uscale = (const float*)(slot + a.up_s_off);
+
+    int next_pair = 0;
+    for (;;) {
+      __syncthreads();  // previous group done with s_b and s_pairs
+      if (!grouped) {
+        if (tid < G) s_pairs[tid] = next_pair + tid;
+        if (tid == 0) s_count = min(G, P - next_pair);
+      } else if (wave == 0) {
+        int found = 0;
+        int p = next_pair;
+        while (found < G && p < P) {
+          const int q = p + lane;
+          const bool m = q < P && a.ids[q] == e;
+          const uint64_t bal = __ballot(m);
+          const int before = __popcll(bal & ((1ull << lane) - 1ull));
+          if (m && found + before < G) s_pairs[found + before] = q;
+          found += __popcll(bal);
+          p += 64;
+        }
+        if (lane == 0) s_count = min(found, G);
+      }
+      if (tid < G) s_xmax[tid] = 0;
+      __syncthreads();
+      const int count = s_count;
+      if (count <= 0) break;
+      next_pair = grouped ? s_pairs[count - 1] + 1 : next_pair + count;
+      const int C = 6 * count;
+      const int ntiles = (C + 15) >> 4;
+      const int bs = bat_block_stride(C);
+      const int spc = bat_chunk_steps(C, S);
+      const int nch = (S + spc - 1) / spc;
+      const int nbatch = (t1 - t0 + kBatWaves - 1) / kBatWaves;
+
+      // ---- weights of this wave's first tile go out first ----
+      int lt = t0 + wave;                              // load cursor: tile, step
+      int ls = 0;
+      int left = 0;                                    // K-steps this wave still has to load
+      for (int t = lt; t < t1; t += kBatWaves) left += S;
+      auto row_off = [&](int tile) {
+        const int row = tile * 16 + cc;
+        return (uint32_t)(row < I ? row : I - 1) * (uint32_t)(H / 2) + (uint32_t)(g4 * 16);
+      };
+      uint32_t loff = row_off(lt);
+      auto issue = [&](v4u& g, v4u& u_) {
+        if (left > 0) {
+          const uint32_t o = loff + (uint32_t)ls * 64u;
+          g = load16<VEC>(gsrc, o);
+          u_ = load16<VEC>(usrc, o);
+          --left;
+          if (++ls == S) {
+            ls = 0;
+            lt += kBatWaves;
+            loff = row_off(lt);
+          }
+        }
+      };
+      v4u rg0, ru0, rg1, ru1;
+      issue(rg0, ru0);
+      issue(rg1, ru1);
+
+      // ---- largest |x| of each token ----
+      for (int ti = 0; ti < count; ++ti) {
+        const uint4* xr = (const uint4*)(a.x + (uint64_t)(s_pairs[ti] / a.K) * H);
+        uint32_t mx = 0;
+        for (int w8 = tid; w8 < H / 8; w8 += kBatThreads) mx = max(mx, max_mag8(xr[w8]));
+        if (mx) atomicMax(&s_xmax[ti], (int)mx);
+      }
+      __syncthreads();
+
+      auto stage = [&](int c, uint8_t* buf) {
+        const int k0c = c * spc * 128;
+        const int n8 = min(spc, S - c * spc) * 16;
+        for (int u = tid; u < count * n8; u += kBatThreads) {
+          const int ti = u % count;
+          const int w8 = u / count;
+          const int k0 = k0c + 8 * w8;
+          uint4 xv = make_uint4(0, 0, 0, 0);
+          if (k0 < H) xv = *(const uint4*)(a.x + (uint64_t)(s_pairs[ti] / a.K) * H + k0);
+          uint32_t lo[8], hi[8];
+          x8_digits(xv, max((s_xmax[ti] >> 7) & 0xFF, 1), lo, hi);
+          const int tl = w8 >> 4, gg = (w8 >> 2) & 3, i = w8 & 3;
+#pragma unroll
+          for (int par = 0; par < 2; ++par) {
+            uint32_t d[6];
+            digit_words(lo, hi, par, d);
+            uint8_t* base = buf + ((tl * 2 + par) * 4 + gg) * bs + ti * 96 + 4 * i;
+#pragma unroll
+            for (int s = 0; s < 6; ++s) *(uint32_t*)(base + s * 16) = d[s];
+          }
+        }
+      };
+
+      // B fragment base of this lane in each column tile (columns past C repeat the last)
+      int coff[NT];
+#pragma unroll
+      for (int n = 0; n < NT; ++n) coff[n] = g4 * bs + min(16 * n + cc, C - 1) * 16;
+
+      stage(0, s_b[0]);
+      __syncthreads();
+      int gch = 0;                                     // chunks done in this group (buffer parity)
+      for (int bb = 0; bb < nbatch; ++bb) {
+        const int tile = t0 + bb * kBatWaves + wave;
+        const bool active = tile < t1;
+        v4i accg[NT], accu[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          accg[n] = v4i{0, 0, 0, 0};
+          accu[n] = v4i{0, 0, 0, 0};
+        }
+        for (int c = 0; c < nch; ++c, ++gch) {
+          const uint8_t* buf = s_b[nch == 1 ? 0 : (gch & 1)];
+          const bool more = (c + 1 < nch) || (bb + 1 < nbatch);
+          if (nch > 1 && more) stage((c + 1) % nch, s_b[(gch + 1) & 1]);
+          if (active) {
+            const int sa = c * spc, se = min(S, sa + spc);
+            auto compute = [&](const v4u& g, const v4u& u_, int s) {
+              v4i ge, go, ue, uo;
+              split_weights(g, ge, go);
+              split_weights(u_, ue, uo);
+              const uint8_t* bp = buf + (s - sa) * 8 * bs;
+#pragma unroll
+              for (int n = 0; n < NT; ++n) {
+                if (n < ntiles) {
+                  const v4i be = *(const v4i*)(bp + coff[n]);
+                  const v4i bo = *(const v4i*)(bp + 4 * bs + coff[n]);
+                  accg[n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ge, be, accg[n], 0, 0, 0);
+                  accu[n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ue, be, accu[n], 0, 0, 0);
+                  accg[n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(go, bo, accg[n], 0, 0, 0);
+                  accu[n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(uo, bo, accu[n], 0, 0, 0);
+                }
+              }
+            };
+            for (int s = sa; s < se; s += 2) {
+              compute(rg0, ru0, s);
+              issue(rg0, ru0);
+              compute(rg1, ru1, s + 1);
+              issue(rg1, ru1);
+            }
+          }
+          __syncthreads();
+        }
+
+        // ---- epilogue: owner lane (g4, token cc) gathers its six columns ----
+        if (active) {
+          int64_t glo[4] = {0, 0, 0, 0}, ghi[4] = {0, 0, 0, 0}, ulo[4] = {0, 0, 0, 0}, uhi[4] = {0, 0, 0, 0};
+#pragma unroll
+          for (int s = 0; s < 6; ++s) {
+            const int colx = 6 * cc + s;             // meaningful on owner lanes (cc < count)
+            const int ns = colx >> 4;
+            const int src = g4 * 16 + (colx & 15);
+            const int sh = 8 * (s % 3);
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int vg = __shfl(accg[n][i], src);
+                const int vu = __shfl(accu[n][i], src);
+                if (n == ns) {
+                  if (s < 3) {
+                    glo[i] += (int64_t)vg << sh;
+                    ulo[i] += (int64_t)vu << sh;
+                  } else {
+                    ghi[i] += (int64_t)vg << sh;
+                    uhi[i] += (int64_t)vu << sh;
+                  }
+                }
+              }
+            }
+          }
+          if (cc < count) {
+            const int p = s_pairs[cc];
+            const int xm = s_xmax[cc];
+            const int e2 = sum_exponent(xm);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int row = tile * 16 + 4 * g4 + i;
+              if (row < I) {
+                float gate = round_scaled(ghi[i], glo[i], e2, gscale[row]);
+                float up = round_scaled(uhi[i], ulo[i], e2, uscale[row]);
+                if (xm >= 0x7F80) {
+                  gate = __builtin_nanf("");
+                  up = __builtin_nanf("");
+                }
+                const uint64_t o = (uint64_t)p * I + row;
+                a.out[o] = swiglu_tail(gate, up);
+                if (a.gate_probe) a.gate_probe[o] = gate;
+                if (a.up_probe) a.up_probe[o] = up;
+              }
+            }
+          }
+        }
+      }
+      if (count < G) break;
+      if (!grouped && next_pair >= P) break;
+    }
+  }
+}
+
+// ---- host side ----
+
+namespace {
+
+template <int NT, bool VEC>
+int batch_blocks(int device) {
+  static int cached[64] = {0};
+  if (device < 0 || device >= 64) device = 0;
+  if (!cached[device]) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0)
+      cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(&batch_kernel<NT, VEC>), kBatThreads, 0) != hipSuccess ||
+        per_cu <= 0)
+      per_cu = 1;
+    cached[device] = cus * per_cu;
+  }
+  return cached[device];
+}
+
+template <int NT, bool VEC>
+hipError_t launch_batch_t(GateUpParams& p, hipStream_t stream) {
+  int device = 0;
+  if (hipGetDevice(&device) != hipSuccess) device = 0;
+  const int tiles = p.num_slots * ((p.I + 15) / 16);
+  int nb = batch_blocks<NT, VEC>(device);
+  if (nb > tiles) nb = tiles;
+  void* args[] = {&p};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&batch_kernel<NT, VEC>), dim3((unsigned)nb),
+                         dim3(kBatThreads), args, 0, stream);
+}
+
+}  // namespace
+
+hipError_t launch_batch(GateUpParams p, int tokens_per_slot, hipStream_t stream) {
+  p.steps = (p.H + 127) / 128;
+  p.steps += p.steps & 1;
+  const int nt = tokens_per_slot <= 2 ? 1 : (tokens_per_slot <= 5 ? 2 : 3);
+  p.G = (16 * nt) / 6;
+  const bool vec = (p.H % 32) == 0;
+  if (nt == 1) return vec ? launch_batch_t<1, true>(p, stream) : launch_batch_t<1, false>(p, stream);
+  if (nt == 2) return vec ? launch_batch_t<2, true>(p, stream) : launch_batch_t<2, false>(p, stream);
+  return vec ? launch_batch_t<3, true>(p, stream) : launch_batch_t<3, false>(p, stream);
+}
+
+}  // namespace q4

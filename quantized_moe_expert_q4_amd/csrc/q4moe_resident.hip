@@ -39,7 +39,7 @@ __host__ __device__ constexpr int block_stride(int C) { return C * 16 + 16; }  /
 }  // namespace
 
 template <int D, bool VEC>
-__global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void resident_kernel(const ResidentParams a) {
+__global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void resident_kernel(const GateUpParams a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_b[kResBBytes];
   __shared__ int32_t s_acc[kResWaves][2][16 * kResMaxCols];   // per-wave digit matrix of a tile
   __shared__ unsigned long long s_fix[kResWaves][kResItems * 4];
@@ -319,7 +319,7 @@ bool resident_fits(int M_per_slot, int H) {
          (size_t)block_stride(6 * M_per_slot) * 8 * steps <= (size_t)kResBBytes;
 }
 
-hipError_t launch_resident(ResidentParams p, hipStream_t stream) {
+hipError_t launch_resident(GateUpParams p, hipStream_t stream) {
   p.steps = ((p.H + 127) / 128 + kResD - 1) / kResD * kResD;
   const int tokens = 2;
   p.G = (size_t)block_stride(6 * tokens) * 8 * p.steps <= (size_t)kResBBytes ? 2 : 1;
@@ -333,6 +333,10 @@ hipError_t launch_resident(ResidentParams p, hipStream_t stream) {
   const void* fn = vec ? reinterpret_cast<const void*>(&resident_kernel<kResD, true>)
                        : reinterpret_cast<const void*>(&resident_kernel<kResD, false>);
   return hipLaunchKernel(fn, dim3((unsigned)nb), dim3(kResThreads), args, 0, stream);
+}
+
+hipError_t launch_gate_up(const GateUpParams& p, int tokens_per_slot, hipStream_t stream) {
+  return resident_fits(tokens_per_slot, p.H) ? launch_resident(p, stream) : launch_batch(p, tokens_per_slot, stream);
 }
 
 }  // namespace q4

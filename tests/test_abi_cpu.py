@@ -34,8 +34,6 @@ def test_workspace_size_is_aligned_and_positive():
     for M, K, H, I, E in ((1, 1, 8, 1, 1), (32, 8, 6144, 2048, 64), (4096, 16, 7168, 4096, 65535)):
         b = q4.grouped_workspace_bytes(M, K, H, I, E)
         assert b >= 256 and b % 256 == 0
-    # grows with the activations it holds (six digit bytes per position per token)
-    assert q4.grouped_workspace_bytes(8, 1, 8192, 64, 1) > q4.grouped_workspace_bytes(8, 1, 4096, 64, 1)
     assert q4.grouped_workspace_bytes(0, 1, 4096, 64, 1) == 0
     assert q4.grouped_workspace_bytes(1, 1, 4096, 64, 0) == 0
 
