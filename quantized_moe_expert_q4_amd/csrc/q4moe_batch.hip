@@ -16,9 +16,9 @@
 //    one chunk covers K, the digits are staged once per token group.
 //  * Each wave keeps two K-steps of weights in flight in a register ring that
 //    runs on across chunk barriers and into its next batch's tile.
-//  * The epilogue needs no LDS: the owner lane of each (4 rows, token) pulls
-//    the token's six digit columns from the accumulator lanes with cross-lane
-//    shuffles and recombines them exactly.
+//  * Each wave's 16 x C digit matrix goes through the LDS buffer left idle
+//    after the batch's last chunk, and its lanes recombine (row, token) sums
+//    exactly.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -32,12 +32,18 @@ namespace {
 constexpr int kBatWaves = 16;
 constexpr int kBatThreads = kBatWaves * 64;
 constexpr int kBatBuf = 72 * 1024;        // one of two digit buffers
+constexpr int kEpStride = 52;             // int32 row stride of a wave's 16 x C epilogue matrix
 
-__host__ __device__ constexpr int bat_block_stride(int C) { return C * 16 + 16; }  // one padded (step, parity, g) block
+static_assert(kBatWaves * 16 * kEpStride * 4 <= kBatBuf, "epilogue matrices fit one digit buffer");
 
-// K-steps per chunk for C columns and S (even) steps: chunks of equal even length.
-__host__ __device__ inline int bat_chunk_steps(int C, int S) {
-  int mx = kBatBuf / (8 * bat_block_stride(C));
+// Digits of one K-step: [parity 2][column tile n][lane 64][16 bytes], lane =
+// 16*k-group + column in tile: every B fragment is one lane-linear 1 KiB read.
+__host__ __device__ constexpr int bat_step_bytes(int ntiles) { return 2 * ntiles * 1024; }
+
+// K-steps per chunk for `ntiles` column tiles and S (even) steps: chunks of
+// equal even length.
+__host__ __device__ inline int bat_chunk_steps(int ntiles, int S) {
+  int mx = kBatBuf / bat_step_bytes(ntiles);
   mx -= mx & 1;
   if (mx < 2) mx = 2;
   const int n = (S + mx - 1) / mx;
@@ -133,8 +139,8 @@ void batch_kernel(const GateUpParams a) {
       next_pair = grouped ? s_pairs[count - 1] + 1 : next_pair + count;
       const int C = 6 * count;
       const int ntiles = (C + 15) >> 4;
-      const int bs = bat_block_stride(C);
-      const int spc = bat_chunk_steps(C, S);
+      const int sb = bat_step_bytes(ntiles);
+      const int spc = bat_chunk_steps(ntiles, S);
       const int nch = (S + spc - 1) / spc;
       const int nbatch = (t1 - t0 + kBatWaves - 1) / kBatWaves;
 
@@ -190,17 +196,17 @@ void batch_kernel(const GateUpParams a) {
           for (int par = 0; par < 2; ++par) {
             uint32_t d[6];
             digit_words(lo, hi, par, d);
-            uint8_t* base = buf + ((tl * 2 + par) * 4 + gg) * bs + ti * 96 + 4 * i;
+            uint8_t* base = buf + tl * sb + par * ntiles * 1024 + gg * 256 + 4 * i;
 #pragma unroll
-            for (int s = 0; s < 6; ++s) *(uint32_t*)(base + s * 16) = d[s];
+            for (int s = 0; s < 6; ++s) {
+              const int col = ti * 6 + s;
+              *(uint32_t*)(base + (col >> 4) * 1024 + (col & 15) * 16) = d[s];
+            }
           }
         }
       };
 
-      // B fragment base of this lane in each column tile (columns past C repeat the last)
-      int coff[NT];
-#pragma unroll
-      for (int n = 0; n < NT; ++n) coff[n] = g4 * bs + min(16 * n + cc, C - 1) * 16;
+      // columns past C in the last tile hold stale bytes; their results are never read
 
       stage(0, s_b[0]);
       __syncthreads();
@@ -224,12 +230,12 @@ void batch_kernel(const GateUpParams a) {
               v4i ge, go, ue, uo;
               split_weights(g, ge, go);
               split_weights(u_, ue, uo);
-              const uint8_t* bp = buf + (s - sa) * 8 * bs;
+              const uint8_t* bp = buf + (s - sa) * sb + lane * 16;
 #pragma unroll
               for (int n = 0; n < NT; ++n) {
                 if (n < ntiles) {
-                  const v4i be = *(const v4i*)(bp + coff[n]);
-                  const v4i bo = *(const v4i*)(bp + 4 * bs + coff[n]);
+                  const v4i be = *(const v4i*)(bp + n * 1024);
+                  const v4i bo = *(const v4i*)(bp + (ntiles + n) * 1024);
                   accg[n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ge, be, accg[n], 0, 0, 0);
                   accu[n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ue, be, accu[n], 0, 0, 0);
                   accg[n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(go, bo, accg[n], 0, 0, 0);
@@ -247,54 +253,52 @@ void batch_kernel(const GateUpParams a) {
           __syncthreads();
         }
 
-        // ---- epilogue: owner lane (g4, token cc) gathers its six columns ----
-        if (active) {
-          int64_t glo[4] = {0, 0, 0, 0}, ghi[4] = {0, 0, 0, 0}, ulo[4] = {0, 0, 0, 0}, uhi[4] = {0, 0, 0, 0};
+        // ---- epilogue: digit matrix through the free LDS buffer ----
+        // After the batch's last chunk barrier one buffer is idle: the single
+        // buffer's twin when one chunk covers K, else the last chunk's buffer
+        // (the other one already holds the next batch's first chunk).
+        {
+          int32_t* ep = (int32_t*)s_b[nch == 1 ? 1 : ((gch - 1) & 1)] + wave * (16 * kEpStride);
+          if (active) {
+            // gate first, then up, through the same 16 x C matrix
+            float gv[2];
 #pragma unroll
-          for (int s = 0; s < 6; ++s) {
-            const int colx = 6 * cc + s;             // meaningful on owner lanes (cc < count)
-            const int ns = colx >> 4;
-            const int src = g4 * 16 + (colx & 15);
-            const int sh = 8 * (s % 3);
+            for (int part = 0; part < 2; ++part) {
 #pragma unroll
-            for (int n = 0; n < NT; ++n) {
+              for (int n = 0; n < NT; ++n) {
+                const int col = 16 * n + cc;
+                if (n < ntiles && col < C) {
 #pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int vg = __shfl(accg[n][i], src);
-                const int vu = __shfl(accu[n][i], src);
-                if (n == ns) {
-                  if (s < 3) {
-                    glo[i] += (int64_t)vg << sh;
-                    ulo[i] += (int64_t)vu << sh;
+                  for (int i = 0; i < 4; ++i) ep[(4 * g4 + i) * kEpStride + col] = part ? accu[n][i] : accg[n][i];
+                }
+              }
+              wave_sync();
+#pragma unroll
+              for (int j = 0; j < 2; ++j) {
+                const int item = lane + 64 * j;
+                const int rr = item & 15, ti = item >> 4;
+                const int row = tile * 16 + rr;
+                if (ti < count && row < I) {
+                  const int32_t* d = ep + rr * kEpStride + ti * 6;
+                  const int64_t lo = (int64_t)d[0] + ((int64_t)d[1] << 8) + ((int64_t)d[2] << 16);
+                  const int64_t hi = (int64_t)d[3] + ((int64_t)d[4] << 8) + ((int64_t)d[5] << 16);
+                  const int xm = s_xmax[ti];
+                  float r = round_scaled(hi, lo, sum_exponent(xm), part ? uscale[row] : gscale[row]);
+                  if (xm >= 0x7F80) r = __builtin_nanf("");
+                  if (!part) {
+                    gv[j] = r;
                   } else {
-                    ghi[i] += (int64_t)vg << sh;
-                    uhi[i] += (int64_t)vu << sh;
+                    const uint64_t o = (uint64_t)s_pairs[ti] * I + row;
+                    a.out[o] = swiglu_tail(gv[j], r);
+                    if (a.gate_probe) a.gate_probe[o] = gv[j];
+                    if (a.up_probe) a.up_probe[o] = r;
                   }
                 }
               }
+              wave_sync();
             }
           }
-          if (cc < count) {
-            const int p = s_pairs[cc];
-            const int xm = s_xmax[cc];
-            const int e2 = sum_exponent(xm);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int row = tile * 16 + 4 * g4 + i;
-              if (row < I) {
-                float gate = round_scaled(ghi[i], glo[i], e2, gscale[row]);
-                float up = round_scaled(uhi[i], ulo[i], e2, uscale[row]);
-                if (xm >= 0x7F80) {
-                  gate = __builtin_nanf("");
-                  up = __builtin_nanf("");
-                }
-                const uint64_t o = (uint64_t)p * I + row;
-                a.out[o] = swiglu_tail(gate, up);
-                if (a.gate_probe) a.gate_probe[o] = gate;
-                if (a.up_probe) a.up_probe[o] = up;
-              }
-            }
-          }
+          __syncthreads();  // the epilogue buffer is staged into by the next batch
         }
       }
       if (count < G) break;

@@ -94,6 +94,15 @@ __device__ uint16_t swiglu_tail(float gate, float up) {
   return bf16_rne(siluT * uT);
 }
 
+// Orders one wave's LDS stores before its later LDS loads from other lanes
+// (and those loads before later stores): a wave barrier between release and
+// acquire fences, so the compiler keeps every LDS access on its side.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }

@@ -220,7 +220,7 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(4, 
             eu[(4 * g4 + i) * C + cc] = accu[i];
           }
         }
-        __builtin_amdgcn_wave_barrier();
+        wave_sync();
         const int rr = lane & 15, ti = lane >> 4;            // item = (row rr, token ti), ti < 2
         int64_t sm[4] = {0, 0, 0, 0};
         if (ti < count) {
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(4, 
           sm[2] = (int64_t)ud[0] + ((int64_t)ud[1] << 8) + ((int64_t)ud[2] << 16);
           sm[3] = (int64_t)ud[3] + ((int64_t)ud[4] << 8) + ((int64_t)ud[5] << 16);
         }
-        __builtin_amdgcn_wave_barrier();
+        wave_sync();
 
         bool finish = (sa == 0 && se == S);
         if (!finish) {
