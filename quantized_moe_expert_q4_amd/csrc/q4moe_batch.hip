@@ -66,7 +66,7 @@ void batch_kernel(const GateUpParams a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, cc = lane & 15;
   const int H = a.H, I = a.I;
   const int P = a.M * a.K;
@@ -154,18 +154,20 @@ void batch_kernel(const GateUpParams a) {
         return (uint32_t)(row < I ? row : I - 1) * (uint32_t)(H / 2) + (uint32_t)(g4 * 16);
       };
       uint32_t loff = row_off(lt);
+      // always two loads per call (kOffNone once the wave's tiles are all
+      // issued), so that the compiler's wait counts stay exact
       auto issue = [&](v4u& g, v4u& u_) {
-        if (left > 0) {
-          const uint32_t o = loff + (uint32_t)ls * 64u;
-          g = load16<VEC>(gsrc, o);
-          u_ = load16<VEC>(usrc, o);
-          --left;
-          if (++ls == S) {
-            ls = 0;
-            lt += kBatWaves;
-            loff = row_off(lt);
-          }
-        }
+        const bool live = left > 0;
+        const uint32_t o = live ? loff + (uint32_t)ls * 64u : kOffNone;
+        g = load16<VEC>(gsrc, o);
+        u_ = load16<VEC>(usrc, o);
+        // cursor step without branches, so the loads stay unconditional
+        left -= live ? 1 : 0;
+        const int nls = ls + (live ? 1 : 0);
+        const bool wrap = nls == S;
+        ls = wrap ? 0 : nls;
+        lt += wrap ? kBatWaves : 0;
+        loff = wrap ? row_off(lt) : loff;
       };
       v4u rg0, ru0, rg1, ru1;
       issue(rg0, ru0);

@@ -107,6 +107,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// A buffer offset past every weight array (projections are below 2^31 bytes):
+// such a load returns zeros without a memory access.  Loads that are issued
+// only to keep the number of outstanding loads fixed use it, so that the
+// compiler's wait counts stay exact.
+constexpr uint32_t kOffNone = 0x80000000u;
+
 template <bool VEC>
 __device__ __forceinline__ v4u load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   if constexpr (VEC) {
