@@ -68,7 +68,22 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(4, 
   const int tps = (I + 15) / 16;             // tiles per slot
   const int T = a.num_slots * tps;
   const int NB = gridDim.x;
-  const int v0 = (int)((int64_t)blockIdx.x * T / NB), v1 = (int)((int64_t)(blockIdx.x + 1) * T / NB);
+  // Tile range of this work-group.  With two work-groups per CU (pair_share
+  // > 0) the grid is split into CU pairs (b, b + NB/2): the one dispatched
+  // first wins the CU's memory-issue arbitration more often, so it takes
+  // pair_share/1024 of the pair's tiles and both finish together.
+  int v0, v1;
+  if (a.pair_share > 0) {
+    const int P2 = NB / 2;
+    const int pair = (int)blockIdx.x % P2;
+    const int pa = (int)((int64_t)pair * T / P2), pb = (int)((int64_t)(pair + 1) * T / P2);
+    const int mid = pa + (int)(((int64_t)(pb - pa) * a.pair_share + 512) / 1024);
+    v0 = (int)blockIdx.x < P2 ? pa : mid;
+    v1 = (int)blockIdx.x < P2 ? mid : pb;
+  } else {
+    v0 = (int)((int64_t)blockIdx.x * T / NB);
+    v1 = (int)((int64_t)(blockIdx.x + 1) * T / NB);
+  }
   const uint32_t wbytes = (uint32_t)((uint64_t)I * (uint32_t)(H / 2));
   const uint64_t below = (1ull << lane) - 1ull;
 
@@ -376,9 +391,10 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(4, 
 
 namespace {
 
+// Work-groups that fit the device at once, and how many share a CU.
 template <int D, bool VEC>
-int resident_blocks(int device) {
-  static int cached[64] = {0};
+int resident_blocks(int device, int* per_cu_out) {
+  static int cached[64] = {0}, cached_per_cu[64] = {0};
   if (device < 0 || device >= 64) device = 0;
   if (!cached[device]) {
     int cus = 0, per_cu = 0;
@@ -388,10 +404,17 @@ int resident_blocks(int device) {
             &per_cu, reinterpret_cast<const void*>(&resident_kernel<D, VEC>), kResThreads, 0) != hipSuccess ||
         per_cu <= 0)
       per_cu = 1;
+    cached_per_cu[device] = per_cu;
     cached[device] = cus * per_cu;
   }
+  *per_cu_out = cached_per_cu[device];
   return cached[device];
 }
+
+// Share of a CU pair's tiles for the first-dispatched work-group, in 1/1024
+// (measured on MI355X: with equal shares the first-dispatched work-groups
+// finish at about 0.86 of the time of the second ones).
+constexpr int kPairShare = 650;
 
 constexpr int kResD = 2;
 
@@ -410,7 +433,11 @@ hipError_t launch_resident(GateUpParams p, hipStream_t stream) {
   if (hipGetDevice(&device) != hipSuccess) device = 0;
   const bool vec = (p.H % 32) == 0;
   const int tiles = p.num_slots * ((p.I + 15) / 16);
-  int nb = vec ? resident_blocks<kResD, true>(device) : resident_blocks<kResD, false>(device);
+  int per_cu = 1;
+  int nb = vec ? resident_blocks<kResD, true>(device, &per_cu) : resident_blocks<kResD, false>(device, &per_cu);
+  // uneven CU-pair shares only for a full grid of two work-groups per CU,
+  // each with several tiles
+  p.pair_share = (per_cu == 2 && tiles >= 8 * nb) ? kPairShare : 0;
   if (nb > tiles) nb = tiles;
   void* args[] = {&p};
   const void* fn = vec ? reinterpret_cast<const void*>(&resident_kernel<kResD, true>)

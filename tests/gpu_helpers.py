@@ -36,18 +36,23 @@ def run_single(slot_np, layout, xbits, H, I, probes=True):
     return res
 
 
-def run_grouped(slots_np, layout, xbits, ids, H, I, probes=True, ws_fill=None):
+def run_grouped(slots_np, layout, xbits, ids, H, I, probes=True, ws_fill=None, ws=None, slots=None):
+    """One grouped call.  `ws` reuses a workspace (left as the last call left
+    it); otherwise a new one filled with `ws_fill` (default 0xAB).  `slots`
+    passes slots already on the device (then `slots_np` gives only the shape)."""
     M, K = ids.shape
     E = slots_np.shape[0]
-    slots = upload_slots(slots_np)
+    if slots is None:
+        slots = upload_slots(slots_np)
     x = upload_bf16_bits(xbits)
     idt = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda()
     out = torch.empty((M, K, I), dtype=torch.bfloat16, device="cuda")
     g = torch.empty((M, K, I), dtype=torch.float32, device="cuda") if probes else None
     u = torch.empty((M, K, I), dtype=torch.float32, device="cuda") if probes else None
     wsb = q4.grouped_workspace_bytes(M, K, H, I, E)
-    ws = aligned_empty(wsb, 256)
-    ws.fill_(0xAB if ws_fill is None else ws_fill)
+    if ws is None:
+        ws = aligned_empty(wsb, 256)
+        ws.fill_(0xAB if ws_fill is None else ws_fill)
     q4.expert_gate_up_grouped(slots, slots_np.shape[1], E, layout, x, M, idt, K, H, I, out, ws, wsb, g, u)
     torch.cuda.synchronize()
     invalid = int(ws[:4].cpu().numpy().view(np.int32)[0])
