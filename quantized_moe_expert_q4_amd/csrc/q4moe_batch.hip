@@ -61,7 +61,7 @@ void batch_kernel(const GateUpParams a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_b[2][kBatBuf];
   __shared__ int s_pairs[G];
   __shared__ int s_xmax[G];
-  __shared__ int s_count;
+  __shared__ int s_wcnt[kBatWaves];
   __shared__ int s_invalid;
 
   const int tid = threadIdx.x;
@@ -113,30 +113,49 @@ void batch_kernel(const GateUpParams a) {
     const float* uscale = (const float*)(slot + a.up_s_off);
 
     int next_pair = 0;
+    int idv = -1;                                      // ids of the scan window at next_pair
+    if (grouped && tid < P) idv = a.ids[tid];
     for (;;) {
       __syncthreads();  // previous group done with s_b and s_pairs
-      if (!grouped) {
-        if (tid < G) s_pairs[tid] = next_pair + tid;
-        if (tid == 0) s_count = min(G, P - next_pair);
-      } else if (wave == 0) {
-        int found = 0;
-        int p = next_pair;
-        while (found < G && p < P) {
-          const int q = p + lane;
-          const bool m = q < P && a.ids[q] == e;
-          const uint64_t bal = __ballot(m);
-          const int before = __popcll(bal & ((1ull << lane) - 1ull));
-          if (m && found + before < G) s_pairs[found + before] = q;
-          found += __popcll(bal);
-          p += 64;
-        }
-        if (lane == 0) s_count = min(found, G);
-      }
       if (tid < G) s_xmax[tid] = 0;
-      __syncthreads();
-      const int count = s_count;
+      // ---- next group of up to G pairs routed to slot e ----
+      int count, more;
+      if (!grouped) {
+        count = min(G, P - next_pair);
+        more = next_pair + count < P;
+        if (tid < count) s_pairs[tid] = next_pair + tid;
+        __syncthreads();
+      } else {
+        // block-wide scan of ids[next_pair..P) in windows of kBatThreads;
+        // stops once a further match proves there is another group
+        int found = 0;
+        int base = next_pair;
+        more = 0;
+        for (;;) {
+          const bool m = idv == e;
+          const uint64_t bal = __ballot(m);
+          if (lane == 0) s_wcnt[wave] = __popcll(bal);
+          __syncthreads();
+          int before = found;
+#pragma unroll 1
+          for (int w = 0; w < wave; ++w) before += s_wcnt[w];
+          int total = before;
+#pragma unroll 1
+          for (int w = wave; w < kBatWaves; ++w) total += s_wcnt[w];
+          before += __popcll(bal & ((1ull << lane) - 1ull));
+          if (m && before < G) s_pairs[before] = base + tid;
+          found = total;
+          base += kBatThreads;
+          if (found > G) more = 1;
+          __syncthreads();  // s_wcnt reused; s_pairs visible
+          if (more || base >= P) break;
+          idv = (base + tid < P) ? a.ids[base + tid] : -1;
+        }
+        count = min(found, G);
+      }
       if (count <= 0) break;
-      next_pair = grouped ? s_pairs[count - 1] + 1 : next_pair + count;
+      next_pair = s_pairs[count - 1] + 1;
+      if (grouped && more) idv = (next_pair + tid < P) ? a.ids[next_pair + tid] : -1;
       const int C = 6 * count;
       const int ntiles = (C + 15) >> 4;
       const int sb = bat_step_bytes(ntiles);
@@ -144,7 +163,9 @@ void batch_kernel(const GateUpParams a) {
       const int nch = (S + spc - 1) / spc;
       const int nbatch = (t1 - t0 + kBatWaves - 1) / kBatWaves;
 
-      // ---- weights of this wave's first tile go out first ----
+      const int nxu = count * (H / 8);                 // 16-byte units of x, token-major
+
+      // ---- load cursor over this wave's tiles ----
       int lt = t0 + wave;                              // load cursor: tile, step
       int ls = 0;
       int left = 0;                                    // K-steps this wave still has to load
@@ -169,19 +190,43 @@ void batch_kernel(const GateUpParams a) {
         lt += wrap ? kBatWaves : 0;
         loff = wrap ? row_off(lt) : loff;
       };
-      v4u rg0, ru0, rg1, ru1;
-      issue(rg0, ru0);
-      issue(rg1, ru1);
-
-      // ---- largest |x| of each token ----
-      for (int ti = 0; ti < count; ++ti) {
-        const uint4* xr = (const uint4*)(a.x + (uint64_t)(s_pairs[ti] / a.K) * H);
+      // ---- largest |x| of each token (one LDS atomic per wave when its 64
+      // units belong to one token) ----
+      for (int u0 = 0; u0 < nxu; u0 += kBatThreads) {
+        const int u = u0 + tid;
+        const int ti = min(u, nxu - 1) / (H / 8);
         uint32_t mx = 0;
-        for (int w8 = tid; w8 < H / 8; w8 += kBatThreads) mx = max(mx, max_mag8(xr[w8]));
-        if (mx) atomicMax(&s_xmax[ti], (int)mx);
+        if (u < nxu) {
+          const int w8 = u - ti * (H / 8);
+          mx = max_mag8(*(const uint4*)(a.x + (uint64_t)(s_pairs[ti] / a.K) * H + 8 * w8));
+        }
+        if (__shfl(ti, 0) == __shfl(ti, 63)) {
+#pragma unroll
+          for (int off = 32; off > 0; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
+          if (lane == 0 && mx) atomicMax(&s_xmax[ti], (int)mx);
+        } else if (mx) {
+          atomicMax(&s_xmax[ti], (int)mx);
+        }
       }
       __syncthreads();
 
+      // digits of 8 consecutive K values (unit w8 of a chunk) of token ti
+      auto stage_unit = [&](uint8_t* buf, int ti, int w8, const uint4 xq) {
+        uint32_t lo[8], hi[8];
+        x8_digits(xq, max((s_xmax[ti] >> 7) & 0xFF, 1), lo, hi);
+        const int tl = w8 >> 4, gg = (w8 >> 2) & 3, i = w8 & 3;
+#pragma unroll
+        for (int par = 0; par < 2; ++par) {
+          uint32_t d[6];
+          digit_words(lo, hi, par, d);
+          uint8_t* base = buf + tl * sb + par * ntiles * 1024 + gg * 256 + 4 * i;
+#pragma unroll
+          for (int s = 0; s < 6; ++s) {
+            const int col = ti * 6 + s;
+            *(uint32_t*)(base + (col >> 4) * 1024 + (col & 15) * 16) = d[s];
+          }
+        }
+      };
       auto stage = [&](int c, uint8_t* buf) {
         const int k0c = c * spc * 128;
         const int n8 = min(spc, S - c * spc) * 16;
@@ -189,22 +234,9 @@ void batch_kernel(const GateUpParams a) {
           const int ti = u % count;
           const int w8 = u / count;
           const int k0 = k0c + 8 * w8;
-          uint4 xv = make_uint4(0, 0, 0, 0);
-          if (k0 < H) xv = *(const uint4*)(a.x + (uint64_t)(s_pairs[ti] / a.K) * H + k0);
-          uint32_t lo[8], hi[8];
-          x8_digits(xv, max((s_xmax[ti] >> 7) & 0xFF, 1), lo, hi);
-          const int tl = w8 >> 4, gg = (w8 >> 2) & 3, i = w8 & 3;
-#pragma unroll
-          for (int par = 0; par < 2; ++par) {
-            uint32_t d[6];
-            digit_words(lo, hi, par, d);
-            uint8_t* base = buf + tl * sb + par * ntiles * 1024 + gg * 256 + 4 * i;
-#pragma unroll
-            for (int s = 0; s < 6; ++s) {
-              const int col = ti * 6 + s;
-              *(uint32_t*)(base + (col >> 4) * 1024 + (col & 15) * 16) = d[s];
-            }
-          }
+          uint4 xq = make_uint4(0, 0, 0, 0);
+          if (k0 < H) xq = *(const uint4*)(a.x + (uint64_t)(s_pairs[ti] / a.K) * H + k0);
+          stage_unit(buf, ti, w8, xq);
         }
       };
 
@@ -212,6 +244,10 @@ void batch_kernel(const GateUpParams a) {
 
       stage(0, s_b[0]);
       __syncthreads();
+      // the weights of this wave's first tile go out now
+      v4u rg0, ru0, rg1, ru1;
+      issue(rg0, ru0);
+      issue(rg1, ru1);
       int gch = 0;                                     // chunks done in this group (buffer parity)
       for (int bb = 0; bb < nbatch; ++bb) {
         const int tile = t0 + bb * kBatWaves + wave;
@@ -303,8 +339,7 @@ void batch_kernel(const GateUpParams a) {
           __syncthreads();  // the epilogue buffer is staged into by the next batch
         }
       }
-      if (count < G) break;
-      if (!grouped && next_pair >= P) break;
+      if (!more) break;
     }
   }
 }
