@@ -160,15 +160,19 @@ def cpu_model() -> str:
 
 
 def load_traffic(bytes_per_launch: float):
+    """HBM bytes per launch of the timed kernel (FETCH_SIZE + WRITE_SIZE, each
+    scaled by what the counter reads for a plain copy of known size), from the
+    committed counter summary; None when the kernels changed since."""
     if not os.path.exists(TRAFFIC_FILE):
-        return None
+        return None, None
     with open(TRAFFIC_FILE) as f:
         t = json.load(f)
     if t.get("kernel_sha256") != kernel_sha():
-        return None
-    return {"fetch_bytes": t["fetch_bytes_per_launch"], "write_bytes": t["write_bytes_per_launch"],
-            "fetch_over_algorithmic": round(t["fetch_bytes_per_launch"] / bytes_per_launch, 4),
-            "source": os.path.relpath(TRAFFIC_FILE, ROOT)}
+        return None, None
+    detail = {"fetch_bytes": t["fetch_bytes_per_launch"], "write_bytes": t["write_bytes_per_launch"],
+              "fetch_over_algorithmic": round(t["fetch_bytes_per_launch"] / bytes_per_launch, 4),
+              "source": os.path.relpath(TRAFFIC_FILE, ROOT)}
+    return t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"], detail
 
 
 def main():
@@ -259,8 +263,10 @@ def main():
     # One step is one launch of the gate/up kernel; the HIP events bracket the
     # launches on their own stream, so the per-launch mean is seconds/steps.
     achieved = bytes_step / sec_per_step / 1e9
+    traffic, traffic_detail = load_traffic(bytes_step) if M == 1 else (None, None)
     out["roofline"] = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                       "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(bytes_step),
+                       "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                       "traffic_detail": traffic_detail,
                        "kernel": ("q4::resident_kernel" if M <= 2 else "q4::batch_kernel") + " (grouped call, M=%d)" % M,
                        "algorithmic_bytes_per_launch": bytes_step}
     if not args.no_cpu:
