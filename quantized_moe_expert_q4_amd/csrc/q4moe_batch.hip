@@ -63,6 +63,7 @@ void batch_kernel(const GateUpParams a) {
   __shared__ int s_xmax[G];
   __shared__ int s_wcnt[kBatWaves];
   __shared__ int s_invalid;
+  __shared__ uint16_t s_sig[kSigTable];      // bf16 sigmoid of the tabulated gT
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -77,6 +78,8 @@ void batch_kernel(const GateUpParams a) {
   const int NB = gridDim.x;
   const int v0 = (int)((int64_t)blockIdx.x * T / NB), v1 = (int)((int64_t)(blockIdx.x + 1) * T / NB);
   const uint32_t wbytes = (uint32_t)((uint64_t)I * (uint32_t)(H / 2));
+
+  for (int i = tid; i < kSigTable; i += kBatThreads) s_sig[i] = sigmoid_bf16(sig_table_bits(i));
 
   // ---- invalid routing ids (grouped): zero-filled by work-group 0 ----
   if (grouped && blockIdx.x == 0) {
@@ -327,7 +330,7 @@ void batch_kernel(const GateUpParams a) {
                     gv[j] = r;
                   } else {
                     const uint64_t o = (uint64_t)s_pairs[ti] * I + row;
-                    a.out[o] = swiglu_tail(gv[j], r);
+                    a.out[o] = swiglu_tail_tab(gv[j], r, s_sig);
                     if (a.gate_probe) a.gate_probe[o] = gv[j];
                     if (a.up_probe) a.up_probe[o] = r;
                   }

@@ -79,17 +79,55 @@ __device__ float round_scaled(int64_t hi, int64_t lo, int e2, float s) {
   return r;
 }
 
-// The lane-0 tail of GATE_UP_SOURCE: gate and up rounded to bf16, sigmoid in
-// F32 (exp evaluated in double and rounded once to F32), silu and the product
-// each rounded to bf16.
-__device__ uint16_t swiglu_tail(float gate, float up) {
+// bf16 sigmoid of the lane-0 tail of GATE_UP_SOURCE for a bf16 gate gT:
+// exp(-gT) evaluated in double and rounded once to F32, then 1 + e and 1 / d
+// in F32, rounded to bf16.
+__device__ uint16_t sigmoid_bf16(uint16_t gb) {
 #pragma clang fp contract(off)
-  const float gT = bf16_val(bf16_rne(gate));
-  const float uT = bf16_val(bf16_rne(up));
+  const float gT = bf16_val(gb);
   const float e = (float)exp(-(double)gT);
   const float d = 1.0f + e;
   const float sig = 1.0f / d;
-  const float sT = bf16_val(bf16_rne(sig));
+  return bf16_rne(sig);
+}
+
+// The lane-0 tail: gate and up rounded to bf16, the bf16 sigmoid, silu and the
+// product each rounded to bf16.
+__device__ uint16_t swiglu_tail(float gate, float up) {
+#pragma clang fp contract(off)
+  const uint16_t gb = bf16_rne(gate);
+  const float gT = bf16_val(gb);
+  const float uT = bf16_val(bf16_rne(up));
+  const float sT = bf16_val(sigmoid_bf16(gb));
+  const float siluT = bf16_val(bf16_rne(gT * sT));
+  return bf16_rne(siluT * uT);
+}
+
+// The bf16 sigmoid depends on the 16 bits of gT only.  For |gT| < 2^-9
+// (exponent field below 118, zeros and subnormals included) it is exactly 0.5;
+// for |gT| >= 128 (field 134 and up, infinities included) it is 1 for positive
+// and +0 for negative gT; NaN stays NaN.  The 4096 values in between are
+// tabulated once per work-group (kSigTable entries: sign, field 118..133,
+// 7-bit mantissa), which keeps the double exp out of the per-row tail.
+constexpr int kSigTable = 2 * 16 * 128;
+
+__device__ __forceinline__ uint16_t sig_table_bits(int i) {
+  // entry i -> the bf16 gT it holds
+  return (uint16_t)(((i >> 11) << 15) | ((118 + ((i >> 7) & 15)) << 7) | (i & 127));
+}
+
+__device__ __forceinline__ uint16_t swiglu_tail_tab(float gate, float up, const uint16_t* tab) {
+#pragma clang fp contract(off)
+  const uint16_t gb = bf16_rne(gate);
+  const float gT = bf16_val(gb);
+  const float uT = bf16_val(bf16_rne(up));
+  const int ef = (gb >> 7) & 0xFF;
+  uint16_t sb;
+  if (ef < 118) sb = 0x3F00;
+  else if (ef < 134) sb = tab[((gb >> 15) << 11) | ((ef - 118) << 7) | (gb & 127)];
+  else if (ef < 255 || (gb & 127) == 0) sb = (gb & 0x8000) ? 0x0000 : 0x3F80;
+  else sb = 0x7FC0;
+  const float sT = bf16_val(sb);
   const float siluT = bf16_val(bf16_rne(gT * sT));
   return bf16_rne(siluT * uT);
 }
