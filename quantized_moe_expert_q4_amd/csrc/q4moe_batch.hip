@@ -3,9 +3,12 @@
 // Arithmetic: GATE_UP_SOURCE of the @mlx-bun/inference 1.0.0 diff, page 52
 // (kernels/glm52/streamed-experts.ts), made exact as in q4moe_device.h.
 //
-// A group of up to G = 16*NT/6 tokens has C = 6*count digit columns; for the
-// whole K they do not fit LDS, so the sixteen waves of a work-group move
-// through K together, one K-chunk at a time:
+// A group of up to G = 16*NT/6 tokens has C = L*count digit columns, with
+// L = 4 digits per value when every value of the group's tokens lies within
+// 22 binades of its token's largest (exact, see digits_for) and L = 6
+// otherwise.  For the whole K the digits do not fit LDS in general, so the
+// sixteen waves of a work-group move through K together, one K-chunk at a
+// time:
 //  * One persistent launch, one 1024-thread work-group per CU: work-group b
 //    takes the whole 16-row tiles [bT/NB, (b+1)T/NB); it walks them in
 //    batches of sixteen (one tile per wave), so the per-CU weight bytes
@@ -58,9 +61,10 @@ template <int NT, bool VEC>
 __global__ __launch_bounds__(kBatThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void batch_kernel(const GateUpParams a) {
   constexpr int G = (16 * NT) / 6;
-  __shared__ __attribute__((aligned(16))) uint8_t s_b[2][kBatBuf];
+  __shared__ __attribute__((aligned(16))) uint8_t s_buf[2 * kBatBuf];  // two digit buffers, or one spanning both
   __shared__ int s_pairs[G];
   __shared__ int s_xmax[G];
+  __shared__ int s_xmin[G];                  // smallest non-zero exponent field of each token
   __shared__ int s_wcnt[kBatWaves];
   __shared__ int s_invalid;
   __shared__ uint16_t s_sig[kSigTable];      // bf16 sigmoid of the tabulated gT
@@ -120,7 +124,10 @@ void batch_kernel(const GateUpParams a) {
     if (grouped && tid < P) idv = a.ids[tid];
     for (;;) {
       __syncthreads();  // previous group done with s_b and s_pairs
-      if (tid < G) s_xmax[tid] = 0;
+      if (tid < G) {
+        s_xmax[tid] = 0;
+        s_xmin[tid] = 255;
+      }
       // ---- next group of up to G pairs routed to slot e ----
       int count, more;
       if (!grouped) {
@@ -159,11 +166,6 @@ void batch_kernel(const GateUpParams a) {
       if (count <= 0) break;
       next_pair = s_pairs[count - 1] + 1;
       if (grouped && more) idv = (next_pair + tid < P) ? a.ids[next_pair + tid] : -1;
-      const int C = 6 * count;
-      const int ntiles = (C + 15) >> 4;
-      const int sb = bat_step_bytes(ntiles);
-      const int spc = bat_chunk_steps(ntiles, S);
-      const int nch = (S + spc - 1) / spc;
       const int nbatch = (t1 - t0 + kBatWaves - 1) / kBatWaves;
 
       const int nxu = count * (H / 8);                 // 16-byte units of x, token-major
@@ -198,25 +200,46 @@ void batch_kernel(const GateUpParams a) {
       for (int u0 = 0; u0 < nxu; u0 += kBatThreads) {
         const int u = u0 + tid;
         const int ti = min(u, nxu - 1) / (H / 8);
-        uint32_t mx = 0;
+        uint32_t mx = 0, mn = 255;
         if (u < nxu) {
           const int w8 = u - ti * (H / 8);
-          mx = max_mag8(*(const uint4*)(a.x + (uint64_t)(s_pairs[ti] / a.K) * H + 8 * w8));
+          const uint4 xq = *(const uint4*)(a.x + (uint64_t)(s_pairs[ti] / a.K) * H + 8 * w8);
+          mx = max_mag8(xq);
+          mn = min_exp8(xq);
         }
         if (__shfl(ti, 0) == __shfl(ti, 63)) {
 #pragma unroll
-          for (int off = 32; off > 0; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
+          for (int off = 32; off > 0; off >>= 1) {
+            mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
+            mn = min(mn, (uint32_t)__shfl_xor((int)mn, off));
+          }
           if (lane == 0 && mx) atomicMax(&s_xmax[ti], (int)mx);
-        } else if (mx) {
-          atomicMax(&s_xmax[ti], (int)mx);
+          if (lane == 0 && mn < 255) atomicMin(&s_xmin[ti], (int)mn);
+        } else {
+          if (mx) atomicMax(&s_xmax[ti], (int)mx);
+          if (mn < 255) atomicMin(&s_xmin[ti], (int)mn);
         }
       }
       __syncthreads();
+      // digits per value for the whole group: four when every token allows it
+      int L = 4;
+      for (int ti = 0; ti < count; ++ti) L = max(L, digits_for(s_xmax[ti], s_xmin[ti]));
+      L = __builtin_amdgcn_readfirstlane(L);
+      const int C = L * count;
+      const int ntiles = (C + 15) >> 4;
+      const int sb = bat_step_bytes(ntiles);
+      // Four-digit groups whose digits for the whole K fit both buffers keep
+      // them resident for the group: no chunk barriers, no restaging per
+      // batch, and the epilogue recombines digits across lanes (no LDS).
+      const bool whole = L == 4 && S * sb <= 2 * kBatBuf;
+      const int spc = whole ? S : bat_chunk_steps(ntiles, S);
+      const int nch = (S + spc - 1) / spc;
+      auto half = [&](int h) { return s_buf + (h & 1) * kBatBuf; };
 
       // digits of 8 consecutive K values (unit w8 of a chunk) of token ti
       auto stage_unit = [&](uint8_t* buf, int ti, int w8, const uint4 xq) {
         uint32_t lo[8], hi[8];
-        x8_digits(xq, max((s_xmax[ti] >> 7) & 0xFF, 1), lo, hi);
+        x8_digits(xq, max((s_xmax[ti] >> 7) & 0xFF, 1) + 8 * (6 - L), lo, hi);
         const int tl = w8 >> 4, gg = (w8 >> 2) & 3, i = w8 & 3;
 #pragma unroll
         for (int par = 0; par < 2; ++par) {
@@ -225,8 +248,8 @@ void batch_kernel(const GateUpParams a) {
           uint8_t* base = buf + tl * sb + par * ntiles * 1024 + gg * 256 + 4 * i;
 #pragma unroll
           for (int s = 0; s < 6; ++s) {
-            const int col = ti * 6 + s;
-            *(uint32_t*)(base + (col >> 4) * 1024 + (col & 15) * 16) = d[s];
+            const int col = ti * L + s;
+            if (s < L) *(uint32_t*)(base + (col >> 4) * 1024 + (col & 15) * 16) = d[s];
           }
         }
       };
@@ -245,7 +268,7 @@ void batch_kernel(const GateUpParams a) {
 
       // columns past C in the last tile hold stale bytes; their results are never read
 
-      stage(0, s_b[0]);
+      stage(0, s_buf);
       __syncthreads();
       // the weights of this wave's first tile go out now
       v4u rg0, ru0, rg1, ru1;
@@ -262,9 +285,9 @@ void batch_kernel(const GateUpParams a) {
           accu[n] = v4i{0, 0, 0, 0};
         }
         for (int c = 0; c < nch; ++c, ++gch) {
-          const uint8_t* buf = s_b[nch == 1 ? 0 : (gch & 1)];
+          const uint8_t* buf = nch == 1 ? s_buf : half(gch);
           const bool more = (c + 1 < nch) || (bb + 1 < nbatch);
-          if (nch > 1 && more) stage((c + 1) % nch, s_b[(gch + 1) & 1]);
+          if (nch > 1 && more) stage((c + 1) % nch, half(gch + 1));
           if (active) {
             const int sa = c * spc, se = min(S, sa + spc);
             auto compute = [&](const v4u& g, const v4u& u_, int s) {
@@ -291,7 +314,44 @@ void batch_kernel(const GateUpParams a) {
               issue(rg1, ru1);
             }
           }
-          __syncthreads();
+          if (!whole) __syncthreads();
+        }
+
+        if (whole) {
+          // ---- epilogue across lanes: with four digits per token, the digits of
+          // a (row, token) sum sit in the four lanes of a quad (columns 4t..4t+3);
+          // a transposing quad reduction leaves lane j of the quad with row j ----
+          if (active) {
+            const int j = cc & 3;
+            const int row = tile * 16 + 4 * g4 + j;
+            auto quad_row_sum = [&](const v4i acc) {
+              const int64_t w0 = (int64_t)acc[0] << (8 * j), w1 = (int64_t)acc[1] << (8 * j);
+              const int64_t w2 = (int64_t)acc[2] << (8 * j), w3 = (int64_t)acc[3] << (8 * j);
+              const bool up2 = (j & 2) != 0;
+              const int64_t r0 = __shfl_xor(up2 ? w0 : w2, 2), r1 = __shfl_xor(up2 ? w1 : w3, 2);
+              const int64_t k0 = (up2 ? w2 : w0) + r0, k1 = (up2 ? w3 : w1) + r1;   // rows (j&2), (j&2)+1
+              const int64_t r = __shfl_xor((j & 1) ? k0 : k1, 1);
+              return ((j & 1) ? k1 : k0) + r;
+            };
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+              if (n < ntiles) {
+                const int ti = 4 * n + (cc >> 2);
+                const int64_t vg = quad_row_sum(accg[n]);
+                const int64_t vu = quad_row_sum(accu[n]);
+                if (ti < count && row < I) {
+                  const int e2 = sum_exponent(s_xmax[ti]) + 16;
+                  const float gate = round_scaled(vg >> 24, vg & 0xFFFFFF, e2, gscale[row]);
+                  const float up = round_scaled(vu >> 24, vu & 0xFFFFFF, e2, uscale[row]);
+                  const uint64_t o = (uint64_t)s_pairs[ti] * I + row;
+                  a.out[o] = swiglu_tail_tab(gate, up, s_sig);
+                  if (a.gate_probe) a.gate_probe[o] = gate;
+                  if (a.up_probe) a.up_probe[o] = up;
+                }
+              }
+            }
+          }
+          continue;
         }
 
         // ---- epilogue: digit matrix through the free LDS buffer ----
@@ -299,7 +359,7 @@ void batch_kernel(const GateUpParams a) {
         // buffer's twin when one chunk covers K, else the last chunk's buffer
         // (the other one already holds the next batch's first chunk).
         {
-          int32_t* ep = (int32_t*)s_b[nch == 1 ? 1 : ((gch - 1) & 1)] + wave * (16 * kEpStride);
+          int32_t* ep = (int32_t*)half(nch == 1 ? 1 : gch - 1) + wave * (16 * kEpStride);
           if (active) {
             // gate first, then up, through the same 16 x C matrix
             float gv[2];
@@ -320,11 +380,12 @@ void batch_kernel(const GateUpParams a) {
                 const int rr = item & 15, ti = item >> 4;
                 const int row = tile * 16 + rr;
                 if (ti < count && row < I) {
-                  const int32_t* d = ep + rr * kEpStride + ti * 6;
+                  const int32_t* d = ep + rr * kEpStride + ti * L;
                   const int64_t lo = (int64_t)d[0] + ((int64_t)d[1] << 8) + ((int64_t)d[2] << 16);
-                  const int64_t hi = (int64_t)d[3] + ((int64_t)d[4] << 8) + ((int64_t)d[5] << 16);
+                  const int64_t hi = L == 6 ? (int64_t)d[3] + ((int64_t)d[4] << 8) + ((int64_t)d[5] << 16)
+                                            : (int64_t)d[3];
                   const int xm = s_xmax[ti];
-                  float r = round_scaled(hi, lo, sum_exponent(xm), part ? uscale[row] : gscale[row]);
+                  float r = round_scaled(hi, lo, sum_exponent(xm) + 8 * (6 - L), part ? uscale[row] : gscale[row]);
                   if (xm >= 0x7F80) r = __builtin_nanf("");
                   if (!part) {
                     gv[j] = r;

@@ -222,4 +222,28 @@ __device__ __forceinline__ uint32_t max_mag8(const uint4 v) {
 // (X = x * 2^(172 - etop1) and the 16x weight factor).
 __device__ __forceinline__ int sum_exponent(int xmax_bits) { return max((xmax_bits >> 7) & 0xFF, 1) - 176; }
 
+// Smallest exponent field (at least 1) among the non-zero values of 8 bf16, 255 if none.
+__device__ __forceinline__ uint32_t min_exp8(const uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t m = 255u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t b = (w[i] >> (16 * h)) & 0xFFFFu;
+      if (b & 0x7FFFu) m = min(m, max((b >> 7) & 0xFFu, 1u));
+    }
+  }
+  return m;
+}
+
+// Digits per value for a token whose largest |x| has bits xmax and whose
+// smallest non-zero exponent field is emin: four when every value sits
+// within 22 binades of the largest (x * 2^(22 - e_top) is then an integer of
+// magnitude below 2^30, so the four-digit split is exact and gives the same
+// sum as six digits), else six.  Non-finite tokens keep six.
+__device__ __forceinline__ int digits_for(int xmax, int emin) {
+  return (xmax < 0x7F80 && emin >= max((xmax >> 7) & 0xFF, 1) - (kFracBits - 16)) ? 4 : 6;
+}
+
 }  // namespace q4

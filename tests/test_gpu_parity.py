@@ -220,3 +220,22 @@ def test_determinism_and_batch_invariance():
     (og, gg, ug), invalid = run_grouped(c.slots, c.layout, c.x, ids, c.H, c.I)
     assert invalid == 0
     assert np.array_equal(og[:, 0], o1) and np.array_equal(gg[:, 0].view(np.uint32), g1.view(np.uint32))
+
+
+@pytest.mark.parametrize("H,I,M,wide", [(7168, 96, 8, False), (4096, 80, 8, True), (1024, 48, 5, False)])
+def test_digit_count_paths(H, I, M, wide):
+    """Token groups split into four digits per value (all values within 22
+    binades of their token's largest), in K-chunks (H=7168) or resident
+    (H <= 4608), and a group sent back to six digits by one token whose values
+    span more binades."""
+    rng = np.random.default_rng(H + I + M + int(wide))
+    lay = synth.contiguous_layout(H, I)
+    slot = synth.fill_slot(rng, H, I, lay)
+    x = synth.bf16_normal(rng, (M, H))
+    if wide:
+        x[3, 5] = 0x461C                                 # 9984
+        x[3, 6] = 0x3300                                 # 2^-25: 38 binades below it
+    say(f"[digit paths H={H} I={I} M={M} wide={wide}]")
+    out, g, u = run_single(slot, lay, x, H, I)
+    gr, ur, orf = oracle.expert_gate_up(slot, lay, x, H, I)
+    check_parity(out, g, u, gr, ur, orf, f"digit paths H={H} M={M} wide={wide}")
