@@ -295,15 +295,19 @@ void batch_kernel(const GateUpParams a) {
               split_weights(g, ge, go);
               split_weights(u_, ue, uo);
               const uint8_t* bp = buf + (s - sa) * sb + lane * 16;
+              v4i be[NT], bo[NT];
+#pragma unroll
+              for (int n = 0; n < NT; ++n) {
+                be[n] = *(const v4i*)(bp + n * 1024);
+                bo[n] = *(const v4i*)(bp + (ntiles + n) * 1024);
+              }
 #pragma unroll
               for (int n = 0; n < NT; ++n) {
                 if (n < ntiles) {
-                  const v4i be = *(const v4i*)(bp + n * 1024);
-                  const v4i bo = *(const v4i*)(bp + (ntiles + n) * 1024);
-                  accg[n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ge, be, accg[n], 0, 0, 0);
-                  accu[n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ue, be, accu[n], 0, 0, 0);
-                  accg[n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(go, bo, accg[n], 0, 0, 0);
-                  accu[n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(uo, bo, accu[n], 0, 0, 0);
+                  accg[n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ge, be[n], accg[n], 0, 0, 0);
+                  accu[n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ue, be[n], accu[n], 0, 0, 0);
+                  accg[n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(go, bo[n], accg[n], 0, 0, 0);
+                  accu[n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(uo, bo[n], accu[n], 0, 0, 0);
                 }
               }
             };
