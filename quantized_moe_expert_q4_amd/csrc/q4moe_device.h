@@ -212,6 +212,43 @@ __device__ __forceinline__ void x8_digits(const uint4 v, int etop1, uint32_t (&l
   }
 }
 
+// Four-digit split for tokens whose values all lie within 22 binades of the
+// largest (see digits_for): X = x * 2^(22 - e_top) is an integer below 2^30
+// in magnitude, and its four balanced base-256 digits are the bytes of one
+// 32-bit word.  The digits equal digits 0..3 of x_digits(b, etop1 + 16),
+// whose digits 4 and 5 are then zero.  Zero values give zero digits for any
+// shift; non-zero values have a shift in [0, 22].
+__device__ __forceinline__ uint32_t x_digits4(uint32_t b, int etop1) {
+  const uint32_t E = (b >> 7) & 0xFFu;
+  const uint32_t mag = (b & 0x7Fu) | (E ? 0x80u : 0u);
+  const int sh = (int)(E ? E : 1u) - etop1 + (kFracBits - 16);
+  uint32_t X = mag << (sh & 31);
+  X = (b & 0x8000u) ? 0u - X : X;
+  return (X + 0x80808080u) ^ 0x80808080u;
+}
+
+// Four-digit words of eight packed bf16 activations: d[par][s] holds digit s
+// of positions par, par+2, par+4, par+6 (one byte each), the byte order of
+// one MFMA B-operand dword.
+__device__ __forceinline__ void x8_digits4(const uint4 v, int etop1, uint32_t (&d)[2][4]) {
+  const uint32_t xb[8] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16,
+                          v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
+  uint32_t w[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) w[p] = x_digits4(xb[p], etop1);
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const uint32_t u01 = perm(w[par + 2], w[par], 0x05010400u);
+    const uint32_t u23 = perm(w[par + 2], w[par], 0x07030602u);
+    const uint32_t v01 = perm(w[par + 6], w[par + 4], 0x05010400u);
+    const uint32_t v23 = perm(w[par + 6], w[par + 4], 0x07030602u);
+    d[par][0] = perm(v01, u01, 0x05040100u);
+    d[par][1] = perm(v01, u01, 0x07060302u);
+    d[par][2] = perm(v23, u23, 0x05040100u);
+    d[par][3] = perm(v23, u23, 0x07060302u);
+  }
+}
+
 // Largest bf16 magnitude bits among eight packed activations.
 __device__ __forceinline__ uint32_t max_mag8(const uint4 v) {
   uint32_t m = max(max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu), max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu));

@@ -19,7 +19,7 @@ struct GateUpParams {
   int32_t* invalid_count;    // grouped: number of out-of-range ids, or nullptr
   int M, K, H, I, num_slots;
   int G, steps;              // set by the launchers: tokens per group, K-steps per tile
-  int pair_share;            // set by the launchers: see launch_resident
+  int wave_share;            // set by launch_resident: a SIMD's first-wave share, 1/1024
 };
 
 // Resident-digits kernel for token groups of at most two (decode widths):

@@ -1,23 +1,26 @@
-// Q4 gate/up + SwiGLU for narrow token sets (decode): digits resident in LDS.
+// Q4 gate/up + SwiGLU for narrow token sets (decode and verify widths): the
+// digits of every token of the call stay resident in LDS for the launch.
 //
 // Arithmetic: GATE_UP_SOURCE of the @mlx-bun/inference 1.0.0 diff, page 52
 // (kernels/glm52/streamed-experts.ts), made exact as in q4moe_device.h.
 //
-// With at most two tokens in the call, the digit-split activations of every
-// token (C = 6*M columns) for the whole K fit one LDS buffer.  A work-group
-// splits them once, from a single read of x, and keeps them for the whole
-// launch: every slot's group of routed pairs reads the columns of its own
-// tokens, so nothing is staged again when the slot changes.
-//  * One persistent launch: work-group b takes the whole tiles
-//    [bT/NB, (b+1)T/NB) of the T = slots x tiles-per-slot tiles, so the
-//    weight bytes per work-group differ by at most one tile.
-//  * Inside a work-group the unit range of a slot segment is cut into eight
-//    equal wave ranges (multiples of D steps).  Each wave streams its own
-//    (16-row tile, K-step) units, keeping D K-steps of weights in flight in a
-//    register ring; the first loads of a segment go out before the routing
-//    scan and (first segment) before x is read.
+// Digit columns: each token of a pass owns W adjacent columns of the MFMA B
+// operand, W = 4 when every token of the call allows four digits per value
+// (digits_for) and W = 8 otherwise, laid out [d0 d1 d2 0 d3 d4 d5 0].  Either
+// way the digits of one (row, token) sum fill whole lane quads of the MFMA
+// result and recombine with quad shuffles, without LDS.  NT 16-column tiles
+// hold 16*NT/W tokens; a call with more tokens than that takes several passes
+// over its weights (only with W = 8 and more than 16*NT/8 tokens).
+//  * One persistent launch, one 8-wave work-group per CU: work-group b takes
+//    the whole tiles [bT/NB, (b+1)T/NB) of the T = slots x tiles-per-slot tiles.
+//  * Inside a work-group the (tile, K-step) units of a slot segment are cut
+//    into eight wave ranges (multiples of D steps; the first wave of each
+//    SIMD takes a little more, see wave_share).  Each wave streams its own
+//    units with D K-steps of weights in flight in a register ring; the first
+//    loads of a segment go out before its routing scan and, in the first
+//    segment, before x is split.
 //  * A tile cut by a wave boundary has several contributors; each adds its
-//    exact int64 partial sums into an LDS slot with LDS atomics and bumps the
+//    exact quad sums into an LDS fix-up slot with LDS atomics and bumps the
 //    slot's counter; the last one to arrive finishes the tile.  No wave waits
 //    on another inside a segment.
 //  * K-steps per tile are padded to a multiple of D; the padding steps meet
@@ -34,60 +37,73 @@ namespace {
 
 constexpr int kResWaves = 8;
 constexpr int kResThreads = kResWaves * 64;
-constexpr int kResBBytes = 56 * 1024;     // digits of all tokens over the whole K
-constexpr int kResMaxCols = 12;           // two tokens of six digits
-constexpr int kResGroup = 2;              // routed pairs finished per pass over a slot
-constexpr int kResItems = 16 * kResGroup; // (row, pair) results of one tile
-constexpr int kResXRegs = 3;              // 16-byte chunks of x held per thread while splitting
+constexpr int kResD = 4;                   // K-steps of weights in flight per wave
+constexpr int kResLds = 150 * 1024;        // digits, then the fix-up slots
+constexpr int kResXRegs = 8;               // 16-byte chunks of x held per thread while splitting
+constexpr int kResMaxTokens = 8;           // tokens per call
+constexpr int kResMaxPairs = 16;           // routed pairs finished per pass over a slot
+constexpr int kResFixSlots = kResWaves - 1;
+constexpr int kResIdRegs = 4;              // routing ids held per thread (2048 pairs)
 
-__host__ __device__ constexpr int block_stride(int C) { return C * 16 + 16; }  // one padded (step, parity, g) block
+// One K-step of digits: [parity 2][column tile n][k-group g 4][16 x 16 bytes].
+// The 16-byte chunk of column c sits at position c ^ (4g + step % 4) of its
+// k-group row, so that both the B-fragment reads (the sixteen lanes of one
+// k-group read sixteen distinct chunks) and the digit stores of one wave
+// (lanes spread over dwords, k-groups and four steps) hit distinct banks.
+__host__ __device__ constexpr int res_step_bytes(int nt) { return 2 * nt * 1024; }
+__host__ __device__ constexpr int res_chunk(int g, int c, int step) { return g * 16 + (c ^ (4 * g + (step & 3))); }
+// One fix-up slot: int64 [tile][gate, up][lane] (quad sums).
+__host__ __device__ constexpr int res_fix_words(int nt) { return nt * 2 * 64; }
+// K-steps per tile, padded to whole rings.
+__host__ __device__ constexpr int res_steps(int H) { return ((H + 127) / 128 + kResD - 1) / kResD * kResD; }
+// Column tiles for a call of M tokens: one up to two tokens, else two.
+__host__ __device__ constexpr int res_tiles(int M) { return M <= 2 ? 1 : 2; }
 
 }  // namespace
 
-template <int D, bool VEC>
-__global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void resident_kernel(const GateUpParams a) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_b[kResBBytes];
-  __shared__ int32_t s_acc[kResWaves][2][16 * kResMaxCols];   // per-wave digit matrix of a tile
-  __shared__ unsigned long long s_fix[kResWaves][kResItems * 4];
-  __shared__ int s_fixcnt[kResWaves];
-  __shared__ int s_pairs[kResGroup];
+template <int NT, bool VEC>
+__global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void resident_kernel(const GateUpParams a) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_lds[kResLds];
+  __shared__ int s_pairs[kResMaxPairs];
+  __shared__ int s_ptok[kResMaxPairs];       // token of each pair, relative to the pass
+  __shared__ int s_xmax[kResMaxTokens];
+  __shared__ int s_xmin[kResMaxTokens];      // smallest non-zero exponent field of each token
   __shared__ int s_wcnt[kResWaves];
-  __shared__ int s_xmax[2];
+  __shared__ int s_fixcnt[kResFixSlots];
+  __shared__ int s_bound[kResWaves + 1];     // unit ranges of the segment, by position
   __shared__ int s_invalid;
+  __shared__ uint16_t s_sig[kSigTable];      // bf16 sigmoid of the tabulated gT
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, cc = lane & 15;
-  const int H = a.H, I = a.I;
-  const int P = a.M * a.K;
+  const int H = a.H, I = a.I, M = a.M, K = a.K;
+  const int P = M * K;
   const bool grouped = a.ids != nullptr;
   const int S = a.steps;                     // K-steps per tile, a multiple of D
-  const int C = 6 * a.M;                     // digit columns: every token of the call
-  const int bs = block_stride(C);
+  const int sbytes = res_step_bytes(NT);
+  const int hw = H / 8;                      // 16-byte chunks of one token's x
   const int tps = (I + 15) / 16;             // tiles per slot
   const int T = a.num_slots * tps;
   const int NB = gridDim.x;
-  // Tile range of this work-group.  With two work-groups per CU (pair_share
-  // > 0) the grid is split into CU pairs (b, b + NB/2): the one dispatched
-  // first wins the CU's memory-issue arbitration more often, so it takes
-  // pair_share/1024 of the pair's tiles and both finish together.
-  int v0, v1;
-  if (a.pair_share > 0) {
-    const int P2 = NB / 2;
-    const int pair = (int)blockIdx.x % P2;
-    const int pa = (int)((int64_t)pair * T / P2), pb = (int)((int64_t)(pair + 1) * T / P2);
-    const int mid = pa + (int)(((int64_t)(pb - pa) * a.pair_share + 512) / 1024);
-    v0 = (int)blockIdx.x < P2 ? pa : mid;
-    v1 = (int)blockIdx.x < P2 ? mid : pb;
-  } else {
-    v0 = (int)((int64_t)blockIdx.x * T / NB);
-    v1 = (int)((int64_t)(blockIdx.x + 1) * T / NB);
-  }
+  const int v0 = (int)((int64_t)blockIdx.x * T / NB), v1 = (int)((int64_t)(blockIdx.x + 1) * T / NB);
   const uint32_t wbytes = (uint32_t)((uint64_t)I * (uint32_t)(H / 2));
   const uint64_t below = (1ull << lane) - 1ull;
+  unsigned long long* const s_fix = (unsigned long long*)(s_lds + S * sbytes);
 
-  if (tid < 2) s_xmax[tid] = 0;
+  // routing ids of the first pairs, read once, before any weight load
+  int idr[kResIdRegs];
+#pragma unroll
+  for (int j = 0; j < kResIdRegs; ++j) {
+    const int p = tid + j * kResThreads;
+    idr[j] = (grouped && p < P) ? a.ids[p] : -1;
+  }
+
+  if (tid < kResMaxTokens) {
+    s_xmax[tid] = 0;
+    s_xmin[tid] = 255;
+  }
   if (tid == 0) s_invalid = 0;
   __syncthreads();
 
@@ -111,149 +127,231 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(4, 
     if (tid == 0 && a.invalid_count) *a.invalid_count = s_invalid;
   }
 
+  // ---- x of every token, loaded before any weight load ----
+  uint4 xv[kResXRegs];
+  const int nxc = M * hw;
+#pragma unroll
+  for (int j = 0; j < kResXRegs; ++j) {
+    const int q = tid + j * kResThreads;
+    xv[j] = q < nxc ? ((const uint4*)a.x)[q] : make_uint4(0, 0, 0, 0);
+  }
+
+  // ---- the current slot segment: tiles [t0, t1) of slot e ----
+  int v = v0;
+  int e = 0, t0 = 0, t1 = 0, nunits = 0, ua = 0, ub = 0;
+  __amdgpu_buffer_rsrc_t gsrc, usrc;
+  const float* gscale = nullptr;
+  const float* uscale = nullptr;
+  // Unit range start of position k (0..8).  The units are cut into four equal
+  // quarters, one per SIMD; quarter q goes to waves q (first on its SIMD,
+  // which wins the SIMD's issue arbitration more often) and q + 4, the first
+  // taking wave_share/1024.  Position k = 2*(wave % 4) + wave / 4 orders the
+  // ranges by unit.
+  auto bound = [&](int k) {
+    if (k >= kResWaves) return nunits;
+    const int q = k >> 1;
+    const int qa = (int)(((int64_t)q * nunits / 4) / kResD * kResD);
+    if (!(k & 1)) return qa;
+    const int qb = q == 3 ? nunits : (int)(((int64_t)(q + 1) * nunits / 4) / kResD * kResD);
+    return qa + (int)(((int64_t)(qb - qa) * a.wave_share / 1024) / kResD * kResD);
+  };
+  const int wpos = 2 * (wave & 3) + (wave >> 2);
+  auto open_segment = [&]() {
+    e = v / tps;
+    t0 = v - e * tps;
+    t1 = min(v1, (e + 1) * tps) - e * tps;
+    v = e * tps + t1;
+    const uint8_t* slot = a.slots + (uint64_t)e * a.slot_stride;
+    gsrc = make_rsrc(slot + a.gate_w_off, wbytes);
+    usrc = make_rsrc(slot + a.up_w_off, wbytes);
+    gscale = (const float*)(slot + a.gate_s_off);
+    uscale = (const float*)(slot + a.up_s_off);
+    nunits = (t1 - t0) * S;
+    ua = bound(wpos);
+    ub = bound(wpos + 1);
+  };
+
   auto row_off = [&](int tile) {
     const int row = tile * 16 + cc;
     return (uint32_t)(row < I ? row : I - 1) * (uint32_t)(H / 2) + (uint32_t)(g4 * 16);
   };
-  const int col = min(cc, C - 1);
-  const uint8_t* bl = s_b + g4 * bs + col * 16;                // + (step*2 + par)*4*bs
-
-  bool staged = false;
-  int v = v0;
-  while (v < v1) {
-    const int e = v / tps;
-    const int t0 = v - e * tps;                               // first tile of the segment in slot e
-    const int t1 = min(v1, (e + 1) * tps) - e * tps;          // end tile
-    v = e * tps + t1;
-    const uint8_t* slot = a.slots + (uint64_t)e * a.slot_stride;
-    const __amdgpu_buffer_rsrc_t gsrc = make_rsrc(slot + a.gate_w_off, wbytes);
-    const __amdgpu_buffer_rsrc_t usrc = make_rsrc(slot + a.up_w_off, wbytes);
-    const float* gscale = (const float*)(slot + a.gate_s_off);
-    const float* uscale = (const float*)(slot + a.up_s_off);
-
-    // ---- this wave's unit range of the segment ----
-    const int nunits = (t1 - t0) * S;
-    auto bound = [&](int q) { return (int)(((int64_t)q * nunits / kResWaves) / D * D); };
-    const int ua = bound(wave), ub = (wave + 1 == kResWaves) ? nunits : bound(wave + 1);
-
-    v4u rg[D], ru[D];
-    int lt, ls;                                              // load cursor (tile, step)
-    uint32_t loff;
-    auto issue = [&](v4u& g, v4u& u_, bool live) {
-      const uint32_t o = live ? loff + (uint32_t)ls * 64u : kOffNone;
-      g = load16<VEC>(gsrc, o);
-      u_ = load16<VEC>(usrc, o);
-      // cursor step without branches, so the loads stay unconditional
-      const int nls = ls + (live ? 1 : 0);
-      const bool wrap = nls == S;
-      ls = wrap ? 0 : nls;
-      lt += wrap ? 1 : 0;
-      loff = wrap ? row_off(lt) : loff;
-    };
-    // The ring always holds D loads per array: slots past the wave's range
-    // load nothing (kOffNone) and are never consumed.
-    auto start_ring = [&]() {
-      lt = t0 + ua / S;
-      ls = ua % S;
-      loff = row_off(lt);
+  v4u rg[kResD], ru[kResD];
+  int lt = 0, ls = 0;                        // load cursor (tile, step)
+  uint32_t loff = 0;
+  auto issue = [&](v4u& g, v4u& u_, bool live) {
+    const uint32_t o = live ? loff + (uint32_t)ls * 64u : kOffNone;
+    g = load16<VEC>(gsrc, o);
+    u_ = load16<VEC>(usrc, o);
+    // cursor step without branches, so the loads stay unconditional
+    const int nls = ls + (live ? 1 : 0);
+    const bool wrap = nls == S;
+    ls = wrap ? 0 : nls;
+    lt += wrap ? 1 : 0;
+    loff = wrap ? row_off(lt) : loff;
+  };
+  // The ring always holds D loads per array: slots past the wave's range
+  // load nothing (kOffNone) and are never consumed.
+  auto start_ring = [&]() {
+    lt = t0 + ua / S;
+    ls = ua % S;
+    loff = row_off(lt);
 #pragma unroll
-      for (int d = 0; d < D; ++d) issue(rg[d], ru[d], ua + d < ub);
-    };
+    for (int d = 0; d < kResD; ++d) issue(rg[d], ru[d], ua + d < ub);
+  };
 
-    // first routing-scan window, loaded before the ring so that its wait
-    // does not include the weight loads
-    int next_pair = 0;
-    int idv = -1;
-    if (grouped && tid < P) idv = a.ids[tid];
-
-    // ---- first segment: x of every token, loaded before the ring ----
-    uint4 xv[kResXRegs];
-    const int nxc = a.M * (H / 8);                            // 16-byte chunks of x
-    if (!staged) {
+  // digits per value and columns per token, fixed once x has been read
+  int L = 6, W = 8;
+  auto etop = [&](int m) { return max((s_xmax[m] >> 7) & 0xFF, 1); };
+  // digits of chunk w8 (8 consecutive K values) of pass token tl
+  auto stage_unit = [&](int tl, int w8, const uint4 xq, int etop1) {
+    const int st = w8 >> 4, gg = (w8 >> 2) & 3, i = w8 & 3;
+    if (W == 4) {
+      uint32_t d[2][4];
+      x8_digits4(xq, etop1, d);
 #pragma unroll
-      for (int j = 0; j < kResXRegs; ++j) {
-        const int q = tid + j * kResThreads;
-        xv[j] = q < nxc ? ((const uint4*)a.x)[q] : make_uint4(0, 0, 0, 0);
+      for (int par = 0; par < 2; ++par) {
+        uint8_t* base = s_lds + st * sbytes + par * NT * 1024 + 4 * i;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int col = tl * 4 + s;
+          *(uint32_t*)(base + (col >> 4) * 1024 + res_chunk(gg, col & 15, st) * 16) = d[par][s];
+        }
+      }
+      return;
+    }
+    uint32_t lo[8], hi[8];
+    x8_digits(xq, etop1, lo, hi);
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      uint32_t d[6];
+      digit_words(lo, hi, par, d);
+      uint8_t* base = s_lds + st * sbytes + par * NT * 1024 + 4 * i;
+      auto put = [&](int col, uint32_t w) {
+        *(uint32_t*)(base + (col >> 4) * 1024 + res_chunk(gg, col & 15, st) * 16) = w;
+      };
+      put(tl * 8 + 0, d[0]);
+      put(tl * 8 + 1, d[1]);
+      put(tl * 8 + 2, d[2]);
+      put(tl * 8 + 3, 0u);
+      put(tl * 8 + 4, d[3]);
+      put(tl * 8 + 5, d[4]);
+      put(tl * 8 + 6, d[5]);
+      put(tl * 8 + 7, 0u);
+    }
+  };
+
+  // ---- first segment's weights in flight, then the digits of the first pass ----
+  open_segment();
+  start_ring();
+  for (int i = tid; i < kSigTable; i += kResThreads) s_sig[i] = sigmoid_bf16(sig_table_bits(i));
+  // largest |x| and smallest non-zero exponent of each token
+#pragma unroll
+  for (int j = 0; j < kResXRegs; ++j) {
+    const int q0 = j * kResThreads + (tid & ~63);          // first chunk of this wave
+    if (q0 < nxc) {
+      const int q = q0 + lane;
+      const int m = min(q, nxc - 1) / hw;
+      uint32_t mx = 0, mn = 255;
+      if (q < nxc) {
+        mx = max_mag8(xv[j]);
+        mn = min_exp8(xv[j]);
+      }
+      if (min(q0 + 63, nxc - 1) / hw == q0 / hw) {
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+          mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
+          mn = min(mn, (uint32_t)__shfl_xor((int)mn, off));
+        }
+        if (lane == 0 && mx) atomicMax(&s_xmax[m], (int)mx);
+        if (lane == 0 && mn < 255) atomicMin(&s_xmin[m], (int)mn);
+      } else {
+        if (mx) atomicMax(&s_xmax[m], (int)mx);
+        if (mn < 255) atomicMin(&s_xmin[m], (int)mn);
       }
     }
-    start_ring();
-
-    if (!staged) {
-      // largest |x| of each token
-      uint32_t m0 = 0, m1 = 0;
+  }
+  __syncthreads();
+  {
+    int l = 4;
+    for (int m = 0; m < M; ++m) l = max(l, digits_for(s_xmax[m], s_xmin[m]));
+    L = __builtin_amdgcn_readfirstlane(l);
+  }
+  W = L == 4 ? 4 : 8;
+  const int tpp = 16 * NT / W;                              // tokens per pass
+  const int npass = (M + tpp - 1) / tpp;
+  {
+    const int ntok = min(M, tpp);
 #pragma unroll
-      for (int j = 0; j < kResXRegs; ++j) {
-        const int q = tid + j * kResThreads;
-        const uint32_t mx = max_mag8(xv[j]);
-        if (q < nxc) {
-          if (q < H / 8) m0 = max(m0, mx);
-          else m1 = max(m1, mx);
-        }
+    for (int j = 0; j < kResXRegs; ++j) {
+      const int q = tid + j * kResThreads;
+      if (q < nxc) {
+        const int m = q / hw;
+        if (m < ntok) stage_unit(m, q - m * hw, xv[j], etop(m));
       }
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        m0 = max(m0, (uint32_t)__shfl_xor((int)m0, off));
-        m1 = max(m1, (uint32_t)__shfl_xor((int)m1, off));
-      }
-      if (lane == 0) {
-        if (m0) atomicMax(&s_xmax[0], (int)m0);
-        if (m1) atomicMax(&s_xmax[1], (int)m1);
-      }
-      __syncthreads();
-      // the digits of every token, and zero digits for the padding steps
-#pragma unroll
-      for (int j = 0; j < kResXRegs; ++j) {
-        const int q = tid + j * kResThreads;
-        if (q < nxc) {
-          const int m = q / (H / 8), w8 = q - m * (H / 8);
-          uint32_t lo[8], hi[8];
-          x8_digits(xv[j], max((s_xmax[m] >> 7) & 0xFF, 1), lo, hi);
-          const int tl = w8 >> 4, gg = (w8 >> 2) & 3, i = w8 & 3;
-#pragma unroll
-          for (int par = 0; par < 2; ++par) {
-            uint32_t d[6];
-            digit_words(lo, hi, par, d);
-            uint8_t* base = s_b + ((tl * 2 + par) * 4 + gg) * bs + m * 96 + 4 * i;
-#pragma unroll
-            for (int s = 0; s < 6; ++s) *(uint32_t*)(base + s * 16) = d[s];
-          }
-        }
-      }
-      const int padw = S * 16 - H / 8;
-      for (int u = tid; u < a.M * padw; u += kResThreads) {
-        const int m = u % a.M, w8 = H / 8 + u / a.M;
-        const int tl = w8 >> 4, gg = (w8 >> 2) & 3, i = w8 & 3;
-#pragma unroll
-        for (int par = 0; par < 2; ++par) {
-          uint8_t* base = s_b + ((tl * 2 + par) * 4 + gg) * bs + m * 96 + 4 * i;
-#pragma unroll
-          for (int s = 0; s < 6; ++s) *(uint32_t*)(base + s * 16) = 0u;
-        }
-      }
-      staged = true;
     }
+    // zero digits for the padding steps
+    const int padw = S * 16 - hw;
+    for (int u = tid; u < ntok * padw; u += kResThreads)
+      stage_unit(u % ntok, hw + u / ntok, make_uint4(0, 0, 0, 0), 1);
+  }
 
+  // exact (row, token) sum of the four digit columns of a lane quad: lane j
+  // of the quad receives row 4*g4 + j (transposing quad reduction)
+  const int qj = cc & 3;
+  auto quad_row_sum = [&](const v4i acc) {
+    const int64_t w0 = (int64_t)acc[0] << (8 * qj), w1 = (int64_t)acc[1] << (8 * qj);
+    const int64_t w2 = (int64_t)acc[2] << (8 * qj), w3 = (int64_t)acc[3] << (8 * qj);
+    const bool up2 = (qj & 2) != 0;
+    const int64_t r0 = __shfl_xor(up2 ? w0 : w2, 2), r1 = __shfl_xor(up2 ? w1 : w3, 2);
+    const int64_t k0 = (up2 ? w2 : w0) + r0, k1 = (up2 ? w3 : w1) + r1;  // rows (qj&2), (qj&2)+1
+    const int64_t r = __shfl_xor((qj & 1) ? k0 : k1, 1);
+    return ((qj & 1) ? k1 : k0) + r;
+  };
+  // this lane's B-fragment chunk for steps 0..3 mod 4
+  static_assert(kResD % 4 == 0, "ring depth keeps step % 4 fixed per ring slot");
+  int rdo[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) rdo[d] = res_chunk(g4, cc, d) * 16;
+
+  for (int pass = 0;;) {
+    const int tp0 = pass * tpp;                             // first token of the pass
+    const int tp1 = min(M, tp0 + tpp);                      // end token
+    const int pend = tp1 * K;                               // end pair
+    int next_pair = tp0 * K;
     bool first_group = true;
     for (;;) {
-      __syncthreads();  // previous group done with s_fix and s_pairs; digits visible
-      if (tid < kResWaves) s_fixcnt[tid] = 0;
-      for (int i = tid; i < kResWaves * kResItems * 4; i += kResThreads) (&s_fix[0][0])[i] = 0ull;
+      __syncthreads();  // previous group done with the fix-up slots, s_bound and s_pairs; digits visible
+      if (tid < kResFixSlots) s_fixcnt[tid] = 0;
+      if (tid <= kResWaves) s_bound[tid] = bound(tid);
+      for (int i = tid; i < kResFixSlots * res_fix_words(NT); i += kResThreads) s_fix[i] = 0;
 
-      // ---- next group of up to kResGroup pairs routed to slot e ----
+      // ---- next group of up to kResMaxPairs pairs of the pass routed to slot e ----
       int count, more;
       if (!grouped) {
-        count = min(kResGroup, P - next_pair);
-        more = next_pair + count < P;
-        if (tid < count) s_pairs[tid] = next_pair + tid;
-        __syncthreads();  // s_pairs and the cleared fix-up slots visible
+        count = min(kResMaxPairs, pend - next_pair);
+        more = next_pair + count < pend;
+        if (tid < count) {
+          s_pairs[tid] = next_pair + tid;
+          s_ptok[tid] = next_pair + tid - tp0;               // K == 1
+        }
+        __syncthreads();  // s_pairs, s_bound and the cleared fix-up slots visible
       } else {
-        // block-wide scan of ids[next_pair..P) in windows of kResThreads;
-        // stops once a further match proves there is another group
+        // block-wide scan of ids[next_pair..pend) in aligned windows of
+        // kResThreads (the first kResIdRegs from registers); stops once a
+        // further match proves there is another group
         int found = 0;
-        int base = next_pair;
+        int base = next_pair & ~(kResThreads - 1);
         more = 0;
         for (;;) {
-          const bool m = idv == e;
+          const int p = base + tid;
+          const int k = base / kResThreads;
+          int id;
+          if (k < kResIdRegs) {
+            id = k == 0 ? idr[0] : k == 1 ? idr[1] : k == 2 ? idr[2] : idr[3];
+          } else {
+            id = p < P ? a.ids[p] : -1;
+          }
+          const bool m = id == e && p >= next_pair && p < pend;
           const uint64_t bal = __ballot(m);
           if (lane == 0) s_wcnt[wave] = __popcll(bal);
           __syncthreads();
@@ -265,19 +363,20 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(4, 
             total += c;
           }
           before += __popcll(bal & below);
-          if (m && before < kResGroup) s_pairs[before] = base + tid;
+          if (m && before < kResMaxPairs) {
+            s_pairs[before] = p;
+            s_ptok[before] = p / K - tp0;
+          }
           found = total;
           base += kResThreads;
-          if (found > kResGroup) more = 1;
+          if (found > kResMaxPairs) more = 1;
           __syncthreads();  // s_wcnt reused; s_pairs visible
-          if (more || base >= P) break;
-          idv = (base + tid < P) ? a.ids[base + tid] : -1;
+          if (more || base >= pend) break;
         }
-        count = min(found, kResGroup);
+        count = min(found, kResMaxPairs);
       }
       if (count <= 0) break;
       next_pair = s_pairs[count - 1] + 1;
-      if (grouped && more) idv = (next_pair + tid < P) ? a.ids[next_pair + tid] : -1;
       if (!first_group) start_ring();
       first_group = false;
 
@@ -286,69 +385,64 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(4, 
         // one portion: the rest of the current tile inside [u, ub)
         const int tile = t0 + u / S;
         const int sa = u % S;
-        const int pe = min(ub, (u / S + 1) * S);             // portion end (unit)
-        v4i accg = {0, 0, 0, 0}, accu = {0, 0, 0, 0};
-        int s = sa;
-        for (; u < pe; u += D) {
+        const int pe = min(ub, (u / S + 1) * S);              // portion end (unit)
+        v4i accg[NT], accu[NT];
 #pragma unroll
-          for (int d = 0; d < D; ++d) {
+        for (int n = 0; n < NT; ++n) {
+          accg[n] = v4i{0, 0, 0, 0};
+          accu[n] = v4i{0, 0, 0, 0};
+        }
+        int s = sa;                                           // a multiple of 4: (s + d) % 4 == d % 4
+        for (; u < pe; u += kResD) {
+#pragma unroll
+          for (int d = 0; d < kResD; ++d) {
             v4i ge, go, ue, uo;
             split_weights(rg[d], ge, go);
             split_weights(ru[d], ue, uo);
-            const uint8_t* bp = bl + (s + d) * 8 * bs;
-            const v4i be = *(const v4i*)bp;
-            const v4i bo = *(const v4i*)(bp + 4 * bs);
-            accg = __builtin_amdgcn_mfma_i32_16x16x64_i8(ge, be, accg, 0, 0, 0);
-            accu = __builtin_amdgcn_mfma_i32_16x16x64_i8(ue, be, accu, 0, 0, 0);
-            accg = __builtin_amdgcn_mfma_i32_16x16x64_i8(go, bo, accg, 0, 0, 0);
-            accu = __builtin_amdgcn_mfma_i32_16x16x64_i8(uo, bo, accu, 0, 0, 0);
-            issue(rg[d], ru[d], u + d + D < ub);
-          }
-          s += D;
-        }
-        const int se = s;                                    // portion covers steps [sa, se)
-
-        // ---- digit matrix -> (row, pair) exact int64 sums ----
-        int32_t* eg = s_acc[wave][0];
-        int32_t* eu = s_acc[wave][1];
-        if (cc < C) {
+            const uint8_t* bp = s_lds + (s + d) * sbytes + rdo[d & 3];
+            v4i be[NT], bo[NT];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            eg[(4 * g4 + i) * C + cc] = accg[i];
-            eu[(4 * g4 + i) * C + cc] = accu[i];
+            for (int n = 0; n < NT; ++n) {
+              be[n] = *(const v4i*)(bp + n * 1024);
+              bo[n] = *(const v4i*)(bp + (NT + n) * 1024);
+            }
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+              accg[n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ge, be[n], accg[n], 0, 0, 0);
+              accu[n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ue, be[n], accu[n], 0, 0, 0);
+              accg[n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(go, bo[n], accg[n], 0, 0, 0);
+              accu[n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(uo, bo[n], accu[n], 0, 0, 0);
+            }
+            issue(rg[d], ru[d], u + d + kResD < ub);
           }
+          s += kResD;
         }
-        wave_sync();
-        const int rr = lane & 15, ti = lane >> 4;            // item = (row rr, pair ti), ti < kResGroup
-        int64_t sm[4] = {0, 0, 0, 0};
-        int tok = 0;
-        if (ti < count) {
-          tok = s_pairs[ti] / a.K;
-          const int32_t* gd = eg + rr * C + tok * 6;
-          const int32_t* ud = eu + rr * C + tok * 6;
-          sm[0] = (int64_t)gd[0] + ((int64_t)gd[1] << 8) + ((int64_t)gd[2] << 16);
-          sm[1] = (int64_t)gd[3] + ((int64_t)gd[4] << 8) + ((int64_t)gd[5] << 16);
-          sm[2] = (int64_t)ud[0] + ((int64_t)ud[1] << 8) + ((int64_t)ud[2] << 16);
-          sm[3] = (int64_t)ud[3] + ((int64_t)ud[4] << 8) + ((int64_t)ud[5] << 16);
-        }
-        wave_sync();
+        const int se = s;                                     // portion covers steps [sa, se)
 
+        int64_t gq[NT], uq[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          gq[n] = quad_row_sum(accg[n]);
+          uq[n] = quad_row_sum(accu[n]);
+        }
         bool finish = (sa == 0 && se == S);
         if (!finish) {
-          // contributors of this tile: waves whose ranges meet its units
+          // contributors of this tile: ranges that meet its units, by position
           const int tu0 = (tile - t0) * S, tu1 = tu0 + S;
           int first = -1, ncontrib = 0;
-          for (int q = 0; q < kResWaves; ++q) {
-            const int qa = bound(q), qb = (q + 1 == kResWaves) ? nunits : bound(q + 1);
+          for (int k = 0; k < kResWaves; ++k) {
+            const int qa = s_bound[k], qb = s_bound[k + 1];
             if (qa < qb && qa < tu1 && qb > tu0) {
-              if (first < 0) first = q;
+              if (first < 0) first = k;
               ++ncontrib;
             }
           }
-          unsigned long long* slotp = s_fix[first];
-          if (lane < kResItems && ti < count) {
+          // first < kResFixSlots: the last range ends on a tile end
+          unsigned long long* fx = s_fix + first * res_fix_words(NT) + lane;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) atomicAdd(&slotp[lane * 4 + j], (unsigned long long)sm[j]);
+          for (int n = 0; n < NT; ++n) {
+            atomicAdd(&fx[(2 * n) * 64], (unsigned long long)gq[n]);
+            atomicAdd(&fx[(2 * n + 1) * 64], (unsigned long long)uq[n]);
           }
           __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
           int prev = 0;
@@ -356,34 +450,92 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(4, 
           prev = __shfl(prev, 0);
           if (prev == ncontrib - 1) {
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-            if (lane < kResItems && ti < count) {
 #pragma unroll
-              for (int j = 0; j < 4; ++j) sm[j] = (int64_t)atomicAdd(&slotp[lane * 4 + j], 0ull);
+            for (int n = 0; n < NT; ++n) {
+              gq[n] = (int64_t)fx[(2 * n) * 64];
+              uq[n] = (int64_t)fx[(2 * n + 1) * 64];
             }
             finish = true;
           }
         }
-        if (finish && ti < count) {
-          const int row = tile * 16 + rr;
-          if (row < I) {
-            const int p = s_pairs[ti];
-            const int xm = s_xmax[tok];
-            const int e2 = sum_exponent(xm);
-            float gate = round_scaled(sm[1], sm[0], e2, gscale[row]);
-            float up = round_scaled(sm[3], sm[2], e2, uscale[row]);
-            if (xm >= 0x7F80) {
-              gate = __builtin_nanf("");
-              up = __builtin_nanf("");
+        if (finish) {
+          // ---- (row, token) sums, F32 rounding, SwiGLU tail, routed stores ----
+          const int row = tile * 16 + 4 * g4 + qj;
+#pragma unroll
+          for (int n = 0; n < NT; ++n) {
+            int tl;
+            int64_t ghi, glo, uhi, ulo;
+            bool lane_ok;
+            int e2off;
+            if (W == 4) {
+              // the quad holds digits 0..3 of one token
+              tl = 4 * n + (cc >> 2);
+              ghi = gq[n] >> 24;
+              glo = gq[n] & 0xFFFFFF;
+              uhi = uq[n] >> 24;
+              ulo = uq[n] & 0xFFFFFF;
+              lane_ok = true;
+              e2off = 16;
+            } else {
+              // quads [d0 d1 d2 0] and [d3 d4 d5 0]: the low half of the
+              // sum, and its high half from the next quad
+              const int64_t gx = __shfl_xor(gq[n], 4), ux = __shfl_xor(uq[n], 4);
+              tl = 2 * n + (cc >> 3);
+              glo = gq[n];
+              ghi = gx;
+              ulo = uq[n];
+              uhi = ux;
+              lane_ok = (cc & 4) == 0;
+              e2off = 0;
             }
-            const uint64_t o = (uint64_t)p * I + row;
-            a.out[o] = swiglu_tail(gate, up);
-            if (a.gate_probe) a.gate_probe[o] = gate;
-            if (a.up_probe) a.up_probe[o] = up;
+            const bool ok = lane_ok && tl < tp1 - tp0 && row < I;
+            float gate = 0.0f, up = 0.0f;
+            uint16_t ov = 0;
+            if (ok) {
+              const int xm = s_xmax[tp0 + tl];
+              const int e2 = sum_exponent(xm) + e2off;
+              gate = round_scaled(ghi, glo, e2, gscale[row]);
+              up = round_scaled(uhi, ulo, e2, uscale[row]);
+              if (xm >= 0x7F80) {
+                gate = __builtin_nanf("");
+                up = __builtin_nanf("");
+              }
+              ov = swiglu_tail_tab(gate, up, s_sig);
+            }
+            for (int q = 0; q < count; ++q) {
+              if (ok && s_ptok[q] == tl) {
+                const uint64_t o = (uint64_t)s_pairs[q] * I + row;
+                a.out[o] = ov;
+                if (a.gate_probe) a.gate_probe[o] = gate;
+                if (a.up_probe) a.up_probe[o] = up;
+              }
+            }
           }
         }
       }
       if (!more) break;
     }
+
+    // ---- next segment, or the next pass from the first segment ----
+    if (v < v1) {
+      open_segment();
+      start_ring();
+      continue;
+    }
+    if (++pass >= npass) break;
+    __syncthreads();  // every wave is done with the previous pass's digits
+    {
+      const int p0 = pass * tpp;
+      const int ntok = min(M, p0 + tpp) - p0;
+      for (int u = tid; u < ntok * S * 16; u += kResThreads) {
+        const int tl = u % ntok, w8 = u / ntok;
+        const uint4 xq = w8 < hw ? ((const uint4*)a.x)[(uint64_t)(p0 + tl) * hw + w8] : make_uint4(0, 0, 0, 0);
+        stage_unit(tl, w8, xq, etop(p0 + tl));
+      }
+    }
+    v = v0;
+    open_segment();
+    start_ring();
   }
 }
 
@@ -391,58 +543,60 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(4, 
 
 namespace {
 
-// Work-groups that fit the device at once, and how many share a CU.
-template <int D, bool VEC>
-int resident_blocks(int device, int* per_cu_out) {
-  static int cached[64] = {0}, cached_per_cu[64] = {0};
+// Share of a SIMD's units for its first wave, in 1/1024, by column tiles
+// (measured on MI355X: the first wave of a SIMD streams ~29% faster than the
+// second with one column tile and ~14% faster with two).
+constexpr int kWaveShare1 = 577;
+constexpr int kWaveShare2 = 547;
+
+// Work-groups that fit the device at once (one per CU: the LDS arrays take
+// most of a CU's 160 KiB).
+template <int NT, bool VEC>
+int resident_blocks(int device) {
+  static int cached[64] = {0};
   if (device < 0 || device >= 64) device = 0;
   if (!cached[device]) {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0)
       cus = 256;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&resident_kernel<D, VEC>), kResThreads, 0) != hipSuccess ||
+            &per_cu, reinterpret_cast<const void*>(&resident_kernel<NT, VEC>), kResThreads, 0) != hipSuccess ||
         per_cu <= 0)
       per_cu = 1;
-    cached_per_cu[device] = per_cu;
     cached[device] = cus * per_cu;
   }
-  *per_cu_out = cached_per_cu[device];
   return cached[device];
 }
 
-// Share of a CU pair's tiles for the first-dispatched work-group, in 1/1024
-// (measured on MI355X: with equal shares the first-dispatched work-groups
-// finish at about 0.86 of the time of the second ones).
-constexpr int kPairShare = 650;
-
-constexpr int kResD = 2;
+template <int NT, bool VEC>
+hipError_t launch_resident_t(GateUpParams& p, hipStream_t stream) {
+  int device = 0;
+  if (hipGetDevice(&device) != hipSuccess) device = 0;
+  const int tiles = p.num_slots * ((p.I + 15) / 16);
+  int nb = resident_blocks<NT, VEC>(device);
+  if (nb > tiles) nb = tiles;
+  void* args[] = {&p};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&resident_kernel<NT, VEC>), dim3((unsigned)nb),
+                         dim3(kResThreads), args, 0, stream);
+}
 
 }  // namespace
 
 bool resident_fits(int M, int H) {
-  const int steps = ((H + 127) / 128 + kResD - 1) / kResD * kResD;
-  return M >= 1 && M <= 2 && (size_t)block_stride(6 * M) * 8 * steps <= (size_t)kResBBytes &&
-         (int64_t)M * (H / 8) <= (int64_t)kResXRegs * kResThreads;
+  if (M < 1 || M > kResMaxTokens) return false;
+  const int nt = res_tiles(M);
+  return (int64_t)M * (H / 8) <= (int64_t)kResXRegs * kResThreads &&
+         (int64_t)res_steps(H) * res_step_bytes(nt) + (int64_t)kResFixSlots * res_fix_words(nt) * 8 <=
+             (int64_t)kResLds;
 }
 
 hipError_t launch_resident(GateUpParams p, hipStream_t stream) {
-  p.steps = ((p.H + 127) / 128 + kResD - 1) / kResD * kResD;
-  p.G = kResGroup;
-  int device = 0;
-  if (hipGetDevice(&device) != hipSuccess) device = 0;
+  p.steps = res_steps(p.H);
+  p.G = kResMaxPairs;
+  p.wave_share = res_tiles(p.M) == 1 ? kWaveShare1 : kWaveShare2;
   const bool vec = (p.H % 32) == 0;
-  const int tiles = p.num_slots * ((p.I + 15) / 16);
-  int per_cu = 1;
-  int nb = vec ? resident_blocks<kResD, true>(device, &per_cu) : resident_blocks<kResD, false>(device, &per_cu);
-  // uneven CU-pair shares only for a full grid of two work-groups per CU,
-  // each with several tiles
-  p.pair_share = (per_cu == 2 && tiles >= 8 * nb) ? kPairShare : 0;
-  if (nb > tiles) nb = tiles;
-  void* args[] = {&p};
-  const void* fn = vec ? reinterpret_cast<const void*>(&resident_kernel<kResD, true>)
-                       : reinterpret_cast<const void*>(&resident_kernel<kResD, false>);
-  return hipLaunchKernel(fn, dim3((unsigned)nb), dim3(kResThreads), args, 0, stream);
+  if (res_tiles(p.M) == 1) return vec ? launch_resident_t<1, true>(p, stream) : launch_resident_t<1, false>(p, stream);
+  return vec ? launch_resident_t<2, true>(p, stream) : launch_resident_t<2, false>(p, stream);
 }
 
 hipError_t launch_gate_up(const GateUpParams& p, int tokens_per_slot, hipStream_t stream) {

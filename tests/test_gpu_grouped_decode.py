@@ -85,6 +85,10 @@ CASES = [
     (700, 1, 700, 256, 16, "perm"),      # one tile per slot, more tiles than work-groups
     (1, 2, 1, 4096, 1536, "perm"),       # one slot, both tokens
     (1500, 1, 40, 256, 32, "topk"),      # a large pool, few routed slots
+    (64, 8, 8, 1024, 200, "topk"),       # verify width: two column tiles, sparse slots
+    (16, 5, 16, 512, 64, "perm"),        # five tokens on every slot
+    (300, 8, 300, 256, 16, "perm"),      # 2400 pairs: routing windows past the id registers
+    (3, 3, 3, 4096, 48, "perm"),         # three tokens, three slots
 ]
 
 
@@ -113,6 +117,21 @@ def test_decode_duplicates_and_invalid_ids():
                     [3, 3, 3, E, 0]], np.int32)
     say("[decode duplicates and invalid ids]")
     _check(slots, lay, x, ids, H, I, "decode duplicates and invalid ids")
+
+
+def test_verify_width_many_pairs_on_one_slot():
+    """Eight tokens each routed several times to one slot: more pairs than one
+    pass over the slot finishes, duplicates, and an unrouted slot."""
+    E, M, K, H, I = 3, 8, 5, 2048, 96
+    rng = np.random.default_rng(515)
+    lay, slots = _pool(rng, E, H, I)
+    x = synth.bf16_normal(rng, (M, H))
+    ids = np.full((M, K), 1, np.int32)
+    ids[:, 4] = 0
+    ids[2, 1] = 0
+    ids[5, 3] = -7
+    say("[verify width, many pairs on one slot]")
+    _check(slots, lay, x, ids, H, I, "verify width many pairs")
 
 
 def test_decode_workspace_reuse():

@@ -222,19 +222,31 @@ def test_determinism_and_batch_invariance():
     assert np.array_equal(og[:, 0], o1) and np.array_equal(gg[:, 0].view(np.uint32), g1.view(np.uint32))
 
 
-@pytest.mark.parametrize("H,I,M,wide", [(7168, 96, 8, False), (4096, 80, 8, True), (1024, 48, 5, False)])
+DIGIT_PATHS = [
+    (7168, 96, 8, False),   # batch kernel, three column tiles, K-chunks, four digits
+    (7168, 64, 4, True),    # batch kernel, two column tiles, six digits
+    (8832, 40, 2, False),   # batch kernel, one column tile (too long for resident digits)
+    (4096, 80, 8, True),    # resident digits, two column tiles, six digits: two passes
+    (2048, 40, 4, True),    # resident, two column tiles, six digits, one pass
+    (1024, 48, 5, False),   # resident, two column tiles, four digits
+    (2048, 40, 2, True),    # resident, one column tile, six digits
+]
+
+
+@pytest.mark.parametrize("H,I,M,wide", DIGIT_PATHS)
 def test_digit_count_paths(H, I, M, wide):
-    """Token groups split into four digits per value (all values within 22
-    binades of their token's largest), in K-chunks (H=7168) or resident
-    (H <= 4608), and a group sent back to six digits by one token whose values
-    span more binades."""
+    """Calls whose tokens all have their values within 22 binades of the
+    token's largest (four digits per value) and calls sent back to six digits
+    by one token whose values span more binades, through every kernel and
+    column-tile count that the width and H select."""
     rng = np.random.default_rng(H + I + M + int(wide))
     lay = synth.contiguous_layout(H, I)
     slot = synth.fill_slot(rng, H, I, lay)
     x = synth.bf16_normal(rng, (M, H))
     if wide:
-        x[3, 5] = 0x461C                                 # 9984
-        x[3, 6] = 0x3300                                 # 2^-25: 38 binades below it
+        t = min(3, M - 1)
+        x[t, 5] = 0x461C                                 # 9984
+        x[t, 6] = 0x3300                                 # 2^-25: 38 binades below it
     say(f"[digit paths H={H} I={I} M={M} wide={wide}]")
     out, g, u = run_single(slot, lay, x, H, I)
     gr, ur, orf = oracle.expert_gate_up(slot, lay, x, H, I)
