@@ -10,6 +10,10 @@ exact accumulation, scale and SwiGLU tail of every slot, in one launch.
 The headline ``value`` is algorithmic weight bytes (packed gate and up
 nibbles plus their F32 row scales) per second at M=1; the same pool at M=8
 (eight tokens on every slot, the verify width) is reported in ``m8``.
+``shapes`` repeats the measurement on the large expert shape H=7168, I=4096
+(a 37-slot pool, 1.09 GB, x with 1% of entries at +-9984) at M=1 and M=8,
+and on one routed step of 64 experts of H=6144, I=2048 (32 tokens, top-8
+routing; the bytes are those of the slots the routing touches).
 
 ``roofline`` prices the gate/up kernel against MI355X's 8 TB/s HBM peak;
 ``achieved`` is the algorithmic bytes of one launch divided by the mean
@@ -64,38 +68,79 @@ def make_pool_host():
     return lay, contents, x
 
 
-def weight_bytes_per_slot() -> int:
-    return 2 * (I * H // 2) + 2 * 4 * I
+def weight_bytes_per_slot(H_: int = H, I_: int = I) -> int:
+    return 2 * (I_ * H_ // 2) + 2 * 4 * I_
+
+
+def kernel_label(M: int, H_: int) -> str:
+    """The gate/up kernel the library launches for a call of M tokens (the
+    selection rule of q4moe_resident.hip: resident digits for up to eight
+    tokens when their digits fit LDS, else the K-chunked batch kernel)."""
+    nt = 1 if M <= 2 else 2
+    steps = ((H_ + 127) // 128 + 3) // 4 * 4
+    fits = M <= 8 and M * (H_ // 8) <= 8 * 512 and steps * 2048 * nt + 7 * nt * 1024 <= 150 * 1024
+    return "q4::resident_kernel" if fits else "q4::batch_kernel"
+
+
+LARGE_H, LARGE_I, LARGE_SLOTS = 7168, 4096, 37
+ROUTED_SLOTS = 64
+
+
+def large_shape_pool():
+    """The large expert shape (H=7168, I=4096): its seeded slot (1% all-8 rows per
+    matrix) repeated over 37 slots, and 8 tokens of N(0,1) bf16 with 1% of
+    entries at +-9984 (x drawn as for M=8 from seed 105+8)."""
+    import synth
+    c = synth.make_config("cfg5", M=8)
+    return c.layout, c.slots[:1], c.x
+
+
+def routed_step_config():
+    import synth
+    return synth.make_config("cfg4")
 
 
 class Pool:
-    def __init__(self, lay, contents, x8):
+    """``nslots`` device slots of one shape, filled round-robin from ``contents``."""
+
+    def __init__(self, lay, contents, x8, nslots: int = POOL_SLOTS, H_: int = H, I_: int = I):
         import torch
         from quantized_moe_expert_q4_amd.device import aligned_empty, upload_bf16_bits
         self.torch = torch
         self.lay = lay
+        self.H, self.I, self.nslots = H_, I_, nslots
         self.stride = lay.slot_bytes
-        self.slots = aligned_empty(POOL_SLOTS * self.stride)
-        dev_contents = torch.from_numpy(contents).cuda()
-        for s in range(POOL_SLOTS):
-            self.slots[s * self.stride:(s + 1) * self.stride].copy_(dev_contents[s % DISTINCT_CONTENTS])
-        del dev_contents
+        self.slots = aligned_empty(nslots * self.stride)
+        for d in range(contents.shape[0]):
+            dev = torch.from_numpy(contents[d]).cuda()
+            for s in range(d, nslots, contents.shape[0]):
+                self.slots[s * self.stride:(s + 1) * self.stride].copy_(dev)
+            del dev
         self.x8 = upload_bf16_bits(x8)
         torch.cuda.synchronize()
 
+    def bytes_per_step(self) -> int:
+        return self.nslots * weight_bytes_per_slot(self.H, self.I)
+
     def step_fn(self, M: int):
+        """One grouped call routing each of M tokens to every slot."""
+        n = self.nslots
+        ids = self.torch.arange(n, dtype=self.torch.int32, device="cuda").repeat(M, 1).contiguous()
+        return self.routed_fn(M, ids)
+
+    def routed_fn(self, M: int, ids):
         import quantized_moe_expert_q4_amd as q4
         torch = self.torch
         from quantized_moe_expert_q4_amd.device import aligned_empty
         x = self.x8[:M].contiguous()
-        ids = torch.arange(POOL_SLOTS, dtype=torch.int32, device="cuda").repeat(M, 1).contiguous()
-        out = torch.empty((M, POOL_SLOTS, I), dtype=torch.bfloat16, device="cuda")
-        wsb = q4.grouped_workspace_bytes(M, POOL_SLOTS, H, I, POOL_SLOTS)
+        K = ids.shape[1]
+        out = torch.empty((M, K, self.I), dtype=torch.bfloat16, device="cuda")
+        wsb = q4.grouped_workspace_bytes(M, K, self.H, self.I, self.nslots)
         ws = aligned_empty(wsb, 256)
         stream = torch.cuda.current_stream()
 
         def step():
-            q4.expert_gate_up_grouped(self.slots, self.stride, POOL_SLOTS, self.lay, x, M, ids, POOL_SLOTS, H, I,
+            q4.expert_gate_up_grouped(self.slots, self.stride, self.nslots, self.lay, x, M, ids, K, self.H, self.I,
                                       out, ws, wsb, stream=stream)
         return step, stream
 
@@ -182,7 +227,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--only", choices=["m1", "m8", "single", "copy"], default=None,
+    ap.add_argument("--no-shapes", action="store_true", help="skip the large-shape and routed-step legs")
+    ap.add_argument("--only", choices=["m1", "m8", "single", "large_m1", "large_m8", "routed", "copy"], default=None,
                     help="run one leg only (for profiling); 'copy' times a plain 1 GiB device copy, "
                          "the reference for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE to bytes")
     args = ap.parse_args()
@@ -208,12 +254,15 @@ def main():
         return
 
     lay, contents, x8 = make_pool_host()
-    pool = Pool(lay, contents, x8)
     bytes_step = POOL_SLOTS * weight_bytes_per_slot()
 
     res = {}
-    legs = [args.only] if args.only else ["m1", "m8", "single"]
-    for leg in legs:
+    if args.only:
+        legs = [args.only]
+    else:
+        legs = ["m1", "m8", "single"] + ([] if args.no_shapes else ["large_m1", "large_m8", "routed"])
+    pool = Pool(lay, contents, x8) if any(l in ("m1", "m8", "single") for l in legs) else None
+    for leg in [l for l in legs if l in ("m1", "m8", "single")]:
         if leg == "single":
             step, stream = pool.single_fn()
             steps = max(1, args.steps // 5)
@@ -222,9 +271,52 @@ def main():
             steps = args.steps
         t, wall = time_steps(step, stream, steps, args.warmup)
         res[leg] = dict(seconds=t, wall=wall, steps=steps)
+    if pool is not None:
+        del pool
+        torch.cuda.empty_cache()
+    shapes = {}
+    if any(l in ("large_m1", "large_m8") for l in legs):
+        llay, lcontents, lx8 = large_shape_pool()
+        lpool = Pool(llay, lcontents, lx8, LARGE_SLOTS, LARGE_H, LARGE_I)
+        for leg in [l for l in legs if l in ("large_m1", "large_m8")]:
+            M = 1 if leg == "large_m1" else 8
+            step, stream = lpool.step_fn(M)
+            t, _ = time_steps(step, stream, args.steps, args.warmup)
+            sps = t / args.steps
+            v = lpool.bytes_per_step() / sps / 1e9
+            shapes[f"large_pool_m{M}"] = {
+                "value": round(v, 2), "unit": "GB/s", "pct_hbm_peak": round(100 * v / HBM_PEAK_GBS, 2),
+                "ms_per_step": round(sps * 1e3, 4), "rows_per_s": round(M * LARGE_SLOTS * LARGE_I / sps, 1),
+                "workload": f"H={LARGE_H} I={LARGE_I}, M={M}, {LARGE_SLOTS}-slot cold pool "
+                            f"({lpool.bytes_per_step() / 1e9:.3f} GB per step), one grouped launch per step",
+                "kernel": kernel_label(M, LARGE_H)}
+        del lpool
+        torch.cuda.empty_cache()
+    if "routed" in legs:
+        c = routed_step_config()
+        rpool = Pool(c.layout, c.slots, c.x, c.num_slots, c.H, c.I)
+        ids = torch.from_numpy(c.ids).cuda()
+        step, stream = rpool.routed_fn(c.M, ids)
+        t, _ = time_steps(step, stream, args.steps, args.warmup)
+        sps = t / args.steps
+        touched = len(np.unique(c.ids))
+        nbytes = touched * weight_bytes_per_slot(c.H, c.I)
+        v = nbytes / sps / 1e9
+        shapes["routed_step_m32_top8"] = {
+            "value": round(v, 2), "unit": "GB/s", "pct_hbm_peak": round(100 * v / HBM_PEAK_GBS, 2),
+            "ms_per_step": round(sps * 1e3, 4), "rows_per_s": round(c.M * c.K * c.I / sps, 1),
+            "workload": f"{c.num_slots} experts of H={c.H} I={c.I}, M={c.M} tokens, top-{c.K} routing "
+                        f"({touched} slots touched, {nbytes / 1e9:.3f} GB per step), one grouped launch per step",
+            "kernel": kernel_label(c.M, c.H)}
+        del rpool
+        torch.cuda.empty_cache()
 
     out = {}
-    primary = "m1" if "m1" in res else legs[0]
+    if not any(l in res for l in ("m1", "m8")):
+        # shape legs only (profiling runs)
+        print(json.dumps({"shapes": shapes}), flush=True)
+        return
+    primary = "m1" if "m1" in res else "m8"
     r = res[primary]
     sec_per_step = r["seconds"] / r["steps"]
     value = bytes_step / sec_per_step / 1e9
@@ -267,8 +359,10 @@ def main():
     out["roofline"] = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                        "traffic_detail": traffic_detail,
-                       "kernel": ("q4::resident_kernel" if M <= 2 else "q4::batch_kernel") + " (grouped call, M=%d)" % M,
+                       "kernel": kernel_label(M, H) + " (grouped call, M=%d)" % M,
                        "algorithmic_bytes_per_launch": bytes_step}
+    if shapes:
+        out["shapes"] = shapes
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(lay, contents, x8, args.cpu_budget)
     else:

@@ -60,7 +60,9 @@ __host__ __device__ inline int bat_chunk_steps(int ntiles, int S) {
 template <int NT, bool VEC>
 __global__ __launch_bounds__(kBatThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void batch_kernel(const GateUpParams a) {
-  constexpr int G = (16 * NT) / 6;
+  // pairs per token group: up to 16*NT/4 (four digits), trimmed to 16*NT/6
+  // once the group's tokens turn out to need six
+  constexpr int G = (16 * NT) / 4;
   __shared__ __attribute__((aligned(16))) uint8_t s_buf[2 * kBatBuf];  // two digit buffers, or one spanning both
   __shared__ int s_pairs[G];
   __shared__ int s_xmax[G];
@@ -164,8 +166,6 @@ void batch_kernel(const GateUpParams a) {
         count = min(found, G);
       }
       if (count <= 0) break;
-      next_pair = s_pairs[count - 1] + 1;
-      if (grouped && more) idv = (next_pair + tid < P) ? a.ids[next_pair + tid] : -1;
       const int nbatch = (t1 - t0 + kBatWaves - 1) / kBatWaves;
 
       const int nxu = count * (H / 8);                 // 16-byte units of x, token-major
@@ -225,6 +225,12 @@ void batch_kernel(const GateUpParams a) {
       int L = 4;
       for (int ti = 0; ti < count; ++ti) L = max(L, digits_for(s_xmax[ti], s_xmin[ti]));
       L = __builtin_amdgcn_readfirstlane(L);
+      if (L == 6 && count > (16 * NT) / 6) {
+        count = (16 * NT) / 6;                         // the rest go to the next group
+        more = 1;
+      }
+      next_pair = s_pairs[count - 1] + 1;
+      if (grouped && more) idv = (next_pair + tid < P) ? a.ids[next_pair + tid] : -1;
       const int C = L * count;
       const int ntiles = (C + 15) >> 4;
       const int sb = bat_step_bytes(ntiles);
@@ -366,7 +372,8 @@ void batch_kernel(const GateUpParams a) {
           int32_t* ep = (int32_t*)half(nch == 1 ? 1 : gch - 1) + wave * (16 * kEpStride);
           if (active) {
             // gate first, then up, through the same 16 x C matrix
-            float gv[2];
+            constexpr int kItemRounds = (16 * G + 63) / 64;   // (row, token) items per lane
+            float gv[kItemRounds];
 #pragma unroll
             for (int part = 0; part < 2; ++part) {
 #pragma unroll
@@ -379,7 +386,7 @@ void batch_kernel(const GateUpParams a) {
               }
               wave_sync();
 #pragma unroll
-              for (int j = 0; j < 2; ++j) {
+              for (int j = 0; j < kItemRounds; ++j) {
                 const int item = lane + 64 * j;
                 const int rr = item & 15, ti = item >> 4;
                 const int row = tile * 16 + rr;
@@ -451,7 +458,7 @@ hipError_t launch_batch(GateUpParams p, int tokens_per_slot, hipStream_t stream)
   p.steps = (p.H + 127) / 128;
   p.steps += p.steps & 1;
   const int nt = tokens_per_slot <= 2 ? 1 : (tokens_per_slot <= 5 ? 2 : 3);
-  p.G = (16 * nt) / 6;
+  p.G = (16 * nt) / 4;
   const bool vec = (p.H % 32) == 0;
   if (nt == 1) return vec ? launch_batch_t<1, true>(p, stream) : launch_batch_t<1, false>(p, stream);
   if (nt == 2) return vec ? launch_batch_t<2, true>(p, stream) : launch_batch_t<2, false>(p, stream);
