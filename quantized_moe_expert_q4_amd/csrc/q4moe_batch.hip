@@ -244,9 +244,24 @@ void batch_kernel(const GateUpParams a) {
 
       // digits of 8 consecutive K values (unit w8 of a chunk) of token ti
       auto stage_unit = [&](uint8_t* buf, int ti, int w8, const uint4 xq) {
-        uint32_t lo[8], hi[8];
-        x8_digits(xq, max((s_xmax[ti] >> 7) & 0xFF, 1) + 8 * (6 - L), lo, hi);
+        const int etop1 = max((s_xmax[ti] >> 7) & 0xFF, 1);
         const int tl = w8 >> 4, gg = (w8 >> 2) & 3, i = w8 & 3;
+        if (L == 4) {
+          uint32_t d[2][4];
+          x8_digits4(xq, etop1, d);
+#pragma unroll
+          for (int par = 0; par < 2; ++par) {
+            uint8_t* base = buf + tl * sb + par * ntiles * 1024 + gg * 256 + 4 * i;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+              const int col = ti * 4 + s;
+              *(uint32_t*)(base + (col >> 4) * 1024 + (col & 15) * 16) = d[par][s];
+            }
+          }
+          return;
+        }
+        uint32_t lo[8], hi[8];
+        x8_digits(xq, etop1, lo, hi);
 #pragma unroll
         for (int par = 0; par < 2; ++par) {
           uint32_t d[6];
@@ -254,8 +269,8 @@ void batch_kernel(const GateUpParams a) {
           uint8_t* base = buf + tl * sb + par * ntiles * 1024 + gg * 256 + 4 * i;
 #pragma unroll
           for (int s = 0; s < 6; ++s) {
-            const int col = ti * L + s;
-            if (s < L) *(uint32_t*)(base + (col >> 4) * 1024 + (col & 15) * 16) = d[s];
+            const int col = ti * 6 + s;
+            *(uint32_t*)(base + (col >> 4) * 1024 + (col & 15) * 16) = d[s];
           }
         }
       };
