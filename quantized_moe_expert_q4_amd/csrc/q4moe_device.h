@@ -79,6 +79,28 @@ __device__ float round_scaled(int64_t hi, int64_t lo, int e2, float s) {
   return r;
 }
 
+// Round V * 2^e2 * s to F32 once (nearest, ties to even) for |V| < 2^53,
+// where V converts to double exactly.  The double product is rounded to odd
+// (truncated toward zero, lowest bit set when inexact; the error term of one
+// FMA says which), then scaled and rounded to F32: rounding to odd at 53 >=
+// 24 + 2 bits followed by rounding to nearest gives the correctly rounded
+// result (Boldo and Melquiond, "Emulation of FMA and correctly rounded sums:
+// proved algorithms using rounding to odd", IEEE TC 2008), for normal and
+// subnormal F32 results alike.  Same value as round_scaled(V >> 24, V & 0xFFFFFF, e2, s).
+__device__ __forceinline__ float round_scaled53(int64_t V, int e2, float s) {
+#pragma clang fp contract(off)
+  const double v = (double)V;
+  const double sd = (double)s;
+  double P = v * sd;
+  const double err = __builtin_fma(v, sd, -P);  // v*sd == P + err exactly
+  if (err != 0.0 && __builtin_isfinite(P)) {
+    uint64_t b = (uint64_t)__double_as_longlong(P);
+    if ((err < 0.0) != (P < 0.0)) b -= 1;       // P was rounded away from zero: step back toward it
+    P = __longlong_as_double((long long)(b | 1u));
+  }
+  return (float)__builtin_ldexp(P, e2);
+}
+
 // bf16 sigmoid of the lane-0 tail of GATE_UP_SOURCE for a bf16 gate gT:
 // exp(-gT) evaluated in double and rounded once to F32, then 1 + e and 1 / d
 // in F32, rounded to bf16.
@@ -130,6 +152,17 @@ __device__ __forceinline__ uint16_t swiglu_tail_tab(float gate, float up, const 
   const float sT = bf16_val(sb);
   const float siluT = bf16_val(bf16_rne(gT * sT));
   return bf16_rne(siluT * uT);
+}
+
+// The value held by lane l ^ 1 (or l ^ 2) of the same lane quad, through a
+// DPP quad permute (no LDS round trip).
+template <int X>
+__device__ __forceinline__ int64_t quad_xor(int64_t v) {
+  static_assert(X == 1 || X == 2, "quad lane xor");
+  constexpr int ctrl = X == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, ctrl, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)((uint64_t)v >> 32), ctrl, 0xF, 0xF, false);
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
 
 // Orders one wave's LDS stores before its later LDS loads from other lanes

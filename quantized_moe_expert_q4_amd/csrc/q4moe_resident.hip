@@ -302,9 +302,9 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
     const int64_t w0 = (int64_t)acc[0] << (8 * qj), w1 = (int64_t)acc[1] << (8 * qj);
     const int64_t w2 = (int64_t)acc[2] << (8 * qj), w3 = (int64_t)acc[3] << (8 * qj);
     const bool up2 = (qj & 2) != 0;
-    const int64_t r0 = __shfl_xor(up2 ? w0 : w2, 2), r1 = __shfl_xor(up2 ? w1 : w3, 2);
+    const int64_t r0 = quad_xor<2>(up2 ? w0 : w2), r1 = quad_xor<2>(up2 ? w1 : w3);
     const int64_t k0 = (up2 ? w2 : w0) + r0, k1 = (up2 ? w3 : w1) + r1;  // rows (qj&2), (qj&2)+1
-    const int64_t r = __shfl_xor((qj & 1) ? k0 : k1, 1);
+    const int64_t r = quad_xor<1>((qj & 1) ? k0 : k1);
     return ((qj & 1) ? k1 : k0) + r;
   };
   // this lane's B-fragment chunk for steps 0..3 mod 4
@@ -319,6 +319,15 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
     const int pend = tp1 * K;                               // end pair
     int next_pair = tp0 * K;
     bool first_group = true;
+    // the pass token of this lane's quad in each column tile, and its exponent
+    int ltok[NT], lxm[NT];
+    bool lok[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      ltok[n] = W == 4 ? 4 * n + (cc >> 2) : 2 * n + (cc >> 3);
+      lok[n] = (W == 4 || (cc & 4) == 0) && ltok[n] < tp1 - tp0;
+      lxm[n] = lok[n] ? s_xmax[tp0 + ltok[n]] : 0;
+    }
     for (;;) {
       __syncthreads();  // previous group done with the fix-up slots, s_bound and s_pairs; digits visible
       if (tid < kResFixSlots) s_fixcnt[tid] = 0;
@@ -377,6 +386,25 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
       }
       if (count <= 0) break;
       next_pair = s_pairs[count - 1] + 1;
+      // the group's pairs and their pass tokens, uniform: held in scalar registers
+      int gpair[kResMaxPairs], gtok[kResMaxPairs];
+#pragma unroll
+      for (int q = 0; q < kResMaxPairs; ++q) {
+        gpair[q] = __builtin_amdgcn_readfirstlane(q < count ? s_pairs[q] : 0);
+        gtok[q] = __builtin_amdgcn_readfirstlane(q < count ? s_ptok[q] : -1);
+      }
+      // the pair of this lane's token in each column tile when it has exactly
+      // one in the group (-1: none); several pairs of one token take the loop
+      int mypair[NT];
+      bool multi = false;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        int mp = -1;
+        for (int q = 0; q < count; ++q)
+          if (gtok[q] == ltok[n]) mp = mp < 0 ? gpair[q] : -2;
+        mypair[n] = mp;
+        multi = multi || __ballot(lok[n] && mp == -2) != 0;
+      }
       if (!first_group) start_ring();
       first_group = false;
 
@@ -386,6 +414,12 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
         const int tile = t0 + u / S;
         const int sa = u % S;
         const int pe = min(ub, (u / S + 1) * S);              // portion end (unit)
+        // the row scales this lane may finish with, loaded ahead of the
+        // portion's weight loads: loads complete in order, so a scale load
+        // issued at the finish would wait for every weight load in flight
+        const int row = tile * 16 + 4 * g4 + qj;
+        const float gsc = gscale[min(row, I - 1)], usc = uscale[min(row, I - 1)];
+        float gscr = 0.0f, uscr = 0.0f;
         v4i accg[NT], accu[NT];
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
@@ -399,6 +433,8 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
             v4i ge, go, ue, uo;
             split_weights(rg[d], ge, go);
             split_weights(ru[d], ue, uo);
+            // the slot's registers are free once split: refill it before the multiply
+            issue(rg[d], ru[d], u + d + kResD < ub);
             const uint8_t* bp = s_lds + (s + d) * sbytes + rdo[d & 3];
             v4i be[NT], bo[NT];
 #pragma unroll
@@ -413,9 +449,12 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
               accg[n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(go, bo[n], accg[n], 0, 0, 0);
               accu[n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(uo, bo[n], accu[n], 0, 0, 0);
             }
-            issue(rg[d], ru[d], u + d + kResD < ub);
           }
           s += kResD;
+          // take the row scales over here, where the compiler counts the
+          // weight loads issued after them exactly (left to the finish, the
+          // wait for them covers every load in flight)
+          __asm__ volatile("v_mov_b32 %0, %2\n\tv_mov_b32 %1, %3" : "=v"(gscr), "=v"(uscr) : "v"(gsc), "v"(usc));
         }
         const int se = s;                                     // portion covers steps [sa, se)
 
@@ -460,54 +499,62 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
         }
         if (finish) {
           // ---- (row, token) sums, F32 rounding, SwiGLU tail, routed stores ----
-          const int row = tile * 16 + 4 * g4 + qj;
 #pragma unroll
           for (int n = 0; n < NT; ++n) {
-            int tl;
+            const int tl = ltok[n];
             int64_t ghi, glo, uhi, ulo;
-            bool lane_ok;
             int e2off;
             if (W == 4) {
               // the quad holds digits 0..3 of one token
-              tl = 4 * n + (cc >> 2);
               ghi = gq[n] >> 24;
               glo = gq[n] & 0xFFFFFF;
               uhi = uq[n] >> 24;
               ulo = uq[n] & 0xFFFFFF;
-              lane_ok = true;
               e2off = 16;
             } else {
               // quads [d0 d1 d2 0] and [d3 d4 d5 0]: the low half of the
               // sum, and its high half from the next quad
               const int64_t gx = __shfl_xor(gq[n], 4), ux = __shfl_xor(uq[n], 4);
-              tl = 2 * n + (cc >> 3);
               glo = gq[n];
               ghi = gx;
               ulo = uq[n];
               uhi = ux;
-              lane_ok = (cc & 4) == 0;
               e2off = 0;
             }
-            const bool ok = lane_ok && tl < tp1 - tp0 && row < I;
+            const bool ok = lok[n] && row < I;
             float gate = 0.0f, up = 0.0f;
             uint16_t ov = 0;
             if (ok) {
-              const int xm = s_xmax[tp0 + tl];
+              const int xm = lxm[n];
               const int e2 = sum_exponent(xm) + e2off;
-              gate = round_scaled(ghi, glo, e2, gscale[row]);
-              up = round_scaled(uhi, ulo, e2, uscale[row]);
+              if (W == 4) {
+                gate = round_scaled53(gq[n], e2, gscr);
+                up = round_scaled53(uq[n], e2, uscr);
+              } else {
+                gate = round_scaled(ghi, glo, e2, gscr);
+                up = round_scaled(uhi, ulo, e2, uscr);
+              }
               if (xm >= 0x7F80) {
                 gate = __builtin_nanf("");
                 up = __builtin_nanf("");
               }
               ov = swiglu_tail_tab(gate, up, s_sig);
             }
-            for (int q = 0; q < count; ++q) {
-              if (ok && s_ptok[q] == tl) {
-                const uint64_t o = (uint64_t)s_pairs[q] * I + row;
+            if (!multi) {
+              if (ok && mypair[n] >= 0) {
+                const uint64_t o = (uint64_t)mypair[n] * I + row;
                 a.out[o] = ov;
                 if (a.gate_probe) a.gate_probe[o] = gate;
                 if (a.up_probe) a.up_probe[o] = up;
+              }
+            } else {
+              for (int q = 0; q < count; ++q) {
+                if (ok && gtok[q] == tl) {
+                  const uint64_t o = (uint64_t)gpair[q] * I + row;
+                  a.out[o] = ov;
+                  if (a.gate_probe) a.gate_probe[o] = gate;
+                  if (a.up_probe) a.up_probe[o] = up;
+                }
               }
             }
           }
