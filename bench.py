@@ -95,6 +95,26 @@ def large_shape_pool():
     return c.layout, c.slots[:1], c.x
 
 
+EXPERT_SLOTS = 114
+
+
+def expert_pool_host():
+    """Whole-expert slots of the decode shape (gate, up and down fields):
+    eight seeded contents, repeated over a 114-slot pool (1.08 GB)."""
+    import synth
+    lay = synth.expert_layout(H, I)
+    rng = np.random.default_rng(SEED + 1000)
+    contents = np.zeros((DISTINCT_CONTENTS, lay.slot_bytes), np.uint8)
+    for d in range(DISTINCT_CONTENTS):
+        synth.fill_slot(rng, H, I, lay, out=contents[d])
+    x = synth.bf16_normal(rng, (8, H))
+    return lay, contents, x
+
+
+def down_bytes_per_slot(H_: int = H, I_: int = I) -> int:
+    return H_ * I_ // 2 + 4 * H_
+
+
 def routed_step_config():
     import synth
     return synth.make_config("cfg4")
@@ -142,6 +162,48 @@ class Pool:
         def step():
             q4.expert_gate_up_grouped(self.slots, self.stride, self.nslots, self.lay, x, M, ids, K, self.H, self.I,
                                       out, ws, wsb, stream=stream)
+        return step, stream
+
+    def down_fn(self):
+        """One grouped down call: the token's own mid row on every slot, the
+        mid rows being the gate/up + SwiGLU output of that token on each slot
+        (one grouped gate/up call, made once before timing)."""
+        import quantized_moe_expert_q4_amd as q4
+        torch = self.torch
+        from quantized_moe_expert_q4_amd.device import aligned_empty
+        n = self.nslots
+        ids = torch.arange(n, dtype=torch.int32, device="cuda").reshape(1, n).contiguous()
+        x = self.x8[:1].contiguous()
+        mid = torch.empty((1, n, self.I), dtype=torch.bfloat16, device="cuda")
+        out = torch.empty((1, n, self.H), dtype=torch.bfloat16, device="cuda")
+        wsb = q4.grouped_workspace_bytes(1, n, self.H, self.I, n)
+        ws = aligned_empty(wsb, 256)
+        stream = torch.cuda.current_stream()
+        q4.expert_gate_up_grouped(self.slots, self.stride, n, self.lay, x, 1, ids, n, self.H, self.I, mid, ws, wsb,
+                                  stream=stream)
+
+        def step():
+            q4.expert_down_grouped(self.slots, self.stride, n, self.lay, mid, 1, ids, n, self.H, self.I, out, ws,
+                                   wsb, stream=stream)
+        return step, stream
+
+    def forward_fn(self):
+        """One grouped whole-expert call (gate/up then down) routing the token to every slot."""
+        import quantized_moe_expert_q4_amd as q4
+        torch = self.torch
+        from quantized_moe_expert_q4_amd.device import aligned_empty
+        n = self.nslots
+        ids = torch.arange(n, dtype=torch.int32, device="cuda").reshape(1, n).contiguous()
+        x = self.x8[:1].contiguous()
+        mid = torch.empty((1, n, self.I), dtype=torch.bfloat16, device="cuda")
+        out = torch.empty((1, n, self.H), dtype=torch.bfloat16, device="cuda")
+        wsb = q4.grouped_workspace_bytes(1, n, self.H, self.I, n)
+        ws = aligned_empty(wsb, 256)
+        stream = torch.cuda.current_stream()
+
+        def step():
+            q4.expert_forward_grouped(self.slots, self.stride, n, self.lay, x, 1, ids, n, self.H, self.I, mid, out,
+                                      ws, wsb, stream=stream)
         return step, stream
 
     def single_fn(self):
@@ -228,7 +290,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-shapes", action="store_true", help="skip the large-shape and routed-step legs")
-    ap.add_argument("--only", choices=["m1", "m8", "single", "large_m1", "large_m8", "routed", "copy"], default=None,
+    ap.add_argument("--only", choices=["m1", "m8", "single", "large_m1", "large_m8", "routed", "down", "forward",
+                                       "copy"], default=None,
                     help="run one leg only (for profiling); 'copy' times a plain 1 GiB device copy, "
                          "the reference for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE to bytes")
     args = ap.parse_args()
@@ -260,7 +323,8 @@ def main():
     if args.only:
         legs = [args.only]
     else:
-        legs = ["m1", "m8", "single"] + ([] if args.no_shapes else ["large_m1", "large_m8", "routed"])
+        legs = ["m1", "m8", "single"] + ([] if args.no_shapes else ["large_m1", "large_m8", "routed", "down",
+                                                                      "forward"])
     pool = Pool(lay, contents, x8) if any(l in ("m1", "m8", "single") for l in legs) else None
     for leg in [l for l in legs if l in ("m1", "m8", "single")]:
         if leg == "single":
@@ -309,6 +373,38 @@ def main():
                         f"({touched} slots touched, {nbytes / 1e9:.3f} GB per step), one grouped launch per step",
             "kernel": kernel_label(c.M, c.H)}
         del rpool
+        torch.cuda.empty_cache()
+
+    if any(l in ("down", "forward") for l in legs):
+        elay, econtents, ex8 = expert_pool_host()
+        epool = Pool(elay, econtents, ex8, EXPERT_SLOTS, H, I)
+        if "down" in legs:
+            step, stream = epool.down_fn()
+            t, _ = time_steps(step, stream, args.steps, args.warmup)
+            sps = t / args.steps
+            nbytes = EXPERT_SLOTS * down_bytes_per_slot()
+            v = nbytes / sps / 1e9
+            shapes["down_pool_m1"] = {
+                "value": round(v, 2), "unit": "GB/s", "pct_hbm_peak": round(100 * v / HBM_PEAK_GBS, 2),
+                "ms_per_step": round(sps * 1e3, 4), "rows_per_s": round(EXPERT_SLOTS * H / sps, 1),
+                "workload": f"down projection H={H} I={I}, one token's mid row per slot on a {EXPERT_SLOTS}-slot "
+                            f"cold pool of whole-expert slots ({nbytes / 1e9:.3f} GB of down weights+scales per "
+                            f"step), one grouped launch per step",
+                "kernel": "q4::batch_kernel (down mode)"}
+        if "forward" in legs:
+            step, stream = epool.forward_fn()
+            t, _ = time_steps(step, stream, args.steps, args.warmup)
+            sps = t / args.steps
+            nbytes = EXPERT_SLOTS * (weight_bytes_per_slot() + down_bytes_per_slot())
+            v = nbytes / sps / 1e9
+            shapes["forward_pool_m1"] = {
+                "value": round(v, 2), "unit": "GB/s", "pct_hbm_peak": round(100 * v / HBM_PEAK_GBS, 2),
+                "ms_per_step": round(sps * 1e3, 4),
+                "workload": f"whole expert (gate/up+SwiGLU then down) H={H} I={I}, one token routed to every "
+                            f"slot of a {EXPERT_SLOTS}-slot cold pool ({nbytes / 1e9:.3f} GB per step), two "
+                            f"launches per step",
+                "kernel": "q4::resident_kernel then q4::batch_kernel (down mode)"}
+        del epool
         torch.cuda.empty_cache()
 
     out = {}

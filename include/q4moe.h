@@ -1,5 +1,6 @@
 /*
- * q4moe.h -- C ABI of the MI355X (gfx950) Q4 expert gate/up + SwiGLU library.
+ * q4moe.h -- C ABI of the MI355X (gfx950) Q4 expert library: gate/up +
+ * SwiGLU, the down projection and the whole expert, over expert slots.
  *
  * What is computed (diff of @mlx-bun/inference 1.0.0, page 52,
  * kernels/glm52/streamed-experts.ts, GATE_UP_SOURCE and its launch in
@@ -73,8 +74,8 @@ enum {
  * Byte offsets of an expert slot's fields from the slot base (page 51,
  * Glm52CanonicalMetalLayout).  gate/up weights: uint32 [I][H/8] little-endian,
  * 16-byte aligned offsets.  gate/up scales: float32 [I], 4-byte aligned.
- * The down fields belong to the down projection, which this library does not
- * compute; they may be Q4_OFFSET_ABSENT, otherwise they are range-checked
+ * The down fields are read by the down and whole-expert calls only; for the
+ * gate/up calls they may be Q4_OFFSET_ABSENT, otherwise they are range-checked
  * (down weights I*H/2 bytes, down scales 4*H bytes) as on page 52
  * (validateCall).
  */
@@ -159,10 +160,98 @@ int q4_validate_grouped(const void *slots_base, uint64_t slot_stride,
                         int64_t K, int64_t H, int64_t I, const void *out_bf16,
                         const void *workspace, size_t workspace_bytes);
 
+/*
+ * Down projection (page 52, DOWN_SOURCE): for every token m and hidden row h
+ *
+ *   down[m,h] = (sum_i (qd[h,i] - 8) * mid[m,i]) * down_scale[h]     (F32)
+ *   out[m,h]  = bf16(down[m,h])                                 (nearest even)
+ *
+ * qd[h,i] is nibble (i % 8) of the little-endian uint32 word (h*I/8 + i/8) of
+ * the down weights (uint32 [H][I/8] at down_weight_offset, 16-byte aligned);
+ * down scales are float32 [H] at down_scale_offset (4-byte aligned).  The sum
+ * is exact and rounded once to F32 with the scale, as for gate/up.  Needs
+ * I % 8 == 0, I <= 65536 and both down offsets present (not
+ * Q4_OFFSET_ABSENT).
+ *   mid_bf16  device, row-major [M][I], 16-byte aligned.
+ *   out_bf16  device, row-major [M][H], 2-byte aligned.
+ * Returns Q4_OK or a negative status.
+ */
+int q4_expert_down(const void *slot, const q4_slot_layout *layout,
+                   const void *mid_bf16, int64_t M, int64_t H, int64_t I,
+                   void *out_bf16, q4_stream_t stream);
+
+/* As q4_expert_down, and also writes the F32 values before their bf16
+ * rounding to down_f32 ([M][H], 4-byte aligned; NULL to skip). */
+int q4_expert_down_probe(const void *slot, const q4_slot_layout *layout,
+                         const void *mid_bf16, int64_t M, int64_t H, int64_t I,
+                         void *out_bf16, float *down_f32, q4_stream_t stream);
+
+/*
+ * Grouped down projection.  Pair (t, j) runs its own input row
+ * mid[t][j][:] (bf16 [M][K][I], the layout the grouped gate/up call writes)
+ * against slot slot_ids[t*K + j] and writes out[t][j][:] (bf16 [M][K][H]).
+ * Slots, ids and workspace as for q4_expert_gate_up_grouped (workspace size
+ * from q4_grouped_workspace_bytes(M, K, H, I, num_slots)); an id outside
+ * [0, num_slots) gives a zero output row and is counted in workspace[0].
+ * Needs M*K <= 65535.
+ */
+int q4_expert_down_grouped(const void *slots_base, uint64_t slot_stride,
+                           int64_t num_slots, const q4_slot_layout *layout,
+                           const void *mid_bf16, int64_t M,
+                           const int32_t *slot_ids, int64_t K,
+                           int64_t H, int64_t I, void *out_bf16,
+                           void *workspace, size_t workspace_bytes,
+                           q4_stream_t stream);
+
+/* As q4_expert_down_grouped with an optional F32 probe [M][K][H]. */
+int q4_expert_down_grouped_probe(const void *slots_base, uint64_t slot_stride,
+                                 int64_t num_slots, const q4_slot_layout *layout,
+                                 const void *mid_bf16, int64_t M,
+                                 const int32_t *slot_ids, int64_t K,
+                                 int64_t H, int64_t I, void *out_bf16,
+                                 float *down_f32,
+                                 void *workspace, size_t workspace_bytes,
+                                 q4_stream_t stream);
+
+/*
+ * The whole expert of one slot (page 52, Glm52CanonicalMetalExecutor.execute:
+ * the gate/up kernel, then the down kernel on its bf16 output):
+ *   mid = q4_expert_gate_up(x), out = q4_expert_down(mid).
+ *   mid_bf16  device [M][I], 16-byte aligned, caller-owned: receives the
+ *             gate/up + SwiGLU output (the library allocates nothing).
+ *   out_bf16  device [M][H].
+ * Both steps are validated before either is enqueued.
+ */
+int q4_expert_forward(const void *slot, const q4_slot_layout *layout,
+                      const void *x_bf16, int64_t M, int64_t H, int64_t I,
+                      void *mid_bf16, void *out_bf16, q4_stream_t stream);
+
+/* Grouped whole expert: q4_expert_gate_up_grouped into mid [M][K][I], then
+ * q4_expert_down_grouped into out [M][K][H] (per-pair expert outputs, before
+ * any weighting across the K experts).  One workspace serves both steps. */
+int q4_expert_forward_grouped(const void *slots_base, uint64_t slot_stride,
+                              int64_t num_slots, const q4_slot_layout *layout,
+                              const void *x_bf16, int64_t M,
+                              const int32_t *slot_ids, int64_t K,
+                              int64_t H, int64_t I, void *mid_bf16,
+                              void *out_bf16, void *workspace,
+                              size_t workspace_bytes, q4_stream_t stream);
+
+/* Host-only argument checks of the down calls (as q4_validate_gate_up). */
+int q4_validate_down(const void *slot, const q4_slot_layout *layout,
+                     const void *mid_bf16, int64_t M, int64_t H, int64_t I,
+                     const void *out_bf16);
+int q4_validate_down_grouped(const void *slots_base, uint64_t slot_stride,
+                             int64_t num_slots, const q4_slot_layout *layout,
+                             const void *mid_bf16, int64_t M,
+                             const int32_t *slot_ids, int64_t K, int64_t H,
+                             int64_t I, const void *out_bf16,
+                             const void *workspace, size_t workspace_bytes);
+
 /* Message for the last failing call on this thread ("" after success). */
 const char *q4_last_error(void);
 
-/* ABI version: 1. */
+/* ABI version: 2 (1 plus the down projection and whole-expert calls). */
 int q4_abi_version(void);
 
 #ifdef __cplusplus

@@ -1,4 +1,4 @@
-"""CPU oracle for the Q4 expert gate/up + SwiGLU path (test infrastructure only).
+"""CPU oracle for the Q4 expert path: gate/up + SwiGLU, down, whole expert (test infrastructure only).
 
 Only tests, the smoke check and the benchmark's CPU-baseline leg import this
 package.  It shares no code with the HIP path.
@@ -17,4 +17,9 @@ from .q4_oracle import (  # noqa: F401
     swiglu_tail,
     expert_gate_up,
     expert_gate_up_grouped,
+    check_down_layout,
+    expert_down,
+    expert_forward,
+    expert_down_grouped,
+    expert_forward_grouped,
 )

@@ -24,6 +24,13 @@ What it computes, and where the pages define it (pages of the diff of
   ``s = bf16(1 / (1 + exp(-g)))`` evaluated in F32, ``silu = bf16(g * s)``,
   ``out = bf16(silu * u)``.  F32 -> bf16 rounding is round to nearest even,
   the rule of the ``trellis_bf16`` helper on page 54, kernels/trellis/codebook.ts.
+* Down projection and the whole expert -- page 52, streamed-experts.ts,
+  ``DOWN_SOURCE`` and ``Glm52CanonicalMetalExecutor.execute``: the gate/up
+  kernel's bf16 output ``mid[M, I]`` is the input of the down kernel, whose row
+  ``h`` (of ``H``) holds ``I/8`` words in the same nibble order;
+  ``out[m, h] = bf16((sum_i (q_hi - 8) mid[m, i]) * down_scale[h])``, the sum
+  again taken exactly and the F32 product rounded once.  ``validateCall``
+  requires both dimensions divisible by 8 and every field inside the slot.
 * Grouped call -- row independence stated on page 52 (one launch geometry for
   every batch width; each sample and row is computed on its own): output
   ``[t, j, :]`` is the single-expert result for token ``t`` on slot
@@ -331,3 +338,86 @@ def expert_gate_up_grouped(slots: np.ndarray, slot_stride: int, num_slots: int, 
             up[t, j] = u[r]
             out[t, j] = o[r]
     return gate, up, out, invalid
+
+
+# ---------------------------------------------------------------------------
+# Down projection and the whole expert (page 52, DOWN_SOURCE and execute)
+# ---------------------------------------------------------------------------
+
+def check_down_layout(layout, H: int, I: int) -> None:
+    """validateCall's rules for a call that reads the down fields too."""
+    check_layout(layout, H, I)
+    if I % 8:
+        raise ValueError("Q4 expert dimensions must be divisible by 8")
+    if layout.down_weight_offset == OFFSET_ABSENT or layout.down_scale_offset == OFFSET_ABSENT:
+        raise ValueError("down weights exceeds the canonical expert slot")
+
+
+def expert_down(slot: np.ndarray, layout, midbits: np.ndarray, H: int, I: int):
+    """Down projection of one slot: returns ``(down f32 [M,H], out bf16 bits [M,H])``.
+
+    Row ``h`` of the down matrix is ``I/8`` words at
+    ``down_weight_offset + 4 * (h * I/8 + w)``; nibble ``p`` of word ``w`` is
+    input position ``8w + p``.  ``down = RN_f32(S_exact * down_scale[h])`` and
+    the output is its bf16 rounding (the kernel's ``T(value)``).
+    """
+    slot = np.ascontiguousarray(slot, dtype=np.uint8).reshape(-1)
+    midbits = np.ascontiguousarray(midbits, dtype=np.uint16).reshape(-1, I)
+    check_down_layout(layout, H, I)
+    if slot.size < layout.slot_bytes:
+        raise ValueError("canonical expert slot array is shorter than its layout")
+    wd = q4_weights(slot, layout.down_weight_offset, H, I)
+    sd = row_scales(slot, layout.down_scale_offset, H)
+    down = scaled_f32(*exact_dots(wd, midbits), sd)
+    return down, f32_to_bf16(down)
+
+
+def expert_forward(slot: np.ndarray, layout, xbits: np.ndarray, H: int, I: int):
+    """The whole expert of one slot, as ``execute`` chains its two kernels:
+    returns ``(mid bf16 bits [M,I], out bf16 bits [M,H])``."""
+    check_down_layout(layout, H, I)
+    _, _, mid = expert_gate_up(slot, layout, xbits, H, I)
+    _, out = expert_down(slot, layout, mid, H, I)
+    return mid, out
+
+
+def expert_down_grouped(slots: np.ndarray, slot_stride: int, num_slots: int, layout,
+                        midbits: np.ndarray, ids: np.ndarray, H: int, I: int):
+    """Grouped down projection: pair ``(t, j)`` runs its own input row
+    ``mid[t, j, :]`` against slot ``ids[t, j]`` and writes ``out[t, j, :]``.
+
+    Returns ``(down f32 [M,K,H], out bits [M,K,H], invalid_count)``; invalid
+    ids give zeros, as in the grouped gate/up call.
+    """
+    flat = np.ascontiguousarray(slots, dtype=np.uint8).reshape(-1)
+    ids = np.asarray(ids, dtype=np.int64)
+    M, K = ids.shape
+    midbits = np.ascontiguousarray(midbits, dtype=np.uint16).reshape(M, K, I)
+    down = np.zeros((M, K, H), dtype=np.float32)
+    out = np.zeros((M, K, H), dtype=np.uint16)
+    invalid = 0
+    by_slot: Dict[int, List[Tuple[int, int]]] = {}
+    for t in range(M):
+        for j in range(K):
+            e = int(ids[t, j])
+            if 0 <= e < num_slots:
+                by_slot.setdefault(e, []).append((t, j))
+            else:
+                invalid += 1
+    for e, pairs in sorted(by_slot.items()):
+        slot = flat[e * slot_stride:e * slot_stride + layout.slot_bytes]
+        rows = np.stack([midbits[t, j] for t, j in pairs])
+        d, o = expert_down(slot, layout, rows, H, I)
+        for r, (t, j) in enumerate(pairs):
+            down[t, j] = d[r]
+            out[t, j] = o[r]
+    return down, out, invalid
+
+
+def expert_forward_grouped(slots: np.ndarray, slot_stride: int, num_slots: int, layout,
+                           xbits: np.ndarray, ids: np.ndarray, H: int, I: int):
+    """Grouped whole expert: returns ``(mid bits [M,K,I], out bits [M,K,H], invalid_count)``."""
+    check_down_layout(layout, H, I)
+    _, _, mid, invalid = expert_gate_up_grouped(slots, slot_stride, num_slots, layout, xbits, ids, H, I)
+    _, out, _ = expert_down_grouped(slots, slot_stride, num_slots, layout, mid, ids, H, I)
+    return mid, out, invalid

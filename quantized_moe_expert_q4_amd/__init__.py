@@ -1,4 +1,4 @@
-"""MI355X-native Q4 expert gate/up + SwiGLU.
+"""MI355X-native Q4 expert: gate/up + SwiGLU, down projection, whole expert.
 
 The computation lives in hand-written HIP kernels for gfx950 behind the C ABI
 of ``include/q4moe.h`` (``libq4moe.so`` in this package directory).  This
@@ -24,4 +24,10 @@ from ._lib import (  # noqa: F401
     expert_gate_up_grouped,
     validate_gate_up,
     validate_grouped,
+    expert_down,
+    expert_down_grouped,
+    expert_forward,
+    expert_forward_grouped,
+    validate_down,
+    validate_down_grouped,
 )

@@ -72,6 +72,18 @@ _SIGNATURES = {
     "q4_validate_gate_up": (ctypes.c_int, [_P, _LAYOUT, _P, _I64, _I64, _I64, _P]),
     "q4_validate_grouped": (ctypes.c_int, [_P, _U64, _I64, _LAYOUT, _P, _I64, _P, _I64, _I64, _I64, _P, _P,
                                            _SZ]),
+    "q4_expert_down": (ctypes.c_int, [_P, _LAYOUT, _P, _I64, _I64, _I64, _P, _P]),
+    "q4_expert_down_probe": (ctypes.c_int, [_P, _LAYOUT, _P, _I64, _I64, _I64, _P, _P, _P]),
+    "q4_expert_down_grouped": (ctypes.c_int, [_P, _U64, _I64, _LAYOUT, _P, _I64, _P, _I64, _I64, _I64,
+                                              _P, _P, _SZ, _P]),
+    "q4_expert_down_grouped_probe": (ctypes.c_int, [_P, _U64, _I64, _LAYOUT, _P, _I64, _P, _I64, _I64, _I64,
+                                                    _P, _P, _P, _SZ, _P]),
+    "q4_expert_forward": (ctypes.c_int, [_P, _LAYOUT, _P, _I64, _I64, _I64, _P, _P, _P]),
+    "q4_expert_forward_grouped": (ctypes.c_int, [_P, _U64, _I64, _LAYOUT, _P, _I64, _P, _I64, _I64, _I64,
+                                                 _P, _P, _P, _SZ, _P]),
+    "q4_validate_down": (ctypes.c_int, [_P, _LAYOUT, _P, _I64, _I64, _I64, _P]),
+    "q4_validate_down_grouped": (ctypes.c_int, [_P, _U64, _I64, _LAYOUT, _P, _I64, _P, _I64, _I64, _I64, _P,
+                                                _P, _SZ]),
     "q4_last_error": (ctypes.c_char_p, []),
     "q4_abi_version": (ctypes.c_int, []),
 }
@@ -185,3 +197,64 @@ def validate_grouped(slots_base, slot_stride, num_slots, layout, x, M, slot_ids,
     return load().q4_validate_grouped(_ptr(slots_base), slot_stride, num_slots,
                                       None if lay is None else ctypes.byref(lay), _ptr(x), M, _ptr(slot_ids), K,
                                       H, I, _ptr(out), _ptr(workspace), workspace_bytes)
+
+
+def expert_down(slot, layout, mid, M: int, H: int, I: int, out, down_probe=None, stream=None) -> None:
+    """Enqueue the down projection of one slot (see q4_expert_down in include/q4moe.h)."""
+    lib = load()
+    lay = layout_c(layout)
+    if down_probe is None:
+        st = lib.q4_expert_down(_ptr(slot), ctypes.byref(lay), _ptr(mid), M, H, I, _ptr(out), _stream(stream))
+    else:
+        st = lib.q4_expert_down_probe(_ptr(slot), ctypes.byref(lay), _ptr(mid), M, H, I, _ptr(out),
+                                      _ptr(down_probe), _stream(stream))
+    _check(st)
+
+
+def expert_down_grouped(slots_base, slot_stride: int, num_slots: int, layout, mid, M: int, slot_ids, K: int,
+                        H: int, I: int, out, workspace, workspace_bytes: int, down_probe=None,
+                        stream=None) -> None:
+    """Enqueue the grouped down projection (see q4_expert_down_grouped in include/q4moe.h)."""
+    lib = load()
+    lay = layout_c(layout)
+    if down_probe is None:
+        st = lib.q4_expert_down_grouped(_ptr(slots_base), slot_stride, num_slots, ctypes.byref(lay), _ptr(mid),
+                                        M, _ptr(slot_ids), K, H, I, _ptr(out), _ptr(workspace),
+                                        workspace_bytes, _stream(stream))
+    else:
+        st = lib.q4_expert_down_grouped_probe(_ptr(slots_base), slot_stride, num_slots, ctypes.byref(lay),
+                                              _ptr(mid), M, _ptr(slot_ids), K, H, I, _ptr(out),
+                                              _ptr(down_probe), _ptr(workspace), workspace_bytes,
+                                              _stream(stream))
+    _check(st)
+
+
+def expert_forward(slot, layout, x, M: int, H: int, I: int, mid, out, stream=None) -> None:
+    """Enqueue the whole expert of one slot (see q4_expert_forward in include/q4moe.h)."""
+    lay = layout_c(layout)
+    _check(load().q4_expert_forward(_ptr(slot), ctypes.byref(lay), _ptr(x), M, H, I, _ptr(mid), _ptr(out),
+                                    _stream(stream)))
+
+
+def expert_forward_grouped(slots_base, slot_stride: int, num_slots: int, layout, x, M: int, slot_ids, K: int,
+                           H: int, I: int, mid, out, workspace, workspace_bytes: int, stream=None) -> None:
+    """Enqueue the grouped whole expert (see q4_expert_forward_grouped in include/q4moe.h)."""
+    lay = layout_c(layout)
+    _check(load().q4_expert_forward_grouped(_ptr(slots_base), slot_stride, num_slots, ctypes.byref(lay),
+                                            _ptr(x), M, _ptr(slot_ids), K, H, I, _ptr(mid), _ptr(out),
+                                            _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def validate_down(slot, layout, mid, M: int, H: int, I: int, out) -> int:
+    """Host-only argument check of the down call; returns the status."""
+    lay = None if layout is None else layout_c(layout)
+    return load().q4_validate_down(_ptr(slot), None if lay is None else ctypes.byref(lay), _ptr(mid), M, H, I,
+                                   _ptr(out))
+
+
+def validate_down_grouped(slots_base, slot_stride, num_slots, layout, mid, M, slot_ids, K, H, I, out, workspace,
+                          workspace_bytes) -> int:
+    lay = None if layout is None else layout_c(layout)
+    return load().q4_validate_down_grouped(_ptr(slots_base), slot_stride, num_slots,
+                                           None if lay is None else ctypes.byref(lay), _ptr(mid), M,
+                                           _ptr(slot_ids), K, H, I, _ptr(out), _ptr(workspace), workspace_bytes)

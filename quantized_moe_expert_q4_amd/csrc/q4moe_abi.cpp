@@ -79,6 +79,19 @@ int check_layout(const q4_slot_layout* L, int64_t H, int64_t I) {
   return Q4_OK;
 }
 
+// Extra rules of a call that reads the down fields (DOWN_SOURCE and
+// validateCall, page 52): both dimensions divisible by 8, the down fields
+// present and aligned for the kernels' loads.
+int check_down_layout(const q4_slot_layout* L, int64_t I) {
+  if (I % 8 != 0) return fail(Q4_ERR_INVALID_ARGUMENT, "Q4 expert dimensions must be divisible by 8");
+  if (I > kMaxH) return fail(Q4_ERR_UNSUPPORTED, "intermediate size above 65536 is not supported by the down projection");
+  if (L->down_weight_offset == Q4_OFFSET_ABSENT || L->down_scale_offset == Q4_OFFSET_ABSENT)
+    return fail(Q4_ERR_INVALID_ARGUMENT, "the down projection needs down weight and scale offsets");
+  if (L->down_weight_offset % 16) return fail(Q4_ERR_ALIGNMENT, "down weight offset must be a multiple of 16 bytes");
+  if (L->down_scale_offset % 4) return fail(Q4_ERR_ALIGNMENT, "down scale offset must be a multiple of 4 bytes");
+  return Q4_OK;
+}
+
 int check_io(const void* x, const void* out, const void* gate_probe, const void* up_probe) {
   if (!x) return fail(Q4_ERR_INVALID_ARGUMENT, "input x must be a non-null device pointer");
   if (!out) return fail(Q4_ERR_INVALID_ARGUMENT, "output must be a non-null device pointer");
@@ -152,8 +165,24 @@ q4::GateUpParams make_params(const void* base, uint64_t stride, int64_t num_slot
   return p;
 }
 
-int launch(const q4::GateUpParams& p, q4_stream_t stream) {
-  const hipError_t e = q4::launch_gate_up(p, p.M, reinterpret_cast<hipStream_t>(stream));
+// The down projection as a kernel launch: x = mid (one row of I per token),
+// output rows H, the down fields in the gate/scale slots of the parameters.
+q4::GateUpParams down_params(q4::GateUpParams p, const q4_slot_layout* layout, int64_t H, int64_t I) {
+  p.gate_w_off = p.up_w_off = layout->down_weight_offset;
+  p.gate_s_off = p.up_s_off = layout->down_scale_offset;
+  p.H = (int)I;
+  p.I = (int)H;
+  p.up_probe = nullptr;
+  p.down = 1;
+  return p;
+}
+
+// pairs_per_slot > 0: a down launch whose slots see about that many of its
+// p.M routed pairs (the caller's token count: top-k ids are distinct per token)
+int launch(const q4::GateUpParams& p, q4_stream_t stream, int pairs_per_slot = 0) {
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const hipError_t e = p.down ? q4::launch_down(p, pairs_per_slot > 0 ? pairs_per_slot : p.M, s)
+                              : q4::launch_gate_up(p, p.M, s);
   if (e != hipSuccess) return fail(Q4_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
   return ok();
 }
@@ -172,6 +201,48 @@ int run_grouped(const void* base, uint64_t stride, int64_t num_slots, const q4_s
   const int rc = check_grouped(base, stride, num_slots, layout, x, M, ids, K, H, I, out, gp, up, ws, ws_bytes);
   if (rc) return rc;
   return launch(make_params(base, stride, num_slots, layout, x, M, ids, K, H, I, out, gp, up, ws), stream);
+}
+
+int check_down_single(const void* slot, const q4_slot_layout* layout, const void* mid, int64_t M, int64_t H,
+                      int64_t I, const void* out, const void* probe) {
+  int rc;
+  if ((rc = check_single(slot, layout, mid, M, H, I, out, probe, nullptr))) return rc;
+  if ((rc = check_down_layout(layout, I))) return rc;
+  return ok();
+}
+
+int check_down_grouped(const void* base, uint64_t stride, int64_t num_slots, const q4_slot_layout* layout,
+                       const void* mid, int64_t M, const int32_t* ids, int64_t K, int64_t H, int64_t I,
+                       const void* out, const void* probe, const void* ws, size_t ws_bytes) {
+  int rc;
+  if ((rc = check_grouped(base, stride, num_slots, layout, mid, M, ids, K, H, I, out, probe, nullptr, ws, ws_bytes)))
+    return rc;
+  if ((rc = check_down_layout(layout, I))) return rc;
+  if (M * K > kMaxM) return fail(Q4_ERR_UNSUPPORTED, "more than 65535 routed pairs per down call is not supported");
+  return ok();
+}
+
+int run_down_single(const void* slot, const q4_slot_layout* layout, const void* mid, int64_t M, int64_t H,
+                    int64_t I, void* out, float* probe, q4_stream_t stream) {
+  const int rc = check_down_single(slot, layout, mid, M, H, I, out, probe);
+  if (rc) return rc;
+  return launch(down_params(make_params(slot, layout->slot_bytes, 1, layout, mid, M, nullptr, 1, H, I, out, probe,
+                                        nullptr, nullptr),
+                            layout, H, I),
+                stream);
+}
+
+// Pair p = t*K + j reads its own input row mid[p] against slot ids[p]: the
+// launch sees M*K tokens routed one each (K = 1) through the same id array.
+int run_down_grouped(const void* base, uint64_t stride, int64_t num_slots, const q4_slot_layout* layout,
+                     const void* mid, int64_t M, const int32_t* ids, int64_t K, int64_t H, int64_t I, void* out,
+                     float* probe, void* ws, size_t ws_bytes, q4_stream_t stream) {
+  const int rc = check_down_grouped(base, stride, num_slots, layout, mid, M, ids, K, H, I, out, probe, ws, ws_bytes);
+  if (rc) return rc;
+  return launch(down_params(make_params(base, stride, num_slots, layout, mid, M * K, ids, 1, H, I, out, probe,
+                                        nullptr, ws),
+                            layout, H, I),
+                stream, (int)M);
 }
 
 }  // namespace
@@ -226,8 +297,74 @@ int q4_validate_grouped(const void* slots_base, uint64_t slot_stride, int64_t nu
                        nullptr, workspace, workspace_bytes);
 }
 
+int q4_expert_down(const void* slot, const q4_slot_layout* layout, const void* mid_bf16, int64_t M, int64_t H,
+                   int64_t I, void* out_bf16, q4_stream_t stream) {
+  return run_down_single(slot, layout, mid_bf16, M, H, I, out_bf16, nullptr, stream);
+}
+
+int q4_expert_down_probe(const void* slot, const q4_slot_layout* layout, const void* mid_bf16, int64_t M, int64_t H,
+                         int64_t I, void* out_bf16, float* down_f32, q4_stream_t stream) {
+  return run_down_single(slot, layout, mid_bf16, M, H, I, out_bf16, down_f32, stream);
+}
+
+int q4_expert_down_grouped(const void* slots_base, uint64_t slot_stride, int64_t num_slots,
+                           const q4_slot_layout* layout, const void* mid_bf16, int64_t M, const int32_t* slot_ids,
+                           int64_t K, int64_t H, int64_t I, void* out_bf16, void* workspace, size_t workspace_bytes,
+                           q4_stream_t stream) {
+  return run_down_grouped(slots_base, slot_stride, num_slots, layout, mid_bf16, M, slot_ids, K, H, I, out_bf16,
+                          nullptr, workspace, workspace_bytes, stream);
+}
+
+int q4_expert_down_grouped_probe(const void* slots_base, uint64_t slot_stride, int64_t num_slots,
+                                 const q4_slot_layout* layout, const void* mid_bf16, int64_t M,
+                                 const int32_t* slot_ids, int64_t K, int64_t H, int64_t I, void* out_bf16,
+                                 float* down_f32, void* workspace, size_t workspace_bytes, q4_stream_t stream) {
+  return run_down_grouped(slots_base, slot_stride, num_slots, layout, mid_bf16, M, slot_ids, K, H, I, out_bf16,
+                          down_f32, workspace, workspace_bytes, stream);
+}
+
+int q4_expert_forward(const void* slot, const q4_slot_layout* layout, const void* x_bf16, int64_t M, int64_t H,
+                      int64_t I, void* mid_bf16, void* out_bf16, q4_stream_t stream) {
+  int rc;
+  if ((rc = check_single(slot, layout, x_bf16, M, H, I, mid_bf16, nullptr, nullptr))) return rc;
+  if ((rc = check_down_single(slot, layout, mid_bf16, M, H, I, out_bf16, nullptr))) return rc;
+  if ((rc = run_single(slot, layout, x_bf16, M, H, I, mid_bf16, nullptr, nullptr, stream))) return rc;
+  return run_down_single(slot, layout, mid_bf16, M, H, I, out_bf16, nullptr, stream);
+}
+
+int q4_expert_forward_grouped(const void* slots_base, uint64_t slot_stride, int64_t num_slots,
+                              const q4_slot_layout* layout, const void* x_bf16, int64_t M, const int32_t* slot_ids,
+                              int64_t K, int64_t H, int64_t I, void* mid_bf16, void* out_bf16, void* workspace,
+                              size_t workspace_bytes, q4_stream_t stream) {
+  int rc;
+  if ((rc = check_grouped(slots_base, slot_stride, num_slots, layout, x_bf16, M, slot_ids, K, H, I, mid_bf16,
+                          nullptr, nullptr, workspace, workspace_bytes)))
+    return rc;
+  if ((rc = check_down_grouped(slots_base, slot_stride, num_slots, layout, mid_bf16, M, slot_ids, K, H, I, out_bf16,
+                               nullptr, workspace, workspace_bytes)))
+    return rc;
+  if ((rc = run_grouped(slots_base, slot_stride, num_slots, layout, x_bf16, M, slot_ids, K, H, I, mid_bf16, nullptr,
+                        nullptr, workspace, workspace_bytes, stream)))
+    return rc;
+  return run_down_grouped(slots_base, slot_stride, num_slots, layout, mid_bf16, M, slot_ids, K, H, I, out_bf16,
+                          nullptr, workspace, workspace_bytes, stream);
+}
+
+int q4_validate_down(const void* slot, const q4_slot_layout* layout, const void* mid_bf16, int64_t M, int64_t H,
+                     int64_t I, const void* out_bf16) {
+  return check_down_single(slot, layout, mid_bf16, M, H, I, out_bf16, nullptr);
+}
+
+int q4_validate_down_grouped(const void* slots_base, uint64_t slot_stride, int64_t num_slots,
+                             const q4_slot_layout* layout, const void* mid_bf16, int64_t M, const int32_t* slot_ids,
+                             int64_t K, int64_t H, int64_t I, const void* out_bf16, const void* workspace,
+                             size_t workspace_bytes) {
+  return check_down_grouped(slots_base, slot_stride, num_slots, layout, mid_bf16, M, slot_ids, K, H, I, out_bf16,
+                            nullptr, workspace, workspace_bytes);
+}
+
 const char* q4_last_error(void) { return g_err.c_str(); }
 
-int q4_abi_version(void) { return 1; }
+int q4_abi_version(void) { return 2; }
 
 }  // extern "C"

@@ -57,7 +57,10 @@ __host__ __device__ inline int bat_chunk_steps(int ntiles, int S) {
 
 }  // namespace
 
-template <int NT, bool VEC>
+// DOWN: the down projection (one matrix of a.I rows over a.H inputs; a tile is
+// 32 rows, its first 16 taking the gate role and the next 16 the up role,
+// each output rounded to bf16 on its own) instead of gate/up + SwiGLU.
+template <int NT, bool VEC, bool DOWN>
 __global__ __launch_bounds__(kBatThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void batch_kernel(const GateUpParams a) {
   // pairs per token group: up to 16*NT/4 (four digits), trimmed to 16*NT/6
@@ -79,13 +82,15 @@ void batch_kernel(const GateUpParams a) {
   const int P = a.M * a.K;
   const bool grouped = a.ids != nullptr;
   const int S = a.steps;                     // K-steps per tile, even
-  const int tps = (I + 15) / 16;
+  constexpr int RT = DOWN ? 32 : 16;         // rows per tile
+  const int tps = (I + RT - 1) / RT;
   const int T = a.num_slots * tps;
   const int NB = gridDim.x;
   const int v0 = (int)((int64_t)blockIdx.x * T / NB), v1 = (int)((int64_t)(blockIdx.x + 1) * T / NB);
   const uint32_t wbytes = (uint32_t)((uint64_t)I * (uint32_t)(H / 2));
 
-  for (int i = tid; i < kSigTable; i += kBatThreads) s_sig[i] = sigmoid_bf16(sig_table_bits(i));
+  if constexpr (!DOWN)
+    for (int i = tid; i < kSigTable; i += kBatThreads) s_sig[i] = sigmoid_bf16(sig_table_bits(i));
 
   // ---- invalid routing ids (grouped): zero-filled by work-group 0 ----
   if (grouped && blockIdx.x == 0) {
@@ -117,7 +122,12 @@ void batch_kernel(const GateUpParams a) {
     v = e * tps + t1;
     const uint8_t* slot = a.slots + (uint64_t)e * a.slot_stride;
     const __amdgpu_buffer_rsrc_t gsrc = make_rsrc(slot + a.gate_w_off, wbytes);
-    const __amdgpu_buffer_rsrc_t usrc = make_rsrc(slot + a.up_w_off, wbytes);
+    // DOWN: rows 16..31 of each tile are the same matrix 16 rows further on
+    // (loads past its end return zeros, for rows that are never stored)
+    const uint32_t skip = 16u * (uint32_t)(H / 2);
+    const __amdgpu_buffer_rsrc_t usrc =
+        DOWN ? make_rsrc(slot + a.gate_w_off + skip, wbytes > skip ? wbytes - skip : 0u)
+             : make_rsrc(slot + a.up_w_off, wbytes);
     const float* gscale = (const float*)(slot + a.gate_s_off);
     const float* uscale = (const float*)(slot + a.up_s_off);
 
@@ -176,7 +186,7 @@ void batch_kernel(const GateUpParams a) {
       int left = 0;                                    // K-steps this wave still has to load
       for (int t = lt; t < t1; t += kBatWaves) left += S;
       auto row_off = [&](int tile) {
-        const int row = tile * 16 + cc;
+        const int row = tile * RT + cc;
         return (uint32_t)(row < I ? row : I - 1) * (uint32_t)(H / 2) + (uint32_t)(g4 * 16);
       };
       uint32_t loff = row_off(lt);
@@ -348,7 +358,7 @@ void batch_kernel(const GateUpParams a) {
           // a transposing quad reduction leaves lane j of the quad with row j ----
           if (active) {
             const int j = cc & 3;
-            const int row = tile * 16 + 4 * g4 + j;
+            const int row = tile * RT + 4 * g4 + j;
             auto quad_row_sum = [&](const v4i acc) {
               const int64_t w0 = (int64_t)acc[0] << (8 * j), w1 = (int64_t)acc[1] << (8 * j);
               const int64_t w2 = (int64_t)acc[2] << (8 * j), w3 = (int64_t)acc[3] << (8 * j);
@@ -367,11 +377,21 @@ void batch_kernel(const GateUpParams a) {
                 if (ti < count && row < I) {
                   const int e2 = sum_exponent(s_xmax[ti]) + 16;
                   const float gate = round_scaled(vg >> 24, vg & 0xFFFFFF, e2, gscale[row]);
-                  const float up = round_scaled(vu >> 24, vu & 0xFFFFFF, e2, uscale[row]);
                   const uint64_t o = (uint64_t)s_pairs[ti] * I + row;
-                  a.out[o] = swiglu_tail_tab(gate, up, s_sig);
-                  if (a.gate_probe) a.gate_probe[o] = gate;
-                  if (a.up_probe) a.up_probe[o] = up;
+                  if constexpr (DOWN) {
+                    a.out[o] = bf16_rne(gate);
+                    if (a.gate_probe) a.gate_probe[o] = gate;
+                    if (row + 16 < I) {
+                      const float r16 = round_scaled(vu >> 24, vu & 0xFFFFFF, e2, gscale[row + 16]);
+                      a.out[o + 16] = bf16_rne(r16);
+                      if (a.gate_probe) a.gate_probe[o + 16] = r16;
+                    }
+                  } else {
+                    const float up = round_scaled(vu >> 24, vu & 0xFFFFFF, e2, uscale[row]);
+                    a.out[o] = swiglu_tail_tab(gate, up, s_sig);
+                    if (a.gate_probe) a.gate_probe[o] = gate;
+                    if (a.up_probe) a.up_probe[o] = up;
+                  }
                 }
               }
             }
@@ -404,16 +424,21 @@ void batch_kernel(const GateUpParams a) {
               for (int j = 0; j < kItemRounds; ++j) {
                 const int item = lane + 64 * j;
                 const int rr = item & 15, ti = item >> 4;
-                const int row = tile * 16 + rr;
+                const int row = tile * RT + rr + (DOWN ? 16 * part : 0);
                 if (ti < count && row < I) {
                   const int32_t* d = ep + rr * kEpStride + ti * L;
                   const int64_t lo = (int64_t)d[0] + ((int64_t)d[1] << 8) + ((int64_t)d[2] << 16);
                   const int64_t hi = L == 6 ? (int64_t)d[3] + ((int64_t)d[4] << 8) + ((int64_t)d[5] << 16)
                                             : (int64_t)d[3];
                   const int xm = s_xmax[ti];
-                  float r = round_scaled(hi, lo, sum_exponent(xm) + 8 * (6 - L), part ? uscale[row] : gscale[row]);
+                  float r = round_scaled(hi, lo, sum_exponent(xm) + 8 * (6 - L),
+                                         (part && !DOWN) ? uscale[row] : gscale[row]);
                   if (xm >= 0x7F80) r = __builtin_nanf("");
-                  if (!part) {
+                  if constexpr (DOWN) {
+                    const uint64_t o = (uint64_t)s_pairs[ti] * I + row;
+                    a.out[o] = bf16_rne(r);
+                    if (a.gate_probe) a.gate_probe[o] = r;
+                  } else if (!part) {
                     gv[j] = r;
                   } else {
                     const uint64_t o = (uint64_t)s_pairs[ti] * I + row;
@@ -438,7 +463,7 @@ void batch_kernel(const GateUpParams a) {
 
 namespace {
 
-template <int NT, bool VEC>
+template <int NT, bool VEC, bool DOWN>
 int batch_blocks(int device) {
   static int cached[64] = {0};
   if (device < 0 || device >= 64) device = 0;
@@ -447,7 +472,7 @@ int batch_blocks(int device) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0)
       cus = 256;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&batch_kernel<NT, VEC>), kBatThreads, 0) != hipSuccess ||
+            &per_cu, reinterpret_cast<const void*>(&batch_kernel<NT, VEC, DOWN>), kBatThreads, 0) != hipSuccess ||
         per_cu <= 0)
       per_cu = 1;
     cached[device] = cus * per_cu;
@@ -455,16 +480,25 @@ int batch_blocks(int device) {
   return cached[device];
 }
 
-template <int NT, bool VEC>
+template <int NT, bool VEC, bool DOWN>
 hipError_t launch_batch_t(GateUpParams& p, hipStream_t stream) {
   int device = 0;
   if (hipGetDevice(&device) != hipSuccess) device = 0;
-  const int tiles = p.num_slots * ((p.I + 15) / 16);
-  int nb = batch_blocks<NT, VEC>(device);
+  const int rt = DOWN ? 32 : 16;
+  const int tiles = p.num_slots * ((p.I + rt - 1) / rt);
+  int nb = batch_blocks<NT, VEC, DOWN>(device);
   if (nb > tiles) nb = tiles;
   void* args[] = {&p};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&batch_kernel<NT, VEC>), dim3((unsigned)nb),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&batch_kernel<NT, VEC, DOWN>), dim3((unsigned)nb),
                          dim3(kBatThreads), args, 0, stream);
+}
+
+template <bool DOWN>
+hipError_t launch_batch_m(GateUpParams& p, int nt, hipStream_t stream) {
+  const bool vec = (p.H % 32) == 0;
+  if (nt == 1) return vec ? launch_batch_t<1, true, DOWN>(p, stream) : launch_batch_t<1, false, DOWN>(p, stream);
+  if (nt == 2) return vec ? launch_batch_t<2, true, DOWN>(p, stream) : launch_batch_t<2, false, DOWN>(p, stream);
+  return vec ? launch_batch_t<3, true, DOWN>(p, stream) : launch_batch_t<3, false, DOWN>(p, stream);
 }
 
 }  // namespace
@@ -474,10 +508,7 @@ hipError_t launch_batch(GateUpParams p, int tokens_per_slot, hipStream_t stream)
   p.steps += p.steps & 1;
   const int nt = tokens_per_slot <= 2 ? 1 : (tokens_per_slot <= 5 ? 2 : 3);
   p.G = (16 * nt) / 4;
-  const bool vec = (p.H % 32) == 0;
-  if (nt == 1) return vec ? launch_batch_t<1, true>(p, stream) : launch_batch_t<1, false>(p, stream);
-  if (nt == 2) return vec ? launch_batch_t<2, true>(p, stream) : launch_batch_t<2, false>(p, stream);
-  return vec ? launch_batch_t<3, true>(p, stream) : launch_batch_t<3, false>(p, stream);
+  return p.down ? launch_batch_m<true>(p, nt, stream) : launch_batch_m<false>(p, nt, stream);
 }
 
 }  // namespace q4

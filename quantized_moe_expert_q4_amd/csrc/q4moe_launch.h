@@ -5,8 +5,12 @@
 
 namespace q4 {
 
-// Everything one launch of a gate/up kernel reads.  `ids == nullptr` is the
-// single-expert call: every token routed to slot 0 with K == 1.
+// Everything one launch of a gate/up or down kernel reads.  `ids == nullptr`
+// is the single-expert call: every token routed to slot 0 with K == 1.
+// With `down` set the launch is the down projection: H is the reduction
+// length (the expert's intermediate size), I the number of output rows (its
+// hidden size), gate_w_off/gate_s_off locate the down weights and scales, and
+// gate_probe (if any) receives the F32 values before their bf16 rounding.
 struct GateUpParams {
   const uint8_t* slots;      // slot 0 base (4096-aligned)
   uint64_t slot_stride;      // bytes between slots
@@ -20,6 +24,7 @@ struct GateUpParams {
   int M, K, H, I, num_slots;
   int G, steps;              // set by the launchers: tokens per group, K-steps per tile
   int wave_share;            // set by launch_resident: a SIMD's first-wave share, 1/1024
+  int down;                  // 1: down projection (see above)
 };
 
 // Resident-digits kernel for token groups of at most two (decode widths):
@@ -33,5 +38,11 @@ hipError_t launch_batch(GateUpParams p, int tokens_per_slot, hipStream_t stream)
 // Pick and launch the kernel for a call whose slots see at most
 // `tokens_per_slot` tokens (more are processed in further token groups).
 hipError_t launch_gate_up(const GateUpParams& p, int tokens_per_slot, hipStream_t stream);
+
+// Down launch whose p.M tokens are routed pairs (one input row each) and
+// whose slots are expected to see `pairs_per_slot` of them: the resident
+// kernel when all p.M rows fit it, else the batch kernel sized for
+// `pairs_per_slot` (more are processed in further groups).
+hipError_t launch_down(const GateUpParams& p, int pairs_per_slot, hipStream_t stream);
 
 }  // namespace q4

@@ -61,7 +61,10 @@ __host__ __device__ constexpr int res_tiles(int M) { return M <= 2 ? 1 : 2; }
 
 }  // namespace
 
-template <int NT, bool VEC>
+// DOWN: the down projection (one matrix of a.I rows over a.H inputs; a tile is
+// 32 rows, its first 16 taking the gate role and the next 16 the up role,
+// each output rounded to bf16 on its own) instead of gate/up + SwiGLU.
+template <int NT, bool VEC, bool DOWN>
 __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void resident_kernel(const GateUpParams a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_lds[kResLds];
   __shared__ int s_pairs[kResMaxPairs];
@@ -84,7 +87,8 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int S = a.steps;                     // K-steps per tile, a multiple of D
   const int sbytes = res_step_bytes(NT);
   const int hw = H / 8;                      // 16-byte chunks of one token's x
-  const int tps = (I + 15) / 16;             // tiles per slot
+  constexpr int RT = DOWN ? 32 : 16;         // rows per tile
+  const int tps = (I + RT - 1) / RT;         // tiles per slot
   const int T = a.num_slots * tps;
   const int NB = gridDim.x;
   const int v0 = (int)((int64_t)blockIdx.x * T / NB), v1 = (int)((int64_t)(blockIdx.x + 1) * T / NB);
@@ -163,7 +167,14 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
     v = e * tps + t1;
     const uint8_t* slot = a.slots + (uint64_t)e * a.slot_stride;
     gsrc = make_rsrc(slot + a.gate_w_off, wbytes);
-    usrc = make_rsrc(slot + a.up_w_off, wbytes);
+    if constexpr (DOWN) {
+      // rows 16..31 of each tile: the same matrix 16 rows further on (loads
+      // past its end return zeros, for rows that are never stored)
+      const uint32_t skip = 16u * (uint32_t)(H / 2);
+      usrc = make_rsrc(slot + a.gate_w_off + skip, wbytes > skip ? wbytes - skip : 0u);
+    } else {
+      usrc = make_rsrc(slot + a.up_w_off, wbytes);
+    }
     gscale = (const float*)(slot + a.gate_s_off);
     uscale = (const float*)(slot + a.up_s_off);
     nunits = (t1 - t0) * S;
@@ -172,7 +183,7 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
   };
 
   auto row_off = [&](int tile) {
-    const int row = tile * 16 + cc;
+    const int row = tile * RT + cc;
     return (uint32_t)(row < I ? row : I - 1) * (uint32_t)(H / 2) + (uint32_t)(g4 * 16);
   };
   v4u rg[kResD], ru[kResD];
@@ -243,7 +254,8 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
   // ---- first segment's weights in flight, then the digits of the first pass ----
   open_segment();
   start_ring();
-  for (int i = tid; i < kSigTable; i += kResThreads) s_sig[i] = sigmoid_bf16(sig_table_bits(i));
+  if constexpr (!DOWN)
+    for (int i = tid; i < kSigTable; i += kResThreads) s_sig[i] = sigmoid_bf16(sig_table_bits(i));
   // largest |x| and smallest non-zero exponent of each token
 #pragma unroll
   for (int j = 0; j < kResXRegs; ++j) {
@@ -417,8 +429,9 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
         // the row scales this lane may finish with, loaded ahead of the
         // portion's weight loads: loads complete in order, so a scale load
         // issued at the finish would wait for every weight load in flight
-        const int row = tile * 16 + 4 * g4 + qj;
-        const float gsc = gscale[min(row, I - 1)], usc = uscale[min(row, I - 1)];
+        const int row = tile * RT + 4 * g4 + qj;
+        const float gsc = gscale[min(row, I - 1)];
+        const float usc = DOWN ? gscale[min(row + 16, I - 1)] : uscale[min(row, I - 1)];
         float gscr = 0.0f, uscr = 0.0f;
         v4i accg[NT], accu[NT];
 #pragma unroll
@@ -538,24 +551,30 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
                 gate = __builtin_nanf("");
                 up = __builtin_nanf("");
               }
-              ov = swiglu_tail_tab(gate, up, s_sig);
+              if constexpr (!DOWN) ov = swiglu_tail_tab(gate, up, s_sig);
             }
-            if (!multi) {
-              if (ok && mypair[n] >= 0) {
-                const uint64_t o = (uint64_t)mypair[n] * I + row;
+            // results of this (row, token) for routed pair `pair`
+            auto store = [&](int pair) {
+              const uint64_t o = (uint64_t)pair * I + row;
+              if constexpr (DOWN) {
+                // rows `row` and `row + 16`, each its own bf16 output
+                a.out[o] = bf16_rne(gate);
+                if (a.gate_probe) a.gate_probe[o] = gate;
+                if (row + 16 < I) {
+                  a.out[o + 16] = bf16_rne(up);
+                  if (a.gate_probe) a.gate_probe[o + 16] = up;
+                }
+              } else {
                 a.out[o] = ov;
                 if (a.gate_probe) a.gate_probe[o] = gate;
                 if (a.up_probe) a.up_probe[o] = up;
               }
+            };
+            if (!multi) {
+              if (ok && mypair[n] >= 0) store(mypair[n]);
             } else {
-              for (int q = 0; q < count; ++q) {
-                if (ok && gtok[q] == tl) {
-                  const uint64_t o = (uint64_t)gpair[q] * I + row;
-                  a.out[o] = ov;
-                  if (a.gate_probe) a.gate_probe[o] = gate;
-                  if (a.up_probe) a.up_probe[o] = up;
-                }
-              }
+              for (int q = 0; q < count; ++q)
+                if (ok && gtok[q] == tl) store(gpair[q]);
             }
           }
         }
@@ -598,7 +617,7 @@ constexpr int kWaveShare2 = 547;
 
 // Work-groups that fit the device at once (one per CU: the LDS arrays take
 // most of a CU's 160 KiB).
-template <int NT, bool VEC>
+template <int NT, bool VEC, bool DOWN>
 int resident_blocks(int device) {
   static int cached[64] = {0};
   if (device < 0 || device >= 64) device = 0;
@@ -607,7 +626,7 @@ int resident_blocks(int device) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0)
       cus = 256;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&resident_kernel<NT, VEC>), kResThreads, 0) != hipSuccess ||
+            &per_cu, reinterpret_cast<const void*>(&resident_kernel<NT, VEC, DOWN>), kResThreads, 0) != hipSuccess ||
         per_cu <= 0)
       per_cu = 1;
     cached[device] = cus * per_cu;
@@ -615,16 +634,25 @@ int resident_blocks(int device) {
   return cached[device];
 }
 
-template <int NT, bool VEC>
+template <int NT, bool VEC, bool DOWN>
 hipError_t launch_resident_t(GateUpParams& p, hipStream_t stream) {
   int device = 0;
   if (hipGetDevice(&device) != hipSuccess) device = 0;
-  const int tiles = p.num_slots * ((p.I + 15) / 16);
-  int nb = resident_blocks<NT, VEC>(device);
+  const int rt = DOWN ? 32 : 16;
+  const int tiles = p.num_slots * ((p.I + rt - 1) / rt);
+  int nb = resident_blocks<NT, VEC, DOWN>(device);
   if (nb > tiles) nb = tiles;
   void* args[] = {&p};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&resident_kernel<NT, VEC>), dim3((unsigned)nb),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&resident_kernel<NT, VEC, DOWN>), dim3((unsigned)nb),
                          dim3(kResThreads), args, 0, stream);
+}
+
+template <bool DOWN>
+hipError_t launch_resident_m(GateUpParams& p, hipStream_t stream) {
+  const bool vec = (p.H % 32) == 0;
+  if (res_tiles(p.M) == 1)
+    return vec ? launch_resident_t<1, true, DOWN>(p, stream) : launch_resident_t<1, false, DOWN>(p, stream);
+  return vec ? launch_resident_t<2, true, DOWN>(p, stream) : launch_resident_t<2, false, DOWN>(p, stream);
 }
 
 }  // namespace
@@ -641,13 +669,15 @@ hipError_t launch_resident(GateUpParams p, hipStream_t stream) {
   p.steps = res_steps(p.H);
   p.G = kResMaxPairs;
   p.wave_share = res_tiles(p.M) == 1 ? kWaveShare1 : kWaveShare2;
-  const bool vec = (p.H % 32) == 0;
-  if (res_tiles(p.M) == 1) return vec ? launch_resident_t<1, true>(p, stream) : launch_resident_t<1, false>(p, stream);
-  return vec ? launch_resident_t<2, true>(p, stream) : launch_resident_t<2, false>(p, stream);
+  return p.down ? launch_resident_m<true>(p, stream) : launch_resident_m<false>(p, stream);
 }
 
 hipError_t launch_gate_up(const GateUpParams& p, int tokens_per_slot, hipStream_t stream) {
   return resident_fits(tokens_per_slot, p.H) ? launch_resident(p, stream) : launch_batch(p, tokens_per_slot, stream);
+}
+
+hipError_t launch_down(const GateUpParams& p, int pairs_per_slot, hipStream_t stream) {
+  return resident_fits(p.M, p.H) ? launch_resident(p, stream) : launch_batch(p, pairs_per_slot, stream);
 }
 
 }  // namespace q4

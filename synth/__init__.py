@@ -10,6 +10,7 @@ from .generators import (  # noqa: F401
     OFFSET_ABSENT,
     SlotLayout,
     contiguous_layout,
+    expert_layout,
     pack_nibbles,
     fill_slot,
     write_slot,

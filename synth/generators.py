@@ -73,6 +73,25 @@ def contiguous_layout(H: int, I: int, align: int = 4096) -> SlotLayout:
     return SlotLayout(slot, gate_w, up_w, gate_s, up_s)
 
 
+def expert_layout(H: int, I: int, align: int = 4096) -> SlotLayout:
+    """A whole-expert slot: gate words, up words, down words, gate scales, up
+    scales, down scales back to back (16-byte aligned fields), padded to
+    ``align``.  Down words are ``[H][I/8]``, down scales ``[H]``."""
+    def up16(n):
+        return (n + 15) // 16 * 16
+
+    wbytes = I * H // 2
+    gate_w = 0
+    up_w = up16(wbytes)
+    down_w = up16(up_w + wbytes)
+    gate_s = up16(down_w + wbytes)
+    up_s = up16(gate_s + 4 * I)
+    down_s = up16(up_s + 4 * I)
+    end = down_s + 4 * H
+    slot = (end + align - 1) // align * align
+    return SlotLayout(slot, gate_w, up_w, gate_s, up_s, down_w, down_s)
+
+
 def pack_nibbles(nibbles: np.ndarray) -> np.ndarray:
     """Pack a ``[R, H]`` array of values 0..15 into ``[R, H/8]`` uint32 words.
 
@@ -122,7 +141,9 @@ def fill_slot(
 
     Draw order: gate words, up words, gate scales, up scales, then (if
     ``zero_row_fraction``) the gate rows and the up rows forced to all-8.
-    Padding bytes are zero.
+    When the layout has down fields, then down words ``[H, I/8]``, down
+    scales ``[H]`` and (if ``zero_row_fraction``) the down rows forced to
+    all-8.  Padding bytes are zero.
     """
     if out is None:
         out = np.zeros(layout.slot_bytes, dtype=np.uint8)
@@ -142,6 +163,13 @@ def fill_slot(
     out[layout.up_weight_offset:layout.up_weight_offset + wb] = uw.astype("<u4").view(np.uint8).ravel()
     out[layout.gate_scale_offset:layout.gate_scale_offset + 4 * I] = gs.astype("<f4").view(np.uint8)
     out[layout.up_scale_offset:layout.up_scale_offset + 4 * I] = us.astype("<f4").view(np.uint8)
+    if layout.down_weight_offset != OFFSET_ABSENT:
+        dw = _uniform_words(rng, H, I)
+        ds = rng.uniform(lo, hi, size=H).astype(np.float32)
+        if zero_row_fraction:
+            dw[rng.choice(H, int(round(zero_row_fraction * H)), replace=False)] = ALL_EIGHT_WORD
+        out[layout.down_weight_offset:layout.down_weight_offset + wb] = dw.astype("<u4").view(np.uint8).ravel()
+        out[layout.down_scale_offset:layout.down_scale_offset + 4 * H] = ds.astype("<f4").view(np.uint8)
     return out
 
 
@@ -209,18 +237,21 @@ CONFIGS: Dict[str, dict] = {
 
 
 def make_config(name: str, M: Optional[int] = None, num_slots: Optional[int] = None,
-                H: Optional[int] = None, I: Optional[int] = None, seed: Optional[int] = None) -> Config:
+                H: Optional[int] = None, I: Optional[int] = None, seed: Optional[int] = None,
+                with_down: bool = False) -> Config:
     """Build one of the five workloads (or a resized variant of it).
 
     ``cfg5`` needs ``M`` in {1, 4, 16, 32}; its x is drawn from seed 105+M.
     ``num_slots``/``H``/``I``/``seed`` override the defaults for scaled-down
-    or scaled-up variants with the same distributions.
+    or scaled-up variants with the same distributions.  ``with_down`` lays
+    the slots out as whole experts (``expert_layout``) and draws down weights
+    and scales of the same distributions after each slot's gate/up fields.
     """
     spec = dict(CONFIGS[name])
     H = H or spec["H"]
     I = I or spec["I"]
     seed = spec["seed"] if seed is None else seed
-    layout = contiguous_layout(H, I)
+    layout = expert_layout(H, I) if with_down else contiguous_layout(H, I)
     rng = np.random.default_rng(seed)
     if name == "cfg4":
         E = num_slots or spec["num_slots"]

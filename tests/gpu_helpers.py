@@ -102,3 +102,49 @@ def check_parity(out, g, u, g_ref, u_ref, out_ref, label, require_exact_gate_up=
         assert exact_g == n and exact_u == n, label
     return dict(n=n, exact_gate=exact_g, exact_up=exact_u, exact_out=exact_o, t2_max=int(t2.max()),
                 e2e_max=int(e2e.max()))
+
+
+def run_down_single(slot_np, layout, midbits, H, I):
+    """One single-slot down call: returns (out bf16 bits [M,H], F32 probe [M,H])."""
+    M = midbits.shape[0]
+    slot = upload_slots(slot_np.reshape(1, -1))
+    mid = upload_bf16_bits(midbits)
+    out = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    d = torch.empty((M, H), dtype=torch.float32, device="cuda")
+    q4.expert_down(slot, layout, mid, M, H, I, out, d)
+    torch.cuda.synchronize()
+    return bf16_bits(out), d.cpu().numpy()
+
+
+def run_down_grouped(slots_np, layout, midbits, ids, H, I, slots=None):
+    """One grouped down call on mid [M,K,I]: returns ((out [M,K,H], probe), invalid count)."""
+    M, K = ids.shape
+    E = slots_np.shape[0]
+    if slots is None:
+        slots = upload_slots(slots_np)
+    mid = upload_bf16_bits(np.ascontiguousarray(midbits).reshape(M, K, I))
+    idt = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda()
+    out = torch.empty((M, K, H), dtype=torch.bfloat16, device="cuda")
+    d = torch.empty((M, K, H), dtype=torch.float32, device="cuda")
+    wsb = q4.grouped_workspace_bytes(M, K, H, I, E)
+    ws = aligned_empty(wsb, 256)
+    ws.fill_(0xAB)
+    q4.expert_down_grouped(slots, slots_np.shape[1], E, layout, mid, M, idt, K, H, I, out, ws, wsb, d)
+    torch.cuda.synchronize()
+    invalid = int(ws[:4].cpu().numpy().view(np.int32)[0])
+    return (bf16_bits(out), d.cpu().numpy()), invalid
+
+
+def check_down_parity(out, d, d_ref, out_ref, label):
+    """T1 on the F32 values before rounding, the bf16 output within one ulp of
+    the oracle's; both are also required to be bit-exact (exact sums)."""
+    n = out.size
+    t1 = t1_violations(d, d_ref)
+    e2e = bf16_dist(out, out_ref)
+    exact_d = int(np.sum(d.view(np.uint32) == np.asarray(d_ref, np.float32).view(np.uint32)))
+    exact_o = int(np.sum(out == out_ref))
+    say(f"[{label}] n={n} T1 fail={t1}; out max dist={int(e2e.max()) if n else 0}; "
+        f"bit-exact down={exact_d}/{n} out={exact_o}/{n}")
+    assert t1 == 0, label
+    assert n == 0 or int(e2e.max()) <= 1, label
+    assert exact_d == n and exact_o == n, label

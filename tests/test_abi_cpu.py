@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 9, names
     for n in names:
         assert hasattr(lib, n), n
-    assert q4.abi_version() == 1
+    assert q4.abi_version() == 2
 
 
 def test_workspace_size_is_aligned_and_positive():
@@ -156,4 +156,80 @@ def test_entry_points_reject_before_touching_the_device():
     assert ei.value.status == q4.Q4_ERR_ALIGNMENT
     with pytest.raises(q4.Q4Error) as ei:
         q4.expert_gate_up_grouped(SLOT, 4096, 1, _lay(), X, 1, IDS, 1, 4096, 1536, OUT, WS, 256, stream=0)
+    assert ei.value.status == q4.Q4_ERR_RANGE
+
+
+# ---- down projection and whole expert (page 52 DOWN_SOURCE / validateCall) ----
+
+def _down(**kw):
+    a = dict(slot=SLOT, layout=synth.expert_layout(4096, 1536), mid=X, M=1, H=4096, I=1536, out=OUT)
+    a.update(kw)
+    st = q4.validate_down(a["slot"], a["layout"], a["mid"], a["M"], a["H"], a["I"], a["out"])
+    return st, q4.last_error()
+
+
+def test_down_valid_arguments_pass():
+    assert _down() == (0, "")
+    assert _down(M=65535) == (0, "")
+
+
+def _shift_down(lay, dw=0, ds=0):
+    from dataclasses import replace
+    return replace(lay, down_weight_offset=lay.down_weight_offset + dw, down_scale_offset=lay.down_scale_offset + ds)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(I=1540, layout=synth.expert_layout(4096, 1540)), q4.Q4_ERR_INVALID_ARGUMENT, "divisible by 8"),
+    (dict(layout=synth.contiguous_layout(4096, 1536)), q4.Q4_ERR_INVALID_ARGUMENT, "down weight and scale"),
+    (dict(layout=_shift_down(synth.expert_layout(4096, 1536), dw=8)), q4.Q4_ERR_ALIGNMENT, "down weight offset"),
+    (dict(layout=_shift_down(synth.expert_layout(4096, 1536), ds=-2)), q4.Q4_ERR_ALIGNMENT, "down scale offset"),
+    (dict(layout=_shift_down(synth.expert_layout(4096, 1536), dw=1 << 24)), q4.Q4_ERR_RANGE,
+     "down weights exceeds the canonical expert slot"),
+    (dict(layout=_shift_down(synth.expert_layout(4096, 1536), ds=1 << 24)), q4.Q4_ERR_RANGE,
+     "down scales exceeds the canonical expert slot"),
+    (dict(mid=X + 8), q4.Q4_ERR_ALIGNMENT, "16-byte"),
+    (dict(M=0), q4.Q4_ERR_INVALID_ARGUMENT, "M >= 1"),
+    (dict(slot=SLOT + 4096 + 64), q4.Q4_ERR_ALIGNMENT, "page-aligned"),
+])
+def test_down_rejections(kw, status, msg):
+    st, err = _down(**kw)
+    assert st == status, err
+    assert msg in err
+
+
+def _down_grouped(**kw):
+    lay = synth.expert_layout(6144, 2048)
+    a = dict(base=SLOT, stride=lay.slot_bytes, E=64, layout=lay, mid=X, M=32, ids=IDS, K=8, H=6144, I=2048,
+             out=OUT, ws=WS, wsb=q4.grouped_workspace_bytes(32, 8, 6144, 2048, 64))
+    a.update(kw)
+    st = q4.validate_down_grouped(a["base"], a["stride"], a["E"], a["layout"], a["mid"], a["M"], a["ids"], a["K"],
+                                  a["H"], a["I"], a["out"], a["ws"], a["wsb"])
+    return st, q4.last_error()
+
+
+def test_down_grouped_valid_and_rejected():
+    assert _down_grouped() == (0, "")
+    st, err = _down_grouped(layout=synth.contiguous_layout(6144, 2048), stride=synth.contiguous_layout(6144, 2048).slot_bytes)
+    assert st == q4.Q4_ERR_INVALID_ARGUMENT and "down" in err
+    st, err = _down_grouped(M=65536, K=1, wsb=q4.grouped_workspace_bytes(65535, 1, 6144, 2048, 64))
+    assert st == q4.Q4_ERR_UNSUPPORTED
+    st, err = _down_grouped(wsb=0)
+    assert st == q4.Q4_ERR_WORKSPACE
+
+
+def test_down_and_forward_entry_points_reject_before_touching_the_device():
+    lay = synth.expert_layout(4096, 1536)
+    with pytest.raises(q4.Q4Error) as ei:
+        q4.expert_down(SLOT + 8, lay, X, 1, 4096, 1536, OUT, stream=0)
+    assert ei.value.status == q4.Q4_ERR_ALIGNMENT
+    # forward validates both steps before enqueueing either: a gate/up-only layout fails
+    with pytest.raises(q4.Q4Error) as ei:
+        q4.expert_forward(SLOT, synth.contiguous_layout(4096, 1536), X, 1, 4096, 1536, X + (1 << 20), OUT, stream=0)
+    assert ei.value.status == q4.Q4_ERR_INVALID_ARGUMENT
+    with pytest.raises(q4.Q4Error) as ei:
+        q4.expert_forward_grouped(SLOT, lay.slot_bytes, 2, lay, X, 1, IDS, 2, 4096, 1536, X + 8, OUT, WS, 256,
+                                  stream=0)
+    assert ei.value.status == q4.Q4_ERR_ALIGNMENT
+    with pytest.raises(q4.Q4Error) as ei:
+        q4.expert_down_grouped(SLOT, 4096, 1, lay, X, 1, IDS, 1, 4096, 1536, OUT, WS, 256, stream=0)
     assert ei.value.status == q4.Q4_ERR_RANGE
