@@ -1,5 +1,5 @@
 /*
- * q4moe.h -- C ABI of the MI355X (gfx950) Q4 expert library: gate/up +
+ * q4moe.h -- C ABI of the MI355X (gfx950) Q4/Q8 expert library: gate/up +
  * SwiGLU, the down projection and the whole expert, over expert slots.
  *
  * What is computed (diff of @mlx-bun/inference 1.0.0, page 52,
@@ -248,10 +248,96 @@ int q4_validate_down_grouped(const void *slots_base, uint64_t slot_stride,
                              int64_t I, const void *out_bf16,
                              const void *workspace, size_t workspace_bytes);
 
+/*
+ * The Q8 family (page 52, Q8_GATE_UP_SOURCE, Q8_DOWN_SOURCE and
+ * Glm52CanonicalQ8MetalExecutor): the same calls, arguments, layout struct
+ * and results as their q4_ namesakes, with signed int8 weights, one byte per
+ * weight and no zero point:
+ *   gate/up weights  int8 [I][H] row-major at gate/up_weight_offset
+ *                    (I*H bytes each), weight = the byte read as int8;
+ *   down weights     int8 [H][I] row-major at down_weight_offset (H*I bytes);
+ *   scales           float32 per row, as for Q4.
+ * Weight offsets are 16-byte aligned.  H % 8 == 0 (and I % 8 == 0 for the
+ * down and whole-expert calls) is this library's rule, not the pages': the
+ * kernels read activations in 8-value units.  Sums are exact and rounded once
+ * to F32 with the row scale, as for Q4.
+ */
+int q8_expert_gate_up(const void *slot, const q4_slot_layout *layout,
+                      const void *x_bf16, int64_t M, int64_t H, int64_t I,
+                      void *out_bf16, q4_stream_t stream);
+int q8_expert_gate_up_probe(const void *slot, const q4_slot_layout *layout,
+                            const void *x_bf16, int64_t M, int64_t H, int64_t I,
+                            void *out_bf16, float *gate_f32, float *up_f32,
+                            q4_stream_t stream);
+int q8_expert_gate_up_grouped(const void *slots_base, uint64_t slot_stride,
+                              int64_t num_slots, const q4_slot_layout *layout,
+                              const void *x_bf16, int64_t M,
+                              const int32_t *slot_ids, int64_t K,
+                              int64_t H, int64_t I, void *out_bf16,
+                              void *workspace, size_t workspace_bytes,
+                              q4_stream_t stream);
+int q8_expert_gate_up_grouped_probe(const void *slots_base, uint64_t slot_stride,
+                                    int64_t num_slots, const q4_slot_layout *layout,
+                                    const void *x_bf16, int64_t M,
+                                    const int32_t *slot_ids, int64_t K,
+                                    int64_t H, int64_t I, void *out_bf16,
+                                    float *gate_f32, float *up_f32,
+                                    void *workspace, size_t workspace_bytes,
+                                    q4_stream_t stream);
+int q8_expert_down(const void *slot, const q4_slot_layout *layout,
+                   const void *mid_bf16, int64_t M, int64_t H, int64_t I,
+                   void *out_bf16, q4_stream_t stream);
+int q8_expert_down_probe(const void *slot, const q4_slot_layout *layout,
+                         const void *mid_bf16, int64_t M, int64_t H, int64_t I,
+                         void *out_bf16, float *down_f32, q4_stream_t stream);
+int q8_expert_down_grouped(const void *slots_base, uint64_t slot_stride,
+                           int64_t num_slots, const q4_slot_layout *layout,
+                           const void *mid_bf16, int64_t M,
+                           const int32_t *slot_ids, int64_t K,
+                           int64_t H, int64_t I, void *out_bf16,
+                           void *workspace, size_t workspace_bytes,
+                           q4_stream_t stream);
+int q8_expert_down_grouped_probe(const void *slots_base, uint64_t slot_stride,
+                                 int64_t num_slots, const q4_slot_layout *layout,
+                                 const void *mid_bf16, int64_t M,
+                                 const int32_t *slot_ids, int64_t K,
+                                 int64_t H, int64_t I, void *out_bf16,
+                                 float *down_f32,
+                                 void *workspace, size_t workspace_bytes,
+                                 q4_stream_t stream);
+int q8_expert_forward(const void *slot, const q4_slot_layout *layout,
+                      const void *x_bf16, int64_t M, int64_t H, int64_t I,
+                      void *mid_bf16, void *out_bf16, q4_stream_t stream);
+int q8_expert_forward_grouped(const void *slots_base, uint64_t slot_stride,
+                              int64_t num_slots, const q4_slot_layout *layout,
+                              const void *x_bf16, int64_t M,
+                              const int32_t *slot_ids, int64_t K,
+                              int64_t H, int64_t I, void *mid_bf16,
+                              void *out_bf16, void *workspace,
+                              size_t workspace_bytes, q4_stream_t stream);
+int q8_validate_gate_up(const void *slot, const q4_slot_layout *layout,
+                        const void *x_bf16, int64_t M, int64_t H, int64_t I,
+                        const void *out_bf16);
+int q8_validate_grouped(const void *slots_base, uint64_t slot_stride,
+                        int64_t num_slots, const q4_slot_layout *layout,
+                        const void *x_bf16, int64_t M, const int32_t *slot_ids,
+                        int64_t K, int64_t H, int64_t I, const void *out_bf16,
+                        const void *workspace, size_t workspace_bytes);
+int q8_validate_down(const void *slot, const q4_slot_layout *layout,
+                     const void *mid_bf16, int64_t M, int64_t H, int64_t I,
+                     const void *out_bf16);
+int q8_validate_down_grouped(const void *slots_base, uint64_t slot_stride,
+                             int64_t num_slots, const q4_slot_layout *layout,
+                             const void *mid_bf16, int64_t M,
+                             const int32_t *slot_ids, int64_t K, int64_t H,
+                             int64_t I, const void *out_bf16,
+                             const void *workspace, size_t workspace_bytes);
+
 /* Message for the last failing call on this thread ("" after success). */
 const char *q4_last_error(void);
 
-/* ABI version: 2 (1 plus the down projection and whole-expert calls). */
+/* ABI version: 3 (1 plus the down projection and whole-expert calls, and the
+ * Q8 family). */
 int q4_abi_version(void);
 
 #ifdef __cplusplus

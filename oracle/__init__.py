@@ -11,6 +11,8 @@ from .q4_oracle import (  # noqa: F401
     f32_parts,
     check_layout,
     q4_weights,
+    q8_weights,
+    weight_bytes,
     row_scales,
     exact_dots,
     scaled_f32,

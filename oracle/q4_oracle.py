@@ -31,6 +31,11 @@ What it computes, and where the pages define it (pages of the diff of
   ``out[m, h] = bf16((sum_i (q_hi - 8) mid[m, i]) * down_scale[h])``, the sum
   again taken exactly and the F32 product rounded once.  ``validateCall``
   requires both dimensions divisible by 8 and every field inside the slot.
+* Q8 family -- same page, ``Q8_GATE_UP_SOURCE``, ``Q8_DOWN_SOURCE`` and
+  ``Glm52CanonicalQ8MetalExecutor``: the same computation with signed int8
+  weights, one byte per weight, row-major (``[I][H]`` for gate/up,
+  ``[H][I]`` for down), no zero point.  Every call below takes
+  ``fmt="q4"`` or ``fmt="q8"``.
 * Grouped call -- row independence stated on page 52 (one launch geometry for
   every batch width; each sample and row is computed on its own): output
   ``[t, j, :]`` is the single-expert result for token ``t`` on slot
@@ -149,13 +154,13 @@ def _check_range(offset: int, length: int, slot_bytes: int, label: str) -> None:
         raise ValueError(f"{label} exceeds the canonical expert slot")
 
 
-def check_layout(layout, H: int, I: int) -> None:
+def check_layout(layout, H: int, I: int, fmt: str = "q4") -> None:
     """Range rules of validateRange / validateCall for the gate/up fields."""
     if H <= 0 or I <= 0 or layout.slot_bytes <= 0:
         raise ValueError("hidden size, intermediate size and slot bytes must be positive")
     if H % 8:
-        raise ValueError("Q4 expert dimensions must be divisible by 8")
-    wb = I * H // 2
+        raise ValueError(f"{fmt.upper()} expert dimensions must be divisible by 8")
+    wb = weight_bytes(I, H, fmt)
     _check_range(layout.gate_weight_offset, wb, layout.slot_bytes, "gate weights")
     _check_range(layout.up_weight_offset, wb, layout.slot_bytes, "up weights")
     _check_range(layout.gate_scale_offset, 4 * I, layout.slot_bytes, "gate scales")
@@ -164,6 +169,24 @@ def check_layout(layout, H: int, I: int) -> None:
         _check_range(layout.down_weight_offset, wb, layout.slot_bytes, "down weights")
     if layout.down_scale_offset != OFFSET_ABSENT:
         _check_range(layout.down_scale_offset, 4 * H, layout.slot_bytes, "down scales")
+
+
+def weight_bytes(rows: int, K: int, fmt: str) -> int:
+    """Bytes of a ``[rows, K]`` weight matrix: two weights per byte (Q4) or one (Q8)."""
+    if fmt == "q4":
+        return rows * K // 2
+    if fmt == "q8":
+        return rows * K
+    raise ValueError(f"unknown weight format {fmt!r}")
+
+
+def q8_weights(slot: np.ndarray, offset: int, R: int, C: int) -> np.ndarray:
+    """Decode a ``[R, C]`` matrix of signed int8 weights stored row-major at ``offset``."""
+    return np.frombuffer(slot, dtype=np.int8, count=R * C, offset=offset).reshape(R, C).copy()
+
+
+def decode_weights(slot: np.ndarray, offset: int, R: int, C: int, fmt: str) -> np.ndarray:
+    return q4_weights(slot, offset, R, C) if fmt == "q4" else q8_weights(slot, offset, R, C)
 
 
 def q4_weights(slot: np.ndarray, offset: int, I: int, H: int) -> np.ndarray:
@@ -210,9 +233,9 @@ def exact_dots(w: np.ndarray, xbits: np.ndarray) -> Tuple[List[List[int]], List[
     Each token's x is scaled by a power of two to integers ``X`` (exact: the
     scale is that token's smallest exponent).  ``|X|`` may be wider than 64
     bits, so it is cut into signed 24-bit limbs.  Each limb product is a
-    float64 matrix product in which every product ``w * limb`` (|w| <= 8) and
-    every partial sum of at most H <= 2**16 of them is an integer of magnitude
-    below 2**43, hence exactly representable: the product is exact whatever
+    float64 matrix product in which every product ``w * limb`` (|w| <= 128)
+    and every partial sum of at most H <= 2**16 of them is an integer of
+    magnitude below 2**47, hence exactly representable: the product is exact whatever
     order the library sums in.  Limbs are recombined in Python integers.
     """
     I, H = w.shape
@@ -287,17 +310,17 @@ def swiglu_tail(gate: np.ndarray, up: np.ndarray) -> np.ndarray:
 # The two calls
 # ---------------------------------------------------------------------------
 
-def expert_gate_up(slot: np.ndarray, layout, xbits: np.ndarray, H: int, I: int):
+def expert_gate_up(slot: np.ndarray, layout, xbits: np.ndarray, H: int, I: int, fmt: str = "q4"):
     """Single expert: returns ``(gate f32 [M,I], up f32 [M,I], out bf16 bits [M,I])``."""
     slot = np.ascontiguousarray(slot, dtype=np.uint8).reshape(-1)
     xbits = np.ascontiguousarray(xbits, dtype=np.uint16).reshape(-1, H)
-    check_layout(layout, H, I)
+    check_layout(layout, H, I, fmt)
     if slot.size < layout.slot_bytes:
         raise ValueError("canonical expert slot array is shorter than its layout")
     if xbits.shape[0] < 1:
         raise ValueError("Q4 expert gate/up requires input [M,H] with M >= 1")
-    wg = q4_weights(slot, layout.gate_weight_offset, I, H)
-    wu = q4_weights(slot, layout.up_weight_offset, I, H)
+    wg = decode_weights(slot, layout.gate_weight_offset, I, H, fmt)
+    wu = decode_weights(slot, layout.up_weight_offset, I, H, fmt)
     sg = row_scales(slot, layout.gate_scale_offset, I)
     su = row_scales(slot, layout.up_scale_offset, I)
     gate = scaled_f32(*exact_dots(wg, xbits), sg)
@@ -306,7 +329,7 @@ def expert_gate_up(slot: np.ndarray, layout, xbits: np.ndarray, H: int, I: int):
 
 
 def expert_gate_up_grouped(slots: np.ndarray, slot_stride: int, num_slots: int, layout,
-                           xbits: np.ndarray, ids: np.ndarray, H: int, I: int):
+                           xbits: np.ndarray, ids: np.ndarray, H: int, I: int, fmt: str = "q4"):
     """Grouped call over routed slots.
 
     Returns ``(gate [M,K,I], up [M,K,I], out bits [M,K,I], invalid_count)``.
@@ -332,7 +355,7 @@ def expert_gate_up_grouped(slots: np.ndarray, slot_stride: int, num_slots: int, 
     for e, pairs in sorted(by_slot.items()):
         slot = flat[e * slot_stride:e * slot_stride + layout.slot_bytes]
         toks = [t for t, _ in pairs]
-        g, u, o = expert_gate_up(slot, layout, xbits[toks], H, I)
+        g, u, o = expert_gate_up(slot, layout, xbits[toks], H, I, fmt)
         for r, (t, j) in enumerate(pairs):
             gate[t, j] = g[r]
             up[t, j] = u[r]
@@ -344,16 +367,16 @@ def expert_gate_up_grouped(slots: np.ndarray, slot_stride: int, num_slots: int, 
 # Down projection and the whole expert (page 52, DOWN_SOURCE and execute)
 # ---------------------------------------------------------------------------
 
-def check_down_layout(layout, H: int, I: int) -> None:
+def check_down_layout(layout, H: int, I: int, fmt: str = "q4") -> None:
     """validateCall's rules for a call that reads the down fields too."""
-    check_layout(layout, H, I)
+    check_layout(layout, H, I, fmt)
     if I % 8:
-        raise ValueError("Q4 expert dimensions must be divisible by 8")
+        raise ValueError(f"{fmt.upper()} expert dimensions must be divisible by 8")
     if layout.down_weight_offset == OFFSET_ABSENT or layout.down_scale_offset == OFFSET_ABSENT:
         raise ValueError("down weights exceeds the canonical expert slot")
 
 
-def expert_down(slot: np.ndarray, layout, midbits: np.ndarray, H: int, I: int):
+def expert_down(slot: np.ndarray, layout, midbits: np.ndarray, H: int, I: int, fmt: str = "q4"):
     """Down projection of one slot: returns ``(down f32 [M,H], out bf16 bits [M,H])``.
 
     Row ``h`` of the down matrix is ``I/8`` words at
@@ -363,26 +386,26 @@ def expert_down(slot: np.ndarray, layout, midbits: np.ndarray, H: int, I: int):
     """
     slot = np.ascontiguousarray(slot, dtype=np.uint8).reshape(-1)
     midbits = np.ascontiguousarray(midbits, dtype=np.uint16).reshape(-1, I)
-    check_down_layout(layout, H, I)
+    check_down_layout(layout, H, I, fmt)
     if slot.size < layout.slot_bytes:
         raise ValueError("canonical expert slot array is shorter than its layout")
-    wd = q4_weights(slot, layout.down_weight_offset, H, I)
+    wd = decode_weights(slot, layout.down_weight_offset, H, I, fmt)
     sd = row_scales(slot, layout.down_scale_offset, H)
     down = scaled_f32(*exact_dots(wd, midbits), sd)
     return down, f32_to_bf16(down)
 
 
-def expert_forward(slot: np.ndarray, layout, xbits: np.ndarray, H: int, I: int):
+def expert_forward(slot: np.ndarray, layout, xbits: np.ndarray, H: int, I: int, fmt: str = "q4"):
     """The whole expert of one slot, as ``execute`` chains its two kernels:
     returns ``(mid bf16 bits [M,I], out bf16 bits [M,H])``."""
-    check_down_layout(layout, H, I)
-    _, _, mid = expert_gate_up(slot, layout, xbits, H, I)
-    _, out = expert_down(slot, layout, mid, H, I)
+    check_down_layout(layout, H, I, fmt)
+    _, _, mid = expert_gate_up(slot, layout, xbits, H, I, fmt)
+    _, out = expert_down(slot, layout, mid, H, I, fmt)
     return mid, out
 
 
 def expert_down_grouped(slots: np.ndarray, slot_stride: int, num_slots: int, layout,
-                        midbits: np.ndarray, ids: np.ndarray, H: int, I: int):
+                        midbits: np.ndarray, ids: np.ndarray, H: int, I: int, fmt: str = "q4"):
     """Grouped down projection: pair ``(t, j)`` runs its own input row
     ``mid[t, j, :]`` against slot ``ids[t, j]`` and writes ``out[t, j, :]``.
 
@@ -407,7 +430,7 @@ def expert_down_grouped(slots: np.ndarray, slot_stride: int, num_slots: int, lay
     for e, pairs in sorted(by_slot.items()):
         slot = flat[e * slot_stride:e * slot_stride + layout.slot_bytes]
         rows = np.stack([midbits[t, j] for t, j in pairs])
-        d, o = expert_down(slot, layout, rows, H, I)
+        d, o = expert_down(slot, layout, rows, H, I, fmt)
         for r, (t, j) in enumerate(pairs):
             down[t, j] = d[r]
             out[t, j] = o[r]
@@ -415,9 +438,9 @@ def expert_down_grouped(slots: np.ndarray, slot_stride: int, num_slots: int, lay
 
 
 def expert_forward_grouped(slots: np.ndarray, slot_stride: int, num_slots: int, layout,
-                           xbits: np.ndarray, ids: np.ndarray, H: int, I: int):
+                           xbits: np.ndarray, ids: np.ndarray, H: int, I: int, fmt: str = "q4"):
     """Grouped whole expert: returns ``(mid bits [M,K,I], out bits [M,K,H], invalid_count)``."""
-    check_down_layout(layout, H, I)
-    _, _, mid, invalid = expert_gate_up_grouped(slots, slot_stride, num_slots, layout, xbits, ids, H, I)
-    _, out, _ = expert_down_grouped(slots, slot_stride, num_slots, layout, mid, ids, H, I)
+    check_down_layout(layout, H, I, fmt)
+    _, _, mid, invalid = expert_gate_up_grouped(slots, slot_stride, num_slots, layout, xbits, ids, H, I, fmt)
+    _, out, _ = expert_down_grouped(slots, slot_stride, num_slots, layout, mid, ids, H, I, fmt)
     return mid, out, invalid

@@ -60,7 +60,8 @@ __host__ __device__ inline int bat_chunk_steps(int ntiles, int S) {
 // DOWN: the down projection (one matrix of a.I rows over a.H inputs; a tile is
 // 32 rows, its first 16 taking the gate role and the next 16 the up role,
 // each output rounded to bf16 on its own) instead of gate/up + SwiGLU.
-template <int NT, bool VEC, bool DOWN>
+// Q8: signed int8 weights, one byte per weight (else packed nibbles).
+template <int NT, bool VEC, bool DOWN, bool Q8>
 __global__ __launch_bounds__(kBatThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void batch_kernel(const GateUpParams a) {
   // pairs per token group: up to 16*NT/4 (four digits), trimmed to 16*NT/6
@@ -87,7 +88,8 @@ void batch_kernel(const GateUpParams a) {
   const int T = a.num_slots * tps;
   const int NB = gridDim.x;
   const int v0 = (int)((int64_t)blockIdx.x * T / NB), v1 = (int)((int64_t)(blockIdx.x + 1) * T / NB);
-  const uint32_t wbytes = (uint32_t)((uint64_t)I * (uint32_t)(H / 2));
+  const uint32_t rbytes = row_bytes<Q8>(H);  // bytes of one weight row
+  const uint32_t wbytes = (uint32_t)((uint64_t)I * rbytes);
 
   if constexpr (!DOWN)
     for (int i = tid; i < kSigTable; i += kBatThreads) s_sig[i] = sigmoid_bf16(sig_table_bits(i));
@@ -124,7 +126,7 @@ void batch_kernel(const GateUpParams a) {
     const __amdgpu_buffer_rsrc_t gsrc = make_rsrc(slot + a.gate_w_off, wbytes);
     // DOWN: rows 16..31 of each tile are the same matrix 16 rows further on
     // (loads past its end return zeros, for rows that are never stored)
-    const uint32_t skip = 16u * (uint32_t)(H / 2);
+    const uint32_t skip = 16u * rbytes;
     const __amdgpu_buffer_rsrc_t usrc =
         DOWN ? make_rsrc(slot + a.gate_w_off + skip, wbytes > skip ? wbytes - skip : 0u)
              : make_rsrc(slot + a.up_w_off, wbytes);
@@ -187,16 +189,16 @@ void batch_kernel(const GateUpParams a) {
       for (int t = lt; t < t1; t += kBatWaves) left += S;
       auto row_off = [&](int tile) {
         const int row = tile * RT + cc;
-        return (uint32_t)(row < I ? row : I - 1) * (uint32_t)(H / 2) + (uint32_t)(g4 * 16);
+        return (uint32_t)(row < I ? row : I - 1) * rbytes + (uint32_t)g4 * group_bytes<Q8>();
       };
       uint32_t loff = row_off(lt);
       // always two loads per call (kOffNone once the wave's tiles are all
       // issued), so that the compiler's wait counts stay exact
-      auto issue = [&](v4u& g, v4u& u_) {
+      auto issue = [&](StepW<Q8>& g, StepW<Q8>& u_) {
         const bool live = left > 0;
-        const uint32_t o = live ? loff + (uint32_t)ls * 64u : kOffNone;
-        g = load16<VEC>(gsrc, o);
-        u_ = load16<VEC>(usrc, o);
+        const uint32_t o = live ? loff + (uint32_t)ls * step_row_bytes<Q8>() : kOffNone;
+        load_step<Q8, VEC>(g, gsrc, o);
+        load_step<Q8, VEC>(u_, usrc, o);
         // cursor step without branches, so the loads stay unconditional
         left -= live ? 1 : 0;
         const int nls = ls + (live ? 1 : 0);
@@ -302,7 +304,7 @@ void batch_kernel(const GateUpParams a) {
       stage(0, s_buf);
       __syncthreads();
       // the weights of this wave's first tile go out now
-      v4u rg0, ru0, rg1, ru1;
+      StepW<Q8> rg0, ru0, rg1, ru1;
       issue(rg0, ru0);
       issue(rg1, ru1);
       int gch = 0;                                     // chunks done in this group (buffer parity)
@@ -321,10 +323,10 @@ void batch_kernel(const GateUpParams a) {
           if (nch > 1 && more) stage((c + 1) % nch, half(gch + 1));
           if (active) {
             const int sa = c * spc, se = min(S, sa + spc);
-            auto compute = [&](const v4u& g, const v4u& u_, int s) {
+            auto compute = [&](const StepW<Q8>& g, const StepW<Q8>& u_, int s) {
               v4i ge, go, ue, uo;
-              split_weights(g, ge, go);
-              split_weights(u_, ue, uo);
+              split_step(g, ge, go);
+              split_step(u_, ue, uo);
               const uint8_t* bp = buf + (s - sa) * sb + lane * 16;
               v4i be[NT], bo[NT];
 #pragma unroll
@@ -375,7 +377,7 @@ void batch_kernel(const GateUpParams a) {
                 const int64_t vg = quad_row_sum(accg[n]);
                 const int64_t vu = quad_row_sum(accu[n]);
                 if (ti < count && row < I) {
-                  const int e2 = sum_exponent(s_xmax[ti]) + 16;
+                  const int e2 = sum_exponent(s_xmax[ti]) + 16 + weight_exp_shift<Q8>();
                   const float gate = round_scaled(vg >> 24, vg & 0xFFFFFF, e2, gscale[row]);
                   const uint64_t o = (uint64_t)s_pairs[ti] * I + row;
                   if constexpr (DOWN) {
@@ -431,7 +433,7 @@ void batch_kernel(const GateUpParams a) {
                   const int64_t hi = L == 6 ? (int64_t)d[3] + ((int64_t)d[4] << 8) + ((int64_t)d[5] << 16)
                                             : (int64_t)d[3];
                   const int xm = s_xmax[ti];
-                  float r = round_scaled(hi, lo, sum_exponent(xm) + 8 * (6 - L),
+                  float r = round_scaled(hi, lo, sum_exponent(xm) + 8 * (6 - L) + weight_exp_shift<Q8>(),
                                          (part && !DOWN) ? uscale[row] : gscale[row]);
                   if (xm >= 0x7F80) r = __builtin_nanf("");
                   if constexpr (DOWN) {
@@ -463,7 +465,7 @@ void batch_kernel(const GateUpParams a) {
 
 namespace {
 
-template <int NT, bool VEC, bool DOWN>
+template <int NT, bool VEC, bool DOWN, bool Q8>
 int batch_blocks(int device) {
   static int cached[64] = {0};
   if (device < 0 || device >= 64) device = 0;
@@ -472,7 +474,7 @@ int batch_blocks(int device) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0)
       cus = 256;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&batch_kernel<NT, VEC, DOWN>), kBatThreads, 0) != hipSuccess ||
+            &per_cu, reinterpret_cast<const void*>(&batch_kernel<NT, VEC, DOWN, Q8>), kBatThreads, 0) != hipSuccess ||
         per_cu <= 0)
       per_cu = 1;
     cached[device] = cus * per_cu;
@@ -480,25 +482,27 @@ int batch_blocks(int device) {
   return cached[device];
 }
 
-template <int NT, bool VEC, bool DOWN>
+template <int NT, bool VEC, bool DOWN, bool Q8>
 hipError_t launch_batch_t(GateUpParams& p, hipStream_t stream) {
   int device = 0;
   if (hipGetDevice(&device) != hipSuccess) device = 0;
   const int rt = DOWN ? 32 : 16;
   const int tiles = p.num_slots * ((p.I + rt - 1) / rt);
-  int nb = batch_blocks<NT, VEC, DOWN>(device);
+  int nb = batch_blocks<NT, VEC, DOWN, Q8>(device);
   if (nb > tiles) nb = tiles;
   void* args[] = {&p};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&batch_kernel<NT, VEC, DOWN>), dim3((unsigned)nb),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&batch_kernel<NT, VEC, DOWN, Q8>), dim3((unsigned)nb),
                          dim3(kBatThreads), args, 0, stream);
 }
 
-template <bool DOWN>
+template <bool DOWN, bool Q8>
 hipError_t launch_batch_m(GateUpParams& p, int nt, hipStream_t stream) {
-  const bool vec = (p.H % 32) == 0;
-  if (nt == 1) return vec ? launch_batch_t<1, true, DOWN>(p, stream) : launch_batch_t<1, false, DOWN>(p, stream);
-  if (nt == 2) return vec ? launch_batch_t<2, true, DOWN>(p, stream) : launch_batch_t<2, false, DOWN>(p, stream);
-  return vec ? launch_batch_t<3, true, DOWN>(p, stream) : launch_batch_t<3, false, DOWN>(p, stream);
+  const bool vec = row_bytes<Q8>(p.H) % 16 == 0;
+  if (nt == 1)
+    return vec ? launch_batch_t<1, true, DOWN, Q8>(p, stream) : launch_batch_t<1, false, DOWN, Q8>(p, stream);
+  if (nt == 2)
+    return vec ? launch_batch_t<2, true, DOWN, Q8>(p, stream) : launch_batch_t<2, false, DOWN, Q8>(p, stream);
+  return vec ? launch_batch_t<3, true, DOWN, Q8>(p, stream) : launch_batch_t<3, false, DOWN, Q8>(p, stream);
 }
 
 }  // namespace
@@ -508,7 +512,8 @@ hipError_t launch_batch(GateUpParams p, int tokens_per_slot, hipStream_t stream)
   p.steps += p.steps & 1;
   const int nt = tokens_per_slot <= 2 ? 1 : (tokens_per_slot <= 5 ? 2 : 3);
   p.G = (16 * nt) / 4;
-  return p.down ? launch_batch_m<true>(p, nt, stream) : launch_batch_m<false>(p, nt, stream);
+  if (p.q8) return p.down ? launch_batch_m<true, true>(p, nt, stream) : launch_batch_m<false, true>(p, nt, stream);
+  return p.down ? launch_batch_m<true, false>(p, nt, stream) : launch_batch_m<false, false>(p, nt, stream);
 }
 
 }  // namespace q4

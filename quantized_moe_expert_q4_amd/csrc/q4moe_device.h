@@ -1,7 +1,8 @@
-// Device arithmetic shared by the Q4 gate/up kernels (single-expert and
-// grouped paths): activation digit split, weight split, exact recombination
-// with one F32 rounding, and the SwiGLU tail of GATE_UP_SOURCE (diff page 52
-// of @mlx-bun/inference 1.0.0, kernels/glm52/streamed-experts.ts).
+// Device arithmetic shared by the expert kernels (single-expert and grouped
+// paths, Q4 and Q8 weights, gate/up and down): activation digit split, weight
+// split, exact recombination with one F32 rounding, and the SwiGLU tail of
+// GATE_UP_SOURCE (diff page 52 of @mlx-bun/inference 1.0.0,
+// kernels/glm52/streamed-experts.ts).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -212,6 +213,53 @@ __device__ __forceinline__ void split_weights(const v4u w, v4i& ev, v4i& od) {
   ev.w = (int)((a3 << 4) & 0xF0F0F0F0u);
 }
 
+
+// Signed int8 weights (the Q8 family of page 52, Q8_GATE_UP_SOURCE): the
+// even (positions 0,2,..,30) and odd bytes of 32 consecutive weights, the
+// same operand order split_weights gives for 32 nibbles, with weight factor 1.
+__device__ __forceinline__ void split_bytes(const v4u a, const v4u b, v4i& ev, v4i& od) {
+  ev.x = (int)perm(a.y, a.x, 0x06040200u);
+  od.x = (int)perm(a.y, a.x, 0x07050301u);
+  ev.y = (int)perm(a.w, a.z, 0x06040200u);
+  od.y = (int)perm(a.w, a.z, 0x07050301u);
+  ev.z = (int)perm(b.y, b.x, 0x06040200u);
+  od.z = (int)perm(b.y, b.x, 0x07050301u);
+  ev.w = (int)perm(b.w, b.z, 0x06040200u);
+  od.w = (int)perm(b.w, b.z, 0x07050301u);
+}
+
+// One lane's weights of one K-step (128 weights of a row, the lane's k-group
+// holding 32 of them): 16 bytes of packed nibbles (Q4) or 32 int8 (Q8).
+template <bool Q8>
+struct StepW {
+  v4u a;
+};
+template <>
+struct StepW<true> {
+  v4u a, b;
+};
+
+// Row bytes of one K-step and of one k-group's share of it.
+template <bool Q8>
+__host__ __device__ constexpr uint32_t step_row_bytes() { return Q8 ? 128u : 64u; }
+template <bool Q8>
+__host__ __device__ constexpr uint32_t group_bytes() { return Q8 ? 32u : 16u; }
+// Bytes of one weight row of K values.
+template <bool Q8>
+__host__ __device__ constexpr uint32_t row_bytes(int K) { return Q8 ? (uint32_t)K : (uint32_t)(K / 2); }
+// Exponent of the integer weight factor the MFMA operands carry (16 for the
+// nibble split, 1 for int8 bytes), relative to the nibble split.
+template <bool Q8>
+__host__ __device__ constexpr int weight_exp_shift() { return Q8 ? 4 : 0; }
+
+template <bool Q8, bool VEC>
+__device__ __forceinline__ void load_step(StepW<Q8>& w, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  w.a = load16<VEC>(r, off);
+  if constexpr (Q8) w.b = load16<VEC>(r, off + 16u);
+}
+
+__device__ __forceinline__ void split_step(const StepW<false>& w, v4i& ev, v4i& od) { split_weights(w.a, ev, od); }
+__device__ __forceinline__ void split_step(const StepW<true>& w, v4i& ev, v4i& od) { split_bytes(w.a, w.b, ev, od); }
 
 // Byte transpose of eight digit words: lo[p]/hi[p] hold digits 0..3 / 4..5 of
 // position p (p = 0..7 of one packed word); d[s] receives digit s of the four

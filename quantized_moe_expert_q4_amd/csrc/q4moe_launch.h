@@ -25,6 +25,7 @@ struct GateUpParams {
   int G, steps;              // set by the launchers: tokens per group, K-steps per tile
   int wave_share;            // set by launch_resident: a SIMD's first-wave share, 1/1024
   int down;                  // 1: down projection (see above)
+  int q8;                    // 1: signed int8 weights [rows][H] (else packed nibbles [rows][H/8] words)
 };
 
 // Resident-digits kernel for token groups of at most two (decode widths):

@@ -64,7 +64,8 @@ __host__ __device__ constexpr int res_tiles(int M) { return M <= 2 ? 1 : 2; }
 // DOWN: the down projection (one matrix of a.I rows over a.H inputs; a tile is
 // 32 rows, its first 16 taking the gate role and the next 16 the up role,
 // each output rounded to bf16 on its own) instead of gate/up + SwiGLU.
-template <int NT, bool VEC, bool DOWN>
+// Q8: signed int8 weights, one byte per weight (else packed nibbles).
+template <int NT, bool VEC, bool DOWN, bool Q8>
 __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void resident_kernel(const GateUpParams a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_lds[kResLds];
   __shared__ int s_pairs[kResMaxPairs];
@@ -92,7 +93,8 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int T = a.num_slots * tps;
   const int NB = gridDim.x;
   const int v0 = (int)((int64_t)blockIdx.x * T / NB), v1 = (int)((int64_t)(blockIdx.x + 1) * T / NB);
-  const uint32_t wbytes = (uint32_t)((uint64_t)I * (uint32_t)(H / 2));
+  const uint32_t rbytes = row_bytes<Q8>(H);  // bytes of one weight row
+  const uint32_t wbytes = (uint32_t)((uint64_t)I * rbytes);
   const uint64_t below = (1ull << lane) - 1ull;
   unsigned long long* const s_fix = (unsigned long long*)(s_lds + S * sbytes);
 
@@ -170,7 +172,7 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
     if constexpr (DOWN) {
       // rows 16..31 of each tile: the same matrix 16 rows further on (loads
       // past its end return zeros, for rows that are never stored)
-      const uint32_t skip = 16u * (uint32_t)(H / 2);
+      const uint32_t skip = 16u * rbytes;
       usrc = make_rsrc(slot + a.gate_w_off + skip, wbytes > skip ? wbytes - skip : 0u);
     } else {
       usrc = make_rsrc(slot + a.up_w_off, wbytes);
@@ -184,15 +186,15 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
 
   auto row_off = [&](int tile) {
     const int row = tile * RT + cc;
-    return (uint32_t)(row < I ? row : I - 1) * (uint32_t)(H / 2) + (uint32_t)(g4 * 16);
+    return (uint32_t)(row < I ? row : I - 1) * rbytes + (uint32_t)g4 * group_bytes<Q8>();
   };
-  v4u rg[kResD], ru[kResD];
+  StepW<Q8> rg[kResD], ru[kResD];
   int lt = 0, ls = 0;                        // load cursor (tile, step)
   uint32_t loff = 0;
-  auto issue = [&](v4u& g, v4u& u_, bool live) {
-    const uint32_t o = live ? loff + (uint32_t)ls * 64u : kOffNone;
-    g = load16<VEC>(gsrc, o);
-    u_ = load16<VEC>(usrc, o);
+  auto issue = [&](StepW<Q8>& g, StepW<Q8>& u_, bool live) {
+    const uint32_t o = live ? loff + (uint32_t)ls * step_row_bytes<Q8>() : kOffNone;
+    load_step<Q8, VEC>(g, gsrc, o);
+    load_step<Q8, VEC>(u_, usrc, o);
     // cursor step without branches, so the loads stay unconditional
     const int nls = ls + (live ? 1 : 0);
     const bool wrap = nls == S;
@@ -413,7 +415,7 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
       for (int n = 0; n < NT; ++n) {
         int mp = -1;
         for (int q = 0; q < count; ++q)
-          if (gtok[q] == ltok[n]) mp = mp < 0 ? gpair[q] : -2;
+          if (gtok[q] == ltok[n]) mp = mp == -1 ? gpair[q] : -2;   // -2: two or more
         mypair[n] = mp;
         multi = multi || __ballot(lok[n] && mp == -2) != 0;
       }
@@ -444,8 +446,8 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
           for (int d = 0; d < kResD; ++d) {
             v4i ge, go, ue, uo;
-            split_weights(rg[d], ge, go);
-            split_weights(ru[d], ue, uo);
+            split_step(rg[d], ge, go);
+            split_step(ru[d], ue, uo);
             // the slot's registers are free once split: refill it before the multiply
             issue(rg[d], ru[d], u + d + kResD < ub);
             const uint8_t* bp = s_lds + (s + d) * sbytes + rdo[d & 3];
@@ -539,7 +541,7 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
             uint16_t ov = 0;
             if (ok) {
               const int xm = lxm[n];
-              const int e2 = sum_exponent(xm) + e2off;
+              const int e2 = sum_exponent(xm) + e2off + weight_exp_shift<Q8>();
               if (W == 4) {
                 gate = round_scaled53(gq[n], e2, gscr);
                 up = round_scaled53(uq[n], e2, uscr);
@@ -617,7 +619,7 @@ constexpr int kWaveShare2 = 547;
 
 // Work-groups that fit the device at once (one per CU: the LDS arrays take
 // most of a CU's 160 KiB).
-template <int NT, bool VEC, bool DOWN>
+template <int NT, bool VEC, bool DOWN, bool Q8>
 int resident_blocks(int device) {
   static int cached[64] = {0};
   if (device < 0 || device >= 64) device = 0;
@@ -626,7 +628,7 @@ int resident_blocks(int device) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0)
       cus = 256;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&resident_kernel<NT, VEC, DOWN>), kResThreads, 0) != hipSuccess ||
+            &per_cu, reinterpret_cast<const void*>(&resident_kernel<NT, VEC, DOWN, Q8>), kResThreads, 0) != hipSuccess ||
         per_cu <= 0)
       per_cu = 1;
     cached[device] = cus * per_cu;
@@ -634,25 +636,25 @@ int resident_blocks(int device) {
   return cached[device];
 }
 
-template <int NT, bool VEC, bool DOWN>
+template <int NT, bool VEC, bool DOWN, bool Q8>
 hipError_t launch_resident_t(GateUpParams& p, hipStream_t stream) {
   int device = 0;
   if (hipGetDevice(&device) != hipSuccess) device = 0;
   const int rt = DOWN ? 32 : 16;
   const int tiles = p.num_slots * ((p.I + rt - 1) / rt);
-  int nb = resident_blocks<NT, VEC, DOWN>(device);
+  int nb = resident_blocks<NT, VEC, DOWN, Q8>(device);
   if (nb > tiles) nb = tiles;
   void* args[] = {&p};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&resident_kernel<NT, VEC, DOWN>), dim3((unsigned)nb),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&resident_kernel<NT, VEC, DOWN, Q8>), dim3((unsigned)nb),
                          dim3(kResThreads), args, 0, stream);
 }
 
-template <bool DOWN>
+template <bool DOWN, bool Q8>
 hipError_t launch_resident_m(GateUpParams& p, hipStream_t stream) {
-  const bool vec = (p.H % 32) == 0;
+  const bool vec = row_bytes<Q8>(p.H) % 16 == 0;
   if (res_tiles(p.M) == 1)
-    return vec ? launch_resident_t<1, true, DOWN>(p, stream) : launch_resident_t<1, false, DOWN>(p, stream);
-  return vec ? launch_resident_t<2, true, DOWN>(p, stream) : launch_resident_t<2, false, DOWN>(p, stream);
+    return vec ? launch_resident_t<1, true, DOWN, Q8>(p, stream) : launch_resident_t<1, false, DOWN, Q8>(p, stream);
+  return vec ? launch_resident_t<2, true, DOWN, Q8>(p, stream) : launch_resident_t<2, false, DOWN, Q8>(p, stream);
 }
 
 }  // namespace
@@ -669,7 +671,8 @@ hipError_t launch_resident(GateUpParams p, hipStream_t stream) {
   p.steps = res_steps(p.H);
   p.G = kResMaxPairs;
   p.wave_share = res_tiles(p.M) == 1 ? kWaveShare1 : kWaveShare2;
-  return p.down ? launch_resident_m<true>(p, stream) : launch_resident_m<false>(p, stream);
+  if (p.q8) return p.down ? launch_resident_m<true, true>(p, stream) : launch_resident_m<false, true>(p, stream);
+  return p.down ? launch_resident_m<true, false>(p, stream) : launch_resident_m<false, false>(p, stream);
 }
 
 hipError_t launch_gate_up(const GateUpParams& p, int tokens_per_slot, hipStream_t stream) {

@@ -54,16 +54,22 @@ class SlotLayout:
     down_scale_offset: int = OFFSET_ABSENT
 
 
-def contiguous_layout(H: int, I: int, align: int = 4096) -> SlotLayout:
+def _wbytes(rows: int, K: int, fmt: str) -> int:
+    """Bytes of a ``[rows, K]`` weight matrix: packed nibbles (q4) or int8 (q8)."""
+    return rows * K // 2 if fmt == "q4" else rows * K
+
+
+def contiguous_layout(H: int, I: int, align: int = 4096, fmt: str = "q4") -> SlotLayout:
     """Gate words, up words, gate scales, up scales back to back.
 
     Each field starts on a 16-byte boundary (a no-op for the five workloads,
-    whose fields are all multiples of 16 bytes long).
+    whose fields are all multiples of 16 bytes long).  ``fmt="q8"`` sizes
+    the weight fields for one int8 weight per byte.
     """
     def up16(n):
         return (n + 15) // 16 * 16
 
-    wbytes = I * H // 2
+    wbytes = _wbytes(I, H, fmt)
     gate_w = 0
     up_w = up16(wbytes)
     gate_s = up16(up_w + wbytes)
@@ -73,14 +79,15 @@ def contiguous_layout(H: int, I: int, align: int = 4096) -> SlotLayout:
     return SlotLayout(slot, gate_w, up_w, gate_s, up_s)
 
 
-def expert_layout(H: int, I: int, align: int = 4096) -> SlotLayout:
+def expert_layout(H: int, I: int, align: int = 4096, fmt: str = "q4") -> SlotLayout:
     """A whole-expert slot: gate words, up words, down words, gate scales, up
     scales, down scales back to back (16-byte aligned fields), padded to
-    ``align``.  Down words are ``[H][I/8]``, down scales ``[H]``."""
+    ``align``.  Down words are ``[H][I/8]`` (int8 ``[H][I]`` for q8), down
+    scales ``[H]``."""
     def up16(n):
         return (n + 15) // 16 * 16
 
-    wbytes = I * H // 2
+    wbytes = _wbytes(I, H, fmt)
     gate_w = 0
     up_w = up16(wbytes)
     down_w = up16(up_w + wbytes)
@@ -128,6 +135,21 @@ def _uniform_words(rng: np.random.Generator, I: int, H: int) -> np.ndarray:
     return rng.integers(0, 1 << 32, size=(I, H // 8), dtype=np.uint64).astype(np.uint32)
 
 
+def _uniform_weights(rng: np.random.Generator, rows: int, K: int, fmt: str) -> np.ndarray:
+    """A weight matrix as raw little-endian bytes: uniform nibbles packed in
+    words (q4), or uniform int8 in [-128, 127] (q8, drawn as 32-bit words
+    whose bytes are the weights, row-major)."""
+    if fmt == "q4":
+        return _uniform_words(rng, rows, K).astype("<u4").view(np.uint8).reshape(rows, K // 2)
+    w = rng.integers(0, 1 << 32, size=(rows, (K + 3) // 4), dtype=np.uint64).astype("<u4")
+    return w.view(np.uint8).reshape(rows, -1)[:, :K]
+
+
+def _zero_weight_row(fmt: str, K: int) -> np.ndarray:
+    """Bytes of a row of zero weights: all-8 nibbles (q4) or zero bytes (q8)."""
+    return np.full(K // 2, 0x88, np.uint8) if fmt == "q4" else np.zeros(K, np.uint8)
+
+
 def fill_slot(
     rng: np.random.Generator,
     H: int,
@@ -136,6 +158,7 @@ def fill_slot(
     scale_range=(0.005, 0.02),
     zero_row_fraction: float = 0.0,
     out: Optional[np.ndarray] = None,
+    fmt: str = "q4",
 ) -> np.ndarray:
     """Draw one expert slot into a uint8 array of ``layout.slot_bytes``.
 
@@ -149,26 +172,26 @@ def fill_slot(
         out = np.zeros(layout.slot_bytes, dtype=np.uint8)
     else:
         out[:] = 0
-    gw = _uniform_words(rng, I, H)
-    uw = _uniform_words(rng, I, H)
+    gw = _uniform_weights(rng, I, H, fmt)
+    uw = _uniform_weights(rng, I, H, fmt)
     lo, hi = scale_range
     gs = rng.uniform(lo, hi, size=I).astype(np.float32)
     us = rng.uniform(lo, hi, size=I).astype(np.float32)
     if zero_row_fraction:
         n = int(round(zero_row_fraction * I))
-        gw[rng.choice(I, n, replace=False)] = ALL_EIGHT_WORD
-        uw[rng.choice(I, n, replace=False)] = ALL_EIGHT_WORD
-    wb = I * H // 2
-    out[layout.gate_weight_offset:layout.gate_weight_offset + wb] = gw.astype("<u4").view(np.uint8).ravel()
-    out[layout.up_weight_offset:layout.up_weight_offset + wb] = uw.astype("<u4").view(np.uint8).ravel()
+        gw[rng.choice(I, n, replace=False)] = _zero_weight_row(fmt, H)
+        uw[rng.choice(I, n, replace=False)] = _zero_weight_row(fmt, H)
+    wb = _wbytes(I, H, fmt)
+    out[layout.gate_weight_offset:layout.gate_weight_offset + wb] = gw.ravel()
+    out[layout.up_weight_offset:layout.up_weight_offset + wb] = uw.ravel()
     out[layout.gate_scale_offset:layout.gate_scale_offset + 4 * I] = gs.astype("<f4").view(np.uint8)
     out[layout.up_scale_offset:layout.up_scale_offset + 4 * I] = us.astype("<f4").view(np.uint8)
     if layout.down_weight_offset != OFFSET_ABSENT:
-        dw = _uniform_words(rng, H, I)
+        dw = _uniform_weights(rng, H, I, fmt)
         ds = rng.uniform(lo, hi, size=H).astype(np.float32)
         if zero_row_fraction:
-            dw[rng.choice(H, int(round(zero_row_fraction * H)), replace=False)] = ALL_EIGHT_WORD
-        out[layout.down_weight_offset:layout.down_weight_offset + wb] = dw.astype("<u4").view(np.uint8).ravel()
+            dw[rng.choice(H, int(round(zero_row_fraction * H)), replace=False)] = _zero_weight_row(fmt, I)
+        out[layout.down_weight_offset:layout.down_weight_offset + wb] = dw.ravel()
         out[layout.down_scale_offset:layout.down_scale_offset + 4 * H] = ds.astype("<f4").view(np.uint8)
     return out
 
@@ -238,7 +261,7 @@ CONFIGS: Dict[str, dict] = {
 
 def make_config(name: str, M: Optional[int] = None, num_slots: Optional[int] = None,
                 H: Optional[int] = None, I: Optional[int] = None, seed: Optional[int] = None,
-                with_down: bool = False) -> Config:
+                with_down: bool = False, fmt: str = "q4") -> Config:
     """Build one of the five workloads (or a resized variant of it).
 
     ``cfg5`` needs ``M`` in {1, 4, 16, 32}; its x is drawn from seed 105+M.
@@ -246,12 +269,14 @@ def make_config(name: str, M: Optional[int] = None, num_slots: Optional[int] = N
     or scaled-up variants with the same distributions.  ``with_down`` lays
     the slots out as whole experts (``expert_layout``) and draws down weights
     and scales of the same distributions after each slot's gate/up fields.
+    ``fmt="q8"`` draws int8 weights uniform on [-128, 127] (one byte each)
+    in place of the packed nibbles; all-8 rows become zero rows.
     """
     spec = dict(CONFIGS[name])
     H = H or spec["H"]
     I = I or spec["I"]
     seed = spec["seed"] if seed is None else seed
-    layout = expert_layout(H, I) if with_down else contiguous_layout(H, I)
+    layout = expert_layout(H, I, fmt=fmt) if with_down else contiguous_layout(H, I, fmt=fmt)
     rng = np.random.default_rng(seed)
     if name == "cfg4":
         E = num_slots or spec["num_slots"]
@@ -259,14 +284,14 @@ def make_config(name: str, M: Optional[int] = None, num_slots: Optional[int] = N
         K = spec["K"] if E >= spec["K"] else E
         slots = np.zeros((E, layout.slot_bytes), dtype=np.uint8)
         for e in range(E):
-            fill_slot(rng, H, I, layout, spec["scale"], out=slots[e])
+            fill_slot(rng, H, I, layout, spec["scale"], out=slots[e], fmt=fmt)
         x = bf16_normal(rng, (M, H))
         ids = top_k_routing(rng, M, K, E)
         return Config(name, seed, H, I, M, layout, slots, x, ids, K)
     if name == "cfg5":
         if M is None:
             raise ValueError("cfg5 needs M")
-        slots = fill_slot(rng, H, I, layout, spec["scale"], spec["zero_rows"])[None, :]
+        slots = fill_slot(rng, H, I, layout, spec["scale"], spec["zero_rows"], fmt=fmt)[None, :]
         xrng = np.random.default_rng(seed + M)
         x = bf16_normal(xrng, (M, H))
         x = add_outliers(xrng, x, spec["outliers"])
@@ -275,6 +300,6 @@ def make_config(name: str, M: Optional[int] = None, num_slots: Optional[int] = N
     E = num_slots or 1
     slots = np.zeros((E, layout.slot_bytes), dtype=np.uint8)
     for e in range(E):
-        fill_slot(rng, H, I, layout, spec["scale"], out=slots[e])
+        fill_slot(rng, H, I, layout, spec["scale"], out=slots[e], fmt=fmt)
     x = bf16_normal(rng, (M, H))
     return Config(name, seed, H, I, M, layout, slots, x)

@@ -21,14 +21,14 @@ def say(*a):
     sys.stdout.flush()
 
 
-def run_single(slot_np, layout, xbits, H, I, probes=True):
+def run_single(slot_np, layout, xbits, H, I, probes=True, fmt="q4"):
     M = xbits.shape[0]
     slot = upload_slots(slot_np.reshape(1, -1))
     x = upload_bf16_bits(xbits)
     out = torch.empty((M, I), dtype=torch.bfloat16, device="cuda")
     g = torch.empty((M, I), dtype=torch.float32, device="cuda") if probes else None
     u = torch.empty((M, I), dtype=torch.float32, device="cuda") if probes else None
-    q4.expert_gate_up(slot, layout, x, M, H, I, out, g, u)
+    q4.expert_gate_up(slot, layout, x, M, H, I, out, g, u, fmt=fmt)
     torch.cuda.synchronize()
     res = [bf16_bits(out)]
     if probes:
@@ -36,7 +36,7 @@ def run_single(slot_np, layout, xbits, H, I, probes=True):
     return res
 
 
-def run_grouped(slots_np, layout, xbits, ids, H, I, probes=True, ws_fill=None, ws=None, slots=None):
+def run_grouped(slots_np, layout, xbits, ids, H, I, probes=True, ws_fill=None, ws=None, slots=None, fmt="q4"):
     """One grouped call.  `ws` reuses a workspace (left as the last call left
     it); otherwise a new one filled with `ws_fill` (default 0xAB).  `slots`
     passes slots already on the device (then `slots_np` gives only the shape)."""
@@ -53,7 +53,7 @@ def run_grouped(slots_np, layout, xbits, ids, H, I, probes=True, ws_fill=None, w
     if ws is None:
         ws = aligned_empty(wsb, 256)
         ws.fill_(0xAB if ws_fill is None else ws_fill)
-    q4.expert_gate_up_grouped(slots, slots_np.shape[1], E, layout, x, M, idt, K, H, I, out, ws, wsb, g, u)
+    q4.expert_gate_up_grouped(slots, slots_np.shape[1], E, layout, x, M, idt, K, H, I, out, ws, wsb, g, u, fmt=fmt)
     torch.cuda.synchronize()
     invalid = int(ws[:4].cpu().numpy().view(np.int32)[0])
     res = [bf16_bits(out)]
@@ -104,19 +104,19 @@ def check_parity(out, g, u, g_ref, u_ref, out_ref, label, require_exact_gate_up=
                 e2e_max=int(e2e.max()))
 
 
-def run_down_single(slot_np, layout, midbits, H, I):
+def run_down_single(slot_np, layout, midbits, H, I, fmt="q4"):
     """One single-slot down call: returns (out bf16 bits [M,H], F32 probe [M,H])."""
     M = midbits.shape[0]
     slot = upload_slots(slot_np.reshape(1, -1))
     mid = upload_bf16_bits(midbits)
     out = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
     d = torch.empty((M, H), dtype=torch.float32, device="cuda")
-    q4.expert_down(slot, layout, mid, M, H, I, out, d)
+    q4.expert_down(slot, layout, mid, M, H, I, out, d, fmt=fmt)
     torch.cuda.synchronize()
     return bf16_bits(out), d.cpu().numpy()
 
 
-def run_down_grouped(slots_np, layout, midbits, ids, H, I, slots=None):
+def run_down_grouped(slots_np, layout, midbits, ids, H, I, slots=None, fmt="q4"):
     """One grouped down call on mid [M,K,I]: returns ((out [M,K,H], probe), invalid count)."""
     M, K = ids.shape
     E = slots_np.shape[0]
@@ -129,7 +129,7 @@ def run_down_grouped(slots_np, layout, midbits, ids, H, I, slots=None):
     wsb = q4.grouped_workspace_bytes(M, K, H, I, E)
     ws = aligned_empty(wsb, 256)
     ws.fill_(0xAB)
-    q4.expert_down_grouped(slots, slots_np.shape[1], E, layout, mid, M, idt, K, H, I, out, ws, wsb, d)
+    q4.expert_down_grouped(slots, slots_np.shape[1], E, layout, mid, M, idt, K, H, I, out, ws, wsb, d, fmt=fmt)
     torch.cuda.synchronize()
     invalid = int(ws[:4].cpu().numpy().view(np.int32)[0])
     return (bf16_bits(out), d.cpu().numpy()), invalid

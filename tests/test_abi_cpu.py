@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 9, names
     for n in names:
         assert hasattr(lib, n), n
-    assert q4.abi_version() == 2
+    assert q4.abi_version() == 3
 
 
 def test_workspace_size_is_aligned_and_positive():
@@ -233,3 +233,27 @@ def test_down_and_forward_entry_points_reject_before_touching_the_device():
     with pytest.raises(q4.Q4Error) as ei:
         q4.expert_down_grouped(SLOT, 4096, 1, lay, X, 1, IDS, 1, 4096, 1536, OUT, WS, 256, stream=0)
     assert ei.value.status == q4.Q4_ERR_RANGE
+
+
+# ---- the Q8 family (page 52, Q8_GATE_UP_SOURCE / Glm52CanonicalQ8MetalExecutor) ----
+
+def test_q8_validation_sizes_weights_one_per_byte():
+    lay8 = synth.contiguous_layout(4096, 1536, fmt="q8")
+    assert q4.validate_gate_up(SLOT, lay8, X, 1, 4096, 1536, OUT, fmt="q8") == 0
+    # a Q4-sized slot is too short for int8 weights
+    st = q4.validate_gate_up(SLOT, synth.contiguous_layout(4096, 1536), X, 1, 4096, 1536, OUT, fmt="q8")
+    assert st == q4.Q4_ERR_RANGE and "exceeds the canonical expert slot" in q4.last_error()
+    st = q4.validate_gate_up(SLOT, lay8, X, 1, 4100, 1536, OUT, fmt="q8")
+    assert st == q4.Q4_ERR_INVALID_ARGUMENT and "Q8 expert dimensions" in q4.last_error()
+    el8 = synth.expert_layout(4096, 1536, fmt="q8")
+    assert q4.validate_down(SLOT, el8, X, 1, 4096, 1536, OUT, fmt="q8") == 0
+    assert q4.validate_down_grouped(SLOT, el8.slot_bytes, 4, el8, X, 2, IDS, 2, 4096, 1536, OUT, WS, 256,
+                                    fmt="q8") == 0
+    assert q4.validate_grouped(SLOT, lay8.slot_bytes, 4, lay8, X, 2, IDS, 2, 4096, 1536, OUT, WS, 256,
+                               fmt="q8") == 0
+    # a projection above 2^31 - 16 bytes
+    st = q4.validate_gate_up(SLOT, synth.contiguous_layout(65536, 32768, fmt="q8"), X, 1, 65536, 32768, OUT,
+                             fmt="q8")
+    assert st == q4.Q4_ERR_UNSUPPORTED
+    with pytest.raises(ValueError):
+        q4.validate_gate_up(SLOT, lay8, X, 1, 4096, 1536, OUT, fmt="q5")

@@ -119,6 +119,24 @@ def test_decode_duplicates_and_invalid_ids():
     _check(slots, lay, x, ids, H, I, "decode duplicates and invalid ids")
 
 
+@pytest.mark.parametrize("M", [2, 5])
+def test_token_routed_three_times_to_one_slot(M):
+    """A token routed an odd number (3) of times to one slot while every other
+    token of the slot's group has a single pair there: each of the three
+    pairs gets the result (regression: the third match once undid the
+    several-pairs flag, and only the last pair was written)."""
+    E, K, H, I = 6, 3, 1024, 200
+    rng = np.random.default_rng(77 + M)
+    lay, slots = _pool(rng, E, H, I)
+    x = synth.bf16_normal(rng, (M, H))
+    ids = np.array([[(t + j) % E for j in range(K)] for t in range(M)], np.int32)
+    ids[0] = [5, 1, 0]
+    ids[1] = [5, 5, 5]
+    label = f"token routed three times, M={M}"
+    say(f"[{label}]")
+    _check(slots, lay, x, ids, H, I, label)
+
+
 def test_verify_width_many_pairs_on_one_slot():
     """Eight tokens each routed several times to one slot: more pairs than one
     pass over the slot finishes, duplicates, and an unrouted slot."""
