@@ -216,9 +216,9 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
   int L = 6, W = 8;
   auto etop = [&](int m) { return max((s_xmax[m] >> 7) & 0xFF, 1); };
   // digits of chunk w8 (8 consecutive K values) of pass token tl
-  auto stage_unit = [&](int tl, int w8, const uint4 xq, int etop1) {
+  auto stage_unit4 = [&](int tl, int w8, const uint4 xq, int etop1) {
     const int st = w8 >> 4, gg = (w8 >> 2) & 3, i = w8 & 3;
-    if (W == 4) {
+    {
       uint32_t d[2][4];
       x8_digits4(xq, etop1, d);
 #pragma unroll
@@ -230,8 +230,10 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
           *(uint32_t*)(base + (col >> 4) * 1024 + res_chunk(gg, col & 15, st) * 16) = d[par][s];
         }
       }
-      return;
     }
+  };
+  auto stage_unit8 = [&](int tl, int w8, const uint4 xq, int etop1) {
+    const int st = w8 >> 4, gg = (w8 >> 2) & 3, i = w8 & 3;
     uint32_t lo[8], hi[8];
     x8_digits(xq, etop1, lo, hi);
 #pragma unroll
@@ -252,35 +254,62 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
       put(tl * 8 + 7, 0u);
     }
   };
+  auto stage_unit = [&](int tl, int w8, const uint4 xq, int etop1) {
+    if (W == 4)
+      stage_unit4(tl, w8, xq, etop1);
+    else
+      stage_unit8(tl, w8, xq, etop1);
+  };
 
   // ---- first segment's weights in flight, then the digits of the first pass ----
   open_segment();
   start_ring();
   if constexpr (!DOWN)
     for (int i = tid; i < kSigTable; i += kResThreads) s_sig[i] = sigmoid_bf16(sig_table_bits(i));
-  // largest |x| and smallest non-zero exponent of each token
+  // largest |x| and smallest non-zero exponent of each token.  When a token's
+  // chunks fill whole waves (hw % 64 == 0), each wave's 64 chunks of x
+  // register j belong to one token: the eight wave reductions run
+  // interleaved (six dependent shuffle rounds in all) and lane 0 posts them;
+  // otherwise every lane posts its own values.
+  {
+    uint32_t mx[kResXRegs], mn[kResXRegs];
 #pragma unroll
-  for (int j = 0; j < kResXRegs; ++j) {
-    const int q0 = j * kResThreads + (tid & ~63);          // first chunk of this wave
-    if (q0 < nxc) {
-      const int q = q0 + lane;
-      const int m = min(q, nxc - 1) / hw;
-      uint32_t mx = 0, mn = 255;
-      if (q < nxc) {
-        mx = max_mag8(xv[j]);
-        mn = min_exp8(xv[j]);
-      }
-      if (min(q0 + 63, nxc - 1) / hw == q0 / hw) {
+    for (int j = 0; j < kResXRegs; ++j) {
+      const bool live = tid + j * kResThreads < nxc;
+      mx[j] = live ? max_mag8(xv[j]) : 0u;
+      mn[j] = live ? min_exp8(xv[j]) : 255u;
+    }
+    if (hw % 64 == 0) {
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-          mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
-          mn = min(mn, (uint32_t)__shfl_xor((int)mn, off));
+      for (int off = 32; off > 0; off >>= 1) {
+#pragma unroll
+        for (int j = 0; j < kResXRegs; ++j) {
+          if (j * kResThreads < nxc) {
+            mx[j] = max(mx[j], (uint32_t)__shfl_xor((int)mx[j], off));
+            mn[j] = min(mn[j], (uint32_t)__shfl_xor((int)mn[j], off));
+          }
         }
-        if (lane == 0 && mx) atomicMax(&s_xmax[m], (int)mx);
-        if (lane == 0 && mn < 255) atomicMin(&s_xmin[m], (int)mn);
-      } else {
-        if (mx) atomicMax(&s_xmax[m], (int)mx);
-        if (mn < 255) atomicMin(&s_xmin[m], (int)mn);
+      }
+      if (lane == 0) {
+#pragma unroll
+        for (int j = 0; j < kResXRegs; ++j) {
+          const int q0 = j * kResThreads + (tid & ~63);
+          if (q0 < nxc) {
+            const int m = q0 / hw;
+            if (mx[j]) atomicMax(&s_xmax[m], (int)mx[j]);
+            if (mn[j] < 255) atomicMin(&s_xmin[m], (int)mn[j]);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kResXRegs; ++j) {
+        const int q = tid + j * kResThreads;
+        if (q < nxc) {
+          const int m = q / hw;
+          if (mx[j]) atomicMax(&s_xmax[m], (int)mx[j]);
+          if (mn[j] < 255) atomicMin(&s_xmin[m], (int)mn[j]);
+        }
       }
     }
   }
@@ -295,12 +324,29 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int npass = (M + tpp - 1) / tpp;
   {
     const int ntok = min(M, tpp);
+    if (W == 4) {
+      // from the registers loaded at the start (one token per pass column quad)
 #pragma unroll
-    for (int j = 0; j < kResXRegs; ++j) {
-      const int q = tid + j * kResThreads;
-      if (q < nxc) {
+      for (int j = 0; j < kResXRegs; ++j) {
+        const int q = tid + j * kResThreads;
+        if (q < nxc) {
+          const int m = q / hw;
+          if (m < ntok) stage_unit4(m, q - m * hw, xv[j], etop(m));
+        }
+      }
+    } else {
+      // six digits: a rolled loop that reads x again (keeps the straight-line
+      // code of the launch's setup short), the next chunk's load in flight
+      const int nq = ntok * hw;
+      int q = tid;
+      uint4 xq = q < nq ? ((const uint4*)a.x)[q] : make_uint4(0, 0, 0, 0);
+#pragma unroll 1
+      for (; q < nq; q += kResThreads) {
+        const int qn = q + kResThreads;
+        const uint4 xn = qn < nq ? ((const uint4*)a.x)[qn] : make_uint4(0, 0, 0, 0);
         const int m = q / hw;
-        if (m < ntok) stage_unit(m, q - m * hw, xv[j], etop(m));
+        stage_unit8(m, q - m * hw, xq, etop(m));
+        xq = xn;
       }
     }
     // zero digits for the padding steps
