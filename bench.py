@@ -77,7 +77,8 @@ def kernel_label(M: int, H_: int) -> str:
     selection rule of q4moe_resident.hip: resident digits for up to eight
     tokens when their digits fit LDS, else the K-chunked batch kernel)."""
     nt = 1 if M <= 2 else 2
-    steps = ((H_ + 127) // 128 + 3) // 4 * 4
+    depth = 4
+    steps = ((H_ + 127) // 128 + depth - 1) // depth * depth
     fits = M <= 8 and M * (H_ // 8) <= 8 * 512 and steps * 2048 * nt + 7 * nt * 1024 <= 150 * 1024
     return "q4::resident_kernel" if fits else "q4::batch_kernel"
 

@@ -37,7 +37,9 @@ namespace {
 
 constexpr int kResWaves = 8;
 constexpr int kResThreads = kResWaves * 64;
-constexpr int kResD = 4;                   // K-steps of weights in flight per wave
+// K-steps of weights in flight per wave (a multiple of 4).  Measured: 8 with
+// two column tiles spills ~30 VGPRs and streams 6% slower at eight tokens.
+__host__ __device__ constexpr int res_depth(int nt, bool q8) { return (void)nt, (void)q8, 4; }
 constexpr int kResLds = 150 * 1024;        // digits, then the fix-up slots
 constexpr int kResXRegs = 8;               // 16-byte chunks of x held per thread while splitting
 constexpr int kResMaxTokens = 8;           // tokens per call
@@ -55,7 +57,7 @@ __host__ __device__ constexpr int res_chunk(int g, int c, int step) { return g *
 // One fix-up slot: int64 [tile][gate, up][lane] (quad sums).
 __host__ __device__ constexpr int res_fix_words(int nt) { return nt * 2 * 64; }
 // K-steps per tile, padded to whole rings.
-__host__ __device__ constexpr int res_steps(int H) { return ((H + 127) / 128 + kResD - 1) / kResD * kResD; }
+__host__ __device__ constexpr int res_steps(int H, int D) { return ((H + 127) / 128 + D - 1) / D * D; }
 // Column tiles for a call of M tokens: one up to two tokens, else two.
 __host__ __device__ constexpr int res_tiles(int M) { return M <= 2 ? 1 : 2; }
 
@@ -78,6 +80,7 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
   __shared__ int s_invalid;
   __shared__ uint16_t s_sig[kSigTable];      // bf16 sigmoid of the tabulated gT
 
+  constexpr int kResD = res_depth(NT, Q8);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -261,11 +264,9 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
       stage_unit8(tl, w8, xq, etop1);
   };
 
-  // ---- first segment's weights in flight, then the digits of the first pass ----
-  open_segment();
-  start_ring();
-  if constexpr (!DOWN)
-    for (int i = tid; i < kSigTable; i += kResThreads) s_sig[i] = sigmoid_bf16(sig_table_bits(i));
+  // ---- the digits of the first pass, then the first segment's weights in flight ----
+  // (x is split before any weight load is issued: a load issued after the ring,
+  // such as a rematerialised x chunk, would wait for the whole ring to arrive)
   // largest |x| and smallest non-zero exponent of each token.  When a token's
   // chunks fill whole waves (hw % 64 == 0), each wave's 64 chunks of x
   // register j belong to one token: the eight wave reductions run
@@ -324,22 +325,22 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int npass = (M + tpp - 1) / tpp;
   {
     const int ntok = min(M, tpp);
+    // a rolled loop that reads x again (cache hits: no weight load is in
+    // flight yet), the next chunk's load in flight: the launch's setup runs
+    // once per work-group, so its straight-line code is fetched cold
+    const int nq = ntok * hw;
+    int q = tid;
+    uint4 xq = q < nq ? ((const uint4*)a.x)[q] : make_uint4(0, 0, 0, 0);
     if (W == 4) {
-      // from the registers loaded at the start (one token per pass column quad)
-#pragma unroll
-      for (int j = 0; j < kResXRegs; ++j) {
-        const int q = tid + j * kResThreads;
-        if (q < nxc) {
-          const int m = q / hw;
-          if (m < ntok) stage_unit4(m, q - m * hw, xv[j], etop(m));
-        }
+#pragma unroll 1
+      for (; q < nq; q += kResThreads) {
+        const int qn = q + kResThreads;
+        const uint4 xn = qn < nq ? ((const uint4*)a.x)[qn] : make_uint4(0, 0, 0, 0);
+        const int m = q / hw;
+        stage_unit4(m, q - m * hw, xq, etop(m));
+        xq = xn;
       }
     } else {
-      // six digits: a rolled loop that reads x again (keeps the straight-line
-      // code of the launch's setup short), the next chunk's load in flight
-      const int nq = ntok * hw;
-      int q = tid;
-      uint4 xq = q < nq ? ((const uint4*)a.x)[q] : make_uint4(0, 0, 0, 0);
 #pragma unroll 1
       for (; q < nq; q += kResThreads) {
         const int qn = q + kResThreads;
@@ -354,6 +355,11 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
     for (int u = tid; u < ntok * padw; u += kResThreads)
       stage_unit(u % ntok, hw + u / ntok, make_uint4(0, 0, 0, 0), 1);
   }
+  open_segment();
+  start_ring();
+  // the sigmoid table while the first weights are on their way
+  if constexpr (!DOWN)
+    for (int i = tid; i < kSigTable; i += kResThreads) s_sig[i] = sigmoid_bf16(sig_table_bits(i));
 
   // exact (row, token) sum of the four digit columns of a lane quad: lane j
   // of the quad receives row 4*g4 + j (transposing quad reduction)
@@ -705,16 +711,17 @@ hipError_t launch_resident_m(GateUpParams& p, hipStream_t stream) {
 
 }  // namespace
 
-bool resident_fits(int M, int H) {
+bool resident_fits(int M, int H, bool q8) {
   if (M < 1 || M > kResMaxTokens) return false;
   const int nt = res_tiles(M);
   return (int64_t)M * (H / 8) <= (int64_t)kResXRegs * kResThreads &&
-         (int64_t)res_steps(H) * res_step_bytes(nt) + (int64_t)kResFixSlots * res_fix_words(nt) * 8 <=
+         (int64_t)res_steps(H, res_depth(nt, q8)) * res_step_bytes(nt) +
+                 (int64_t)kResFixSlots * res_fix_words(nt) * 8 <=
              (int64_t)kResLds;
 }
 
 hipError_t launch_resident(GateUpParams p, hipStream_t stream) {
-  p.steps = res_steps(p.H);
+  p.steps = res_steps(p.H, res_depth(res_tiles(p.M), p.q8 != 0));
   p.G = kResMaxPairs;
   p.wave_share = res_tiles(p.M) == 1 ? kWaveShare1 : kWaveShare2;
   if (p.q8) return p.down ? launch_resident_m<true, true>(p, stream) : launch_resident_m<false, true>(p, stream);
@@ -722,11 +729,12 @@ hipError_t launch_resident(GateUpParams p, hipStream_t stream) {
 }
 
 hipError_t launch_gate_up(const GateUpParams& p, int tokens_per_slot, hipStream_t stream) {
-  return resident_fits(tokens_per_slot, p.H) ? launch_resident(p, stream) : launch_batch(p, tokens_per_slot, stream);
+  return resident_fits(tokens_per_slot, p.H, p.q8 != 0) ? launch_resident(p, stream)
+                                                         : launch_batch(p, tokens_per_slot, stream);
 }
 
 hipError_t launch_down(const GateUpParams& p, int pairs_per_slot, hipStream_t stream) {
-  return resident_fits(p.M, p.H) ? launch_resident(p, stream) : launch_batch(p, pairs_per_slot, stream);
+  return resident_fits(p.M, p.H, p.q8 != 0) ? launch_resident(p, stream) : launch_batch(p, pairs_per_slot, stream);
 }
 
 }  // namespace q4
