@@ -17,6 +17,8 @@ from .q4_oracle import (  # noqa: F401
     exact_dots,
     scaled_f32,
     swiglu_tail,
+    swiglu_tail_f32,
+    f32_integer_parts,
     expert_gate_up,
     expert_gate_up_grouped,
     check_down_layout,

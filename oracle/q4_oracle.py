@@ -36,6 +36,12 @@ What it computes, and where the pages define it (pages of the diff of
   weights, one byte per weight, row-major (``[I][H]`` for gate/up,
   ``[H][I]`` for down), no zero point.  Every call below takes
   ``fmt="q4"`` or ``fmt="q8"``.
+* f32 activations -- same page: ``validateCall`` accepts bfloat16 or float32
+  input and ``execute`` gives every output the input's dtype ``T``.  With
+  ``T = float`` the tail's conversions are identities: ``s = 1 / (1 +
+  exp(-gate))``, ``silu = gate * s``, ``out = silu * up``, each an F32
+  operation; the down output is the F32 value itself.  Calls take
+  ``xdtype="bf16"`` (bit patterns, uint16) or ``xdtype="f32"`` (float32).
 * Grouped call -- row independence stated on page 52 (one launch geometry for
   every batch width; each sample and row is computed on its own): output
   ``[t, j, :]`` is the single-expert result for token ``t`` on slot
@@ -224,10 +230,23 @@ def bf16_integer_parts(xbits: np.ndarray):
     return sign, mag, exp
 
 
+def f32_integer_parts(x):
+    """Write each finite float32 as ``sign * mag * 2**exp``, integer ``mag`` < 2**24."""
+    b = np.ascontiguousarray(np.asarray(x, dtype=np.float32)).view(np.uint32).astype(np.int64)
+    ef = (b >> 23) & 0xFF
+    if np.any(ef == 0xFF):
+        raise ValueError("non-finite activations are outside the oracle's contract")
+    frac = b & 0x7FFFFF
+    mag = np.where(ef == 0, frac, frac | 0x800000)
+    exp = np.where(ef == 0, 1, ef) - 127 - 23
+    sign = np.where(b & 0x80000000, -1, 1)
+    return sign, mag, exp
+
+
 _LIMB_BITS = 24
 
 
-def exact_dots(w: np.ndarray, xbits: np.ndarray) -> Tuple[List[List[int]], List[int]]:
+def exact_dots(w: np.ndarray, xbits: np.ndarray, xdtype: str = "bf16") -> Tuple[List[List[int]], List[int]]:
     """Exact ``S[i][m] = sum_k w[i, k] * x[m, k]`` as ``num[i][m] * 2**e[m]``.
 
     Each token's x is scaled by a power of two to integers ``X`` (exact: the
@@ -241,12 +260,19 @@ def exact_dots(w: np.ndarray, xbits: np.ndarray) -> Tuple[List[List[int]], List[
     I, H = w.shape
     if H > (1 << 16):
         raise ValueError("oracle supports H <= 65536")
-    sign, mag, exp = bf16_integer_parts(xbits)
+    if xdtype == "bf16":
+        sign, mag, exp = bf16_integer_parts(xbits)
+        mag_bits = 8
+    elif xdtype == "f32":
+        sign, mag, exp = f32_integer_parts(xbits)
+        mag_bits = 24
+    else:
+        raise ValueError(f"unknown activation dtype {xdtype!r}")
     M = xbits.shape[0]
     nz = mag != 0
     exps = [int(exp[m][nz[m]].min()) if np.any(nz[m]) else 0 for m in range(M)]
     shifts = np.where(nz, exp - np.array(exps, dtype=np.int64)[:, None], 0)
-    nlimbs = max(1, (int(shifts.max()) + 8 + _LIMB_BITS - 1) // _LIMB_BITS)
+    nlimbs = max(1, (int(shifts.max()) + mag_bits + _LIMB_BITS - 1) // _LIMB_BITS)
     mask = (1 << _LIMB_BITS) - 1
     wf = np.asarray(w, dtype=np.float64)
     acc = None
@@ -306,14 +332,40 @@ def swiglu_tail(gate: np.ndarray, up: np.ndarray) -> np.ndarray:
     return f32_to_bf16(siluT * uT)
 
 
+def swiglu_tail_f32(gate: np.ndarray, up: np.ndarray) -> np.ndarray:
+    """The tail with ``T = float``: every conversion to T is the identity, so
+    ``s = 1/(1 + exp(-gate))`` (exp in double, rounded once to F32, as for
+    bf16), ``out = (gate * s) * up``, each step an F32 operation."""
+    gate = np.asarray(gate, dtype=np.float32)
+    up = np.asarray(up, dtype=np.float32)
+    flat = gate.reshape(-1)
+    e = np.array([_exp_f32(-float(g)) for g in flat], dtype=np.float32).reshape(gate.shape)
+    one = np.float32(1.0)
+    with np.errstate(over="ignore", under="ignore", divide="ignore", invalid="ignore"):
+        d = one + e
+        sig = one / d
+        silu = gate * sig
+        return (silu * up).astype(np.float32)
+
+
+def _x_rows(x, H: int, xdtype: str) -> np.ndarray:
+    if xdtype == "bf16":
+        return np.ascontiguousarray(x, dtype=np.uint16).reshape(-1, H)
+    if xdtype == "f32":
+        return np.ascontiguousarray(x, dtype=np.float32).reshape(-1, H)
+    raise ValueError(f"unknown activation dtype {xdtype!r}")
+
+
 # ---------------------------------------------------------------------------
 # The two calls
 # ---------------------------------------------------------------------------
 
-def expert_gate_up(slot: np.ndarray, layout, xbits: np.ndarray, H: int, I: int, fmt: str = "q4"):
-    """Single expert: returns ``(gate f32 [M,I], up f32 [M,I], out bf16 bits [M,I])``."""
+def expert_gate_up(slot: np.ndarray, layout, xbits: np.ndarray, H: int, I: int, fmt: str = "q4",
+                   xdtype: str = "bf16"):
+    """Single expert: returns ``(gate f32 [M,I], up f32 [M,I], out [M,I])``; ``out``
+    is bf16 bit patterns for bf16 x and float32 values for f32 x."""
     slot = np.ascontiguousarray(slot, dtype=np.uint8).reshape(-1)
-    xbits = np.ascontiguousarray(xbits, dtype=np.uint16).reshape(-1, H)
+    xbits = _x_rows(xbits, H, xdtype)
     check_layout(layout, H, I, fmt)
     if slot.size < layout.slot_bytes:
         raise ValueError("canonical expert slot array is shorter than its layout")
@@ -323,13 +375,14 @@ def expert_gate_up(slot: np.ndarray, layout, xbits: np.ndarray, H: int, I: int, 
     wu = decode_weights(slot, layout.up_weight_offset, I, H, fmt)
     sg = row_scales(slot, layout.gate_scale_offset, I)
     su = row_scales(slot, layout.up_scale_offset, I)
-    gate = scaled_f32(*exact_dots(wg, xbits), sg)
-    up = scaled_f32(*exact_dots(wu, xbits), su)
-    return gate, up, swiglu_tail(gate, up)
+    gate = scaled_f32(*exact_dots(wg, xbits, xdtype), sg)
+    up = scaled_f32(*exact_dots(wu, xbits, xdtype), su)
+    return gate, up, (swiglu_tail(gate, up) if xdtype == "bf16" else swiglu_tail_f32(gate, up))
 
 
 def expert_gate_up_grouped(slots: np.ndarray, slot_stride: int, num_slots: int, layout,
-                           xbits: np.ndarray, ids: np.ndarray, H: int, I: int, fmt: str = "q4"):
+                           xbits: np.ndarray, ids: np.ndarray, H: int, I: int, fmt: str = "q4",
+                           xdtype: str = "bf16"):
     """Grouped call over routed slots.
 
     Returns ``(gate [M,K,I], up [M,K,I], out bits [M,K,I], invalid_count)``.
@@ -337,12 +390,12 @@ def expert_gate_up_grouped(slots: np.ndarray, slot_stride: int, num_slots: int, 
     zero gate, up and output.
     """
     flat = np.ascontiguousarray(slots, dtype=np.uint8).reshape(-1)
-    xbits = np.ascontiguousarray(xbits, dtype=np.uint16).reshape(-1, H)
+    xbits = _x_rows(xbits, H, xdtype)
     ids = np.asarray(ids, dtype=np.int64)
     M, K = ids.shape
     gate = np.zeros((M, K, I), dtype=np.float32)
     up = np.zeros((M, K, I), dtype=np.float32)
-    out = np.zeros((M, K, I), dtype=np.uint16)
+    out = np.zeros((M, K, I), dtype=np.uint16 if xdtype == "bf16" else np.float32)
     invalid = 0
     by_slot: Dict[int, List[Tuple[int, int]]] = {}
     for t in range(M):
@@ -355,7 +408,7 @@ def expert_gate_up_grouped(slots: np.ndarray, slot_stride: int, num_slots: int, 
     for e, pairs in sorted(by_slot.items()):
         slot = flat[e * slot_stride:e * slot_stride + layout.slot_bytes]
         toks = [t for t, _ in pairs]
-        g, u, o = expert_gate_up(slot, layout, xbits[toks], H, I, fmt)
+        g, u, o = expert_gate_up(slot, layout, xbits[toks], H, I, fmt, xdtype)
         for r, (t, j) in enumerate(pairs):
             gate[t, j] = g[r]
             up[t, j] = u[r]
@@ -376,7 +429,8 @@ def check_down_layout(layout, H: int, I: int, fmt: str = "q4") -> None:
         raise ValueError("down weights exceeds the canonical expert slot")
 
 
-def expert_down(slot: np.ndarray, layout, midbits: np.ndarray, H: int, I: int, fmt: str = "q4"):
+def expert_down(slot: np.ndarray, layout, midbits: np.ndarray, H: int, I: int, fmt: str = "q4",
+                xdtype: str = "bf16"):
     """Down projection of one slot: returns ``(down f32 [M,H], out bf16 bits [M,H])``.
 
     Row ``h`` of the down matrix is ``I/8`` words at
@@ -385,27 +439,29 @@ def expert_down(slot: np.ndarray, layout, midbits: np.ndarray, H: int, I: int, f
     the output is its bf16 rounding (the kernel's ``T(value)``).
     """
     slot = np.ascontiguousarray(slot, dtype=np.uint8).reshape(-1)
-    midbits = np.ascontiguousarray(midbits, dtype=np.uint16).reshape(-1, I)
+    midbits = _x_rows(midbits, I, xdtype)
     check_down_layout(layout, H, I, fmt)
     if slot.size < layout.slot_bytes:
         raise ValueError("canonical expert slot array is shorter than its layout")
     wd = decode_weights(slot, layout.down_weight_offset, H, I, fmt)
     sd = row_scales(slot, layout.down_scale_offset, H)
-    down = scaled_f32(*exact_dots(wd, midbits), sd)
-    return down, f32_to_bf16(down)
+    down = scaled_f32(*exact_dots(wd, midbits, xdtype), sd)
+    return down, (f32_to_bf16(down) if xdtype == "bf16" else down.copy())
 
 
-def expert_forward(slot: np.ndarray, layout, xbits: np.ndarray, H: int, I: int, fmt: str = "q4"):
+def expert_forward(slot: np.ndarray, layout, xbits: np.ndarray, H: int, I: int, fmt: str = "q4",
+                   xdtype: str = "bf16"):
     """The whole expert of one slot, as ``execute`` chains its two kernels:
-    returns ``(mid bf16 bits [M,I], out bf16 bits [M,H])``."""
+    returns ``(mid [M,I], out [M,H])`` in the input's dtype."""
     check_down_layout(layout, H, I, fmt)
-    _, _, mid = expert_gate_up(slot, layout, xbits, H, I, fmt)
-    _, out = expert_down(slot, layout, mid, H, I, fmt)
+    _, _, mid = expert_gate_up(slot, layout, xbits, H, I, fmt, xdtype)
+    _, out = expert_down(slot, layout, mid, H, I, fmt, xdtype)
     return mid, out
 
 
 def expert_down_grouped(slots: np.ndarray, slot_stride: int, num_slots: int, layout,
-                        midbits: np.ndarray, ids: np.ndarray, H: int, I: int, fmt: str = "q4"):
+                        midbits: np.ndarray, ids: np.ndarray, H: int, I: int, fmt: str = "q4",
+                        xdtype: str = "bf16"):
     """Grouped down projection: pair ``(t, j)`` runs its own input row
     ``mid[t, j, :]`` against slot ``ids[t, j]`` and writes ``out[t, j, :]``.
 
@@ -415,9 +471,9 @@ def expert_down_grouped(slots: np.ndarray, slot_stride: int, num_slots: int, lay
     flat = np.ascontiguousarray(slots, dtype=np.uint8).reshape(-1)
     ids = np.asarray(ids, dtype=np.int64)
     M, K = ids.shape
-    midbits = np.ascontiguousarray(midbits, dtype=np.uint16).reshape(M, K, I)
+    midbits = _x_rows(midbits, I, xdtype).reshape(M, K, I)
     down = np.zeros((M, K, H), dtype=np.float32)
-    out = np.zeros((M, K, H), dtype=np.uint16)
+    out = np.zeros((M, K, H), dtype=np.uint16 if xdtype == "bf16" else np.float32)
     invalid = 0
     by_slot: Dict[int, List[Tuple[int, int]]] = {}
     for t in range(M):
@@ -430,7 +486,7 @@ def expert_down_grouped(slots: np.ndarray, slot_stride: int, num_slots: int, lay
     for e, pairs in sorted(by_slot.items()):
         slot = flat[e * slot_stride:e * slot_stride + layout.slot_bytes]
         rows = np.stack([midbits[t, j] for t, j in pairs])
-        d, o = expert_down(slot, layout, rows, H, I, fmt)
+        d, o = expert_down(slot, layout, rows, H, I, fmt, xdtype)
         for r, (t, j) in enumerate(pairs):
             down[t, j] = d[r]
             out[t, j] = o[r]
@@ -438,9 +494,11 @@ def expert_down_grouped(slots: np.ndarray, slot_stride: int, num_slots: int, lay
 
 
 def expert_forward_grouped(slots: np.ndarray, slot_stride: int, num_slots: int, layout,
-                           xbits: np.ndarray, ids: np.ndarray, H: int, I: int, fmt: str = "q4"):
-    """Grouped whole expert: returns ``(mid bits [M,K,I], out bits [M,K,H], invalid_count)``."""
+                           xbits: np.ndarray, ids: np.ndarray, H: int, I: int, fmt: str = "q4",
+                           xdtype: str = "bf16"):
+    """Grouped whole expert: returns ``(mid [M,K,I], out [M,K,H], invalid_count)``."""
     check_down_layout(layout, H, I, fmt)
-    _, _, mid, invalid = expert_gate_up_grouped(slots, slot_stride, num_slots, layout, xbits, ids, H, I, fmt)
-    _, out, _ = expert_down_grouped(slots, slot_stride, num_slots, layout, mid, ids, H, I, fmt)
+    _, _, mid, invalid = expert_gate_up_grouped(slots, slot_stride, num_slots, layout, xbits, ids, H, I, fmt,
+                                                xdtype)
+    _, out, _ = expert_down_grouped(slots, slot_stride, num_slots, layout, mid, ids, H, I, fmt, xdtype)
     return mid, out, invalid
