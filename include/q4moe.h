@@ -333,11 +333,53 @@ int q8_validate_down_grouped(const void *slots_base, uint64_t slot_stride,
                              int64_t I, const void *out_bf16,
                              const void *workspace, size_t workspace_bytes);
 
+/*
+ * f32 activations (page 52: validateCall accepts bfloat16 or float32 input,
+ * execute gives every output the input's dtype).  Each call below is its
+ * namesake without the _f32 suffix with x (and mid) float32 instead of bf16
+ * -- same shapes, 16-byte aligned -- and float32 outputs (4-byte aligned).
+ * With T = float the tail's conversions are identities:
+ *   s = 1 / (1 + exp(-gate)), out = (gate * s) * up     (each an F32 operation;
+ *   exp evaluated to within the F32 rounding of the exact value)
+ * and the down output is its F32 value.  Each f32 value is split into eight
+ * signed 8-bit digits on its token's largest exponent, so sums are exact for
+ * values at most 38 binades below the token's largest |x| (smaller entries
+ * are rounded to that grid) and rounded once to F32 with the row scale.
+ */
+int q4_expert_gate_up_f32(const void *slot, const q4_slot_layout *layout, const void *x_f32, int64_t M, int64_t H, int64_t I, void *out_f32, q4_stream_t stream);
+int q4_expert_gate_up_probe_f32(const void *slot, const q4_slot_layout *layout, const void *x_f32, int64_t M, int64_t H, int64_t I, void *out_f32, float *gate_f32, float *up_f32, q4_stream_t stream);
+int q4_expert_gate_up_grouped_f32(const void *slots_base, uint64_t slot_stride, int64_t num_slots, const q4_slot_layout *layout, const void *x_f32, int64_t M, const int32_t *slot_ids, int64_t K, int64_t H, int64_t I, void *out_f32, void *workspace, size_t workspace_bytes, q4_stream_t stream);
+int q4_expert_gate_up_grouped_probe_f32(const void *slots_base, uint64_t slot_stride, int64_t num_slots, const q4_slot_layout *layout, const void *x_f32, int64_t M, const int32_t *slot_ids, int64_t K, int64_t H, int64_t I, void *out_f32, float *gate_f32, float *up_f32, void *workspace, size_t workspace_bytes, q4_stream_t stream);
+int q4_validate_gate_up_f32(const void *slot, const q4_slot_layout *layout, const void *x_f32, int64_t M, int64_t H, int64_t I, const void *out_f32);
+int q4_validate_grouped_f32(const void *slots_base, uint64_t slot_stride, int64_t num_slots, const q4_slot_layout *layout, const void *x_f32, int64_t M, const int32_t *slot_ids, int64_t K, int64_t H, int64_t I, const void *out_f32, const void *workspace, size_t workspace_bytes);
+int q4_expert_down_f32(const void *slot, const q4_slot_layout *layout, const void *mid_f32, int64_t M, int64_t H, int64_t I, void *out_f32, q4_stream_t stream);
+int q4_expert_down_probe_f32(const void *slot, const q4_slot_layout *layout, const void *mid_f32, int64_t M, int64_t H, int64_t I, void *out_f32, float *down_f32, q4_stream_t stream);
+int q4_expert_down_grouped_f32(const void *slots_base, uint64_t slot_stride, int64_t num_slots, const q4_slot_layout *layout, const void *mid_f32, int64_t M, const int32_t *slot_ids, int64_t K, int64_t H, int64_t I, void *out_f32, void *workspace, size_t workspace_bytes, q4_stream_t stream);
+int q4_expert_down_grouped_probe_f32(const void *slots_base, uint64_t slot_stride, int64_t num_slots, const q4_slot_layout *layout, const void *mid_f32, int64_t M, const int32_t *slot_ids, int64_t K, int64_t H, int64_t I, void *out_f32, float *down_f32, void *workspace, size_t workspace_bytes, q4_stream_t stream);
+int q4_expert_forward_f32(const void *slot, const q4_slot_layout *layout, const void *x_f32, int64_t M, int64_t H, int64_t I, void *mid_f32, void *out_f32, q4_stream_t stream);
+int q4_expert_forward_grouped_f32(const void *slots_base, uint64_t slot_stride, int64_t num_slots, const q4_slot_layout *layout, const void *x_f32, int64_t M, const int32_t *slot_ids, int64_t K, int64_t H, int64_t I, void *mid_f32, void *out_f32, void *workspace, size_t workspace_bytes, q4_stream_t stream);
+int q4_validate_down_f32(const void *slot, const q4_slot_layout *layout, const void *mid_f32, int64_t M, int64_t H, int64_t I, const void *out_f32);
+int q4_validate_down_grouped_f32(const void *slots_base, uint64_t slot_stride, int64_t num_slots, const q4_slot_layout *layout, const void *mid_f32, int64_t M, const int32_t *slot_ids, int64_t K, int64_t H, int64_t I, const void *out_f32, const void *workspace, size_t workspace_bytes);
+int q8_expert_gate_up_f32(const void *slot, const q4_slot_layout *layout, const void *x_f32, int64_t M, int64_t H, int64_t I, void *out_f32, q4_stream_t stream);
+int q8_expert_gate_up_probe_f32(const void *slot, const q4_slot_layout *layout, const void *x_f32, int64_t M, int64_t H, int64_t I, void *out_f32, float *gate_f32, float *up_f32, q4_stream_t stream);
+int q8_expert_gate_up_grouped_f32(const void *slots_base, uint64_t slot_stride, int64_t num_slots, const q4_slot_layout *layout, const void *x_f32, int64_t M, const int32_t *slot_ids, int64_t K, int64_t H, int64_t I, void *out_f32, void *workspace, size_t workspace_bytes, q4_stream_t stream);
+int q8_expert_gate_up_grouped_probe_f32(const void *slots_base, uint64_t slot_stride, int64_t num_slots, const q4_slot_layout *layout, const void *x_f32, int64_t M, const int32_t *slot_ids, int64_t K, int64_t H, int64_t I, void *out_f32, float *gate_f32, float *up_f32, void *workspace, size_t workspace_bytes, q4_stream_t stream);
+int q8_validate_gate_up_f32(const void *slot, const q4_slot_layout *layout, const void *x_f32, int64_t M, int64_t H, int64_t I, const void *out_f32);
+int q8_validate_grouped_f32(const void *slots_base, uint64_t slot_stride, int64_t num_slots, const q4_slot_layout *layout, const void *x_f32, int64_t M, const int32_t *slot_ids, int64_t K, int64_t H, int64_t I, const void *out_f32, const void *workspace, size_t workspace_bytes);
+int q8_expert_down_f32(const void *slot, const q4_slot_layout *layout, const void *mid_f32, int64_t M, int64_t H, int64_t I, void *out_f32, q4_stream_t stream);
+int q8_expert_down_probe_f32(const void *slot, const q4_slot_layout *layout, const void *mid_f32, int64_t M, int64_t H, int64_t I, void *out_f32, float *down_f32, q4_stream_t stream);
+int q8_expert_down_grouped_f32(const void *slots_base, uint64_t slot_stride, int64_t num_slots, const q4_slot_layout *layout, const void *mid_f32, int64_t M, const int32_t *slot_ids, int64_t K, int64_t H, int64_t I, void *out_f32, void *workspace, size_t workspace_bytes, q4_stream_t stream);
+int q8_expert_down_grouped_probe_f32(const void *slots_base, uint64_t slot_stride, int64_t num_slots, const q4_slot_layout *layout, const void *mid_f32, int64_t M, const int32_t *slot_ids, int64_t K, int64_t H, int64_t I, void *out_f32, float *down_f32, void *workspace, size_t workspace_bytes, q4_stream_t stream);
+int q8_expert_forward_f32(const void *slot, const q4_slot_layout *layout, const void *x_f32, int64_t M, int64_t H, int64_t I, void *mid_f32, void *out_f32, q4_stream_t stream);
+int q8_expert_forward_grouped_f32(const void *slots_base, uint64_t slot_stride, int64_t num_slots, const q4_slot_layout *layout, const void *x_f32, int64_t M, const int32_t *slot_ids, int64_t K, int64_t H, int64_t I, void *mid_f32, void *out_f32, void *workspace, size_t workspace_bytes, q4_stream_t stream);
+int q8_validate_down_f32(const void *slot, const q4_slot_layout *layout, const void *mid_f32, int64_t M, int64_t H, int64_t I, const void *out_f32);
+int q8_validate_down_grouped_f32(const void *slots_base, uint64_t slot_stride, int64_t num_slots, const q4_slot_layout *layout, const void *mid_f32, int64_t M, const int32_t *slot_ids, int64_t K, int64_t H, int64_t I, const void *out_f32, const void *workspace, size_t workspace_bytes);
+
 /* Message for the last failing call on this thread ("" after success). */
 const char *q4_last_error(void);
 
-/* ABI version: 3 (1 plus the down projection and whole-expert calls, and the
- * Q8 family). */
+/* ABI version: 4 (1 plus the down projection and whole-expert calls, the Q8
+ * family and f32 activations). */
 int q4_abi_version(void);
 
 #ifdef __cplusplus

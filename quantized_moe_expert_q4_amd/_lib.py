@@ -107,6 +107,48 @@ _SIGNATURES = {
     "q8_validate_down": (ctypes.c_int, [_P, _LAYOUT, _P, _I64, _I64, _I64, _P]),
     "q8_validate_down_grouped": (ctypes.c_int, [_P, _U64, _I64, _LAYOUT, _P, _I64, _P, _I64, _I64, _I64, _P,
                                                 _P, _SZ]),
+    "q4_expert_gate_up_f32": (ctypes.c_int, [_P, _LAYOUT, _P, _I64, _I64, _I64, _P, _P]),
+    "q4_expert_gate_up_probe_f32": (ctypes.c_int, [_P, _LAYOUT, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
+    "q4_expert_gate_up_grouped_f32": (ctypes.c_int, [_P, _U64, _I64, _LAYOUT, _P, _I64, _P, _I64, _I64, _I64,
+                                                 _P, _P, _SZ, _P]),
+    "q4_expert_gate_up_grouped_probe_f32": (ctypes.c_int, [_P, _U64, _I64, _LAYOUT, _P, _I64, _P, _I64, _I64,
+                                                       _I64, _P, _P, _P, _P, _SZ, _P]),
+    "q4_validate_gate_up_f32": (ctypes.c_int, [_P, _LAYOUT, _P, _I64, _I64, _I64, _P]),
+    "q4_validate_grouped_f32": (ctypes.c_int, [_P, _U64, _I64, _LAYOUT, _P, _I64, _P, _I64, _I64, _I64, _P, _P,
+                                           _SZ]),
+    "q4_expert_down_f32": (ctypes.c_int, [_P, _LAYOUT, _P, _I64, _I64, _I64, _P, _P]),
+    "q4_expert_down_probe_f32": (ctypes.c_int, [_P, _LAYOUT, _P, _I64, _I64, _I64, _P, _P, _P]),
+    "q4_expert_down_grouped_f32": (ctypes.c_int, [_P, _U64, _I64, _LAYOUT, _P, _I64, _P, _I64, _I64, _I64,
+                                              _P, _P, _SZ, _P]),
+    "q4_expert_down_grouped_probe_f32": (ctypes.c_int, [_P, _U64, _I64, _LAYOUT, _P, _I64, _P, _I64, _I64, _I64,
+                                                    _P, _P, _P, _SZ, _P]),
+    "q4_expert_forward_f32": (ctypes.c_int, [_P, _LAYOUT, _P, _I64, _I64, _I64, _P, _P, _P]),
+    "q4_expert_forward_grouped_f32": (ctypes.c_int, [_P, _U64, _I64, _LAYOUT, _P, _I64, _P, _I64, _I64, _I64,
+                                                 _P, _P, _P, _SZ, _P]),
+    "q4_validate_down_f32": (ctypes.c_int, [_P, _LAYOUT, _P, _I64, _I64, _I64, _P]),
+    "q4_validate_down_grouped_f32": (ctypes.c_int, [_P, _U64, _I64, _LAYOUT, _P, _I64, _P, _I64, _I64, _I64, _P,
+                                                _P, _SZ]),
+    "q8_expert_gate_up_f32": (ctypes.c_int, [_P, _LAYOUT, _P, _I64, _I64, _I64, _P, _P]),
+    "q8_expert_gate_up_probe_f32": (ctypes.c_int, [_P, _LAYOUT, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
+    "q8_expert_gate_up_grouped_f32": (ctypes.c_int, [_P, _U64, _I64, _LAYOUT, _P, _I64, _P, _I64, _I64, _I64,
+                                                 _P, _P, _SZ, _P]),
+    "q8_expert_gate_up_grouped_probe_f32": (ctypes.c_int, [_P, _U64, _I64, _LAYOUT, _P, _I64, _P, _I64, _I64,
+                                                       _I64, _P, _P, _P, _P, _SZ, _P]),
+    "q8_validate_gate_up_f32": (ctypes.c_int, [_P, _LAYOUT, _P, _I64, _I64, _I64, _P]),
+    "q8_validate_grouped_f32": (ctypes.c_int, [_P, _U64, _I64, _LAYOUT, _P, _I64, _P, _I64, _I64, _I64, _P, _P,
+                                           _SZ]),
+    "q8_expert_down_f32": (ctypes.c_int, [_P, _LAYOUT, _P, _I64, _I64, _I64, _P, _P]),
+    "q8_expert_down_probe_f32": (ctypes.c_int, [_P, _LAYOUT, _P, _I64, _I64, _I64, _P, _P, _P]),
+    "q8_expert_down_grouped_f32": (ctypes.c_int, [_P, _U64, _I64, _LAYOUT, _P, _I64, _P, _I64, _I64, _I64,
+                                              _P, _P, _SZ, _P]),
+    "q8_expert_down_grouped_probe_f32": (ctypes.c_int, [_P, _U64, _I64, _LAYOUT, _P, _I64, _P, _I64, _I64, _I64,
+                                                    _P, _P, _P, _SZ, _P]),
+    "q8_expert_forward_f32": (ctypes.c_int, [_P, _LAYOUT, _P, _I64, _I64, _I64, _P, _P, _P]),
+    "q8_expert_forward_grouped_f32": (ctypes.c_int, [_P, _U64, _I64, _LAYOUT, _P, _I64, _P, _I64, _I64, _I64,
+                                                 _P, _P, _P, _SZ, _P]),
+    "q8_validate_down_f32": (ctypes.c_int, [_P, _LAYOUT, _P, _I64, _I64, _I64, _P]),
+    "q8_validate_down_grouped_f32": (ctypes.c_int, [_P, _U64, _I64, _LAYOUT, _P, _I64, _P, _I64, _I64, _I64, _P,
+                                                _P, _SZ]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -130,12 +172,15 @@ def load() -> ctypes.CDLL:
     return lib
 
 
-def _fn(lib, fmt: str, name: str):
-    """Entry point ``<fmt>_<name>`` of the library: ``fmt`` is "q4" (packed
-    nibbles) or "q8" (int8 weights)."""
+def _fn(lib, fmt: str, name: str, xdtype: str = "bf16"):
+    """Entry point ``<fmt>_<name>[_f32]`` of the library: ``fmt`` is "q4"
+    (packed nibbles) or "q8" (int8 weights); ``xdtype`` is "bf16" or "f32"
+    (activations and outputs)."""
     if fmt not in ("q4", "q8"):
         raise ValueError(f"weight format must be 'q4' or 'q8', not {fmt!r}")
-    return getattr(lib, f"{fmt}_{name}")
+    if xdtype not in ("bf16", "f32"):
+        raise ValueError(f"activation dtype must be 'bf16' or 'f32', not {xdtype!r}")
+    return getattr(lib, f"{fmt}_{name}" + ("_f32" if xdtype == "f32" else ""))
 
 
 def last_error() -> str:
@@ -183,107 +228,107 @@ def grouped_workspace_bytes(M: int, K: int, H: int, I: int, num_slots: int) -> i
 
 
 def expert_gate_up(slot, layout, x, M: int, H: int, I: int, out, gate_probe=None, up_probe=None,
-                   stream=None, fmt: str = "q4") -> None:
+                   stream=None, fmt: str = "q4", xdtype: str = "bf16") -> None:
     """Enqueue the single-expert kernel (see q4_expert_gate_up in include/q4moe.h)."""
     lib = load()
     lay = layout_c(layout)
     if gate_probe is None and up_probe is None:
-        st = _fn(lib, fmt, "expert_gate_up")(_ptr(slot), ctypes.byref(lay), _ptr(x), M, H, I, _ptr(out), _stream(stream))
+        st = _fn(lib, fmt, "expert_gate_up", xdtype)(_ptr(slot), ctypes.byref(lay), _ptr(x), M, H, I, _ptr(out), _stream(stream))
     else:
-        st = _fn(lib, fmt, "expert_gate_up_probe")(_ptr(slot), ctypes.byref(lay), _ptr(x), M, H, I, _ptr(out),
+        st = _fn(lib, fmt, "expert_gate_up_probe", xdtype)(_ptr(slot), ctypes.byref(lay), _ptr(x), M, H, I, _ptr(out),
                                          _ptr(gate_probe), _ptr(up_probe), _stream(stream))
     _check(st)
 
 
 def expert_gate_up_grouped(slots_base, slot_stride: int, num_slots: int, layout, x, M: int, slot_ids, K: int,
                            H: int, I: int, out, workspace, workspace_bytes: int, gate_probe=None,
-                           up_probe=None, stream=None, fmt: str = "q4") -> None:
+                           up_probe=None, stream=None, fmt: str = "q4", xdtype: str = "bf16") -> None:
     """Enqueue the grouped kernel (see q4_expert_gate_up_grouped in include/q4moe.h)."""
     lib = load()
     lay = layout_c(layout)
     if gate_probe is None and up_probe is None:
-        st = _fn(lib, fmt, "expert_gate_up_grouped")(_ptr(slots_base), slot_stride, num_slots, ctypes.byref(lay), _ptr(x),
+        st = _fn(lib, fmt, "expert_gate_up_grouped", xdtype)(_ptr(slots_base), slot_stride, num_slots, ctypes.byref(lay), _ptr(x),
                                            M, _ptr(slot_ids), K, H, I, _ptr(out), _ptr(workspace),
                                            workspace_bytes, _stream(stream))
     else:
-        st = _fn(lib, fmt, "expert_gate_up_grouped_probe")(_ptr(slots_base), slot_stride, num_slots, ctypes.byref(lay),
+        st = _fn(lib, fmt, "expert_gate_up_grouped_probe", xdtype)(_ptr(slots_base), slot_stride, num_slots, ctypes.byref(lay),
                                                  _ptr(x), M, _ptr(slot_ids), K, H, I, _ptr(out),
                                                  _ptr(gate_probe), _ptr(up_probe), _ptr(workspace),
                                                  workspace_bytes, _stream(stream))
     _check(st)
 
 
-def validate_gate_up(slot, layout, x, M: int, H: int, I: int, out, fmt: str = "q4") -> int:
+def validate_gate_up(slot, layout, x, M: int, H: int, I: int, out, fmt: str = "q4", xdtype: str = "bf16") -> int:
     """Host-only argument check; returns the status (0 or negative)."""
     lay = None if layout is None else layout_c(layout)
-    return _fn(load(), fmt, "validate_gate_up")(_ptr(slot), None if lay is None else ctypes.byref(lay), _ptr(x), M, H, I,
+    return _fn(load(), fmt, "validate_gate_up", xdtype)(_ptr(slot), None if lay is None else ctypes.byref(lay), _ptr(x), M, H, I,
                                       _ptr(out))
 
 
 def validate_grouped(slots_base, slot_stride, num_slots, layout, x, M, slot_ids, K, H, I, out, workspace,
-                     workspace_bytes, fmt: str = "q4") -> int:
+                     workspace_bytes, fmt: str = "q4", xdtype: str = "bf16") -> int:
     lay = None if layout is None else layout_c(layout)
-    return _fn(load(), fmt, "validate_grouped")(_ptr(slots_base), slot_stride, num_slots,
+    return _fn(load(), fmt, "validate_grouped", xdtype)(_ptr(slots_base), slot_stride, num_slots,
                                       None if lay is None else ctypes.byref(lay), _ptr(x), M, _ptr(slot_ids), K,
                                       H, I, _ptr(out), _ptr(workspace), workspace_bytes)
 
 
-def expert_down(slot, layout, mid, M: int, H: int, I: int, out, down_probe=None, stream=None, fmt: str = "q4") -> None:
+def expert_down(slot, layout, mid, M: int, H: int, I: int, out, down_probe=None, stream=None, fmt: str = "q4", xdtype: str = "bf16") -> None:
     """Enqueue the down projection of one slot (see q4_expert_down in include/q4moe.h)."""
     lib = load()
     lay = layout_c(layout)
     if down_probe is None:
-        st = _fn(lib, fmt, "expert_down")(_ptr(slot), ctypes.byref(lay), _ptr(mid), M, H, I, _ptr(out), _stream(stream))
+        st = _fn(lib, fmt, "expert_down", xdtype)(_ptr(slot), ctypes.byref(lay), _ptr(mid), M, H, I, _ptr(out), _stream(stream))
     else:
-        st = _fn(lib, fmt, "expert_down_probe")(_ptr(slot), ctypes.byref(lay), _ptr(mid), M, H, I, _ptr(out),
+        st = _fn(lib, fmt, "expert_down_probe", xdtype)(_ptr(slot), ctypes.byref(lay), _ptr(mid), M, H, I, _ptr(out),
                                       _ptr(down_probe), _stream(stream))
     _check(st)
 
 
 def expert_down_grouped(slots_base, slot_stride: int, num_slots: int, layout, mid, M: int, slot_ids, K: int,
                         H: int, I: int, out, workspace, workspace_bytes: int, down_probe=None,
-                        stream=None, fmt: str = "q4") -> None:
+                        stream=None, fmt: str = "q4", xdtype: str = "bf16") -> None:
     """Enqueue the grouped down projection (see q4_expert_down_grouped in include/q4moe.h)."""
     lib = load()
     lay = layout_c(layout)
     if down_probe is None:
-        st = _fn(lib, fmt, "expert_down_grouped")(_ptr(slots_base), slot_stride, num_slots, ctypes.byref(lay), _ptr(mid),
+        st = _fn(lib, fmt, "expert_down_grouped", xdtype)(_ptr(slots_base), slot_stride, num_slots, ctypes.byref(lay), _ptr(mid),
                                         M, _ptr(slot_ids), K, H, I, _ptr(out), _ptr(workspace),
                                         workspace_bytes, _stream(stream))
     else:
-        st = _fn(lib, fmt, "expert_down_grouped_probe")(_ptr(slots_base), slot_stride, num_slots, ctypes.byref(lay),
+        st = _fn(lib, fmt, "expert_down_grouped_probe", xdtype)(_ptr(slots_base), slot_stride, num_slots, ctypes.byref(lay),
                                               _ptr(mid), M, _ptr(slot_ids), K, H, I, _ptr(out),
                                               _ptr(down_probe), _ptr(workspace), workspace_bytes,
                                               _stream(stream))
     _check(st)
 
 
-def expert_forward(slot, layout, x, M: int, H: int, I: int, mid, out, stream=None, fmt: str = "q4") -> None:
+def expert_forward(slot, layout, x, M: int, H: int, I: int, mid, out, stream=None, fmt: str = "q4", xdtype: str = "bf16") -> None:
     """Enqueue the whole expert of one slot (see q4_expert_forward in include/q4moe.h)."""
     lay = layout_c(layout)
-    _check(_fn(load(), fmt, "expert_forward")(_ptr(slot), ctypes.byref(lay), _ptr(x), M, H, I, _ptr(mid), _ptr(out),
+    _check(_fn(load(), fmt, "expert_forward", xdtype)(_ptr(slot), ctypes.byref(lay), _ptr(x), M, H, I, _ptr(mid), _ptr(out),
                                     _stream(stream)))
 
 
 def expert_forward_grouped(slots_base, slot_stride: int, num_slots: int, layout, x, M: int, slot_ids, K: int,
-                           H: int, I: int, mid, out, workspace, workspace_bytes: int, stream=None, fmt: str = "q4") -> None:
+                           H: int, I: int, mid, out, workspace, workspace_bytes: int, stream=None, fmt: str = "q4", xdtype: str = "bf16") -> None:
     """Enqueue the grouped whole expert (see q4_expert_forward_grouped in include/q4moe.h)."""
     lay = layout_c(layout)
-    _check(_fn(load(), fmt, "expert_forward_grouped")(_ptr(slots_base), slot_stride, num_slots, ctypes.byref(lay),
+    _check(_fn(load(), fmt, "expert_forward_grouped", xdtype)(_ptr(slots_base), slot_stride, num_slots, ctypes.byref(lay),
                                             _ptr(x), M, _ptr(slot_ids), K, H, I, _ptr(mid), _ptr(out),
                                             _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
-def validate_down(slot, layout, mid, M: int, H: int, I: int, out, fmt: str = "q4") -> int:
+def validate_down(slot, layout, mid, M: int, H: int, I: int, out, fmt: str = "q4", xdtype: str = "bf16") -> int:
     """Host-only argument check of the down call; returns the status."""
     lay = None if layout is None else layout_c(layout)
-    return _fn(load(), fmt, "validate_down")(_ptr(slot), None if lay is None else ctypes.byref(lay), _ptr(mid), M, H, I,
+    return _fn(load(), fmt, "validate_down", xdtype)(_ptr(slot), None if lay is None else ctypes.byref(lay), _ptr(mid), M, H, I,
                                    _ptr(out))
 
 
 def validate_down_grouped(slots_base, slot_stride, num_slots, layout, mid, M, slot_ids, K, H, I, out, workspace,
-                          workspace_bytes, fmt: str = "q4") -> int:
+                          workspace_bytes, fmt: str = "q4", xdtype: str = "bf16") -> int:
     lay = None if layout is None else layout_c(layout)
-    return _fn(load(), fmt, "validate_down_grouped")(_ptr(slots_base), slot_stride, num_slots,
+    return _fn(load(), fmt, "validate_down_grouped", xdtype)(_ptr(slots_base), slot_stride, num_slots,
                                            None if lay is None else ctypes.byref(lay), _ptr(mid), M,
                                            _ptr(slot_ids), K, H, I, _ptr(out), _ptr(workspace), workspace_bytes)

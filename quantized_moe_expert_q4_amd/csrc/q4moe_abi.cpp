@@ -39,6 +39,10 @@ constexpr int64_t kMaxSlots = 65535;
 constexpr uint64_t kMaxWeightBytes = (1ull << 31) - 16;
 constexpr size_t kWorkspaceBytes = 256;  // [0]: number of out-of-range ids
 
+// Call formats: int8 weights (else packed nibbles) and f32 activations and
+// outputs (else bf16), or'ed together.
+constexpr unsigned kQ8 = 1u, kF32 = 2u;
+
 // Bytes of one weight row of K weights: packed nibbles (Q4, two per byte) or
 // int8 (Q8, one per byte), the weightsPerByte of the two families on page 52.
 uint64_t weight_row_bytes(bool q8, int64_t K) { return q8 ? (uint64_t)K : (uint64_t)(K / 2); }
@@ -51,24 +55,24 @@ int check_range(uint64_t offset, uint64_t length, uint64_t slot_bytes, const cha
   return Q4_OK;
 }
 
-int check_dims(bool q8, int64_t M, int64_t H, int64_t I) {
+int check_dims(unsigned fmt, int64_t M, int64_t H, int64_t I) {
   if (H <= 0) return fail(Q4_ERR_INVALID_ARGUMENT, "hidden size must be a positive integer");
   if (I <= 0) return fail(Q4_ERR_INVALID_ARGUMENT, "intermediate size must be a positive integer");
   if (H % 8 != 0)
-    return fail(Q4_ERR_INVALID_ARGUMENT, std::string(q8 ? "Q8" : "Q4") + " expert dimensions must be divisible by 8");
+    return fail(Q4_ERR_INVALID_ARGUMENT, std::string((fmt & kQ8) ? "Q8" : "Q4") + " expert dimensions must be divisible by 8");
   if (M < 1)
-    return fail(Q4_ERR_INVALID_ARGUMENT, std::string(q8 ? "Q8" : "Q4") + " expert gate/up requires input [M,H] with M >= 1");
+    return fail(Q4_ERR_INVALID_ARGUMENT, std::string((fmt & kQ8) ? "Q8" : "Q4") + " expert gate/up requires input [M,H] with M >= 1");
   if (H > kMaxH) return fail(Q4_ERR_UNSUPPORTED, "hidden size above 65536 is not supported");
   if (M > kMaxM) return fail(Q4_ERR_UNSUPPORTED, "more than 65535 tokens per call is not supported");
-  if ((uint64_t)I * weight_row_bytes(q8, H) > kMaxWeightBytes)
+  if ((uint64_t)I * weight_row_bytes((fmt & kQ8) != 0, H) > kMaxWeightBytes)
     return fail(Q4_ERR_UNSUPPORTED, "a projection above 2^31 - 16 bytes is not supported");
   return Q4_OK;
 }
 
-int check_layout(bool q8, const q4_slot_layout* L, int64_t H, int64_t I) {
+int check_layout(unsigned fmt, const q4_slot_layout* L, int64_t H, int64_t I) {
   if (!L) return fail(Q4_ERR_INVALID_ARGUMENT, "slot layout must not be null");
   if (L->slot_bytes == 0) return fail(Q4_ERR_INVALID_ARGUMENT, "expert slot bytes must be a positive integer");
-  const uint64_t wb = (uint64_t)I * weight_row_bytes(q8, H);
+  const uint64_t wb = (uint64_t)I * weight_row_bytes((fmt & kQ8) != 0, H);
   int rc;
   if (L->down_weight_offset != Q4_OFFSET_ABSENT &&
       (rc = check_range(L->down_weight_offset, wb, L->slot_bytes, "down weights")))
@@ -90,9 +94,9 @@ int check_layout(bool q8, const q4_slot_layout* L, int64_t H, int64_t I) {
 // Extra rules of a call that reads the down fields (DOWN_SOURCE and
 // validateCall, page 52): both dimensions divisible by 8, the down fields
 // present and aligned for the kernels' loads.
-int check_down_layout(bool q8, const q4_slot_layout* L, int64_t I) {
+int check_down_layout(unsigned fmt, const q4_slot_layout* L, int64_t I) {
   if (I % 8 != 0)
-    return fail(Q4_ERR_INVALID_ARGUMENT, std::string(q8 ? "Q8" : "Q4") + " expert dimensions must be divisible by 8");
+    return fail(Q4_ERR_INVALID_ARGUMENT, std::string((fmt & kQ8) ? "Q8" : "Q4") + " expert dimensions must be divisible by 8");
   if (I > kMaxH) return fail(Q4_ERR_UNSUPPORTED, "intermediate size above 65536 is not supported by the down projection");
   if (L->down_weight_offset == Q4_OFFSET_ABSENT || L->down_scale_offset == Q4_OFFSET_ABSENT)
     return fail(Q4_ERR_INVALID_ARGUMENT, "the down projection needs down weight and scale offsets");
@@ -101,33 +105,34 @@ int check_down_layout(bool q8, const q4_slot_layout* L, int64_t I) {
   return Q4_OK;
 }
 
-int check_io(const void* x, const void* out, const void* gate_probe, const void* up_probe) {
+int check_io(unsigned fmt, const void* x, const void* out, const void* gate_probe, const void* up_probe) {
   if (!x) return fail(Q4_ERR_INVALID_ARGUMENT, "input x must be a non-null device pointer");
   if (!out) return fail(Q4_ERR_INVALID_ARGUMENT, "output must be a non-null device pointer");
   if (!aligned(x, 16)) return fail(Q4_ERR_ALIGNMENT, "input x must be 16-byte aligned");
-  if (!aligned(out, 2)) return fail(Q4_ERR_ALIGNMENT, "output must be 2-byte aligned");
+  if ((fmt & kF32) ? !aligned(out, 4) : !aligned(out, 2))
+    return fail(Q4_ERR_ALIGNMENT, (fmt & kF32) ? "output must be 4-byte aligned" : "output must be 2-byte aligned");
   if ((gate_probe && !aligned(gate_probe, 4)) || (up_probe && !aligned(up_probe, 4)))
     return fail(Q4_ERR_ALIGNMENT, "gate/up probes must be 4-byte aligned");
   return Q4_OK;
 }
 
-int check_single(bool q8, const void* slot, const q4_slot_layout* layout, const void* x, int64_t M, int64_t H,
+int check_single(unsigned fmt, const void* slot, const q4_slot_layout* layout, const void* x, int64_t M, int64_t H,
                  int64_t I, const void* out, const void* gp, const void* up) {
   int rc;
-  if ((rc = check_dims(q8, M, H, I))) return rc;
+  if ((rc = check_dims(fmt, M, H, I))) return rc;
   if (!slot) return fail(Q4_ERR_INVALID_ARGUMENT, "expert slot pointer must be a non-null device pointer");
   if (!aligned(slot, kSlotAlign))
     return fail(Q4_ERR_ALIGNMENT, "expert slot pointer must be page-aligned (4096 bytes) for direct device access");
-  if ((rc = check_layout(q8, layout, H, I))) return rc;
-  if ((rc = check_io(x, out, gp, up))) return rc;
+  if ((rc = check_layout(fmt, layout, H, I))) return rc;
+  if ((rc = check_io(fmt, x, out, gp, up))) return rc;
   return ok();
 }
 
-int check_grouped(bool q8, const void* base, uint64_t stride, int64_t num_slots, const q4_slot_layout* layout,
+int check_grouped(unsigned fmt, const void* base, uint64_t stride, int64_t num_slots, const q4_slot_layout* layout,
                   const void* x, int64_t M, const int32_t* ids, int64_t K, int64_t H, int64_t I,
                   const void* out, const void* gp, const void* up, const void* ws, size_t ws_bytes) {
   int rc;
-  if ((rc = check_dims(q8, M, H, I))) return rc;
+  if ((rc = check_dims(fmt, M, H, I))) return rc;
   if (K < 1) return fail(Q4_ERR_INVALID_ARGUMENT, "top-k must be a positive integer");
   if (num_slots < 1) return fail(Q4_ERR_INVALID_ARGUMENT, "number of slots must be a positive integer");
   if (num_slots > kMaxSlots) return fail(Q4_ERR_UNSUPPORTED, "more than 65535 slots is not supported");
@@ -136,13 +141,13 @@ int check_grouped(bool q8, const void* base, uint64_t stride, int64_t num_slots,
   if (!aligned(base, kSlotAlign))
     return fail(Q4_ERR_ALIGNMENT, "expert slot pointer must be page-aligned (4096 bytes) for direct device access");
   if (stride % kSlotAlign) return fail(Q4_ERR_ALIGNMENT, "slot stride must be a multiple of 4096 bytes");
-  if ((rc = check_layout(q8, layout, H, I))) return rc;
+  if ((rc = check_layout(fmt, layout, H, I))) return rc;
   if (stride < layout->slot_bytes) return fail(Q4_ERR_RANGE, "slot stride is shorter than the slot");
   if ((uint64_t)(num_slots - 1) > (UINT64_MAX - layout->slot_bytes) / stride)
     return fail(Q4_ERR_RANGE, "slot array exceeds the address space");
   if (!ids) return fail(Q4_ERR_INVALID_ARGUMENT, "slot ids must be a non-null device pointer");
   if (!aligned(ids, 4)) return fail(Q4_ERR_ALIGNMENT, "slot ids must be 4-byte aligned");
-  if ((rc = check_io(x, out, gp, up))) return rc;
+  if ((rc = check_io(fmt, x, out, gp, up))) return rc;
   if (!ws) return fail(Q4_ERR_WORKSPACE, "workspace must be a non-null device pointer");
   if (!aligned(ws, 256)) return fail(Q4_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
   if (ws_bytes < q4_grouped_workspace_bytes(M, K, H, I, num_slots))
@@ -150,7 +155,7 @@ int check_grouped(bool q8, const void* base, uint64_t stride, int64_t num_slots,
   return ok();
 }
 
-q4::GateUpParams make_params(bool q8, const void* base, uint64_t stride, int64_t num_slots, const q4_slot_layout* layout,
+q4::GateUpParams make_params(unsigned fmt, const void* base, uint64_t stride, int64_t num_slots, const q4_slot_layout* layout,
                              const void* x, int64_t M, const int32_t* ids, int64_t K, int64_t H, int64_t I,
                              void* out, float* gp, float* up, void* ws) {
   q4::GateUpParams p{};
@@ -171,7 +176,8 @@ q4::GateUpParams make_params(bool q8, const void* base, uint64_t stride, int64_t
   p.H = (int)H;
   p.I = (int)I;
   p.num_slots = (int)num_slots;
-  p.q8 = q8 ? 1 : 0;
+  p.q8 = (fmt & kQ8) ? 1 : 0;
+  p.xf32 = (fmt & kF32) ? 1 : 0;
   return p;
 }
 
@@ -197,46 +203,46 @@ int launch(const q4::GateUpParams& p, q4_stream_t stream, int pairs_per_slot = 0
   return ok();
 }
 
-int run_single(bool q8, const void* slot, const q4_slot_layout* layout, const void* x, int64_t M, int64_t H, int64_t I,
+int run_single(unsigned fmt, const void* slot, const q4_slot_layout* layout, const void* x, int64_t M, int64_t H, int64_t I,
                void* out, float* gp, float* up, q4_stream_t stream) {
-  const int rc = check_single(q8, slot, layout, x, M, H, I, out, gp, up);
+  const int rc = check_single(fmt, slot, layout, x, M, H, I, out, gp, up);
   if (rc) return rc;
-  return launch(make_params(q8, slot, layout->slot_bytes, 1, layout, x, M, nullptr, 1, H, I, out, gp, up, nullptr),
+  return launch(make_params(fmt, slot, layout->slot_bytes, 1, layout, x, M, nullptr, 1, H, I, out, gp, up, nullptr),
                 stream);
 }
 
-int run_grouped(bool q8, const void* base, uint64_t stride, int64_t num_slots, const q4_slot_layout* layout,
+int run_grouped(unsigned fmt, const void* base, uint64_t stride, int64_t num_slots, const q4_slot_layout* layout,
                 const void* x, int64_t M, const int32_t* ids, int64_t K, int64_t H, int64_t I, void* out,
                 float* gp, float* up, void* ws, size_t ws_bytes, q4_stream_t stream) {
-  const int rc = check_grouped(q8, base, stride, num_slots, layout, x, M, ids, K, H, I, out, gp, up, ws, ws_bytes);
+  const int rc = check_grouped(fmt, base, stride, num_slots, layout, x, M, ids, K, H, I, out, gp, up, ws, ws_bytes);
   if (rc) return rc;
-  return launch(make_params(q8, base, stride, num_slots, layout, x, M, ids, K, H, I, out, gp, up, ws), stream);
+  return launch(make_params(fmt, base, stride, num_slots, layout, x, M, ids, K, H, I, out, gp, up, ws), stream);
 }
 
-int check_down_single(bool q8, const void* slot, const q4_slot_layout* layout, const void* mid, int64_t M, int64_t H,
+int check_down_single(unsigned fmt, const void* slot, const q4_slot_layout* layout, const void* mid, int64_t M, int64_t H,
                       int64_t I, const void* out, const void* probe) {
   int rc;
-  if ((rc = check_single(q8, slot, layout, mid, M, H, I, out, probe, nullptr))) return rc;
-  if ((rc = check_down_layout(q8, layout, I))) return rc;
+  if ((rc = check_single(fmt, slot, layout, mid, M, H, I, out, probe, nullptr))) return rc;
+  if ((rc = check_down_layout(fmt, layout, I))) return rc;
   return ok();
 }
 
-int check_down_grouped(bool q8, const void* base, uint64_t stride, int64_t num_slots, const q4_slot_layout* layout,
+int check_down_grouped(unsigned fmt, const void* base, uint64_t stride, int64_t num_slots, const q4_slot_layout* layout,
                        const void* mid, int64_t M, const int32_t* ids, int64_t K, int64_t H, int64_t I,
                        const void* out, const void* probe, const void* ws, size_t ws_bytes) {
   int rc;
-  if ((rc = check_grouped(q8, base, stride, num_slots, layout, mid, M, ids, K, H, I, out, probe, nullptr, ws, ws_bytes)))
+  if ((rc = check_grouped(fmt, base, stride, num_slots, layout, mid, M, ids, K, H, I, out, probe, nullptr, ws, ws_bytes)))
     return rc;
-  if ((rc = check_down_layout(q8, layout, I))) return rc;
+  if ((rc = check_down_layout(fmt, layout, I))) return rc;
   if (M * K > kMaxM) return fail(Q4_ERR_UNSUPPORTED, "more than 65535 routed pairs per down call is not supported");
   return ok();
 }
 
-int run_down_single(bool q8, const void* slot, const q4_slot_layout* layout, const void* mid, int64_t M, int64_t H,
+int run_down_single(unsigned fmt, const void* slot, const q4_slot_layout* layout, const void* mid, int64_t M, int64_t H,
                     int64_t I, void* out, float* probe, q4_stream_t stream) {
-  const int rc = check_down_single(q8, slot, layout, mid, M, H, I, out, probe);
+  const int rc = check_down_single(fmt, slot, layout, mid, M, H, I, out, probe);
   if (rc) return rc;
-  return launch(down_params(make_params(q8, slot, layout->slot_bytes, 1, layout, mid, M, nullptr, 1, H, I, out, probe,
+  return launch(down_params(make_params(fmt, slot, layout->slot_bytes, 1, layout, mid, M, nullptr, 1, H, I, out, probe,
                                         nullptr, nullptr),
                             layout, H, I),
                 stream);
@@ -244,12 +250,12 @@ int run_down_single(bool q8, const void* slot, const q4_slot_layout* layout, con
 
 // Pair p = t*K + j reads its own input row mid[p] against slot ids[p]: the
 // launch sees M*K tokens routed one each (K = 1) through the same id array.
-int run_down_grouped(bool q8, const void* base, uint64_t stride, int64_t num_slots, const q4_slot_layout* layout,
+int run_down_grouped(unsigned fmt, const void* base, uint64_t stride, int64_t num_slots, const q4_slot_layout* layout,
                      const void* mid, int64_t M, const int32_t* ids, int64_t K, int64_t H, int64_t I, void* out,
                      float* probe, void* ws, size_t ws_bytes, q4_stream_t stream) {
-  const int rc = check_down_grouped(q8, base, stride, num_slots, layout, mid, M, ids, K, H, I, out, probe, ws, ws_bytes);
+  const int rc = check_down_grouped(fmt, base, stride, num_slots, layout, mid, M, ids, K, H, I, out, probe, ws, ws_bytes);
   if (rc) return rc;
-  return launch(down_params(make_params(q8, base, stride, num_slots, layout, mid, M * K, ids, 1, H, I, out, probe,
+  return launch(down_params(make_params(fmt, base, stride, num_slots, layout, mid, M * K, ids, 1, H, I, out, probe,
                                         nullptr, ws),
                             layout, H, I),
                 stream, (int)M);
@@ -261,13 +267,13 @@ extern "C" {
 
 int q4_expert_gate_up(const void* slot, const q4_slot_layout* layout, const void* x_bf16, int64_t M, int64_t H,
                       int64_t I, void* out_bf16, q4_stream_t stream) {
-  return run_single(false, slot, layout, x_bf16, M, H, I, out_bf16, nullptr, nullptr, stream);
+  return run_single(0u, slot, layout, x_bf16, M, H, I, out_bf16, nullptr, nullptr, stream);
 }
 
 int q4_expert_gate_up_probe(const void* slot, const q4_slot_layout* layout, const void* x_bf16, int64_t M,
                             int64_t H, int64_t I, void* out_bf16, float* gate_f32, float* up_f32,
                             q4_stream_t stream) {
-  return run_single(false, slot, layout, x_bf16, M, H, I, out_bf16, gate_f32, up_f32, stream);
+  return run_single(0u, slot, layout, x_bf16, M, H, I, out_bf16, gate_f32, up_f32, stream);
 }
 
 size_t q4_grouped_workspace_bytes(int64_t M, int64_t K, int64_t H, int64_t I, int64_t num_slots) {
@@ -281,7 +287,7 @@ int q4_expert_gate_up_grouped(const void* slots_base, uint64_t slot_stride, int6
                               const q4_slot_layout* layout, const void* x_bf16, int64_t M,
                               const int32_t* slot_ids, int64_t K, int64_t H, int64_t I, void* out_bf16,
                               void* workspace, size_t workspace_bytes, q4_stream_t stream) {
-  return run_grouped(false, slots_base, slot_stride, num_slots, layout, x_bf16, M, slot_ids, K, H, I, out_bf16, nullptr,
+  return run_grouped(0u, slots_base, slot_stride, num_slots, layout, x_bf16, M, slot_ids, K, H, I, out_bf16, nullptr,
                      nullptr, workspace, workspace_bytes, stream);
 }
 
@@ -290,38 +296,38 @@ int q4_expert_gate_up_grouped_probe(const void* slots_base, uint64_t slot_stride
                                     const int32_t* slot_ids, int64_t K, int64_t H, int64_t I, void* out_bf16,
                                     float* gate_f32, float* up_f32, void* workspace, size_t workspace_bytes,
                                     q4_stream_t stream) {
-  return run_grouped(false, slots_base, slot_stride, num_slots, layout, x_bf16, M, slot_ids, K, H, I, out_bf16, gate_f32,
+  return run_grouped(0u, slots_base, slot_stride, num_slots, layout, x_bf16, M, slot_ids, K, H, I, out_bf16, gate_f32,
                      up_f32, workspace, workspace_bytes, stream);
 }
 
 int q4_validate_gate_up(const void* slot, const q4_slot_layout* layout, const void* x_bf16, int64_t M, int64_t H,
                         int64_t I, const void* out_bf16) {
-  return check_single(false, slot, layout, x_bf16, M, H, I, out_bf16, nullptr, nullptr);
+  return check_single(0u, slot, layout, x_bf16, M, H, I, out_bf16, nullptr, nullptr);
 }
 
 int q4_validate_grouped(const void* slots_base, uint64_t slot_stride, int64_t num_slots,
                         const q4_slot_layout* layout, const void* x_bf16, int64_t M, const int32_t* slot_ids,
                         int64_t K, int64_t H, int64_t I, const void* out_bf16, const void* workspace,
                         size_t workspace_bytes) {
-  return check_grouped(false, slots_base, slot_stride, num_slots, layout, x_bf16, M, slot_ids, K, H, I, out_bf16, nullptr,
+  return check_grouped(0u, slots_base, slot_stride, num_slots, layout, x_bf16, M, slot_ids, K, H, I, out_bf16, nullptr,
                        nullptr, workspace, workspace_bytes);
 }
 
 int q4_expert_down(const void* slot, const q4_slot_layout* layout, const void* mid_bf16, int64_t M, int64_t H,
                    int64_t I, void* out_bf16, q4_stream_t stream) {
-  return run_down_single(false, slot, layout, mid_bf16, M, H, I, out_bf16, nullptr, stream);
+  return run_down_single(0u, slot, layout, mid_bf16, M, H, I, out_bf16, nullptr, stream);
 }
 
 int q4_expert_down_probe(const void* slot, const q4_slot_layout* layout, const void* mid_bf16, int64_t M, int64_t H,
                          int64_t I, void* out_bf16, float* down_f32, q4_stream_t stream) {
-  return run_down_single(false, slot, layout, mid_bf16, M, H, I, out_bf16, down_f32, stream);
+  return run_down_single(0u, slot, layout, mid_bf16, M, H, I, out_bf16, down_f32, stream);
 }
 
 int q4_expert_down_grouped(const void* slots_base, uint64_t slot_stride, int64_t num_slots,
                            const q4_slot_layout* layout, const void* mid_bf16, int64_t M, const int32_t* slot_ids,
                            int64_t K, int64_t H, int64_t I, void* out_bf16, void* workspace, size_t workspace_bytes,
                            q4_stream_t stream) {
-  return run_down_grouped(false, slots_base, slot_stride, num_slots, layout, mid_bf16, M, slot_ids, K, H, I, out_bf16,
+  return run_down_grouped(0u, slots_base, slot_stride, num_slots, layout, mid_bf16, M, slot_ids, K, H, I, out_bf16,
                           nullptr, workspace, workspace_bytes, stream);
 }
 
@@ -329,17 +335,17 @@ int q4_expert_down_grouped_probe(const void* slots_base, uint64_t slot_stride, i
                                  const q4_slot_layout* layout, const void* mid_bf16, int64_t M,
                                  const int32_t* slot_ids, int64_t K, int64_t H, int64_t I, void* out_bf16,
                                  float* down_f32, void* workspace, size_t workspace_bytes, q4_stream_t stream) {
-  return run_down_grouped(false, slots_base, slot_stride, num_slots, layout, mid_bf16, M, slot_ids, K, H, I, out_bf16,
+  return run_down_grouped(0u, slots_base, slot_stride, num_slots, layout, mid_bf16, M, slot_ids, K, H, I, out_bf16,
                           down_f32, workspace, workspace_bytes, stream);
 }
 
 int q4_expert_forward(const void* slot, const q4_slot_layout* layout, const void* x_bf16, int64_t M, int64_t H,
                       int64_t I, void* mid_bf16, void* out_bf16, q4_stream_t stream) {
   int rc;
-  if ((rc = check_single(false, slot, layout, x_bf16, M, H, I, mid_bf16, nullptr, nullptr))) return rc;
-  if ((rc = check_down_single(false, slot, layout, mid_bf16, M, H, I, out_bf16, nullptr))) return rc;
-  if ((rc = run_single(false, slot, layout, x_bf16, M, H, I, mid_bf16, nullptr, nullptr, stream))) return rc;
-  return run_down_single(false, slot, layout, mid_bf16, M, H, I, out_bf16, nullptr, stream);
+  if ((rc = check_single(0u, slot, layout, x_bf16, M, H, I, mid_bf16, nullptr, nullptr))) return rc;
+  if ((rc = check_down_single(0u, slot, layout, mid_bf16, M, H, I, out_bf16, nullptr))) return rc;
+  if ((rc = run_single(0u, slot, layout, x_bf16, M, H, I, mid_bf16, nullptr, nullptr, stream))) return rc;
+  return run_down_single(0u, slot, layout, mid_bf16, M, H, I, out_bf16, nullptr, stream);
 }
 
 int q4_expert_forward_grouped(const void* slots_base, uint64_t slot_stride, int64_t num_slots,
@@ -347,29 +353,29 @@ int q4_expert_forward_grouped(const void* slots_base, uint64_t slot_stride, int6
                               int64_t K, int64_t H, int64_t I, void* mid_bf16, void* out_bf16, void* workspace,
                               size_t workspace_bytes, q4_stream_t stream) {
   int rc;
-  if ((rc = check_grouped(false, slots_base, slot_stride, num_slots, layout, x_bf16, M, slot_ids, K, H, I, mid_bf16,
+  if ((rc = check_grouped(0u, slots_base, slot_stride, num_slots, layout, x_bf16, M, slot_ids, K, H, I, mid_bf16,
                           nullptr, nullptr, workspace, workspace_bytes)))
     return rc;
-  if ((rc = check_down_grouped(false, slots_base, slot_stride, num_slots, layout, mid_bf16, M, slot_ids, K, H, I, out_bf16,
+  if ((rc = check_down_grouped(0u, slots_base, slot_stride, num_slots, layout, mid_bf16, M, slot_ids, K, H, I, out_bf16,
                                nullptr, workspace, workspace_bytes)))
     return rc;
-  if ((rc = run_grouped(false, slots_base, slot_stride, num_slots, layout, x_bf16, M, slot_ids, K, H, I, mid_bf16, nullptr,
+  if ((rc = run_grouped(0u, slots_base, slot_stride, num_slots, layout, x_bf16, M, slot_ids, K, H, I, mid_bf16, nullptr,
                         nullptr, workspace, workspace_bytes, stream)))
     return rc;
-  return run_down_grouped(false, slots_base, slot_stride, num_slots, layout, mid_bf16, M, slot_ids, K, H, I, out_bf16,
+  return run_down_grouped(0u, slots_base, slot_stride, num_slots, layout, mid_bf16, M, slot_ids, K, H, I, out_bf16,
                           nullptr, workspace, workspace_bytes, stream);
 }
 
 int q4_validate_down(const void* slot, const q4_slot_layout* layout, const void* mid_bf16, int64_t M, int64_t H,
                      int64_t I, const void* out_bf16) {
-  return check_down_single(false, slot, layout, mid_bf16, M, H, I, out_bf16, nullptr);
+  return check_down_single(0u, slot, layout, mid_bf16, M, H, I, out_bf16, nullptr);
 }
 
 int q4_validate_down_grouped(const void* slots_base, uint64_t slot_stride, int64_t num_slots,
                              const q4_slot_layout* layout, const void* mid_bf16, int64_t M, const int32_t* slot_ids,
                              int64_t K, int64_t H, int64_t I, const void* out_bf16, const void* workspace,
                              size_t workspace_bytes) {
-  return check_down_grouped(false, slots_base, slot_stride, num_slots, layout, mid_bf16, M, slot_ids, K, H, I, out_bf16,
+  return check_down_grouped(0u, slots_base, slot_stride, num_slots, layout, mid_bf16, M, slot_ids, K, H, I, out_bf16,
                             nullptr, workspace, workspace_bytes);
 }
 
@@ -378,20 +384,20 @@ int q4_validate_down_grouped(const void* slots_base, uint64_t slot_stride, int64
 
 int q8_expert_gate_up(const void* slot, const q4_slot_layout* layout, const void* x_bf16, int64_t M, int64_t H,
                       int64_t I, void* out_bf16, q4_stream_t stream) {
-  return run_single(true, slot, layout, x_bf16, M, H, I, out_bf16, nullptr, nullptr, stream);
+  return run_single(kQ8, slot, layout, x_bf16, M, H, I, out_bf16, nullptr, nullptr, stream);
 }
 
 int q8_expert_gate_up_probe(const void* slot, const q4_slot_layout* layout, const void* x_bf16, int64_t M,
                             int64_t H, int64_t I, void* out_bf16, float* gate_f32, float* up_f32,
                             q4_stream_t stream) {
-  return run_single(true, slot, layout, x_bf16, M, H, I, out_bf16, gate_f32, up_f32, stream);
+  return run_single(kQ8, slot, layout, x_bf16, M, H, I, out_bf16, gate_f32, up_f32, stream);
 }
 
 int q8_expert_gate_up_grouped(const void* slots_base, uint64_t slot_stride, int64_t num_slots,
                               const q4_slot_layout* layout, const void* x_bf16, int64_t M,
                               const int32_t* slot_ids, int64_t K, int64_t H, int64_t I, void* out_bf16,
                               void* workspace, size_t workspace_bytes, q4_stream_t stream) {
-  return run_grouped(true, slots_base, slot_stride, num_slots, layout, x_bf16, M, slot_ids, K, H, I, out_bf16, nullptr,
+  return run_grouped(kQ8, slots_base, slot_stride, num_slots, layout, x_bf16, M, slot_ids, K, H, I, out_bf16, nullptr,
                      nullptr, workspace, workspace_bytes, stream);
 }
 
@@ -400,38 +406,38 @@ int q8_expert_gate_up_grouped_probe(const void* slots_base, uint64_t slot_stride
                                     const int32_t* slot_ids, int64_t K, int64_t H, int64_t I, void* out_bf16,
                                     float* gate_f32, float* up_f32, void* workspace, size_t workspace_bytes,
                                     q4_stream_t stream) {
-  return run_grouped(true, slots_base, slot_stride, num_slots, layout, x_bf16, M, slot_ids, K, H, I, out_bf16, gate_f32,
+  return run_grouped(kQ8, slots_base, slot_stride, num_slots, layout, x_bf16, M, slot_ids, K, H, I, out_bf16, gate_f32,
                      up_f32, workspace, workspace_bytes, stream);
 }
 
 int q8_validate_gate_up(const void* slot, const q4_slot_layout* layout, const void* x_bf16, int64_t M, int64_t H,
                         int64_t I, const void* out_bf16) {
-  return check_single(true, slot, layout, x_bf16, M, H, I, out_bf16, nullptr, nullptr);
+  return check_single(kQ8, slot, layout, x_bf16, M, H, I, out_bf16, nullptr, nullptr);
 }
 
 int q8_validate_grouped(const void* slots_base, uint64_t slot_stride, int64_t num_slots,
                         const q4_slot_layout* layout, const void* x_bf16, int64_t M, const int32_t* slot_ids,
                         int64_t K, int64_t H, int64_t I, const void* out_bf16, const void* workspace,
                         size_t workspace_bytes) {
-  return check_grouped(true, slots_base, slot_stride, num_slots, layout, x_bf16, M, slot_ids, K, H, I, out_bf16, nullptr,
+  return check_grouped(kQ8, slots_base, slot_stride, num_slots, layout, x_bf16, M, slot_ids, K, H, I, out_bf16, nullptr,
                        nullptr, workspace, workspace_bytes);
 }
 
 int q8_expert_down(const void* slot, const q4_slot_layout* layout, const void* mid_bf16, int64_t M, int64_t H,
                    int64_t I, void* out_bf16, q4_stream_t stream) {
-  return run_down_single(true, slot, layout, mid_bf16, M, H, I, out_bf16, nullptr, stream);
+  return run_down_single(kQ8, slot, layout, mid_bf16, M, H, I, out_bf16, nullptr, stream);
 }
 
 int q8_expert_down_probe(const void* slot, const q4_slot_layout* layout, const void* mid_bf16, int64_t M, int64_t H,
                          int64_t I, void* out_bf16, float* down_f32, q4_stream_t stream) {
-  return run_down_single(true, slot, layout, mid_bf16, M, H, I, out_bf16, down_f32, stream);
+  return run_down_single(kQ8, slot, layout, mid_bf16, M, H, I, out_bf16, down_f32, stream);
 }
 
 int q8_expert_down_grouped(const void* slots_base, uint64_t slot_stride, int64_t num_slots,
                            const q4_slot_layout* layout, const void* mid_bf16, int64_t M, const int32_t* slot_ids,
                            int64_t K, int64_t H, int64_t I, void* out_bf16, void* workspace, size_t workspace_bytes,
                            q4_stream_t stream) {
-  return run_down_grouped(true, slots_base, slot_stride, num_slots, layout, mid_bf16, M, slot_ids, K, H, I, out_bf16,
+  return run_down_grouped(kQ8, slots_base, slot_stride, num_slots, layout, mid_bf16, M, slot_ids, K, H, I, out_bf16,
                           nullptr, workspace, workspace_bytes, stream);
 }
 
@@ -439,17 +445,17 @@ int q8_expert_down_grouped_probe(const void* slots_base, uint64_t slot_stride, i
                                  const q4_slot_layout* layout, const void* mid_bf16, int64_t M,
                                  const int32_t* slot_ids, int64_t K, int64_t H, int64_t I, void* out_bf16,
                                  float* down_f32, void* workspace, size_t workspace_bytes, q4_stream_t stream) {
-  return run_down_grouped(true, slots_base, slot_stride, num_slots, layout, mid_bf16, M, slot_ids, K, H, I, out_bf16,
+  return run_down_grouped(kQ8, slots_base, slot_stride, num_slots, layout, mid_bf16, M, slot_ids, K, H, I, out_bf16,
                           down_f32, workspace, workspace_bytes, stream);
 }
 
 int q8_expert_forward(const void* slot, const q4_slot_layout* layout, const void* x_bf16, int64_t M, int64_t H,
                       int64_t I, void* mid_bf16, void* out_bf16, q4_stream_t stream) {
   int rc;
-  if ((rc = check_single(true, slot, layout, x_bf16, M, H, I, mid_bf16, nullptr, nullptr))) return rc;
-  if ((rc = check_down_single(true, slot, layout, mid_bf16, M, H, I, out_bf16, nullptr))) return rc;
-  if ((rc = run_single(true, slot, layout, x_bf16, M, H, I, mid_bf16, nullptr, nullptr, stream))) return rc;
-  return run_down_single(true, slot, layout, mid_bf16, M, H, I, out_bf16, nullptr, stream);
+  if ((rc = check_single(kQ8, slot, layout, x_bf16, M, H, I, mid_bf16, nullptr, nullptr))) return rc;
+  if ((rc = check_down_single(kQ8, slot, layout, mid_bf16, M, H, I, out_bf16, nullptr))) return rc;
+  if ((rc = run_single(kQ8, slot, layout, x_bf16, M, H, I, mid_bf16, nullptr, nullptr, stream))) return rc;
+  return run_down_single(kQ8, slot, layout, mid_bf16, M, H, I, out_bf16, nullptr, stream);
 }
 
 int q8_expert_forward_grouped(const void* slots_base, uint64_t slot_stride, int64_t num_slots,
@@ -457,34 +463,251 @@ int q8_expert_forward_grouped(const void* slots_base, uint64_t slot_stride, int6
                               int64_t K, int64_t H, int64_t I, void* mid_bf16, void* out_bf16, void* workspace,
                               size_t workspace_bytes, q4_stream_t stream) {
   int rc;
-  if ((rc = check_grouped(true, slots_base, slot_stride, num_slots, layout, x_bf16, M, slot_ids, K, H, I, mid_bf16,
+  if ((rc = check_grouped(kQ8, slots_base, slot_stride, num_slots, layout, x_bf16, M, slot_ids, K, H, I, mid_bf16,
                           nullptr, nullptr, workspace, workspace_bytes)))
     return rc;
-  if ((rc = check_down_grouped(true, slots_base, slot_stride, num_slots, layout, mid_bf16, M, slot_ids, K, H, I, out_bf16,
+  if ((rc = check_down_grouped(kQ8, slots_base, slot_stride, num_slots, layout, mid_bf16, M, slot_ids, K, H, I, out_bf16,
                                nullptr, workspace, workspace_bytes)))
     return rc;
-  if ((rc = run_grouped(true, slots_base, slot_stride, num_slots, layout, x_bf16, M, slot_ids, K, H, I, mid_bf16, nullptr,
+  if ((rc = run_grouped(kQ8, slots_base, slot_stride, num_slots, layout, x_bf16, M, slot_ids, K, H, I, mid_bf16, nullptr,
                         nullptr, workspace, workspace_bytes, stream)))
     return rc;
-  return run_down_grouped(true, slots_base, slot_stride, num_slots, layout, mid_bf16, M, slot_ids, K, H, I, out_bf16,
+  return run_down_grouped(kQ8, slots_base, slot_stride, num_slots, layout, mid_bf16, M, slot_ids, K, H, I, out_bf16,
                           nullptr, workspace, workspace_bytes, stream);
 }
 
 int q8_validate_down(const void* slot, const q4_slot_layout* layout, const void* mid_bf16, int64_t M, int64_t H,
                      int64_t I, const void* out_bf16) {
-  return check_down_single(true, slot, layout, mid_bf16, M, H, I, out_bf16, nullptr);
+  return check_down_single(kQ8, slot, layout, mid_bf16, M, H, I, out_bf16, nullptr);
 }
 
 int q8_validate_down_grouped(const void* slots_base, uint64_t slot_stride, int64_t num_slots,
                              const q4_slot_layout* layout, const void* mid_bf16, int64_t M, const int32_t* slot_ids,
                              int64_t K, int64_t H, int64_t I, const void* out_bf16, const void* workspace,
                              size_t workspace_bytes) {
-  return check_down_grouped(true, slots_base, slot_stride, num_slots, layout, mid_bf16, M, slot_ids, K, H, I, out_bf16,
+  return check_down_grouped(kQ8, slots_base, slot_stride, num_slots, layout, mid_bf16, M, slot_ids, K, H, I, out_bf16,
+                            nullptr, workspace, workspace_bytes);
+}
+
+
+// ---- f32 activations and outputs (page 52: validateCall accepts float32 input, execute returns the input's dtype) ----
+
+int q4_expert_gate_up_f32(const void* slot, const q4_slot_layout* layout, const void* x_f32, int64_t M, int64_t H,
+                      int64_t I, void* out_f32, q4_stream_t stream) {
+  return run_single(kF32, slot, layout, x_f32, M, H, I, out_f32, nullptr, nullptr, stream);
+}
+
+int q4_expert_gate_up_probe_f32(const void* slot, const q4_slot_layout* layout, const void* x_f32, int64_t M,
+                            int64_t H, int64_t I, void* out_f32, float* gate_f32, float* up_f32,
+                            q4_stream_t stream) {
+  return run_single(kF32, slot, layout, x_f32, M, H, I, out_f32, gate_f32, up_f32, stream);
+}
+
+int q4_expert_gate_up_grouped_f32(const void* slots_base, uint64_t slot_stride, int64_t num_slots,
+                              const q4_slot_layout* layout, const void* x_f32, int64_t M,
+                              const int32_t* slot_ids, int64_t K, int64_t H, int64_t I, void* out_f32,
+                              void* workspace, size_t workspace_bytes, q4_stream_t stream) {
+  return run_grouped(kF32, slots_base, slot_stride, num_slots, layout, x_f32, M, slot_ids, K, H, I, out_f32, nullptr,
+                     nullptr, workspace, workspace_bytes, stream);
+}
+
+int q4_expert_gate_up_grouped_probe_f32(const void* slots_base, uint64_t slot_stride, int64_t num_slots,
+                                    const q4_slot_layout* layout, const void* x_f32, int64_t M,
+                                    const int32_t* slot_ids, int64_t K, int64_t H, int64_t I, void* out_f32,
+                                    float* gate_f32, float* up_f32, void* workspace, size_t workspace_bytes,
+                                    q4_stream_t stream) {
+  return run_grouped(kF32, slots_base, slot_stride, num_slots, layout, x_f32, M, slot_ids, K, H, I, out_f32, gate_f32,
+                     up_f32, workspace, workspace_bytes, stream);
+}
+
+int q4_validate_gate_up_f32(const void* slot, const q4_slot_layout* layout, const void* x_f32, int64_t M, int64_t H,
+                        int64_t I, const void* out_f32) {
+  return check_single(kF32, slot, layout, x_f32, M, H, I, out_f32, nullptr, nullptr);
+}
+
+int q4_validate_grouped_f32(const void* slots_base, uint64_t slot_stride, int64_t num_slots,
+                        const q4_slot_layout* layout, const void* x_f32, int64_t M, const int32_t* slot_ids,
+                        int64_t K, int64_t H, int64_t I, const void* out_f32, const void* workspace,
+                        size_t workspace_bytes) {
+  return check_grouped(kF32, slots_base, slot_stride, num_slots, layout, x_f32, M, slot_ids, K, H, I, out_f32, nullptr,
+                       nullptr, workspace, workspace_bytes);
+}
+
+int q4_expert_down_f32(const void* slot, const q4_slot_layout* layout, const void* mid_f32, int64_t M, int64_t H,
+                   int64_t I, void* out_f32, q4_stream_t stream) {
+  return run_down_single(kF32, slot, layout, mid_f32, M, H, I, out_f32, nullptr, stream);
+}
+
+int q4_expert_down_probe_f32(const void* slot, const q4_slot_layout* layout, const void* mid_f32, int64_t M, int64_t H,
+                         int64_t I, void* out_f32, float* down_f32, q4_stream_t stream) {
+  return run_down_single(kF32, slot, layout, mid_f32, M, H, I, out_f32, down_f32, stream);
+}
+
+int q4_expert_down_grouped_f32(const void* slots_base, uint64_t slot_stride, int64_t num_slots,
+                           const q4_slot_layout* layout, const void* mid_f32, int64_t M, const int32_t* slot_ids,
+                           int64_t K, int64_t H, int64_t I, void* out_f32, void* workspace, size_t workspace_bytes,
+                           q4_stream_t stream) {
+  return run_down_grouped(kF32, slots_base, slot_stride, num_slots, layout, mid_f32, M, slot_ids, K, H, I, out_f32,
+                          nullptr, workspace, workspace_bytes, stream);
+}
+
+int q4_expert_down_grouped_probe_f32(const void* slots_base, uint64_t slot_stride, int64_t num_slots,
+                                 const q4_slot_layout* layout, const void* mid_f32, int64_t M,
+                                 const int32_t* slot_ids, int64_t K, int64_t H, int64_t I, void* out_f32,
+                                 float* down_f32, void* workspace, size_t workspace_bytes, q4_stream_t stream) {
+  return run_down_grouped(kF32, slots_base, slot_stride, num_slots, layout, mid_f32, M, slot_ids, K, H, I, out_f32,
+                          down_f32, workspace, workspace_bytes, stream);
+}
+
+int q4_expert_forward_f32(const void* slot, const q4_slot_layout* layout, const void* x_f32, int64_t M, int64_t H,
+                      int64_t I, void* mid_f32, void* out_f32, q4_stream_t stream) {
+  int rc;
+  if ((rc = check_single(kF32, slot, layout, x_f32, M, H, I, mid_f32, nullptr, nullptr))) return rc;
+  if ((rc = check_down_single(kF32, slot, layout, mid_f32, M, H, I, out_f32, nullptr))) return rc;
+  if ((rc = run_single(kF32, slot, layout, x_f32, M, H, I, mid_f32, nullptr, nullptr, stream))) return rc;
+  return run_down_single(kF32, slot, layout, mid_f32, M, H, I, out_f32, nullptr, stream);
+}
+
+int q4_expert_forward_grouped_f32(const void* slots_base, uint64_t slot_stride, int64_t num_slots,
+                              const q4_slot_layout* layout, const void* x_f32, int64_t M, const int32_t* slot_ids,
+                              int64_t K, int64_t H, int64_t I, void* mid_f32, void* out_f32, void* workspace,
+                              size_t workspace_bytes, q4_stream_t stream) {
+  int rc;
+  if ((rc = check_grouped(kF32, slots_base, slot_stride, num_slots, layout, x_f32, M, slot_ids, K, H, I, mid_f32,
+                          nullptr, nullptr, workspace, workspace_bytes)))
+    return rc;
+  if ((rc = check_down_grouped(kF32, slots_base, slot_stride, num_slots, layout, mid_f32, M, slot_ids, K, H, I, out_f32,
+                               nullptr, workspace, workspace_bytes)))
+    return rc;
+  if ((rc = run_grouped(kF32, slots_base, slot_stride, num_slots, layout, x_f32, M, slot_ids, K, H, I, mid_f32, nullptr,
+                        nullptr, workspace, workspace_bytes, stream)))
+    return rc;
+  return run_down_grouped(kF32, slots_base, slot_stride, num_slots, layout, mid_f32, M, slot_ids, K, H, I, out_f32,
+                          nullptr, workspace, workspace_bytes, stream);
+}
+
+int q4_validate_down_f32(const void* slot, const q4_slot_layout* layout, const void* mid_f32, int64_t M, int64_t H,
+                     int64_t I, const void* out_f32) {
+  return check_down_single(kF32, slot, layout, mid_f32, M, H, I, out_f32, nullptr);
+}
+
+int q4_validate_down_grouped_f32(const void* slots_base, uint64_t slot_stride, int64_t num_slots,
+                             const q4_slot_layout* layout, const void* mid_f32, int64_t M, const int32_t* slot_ids,
+                             int64_t K, int64_t H, int64_t I, const void* out_f32, const void* workspace,
+                             size_t workspace_bytes) {
+  return check_down_grouped(kF32, slots_base, slot_stride, num_slots, layout, mid_f32, M, slot_ids, K, H, I, out_f32,
+                            nullptr, workspace, workspace_bytes);
+}
+
+int q8_expert_gate_up_f32(const void* slot, const q4_slot_layout* layout, const void* x_f32, int64_t M, int64_t H,
+                      int64_t I, void* out_f32, q4_stream_t stream) {
+  return run_single(kQ8 | kF32, slot, layout, x_f32, M, H, I, out_f32, nullptr, nullptr, stream);
+}
+
+int q8_expert_gate_up_probe_f32(const void* slot, const q4_slot_layout* layout, const void* x_f32, int64_t M,
+                            int64_t H, int64_t I, void* out_f32, float* gate_f32, float* up_f32,
+                            q4_stream_t stream) {
+  return run_single(kQ8 | kF32, slot, layout, x_f32, M, H, I, out_f32, gate_f32, up_f32, stream);
+}
+
+int q8_expert_gate_up_grouped_f32(const void* slots_base, uint64_t slot_stride, int64_t num_slots,
+                              const q4_slot_layout* layout, const void* x_f32, int64_t M,
+                              const int32_t* slot_ids, int64_t K, int64_t H, int64_t I, void* out_f32,
+                              void* workspace, size_t workspace_bytes, q4_stream_t stream) {
+  return run_grouped(kQ8 | kF32, slots_base, slot_stride, num_slots, layout, x_f32, M, slot_ids, K, H, I, out_f32, nullptr,
+                     nullptr, workspace, workspace_bytes, stream);
+}
+
+int q8_expert_gate_up_grouped_probe_f32(const void* slots_base, uint64_t slot_stride, int64_t num_slots,
+                                    const q4_slot_layout* layout, const void* x_f32, int64_t M,
+                                    const int32_t* slot_ids, int64_t K, int64_t H, int64_t I, void* out_f32,
+                                    float* gate_f32, float* up_f32, void* workspace, size_t workspace_bytes,
+                                    q4_stream_t stream) {
+  return run_grouped(kQ8 | kF32, slots_base, slot_stride, num_slots, layout, x_f32, M, slot_ids, K, H, I, out_f32, gate_f32,
+                     up_f32, workspace, workspace_bytes, stream);
+}
+
+int q8_validate_gate_up_f32(const void* slot, const q4_slot_layout* layout, const void* x_f32, int64_t M, int64_t H,
+                        int64_t I, const void* out_f32) {
+  return check_single(kQ8 | kF32, slot, layout, x_f32, M, H, I, out_f32, nullptr, nullptr);
+}
+
+int q8_validate_grouped_f32(const void* slots_base, uint64_t slot_stride, int64_t num_slots,
+                        const q4_slot_layout* layout, const void* x_f32, int64_t M, const int32_t* slot_ids,
+                        int64_t K, int64_t H, int64_t I, const void* out_f32, const void* workspace,
+                        size_t workspace_bytes) {
+  return check_grouped(kQ8 | kF32, slots_base, slot_stride, num_slots, layout, x_f32, M, slot_ids, K, H, I, out_f32, nullptr,
+                       nullptr, workspace, workspace_bytes);
+}
+
+int q8_expert_down_f32(const void* slot, const q4_slot_layout* layout, const void* mid_f32, int64_t M, int64_t H,
+                   int64_t I, void* out_f32, q4_stream_t stream) {
+  return run_down_single(kQ8 | kF32, slot, layout, mid_f32, M, H, I, out_f32, nullptr, stream);
+}
+
+int q8_expert_down_probe_f32(const void* slot, const q4_slot_layout* layout, const void* mid_f32, int64_t M, int64_t H,
+                         int64_t I, void* out_f32, float* down_f32, q4_stream_t stream) {
+  return run_down_single(kQ8 | kF32, slot, layout, mid_f32, M, H, I, out_f32, down_f32, stream);
+}
+
+int q8_expert_down_grouped_f32(const void* slots_base, uint64_t slot_stride, int64_t num_slots,
+                           const q4_slot_layout* layout, const void* mid_f32, int64_t M, const int32_t* slot_ids,
+                           int64_t K, int64_t H, int64_t I, void* out_f32, void* workspace, size_t workspace_bytes,
+                           q4_stream_t stream) {
+  return run_down_grouped(kQ8 | kF32, slots_base, slot_stride, num_slots, layout, mid_f32, M, slot_ids, K, H, I, out_f32,
+                          nullptr, workspace, workspace_bytes, stream);
+}
+
+int q8_expert_down_grouped_probe_f32(const void* slots_base, uint64_t slot_stride, int64_t num_slots,
+                                 const q4_slot_layout* layout, const void* mid_f32, int64_t M,
+                                 const int32_t* slot_ids, int64_t K, int64_t H, int64_t I, void* out_f32,
+                                 float* down_f32, void* workspace, size_t workspace_bytes, q4_stream_t stream) {
+  return run_down_grouped(kQ8 | kF32, slots_base, slot_stride, num_slots, layout, mid_f32, M, slot_ids, K, H, I, out_f32,
+                          down_f32, workspace, workspace_bytes, stream);
+}
+
+int q8_expert_forward_f32(const void* slot, const q4_slot_layout* layout, const void* x_f32, int64_t M, int64_t H,
+                      int64_t I, void* mid_f32, void* out_f32, q4_stream_t stream) {
+  int rc;
+  if ((rc = check_single(kQ8 | kF32, slot, layout, x_f32, M, H, I, mid_f32, nullptr, nullptr))) return rc;
+  if ((rc = check_down_single(kQ8 | kF32, slot, layout, mid_f32, M, H, I, out_f32, nullptr))) return rc;
+  if ((rc = run_single(kQ8 | kF32, slot, layout, x_f32, M, H, I, mid_f32, nullptr, nullptr, stream))) return rc;
+  return run_down_single(kQ8 | kF32, slot, layout, mid_f32, M, H, I, out_f32, nullptr, stream);
+}
+
+int q8_expert_forward_grouped_f32(const void* slots_base, uint64_t slot_stride, int64_t num_slots,
+                              const q4_slot_layout* layout, const void* x_f32, int64_t M, const int32_t* slot_ids,
+                              int64_t K, int64_t H, int64_t I, void* mid_f32, void* out_f32, void* workspace,
+                              size_t workspace_bytes, q4_stream_t stream) {
+  int rc;
+  if ((rc = check_grouped(kQ8 | kF32, slots_base, slot_stride, num_slots, layout, x_f32, M, slot_ids, K, H, I, mid_f32,
+                          nullptr, nullptr, workspace, workspace_bytes)))
+    return rc;
+  if ((rc = check_down_grouped(kQ8 | kF32, slots_base, slot_stride, num_slots, layout, mid_f32, M, slot_ids, K, H, I, out_f32,
+                               nullptr, workspace, workspace_bytes)))
+    return rc;
+  if ((rc = run_grouped(kQ8 | kF32, slots_base, slot_stride, num_slots, layout, x_f32, M, slot_ids, K, H, I, mid_f32, nullptr,
+                        nullptr, workspace, workspace_bytes, stream)))
+    return rc;
+  return run_down_grouped(kQ8 | kF32, slots_base, slot_stride, num_slots, layout, mid_f32, M, slot_ids, K, H, I, out_f32,
+                          nullptr, workspace, workspace_bytes, stream);
+}
+
+int q8_validate_down_f32(const void* slot, const q4_slot_layout* layout, const void* mid_f32, int64_t M, int64_t H,
+                     int64_t I, const void* out_f32) {
+  return check_down_single(kQ8 | kF32, slot, layout, mid_f32, M, H, I, out_f32, nullptr);
+}
+
+int q8_validate_down_grouped_f32(const void* slots_base, uint64_t slot_stride, int64_t num_slots,
+                             const q4_slot_layout* layout, const void* mid_f32, int64_t M, const int32_t* slot_ids,
+                             int64_t K, int64_t H, int64_t I, const void* out_f32, const void* workspace,
+                             size_t workspace_bytes) {
+  return check_down_grouped(kQ8 | kF32, slots_base, slot_stride, num_slots, layout, mid_f32, M, slot_ids, K, H, I, out_f32,
                             nullptr, workspace, workspace_bytes);
 }
 
 const char* q4_last_error(void) { return g_err.c_str(); }
 
-int q4_abi_version(void) { return 3; }
+int q4_abi_version(void) { return 4; }
 
 }  // extern "C"

@@ -61,7 +61,8 @@ __host__ __device__ inline int bat_chunk_steps(int ntiles, int S) {
 // 32 rows, its first 16 taking the gate role and the next 16 the up role,
 // each output rounded to bf16 on its own) instead of gate/up + SwiGLU.
 // Q8: signed int8 weights, one byte per weight (else packed nibbles).
-template <int NT, bool VEC, bool DOWN, bool Q8>
+// XF: f32 activations and outputs (else bf16).
+template <int NT, bool VEC, bool DOWN, bool Q8, bool XF>
 __global__ __launch_bounds__(kBatThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void batch_kernel(const GateUpParams a) {
   // pairs per token group: up to 16*NT/4 (four digits), trimmed to 16*NT/6
@@ -82,6 +83,7 @@ void batch_kernel(const GateUpParams a) {
   const int H = a.H, I = a.I;
   const int P = a.M * a.K;
   const bool grouped = a.ids != nullptr;
+  constexpr bool xf = XF;
   const int S = a.steps;                     // K-steps per tile, even
   constexpr int RT = DOWN ? 32 : 16;         // rows per tile
   const int tps = (I + RT - 1) / RT;
@@ -105,7 +107,10 @@ void batch_kernel(const GateUpParams a) {
         ++cnt;
         for (int r = 0; r < I; ++r) {
           const uint64_t o = (uint64_t)p * I + r;
-          a.out[o] = 0;
+          if (xf)
+            ((float*)a.out)[o] = 0.0f;
+          else
+            a.out[o] = 0;
           if (a.gate_probe) a.gate_probe[o] = 0.0f;
           if (a.up_probe) a.up_probe[o] = 0.0f;
         }
@@ -215,9 +220,14 @@ void batch_kernel(const GateUpParams a) {
         uint32_t mx = 0, mn = 255;
         if (u < nxu) {
           const int w8 = u - ti * (H / 8);
-          const uint4 xq = *(const uint4*)(a.x + (uint64_t)(s_pairs[ti] / a.K) * H + 8 * w8);
-          mx = max_mag8(xq);
-          mn = min_exp8(xq);
+          if (xf) {
+            const uint4* xp = (const uint4*)((const float*)a.x + (uint64_t)(s_pairs[ti] / a.K) * H + 8 * w8);
+            f32_range8(xp[0], xp[1], mx, mn);
+          } else {
+            const uint4 xq = *(const uint4*)(a.x + (uint64_t)(s_pairs[ti] / a.K) * H + 8 * w8);
+            mx = max_mag8(xq);
+            mn = min_exp8(xq);
+          }
         }
         if (__shfl(ti, 0) == __shfl(ti, 63)) {
 #pragma unroll
@@ -236,9 +246,9 @@ void batch_kernel(const GateUpParams a) {
       // digits per value for the whole group: four when every token allows it
       int L = 4;
       for (int ti = 0; ti < count; ++ti) L = max(L, digits_for(s_xmax[ti], s_xmin[ti]));
-      L = __builtin_amdgcn_readfirstlane(L);
-      if (L == 6 && count > (16 * NT) / 6) {
-        count = (16 * NT) / 6;                         // the rest go to the next group
+      L = xf ? 8 : __builtin_amdgcn_readfirstlane(L);   // f32: eight digits per value
+      if (L > 4 && count > (16 * NT) / L) {
+        count = (16 * NT) / L;                         // the rest go to the next group
         more = 1;
       }
       next_pair = s_pairs[count - 1] + 1;
@@ -286,6 +296,22 @@ void batch_kernel(const GateUpParams a) {
           }
         }
       };
+      // eight digits of eight f32 activations: columns 8*ti .. 8*ti+7
+      auto stage_unitf = [&](uint8_t* buf, int ti, int w8, const uint4 xa, const uint4 xb) {
+        const int etop1 = max((int)(((uint32_t)s_xmax[ti] >> 23) & 0xFFu), 1);
+        const int tl = w8 >> 4, gg = (w8 >> 2) & 3, i = w8 & 3;
+        uint32_t d[2][8];
+        xf8_digits(xa, xb, etop1, d);
+#pragma unroll
+        for (int par = 0; par < 2; ++par) {
+          uint8_t* base = buf + tl * sb + par * ntiles * 1024 + gg * 256 + 4 * i;
+#pragma unroll
+          for (int sd = 0; sd < 8; ++sd) {
+            const int col = ti * 8 + sd;
+            *(uint32_t*)(base + (col >> 4) * 1024 + (col & 15) * 16) = d[par][sd];
+          }
+        }
+      };
       auto stage = [&](int c, uint8_t* buf) {
         const int k0c = c * spc * 128;
         const int n8 = min(spc, S - c * spc) * 16;
@@ -293,9 +319,19 @@ void batch_kernel(const GateUpParams a) {
           const int ti = u % count;
           const int w8 = u / count;
           const int k0 = k0c + 8 * w8;
-          uint4 xq = make_uint4(0, 0, 0, 0);
-          if (k0 < H) xq = *(const uint4*)(a.x + (uint64_t)(s_pairs[ti] / a.K) * H + k0);
-          stage_unit(buf, ti, w8, xq);
+          if (xf) {
+            uint4 xa = make_uint4(0, 0, 0, 0), xb = make_uint4(0, 0, 0, 0);
+            if (k0 < H) {
+              const uint4* xp = (const uint4*)((const float*)a.x + (uint64_t)(s_pairs[ti] / a.K) * H + k0);
+              xa = xp[0];
+              xb = xp[1];
+            }
+            stage_unitf(buf, ti, w8, xa, xb);
+          } else {
+            uint4 xq = make_uint4(0, 0, 0, 0);
+            if (k0 < H) xq = *(const uint4*)(a.x + (uint64_t)(s_pairs[ti] / a.K) * H + k0);
+            stage_unit(buf, ti, w8, xq);
+          }
         }
       };
 
@@ -429,22 +465,39 @@ void batch_kernel(const GateUpParams a) {
                 const int row = tile * RT + rr + (DOWN ? 16 * part : 0);
                 if (ti < count && row < I) {
                   const int32_t* d = ep + rr * kEpStride + ti * L;
-                  const int64_t lo = (int64_t)d[0] + ((int64_t)d[1] << 8) + ((int64_t)d[2] << 16);
-                  const int64_t hi = L == 6 ? (int64_t)d[3] + ((int64_t)d[4] << 8) + ((int64_t)d[5] << 16)
-                                            : (int64_t)d[3];
                   const int xm = s_xmax[ti];
-                  float r = round_scaled(hi, lo, sum_exponent(xm) + 8 * (6 - L) + weight_exp_shift<Q8>(),
-                                         (part && !DOWN) ? uscale[row] : gscale[row]);
-                  if (xm >= 0x7F80) r = __builtin_nanf("");
+                  const float sc = (part && !DOWN) ? uscale[row] : gscale[row];
+                  float r;
+                  if (xf) {
+                    // eight digits: V = hi * 2^32 + lo
+                    const int64_t lo = (int64_t)d[0] + ((int64_t)d[1] << 8) + ((int64_t)d[2] << 16) +
+                                       ((int64_t)d[3] << 24);
+                    const int64_t hi = (int64_t)d[4] + ((int64_t)d[5] << 8) + ((int64_t)d[6] << 16) +
+                                       ((int64_t)d[7] << 24);
+                    r = round_scaled_wide(hi, lo, sum_exponent_f32((uint32_t)xm) + weight_exp_shift<Q8>(), sc);
+                    if ((uint32_t)xm >= 0x7F800000u) r = __builtin_nanf("");
+                  } else {
+                    const int64_t lo = (int64_t)d[0] + ((int64_t)d[1] << 8) + ((int64_t)d[2] << 16);
+                    const int64_t hi = L == 6 ? (int64_t)d[3] + ((int64_t)d[4] << 8) + ((int64_t)d[5] << 16)
+                                              : (int64_t)d[3];
+                    r = round_scaled(hi, lo, sum_exponent(xm) + 8 * (6 - L) + weight_exp_shift<Q8>(), sc);
+                    if (xm >= 0x7F80) r = __builtin_nanf("");
+                  }
                   if constexpr (DOWN) {
                     const uint64_t o = (uint64_t)s_pairs[ti] * I + row;
-                    a.out[o] = bf16_rne(r);
+                    if (xf)
+                      ((float*)a.out)[o] = r;
+                    else
+                      a.out[o] = bf16_rne(r);
                     if (a.gate_probe) a.gate_probe[o] = r;
                   } else if (!part) {
                     gv[j] = r;
                   } else {
                     const uint64_t o = (uint64_t)s_pairs[ti] * I + row;
-                    a.out[o] = swiglu_tail_tab(gv[j], r, s_sig);
+                    if (xf)
+                      ((float*)a.out)[o] = swiglu_tail_f32(gv[j], r);
+                    else
+                      a.out[o] = swiglu_tail_tab(gv[j], r, s_sig);
                     if (a.gate_probe) a.gate_probe[o] = gv[j];
                     if (a.up_probe) a.up_probe[o] = r;
                   }
@@ -465,7 +518,7 @@ void batch_kernel(const GateUpParams a) {
 
 namespace {
 
-template <int NT, bool VEC, bool DOWN, bool Q8>
+template <int NT, bool VEC, bool DOWN, bool Q8, bool XF>
 int batch_blocks(int device) {
   static int cached[64] = {0};
   if (device < 0 || device >= 64) device = 0;
@@ -474,7 +527,7 @@ int batch_blocks(int device) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0)
       cus = 256;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&batch_kernel<NT, VEC, DOWN, Q8>), kBatThreads, 0) != hipSuccess ||
+            &per_cu, reinterpret_cast<const void*>(&batch_kernel<NT, VEC, DOWN, Q8, XF>), kBatThreads, 0) != hipSuccess ||
         per_cu <= 0)
       per_cu = 1;
     cached[device] = cus * per_cu;
@@ -482,27 +535,33 @@ int batch_blocks(int device) {
   return cached[device];
 }
 
-template <int NT, bool VEC, bool DOWN, bool Q8>
+template <int NT, bool VEC, bool DOWN, bool Q8, bool XF>
 hipError_t launch_batch_t(GateUpParams& p, hipStream_t stream) {
   int device = 0;
   if (hipGetDevice(&device) != hipSuccess) device = 0;
   const int rt = DOWN ? 32 : 16;
   const int tiles = p.num_slots * ((p.I + rt - 1) / rt);
-  int nb = batch_blocks<NT, VEC, DOWN, Q8>(device);
+  int nb = batch_blocks<NT, VEC, DOWN, Q8, XF>(device);
   if (nb > tiles) nb = tiles;
   void* args[] = {&p};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&batch_kernel<NT, VEC, DOWN, Q8>), dim3((unsigned)nb),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&batch_kernel<NT, VEC, DOWN, Q8, XF>), dim3((unsigned)nb),
                          dim3(kBatThreads), args, 0, stream);
 }
 
-template <bool DOWN, bool Q8>
+template <bool DOWN, bool Q8, bool XF>
 hipError_t launch_batch_m(GateUpParams& p, int nt, hipStream_t stream) {
   const bool vec = row_bytes<Q8>(p.H) % 16 == 0;
   if (nt == 1)
-    return vec ? launch_batch_t<1, true, DOWN, Q8>(p, stream) : launch_batch_t<1, false, DOWN, Q8>(p, stream);
+    return vec ? launch_batch_t<1, true, DOWN, Q8, XF>(p, stream) : launch_batch_t<1, false, DOWN, Q8, XF>(p, stream);
   if (nt == 2)
-    return vec ? launch_batch_t<2, true, DOWN, Q8>(p, stream) : launch_batch_t<2, false, DOWN, Q8>(p, stream);
-  return vec ? launch_batch_t<3, true, DOWN, Q8>(p, stream) : launch_batch_t<3, false, DOWN, Q8>(p, stream);
+    return vec ? launch_batch_t<2, true, DOWN, Q8, XF>(p, stream) : launch_batch_t<2, false, DOWN, Q8, XF>(p, stream);
+  return vec ? launch_batch_t<3, true, DOWN, Q8, XF>(p, stream) : launch_batch_t<3, false, DOWN, Q8, XF>(p, stream);
+}
+
+template <bool XF>
+hipError_t launch_batch_x(GateUpParams& p, int nt, hipStream_t stream) {
+  if (p.q8) return p.down ? launch_batch_m<true, true, XF>(p, nt, stream) : launch_batch_m<false, true, XF>(p, nt, stream);
+  return p.down ? launch_batch_m<true, false, XF>(p, nt, stream) : launch_batch_m<false, false, XF>(p, nt, stream);
 }
 
 }  // namespace
@@ -512,8 +571,7 @@ hipError_t launch_batch(GateUpParams p, int tokens_per_slot, hipStream_t stream)
   p.steps += p.steps & 1;
   const int nt = tokens_per_slot <= 2 ? 1 : (tokens_per_slot <= 5 ? 2 : 3);
   p.G = (16 * nt) / 4;
-  if (p.q8) return p.down ? launch_batch_m<true, true>(p, nt, stream) : launch_batch_m<false, true>(p, nt, stream);
-  return p.down ? launch_batch_m<true, false>(p, nt, stream) : launch_batch_m<false, false>(p, nt, stream);
+  return p.xf32 ? launch_batch_x<true>(p, nt, stream) : launch_batch_x<false>(p, nt, stream);
 }
 
 }  // namespace q4

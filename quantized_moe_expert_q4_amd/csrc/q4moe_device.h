@@ -330,6 +330,167 @@ __device__ __forceinline__ void x8_digits4(const uint4 v, int etop1, uint32_t (&
   }
 }
 
+// ---- f32 activations ----
+// Eight balanced base-256 digits of X = round(x * 2^(188 - etop1)) for an f32
+// value x (|X| <= 2^62; `etop1` is max(exponent field of the token's largest
+// |x|, 1)).  Values at most 38 binades below the largest are exact; smaller
+// ones are rounded to the grid (half away from zero).  The sum of products
+// is then V * 2^(etop1 - 192) with the 16x weight factor.
+__device__ __forceinline__ uint64_t xf_digits(uint32_t b, int etop1) {
+  const uint32_t E = (b >> 23) & 0xFFu;
+  const uint32_t mag = (b & 0x7FFFFFu) | (E ? 0x800000u : 0u);
+  const int sh = (int)(E ? E : 1u) - etop1 + 38;
+  int64_t X;
+  if (sh >= 0) {
+    X = (int64_t)mag << sh;
+  } else if (sh >= -24) {
+    X = (int64_t)((mag + (1u << (-sh - 1))) >> (-sh));
+  } else {
+    X = 0;
+  }
+  if (b & 0x80000000u) X = -X;
+  const uint64_t C = 0x8080808080808080ull;
+  return ((uint64_t)X + C) ^ C;
+}
+
+// Byte transpose of eight words of four digits each (positions p = 0..7):
+// d[s] receives digit s of positions par, par+2, par+4, par+6.
+__device__ __forceinline__ void transpose4(const uint32_t (&w)[8], int par, uint32_t (&d)[4]) {
+  const uint32_t u01 = perm(w[par + 2], w[par], 0x05010400u);
+  const uint32_t u23 = perm(w[par + 2], w[par], 0x07030602u);
+  const uint32_t v01 = perm(w[par + 6], w[par + 4], 0x05010400u);
+  const uint32_t v23 = perm(w[par + 6], w[par + 4], 0x07030602u);
+  d[0] = perm(v01, u01, 0x05040100u);
+  d[1] = perm(v01, u01, 0x07060302u);
+  d[2] = perm(v23, u23, 0x05040100u);
+  d[3] = perm(v23, u23, 0x07060302u);
+}
+
+// Digit words of eight f32 activations (positions 0..3 in `a`, 4..7 in `b`):
+// d[par][s], s = 0..7, holds digit s of positions par, par+2, par+4, par+6.
+__device__ __forceinline__ void xf8_digits(const uint4 a, const uint4 b, int etop1, uint32_t (&d)[2][8]) {
+  const uint32_t xb[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t lo[8], hi[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const uint64_t z = xf_digits(xb[p], etop1);
+    lo[p] = (uint32_t)z;
+    hi[p] = (uint32_t)(z >> 32);
+  }
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    uint32_t l4[4], h4[4];
+    transpose4(lo, par, l4);
+    transpose4(hi, par, h4);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      d[par][s] = l4[s];
+      d[par][4 + s] = h4[s];
+    }
+  }
+}
+
+// Largest f32 magnitude bits and smallest non-zero exponent field (at least
+// 1; 255 if none) among eight f32 activations.
+__device__ __forceinline__ void f32_range8(const uint4 a, const uint4 b, uint32_t& mx, uint32_t& mn) {
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  mx = 0u;
+  mn = 255u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t m = w[i] & 0x7FFFFFFFu;
+    mx = max(mx, m);
+    if (m) mn = min(mn, max((m >> 23) & 0xFFu, 1u));
+  }
+}
+
+// Exponent offset of an eight-digit f32 sum: sum(w*x) = V * 2^(etop1 - 192).
+__device__ __forceinline__ int sum_exponent_f32(uint32_t xmax_bits) {
+  return max((int)((xmax_bits >> 23) & 0xFFu), 1) - 192;
+}
+
+// Round (hi * 2^32 + lo) * 2^e2 * s to F32 once (nearest, ties to even),
+// exactly, with integer arithmetic: the eight-digit sums have up to 88
+// significant bits, so the product with the scale's 24-bit significand
+// (up to 112 bits) is formed in two 64-bit words and rounded from its top
+// 64 bits and a sticky bit.  An exact zero takes the sign of the scale.
+__device__ float round_scaled_wide(int64_t hi, int64_t lo, int e2, float s) {
+  // V = hi * 2^32 + lo as a sign and a 128-bit magnitude (vh:vl)
+  const int64_t lo_hi = lo >> 32;                       // arithmetic: floor(lo / 2^32)
+  const uint64_t lo_lo = (uint64_t)lo & 0xFFFFFFFFull;
+  const int64_t top = hi + lo_hi;                        // V = top * 2^32 + lo_lo, |top| < 2^63
+  uint64_t vh, vl;
+  bool neg = top < 0;
+  if (!neg) {
+    vh = (uint64_t)top >> 32;
+    vl = ((uint64_t)top << 32) | lo_lo;
+  } else {
+    // |V| = -(top * 2^32 + lo_lo) = (-top) * 2^32 - lo_lo
+    const uint64_t t = (uint64_t)(-top);
+    uint64_t h = t >> 32, l = t << 32;
+    if (lo_lo) {
+      h -= (l < lo_lo) ? 1u : 0u;
+      l -= lo_lo;
+    }
+    vh = h;
+    vl = l;
+  }
+  const uint32_t sb = __float_as_uint(s);
+  const uint32_t se = (sb >> 23) & 0xFFu;
+  const uint64_t m = (sb & 0x7FFFFFu) | (se ? 0x800000u : 0u);
+  const int es = (int)(se ? se : 1u) - 150;
+  if (sb & 0x80000000u) neg = !neg;
+  // N = |V| * m over three 32-bit limbs of |V| (|V| < 2^88)
+  const uint64_t a0 = vl & 0xFFFFFFFFull, a1 = vl >> 32, a2 = vh;
+  const uint64_t p0 = a0 * m, p1 = a1 * m, p2 = a2 * m;
+  uint64_t nl = p0 + (p1 << 32);
+  const uint64_t c = nl < p0 ? 1u : 0u;
+  const uint64_t nh = (p1 >> 32) + p2 + c;
+  if ((nh | nl) == 0) return __uint_as_float(sb & 0x80000000u);   // exact zero: sign of the scale
+  // top 64 bits T of N (its most significant bit at bit 63) and a sticky bit
+  int msb;
+  uint64_t T;
+  bool sticky;
+  if (nh) {
+    const int lz = __builtin_clzll(nh);
+    msb = 127 - lz;
+    T = lz ? ((nh << lz) | (nl >> (64 - lz))) : nh;
+    sticky = lz ? (nl << lz) != 0 : nl != 0;
+  } else {
+    const int lz = __builtin_clzll(nl);
+    msb = 63 - lz;
+    T = nl << lz;
+    sticky = false;
+  }
+  // value = (T + below) * 2^(E), E the weight of T's bit 0
+  const int E = e2 + es + msb - 63;
+  const int topexp = E + 63;                              // exponent of T's leading bit
+  const int keep = topexp >= -126 ? 24 : 24 - (-126 - topexp);
+  float r;
+  if (keep <= 0) {
+    // below half of the smallest subnormal unless exactly at it with more below
+    const bool up = keep == 0 && (T > (1ull << 63) || sticky);
+    r = up ? __builtin_ldexpf(1.0f, -149) : 0.0f;
+  } else {
+    const int drop = 64 - keep;                           // >= 40
+    uint64_t q = T >> drop;
+    const uint64_t rem = T & ((1ull << drop) - 1ull);
+    const uint64_t half = 1ull << (drop - 1);
+    if (rem > half || (rem == half && (sticky || (q & 1ull)))) ++q;
+    r = __builtin_ldexpf((float)q, E + drop);
+  }
+  return neg ? -r : r;
+}
+
+// The lane-0 tail with T = float: every conversion to T is the identity.
+__device__ float swiglu_tail_f32(float gate, float up) {
+#pragma clang fp contract(off)
+  const float e = (float)exp(-(double)gate);
+  const float d = 1.0f + e;
+  const float sg = 1.0f / d;
+  return (gate * sg) * up;
+}
+
 // Largest bf16 magnitude bits among eight packed activations.
 __device__ __forceinline__ uint32_t max_mag8(const uint4 v) {
   uint32_t m = max(max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu), max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu));

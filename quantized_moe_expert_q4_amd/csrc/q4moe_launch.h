@@ -15,9 +15,9 @@ struct GateUpParams {
   const uint8_t* slots;      // slot 0 base (4096-aligned)
   uint64_t slot_stride;      // bytes between slots
   uint64_t gate_w_off, up_w_off, gate_s_off, up_s_off;
-  const uint16_t* x;         // bf16 [M][H]
+  const uint16_t* x;         // bf16 [M][H] (float [M][H] with xf32)
   const int32_t* ids;        // int32 [M][K] or nullptr
-  uint16_t* out;             // bf16 [M*K][I]
+  uint16_t* out;             // bf16 [M*K][I] (float with xf32)
   float* gate_probe;         // F32 [M*K][I] or nullptr
   float* up_probe;           // F32 [M*K][I] or nullptr
   int32_t* invalid_count;    // grouped: number of out-of-range ids, or nullptr
@@ -26,6 +26,7 @@ struct GateUpParams {
   int wave_share;            // set by launch_resident: a SIMD's first-wave share, 1/1024
   int down;                  // 1: down projection (see above)
   int q8;                    // 1: signed int8 weights [rows][H] (else packed nibbles [rows][H/8] words)
+  int xf32;                  // 1: x and out are float32 (else bf16); probes unchanged
 };
 
 // Resident-digits kernel for token groups of at most two (decode widths):

@@ -67,7 +67,8 @@ __host__ __device__ constexpr int res_tiles(int M) { return M <= 2 ? 1 : 2; }
 // 32 rows, its first 16 taking the gate role and the next 16 the up role,
 // each output rounded to bf16 on its own) instead of gate/up + SwiGLU.
 // Q8: signed int8 weights, one byte per weight (else packed nibbles).
-template <int NT, bool VEC, bool DOWN, bool Q8>
+// XF: f32 activations and outputs (else bf16).
+template <int NT, bool VEC, bool DOWN, bool Q8, bool XF>
 __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void resident_kernel(const GateUpParams a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_lds[kResLds];
   __shared__ int s_pairs[kResMaxPairs];
@@ -88,6 +89,7 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int H = a.H, I = a.I, M = a.M, K = a.K;
   const int P = M * K;
   const bool grouped = a.ids != nullptr;
+  constexpr bool xf = XF;
   const int S = a.steps;                     // K-steps per tile, a multiple of D
   const int sbytes = res_step_bytes(NT);
   const int hw = H / 8;                      // 16-byte chunks of one token's x
@@ -125,7 +127,10 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
         ++cnt;
         for (int r = 0; r < I; ++r) {
           const uint64_t o = (uint64_t)p * I + r;
-          a.out[o] = 0;
+          if (xf)
+            ((float*)a.out)[o] = 0.0f;
+          else
+            a.out[o] = 0;
           if (a.gate_probe) a.gate_probe[o] = 0.0f;
           if (a.up_probe) a.up_probe[o] = 0.0f;
         }
@@ -142,8 +147,14 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
   for (int j = 0; j < kResXRegs; ++j) {
     const int q = tid + j * kResThreads;
-    xv[j] = q < nxc ? ((const uint4*)a.x)[q] : make_uint4(0, 0, 0, 0);
+    xv[j] = (!xf && q < nxc) ? ((const uint4*)a.x)[q] : make_uint4(0, 0, 0, 0);
   }
+  // chunk q (8 consecutive values) of f32 activations: two 16-byte loads
+  auto xf_chunk = [&](int q, uint4& lo4, uint4& hi4) {
+    const uint4* xp = (const uint4*)((const float*)a.x + 8 * (size_t)q);
+    lo4 = xp[0];
+    hi4 = xp[1];
+  };
 
   // ---- the current slot segment: tiles [t0, t1) of slot e ----
   int v = v0;
@@ -217,7 +228,7 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
 
   // digits per value and columns per token, fixed once x has been read
   int L = 6, W = 8;
-  auto etop = [&](int m) { return max((s_xmax[m] >> 7) & 0xFF, 1); };
+  auto etop = [&](int m) { return xf ? max((s_xmax[m] >> 23) & 0xFF, 1) : max((s_xmax[m] >> 7) & 0xFF, 1); };
   // digits of chunk w8 (8 consecutive K values) of pass token tl
   auto stage_unit4 = [&](int tl, int w8, const uint4 xq, int etop1) {
     const int st = w8 >> 4, gg = (w8 >> 2) & 3, i = w8 & 3;
@@ -257,6 +268,21 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
       put(tl * 8 + 7, 0u);
     }
   };
+  // eight digits of eight f32 activations: all eight columns of the token
+  auto stage_unitf = [&](int tl, int w8, const uint4 xa, const uint4 xb, int etop1) {
+    const int st = w8 >> 4, gg = (w8 >> 2) & 3, i = w8 & 3;
+    uint32_t d[2][8];
+    xf8_digits(xa, xb, etop1, d);
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      uint8_t* base = s_lds + st * sbytes + par * NT * 1024 + 4 * i;
+#pragma unroll
+      for (int sd = 0; sd < 8; ++sd) {
+        const int col = tl * 8 + sd;
+        *(uint32_t*)(base + (col >> 4) * 1024 + res_chunk(gg, col & 15, st) * 16) = d[par][sd];
+      }
+    }
+  };
   auto stage_unit = [&](int tl, int w8, const uint4 xq, int etop1) {
     if (W == 4)
       stage_unit4(tl, w8, xq, etop1);
@@ -272,7 +298,35 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
   // register j belong to one token: the eight wave reductions run
   // interleaved (six dependent shuffle rounds in all) and lane 0 posts them;
   // otherwise every lane posts its own values.
-  {
+  if (xf) {
+    // f32: a rolled loop over the chunks, wave reductions when a wave's
+    // chunks belong to one token
+#pragma unroll 1
+    for (int q = tid; q < (nxc + 63) / 64 * 64; q += kResThreads) {
+      uint32_t mx = 0, mn = 255;
+      if (q < nxc) {
+        uint4 xa, xb;
+        xf_chunk(q, xa, xb);
+        f32_range8(xa, xb, mx, mn);
+      }
+      if (hw % 64 == 0) {
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+          mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
+          mn = min(mn, (uint32_t)__shfl_xor((int)mn, off));
+        }
+        if (lane == 0 && q < nxc) {
+          const int m = q / hw;
+          if (mx) atomicMax(&s_xmax[m], (int)mx);
+          if (mn < 255) atomicMin(&s_xmin[m], (int)mn);
+        }
+      } else if (q < nxc) {
+        const int m = q / hw;
+        if (mx) atomicMax(&s_xmax[m], (int)mx);
+        if (mn < 255) atomicMin(&s_xmin[m], (int)mn);
+      }
+    }
+  } else {
     uint32_t mx[kResXRegs], mn[kResXRegs];
 #pragma unroll
     for (int j = 0; j < kResXRegs; ++j) {
@@ -318,7 +372,7 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
   {
     int l = 4;
     for (int m = 0; m < M; ++m) l = max(l, digits_for(s_xmax[m], s_xmin[m]));
-    L = __builtin_amdgcn_readfirstlane(l);
+    L = xf ? 8 : __builtin_amdgcn_readfirstlane(l);
   }
   W = L == 4 ? 4 : 8;
   const int tpp = 16 * NT / W;                              // tokens per pass
@@ -330,8 +384,16 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
     // once per work-group, so its straight-line code is fetched cold
     const int nq = ntok * hw;
     int q = tid;
-    uint4 xq = q < nq ? ((const uint4*)a.x)[q] : make_uint4(0, 0, 0, 0);
-    if (W == 4) {
+    uint4 xq = (!xf && q < nq) ? ((const uint4*)a.x)[q] : make_uint4(0, 0, 0, 0);
+    if (xf) {
+#pragma unroll 1
+      for (; q < nq; q += kResThreads) {
+        uint4 xa, xb;
+        xf_chunk(q, xa, xb);
+        const int m = q / hw;
+        stage_unitf(m, q - m * hw, xa, xb, etop(m));
+      }
+    } else if (W == 4) {
 #pragma unroll 1
       for (; q < nq; q += kResThreads) {
         const int qn = q + kResThreads;
@@ -352,8 +414,12 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
     }
     // zero digits for the padding steps
     const int padw = S * 16 - hw;
-    for (int u = tid; u < ntok * padw; u += kResThreads)
-      stage_unit(u % ntok, hw + u / ntok, make_uint4(0, 0, 0, 0), 1);
+    for (int u = tid; u < ntok * padw; u += kResThreads) {
+      if (xf)
+        stage_unitf(u % ntok, hw + u / ntok, make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), 1);
+      else
+        stage_unit(u % ntok, hw + u / ntok, make_uint4(0, 0, 0, 0), 1);
+    }
   }
   open_segment();
   start_ring();
@@ -589,37 +655,59 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
               e2off = 0;
             }
             const bool ok = lok[n] && row < I;
-            float gate = 0.0f, up = 0.0f;
+            float gate = 0.0f, up = 0.0f, ovf = 0.0f;
             uint16_t ov = 0;
             if (ok) {
               const int xm = lxm[n];
-              const int e2 = sum_exponent(xm) + e2off + weight_exp_shift<Q8>();
-              if (W == 4) {
-                gate = round_scaled53(gq[n], e2, gscr);
-                up = round_scaled53(uq[n], e2, uscr);
+              if (xf) {
+                // eight digits: quads [d0..d3] and [d4..d7], V = hi * 2^32 + lo
+                const int e2 = sum_exponent_f32((uint32_t)xm) + weight_exp_shift<Q8>();
+                gate = round_scaled_wide(ghi, glo, e2, gscr);
+                up = round_scaled_wide(uhi, ulo, e2, uscr);
+                if ((uint32_t)xm >= 0x7F800000u) {
+                  gate = __builtin_nanf("");
+                  up = __builtin_nanf("");
+                }
+                if constexpr (!DOWN) ovf = swiglu_tail_f32(gate, up);
               } else {
-                gate = round_scaled(ghi, glo, e2, gscr);
-                up = round_scaled(uhi, ulo, e2, uscr);
+                const int e2 = sum_exponent(xm) + e2off + weight_exp_shift<Q8>();
+                if (W == 4) {
+                  gate = round_scaled53(gq[n], e2, gscr);
+                  up = round_scaled53(uq[n], e2, uscr);
+                } else {
+                  gate = round_scaled(ghi, glo, e2, gscr);
+                  up = round_scaled(uhi, ulo, e2, uscr);
+                }
+                if (xm >= 0x7F80) {
+                  gate = __builtin_nanf("");
+                  up = __builtin_nanf("");
+                }
+                if constexpr (!DOWN) ov = swiglu_tail_tab(gate, up, s_sig);
               }
-              if (xm >= 0x7F80) {
-                gate = __builtin_nanf("");
-                up = __builtin_nanf("");
-              }
-              if constexpr (!DOWN) ov = swiglu_tail_tab(gate, up, s_sig);
             }
             // results of this (row, token) for routed pair `pair`
             auto store = [&](int pair) {
               const uint64_t o = (uint64_t)pair * I + row;
+              float* const outf = (float*)a.out;
               if constexpr (DOWN) {
-                // rows `row` and `row + 16`, each its own bf16 output
-                a.out[o] = bf16_rne(gate);
+                // rows `row` and `row + 16`, each its own output
+                if (xf)
+                  outf[o] = gate;
+                else
+                  a.out[o] = bf16_rne(gate);
                 if (a.gate_probe) a.gate_probe[o] = gate;
                 if (row + 16 < I) {
-                  a.out[o + 16] = bf16_rne(up);
+                  if (xf)
+                    outf[o + 16] = up;
+                  else
+                    a.out[o + 16] = bf16_rne(up);
                   if (a.gate_probe) a.gate_probe[o + 16] = up;
                 }
               } else {
-                a.out[o] = ov;
+                if (xf)
+                  outf[o] = ovf;
+                else
+                  a.out[o] = ov;
                 if (a.gate_probe) a.gate_probe[o] = gate;
                 if (a.up_probe) a.up_probe[o] = up;
               }
@@ -649,8 +737,14 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
       const int ntok = min(M, p0 + tpp) - p0;
       for (int u = tid; u < ntok * S * 16; u += kResThreads) {
         const int tl = u % ntok, w8 = u / ntok;
-        const uint4 xq = w8 < hw ? ((const uint4*)a.x)[(uint64_t)(p0 + tl) * hw + w8] : make_uint4(0, 0, 0, 0);
-        stage_unit(tl, w8, xq, etop(p0 + tl));
+        if (xf) {
+          uint4 xa = make_uint4(0, 0, 0, 0), xb = make_uint4(0, 0, 0, 0);
+          if (w8 < hw) xf_chunk((p0 + tl) * hw + w8, xa, xb);
+          stage_unitf(tl, w8, xa, xb, etop(p0 + tl));
+        } else {
+          const uint4 xq = w8 < hw ? ((const uint4*)a.x)[(uint64_t)(p0 + tl) * hw + w8] : make_uint4(0, 0, 0, 0);
+          stage_unit(tl, w8, xq, etop(p0 + tl));
+        }
       }
     }
     v = v0;
@@ -671,7 +765,7 @@ constexpr int kWaveShare2 = 547;
 
 // Work-groups that fit the device at once (one per CU: the LDS arrays take
 // most of a CU's 160 KiB).
-template <int NT, bool VEC, bool DOWN, bool Q8>
+template <int NT, bool VEC, bool DOWN, bool Q8, bool XF>
 int resident_blocks(int device) {
   static int cached[64] = {0};
   if (device < 0 || device >= 64) device = 0;
@@ -680,7 +774,7 @@ int resident_blocks(int device) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0)
       cus = 256;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&resident_kernel<NT, VEC, DOWN, Q8>), kResThreads, 0) != hipSuccess ||
+            &per_cu, reinterpret_cast<const void*>(&resident_kernel<NT, VEC, DOWN, Q8, XF>), kResThreads, 0) != hipSuccess ||
         per_cu <= 0)
       per_cu = 1;
     cached[device] = cus * per_cu;
@@ -688,25 +782,31 @@ int resident_blocks(int device) {
   return cached[device];
 }
 
-template <int NT, bool VEC, bool DOWN, bool Q8>
+template <int NT, bool VEC, bool DOWN, bool Q8, bool XF>
 hipError_t launch_resident_t(GateUpParams& p, hipStream_t stream) {
   int device = 0;
   if (hipGetDevice(&device) != hipSuccess) device = 0;
   const int rt = DOWN ? 32 : 16;
   const int tiles = p.num_slots * ((p.I + rt - 1) / rt);
-  int nb = resident_blocks<NT, VEC, DOWN, Q8>(device);
+  int nb = resident_blocks<NT, VEC, DOWN, Q8, XF>(device);
   if (nb > tiles) nb = tiles;
   void* args[] = {&p};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&resident_kernel<NT, VEC, DOWN, Q8>), dim3((unsigned)nb),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&resident_kernel<NT, VEC, DOWN, Q8, XF>), dim3((unsigned)nb),
                          dim3(kResThreads), args, 0, stream);
 }
 
-template <bool DOWN, bool Q8>
+template <bool DOWN, bool Q8, bool XF>
 hipError_t launch_resident_m(GateUpParams& p, hipStream_t stream) {
   const bool vec = row_bytes<Q8>(p.H) % 16 == 0;
   if (res_tiles(p.M) == 1)
-    return vec ? launch_resident_t<1, true, DOWN, Q8>(p, stream) : launch_resident_t<1, false, DOWN, Q8>(p, stream);
-  return vec ? launch_resident_t<2, true, DOWN, Q8>(p, stream) : launch_resident_t<2, false, DOWN, Q8>(p, stream);
+    return vec ? launch_resident_t<1, true, DOWN, Q8, XF>(p, stream) : launch_resident_t<1, false, DOWN, Q8, XF>(p, stream);
+  return vec ? launch_resident_t<2, true, DOWN, Q8, XF>(p, stream) : launch_resident_t<2, false, DOWN, Q8, XF>(p, stream);
+}
+
+template <bool XF>
+hipError_t launch_resident_x(GateUpParams& p, hipStream_t stream) {
+  if (p.q8) return p.down ? launch_resident_m<true, true, XF>(p, stream) : launch_resident_m<false, true, XF>(p, stream);
+  return p.down ? launch_resident_m<true, false, XF>(p, stream) : launch_resident_m<false, false, XF>(p, stream);
 }
 
 }  // namespace
@@ -724,8 +824,7 @@ hipError_t launch_resident(GateUpParams p, hipStream_t stream) {
   p.steps = res_steps(p.H, res_depth(res_tiles(p.M), p.q8 != 0));
   p.G = kResMaxPairs;
   p.wave_share = res_tiles(p.M) == 1 ? kWaveShare1 : kWaveShare2;
-  if (p.q8) return p.down ? launch_resident_m<true, true>(p, stream) : launch_resident_m<false, true>(p, stream);
-  return p.down ? launch_resident_m<true, false>(p, stream) : launch_resident_m<false, false>(p, stream);
+  return p.xf32 ? launch_resident_x<true>(p, stream) : launch_resident_x<false>(p, stream);
 }
 
 hipError_t launch_gate_up(const GateUpParams& p, int tokens_per_slot, hipStream_t stream) {

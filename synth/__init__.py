@@ -16,6 +16,8 @@ from .generators import (  # noqa: F401
     write_slot,
     bf16_normal,
     add_outliers,
+    f32_normal,
+    add_outliers_f32,
     top_k_routing,
     Config,
     CONFIGS,

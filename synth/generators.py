@@ -202,6 +202,22 @@ def bf16_normal(rng: np.random.Generator, shape) -> np.ndarray:
     return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
+def f32_normal(rng: np.random.Generator, shape) -> np.ndarray:
+    """N(0,1) float32 samples (f32 activations)."""
+    return rng.standard_normal(size=shape, dtype=np.float32)
+
+
+def add_outliers_f32(rng: np.random.Generator, x: np.ndarray, fraction: float) -> np.ndarray:
+    """Set ``round(fraction * x.size)`` distinct entries to +-1e4 (equal odds), f32."""
+    x = x.copy()
+    flat = x.reshape(-1)
+    n = int(round(fraction * flat.size))
+    pos = rng.choice(flat.size, n, replace=False)
+    signs = rng.integers(0, 2, size=n)
+    flat[pos] = np.where(signs == 1, -1e4, 1e4).astype(np.float32)
+    return x
+
+
 def add_outliers(rng: np.random.Generator, xbits: np.ndarray, fraction: float) -> np.ndarray:
     """Set ``round(fraction * x.size)`` distinct entries to +-9984 (equal odds)."""
     x = xbits.copy()

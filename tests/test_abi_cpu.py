@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 9, names
     for n in names:
         assert hasattr(lib, n), n
-    assert q4.abi_version() == 3
+    assert q4.abi_version() == 4
 
 
 def test_workspace_size_is_aligned_and_positive():
@@ -257,3 +257,19 @@ def test_q8_validation_sizes_weights_one_per_byte():
     assert st == q4.Q4_ERR_UNSUPPORTED
     with pytest.raises(ValueError):
         q4.validate_gate_up(SLOT, lay8, X, 1, 4096, 1536, OUT, fmt="q5")
+
+
+# ---- f32 activations (page 52: validateCall accepts float32 input) ----
+
+def test_f32_validation_and_output_alignment():
+    lay = synth.contiguous_layout(4096, 1536)
+    assert q4.validate_gate_up(SLOT, lay, X, 1, 4096, 1536, OUT, xdtype="f32") == 0
+    assert q4.validate_gate_up(SLOT, lay, X, 1, 4096, 1536, OUT + 2) == 0          # bf16 output: 2-byte aligned
+    st = q4.validate_gate_up(SLOT, lay, X, 1, 4096, 1536, OUT + 2, xdtype="f32")  # f32 output needs 4
+    assert st == q4.Q4_ERR_ALIGNMENT and "4-byte" in q4.last_error()
+    el = synth.expert_layout(4096, 1536)
+    assert q4.validate_down(SLOT, el, X, 1, 4096, 1536, OUT, xdtype="f32") == 0
+    assert q4.validate_down_grouped(SLOT, el.slot_bytes, 4, el, X, 2, IDS, 2, 4096, 1536, OUT, WS, 256,
+                                    fmt="q8" if False else "q4", xdtype="f32") == 0
+    with pytest.raises(ValueError):
+        q4.validate_gate_up(SLOT, lay, X, 1, 4096, 1536, OUT, xdtype="f16")
