@@ -124,11 +124,13 @@ def routed_step_config():
 class Pool:
     """``nslots`` device slots of one shape, filled round-robin from ``contents``."""
 
-    def __init__(self, lay, contents, x8, nslots: int = POOL_SLOTS, H_: int = H, I_: int = I):
+    def __init__(self, lay, contents, x8, nslots: int = POOL_SLOTS, H_: int = H, I_: int = I, fmt: str = "q4",
+                 xdtype: str = "bf16"):
         import torch
         from quantized_moe_expert_q4_amd.device import aligned_empty, upload_bf16_bits
         self.torch = torch
         self.lay = lay
+        self.fmt, self.xdtype = fmt, xdtype
         self.H, self.I, self.nslots = H_, I_, nslots
         self.stride = lay.slot_bytes
         self.slots = aligned_empty(nslots * self.stride)
@@ -137,11 +139,12 @@ class Pool:
             for s in range(d, nslots, contents.shape[0]):
                 self.slots[s * self.stride:(s + 1) * self.stride].copy_(dev)
             del dev
-        self.x8 = upload_bf16_bits(x8)
+        self.x8 = upload_bf16_bits(x8) if xdtype == "bf16" else torch.from_numpy(x8).cuda()
         torch.cuda.synchronize()
 
     def bytes_per_step(self) -> int:
-        return self.nslots * weight_bytes_per_slot(self.H, self.I)
+        per = weight_bytes_per_slot(self.H, self.I) if self.fmt == "q4" else 2 * self.H * self.I + 8 * self.I
+        return self.nslots * per
 
     def step_fn(self, M: int):
         """One grouped call routing each of M tokens to every slot."""
@@ -155,14 +158,15 @@ class Pool:
         from quantized_moe_expert_q4_amd.device import aligned_empty
         x = self.x8[:M].contiguous()
         K = ids.shape[1]
-        out = torch.empty((M, K, self.I), dtype=torch.bfloat16, device="cuda")
+        odt = torch.bfloat16 if self.xdtype == "bf16" else torch.float32
+        out = torch.empty((M, K, self.I), dtype=odt, device="cuda")
         wsb = q4.grouped_workspace_bytes(M, K, self.H, self.I, self.nslots)
         ws = aligned_empty(wsb, 256)
         stream = torch.cuda.current_stream()
 
         def step():
             q4.expert_gate_up_grouped(self.slots, self.stride, self.nslots, self.lay, x, M, ids, K, self.H, self.I,
-                                      out, ws, wsb, stream=stream)
+                                      out, ws, wsb, stream=stream, fmt=self.fmt, xdtype=self.xdtype)
         return step, stream
 
     def down_fn(self):
@@ -292,7 +296,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-shapes", action="store_true", help="skip the large-shape and routed-step legs")
     ap.add_argument("--only", choices=["m1", "m8", "single", "large_m1", "large_m8", "routed", "down", "forward",
-                                       "copy"], default=None,
+                                       "f32_m1", "q8_m1", "copy"], default=None,
                     help="run one leg only (for profiling); 'copy' times a plain 1 GiB device copy, "
                          "the reference for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE to bytes")
     args = ap.parse_args()
@@ -325,7 +329,7 @@ def main():
         legs = [args.only]
     else:
         legs = ["m1", "m8", "single"] + ([] if args.no_shapes else ["large_m1", "large_m8", "routed", "down",
-                                                                      "forward"])
+                                                                      "forward", "f32_m1", "q8_m1"])
     pool = Pool(lay, contents, x8) if any(l in ("m1", "m8", "single") for l in legs) else None
     for leg in [l for l in legs if l in ("m1", "m8", "single")]:
         if leg == "single":
@@ -406,6 +410,43 @@ def main():
                             f"launches per step",
                 "kernel": "q4::resident_kernel then q4::batch_kernel (down mode)"}
         del epool
+        torch.cuda.empty_cache()
+
+    if "f32_m1" in legs:
+        # the decode pool with f32 activations (f32 outputs)
+        rng = np.random.default_rng(SEED + 2000)
+        fpool = Pool(lay, contents, rng.standard_normal((8, H), dtype=np.float32), xdtype="f32")
+        step, stream = fpool.step_fn(1)
+        t, _ = time_steps(step, stream, args.steps, args.warmup)
+        sps = t / args.steps
+        v = bytes_step / sps / 1e9
+        shapes["f32_pool_m1"] = {
+            "value": round(v, 2), "unit": "GB/s", "pct_hbm_peak": round(100 * v / HBM_PEAK_GBS, 2),
+            "ms_per_step": round(sps * 1e3, 4), "rows_per_s": round(POOL_SLOTS * I / sps, 1),
+            "workload": f"f32 activations and outputs, H={H} I={I}, M=1, the {POOL_SLOTS}-slot cold pool, one "
+                        f"grouped launch per step", "kernel": "q4::resident_kernel (f32 x)"}
+        del fpool
+        torch.cuda.empty_cache()
+    if "q8_m1" in legs:
+        # a Q8 pool of the decode shape: int8 weights, 86 slots (1.08 GB)
+        import synth
+        qlay = synth.contiguous_layout(H, I, fmt="q8")
+        rng = np.random.default_rng(SEED + 3000)
+        qcontents = np.zeros((DISTINCT_CONTENTS, qlay.slot_bytes), np.uint8)
+        for d in range(DISTINCT_CONTENTS):
+            synth.fill_slot(rng, H, I, qlay, out=qcontents[d], fmt="q8")
+        qpool = Pool(qlay, qcontents, x8, 86, H, I, fmt="q8")
+        step, stream = qpool.step_fn(1)
+        t, _ = time_steps(step, stream, args.steps, args.warmup)
+        sps = t / args.steps
+        v = qpool.bytes_per_step() / sps / 1e9
+        shapes["q8_pool_m1"] = {
+            "value": round(v, 2), "unit": "GB/s", "pct_hbm_peak": round(100 * v / HBM_PEAK_GBS, 2),
+            "ms_per_step": round(sps * 1e3, 4), "rows_per_s": round(86 * I / sps, 1),
+            "workload": f"Q8 (int8) expert gate/up+SwiGLU, H={H} I={I}, M=1, 86-slot cold pool "
+                        f"({qpool.bytes_per_step() / 1e9:.3f} GB per step), one grouped launch per step",
+            "kernel": "q4::resident_kernel (int8 weights)"}
+        del qpool
         torch.cuda.empty_cache()
 
     out = {}
