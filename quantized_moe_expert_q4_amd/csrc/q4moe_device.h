@@ -261,6 +261,48 @@ __device__ __forceinline__ void load_step(StepW<Q8>& w, __amdgpu_buffer_rsrc_t r
 __device__ __forceinline__ void split_step(const StepW<false>& w, v4i& ev, v4i& od) { split_weights(w.a, ev, od); }
 __device__ __forceinline__ void split_step(const StepW<true>& w, v4i& ev, v4i& od) { split_bytes(w.a, w.b, ev, od); }
 
+// ---- wide K-steps of packed nibbles (256 weights per row and step) ----
+// A lane holds eight words (64 nibbles, K = base + 8w + p) of its k-group and
+// feeds four MFMAs per step, one per plane: plane 0 takes nibbles p = 0, 4 of
+// each word, plane 1 p = 2, 6, plane 2 p = 1, 5, plane 3 p = 3, 7; dword i of
+// a plane holds (word 2i, first p), (2i, second p), (2i+1, first), (2i+1,
+// second), each as the int8 16*(q-8).  Rows are then read 128 bytes per step.
+__device__ __forceinline__ void split_planes(const v4u a, const v4u b, v4i (&pl)[4]) {
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t lo[8], hi[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t t = w[k] ^ 0x88888888u;
+    lo[k] = (t << 4) & 0xF0F0F0F0u;   // low nibble of each byte (p even)
+    hi[k] = t & 0xF0F0F0F0u;          // high nibble of each byte (p odd)
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    pl[0][i] = (int)perm(lo[2 * i + 1], lo[2 * i], 0x06040200u);   // bytes 0, 2: p = 0, 4
+    pl[1][i] = (int)perm(lo[2 * i + 1], lo[2 * i], 0x07050301u);   // bytes 1, 3: p = 2, 6
+    pl[2][i] = (int)perm(hi[2 * i + 1], hi[2 * i], 0x06040200u);   // p = 1, 5
+    pl[3][i] = (int)perm(hi[2 * i + 1], hi[2 * i], 0x07050301u);   // p = 3, 7
+  }
+}
+
+// Plane dwords of one digit word pair: v0[p] / v1[p] hold four digits (bytes
+// 0..3) of position p of words 2i and 2i+1; d[j][s] receives digit s of
+// plane j's positions in the operand order of split_planes.
+__device__ __forceinline__ void plane_words4(const uint32_t (&v0)[8], const uint32_t (&v1)[8], uint32_t (&d)[4][4]) {
+  constexpr int pa[4] = {0, 2, 1, 3};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int a = pa[j], b = pa[j] + 4;
+    // [a0 b0 a1 b1] and [a2 b2 a3 b3] of each word, then digits across words
+    const uint32_t t01 = perm(v0[b], v0[a], 0x05010400u), t23 = perm(v0[b], v0[a], 0x07030602u);
+    const uint32_t u01 = perm(v1[b], v1[a], 0x05010400u), u23 = perm(v1[b], v1[a], 0x07030602u);
+    d[j][0] = perm(u01, t01, 0x05040100u);
+    d[j][1] = perm(u01, t01, 0x07060302u);
+    d[j][2] = perm(u23, t23, 0x05040100u);
+    d[j][3] = perm(u23, t23, 0x07060302u);
+  }
+}
+
 // Byte transpose of eight digit words: lo[p]/hi[p] hold digits 0..3 / 4..5 of
 // position p (p = 0..7 of one packed word); d[s] receives digit s of the four
 // positions of parity `par` (p = par, par+2, par+4, par+6), one byte each --

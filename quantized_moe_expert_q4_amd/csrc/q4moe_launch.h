@@ -31,7 +31,7 @@ struct GateUpParams {
 
 // Resident-digits kernel for token groups of at most two (decode widths):
 // true when the whole-K digits of `M_per_slot` tokens fit its LDS buffer.
-bool resident_fits(int M_per_slot, int H, bool q8);
+bool resident_fits(int M_per_slot, int H, bool q8, bool xf32);
 hipError_t launch_resident(GateUpParams p, hipStream_t stream);
 
 // Batch kernel for any width (digits staged per K-chunk).

@@ -38,7 +38,8 @@ namespace {
 constexpr int kResWaves = 8;
 constexpr int kResThreads = kResWaves * 64;
 // K-steps of weights in flight per wave (a multiple of 4).  Measured: 8 with
-// two column tiles spills ~30 VGPRs and streams 6% slower at eight tokens.
+// two column tiles spills ~30 VGPRs and streams 6% slower at eight tokens; 8
+// with one column tile (no spills) streams 3.5% slower at one token.
 __host__ __device__ constexpr int res_depth(int nt, bool q8) { return (void)nt, (void)q8, 4; }
 constexpr int kResLds = 150 * 1024;        // digits, then the fix-up slots
 constexpr int kResXRegs = 8;               // 16-byte chunks of x held per thread while splitting
@@ -47,17 +48,22 @@ constexpr int kResMaxPairs = 16;           // routed pairs finished per pass ove
 constexpr int kResFixSlots = kResWaves - 1;
 constexpr int kResIdRegs = 4;              // routing ids held per thread (2048 pairs)
 
-// One K-step of digits: [parity 2][column tile n][k-group g 4][16 x 16 bytes].
+// One K-step of digits: [parity 2][column tile n][k-group g 4][16 x 16 bytes]
+// ([plane 4][...] for wide steps).
 // The 16-byte chunk of column c sits at position c ^ (4g + step % 4) of its
 // k-group row, so that both the B-fragment reads (the sixteen lanes of one
 // k-group read sixteen distinct chunks) and the digit stores of one wave
 // (lanes spread over dwords, k-groups and four steps) hit distinct banks.
-__host__ __device__ constexpr int res_step_bytes(int nt) { return 2 * nt * 1024; }
+__host__ __device__ constexpr int res_step_bytes(int nt, int planes = 2) { return planes * nt * 1024; }
 __host__ __device__ constexpr int res_chunk(int g, int c, int step) { return g * 16 + (c ^ (4 * g + (step & 3))); }
 // One fix-up slot: int64 [tile][gate, up][lane] (quad sums).
 __host__ __device__ constexpr int res_fix_words(int nt) { return nt * 2 * 64; }
 // K-steps per tile, padded to whole rings.
-__host__ __device__ constexpr int res_steps(int H, int D) { return ((H + 127) / 128 + D - 1) / D * D; }
+__host__ __device__ constexpr int res_steps(int H, int D, int kps = 128) { return ((H + kps - 1) / kps + D - 1) / D * D; }
+// Wide K-steps (256 packed nibbles per row, four operand planes) for one
+// column tile of Q4 weights and bf16 activations: rows are read 128 bytes per
+// step (measured: the same bytes stream ~3-6% faster than 64 bytes per step).
+__host__ __device__ constexpr bool res_wide(int nt, bool q8, bool xf) { return nt == 1 && !q8 && !xf; }
 // Column tiles for a call of M tokens: one up to two tokens, else two.
 __host__ __device__ constexpr int res_tiles(int M) { return M <= 2 ? 1 : 2; }
 
@@ -82,6 +88,9 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
   __shared__ uint16_t s_sig[kSigTable];      // bf16 sigmoid of the tabulated gT
 
   constexpr int kResD = res_depth(NT, Q8);
+  constexpr bool WIDE = res_wide(NT, Q8, XF);
+  constexpr bool WL = Q8 || WIDE;            // 32 bytes per lane and step
+  constexpr int NPL = WIDE ? 4 : 2;          // operand planes per step
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -91,7 +100,7 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const bool grouped = a.ids != nullptr;
   constexpr bool xf = XF;
   const int S = a.steps;                     // K-steps per tile, a multiple of D
-  const int sbytes = res_step_bytes(NT);
+  const int sbytes = res_step_bytes(NT, NPL);
   const int hw = H / 8;                      // 16-byte chunks of one token's x
   constexpr int RT = DOWN ? 32 : 16;         // rows per tile
   const int tps = (I + RT - 1) / RT;         // tiles per slot
@@ -200,15 +209,15 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
 
   auto row_off = [&](int tile) {
     const int row = tile * RT + cc;
-    return (uint32_t)(row < I ? row : I - 1) * rbytes + (uint32_t)g4 * group_bytes<Q8>();
+    return (uint32_t)(row < I ? row : I - 1) * rbytes + (uint32_t)g4 * group_bytes<WL>();
   };
-  StepW<Q8> rg[kResD], ru[kResD];
+  StepW<WL> rg[kResD], ru[kResD];
   int lt = 0, ls = 0;                        // load cursor (tile, step)
   uint32_t loff = 0;
-  auto issue = [&](StepW<Q8>& g, StepW<Q8>& u_, bool live) {
-    const uint32_t o = live ? loff + (uint32_t)ls * step_row_bytes<Q8>() : kOffNone;
-    load_step<Q8, VEC>(g, gsrc, o);
-    load_step<Q8, VEC>(u_, usrc, o);
+  auto issue = [&](StepW<WL>& g, StepW<WL>& u_, bool live) {
+    const uint32_t o = live ? loff + (uint32_t)ls * step_row_bytes<WL>() : kOffNone;
+    load_step<WL, VEC>(g, gsrc, o);
+    load_step<WL, VEC>(u_, usrc, o);
     // cursor step without branches, so the loads stay unconditional
     const int nls = ls + (live ? 1 : 0);
     const bool wrap = nls == S;
@@ -288,6 +297,56 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
       stage_unit4(tl, w8, xq, etop1);
     else
       stage_unit8(tl, w8, xq, etop1);
+  };
+  // wide steps: digits of unit pair r (units 2r, 2r+1: words 2i, 2i+1 of k-group
+  // g of step st) of pass token tl, one dword per plane and digit column
+  auto stage_pair = [&](int tl, int r, const uint4 xa, const uint4 xb, int etop1) {
+    const int st = r >> 4, gg = (r >> 2) & 3, i = r & 3;
+    uint8_t* base = s_lds + st * sbytes + 4 * i;
+    auto put = [&](int j, int col, uint32_t v) {
+      *(uint32_t*)(base + (j * NT + (col >> 4)) * 1024 + res_chunk(gg, col & 15, st) * 16) = v;
+    };
+    const uint32_t xs[2][8] = {{xa.x & 0xFFFFu, xa.x >> 16, xa.y & 0xFFFFu, xa.y >> 16, xa.z & 0xFFFFu, xa.z >> 16,
+                                xa.w & 0xFFFFu, xa.w >> 16},
+                               {xb.x & 0xFFFFu, xb.x >> 16, xb.y & 0xFFFFu, xb.y >> 16, xb.z & 0xFFFFu, xb.z >> 16,
+                                xb.w & 0xFFFFu, xb.w >> 16}};
+    uint32_t v0[8], v1[8], d[4][4];
+    if (W == 4) {
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        v0[p] = x_digits4(xs[0][p], etop1);
+        v1[p] = x_digits4(xs[1][p], etop1);
+      }
+      plane_words4(v0, v1, d);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int sd = 0; sd < 4; ++sd) put(j, tl * 4 + sd, d[j][sd]);
+      return;
+    }
+    // six digits: columns [d0 d1 d2 0 d3 d4 d5 0]
+    uint32_t h0[8], h1[8], e[4][4];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const uint64_t z0 = x_digits(xs[0][p], etop1), z1 = x_digits(xs[1][p], etop1);
+      v0[p] = (uint32_t)z0;
+      h0[p] = (uint32_t)(z0 >> 32);
+      v1[p] = (uint32_t)z1;
+      h1[p] = (uint32_t)(z1 >> 32);
+    }
+    plane_words4(v0, v1, d);
+    plane_words4(h0, h1, e);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      put(j, tl * 8 + 0, d[j][0]);
+      put(j, tl * 8 + 1, d[j][1]);
+      put(j, tl * 8 + 2, d[j][2]);
+      put(j, tl * 8 + 3, 0u);
+      put(j, tl * 8 + 4, d[j][3]);
+      put(j, tl * 8 + 5, e[j][0]);
+      put(j, tl * 8 + 6, e[j][1]);
+      put(j, tl * 8 + 7, 0u);
+    }
   };
 
   // ---- the digits of the first pass, then the first segment's weights in flight ----
@@ -377,7 +436,20 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
   W = L == 4 ? 4 : 8;
   const int tpp = 16 * NT / W;                              // tokens per pass
   const int npass = (M + tpp - 1) / tpp;
-  {
+  if constexpr (WIDE) {
+    // wide steps: unit pairs (16 values, one dword of every plane and digit
+    // column) over the whole padded K range, so the padding gets zero digits
+    const int ntok = min(M, tpp);                           // == M: one column tile holds up to 4 (2) tokens
+    const int npair = S * 16;
+#pragma unroll 1
+    for (int u = tid; u < ntok * npair; u += kResThreads) {
+      const int m = u / npair, r = u - m * npair;
+      const int w8 = 2 * r;
+      const uint4 xa = w8 < hw ? ((const uint4*)a.x)[m * hw + w8] : make_uint4(0, 0, 0, 0);
+      const uint4 xb = w8 + 1 < hw ? ((const uint4*)a.x)[m * hw + w8 + 1] : make_uint4(0, 0, 0, 0);
+      stage_pair(m, r, xa, xb, etop(m));
+    }
+  } else {
     const int ntok = min(M, tpp);
     // a rolled loop that reads x again (cache hits: no weight load is in
     // flight yet), the next chunk's load in flight: the launch's setup runs
@@ -563,25 +635,29 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
         for (; u < pe; u += kResD) {
 #pragma unroll
           for (int d = 0; d < kResD; ++d) {
-            v4i ge, go, ue, uo;
-            split_step(rg[d], ge, go);
-            split_step(ru[d], ue, uo);
+            v4i pg[NPL], pu[NPL];
+            if constexpr (WIDE) {
+              split_planes(rg[d].a, rg[d].b, pg);
+              split_planes(ru[d].a, ru[d].b, pu);
+            } else {
+              split_step(rg[d], pg[0], pg[1]);
+              split_step(ru[d], pu[0], pu[1]);
+            }
             // the slot's registers are free once split: refill it before the multiply
             issue(rg[d], ru[d], u + d + kResD < ub);
             const uint8_t* bp = s_lds + (s + d) * sbytes + rdo[d & 3];
-            v4i be[NT], bo[NT];
+            v4i bq[NPL][NT];
 #pragma unroll
-            for (int n = 0; n < NT; ++n) {
-              be[n] = *(const v4i*)(bp + n * 1024);
-              bo[n] = *(const v4i*)(bp + (NT + n) * 1024);
-            }
+            for (int pl = 0; pl < NPL; ++pl)
 #pragma unroll
-            for (int n = 0; n < NT; ++n) {
-              accg[n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ge, be[n], accg[n], 0, 0, 0);
-              accu[n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ue, be[n], accu[n], 0, 0, 0);
-              accg[n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(go, bo[n], accg[n], 0, 0, 0);
-              accu[n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(uo, bo[n], accu[n], 0, 0, 0);
-            }
+              for (int n = 0; n < NT; ++n) bq[pl][n] = *(const v4i*)(bp + (pl * NT + n) * 1024);
+#pragma unroll
+            for (int pl = 0; pl < NPL; ++pl)
+#pragma unroll
+              for (int n = 0; n < NT; ++n) {
+                accg[n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pg[pl], bq[pl][n], accg[n], 0, 0, 0);
+                accu[n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pu[pl], bq[pl][n], accu[n], 0, 0, 0);
+              }
           }
           s += kResD;
           // take the row scales over here, where the compiler counts the
@@ -730,7 +806,7 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
       start_ring();
       continue;
     }
-    if (++pass >= npass) break;
+    if (++pass >= npass) break;                           // wide steps: always one pass (M <= 2)
     __syncthreads();  // every wave is done with the previous pass's digits
     {
       const int p0 = pass * tpp;
@@ -811,29 +887,32 @@ hipError_t launch_resident_x(GateUpParams& p, hipStream_t stream) {
 
 }  // namespace
 
-bool resident_fits(int M, int H, bool q8) {
+bool resident_fits(int M, int H, bool q8, bool xf) {
   if (M < 1 || M > kResMaxTokens) return false;
   const int nt = res_tiles(M);
+  const bool wide = res_wide(nt, q8, xf);
   return (int64_t)M * (H / 8) <= (int64_t)kResXRegs * kResThreads &&
-         (int64_t)res_steps(H, res_depth(nt, q8)) * res_step_bytes(nt) +
+         (int64_t)res_steps(H, res_depth(nt, q8), wide ? 256 : 128) * res_step_bytes(nt, wide ? 4 : 2) +
                  (int64_t)kResFixSlots * res_fix_words(nt) * 8 <=
              (int64_t)kResLds;
 }
 
 hipError_t launch_resident(GateUpParams p, hipStream_t stream) {
-  p.steps = res_steps(p.H, res_depth(res_tiles(p.M), p.q8 != 0));
+  const int nt = res_tiles(p.M);
+  p.steps = res_steps(p.H, res_depth(nt, p.q8 != 0), res_wide(nt, p.q8 != 0, p.xf32 != 0) ? 256 : 128);
   p.G = kResMaxPairs;
   p.wave_share = res_tiles(p.M) == 1 ? kWaveShare1 : kWaveShare2;
   return p.xf32 ? launch_resident_x<true>(p, stream) : launch_resident_x<false>(p, stream);
 }
 
 hipError_t launch_gate_up(const GateUpParams& p, int tokens_per_slot, hipStream_t stream) {
-  return resident_fits(tokens_per_slot, p.H, p.q8 != 0) ? launch_resident(p, stream)
+  return resident_fits(tokens_per_slot, p.H, p.q8 != 0, p.xf32 != 0) ? launch_resident(p, stream)
                                                          : launch_batch(p, tokens_per_slot, stream);
 }
 
 hipError_t launch_down(const GateUpParams& p, int pairs_per_slot, hipStream_t stream) {
-  return resident_fits(p.M, p.H, p.q8 != 0) ? launch_resident(p, stream) : launch_batch(p, pairs_per_slot, stream);
+  return resident_fits(p.M, p.H, p.q8 != 0, p.xf32 != 0) ? launch_resident(p, stream)
+                                                          : launch_batch(p, pairs_per_slot, stream);
 }
 
 }  // namespace q4
