@@ -63,7 +63,7 @@ __host__ __device__ constexpr int res_steps(int H, int D, int kps = 128) { retur
 // Wide K-steps (256 packed nibbles per row, four operand planes) for one
 // column tile of Q4 weights and bf16 activations: rows are read 128 bytes per
 // step (measured: the same bytes stream ~3-6% faster than 64 bytes per step).
-__host__ __device__ constexpr bool res_wide(int nt, bool q8, bool xf) { return nt == 1 && !q8 && !xf; }
+__host__ __device__ constexpr bool res_wide(int nt, bool q8, bool xf) { return (void)nt, !q8 && !xf; }
 // Column tiles for a call of M tokens: one up to two tokens, else two.
 __host__ __device__ constexpr int res_tiles(int M) { return M <= 2 ? 1 : 2; }
 
@@ -439,7 +439,7 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
   if constexpr (WIDE) {
     // wide steps: unit pairs (16 values, one dword of every plane and digit
     // column) over the whole padded K range, so the padding gets zero digits
-    const int ntok = min(M, tpp);                           // == M: one column tile holds up to 4 (2) tokens
+    const int ntok = min(M, tpp);
     const int npair = S * 16;
 #pragma unroll 1
     for (int u = tid; u < ntok * npair; u += kResThreads) {
@@ -806,9 +806,22 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
       start_ring();
       continue;
     }
-    if (++pass >= npass) break;                           // wide steps: always one pass (M <= 2)
+    if (++pass >= npass) break;
     __syncthreads();  // every wave is done with the previous pass's digits
-    {
+    if constexpr (WIDE) {
+      const int p0 = pass * tpp;
+      const int ntok = min(M, p0 + tpp) - p0;
+      const int npair = S * 16;
+#pragma unroll 1
+      for (int u = tid; u < ntok * npair; u += kResThreads) {
+        const int tl = u / npair, r = u - tl * npair;
+        const int w8 = 2 * r;
+        const uint64_t xr = (uint64_t)(p0 + tl) * hw;
+        const uint4 xa = w8 < hw ? ((const uint4*)a.x)[xr + w8] : make_uint4(0, 0, 0, 0);
+        const uint4 xb = w8 + 1 < hw ? ((const uint4*)a.x)[xr + w8 + 1] : make_uint4(0, 0, 0, 0);
+        stage_pair(tl, r, xa, xb, etop(p0 + tl));
+      }
+    } else {
       const int p0 = pass * tpp;
       const int ntok = min(M, p0 + tpp) - p0;
       for (int u = tid; u < ntok * S * 16; u += kResThreads) {
