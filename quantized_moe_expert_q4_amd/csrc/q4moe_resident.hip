@@ -441,13 +441,28 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
     // column) over the whole padded K range, so the padding gets zero digits
     const int ntok = min(M, tpp);
     const int npair = S * 16;
+    // up to four pairs per thread and pass of this loop, their loads issued
+    // together (one round trip instead of four)
+    constexpr int kPairs = 4;
 #pragma unroll 1
-    for (int u = tid; u < ntok * npair; u += kResThreads) {
-      const int m = u / npair, r = u - m * npair;
-      const int w8 = 2 * r;
-      const uint4 xa = w8 < hw ? ((const uint4*)a.x)[m * hw + w8] : make_uint4(0, 0, 0, 0);
-      const uint4 xb = w8 + 1 < hw ? ((const uint4*)a.x)[m * hw + w8 + 1] : make_uint4(0, 0, 0, 0);
-      stage_pair(m, r, xa, xb, etop(m));
+    for (int u0 = tid; u0 < ntok * npair; u0 += kPairs * kResThreads) {
+      uint4 xa[kPairs], xb[kPairs];
+#pragma unroll
+      for (int k = 0; k < kPairs; ++k) {
+        const int u = u0 + k * kResThreads;
+        const int m = u / npair, w8 = 2 * (u - m * npair);
+        const bool live = u < ntok * npair;
+        xa[k] = (live && w8 < hw) ? ((const uint4*)a.x)[m * hw + w8] : make_uint4(0, 0, 0, 0);
+        xb[k] = (live && w8 + 1 < hw) ? ((const uint4*)a.x)[m * hw + w8 + 1] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int k = 0; k < kPairs; ++k) {
+        const int u = u0 + k * kResThreads;
+        if (u < ntok * npair) {
+          const int m = u / npair;
+          stage_pair(m, u - m * npair, xa[k], xb[k], etop(m));
+        }
+      }
     }
   } else {
     const int ntok = min(M, tpp);
