@@ -269,19 +269,16 @@ __device__ __forceinline__ void split_step(const StepW<true>& w, v4i& ev, v4i& o
 // second), each as the int8 16*(q-8).  Rows are then read 128 bytes per step.
 __device__ __forceinline__ void split_planes(const v4u a, const v4u b, v4i (&pl)[4]) {
   const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  uint32_t lo[8], hi[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const uint32_t t = w[k] ^ 0x88888888u;
-    lo[k] = (t << 4) & 0xF0F0F0F0u;   // low nibble of each byte (p even)
-    hi[k] = t & 0xF0F0F0F0u;          // high nibble of each byte (p odd)
-  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    pl[0][i] = (int)perm(lo[2 * i + 1], lo[2 * i], 0x06040200u);   // bytes 0, 2: p = 0, 4
-    pl[1][i] = (int)perm(lo[2 * i + 1], lo[2 * i], 0x07050301u);   // bytes 1, 3: p = 2, 6
-    pl[2][i] = (int)perm(hi[2 * i + 1], hi[2 * i], 0x06040200u);   // p = 1, 5
-    pl[3][i] = (int)perm(hi[2 * i + 1], hi[2 * i], 0x07050301u);   // p = 3, 7
+    // bytes 0, 2 (nibbles p = 0, 1, 4, 5) and bytes 1, 3 (p = 2, 3, 6, 7) of words 2i, 2i+1
+    // (the zero-point xor is folded into each mask: one 3-input op per plane)
+    const uint32_t e = perm(w[2 * i + 1], w[2 * i], 0x06040200u);
+    const uint32_t o = perm(w[2 * i + 1], w[2 * i], 0x07050301u);
+    pl[0][i] = (int)(((e << 4) ^ 0x88888880u) & 0xF0F0F0F0u);   // p = 0, 4
+    pl[2][i] = (int)((e ^ 0x88888888u) & 0xF0F0F0F0u);          // p = 1, 5
+    pl[1][i] = (int)(((o << 4) ^ 0x88888880u) & 0xF0F0F0F0u);   // p = 2, 6
+    pl[3][i] = (int)((o ^ 0x88888888u) & 0xF0F0F0F0u);          // p = 3, 7
   }
 }
 
