@@ -339,12 +339,11 @@ __device__ __forceinline__ void x8_digits(const uint4 v, int etop1, uint32_t (&l
 // whose digits 4 and 5 are then zero.  Zero values give zero digits for any
 // shift; non-zero values have a shift in [0, 22].
 __device__ __forceinline__ uint32_t x_digits4(uint32_t b, int etop1) {
-  const uint32_t E = (b >> 7) & 0xFFu;
-  const uint32_t mag = (b & 0x7Fu) | (E ? 0x80u : 0u);
-  const int sh = (int)(E ? E : 1u) - etop1 + (kFracBits - 16);
-  uint32_t X = mag << (sh & 31);
-  X = (b & 0x8000u) ? 0u - X : X;
-  return (X + 0x80808080u) ^ 0x80808080u;
+  // X = x * 2^(156 - etop1): x = mag * 2^(max(E,1) - 134), so X = mag * 2^(max(E,1)
+  // - etop1 + 22), an integer of at most 30 bits for the values this split
+  // is used for; ldexp and the conversion are exact and carry the sign.
+  const int X = (int)__builtin_ldexpf(__uint_as_float(b << 16), 156 - etop1);
+  return ((uint32_t)X + 0x80808080u) ^ 0x80808080u;
 }
 
 // Four-digit words of eight packed bf16 activations: d[par][s] holds digit s
