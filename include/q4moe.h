@@ -346,34 +346,136 @@ int q8_validate_down_grouped(const void *slots_base, uint64_t slot_stride,
  * values at most 38 binades below the token's largest |x| (smaller entries
  * are rounded to that grid) and rounded once to F32 with the row scale.
  */
-int q4_expert_gate_up_f32(const void *slot, const q4_slot_layout *layout, const void *x_f32, int64_t M, int64_t H, int64_t I, void *out_f32, q4_stream_t stream);
-int q4_expert_gate_up_probe_f32(const void *slot, const q4_slot_layout *layout, const void *x_f32, int64_t M, int64_t H, int64_t I, void *out_f32, float *gate_f32, float *up_f32, q4_stream_t stream);
-int q4_expert_gate_up_grouped_f32(const void *slots_base, uint64_t slot_stride, int64_t num_slots, const q4_slot_layout *layout, const void *x_f32, int64_t M, const int32_t *slot_ids, int64_t K, int64_t H, int64_t I, void *out_f32, void *workspace, size_t workspace_bytes, q4_stream_t stream);
-int q4_expert_gate_up_grouped_probe_f32(const void *slots_base, uint64_t slot_stride, int64_t num_slots, const q4_slot_layout *layout, const void *x_f32, int64_t M, const int32_t *slot_ids, int64_t K, int64_t H, int64_t I, void *out_f32, float *gate_f32, float *up_f32, void *workspace, size_t workspace_bytes, q4_stream_t stream);
-int q4_validate_gate_up_f32(const void *slot, const q4_slot_layout *layout, const void *x_f32, int64_t M, int64_t H, int64_t I, const void *out_f32);
-int q4_validate_grouped_f32(const void *slots_base, uint64_t slot_stride, int64_t num_slots, const q4_slot_layout *layout, const void *x_f32, int64_t M, const int32_t *slot_ids, int64_t K, int64_t H, int64_t I, const void *out_f32, const void *workspace, size_t workspace_bytes);
-int q4_expert_down_f32(const void *slot, const q4_slot_layout *layout, const void *mid_f32, int64_t M, int64_t H, int64_t I, void *out_f32, q4_stream_t stream);
-int q4_expert_down_probe_f32(const void *slot, const q4_slot_layout *layout, const void *mid_f32, int64_t M, int64_t H, int64_t I, void *out_f32, float *down_f32, q4_stream_t stream);
-int q4_expert_down_grouped_f32(const void *slots_base, uint64_t slot_stride, int64_t num_slots, const q4_slot_layout *layout, const void *mid_f32, int64_t M, const int32_t *slot_ids, int64_t K, int64_t H, int64_t I, void *out_f32, void *workspace, size_t workspace_bytes, q4_stream_t stream);
-int q4_expert_down_grouped_probe_f32(const void *slots_base, uint64_t slot_stride, int64_t num_slots, const q4_slot_layout *layout, const void *mid_f32, int64_t M, const int32_t *slot_ids, int64_t K, int64_t H, int64_t I, void *out_f32, float *down_f32, void *workspace, size_t workspace_bytes, q4_stream_t stream);
-int q4_expert_forward_f32(const void *slot, const q4_slot_layout *layout, const void *x_f32, int64_t M, int64_t H, int64_t I, void *mid_f32, void *out_f32, q4_stream_t stream);
-int q4_expert_forward_grouped_f32(const void *slots_base, uint64_t slot_stride, int64_t num_slots, const q4_slot_layout *layout, const void *x_f32, int64_t M, const int32_t *slot_ids, int64_t K, int64_t H, int64_t I, void *mid_f32, void *out_f32, void *workspace, size_t workspace_bytes, q4_stream_t stream);
-int q4_validate_down_f32(const void *slot, const q4_slot_layout *layout, const void *mid_f32, int64_t M, int64_t H, int64_t I, const void *out_f32);
-int q4_validate_down_grouped_f32(const void *slots_base, uint64_t slot_stride, int64_t num_slots, const q4_slot_layout *layout, const void *mid_f32, int64_t M, const int32_t *slot_ids, int64_t K, int64_t H, int64_t I, const void *out_f32, const void *workspace, size_t workspace_bytes);
-int q8_expert_gate_up_f32(const void *slot, const q4_slot_layout *layout, const void *x_f32, int64_t M, int64_t H, int64_t I, void *out_f32, q4_stream_t stream);
-int q8_expert_gate_up_probe_f32(const void *slot, const q4_slot_layout *layout, const void *x_f32, int64_t M, int64_t H, int64_t I, void *out_f32, float *gate_f32, float *up_f32, q4_stream_t stream);
-int q8_expert_gate_up_grouped_f32(const void *slots_base, uint64_t slot_stride, int64_t num_slots, const q4_slot_layout *layout, const void *x_f32, int64_t M, const int32_t *slot_ids, int64_t K, int64_t H, int64_t I, void *out_f32, void *workspace, size_t workspace_bytes, q4_stream_t stream);
-int q8_expert_gate_up_grouped_probe_f32(const void *slots_base, uint64_t slot_stride, int64_t num_slots, const q4_slot_layout *layout, const void *x_f32, int64_t M, const int32_t *slot_ids, int64_t K, int64_t H, int64_t I, void *out_f32, float *gate_f32, float *up_f32, void *workspace, size_t workspace_bytes, q4_stream_t stream);
-int q8_validate_gate_up_f32(const void *slot, const q4_slot_layout *layout, const void *x_f32, int64_t M, int64_t H, int64_t I, const void *out_f32);
-int q8_validate_grouped_f32(const void *slots_base, uint64_t slot_stride, int64_t num_slots, const q4_slot_layout *layout, const void *x_f32, int64_t M, const int32_t *slot_ids, int64_t K, int64_t H, int64_t I, const void *out_f32, const void *workspace, size_t workspace_bytes);
-int q8_expert_down_f32(const void *slot, const q4_slot_layout *layout, const void *mid_f32, int64_t M, int64_t H, int64_t I, void *out_f32, q4_stream_t stream);
-int q8_expert_down_probe_f32(const void *slot, const q4_slot_layout *layout, const void *mid_f32, int64_t M, int64_t H, int64_t I, void *out_f32, float *down_f32, q4_stream_t stream);
-int q8_expert_down_grouped_f32(const void *slots_base, uint64_t slot_stride, int64_t num_slots, const q4_slot_layout *layout, const void *mid_f32, int64_t M, const int32_t *slot_ids, int64_t K, int64_t H, int64_t I, void *out_f32, void *workspace, size_t workspace_bytes, q4_stream_t stream);
-int q8_expert_down_grouped_probe_f32(const void *slots_base, uint64_t slot_stride, int64_t num_slots, const q4_slot_layout *layout, const void *mid_f32, int64_t M, const int32_t *slot_ids, int64_t K, int64_t H, int64_t I, void *out_f32, float *down_f32, void *workspace, size_t workspace_bytes, q4_stream_t stream);
-int q8_expert_forward_f32(const void *slot, const q4_slot_layout *layout, const void *x_f32, int64_t M, int64_t H, int64_t I, void *mid_f32, void *out_f32, q4_stream_t stream);
-int q8_expert_forward_grouped_f32(const void *slots_base, uint64_t slot_stride, int64_t num_slots, const q4_slot_layout *layout, const void *x_f32, int64_t M, const int32_t *slot_ids, int64_t K, int64_t H, int64_t I, void *mid_f32, void *out_f32, void *workspace, size_t workspace_bytes, q4_stream_t stream);
-int q8_validate_down_f32(const void *slot, const q4_slot_layout *layout, const void *mid_f32, int64_t M, int64_t H, int64_t I, const void *out_f32);
-int q8_validate_down_grouped_f32(const void *slots_base, uint64_t slot_stride, int64_t num_slots, const q4_slot_layout *layout, const void *mid_f32, int64_t M, const int32_t *slot_ids, int64_t K, int64_t H, int64_t I, const void *out_f32, const void *workspace, size_t workspace_bytes);
+int q4_expert_gate_up_f32(const void *slot, const q4_slot_layout *layout,
+                          const void *x_f32, int64_t M, int64_t H, int64_t I,
+                          void *out_f32, q4_stream_t stream);
+int q4_expert_gate_up_probe_f32(const void *slot, const q4_slot_layout *layout,
+                                const void *x_f32, int64_t M, int64_t H, int64_t I,
+                                void *out_f32, float *gate_f32, float *up_f32,
+                                q4_stream_t stream);
+int q4_expert_gate_up_grouped_f32(const void *slots_base, uint64_t slot_stride,
+                                  int64_t num_slots, const q4_slot_layout *layout,
+                                  const void *x_f32, int64_t M, const int32_t *slot_ids,
+                                  int64_t K, int64_t H, int64_t I, void *out_f32,
+                                  void *workspace, size_t workspace_bytes,
+                                  q4_stream_t stream);
+int q4_expert_gate_up_grouped_probe_f32(const void *slots_base, uint64_t slot_stride,
+                                        int64_t num_slots, const q4_slot_layout *layout,
+                                        const void *x_f32, int64_t M,
+                                        const int32_t *slot_ids, int64_t K, int64_t H,
+                                        int64_t I, void *out_f32, float *gate_f32,
+                                        float *up_f32, void *workspace,
+                                        size_t workspace_bytes, q4_stream_t stream);
+int q4_validate_gate_up_f32(const void *slot, const q4_slot_layout *layout,
+                            const void *x_f32, int64_t M, int64_t H, int64_t I,
+                            const void *out_f32);
+int q4_validate_grouped_f32(const void *slots_base, uint64_t slot_stride,
+                            int64_t num_slots, const q4_slot_layout *layout,
+                            const void *x_f32, int64_t M, const int32_t *slot_ids,
+                            int64_t K, int64_t H, int64_t I, const void *out_f32,
+                            const void *workspace, size_t workspace_bytes);
+int q4_expert_down_f32(const void *slot, const q4_slot_layout *layout,
+                       const void *mid_f32, int64_t M, int64_t H, int64_t I,
+                       void *out_f32, q4_stream_t stream);
+int q4_expert_down_probe_f32(const void *slot, const q4_slot_layout *layout,
+                             const void *mid_f32, int64_t M, int64_t H, int64_t I,
+                             void *out_f32, float *down_f32, q4_stream_t stream);
+int q4_expert_down_grouped_f32(const void *slots_base, uint64_t slot_stride,
+                               int64_t num_slots, const q4_slot_layout *layout,
+                               const void *mid_f32, int64_t M, const int32_t *slot_ids,
+                               int64_t K, int64_t H, int64_t I, void *out_f32,
+                               void *workspace, size_t workspace_bytes,
+                               q4_stream_t stream);
+int q4_expert_down_grouped_probe_f32(const void *slots_base, uint64_t slot_stride,
+                                     int64_t num_slots, const q4_slot_layout *layout,
+                                     const void *mid_f32, int64_t M,
+                                     const int32_t *slot_ids, int64_t K, int64_t H,
+                                     int64_t I, void *out_f32, float *down_f32,
+                                     void *workspace, size_t workspace_bytes,
+                                     q4_stream_t stream);
+int q4_expert_forward_f32(const void *slot, const q4_slot_layout *layout,
+                          const void *x_f32, int64_t M, int64_t H, int64_t I,
+                          void *mid_f32, void *out_f32, q4_stream_t stream);
+int q4_expert_forward_grouped_f32(const void *slots_base, uint64_t slot_stride,
+                                  int64_t num_slots, const q4_slot_layout *layout,
+                                  const void *x_f32, int64_t M, const int32_t *slot_ids,
+                                  int64_t K, int64_t H, int64_t I, void *mid_f32,
+                                  void *out_f32, void *workspace,
+                                  size_t workspace_bytes, q4_stream_t stream);
+int q4_validate_down_f32(const void *slot, const q4_slot_layout *layout,
+                         const void *mid_f32, int64_t M, int64_t H, int64_t I,
+                         const void *out_f32);
+int q4_validate_down_grouped_f32(const void *slots_base, uint64_t slot_stride,
+                                 int64_t num_slots, const q4_slot_layout *layout,
+                                 const void *mid_f32, int64_t M,
+                                 const int32_t *slot_ids, int64_t K, int64_t H,
+                                 int64_t I, const void *out_f32, const void *workspace,
+                                 size_t workspace_bytes);
+int q8_expert_gate_up_f32(const void *slot, const q4_slot_layout *layout,
+                          const void *x_f32, int64_t M, int64_t H, int64_t I,
+                          void *out_f32, q4_stream_t stream);
+int q8_expert_gate_up_probe_f32(const void *slot, const q4_slot_layout *layout,
+                                const void *x_f32, int64_t M, int64_t H, int64_t I,
+                                void *out_f32, float *gate_f32, float *up_f32,
+                                q4_stream_t stream);
+int q8_expert_gate_up_grouped_f32(const void *slots_base, uint64_t slot_stride,
+                                  int64_t num_slots, const q4_slot_layout *layout,
+                                  const void *x_f32, int64_t M, const int32_t *slot_ids,
+                                  int64_t K, int64_t H, int64_t I, void *out_f32,
+                                  void *workspace, size_t workspace_bytes,
+                                  q4_stream_t stream);
+int q8_expert_gate_up_grouped_probe_f32(const void *slots_base, uint64_t slot_stride,
+                                        int64_t num_slots, const q4_slot_layout *layout,
+                                        const void *x_f32, int64_t M,
+                                        const int32_t *slot_ids, int64_t K, int64_t H,
+                                        int64_t I, void *out_f32, float *gate_f32,
+                                        float *up_f32, void *workspace,
+                                        size_t workspace_bytes, q4_stream_t stream);
+int q8_validate_gate_up_f32(const void *slot, const q4_slot_layout *layout,
+                            const void *x_f32, int64_t M, int64_t H, int64_t I,
+                            const void *out_f32);
+int q8_validate_grouped_f32(const void *slots_base, uint64_t slot_stride,
+                            int64_t num_slots, const q4_slot_layout *layout,
+                            const void *x_f32, int64_t M, const int32_t *slot_ids,
+                            int64_t K, int64_t H, int64_t I, const void *out_f32,
+                            const void *workspace, size_t workspace_bytes);
+int q8_expert_down_f32(const void *slot, const q4_slot_layout *layout,
+                       const void *mid_f32, int64_t M, int64_t H, int64_t I,
+                       void *out_f32, q4_stream_t stream);
+int q8_expert_down_probe_f32(const void *slot, const q4_slot_layout *layout,
+                             const void *mid_f32, int64_t M, int64_t H, int64_t I,
+                             void *out_f32, float *down_f32, q4_stream_t stream);
+int q8_expert_down_grouped_f32(const void *slots_base, uint64_t slot_stride,
+                               int64_t num_slots, const q4_slot_layout *layout,
+                               const void *mid_f32, int64_t M, const int32_t *slot_ids,
+                               int64_t K, int64_t H, int64_t I, void *out_f32,
+                               void *workspace, size_t workspace_bytes,
+                               q4_stream_t stream);
+int q8_expert_down_grouped_probe_f32(const void *slots_base, uint64_t slot_stride,
+                                     int64_t num_slots, const q4_slot_layout *layout,
+                                     const void *mid_f32, int64_t M,
+                                     const int32_t *slot_ids, int64_t K, int64_t H,
+                                     int64_t I, void *out_f32, float *down_f32,
+                                     void *workspace, size_t workspace_bytes,
+                                     q4_stream_t stream);
+int q8_expert_forward_f32(const void *slot, const q4_slot_layout *layout,
+                          const void *x_f32, int64_t M, int64_t H, int64_t I,
+                          void *mid_f32, void *out_f32, q4_stream_t stream);
+int q8_expert_forward_grouped_f32(const void *slots_base, uint64_t slot_stride,
+                                  int64_t num_slots, const q4_slot_layout *layout,
+                                  const void *x_f32, int64_t M, const int32_t *slot_ids,
+                                  int64_t K, int64_t H, int64_t I, void *mid_f32,
+                                  void *out_f32, void *workspace,
+                                  size_t workspace_bytes, q4_stream_t stream);
+int q8_validate_down_f32(const void *slot, const q4_slot_layout *layout,
+                         const void *mid_f32, int64_t M, int64_t H, int64_t I,
+                         const void *out_f32);
+int q8_validate_down_grouped_f32(const void *slots_base, uint64_t slot_stride,
+                                 int64_t num_slots, const q4_slot_layout *layout,
+                                 const void *mid_f32, int64_t M,
+                                 const int32_t *slot_ids, int64_t K, int64_t H,
+                                 int64_t I, const void *out_f32, const void *workspace,
+                                 size_t workspace_bytes);
 
 /* Message for the last failing call on this thread ("" after success). */
 const char *q4_last_error(void);

@@ -270,6 +270,6 @@ def test_f32_validation_and_output_alignment():
     el = synth.expert_layout(4096, 1536)
     assert q4.validate_down(SLOT, el, X, 1, 4096, 1536, OUT, xdtype="f32") == 0
     assert q4.validate_down_grouped(SLOT, el.slot_bytes, 4, el, X, 2, IDS, 2, 4096, 1536, OUT, WS, 256,
-                                    fmt="q8" if False else "q4", xdtype="f32") == 0
+                                    xdtype="f32") == 0
     with pytest.raises(ValueError):
         q4.validate_gate_up(SLOT, lay, X, 1, 4096, 1536, OUT, xdtype="f16")
