@@ -230,11 +230,8 @@ void batch_kernel(const GateUpParams a) {
           }
         }
         if (__shfl(ti, 0) == __shfl(ti, 63)) {
-#pragma unroll
-          for (int off = 32; off > 0; off >>= 1) {
-            mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
-            mn = min(mn, (uint32_t)__shfl_xor((int)mn, off));
-          }
+          mx = wave_extreme<true>(mx);
+          mn = wave_extreme<false>(mn);
           if (lane == 0 && mx) atomicMax(&s_xmax[ti], (int)mx);
           if (lane == 0 && mn < 255) atomicMin(&s_xmin[ti], (int)mn);
         } else {

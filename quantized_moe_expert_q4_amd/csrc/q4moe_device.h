@@ -166,6 +166,24 @@ __device__ __forceinline__ int64_t quad_xor(int64_t v) {
   return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
 
+// Largest (MAX) or smallest value of v over the 64 lanes of a wave, returned
+// wave-uniform; every lane must be active.  Two quad permutes and two row
+// rotations (DPP, no LDS round trip) leave each 16-lane row's extreme in all
+// of its lanes; lanes 0, 16, 32 and 48 then combine on the scalar unit.
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_extreme(uint32_t v) {
+  auto op = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));  // row_ror:4
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));  // row_ror:8
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return op(op(r0, r1), op(r2, r3));
+}
+
 // Orders one wave's LDS stores before its later LDS loads from other lanes
 // (and those loads before later stores): a wave barrier between release and
 // acquire fences, so the compiler keeps every LDS access on its side.
@@ -184,6 +202,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // only to keep the number of outstanding loads fixed use it, so that the
 // compiler's wait counts stay exact.
 constexpr uint32_t kOffNone = 0x80000000u;
+
+// s_waitcnt operand that waits for every vector memory load of the wave and
+// leaves the export and LDS/scalar counters alone (vmcnt 0, expcnt 7,
+// lgkmcnt 15).
+constexpr int kWaitVmem0 = 0x0F70;
 
 template <bool VEC>
 __device__ __forceinline__ v4u load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {

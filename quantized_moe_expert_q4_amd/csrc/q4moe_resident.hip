@@ -214,8 +214,8 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
   StepW<WL> rg[kResD], ru[kResD];
   int lt = 0, ls = 0;                        // load cursor (tile, step)
   uint32_t loff = 0;
-  auto issue = [&](StepW<WL>& g, StepW<WL>& u_, bool live) {
-    const uint32_t o = live ? loff + (uint32_t)ls * step_row_bytes<WL>() : kOffNone;
+  auto issue = [&](StepW<WL>& g, StepW<WL>& u_, bool live, uint32_t dep = 0u) {
+    const uint32_t o = (live ? loff + (uint32_t)ls * step_row_bytes<WL>() : kOffNone) + dep;
     load_step<WL, VEC>(g, gsrc, o);
     load_step<WL, VEC>(u_, usrc, o);
     // cursor step without branches, so the loads stay unconditional
@@ -354,9 +354,9 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
   // such as a rematerialised x chunk, would wait for the whole ring to arrive)
   // largest |x| and smallest non-zero exponent of each token.  When a token's
   // chunks fill whole waves (hw % 64 == 0), each wave's 64 chunks of x
-  // register j belong to one token: the eight wave reductions run
-  // interleaved (six dependent shuffle rounds in all) and lane 0 posts them;
-  // otherwise every lane posts its own values.
+  // register j belong to one token: the sixteen wave reductions (DPP, no
+  // branches, so the scheduler interleaves them) go to lane 0, which posts
+  // them; otherwise every lane posts its own values.
   if (xf) {
     // f32: a rolled loop over the chunks, wave reductions when a wave's
     // chunks belong to one token
@@ -369,11 +369,8 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
         f32_range8(xa, xb, mx, mn);
       }
       if (hw % 64 == 0) {
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-          mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
-          mn = min(mn, (uint32_t)__shfl_xor((int)mn, off));
-        }
+        mx = wave_extreme<true>(mx);
+        mn = wave_extreme<false>(mn);
         if (lane == 0 && q < nxc) {
           const int m = q / hw;
           if (mx) atomicMax(&s_xmax[m], (int)mx);
@@ -395,14 +392,9 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
     }
     if (hw % 64 == 0) {
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-#pragma unroll
-        for (int j = 0; j < kResXRegs; ++j) {
-          if (j * kResThreads < nxc) {
-            mx[j] = max(mx[j], (uint32_t)__shfl_xor((int)mx[j], off));
-            mn[j] = min(mn[j], (uint32_t)__shfl_xor((int)mn[j], off));
-          }
-        }
+      for (int j = 0; j < kResXRegs; ++j) {
+        mx[j] = wave_extreme<true>(mx[j]);
+        mn[j] = wave_extreme<false>(mn[j]);
       }
       if (lane == 0) {
 #pragma unroll
@@ -578,6 +570,11 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
             id = k == 0 ? idr[0] : k == 1 ? idr[1] : k == 2 ? idr[2] : idr[3];
           } else {
             id = p < P ? a.ids[p] : -1;
+            // This load completes after the ring issued before it in any
+            // case.  Waiting here, on this path alone, keeps the compiler
+            // from placing a wait for every load in flight (the whole ring)
+            // on the register path too, where the merged id is used.
+            __builtin_amdgcn_s_waitcnt(kWaitVmem0);
           }
           const bool m = id == e && p >= next_pair && p < pend;
           const uint64_t bal = __ballot(m);
@@ -658,8 +655,19 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
               split_step(rg[d], pg[0], pg[1]);
               split_step(ru[d], pu[0], pu[1]);
             }
-            // the slot's registers are free once split: refill it before the multiply
-            issue(rg[d], ru[d], u + d + kResD < ub);
+            // The slot's registers are free once split: refill it before the
+            // multiply.  The refill's offset passes through an empty asm that
+            // takes the split planes, so the loads are issued after the split
+            // has read the slot and can land in the slot's own registers.
+            // Otherwise the compiler issues them early into other registers
+            // and, at the loop's back edge, copies every slot back, waiting
+            // for all loads in flight each D steps.
+            uint32_t dep = 0u;
+            if constexpr (!XF) {
+#pragma unroll
+              for (int pl = 0; pl < NPL; ++pl) asm volatile("" : "+v"(dep) : "v"(pg[pl]), "v"(pu[pl]));
+            }
+            issue(rg[d], ru[d], u + d + kResD < ub, dep);
             const uint8_t* bp = s_lds + (s + d) * sbytes + rdo[d & 3];
             v4i bq[NPL][NT];
 #pragma unroll
