@@ -225,8 +225,7 @@ void batch_kernel(const GateUpParams a) {
             f32_range8(xp[0], xp[1], mx, mn);
           } else {
             const uint4 xq = *(const uint4*)(a.x + (uint64_t)(s_pairs[ti] / a.K) * H + 8 * w8);
-            mx = max_mag8(xq);
-            mn = min_exp8(xq);
+            range8(xq, mx, mn);
           }
         }
         if (__shfl(ti, 0) == __shfl(ti, 63)) {

@@ -552,30 +552,27 @@ __device__ float swiglu_tail_f32(float gate, float up) {
   return (gate * sg) * up;
 }
 
-// Largest bf16 magnitude bits among eight packed activations.
-__device__ __forceinline__ uint32_t max_mag8(const uint4 v) {
-  uint32_t m = max(max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu), max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu));
-  return max(m, max(max(v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu), max(v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu)));
+// Range of eight packed bf16 activations: the largest magnitude bits (0 if
+// all are zero) and the smallest exponent field, at least 1, among the
+// non-zero values (255 if none).  The field grows with the magnitude, so it
+// is the field of the smallest non-zero magnitude, found as the smallest
+// magnitude - 1 with zero wrapping to the top.
+__device__ __forceinline__ void range8(const uint4 v, uint32_t& mx, uint32_t& mn) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t hi = 0u, lo = 0xFFFFFFFFu;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t a0 = w[i] & 0x7FFFu, a1 = (w[i] >> 16) & 0x7FFFu;
+    hi = max(hi, max(a0, a1));
+    lo = min(lo, min(a0 - 1u, a1 - 1u));
+  }
+  mx = hi;
+  mn = lo == 0xFFFFFFFFu ? 255u : max((lo + 1u) >> 7, 1u);
 }
 
 // Exponent offset of the recombined sum: sum(w*x) = V * 2^(etop1 - 176)
 // (X = x * 2^(172 - etop1) and the 16x weight factor).
 __device__ __forceinline__ int sum_exponent(int xmax_bits) { return max((xmax_bits >> 7) & 0xFF, 1) - 176; }
-
-// Smallest exponent field (at least 1) among the non-zero values of 8 bf16, 255 if none.
-__device__ __forceinline__ uint32_t min_exp8(const uint4 v) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  uint32_t m = 255u;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t b = (w[i] >> (16 * h)) & 0xFFFFu;
-      if (b & 0x7FFFu) m = min(m, max((b >> 7) & 0xFFu, 1u));
-    }
-  }
-  return m;
-}
 
 // Digits per value for a token whose largest |x| has bits xmax and whose
 // smallest non-zero exponent field is emin: four when every value sits

@@ -383,38 +383,30 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
       }
     }
   } else {
-    uint32_t mx[kResXRegs], mn[kResXRegs];
+    // registers past the last chunk in every lane (j * threads >= nxc, the
+    // same for the whole work-group) are skipped; lanes past it hold zeros,
+    // whose range (0, 255) posts nothing
 #pragma unroll
     for (int j = 0; j < kResXRegs; ++j) {
-      const bool live = tid + j * kResThreads < nxc;
-      mx[j] = live ? max_mag8(xv[j]) : 0u;
-      mn[j] = live ? min_exp8(xv[j]) : 255u;
-    }
-    if (hw % 64 == 0) {
-#pragma unroll
-      for (int j = 0; j < kResXRegs; ++j) {
-        mx[j] = wave_extreme<true>(mx[j]);
-        mn[j] = wave_extreme<false>(mn[j]);
-      }
-      if (lane == 0) {
-#pragma unroll
-        for (int j = 0; j < kResXRegs; ++j) {
+      if (j * kResThreads < nxc) {
+        uint32_t mx, mn;
+        range8(xv[j], mx, mn);
+        if (hw % 64 == 0) {
+          mx = wave_extreme<true>(mx);
+          mn = wave_extreme<false>(mn);
           const int q0 = j * kResThreads + (tid & ~63);
-          if (q0 < nxc) {
+          if (lane == 0 && q0 < nxc) {
             const int m = q0 / hw;
-            if (mx[j]) atomicMax(&s_xmax[m], (int)mx[j]);
-            if (mn[j] < 255) atomicMin(&s_xmin[m], (int)mn[j]);
+            if (mx) atomicMax(&s_xmax[m], (int)mx);
+            if (mn < 255) atomicMin(&s_xmin[m], (int)mn);
           }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < kResXRegs; ++j) {
-        const int q = tid + j * kResThreads;
-        if (q < nxc) {
-          const int m = q / hw;
-          if (mx[j]) atomicMax(&s_xmax[m], (int)mx[j]);
-          if (mn[j] < 255) atomicMin(&s_xmin[m], (int)mn[j]);
+        } else {
+          const int q = tid + j * kResThreads;
+          if (q < nxc) {
+            const int m = q / hw;
+            if (mx) atomicMax(&s_xmax[m], (int)mx);
+            if (mn < 255) atomicMin(&s_xmin[m], (int)mn);
+          }
         }
       }
     }

@@ -207,6 +207,33 @@ def test_zero_token_and_all_eight_rows():
     check_parity(out, g, u, gr, ur, orf, "zero token / all-8 rows")
 
 
+@pytest.mark.parametrize("H,M", [(4096, 3), (1024, 6), (264, 2), (7168, 8)])
+def test_subnormal_and_sparse_tokens(H, M):
+    """Tokens of zeros, signed zeros, subnormals and lone values: the largest
+    magnitude and the smallest non-zero exponent each kernel derives per token
+    (its digit count and split exponent) must give the oracle's exact bits.
+    Shapes reach the resident kernel's wave and per-lane range paths and the
+    batch kernel."""
+    I = 48
+    rng = np.random.default_rng(H + 13 * M)
+    lay = synth.contiguous_layout(H, I)
+    slot = synth.fill_slot(rng, H, I, lay)
+    x = synth.bf16_normal(rng, (M, H))
+    x[0] = 0x8000                                      # negative zeros ...
+    x[0, 5] = 0x0001                                   # ... and one subnormal
+    mag = rng.integers(0, 0x80, H).astype(np.uint16)   # subnormal magnitudes and zeros
+    x[1] = mag | (rng.integers(0, 2, H).astype(np.uint16) << 15)
+    if M > 2:
+        x[2, rng.integers(0, H, 7)] = 0x0003           # a normal token with subnormals in it
+    if M > 3:
+        x[3] = 0
+        x[3, H - 1] = 0xC780                           # one value, -65536
+    say(f"[subnormal/sparse tokens] H={H} M={M}")
+    out, g, u = run_single(slot, lay, x, H, I)
+    gr, ur, orf = oracle.expert_gate_up(slot, lay, x, H, I)
+    check_parity(out, g, u, gr, ur, orf, f"subnormal/sparse tokens H={H} M={M}")
+
+
 def test_determinism_and_batch_invariance():
     c = synth.make_config("cfg3")
     say("[invariance] cfg3 twice, per-token M=1 calls, grouped with one slot")
