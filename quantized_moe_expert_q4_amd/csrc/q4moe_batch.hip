@@ -329,6 +329,11 @@ void batch_kernel(const GateUpParams a) {
             stage_unit(buf, ti, w8, xq);
           }
         }
+        // x was loaded after the weights in flight and is used up here, so
+        // none of them is pending any more: said explicitly, the compiler's
+        // wait counts at the head of the step loop stay exact (otherwise a
+        // register the x loads once held makes it wait for every load there)
+        __builtin_amdgcn_s_waitcnt(kWaitVmem0);
       };
 
       // columns past C in the last tile hold stale bytes; their results are never read
