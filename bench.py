@@ -160,7 +160,7 @@ class Pool:
         K = ids.shape[1]
         odt = torch.bfloat16 if self.xdtype == "bf16" else torch.float32
         out = torch.empty((M, K, self.I), dtype=odt, device="cuda")
-        wsb = q4.grouped_workspace_bytes(M, K, self.H, self.I, self.nslots)
+        wsb = q4.grouped_workspace_bytes(M, K, self.nslots)
         ws = aligned_empty(wsb, 256)
         stream = torch.cuda.current_stream()
 
@@ -181,7 +181,7 @@ class Pool:
         x = self.x8[:1].contiguous()
         mid = torch.empty((1, n, self.I), dtype=torch.bfloat16, device="cuda")
         out = torch.empty((1, n, self.H), dtype=torch.bfloat16, device="cuda")
-        wsb = q4.grouped_workspace_bytes(1, n, self.H, self.I, n)
+        wsb = q4.grouped_workspace_bytes(1, n, n)
         ws = aligned_empty(wsb, 256)
         stream = torch.cuda.current_stream()
         q4.expert_gate_up_grouped(self.slots, self.stride, n, self.lay, x, 1, ids, n, self.H, self.I, mid, ws, wsb,
@@ -202,7 +202,7 @@ class Pool:
         x = self.x8[:1].contiguous()
         mid = torch.empty((1, n, self.I), dtype=torch.bfloat16, device="cuda")
         out = torch.empty((1, n, self.H), dtype=torch.bfloat16, device="cuda")
-        wsb = q4.grouped_workspace_bytes(1, n, self.H, self.I, n)
+        wsb = q4.grouped_workspace_bytes(1, n, n)
         ws = aligned_empty(wsb, 256)
         stream = torch.cuda.current_stream()
 
@@ -224,6 +224,35 @@ class Pool:
             for s in range(POOL_SLOTS):
                 q4.expert_gate_up(ptr0 + s * self.stride, self.lay, x, 1, H, I, out, stream=stream)
         return step, stream
+
+
+STREAM_VARIANTS = [("tile_w8_d1", 0, 8, 1), ("tile_w8_d2", 0, 8, 2), ("tile_w8_d4", 0, 8, 4),
+                   ("linear_w8_d2", 1, 8, 2), ("tile_w16_d1", 0, 16, 1), ("tile_w16_d2", 0, 16, 2),
+                   ("tile_w16_d4", 0, 16, 4)]
+
+
+def stream_ceiling(pool, steps: int, warmup: int):
+    """Read-only streaming kernel over the pool's gate and up weights (no
+    arithmetic): the rate this access pattern reaches on this device."""
+    import torch
+    import quantized_moe_expert_q4_amd as q4
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    lay = pool.lay
+    nbytes = pool.nslots * 2 * pool.I * (pool.H // 2)
+    res = {}
+    for name, pattern, waves, depth in STREAM_VARIANTS:
+        def step():
+            q4.stream_read(pool.slots, pool.stride, pool.nslots, lay.gate_weight_offset, lay.up_weight_offset,
+                           pool.I, pool.H // 2, sink, pattern, waves, depth, stream=stream)
+        t, _ = time_steps(step, stream, steps, warmup)
+        res[name] = round(nbytes / (t / steps) / 1e9, 1)
+    best = max(res, key=res.get)
+    return {"best_GBps": res[best], "best_variant": best, "variants_GBps": res,
+            "bytes_per_launch": nbytes,
+            "kernel": "q4::stream_read_kernel: the pool's gate and up weights read once, no arithmetic "
+                      "(tile = the gate/up kernels' 16-row x 128-byte steps; linear = lane-linear 1 KiB runs; "
+                      "w = waves per CU, d = steps in flight per wave)"}
 
 
 def time_steps(step, stream, steps: int, warmup: int):
@@ -296,7 +325,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-shapes", action="store_true", help="skip the large-shape and routed-step legs")
     ap.add_argument("--only", choices=["m1", "m8", "single", "large_m1", "large_m8", "routed", "down", "forward",
-                                       "f32_m1", "q8_m1", "copy"], default=None,
+                                       "f32_m1", "q8_m1", "copy", "stream"], default=None,
                     help="run one leg only (for profiling); 'copy' times a plain 1 GiB device copy, "
                          "the reference for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE to bytes")
     args = ap.parse_args()
@@ -328,9 +357,10 @@ def main():
     if args.only:
         legs = [args.only]
     else:
-        legs = ["m1", "m8", "single"] + ([] if args.no_shapes else ["large_m1", "large_m8", "routed", "down",
+        legs = ["m1", "m8", "single", "stream"] + ([] if args.no_shapes else ["large_m1", "large_m8", "routed", "down",
                                                                       "forward", "f32_m1", "q8_m1"])
-    pool = Pool(lay, contents, x8) if any(l in ("m1", "m8", "single") for l in legs) else None
+    pool = Pool(lay, contents, x8) if any(l in ("m1", "m8", "single", "stream") for l in legs) else None
+    ceiling = stream_ceiling(pool, args.steps, args.warmup) if "stream" in legs else None
     for leg in [l for l in legs if l in ("m1", "m8", "single")]:
         if leg == "single":
             step, stream = pool.single_fn()
@@ -452,7 +482,7 @@ def main():
     out = {}
     if not any(l in res for l in ("m1", "m8")):
         # shape legs only (profiling runs)
-        print(json.dumps({"shapes": shapes}), flush=True)
+        print(json.dumps({"shapes": shapes, "stream_ceiling": ceiling}), flush=True)
         return
     primary = "m1" if "m1" in res else "m8"
     r = res[primary]
@@ -498,7 +528,8 @@ def main():
                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                        "traffic_detail": traffic_detail,
                        "kernel": kernel_label(M, H) + " (grouped call, M=%d)" % M,
-                       "algorithmic_bytes_per_launch": bytes_step}
+                       "algorithmic_bytes_per_launch": bytes_step,
+                       "stream_ceiling": ceiling}
     if shapes:
         out["shapes"] = shapes
     if not args.no_cpu:

@@ -111,11 +111,11 @@ int q4_expert_gate_up_probe(const void *slot, const q4_slot_layout *layout,
                             void *out_bf16, float *gate_f32, float *up_f32,
                             q4_stream_t stream);
 
-/* Bytes of device workspace the grouped call needs for these sizes (a
- * multiple of 256), or 0 for sizes outside the limits.  The workspace
- * receives the count of out-of-range ids; its size may grow with the sizes
- * in later versions, so callers should always ask. */
-size_t q4_grouped_workspace_bytes(int64_t M, int64_t K, int64_t H, int64_t I, int64_t num_slots);
+/* Bytes of device workspace a grouped call of M tokens with top-K routing over
+ * num_slots slots needs (a multiple of 256), or 0 for sizes outside the
+ * limits.  The workspace receives the count of out-of-range ids; its size may
+ * grow with these sizes in later versions, so callers should always ask. */
+size_t q4_grouped_workspace_bytes(int64_t M, int64_t K, int64_t num_slots);
 
 /*
  * Grouped call over routed expert slots.  Pair (t, j) runs token t against
@@ -126,7 +126,7 @@ size_t q4_grouped_workspace_bytes(int64_t M, int64_t K, int64_t H, int64_t I, in
  *   slot_ids  device int32 [M][K]; duplicates are allowed.  An id outside
  *             [0, num_slots) yields zero gate/up/out for that pair, and the
  *             number of such ids is stored as int32 at workspace[0].
- *   workspace device, >= q4_grouped_workspace_bytes(M, K, H, I, num_slots)
+ *   workspace device, >= q4_grouped_workspace_bytes(M, K, num_slots)
  *             bytes, 256-byte aligned; contents on entry are ignored.  Calls
  *             that share one workspace must not overlap in time.
  */
@@ -191,7 +191,7 @@ int q4_expert_down_probe(const void *slot, const q4_slot_layout *layout,
  * mid[t][j][:] (bf16 [M][K][I], the layout the grouped gate/up call writes)
  * against slot slot_ids[t*K + j] and writes out[t][j][:] (bf16 [M][K][H]).
  * Slots, ids and workspace as for q4_expert_gate_up_grouped (workspace size
- * from q4_grouped_workspace_bytes(M, K, H, I, num_slots)); an id outside
+ * from q4_grouped_workspace_bytes(M, K, num_slots)); an id outside
  * [0, num_slots) gives a zero output row and is counted in workspace[0].
  * Needs M*K <= 65535.
  */
@@ -480,8 +480,29 @@ int q8_validate_down_grouped_f32(const void *slots_base, uint64_t slot_stride,
 /* Message for the last failing call on this thread ("" after success). */
 const char *q4_last_error(void);
 
-/* ABI version: 4 (1 plus the down projection and whole-expert calls, the Q8
- * family and f32 activations). */
+/*
+ * Measurement aid (no part of the method): reads, in each of num_slots slots
+ * spaced slot_stride bytes apart from slots_base, two arrays of `rows` rows
+ * of row_bytes bytes at offset_a and offset_b (for an expert slot: its gate
+ * and up weights), each byte once, with no arithmetic.
+ *   pattern 0  the gate/up kernels' weight access: 16-row tiles, 128 bytes of
+ *              each row per step, 32 bytes per lane;
+ *   pattern 1  the same bytes per step as two lane-linear 1 KiB runs.
+ *   waves      8 or 16 waves per work-group (one work-group per CU);
+ *   depth      steps in flight per wave: 1, 2 or 4.
+ *   sink       device, one 4-byte word; written only on a data value that
+ *              real data practically never gives (keeps the loads live).
+ * Needs row_bytes a positive multiple of 128, 16-byte aligned slots_base,
+ * slot_stride and offsets, offset + rows*row_bytes <= slot_stride, and
+ * rows*row_bytes <= 2^31 - 16.  Asynchronous on `stream`.
+ */
+int q4_stream_read(const void *slots_base, uint64_t slot_stride, int64_t num_slots,
+                   uint64_t offset_a, uint64_t offset_b, int64_t rows, int64_t row_bytes,
+                   int pattern, int waves, int depth, void *sink, q4_stream_t stream);
+
+/* ABI version: 5 (1 plus the down projection and whole-expert calls, the Q8
+ * family, f32 activations, the (M, K, num_slots) workspace query and the
+ * streaming-read measurement aid). */
 int q4_abi_version(void);
 
 #ifdef __cplusplus

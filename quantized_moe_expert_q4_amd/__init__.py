@@ -30,4 +30,5 @@ from ._lib import (  # noqa: F401
     expert_forward_grouped,
     validate_down,
     validate_down_grouped,
+    stream_read,
 )

@@ -64,7 +64,9 @@ _LAYOUT = ctypes.POINTER(SlotLayoutC)
 _SIGNATURES = {
     "q4_expert_gate_up": (ctypes.c_int, [_P, _LAYOUT, _P, _I64, _I64, _I64, _P, _P]),
     "q4_expert_gate_up_probe": (ctypes.c_int, [_P, _LAYOUT, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
-    "q4_grouped_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I64]),
+    "q4_grouped_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "q4_stream_read": (ctypes.c_int, [_P, _U64, _I64, _U64, _U64, _I64, _I64, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, _P, _P]),
     "q4_expert_gate_up_grouped": (ctypes.c_int, [_P, _U64, _I64, _LAYOUT, _P, _I64, _P, _I64, _I64, _I64,
                                                  _P, _P, _SZ, _P]),
     "q4_expert_gate_up_grouped_probe": (ctypes.c_int, [_P, _U64, _I64, _LAYOUT, _P, _I64, _P, _I64, _I64,
@@ -223,21 +225,62 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
-def grouped_workspace_bytes(M: int, K: int, H: int, I: int, num_slots: int) -> int:
-    return int(load().q4_grouped_workspace_bytes(M, K, H, I, num_slots))
+_XDTYPE_NAMES = {"bf16": "bfloat16", "f32": "float32"}
+
+
+def _args(*specs) -> None:
+    """Reject tensor arguments the kernels would misread.  Each spec is
+    (name, tensor, dtype, numel): the tensor must have that dtype, be
+    contiguous, hold at least ``numel`` elements and live in device memory
+    (dtype, layout and size of every argument are checked before any
+    device).  Raw integer pointers pass unchecked; None is left to the
+    library's own checks (required pointers) or means "skip" (probes)."""
+    live = [sp for sp in specs if sp[1] is not None and not isinstance(sp[1], int)]
+    for name, t, dtype, numel in live:
+        got = str(t.dtype).replace("torch.", "")
+        if got != dtype:
+            raise ValueError(f"{name} must be a {dtype} tensor, not {got}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.numel() < numel:
+            raise ValueError(f"{name} holds {t.numel()} elements, fewer than the {numel} the call reads or writes")
+    for name, t, _, _ in live:
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a device (cuda) tensor, not on {t.device.type}")
+
+
+def _slots_spec(name: str, t, num_slots: int, stride: int, layout):
+    return (name, t, "uint8", (int(num_slots) - 1) * int(stride) + int(layout.slot_bytes))
+
+
+def grouped_workspace_bytes(M: int, K: int, num_slots: int) -> int:
+    return int(load().q4_grouped_workspace_bytes(M, K, num_slots))
 
 
 def expert_gate_up(slot, layout, x, M: int, H: int, I: int, out, gate_probe=None, up_probe=None,
                    stream=None, fmt: str = "q4", xdtype: str = "bf16") -> None:
     """Enqueue the single-expert kernel (see q4_expert_gate_up in include/q4moe.h)."""
     lib = load()
+    fn = _fn(lib, fmt, "expert_gate_up_probe" if (gate_probe is not None or up_probe is not None)
+             else "expert_gate_up", xdtype)
+    xt = _XDTYPE_NAMES[xdtype]
+    _args(_slots_spec("slot", slot, 1, layout.slot_bytes, layout), ("x", x, xt, M * H), ("out", out, xt, M * I),
+          ("gate_probe", gate_probe, "float32", M * I), ("up_probe", up_probe, "float32", M * I))
     lay = layout_c(layout)
     if gate_probe is None and up_probe is None:
-        st = _fn(lib, fmt, "expert_gate_up", xdtype)(_ptr(slot), ctypes.byref(lay), _ptr(x), M, H, I, _ptr(out), _stream(stream))
+        st = fn(_ptr(slot), ctypes.byref(lay), _ptr(x), M, H, I, _ptr(out), _stream(stream))
     else:
-        st = _fn(lib, fmt, "expert_gate_up_probe", xdtype)(_ptr(slot), ctypes.byref(lay), _ptr(x), M, H, I, _ptr(out),
-                                         _ptr(gate_probe), _ptr(up_probe), _stream(stream))
+        st = fn(_ptr(slot), ctypes.byref(lay), _ptr(x), M, H, I, _ptr(out), _ptr(gate_probe), _ptr(up_probe),
+                _stream(stream))
     _check(st)
+
+
+def _grouped_specs(slots_base, slot_stride, num_slots, layout, x, M, slot_ids, K, n_in, out, n_out, workspace,
+                   workspace_bytes, xdtype, in_name="x"):
+    xt = _XDTYPE_NAMES[xdtype]
+    return [_slots_spec("slots_base", slots_base, num_slots, slot_stride, layout), (in_name, x, xt, n_in),
+            ("slot_ids", slot_ids, "int32", M * K), ("out", out, xt, n_out),
+            ("workspace", workspace, "uint8", workspace_bytes)]
 
 
 def expert_gate_up_grouped(slots_base, slot_stride: int, num_slots: int, layout, x, M: int, slot_ids, K: int,
@@ -245,16 +288,18 @@ def expert_gate_up_grouped(slots_base, slot_stride: int, num_slots: int, layout,
                            up_probe=None, stream=None, fmt: str = "q4", xdtype: str = "bf16") -> None:
     """Enqueue the grouped kernel (see q4_expert_gate_up_grouped in include/q4moe.h)."""
     lib = load()
+    probes = gate_probe is not None or up_probe is not None
+    fn = _fn(lib, fmt, "expert_gate_up_grouped_probe" if probes else "expert_gate_up_grouped", xdtype)
+    _args(*_grouped_specs(slots_base, slot_stride, num_slots, layout, x, M, slot_ids, K, M * H, out, M * K * I,
+                          workspace, workspace_bytes, xdtype),
+          ("gate_probe", gate_probe, "float32", M * K * I), ("up_probe", up_probe, "float32", M * K * I))
     lay = layout_c(layout)
-    if gate_probe is None and up_probe is None:
-        st = _fn(lib, fmt, "expert_gate_up_grouped", xdtype)(_ptr(slots_base), slot_stride, num_slots, ctypes.byref(lay), _ptr(x),
-                                           M, _ptr(slot_ids), K, H, I, _ptr(out), _ptr(workspace),
-                                           workspace_bytes, _stream(stream))
+    if not probes:
+        st = fn(_ptr(slots_base), slot_stride, num_slots, ctypes.byref(lay), _ptr(x), M, _ptr(slot_ids), K, H, I,
+                _ptr(out), _ptr(workspace), workspace_bytes, _stream(stream))
     else:
-        st = _fn(lib, fmt, "expert_gate_up_grouped_probe", xdtype)(_ptr(slots_base), slot_stride, num_slots, ctypes.byref(lay),
-                                                 _ptr(x), M, _ptr(slot_ids), K, H, I, _ptr(out),
-                                                 _ptr(gate_probe), _ptr(up_probe), _ptr(workspace),
-                                                 workspace_bytes, _stream(stream))
+        st = fn(_ptr(slots_base), slot_stride, num_slots, ctypes.byref(lay), _ptr(x), M, _ptr(slot_ids), K, H, I,
+                _ptr(out), _ptr(gate_probe), _ptr(up_probe), _ptr(workspace), workspace_bytes, _stream(stream))
     _check(st)
 
 
@@ -273,15 +318,19 @@ def validate_grouped(slots_base, slot_stride, num_slots, layout, x, M, slot_ids,
                                       H, I, _ptr(out), _ptr(workspace), workspace_bytes)
 
 
-def expert_down(slot, layout, mid, M: int, H: int, I: int, out, down_probe=None, stream=None, fmt: str = "q4", xdtype: str = "bf16") -> None:
+def expert_down(slot, layout, mid, M: int, H: int, I: int, out, down_probe=None, stream=None, fmt: str = "q4",
+                xdtype: str = "bf16") -> None:
     """Enqueue the down projection of one slot (see q4_expert_down in include/q4moe.h)."""
     lib = load()
+    fn = _fn(lib, fmt, "expert_down" if down_probe is None else "expert_down_probe", xdtype)
+    xt = _XDTYPE_NAMES[xdtype]
+    _args(_slots_spec("slot", slot, 1, layout.slot_bytes, layout), ("mid", mid, xt, M * I), ("out", out, xt, M * H),
+          ("down_probe", down_probe, "float32", M * H))
     lay = layout_c(layout)
     if down_probe is None:
-        st = _fn(lib, fmt, "expert_down", xdtype)(_ptr(slot), ctypes.byref(lay), _ptr(mid), M, H, I, _ptr(out), _stream(stream))
+        st = fn(_ptr(slot), ctypes.byref(lay), _ptr(mid), M, H, I, _ptr(out), _stream(stream))
     else:
-        st = _fn(lib, fmt, "expert_down_probe", xdtype)(_ptr(slot), ctypes.byref(lay), _ptr(mid), M, H, I, _ptr(out),
-                                      _ptr(down_probe), _stream(stream))
+        st = fn(_ptr(slot), ctypes.byref(lay), _ptr(mid), M, H, I, _ptr(out), _ptr(down_probe), _stream(stream))
     _check(st)
 
 
@@ -290,33 +339,42 @@ def expert_down_grouped(slots_base, slot_stride: int, num_slots: int, layout, mi
                         stream=None, fmt: str = "q4", xdtype: str = "bf16") -> None:
     """Enqueue the grouped down projection (see q4_expert_down_grouped in include/q4moe.h)."""
     lib = load()
+    fn = _fn(lib, fmt, "expert_down_grouped" if down_probe is None else "expert_down_grouped_probe", xdtype)
+    _args(*_grouped_specs(slots_base, slot_stride, num_slots, layout, mid, M, slot_ids, K, M * K * I, out, M * K * H,
+                          workspace, workspace_bytes, xdtype, in_name="mid"),
+          ("down_probe", down_probe, "float32", M * K * H))
     lay = layout_c(layout)
     if down_probe is None:
-        st = _fn(lib, fmt, "expert_down_grouped", xdtype)(_ptr(slots_base), slot_stride, num_slots, ctypes.byref(lay), _ptr(mid),
-                                        M, _ptr(slot_ids), K, H, I, _ptr(out), _ptr(workspace),
-                                        workspace_bytes, _stream(stream))
+        st = fn(_ptr(slots_base), slot_stride, num_slots, ctypes.byref(lay), _ptr(mid), M, _ptr(slot_ids), K, H, I,
+                _ptr(out), _ptr(workspace), workspace_bytes, _stream(stream))
     else:
-        st = _fn(lib, fmt, "expert_down_grouped_probe", xdtype)(_ptr(slots_base), slot_stride, num_slots, ctypes.byref(lay),
-                                              _ptr(mid), M, _ptr(slot_ids), K, H, I, _ptr(out),
-                                              _ptr(down_probe), _ptr(workspace), workspace_bytes,
-                                              _stream(stream))
+        st = fn(_ptr(slots_base), slot_stride, num_slots, ctypes.byref(lay), _ptr(mid), M, _ptr(slot_ids), K, H, I,
+                _ptr(out), _ptr(down_probe), _ptr(workspace), workspace_bytes, _stream(stream))
     _check(st)
 
 
-def expert_forward(slot, layout, x, M: int, H: int, I: int, mid, out, stream=None, fmt: str = "q4", xdtype: str = "bf16") -> None:
+def expert_forward(slot, layout, x, M: int, H: int, I: int, mid, out, stream=None, fmt: str = "q4",
+                   xdtype: str = "bf16") -> None:
     """Enqueue the whole expert of one slot (see q4_expert_forward in include/q4moe.h)."""
+    fn = _fn(load(), fmt, "expert_forward", xdtype)
+    xt = _XDTYPE_NAMES[xdtype]
+    _args(_slots_spec("slot", slot, 1, layout.slot_bytes, layout), ("x", x, xt, M * H), ("mid", mid, xt, M * I),
+          ("out", out, xt, M * H))
     lay = layout_c(layout)
-    _check(_fn(load(), fmt, "expert_forward", xdtype)(_ptr(slot), ctypes.byref(lay), _ptr(x), M, H, I, _ptr(mid), _ptr(out),
-                                    _stream(stream)))
+    _check(fn(_ptr(slot), ctypes.byref(lay), _ptr(x), M, H, I, _ptr(mid), _ptr(out), _stream(stream)))
 
 
 def expert_forward_grouped(slots_base, slot_stride: int, num_slots: int, layout, x, M: int, slot_ids, K: int,
-                           H: int, I: int, mid, out, workspace, workspace_bytes: int, stream=None, fmt: str = "q4", xdtype: str = "bf16") -> None:
+                           H: int, I: int, mid, out, workspace, workspace_bytes: int, stream=None, fmt: str = "q4",
+                           xdtype: str = "bf16") -> None:
     """Enqueue the grouped whole expert (see q4_expert_forward_grouped in include/q4moe.h)."""
+    fn = _fn(load(), fmt, "expert_forward_grouped", xdtype)
+    _args(*_grouped_specs(slots_base, slot_stride, num_slots, layout, x, M, slot_ids, K, M * H, out, M * K * H,
+                          workspace, workspace_bytes, xdtype),
+          ("mid", mid, _XDTYPE_NAMES[xdtype], M * K * I))
     lay = layout_c(layout)
-    _check(_fn(load(), fmt, "expert_forward_grouped", xdtype)(_ptr(slots_base), slot_stride, num_slots, ctypes.byref(lay),
-                                            _ptr(x), M, _ptr(slot_ids), K, H, I, _ptr(mid), _ptr(out),
-                                            _ptr(workspace), workspace_bytes, _stream(stream)))
+    _check(fn(_ptr(slots_base), slot_stride, num_slots, ctypes.byref(lay), _ptr(x), M, _ptr(slot_ids), K, H, I,
+              _ptr(mid), _ptr(out), _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def validate_down(slot, layout, mid, M: int, H: int, I: int, out, fmt: str = "q4", xdtype: str = "bf16") -> int:
@@ -332,3 +390,12 @@ def validate_down_grouped(slots_base, slot_stride, num_slots, layout, mid, M, sl
     return _fn(load(), fmt, "validate_down_grouped", xdtype)(_ptr(slots_base), slot_stride, num_slots,
                                            None if lay is None else ctypes.byref(lay), _ptr(mid), M,
                                            _ptr(slot_ids), K, H, I, _ptr(out), _ptr(workspace), workspace_bytes)
+
+
+def stream_read(slots_base, slot_stride: int, num_slots: int, offset_a: int, offset_b: int, rows: int,
+                row_bytes: int, sink, pattern: int = 0, waves: int = 8, depth: int = 4, stream=None) -> None:
+    """Enqueue the read-only streaming kernel (see q4_stream_read in include/q4moe.h)."""
+    _args(("slots_base", slots_base, "uint8", (num_slots - 1) * slot_stride + max(offset_a, offset_b) + rows * row_bytes),
+          ("sink", sink, "int32", 1))
+    _check(load().q4_stream_read(_ptr(slots_base), slot_stride, num_slots, offset_a, offset_b, rows, row_bytes,
+                                 pattern, waves, depth, _ptr(sink), _stream(stream)))

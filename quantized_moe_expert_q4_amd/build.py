@@ -7,6 +7,8 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -14,14 +16,13 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libq4moe.so")
 
-SOURCES = ["q4moe_resident.hip", "q4moe_batch.hip", "q4moe_abi.cpp"]
+SOURCES = ["q4moe_resident.hip", "q4moe_batch.hip", "q4moe_stream.hip", "q4moe_abi.cpp"]
 
 FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-ffp-contract=off",
     # packed-FP32 instructions are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -37,10 +38,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libq4moe.so)")
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, "-I", INCLUDE, "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -50,6 +48,20 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + out)
     if out.strip() and verbose:
         print(out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel), then link the library."""
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="q4moe_build_") as tmpdir:
+        objs = [os.path.join(tmpdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+        cmds = [[cc, *FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, s), "-o", o]
+                for s, o in zip(SOURCES, objs)]
+        with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+            for f in [ex.submit(_run, c, verbose) for c in cmds]:
+                f.result()
+        tmp = LIB + ".tmp"
+        _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

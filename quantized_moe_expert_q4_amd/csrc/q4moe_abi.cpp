@@ -16,6 +16,7 @@
 
 #include "q4moe.h"
 #include "q4moe_launch.h"
+#include "q4moe_stream.h"
 
 namespace {
 
@@ -136,7 +137,8 @@ int check_grouped(unsigned fmt, const void* base, uint64_t stride, int64_t num_s
   if (K < 1) return fail(Q4_ERR_INVALID_ARGUMENT, "top-k must be a positive integer");
   if (num_slots < 1) return fail(Q4_ERR_INVALID_ARGUMENT, "number of slots must be a positive integer");
   if (num_slots > kMaxSlots) return fail(Q4_ERR_UNSUPPORTED, "more than 65535 slots is not supported");
-  if (M * K > kMaxPairs) return fail(Q4_ERR_UNSUPPORTED, "more than 65536 routed pairs per call is not supported");
+  if (K > kMaxPairs || M * K > kMaxPairs)
+    return fail(Q4_ERR_UNSUPPORTED, "more than 65536 routed pairs per call is not supported");
   if (!base) return fail(Q4_ERR_INVALID_ARGUMENT, "expert slot pointer must be a non-null device pointer");
   if (!aligned(base, kSlotAlign))
     return fail(Q4_ERR_ALIGNMENT, "expert slot pointer must be page-aligned (4096 bytes) for direct device access");
@@ -150,7 +152,7 @@ int check_grouped(unsigned fmt, const void* base, uint64_t stride, int64_t num_s
   if ((rc = check_io(fmt, x, out, gp, up))) return rc;
   if (!ws) return fail(Q4_ERR_WORKSPACE, "workspace must be a non-null device pointer");
   if (!aligned(ws, 256)) return fail(Q4_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
-  if (ws_bytes < q4_grouped_workspace_bytes(M, K, H, I, num_slots))
+  if (ws_bytes < q4_grouped_workspace_bytes(M, K, num_slots))
     return fail(Q4_ERR_WORKSPACE, "workspace is smaller than q4_grouped_workspace_bytes()");
   return ok();
 }
@@ -276,9 +278,8 @@ int q4_expert_gate_up_probe(const void* slot, const q4_slot_layout* layout, cons
   return run_single(0u, slot, layout, x_bf16, M, H, I, out_bf16, gate_f32, up_f32, stream);
 }
 
-size_t q4_grouped_workspace_bytes(int64_t M, int64_t K, int64_t H, int64_t I, int64_t num_slots) {
-  if (M < 1 || K < 1 || H < 8 || I < 1 || num_slots < 1 || M > kMaxM || H > kMaxH || num_slots > kMaxSlots ||
-      M * K > kMaxPairs)
+size_t q4_grouped_workspace_bytes(int64_t M, int64_t K, int64_t num_slots) {
+  if (M < 1 || K < 1 || num_slots < 1 || M > kMaxM || K > kMaxPairs || num_slots > kMaxSlots || M * K > kMaxPairs)
     return 0;
   return kWorkspaceBytes;
 }
@@ -706,8 +707,38 @@ int q8_validate_down_grouped_f32(const void* slots_base, uint64_t slot_stride, i
                             nullptr, workspace, workspace_bytes);
 }
 
+int q4_stream_read(const void* slots_base, uint64_t slot_stride, int64_t num_slots, uint64_t offset_a,
+                   uint64_t offset_b, int64_t rows, int64_t row_bytes, int pattern, int waves, int depth, void* sink,
+                   q4_stream_t stream) {
+  if (!slots_base || !sink) return fail(Q4_ERR_INVALID_ARGUMENT, "slots and sink must be non-null device pointers");
+  if (!aligned(slots_base, 16) || !aligned(sink, 4) || offset_a % 16 || offset_b % 16 || slot_stride % 16)
+    return fail(Q4_ERR_ALIGNMENT, "slots, stride and offsets must be 16-byte aligned, sink 4-byte aligned");
+  if (num_slots < 1 || num_slots > kMaxSlots || rows < 1 || row_bytes < 128 || row_bytes % 128)
+    return fail(Q4_ERR_INVALID_ARGUMENT, "need 1 <= num_slots <= 65535, rows >= 1 and row_bytes a positive multiple of 128");
+  if ((uint64_t)rows * (uint64_t)row_bytes > kMaxWeightBytes)
+    return fail(Q4_ERR_UNSUPPORTED, "an array above 2^31 - 16 bytes is not supported");
+  const uint64_t len = (uint64_t)rows * (uint64_t)row_bytes;
+  if (offset_a > slot_stride || len > slot_stride - offset_a || offset_b > slot_stride || len > slot_stride - offset_b)
+    return fail(Q4_ERR_RANGE, "an array exceeds the slot stride");
+  if (pattern != 0 && pattern != 1) return fail(Q4_ERR_INVALID_ARGUMENT, "pattern must be 0 (row tiles) or 1 (linear)");
+  if ((waves != 8 && waves != 16) || (depth != 1 && depth != 2 && depth != 4))
+    return fail(Q4_ERR_UNSUPPORTED, "waves must be 8 or 16 and depth 1, 2 or 4");
+  q4::StreamParams p{};
+  p.base = static_cast<const uint8_t*>(slots_base);
+  p.slot_stride = slot_stride;
+  p.off_a = offset_a;
+  p.off_b = offset_b;
+  p.row_bytes = (uint32_t)row_bytes;
+  p.rows = (int)rows;
+  p.num_slots = (int)num_slots;
+  p.sink = static_cast<uint32_t*>(sink);
+  const hipError_t e = q4::launch_stream_read(p, pattern, waves, depth, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(Q4_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  return ok();
+}
+
 const char* q4_last_error(void) { return g_err.c_str(); }
 
-int q4_abi_version(void) { return 4; }
+int q4_abi_version(void) { return 5; }
 
 }  // extern "C"

@@ -37,10 +37,14 @@ namespace {
 
 constexpr int kResWaves = 8;
 constexpr int kResThreads = kResWaves * 64;
-// K-steps of weights in flight per wave (a multiple of 4).  Measured: 8 with
-// two column tiles spills ~30 VGPRs and streams 6% slower at eight tokens; 8
-// with one column tile (no spills) streams 3.5% slower at one token.
-__host__ __device__ constexpr int res_depth(int nt, bool q8) { return (void)nt, (void)q8, 4; }
+#ifndef Q4_RES_DEPTH
+#define Q4_RES_DEPTH 4
+#endif
+// K-steps of weights in flight per wave (1, 2 or 4).
+__host__ __device__ constexpr int res_depth(int nt, bool q8) { return (void)nt, (void)q8, Q4_RES_DEPTH; }
+// K-steps per pass of the step loop: the B-fragment swizzle repeats every
+// four steps, so four steps per pass keep its offsets fixed.
+constexpr int kResU = 4;
 constexpr int kResLds = 150 * 1024;        // digits, then the fix-up slots
 constexpr int kResXRegs = 8;               // 16-byte chunks of x held per thread while splitting
 constexpr int kResMaxTokens = 8;           // tokens per call
@@ -58,8 +62,8 @@ __host__ __device__ constexpr int res_step_bytes(int nt, int planes = 2) { retur
 __host__ __device__ constexpr int res_chunk(int g, int c, int step) { return g * 16 + (c ^ (4 * g + (step & 3))); }
 // One fix-up slot: int64 [tile][gate, up][lane] (quad sums).
 __host__ __device__ constexpr int res_fix_words(int nt) { return nt * 2 * 64; }
-// K-steps per tile, padded to whole rings.
-__host__ __device__ constexpr int res_steps(int H, int D, int kps = 128) { return ((H + kps - 1) / kps + D - 1) / D * D; }
+// K-steps per tile, padded to whole passes of the step loop.
+__host__ __device__ constexpr int res_steps(int H, int kps = 128) { return ((H + kps - 1) / kps + kResU - 1) / kResU * kResU; }
 // Wide K-steps (256 packed nibbles per row, four operand planes) for one
 // column tile of Q4 weights and bf16 activations: rows are read 128 bytes per
 // step (measured: the same bytes stream ~3-6% faster than 64 bytes per step).
@@ -179,10 +183,10 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
   auto bound = [&](int k) {
     if (k >= kResWaves) return nunits;
     const int q = k >> 1;
-    const int qa = (int)(((int64_t)q * nunits / 4) / kResD * kResD);
+    const int qa = (int)(((int64_t)q * nunits / 4) / kResU * kResU);
     if (!(k & 1)) return qa;
-    const int qb = q == 3 ? nunits : (int)(((int64_t)(q + 1) * nunits / 4) / kResD * kResD);
-    return qa + (int)(((int64_t)(qb - qa) * a.wave_share / 1024) / kResD * kResD);
+    const int qb = q == 3 ? nunits : (int)(((int64_t)(q + 1) * nunits / 4) / kResU * kResU);
+    return qa + (int)(((int64_t)(qb - qa) * a.wave_share / 1024) / kResU * kResU);
   };
   const int wpos = 2 * (wave & 3) + (wave >> 2);
   auto open_segment = [&]() {
@@ -511,10 +515,10 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
     return ((qj & 1) ? k1 : k0) + r;
   };
   // this lane's B-fragment chunk for steps 0..3 mod 4
-  static_assert(kResD % 4 == 0, "ring depth keeps step % 4 fixed per ring slot");
-  int rdo[4];
+  static_assert(kResU % kResD == 0, "the step loop's pass covers whole turns of the ring");
+  int rdo[kResU];
 #pragma unroll
-  for (int d = 0; d < 4; ++d) rdo[d] = res_chunk(g4, cc, d) * 16;
+  for (int j = 0; j < kResU; ++j) rdo[j] = res_chunk(g4, cc, j) * 16;
 
   for (int pass = 0;;) {
     const int tp0 = pass * tpp;                             // first token of the pass
@@ -635,10 +639,11 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
           accg[n] = v4i{0, 0, 0, 0};
           accu[n] = v4i{0, 0, 0, 0};
         }
-        int s = sa;                                           // a multiple of 4: (s + d) % 4 == d % 4
-        for (; u < pe; u += kResD) {
+        int s = sa;                                           // a multiple of 4: (s + j) % 4 == j
+        for (; u < pe; u += kResU) {
 #pragma unroll
-          for (int d = 0; d < kResD; ++d) {
+          for (int j = 0; j < kResU; ++j) {
+            const int d = j % kResD;                          // ring slot of step s + j
             v4i pg[NPL], pu[NPL];
             if constexpr (WIDE) {
               split_planes(rg[d].a, rg[d].b, pg);
@@ -653,14 +658,14 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
             // has read the slot and can land in the slot's own registers.
             // Otherwise the compiler issues them early into other registers
             // and, at the loop's back edge, copies every slot back, waiting
-            // for all loads in flight each D steps.
+            // for all loads in flight each pass.
             uint32_t dep = 0u;
             if constexpr (!XF) {
 #pragma unroll
               for (int pl = 0; pl < NPL; ++pl) asm volatile("" : "+v"(dep) : "v"(pg[pl]), "v"(pu[pl]));
             }
-            issue(rg[d], ru[d], u + d + kResD < ub, dep);
-            const uint8_t* bp = s_lds + (s + d) * sbytes + rdo[d & 3];
+            issue(rg[d], ru[d], u + j + kResD < ub, dep);
+            const uint8_t* bp = s_lds + (s + j) * sbytes + rdo[j];
             v4i bq[NPL][NT];
 #pragma unroll
             for (int pl = 0; pl < NPL; ++pl)
@@ -674,7 +679,7 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
                 accu[n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pu[pl], bq[pl][n], accu[n], 0, 0, 0);
               }
           }
-          s += kResD;
+          s += kResU;
           // take the row scales over here, where the compiler counts the
           // weight loads issued after them exactly (left to the finish, the
           // wait for them covers every load in flight)
@@ -920,14 +925,14 @@ bool resident_fits(int M, int H, bool q8, bool xf) {
   const int nt = res_tiles(M);
   const bool wide = res_wide(nt, q8, xf);
   return (int64_t)M * (H / 8) <= (int64_t)kResXRegs * kResThreads &&
-         (int64_t)res_steps(H, res_depth(nt, q8), wide ? 256 : 128) * res_step_bytes(nt, wide ? 4 : 2) +
+         (int64_t)res_steps(H, wide ? 256 : 128) * res_step_bytes(nt, wide ? 4 : 2) +
                  (int64_t)kResFixSlots * res_fix_words(nt) * 8 <=
              (int64_t)kResLds;
 }
 
 hipError_t launch_resident(GateUpParams p, hipStream_t stream) {
   const int nt = res_tiles(p.M);
-  p.steps = res_steps(p.H, res_depth(nt, p.q8 != 0), res_wide(nt, p.q8 != 0, p.xf32 != 0) ? 256 : 128);
+  p.steps = res_steps(p.H, res_wide(nt, p.q8 != 0, p.xf32 != 0) ? 256 : 128);
   p.G = kResMaxPairs;
   p.wave_share = res_tiles(p.M) == 1 ? kWaveShare1 : kWaveShare2;
   return p.xf32 ? launch_resident_x<true>(p, stream) : launch_resident_x<false>(p, stream);

@@ -49,7 +49,7 @@ def run_grouped(slots_np, layout, xbits, ids, H, I, probes=True, ws_fill=None, w
     out = torch.empty((M, K, I), dtype=torch.bfloat16, device="cuda")
     g = torch.empty((M, K, I), dtype=torch.float32, device="cuda") if probes else None
     u = torch.empty((M, K, I), dtype=torch.float32, device="cuda") if probes else None
-    wsb = q4.grouped_workspace_bytes(M, K, H, I, E)
+    wsb = q4.grouped_workspace_bytes(M, K, E)
     if ws is None:
         ws = aligned_empty(wsb, 256)
         ws.fill_(0xAB if ws_fill is None else ws_fill)
@@ -126,7 +126,7 @@ def run_down_grouped(slots_np, layout, midbits, ids, H, I, slots=None, fmt="q4")
     idt = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda()
     out = torch.empty((M, K, H), dtype=torch.bfloat16, device="cuda")
     d = torch.empty((M, K, H), dtype=torch.float32, device="cuda")
-    wsb = q4.grouped_workspace_bytes(M, K, H, I, E)
+    wsb = q4.grouped_workspace_bytes(M, K, E)
     ws = aligned_empty(wsb, 256)
     ws.fill_(0xAB)
     q4.expert_down_grouped(slots, slots_np.shape[1], E, layout, mid, M, idt, K, H, I, out, ws, wsb, d, fmt=fmt)

@@ -27,15 +27,15 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 59, names
     for n in names:
         assert hasattr(lib, n), n
-    assert q4.abi_version() == 4
+    assert q4.abi_version() == 5
 
 
 def test_workspace_size_is_aligned_and_positive():
     for M, K, H, I, E in ((1, 1, 8, 1, 1), (32, 8, 6144, 2048, 64), (4096, 16, 7168, 4096, 65535)):
-        b = q4.grouped_workspace_bytes(M, K, H, I, E)
+        b = q4.grouped_workspace_bytes(M, K, E)
         assert b >= 256 and b % 256 == 0
-    assert q4.grouped_workspace_bytes(0, 1, 4096, 64, 1) == 0
-    assert q4.grouped_workspace_bytes(1, 1, 4096, 64, 0) == 0
+    assert q4.grouped_workspace_bytes(0, 1, 1) == 0
+    assert q4.grouped_workspace_bytes(1, 1, 0) == 0
 
 
 SLOT = 1 << 20           # fake, 4096-aligned "device" addresses: validation never dereferences them
@@ -116,7 +116,7 @@ def test_down_fields_in_range_are_accepted():
 def _grouped(**kw):
     lay = _lay(6144, 2048)
     a = dict(base=SLOT, stride=lay.slot_bytes, E=64, layout=lay, x=X, M=32, ids=IDS, K=8, H=6144, I=2048,
-             out=OUT, ws=WS, wsb=q4.grouped_workspace_bytes(32, 8, 6144, 2048, 64))
+             out=OUT, ws=WS, wsb=q4.grouped_workspace_bytes(32, 8, 64))
     a.update(kw)
     st = q4.validate_grouped(a["base"], a["stride"], a["E"], a["layout"], a["x"], a["M"], a["ids"], a["K"], a["H"],
                              a["I"], a["out"], a["ws"], a["wsb"])
@@ -200,7 +200,7 @@ def test_down_rejections(kw, status, msg):
 def _down_grouped(**kw):
     lay = synth.expert_layout(6144, 2048)
     a = dict(base=SLOT, stride=lay.slot_bytes, E=64, layout=lay, mid=X, M=32, ids=IDS, K=8, H=6144, I=2048,
-             out=OUT, ws=WS, wsb=q4.grouped_workspace_bytes(32, 8, 6144, 2048, 64))
+             out=OUT, ws=WS, wsb=q4.grouped_workspace_bytes(32, 8, 64))
     a.update(kw)
     st = q4.validate_down_grouped(a["base"], a["stride"], a["E"], a["layout"], a["mid"], a["M"], a["ids"], a["K"],
                                   a["H"], a["I"], a["out"], a["ws"], a["wsb"])
@@ -211,7 +211,7 @@ def test_down_grouped_valid_and_rejected():
     assert _down_grouped() == (0, "")
     st, err = _down_grouped(layout=synth.contiguous_layout(6144, 2048), stride=synth.contiguous_layout(6144, 2048).slot_bytes)
     assert st == q4.Q4_ERR_INVALID_ARGUMENT and "down" in err
-    st, err = _down_grouped(M=65536, K=1, wsb=q4.grouped_workspace_bytes(65535, 1, 6144, 2048, 64))
+    st, err = _down_grouped(M=65536, K=1, wsb=q4.grouped_workspace_bytes(65535, 1, 64))
     assert st == q4.Q4_ERR_UNSUPPORTED
     st, err = _down_grouped(wsb=0)
     assert st == q4.Q4_ERR_WORKSPACE
@@ -273,3 +273,70 @@ def test_f32_validation_and_output_alignment():
                                     xdtype="f32") == 0
     with pytest.raises(ValueError):
         q4.validate_gate_up(SLOT, lay, X, 1, 4096, 1536, OUT, xdtype="f16")
+
+
+def test_huge_top_k_is_rejected_before_the_pair_product():
+    # K * M would wrap a signed 64-bit product; K alone is already out of range
+    st, err = _grouped(M=4, K=1 << 62)
+    assert st == q4.Q4_ERR_UNSUPPORTED, err
+    assert "routed pairs" in err
+    assert q4.grouped_workspace_bytes(4, 1 << 62, 64) == 0
+    assert q4.grouped_workspace_bytes(1, 65537, 64) == 0
+
+
+def test_stream_read_rejects_invalid_arguments_on_the_host():
+    lib = q4.load()
+    cases = [
+        (dict(row_bytes=100), q4.Q4_ERR_INVALID_ARGUMENT),
+        (dict(pattern=2), q4.Q4_ERR_INVALID_ARGUMENT),
+        (dict(waves=4), q4.Q4_ERR_UNSUPPORTED),
+        (dict(depth=8), q4.Q4_ERR_UNSUPPORTED),
+        (dict(offset_a=8), q4.Q4_ERR_ALIGNMENT),
+        (dict(offset_b=1 << 30), q4.Q4_ERR_RANGE),
+        (dict(num_slots=0), q4.Q4_ERR_INVALID_ARGUMENT),
+    ]
+    for kw, status in cases:
+        a = dict(base=SLOT, stride=6303744, num_slots=4, offset_a=0, offset_b=3145728, rows=1536, row_bytes=2048,
+                 pattern=0, waves=8, depth=4, sink=WS)
+        a.update(kw)
+        st = lib.q4_stream_read(a["base"], a["stride"], a["num_slots"], a["offset_a"], a["offset_b"], a["rows"],
+                                a["row_bytes"], a["pattern"], a["waves"], a["depth"], a["sink"], None)
+        assert st == status, (kw, q4.last_error())
+
+
+def test_binding_rejects_tensors_the_kernels_would_misread():
+    """The binding checks dtype, contiguity, size and device of every tensor
+    argument before the C call (CPU tensors: the device rule fires last)."""
+    torch = pytest.importorskip("torch")
+    lay = _lay(256, 128)
+    H, I, M, K, E = 256, 128, 2, 2, 3
+    slots = torch.zeros(E * lay.slot_bytes, dtype=torch.uint8)
+    x = torch.zeros(M, H, dtype=torch.bfloat16)
+    ids = torch.zeros(M, K, dtype=torch.int32)
+    out = torch.zeros(M, K, I, dtype=torch.bfloat16)
+    ws = torch.zeros(q4.grouped_workspace_bytes(M, K, E), dtype=torch.uint8)
+
+    def call(**kw):
+        a = dict(slots=slots, x=x, ids=ids, out=out, ws=ws, gate_probe=None, xdtype="bf16")
+        a.update(kw)
+        with pytest.raises(ValueError) as ei:
+            q4.expert_gate_up_grouped(a["slots"], lay.slot_bytes, E, lay, a["x"], M, a["ids"], K, H, I, a["out"],
+                                      a["ws"], ws.numel(), gate_probe=a["gate_probe"], xdtype=a["xdtype"])
+        return str(ei.value)
+
+    assert "slot_ids must be a int32" in call(ids=ids.to(torch.int64))
+    assert "x must be a bfloat16" in call(x=x.float())
+    assert "x must be a float32" in call(xdtype="f32")
+    assert "out must be a bfloat16" in call(out=out.float())
+    assert "gate_probe must be a float32" in call(gate_probe=torch.zeros(M, K, I, dtype=torch.bfloat16))
+    assert "gate_probe holds" in call(gate_probe=torch.zeros(M * K * I - 1, dtype=torch.float32))
+    assert "out holds" in call(out=out[:1])
+    assert "x must be contiguous" in call(x=torch.zeros(H, M, dtype=torch.bfloat16).t())
+    assert "slots_base holds" in call(slots=slots[:-1])
+    assert "workspace holds" in call(ws=ws[:1])
+    assert "must be a device (cuda) tensor" in call()
+    # single-expert and down calls check their own shapes
+    with pytest.raises(ValueError, match="out holds"):
+        q4.expert_gate_up(slots, lay, x, M, H, I, torch.zeros(M * I - 1, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="mid must be a bfloat16"):
+        q4.expert_down(slots, lay, torch.zeros(M, I, dtype=torch.float32), M, H, I, torch.zeros(M, H, dtype=torch.bfloat16))

@@ -106,7 +106,7 @@ def _forward_grouped(c, slots=None):
     idt = torch.from_numpy(np.ascontiguousarray(c.ids, dtype=np.int32)).cuda()
     mid = torch.empty((M, K, c.I), dtype=torch.bfloat16, device="cuda")
     out = torch.empty((M, K, c.H), dtype=torch.bfloat16, device="cuda")
-    wsb = q4.grouped_workspace_bytes(M, K, c.H, c.I, c.num_slots)
+    wsb = q4.grouped_workspace_bytes(M, K, c.num_slots)
     ws = aligned_empty(wsb, 256)
     q4.expert_forward_grouped(slots, c.slot_stride, c.num_slots, c.layout, x, M, idt, K, c.H, c.I, mid, out, ws,
                               wsb)

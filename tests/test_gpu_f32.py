@@ -117,7 +117,7 @@ def test_f32_grouped_edges():
     out = torch.empty((M, K, c.I), dtype=torch.float32, device="cuda")
     g = torch.empty((M, K, c.I), dtype=torch.float32, device="cuda")
     u = torch.empty((M, K, c.I), dtype=torch.float32, device="cuda")
-    wsb = q4.grouped_workspace_bytes(M, K, c.H, c.I, c.num_slots)
+    wsb = q4.grouped_workspace_bytes(M, K, c.num_slots)
     ws = aligned_empty(wsb, 256)
     q4.expert_gate_up_grouped(slots, c.slot_stride, c.num_slots, c.layout, _dev(x), M, idt, K, c.H, c.I, out, ws,
                               wsb, g, u, xdtype="f32")
@@ -161,7 +161,7 @@ def test_f32_forward_grouped():
     idt = torch.from_numpy(np.ascontiguousarray(c.ids, np.int32)).cuda()
     mid = torch.empty((M, K, c.I), dtype=torch.float32, device="cuda")
     out = torch.empty((M, K, c.H), dtype=torch.float32, device="cuda")
-    wsb = q4.grouped_workspace_bytes(M, K, c.H, c.I, c.num_slots)
+    wsb = q4.grouped_workspace_bytes(M, K, c.num_slots)
     ws = aligned_empty(wsb, 256)
     q4.expert_forward_grouped(slots, c.slot_stride, c.num_slots, c.layout, _dev(x), M, idt, K, c.H, c.I, mid, out,
                               ws, wsb, xdtype="f32")

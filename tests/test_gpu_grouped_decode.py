@@ -58,7 +58,7 @@ def test_benchmark_pool_full_size(M):
     out = torch.empty((M, E, I), dtype=torch.bfloat16, device="cuda")
     g = torch.empty((M, E, I), dtype=torch.float32, device="cuda")
     u = torch.empty((M, E, I), dtype=torch.float32, device="cuda")
-    wsb = q4.grouped_workspace_bytes(M, E, H, I, E)
+    wsb = q4.grouped_workspace_bytes(M, E, E)
     ws = aligned_empty(wsb, 256)
     ws.fill_(0xAB)
     idt = torch.from_numpy(ids).cuda()
@@ -161,7 +161,7 @@ def test_decode_workspace_reuse():
     rng = np.random.default_rng(99)
     lay, slots = _pool(rng, E, H, I)
     dev = upload_slots(slots)
-    ws = aligned_empty(q4.grouped_workspace_bytes(M, K, H, I, E), 256)
+    ws = aligned_empty(q4.grouped_workspace_bytes(M, K, E), 256)
     ws.fill_(0x5A)
     for call in range(3):
         x = synth.bf16_normal(rng, (M, H))

@@ -98,7 +98,7 @@ def test_q8_forward_grouped(M, K, E):
     idt = torch.from_numpy(np.ascontiguousarray(c.ids, dtype=np.int32)).cuda()
     mid = torch.empty((Mk, Kk, c.I), dtype=torch.bfloat16, device="cuda")
     out = torch.empty((Mk, Kk, c.H), dtype=torch.bfloat16, device="cuda")
-    wsb = q4.grouped_workspace_bytes(Mk, Kk, c.H, c.I, c.num_slots)
+    wsb = q4.grouped_workspace_bytes(Mk, Kk, c.num_slots)
     ws = aligned_empty(wsb, 256)
     q4.expert_forward_grouped(slots, c.slot_stride, c.num_slots, c.layout, x, Mk, idt, Kk, c.H, c.I, mid, out, ws,
                               wsb, fmt="q8")
