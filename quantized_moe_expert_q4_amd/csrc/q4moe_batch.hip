@@ -25,6 +25,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "q4moe_device.h"
 #include "q4moe_launch.h"
 
@@ -74,7 +76,7 @@ void batch_kernel(const GateUpParams a) {
   __shared__ int s_xmin[G];                  // smallest non-zero exponent field of each token
   __shared__ int s_wcnt[kBatWaves];
   __shared__ int s_invalid;
-  __shared__ uint16_t s_sig[kSigTable];      // bf16 sigmoid of the tabulated gT
+  __shared__ __attribute__((aligned(16))) uint16_t s_sig[kSigTable];  // bf16 sigmoid of the tabulated gT
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -93,8 +95,9 @@ void batch_kernel(const GateUpParams a) {
   const uint32_t rbytes = row_bytes<Q8>(H);  // bytes of one weight row
   const uint32_t wbytes = (uint32_t)((uint64_t)I * rbytes);
 
+  // the device's sigmoid table, 16 bytes per thread of the first half
   if constexpr (!DOWN)
-    for (int i = tid; i < kSigTable; i += kBatThreads) s_sig[i] = sigmoid_bf16(sig_table_bits(i));
+    if (tid < kSigTable / 8) *(uint4*)(s_sig + 8 * tid) = ((const uint4*)a.sig)[tid];
 
   // ---- invalid routing ids (grouped): zero-filled by work-group 0 ----
   if (grouped && blockIdx.x == 0) {
@@ -521,9 +524,10 @@ namespace {
 
 template <int NT, bool VEC, bool DOWN, bool Q8, bool XF>
 int batch_blocks(int device) {
-  static int cached[64] = {0};
+  // per-device cache; concurrent first calls compute the same value
+  static std::atomic<int> cached[64];
   if (device < 0 || device >= 64) device = 0;
-  if (!cached[device]) {
+  if (!cached[device].load(std::memory_order_relaxed)) {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0)
       cus = 256;
@@ -531,9 +535,9 @@ int batch_blocks(int device) {
             &per_cu, reinterpret_cast<const void*>(&batch_kernel<NT, VEC, DOWN, Q8, XF>), kBatThreads, 0) != hipSuccess ||
         per_cu <= 0)
       per_cu = 1;
-    cached[device] = cus * per_cu;
+    cached[device].store(cus * per_cu, std::memory_order_relaxed);
   }
-  return cached[device];
+  return cached[device].load(std::memory_order_relaxed);
 }
 
 template <int NT, bool VEC, bool DOWN, bool Q8, bool XF>

@@ -130,8 +130,9 @@ __device__ uint16_t swiglu_tail(float gate, float up) {
 // (exponent field below 118, zeros and subnormals included) it is exactly 0.5;
 // for |gT| >= 128 (field 134 and up, infinities included) it is 1 for positive
 // and +0 for negative gT; NaN stays NaN.  The 4096 values in between are
-// tabulated once per work-group (kSigTable entries: sign, field 118..133,
-// 7-bit mantissa), which keeps the double exp out of the per-row tail.
+// tabulated once per device (kSigTable entries: sign, field 118..133, 7-bit
+// mantissa) and copied into LDS by each work-group, which keeps the double
+// exp out of the per-row tail.
 constexpr int kSigTable = 2 * 16 * 128;
 
 __device__ __forceinline__ uint16_t sig_table_bits(int i) {
@@ -195,6 +196,12 @@ __device__ __forceinline__ void wave_sync() {
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes at byte offset off through a buffer resource (zeros past its end).
+__device__ __forceinline__ uint4 load_u4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 // A buffer offset past every weight array (projections are below 2^31 bytes):

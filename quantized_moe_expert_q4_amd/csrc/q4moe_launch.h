@@ -27,7 +27,12 @@ struct GateUpParams {
   int down;                  // 1: down projection (see above)
   int q8;                    // 1: signed int8 weights [rows][H] (else packed nibbles [rows][H/8] words)
   int xf32;                  // 1: x and out are float32 (else bf16); probes unchanged
+  const uint16_t* sig;       // set by the launchers: the device's bf16 sigmoid table (sigmoid_table)
 };
+
+// The bf16 sigmoid table of the SwiGLU tail on the current device
+// (kSigTable entries, see q4moe_device.h), built on first use.
+hipError_t sigmoid_table(const uint16_t** table);
 
 // Resident-digits kernel for token groups of at most two (decode widths):
 // true when the whole-K digits of `M_per_slot` tokens fit its LDS buffer.

@@ -11,22 +11,32 @@
 // result and recombine with quad shuffles, without LDS.  NT 16-column tiles
 // hold 16*NT/W tokens; a call with more tokens than that takes several passes
 // over its weights (only with W = 8 and more than 16*NT/8 tokens).
-//  * One persistent launch, one 8-wave work-group per CU: work-group b takes
-//    the whole tiles [bT/NB, (b+1)T/NB) of the T = slots x tiles-per-slot tiles.
-//  * Inside a work-group the (tile, K-step) units of a slot segment are cut
-//    into eight wave ranges (multiples of D steps; the first wave of each
-//    SIMD takes a little more, see wave_share).  Each wave streams its own
-//    units with D K-steps of weights in flight in a register ring; the first
-//    loads of a segment go out before its routing scan and, in the first
-//    segment, before x is split.
+//  * Routing: a grouped call over at most kBitSlots slots first builds, in
+//    every work-group, the bitmap of the slots its ids name; the tiles of
+//    the routed slots only (T = routed slots x tiles per slot) are then cut
+//    into whole-tile ranges, work-group b taking [bT/NB, (b+1)T/NB).  With
+//    more slots every slot counts as routed.
+//  * One persistent launch, one 8-wave work-group per CU.  The slots a
+//    work-group's range touches (its segments, up to kMaxSeg at a time: a
+//    round) are listed in LDS with, for each token, its first routed pair and
+//    pair count there.  The (tile, K-step) units of a round are cut into
+//    eight wave ranges (multiples of four steps; the first wave of each SIMD
+//    takes a little more, see wave_share).  Each wave streams its range with
+//    D K-steps of weights in flight in a register ring that runs on across
+//    tile and slot boundaries; nothing synchronises the waves inside a round.
+//  * The first weight loads go out as soon as the round's slots are known,
+//    before x is split into digits; x is held in registers from the start.
 //  * A tile cut by a wave boundary has several contributors; each adds its
 //    exact quad sums into an LDS fix-up slot with LDS atomics and bumps the
-//    slot's counter; the last one to arrive finishes the tile.  No wave waits
-//    on another inside a segment.
-//  * K-steps per tile are padded to a multiple of D; the padding steps meet
-//    zero digits, so they add nothing.
+//    slot's counter; the last one to arrive finishes the tile.
+//  * K-steps per tile are padded to a multiple of four; the padding steps
+//    meet zero digits, so they add nothing.
+//  * Pairs with an id outside [0, num_slots) get zero outputs; each
+//    work-group zero-fills its share of them once its tiles are done.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <atomic>
 
 #include "q4moe_device.h"
 #include "q4moe_launch.h"
@@ -40,17 +50,23 @@ constexpr int kResThreads = kResWaves * 64;
 #ifndef Q4_RES_DEPTH
 #define Q4_RES_DEPTH 4
 #endif
-// K-steps of weights in flight per wave (1, 2 or 4).
-__host__ __device__ constexpr int res_depth(int nt, bool q8) { return (void)nt, (void)q8, Q4_RES_DEPTH; }
+// K-steps of weights in flight per wave (1, 2 or 4): two for int8 weights
+// with f32 activations at two column tiles (four would spill), else four.
+__host__ __device__ constexpr int res_depth(int nt, bool q8, bool xf) {
+  return (q8 && xf && nt == 2 && Q4_RES_DEPTH > 2) ? 2 : Q4_RES_DEPTH;
+}
 // K-steps per pass of the step loop: the B-fragment swizzle repeats every
 // four steps, so four steps per pass keep its offsets fixed.
 constexpr int kResU = 4;
-constexpr int kResLds = 150 * 1024;        // digits, then the fix-up slots
-constexpr int kResXRegs = 8;               // 16-byte chunks of x held per thread while splitting
+constexpr int kResLds = 144 * 1024;        // digits, then the fix-up slots
+constexpr int kResXRegs = 8;               // 16-byte chunks of x held per thread
 constexpr int kResMaxTokens = 8;           // tokens per call
-constexpr int kResMaxPairs = 16;           // routed pairs finished per pass over a slot
 constexpr int kResFixSlots = kResWaves - 1;
 constexpr int kResIdRegs = 4;              // routing ids held per thread (2048 pairs)
+constexpr int kBitSlots = 2048;            // slots a routing bitmap covers
+constexpr int kBitWords = kBitSlots / 32;
+constexpr int kMaxSeg = 64;                // slots per round
+constexpr int kInvBatch = 64;              // invalid pairs zero-filled per batch
 
 // One K-step of digits: [parity 2][column tile n][k-group g 4][16 x 16 bytes]
 // ([plane 4][...] for wide steps).
@@ -64,12 +80,28 @@ __host__ __device__ constexpr int res_chunk(int g, int c, int step) { return g *
 __host__ __device__ constexpr int res_fix_words(int nt) { return nt * 2 * 64; }
 // K-steps per tile, padded to whole passes of the step loop.
 __host__ __device__ constexpr int res_steps(int H, int kps = 128) { return ((H + kps - 1) / kps + kResU - 1) / kResU * kResU; }
-// Wide K-steps (256 packed nibbles per row, four operand planes) for one
-// column tile of Q4 weights and bf16 activations: rows are read 128 bytes per
-// step (measured: the same bytes stream ~3-6% faster than 64 bytes per step).
+// Wide K-steps (256 packed nibbles per row, four operand planes) for Q4
+// weights and bf16 activations: rows are read 128 bytes per step (measured:
+// the same bytes stream ~3-6% faster than 64 bytes per step).
 __host__ __device__ constexpr bool res_wide(int nt, bool q8, bool xf) { return (void)nt, !q8 && !xf; }
 // Column tiles for a call of M tokens: one up to two tokens, else two.
 __host__ __device__ constexpr int res_tiles(int M) { return M <= 2 ? 1 : 2; }
+
+// Inclusive sum of v over the lanes of a wave, up to lane `lane`.
+__device__ __forceinline__ int wave_incl_sum(int v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(v, d);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// Bit position of the j-th (from 0) set bit of w; j < popcount(w).
+__device__ __forceinline__ int nth_set_bit(uint32_t w, int j) {
+  for (int i = 0; i < j; ++i) w &= w - 1u;
+  return __builtin_ctz(w);
+}
 
 }  // namespace
 
@@ -81,20 +113,33 @@ __host__ __device__ constexpr int res_tiles(int M) { return M <= 2 ? 1 : 2; }
 template <int NT, bool VEC, bool DOWN, bool Q8, bool XF>
 __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void resident_kernel(const GateUpParams a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_lds[kResLds];
-  __shared__ int s_pairs[kResMaxPairs];
-  __shared__ int s_ptok[kResMaxPairs];       // token of each pair, relative to the pass
+  __shared__ __attribute__((aligned(16))) uint16_t s_sig[kSigTable];  // bf16 sigmoid of the tabulated gT
   __shared__ int s_xmax[kResMaxTokens];
   __shared__ int s_xmin[kResMaxTokens];      // smallest non-zero exponent field of each token
-  __shared__ int s_wcnt[kResWaves];
+  __shared__ uint32_t s_bits[kBitWords];     // routed slots
+  __shared__ int s_first[kMaxSeg][kResMaxTokens];  // first pair of token t on segment k
+  __shared__ int s_cnt[kMaxSeg][kResMaxTokens];    // pairs of token t on segment k
   __shared__ int s_fixcnt[kResFixSlots];
-  __shared__ int s_bound[kResWaves + 1];     // unit ranges of the segment, by position
-  __shared__ int s_invalid;
-  __shared__ uint16_t s_sig[kSigTable];      // bf16 sigmoid of the tabulated gT
+  __shared__ int s_bound[kResWaves + 1];     // unit ranges of the round, by position
+  __shared__ int s_inv;
+  __shared__ int s_ninv;
+  __shared__ int s_invl[kInvBatch];
 
-  constexpr int kResD = res_depth(NT, Q8);
+  constexpr int kResD = res_depth(NT, Q8, XF);
   constexpr bool WIDE = res_wide(NT, Q8, XF);
   constexpr bool WL = Q8 || WIDE;            // 32 bytes per lane and step
   constexpr int NPL = WIDE ? 4 : 2;          // operand planes per step
+  constexpr bool xf = XF;
+  // x held in registers from the start and the first weights in flight
+  // before it is split (f32 activations: split first, then the weights)
+  constexpr bool RING_FIRST = !XF;
+  // Every argument is read here, in one batch of scalar loads: left to the
+  // compiler, the fields arrive in several dependent round trips spread over
+  // the prologue.
+  asm volatile("" ::"s"(a.slots), "s"(a.slot_stride), "s"(a.gate_w_off), "s"(a.up_w_off), "s"(a.gate_s_off),
+               "s"(a.up_s_off), "s"(a.x), "s"(a.ids), "s"(a.out), "s"(a.gate_probe), "s"(a.up_probe),
+               "s"(a.invalid_count), "s"(a.M), "s"(a.K), "s"(a.H), "s"(a.I), "s"(a.num_slots), "s"(a.steps),
+               "s"(a.wave_share), "s"(a.sig), "s"(gridDim.x));
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -102,98 +147,119 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int H = a.H, I = a.I, M = a.M, K = a.K;
   const int P = M * K;
   const bool grouped = a.ids != nullptr;
-  constexpr bool xf = XF;
-  const int S = a.steps;                     // K-steps per tile, a multiple of D
+  const int S = a.steps;                     // K-steps per tile, a multiple of 4
   const int sbytes = res_step_bytes(NT, NPL);
   const int hw = H / 8;                      // 16-byte chunks of one token's x
+  const int npr = (hw + 1) / 2;              // chunk pairs of one token's x
   constexpr int RT = DOWN ? 32 : 16;         // rows per tile
   const int tps = (I + RT - 1) / RT;         // tiles per slot
-  const int T = a.num_slots * tps;
   const int NB = gridDim.x;
-  const int v0 = (int)((int64_t)blockIdx.x * T / NB), v1 = (int)((int64_t)(blockIdx.x + 1) * T / NB);
   const uint32_t rbytes = row_bytes<Q8>(H);  // bytes of one weight row
   const uint32_t wbytes = (uint32_t)((uint64_t)I * rbytes);
-  const uint64_t below = (1ull << lane) - 1ull;
   unsigned long long* const s_fix = (unsigned long long*)(s_lds + S * sbytes);
 
-  // routing ids of the first pairs, read once, before any weight load
+  // ---- routing ids, the sigmoid table and x, loaded before anything waits ----
+  // (unconditional buffer loads: lanes past the data read zeros without a
+  // memory access, and the compiler's wait counts stay exact)
+  const __amdgpu_buffer_rsrc_t idsrc = make_rsrc(a.ids, grouped ? (uint32_t)P * 4u : 0u);
   int idr[kResIdRegs];
 #pragma unroll
   for (int j = 0; j < kResIdRegs; ++j) {
     const int p = tid + j * kResThreads;
-    idr[j] = (grouped && p < P) ? a.ids[p] : -1;
+    const int v = (int)__builtin_amdgcn_raw_buffer_load_b32(idsrc, p * 4, 0, 0);
+    idr[j] = p < P ? v : -1;
   }
-
-  if (tid < kResMaxTokens) {
-    s_xmax[tid] = 0;
-    s_xmin[tid] = 255;
-  }
-  if (tid == 0) s_invalid = 0;
-  __syncthreads();
-
-  // ---- invalid routing ids (grouped): zero-filled by work-group 0 ----
-  if (grouped && blockIdx.x == 0) {
-    int cnt = 0;
-    for (int p = tid; p < P; p += kResThreads) {
-      const int e = a.ids[p];
-      if (e < 0 || e >= a.num_slots) {
-        ++cnt;
-        for (int r = 0; r < I; ++r) {
-          const uint64_t o = (uint64_t)p * I + r;
-          if (xf)
-            ((float*)a.out)[o] = 0.0f;
-          else
-            a.out[o] = 0;
-          if (a.gate_probe) a.gate_probe[o] = 0.0f;
-          if (a.up_probe) a.up_probe[o] = 0.0f;
-        }
-      }
-    }
-    if (cnt) atomicAdd(&s_invalid, cnt);
-    __syncthreads();
-    if (tid == 0 && a.invalid_count) *a.invalid_count = s_invalid;
-  }
-
-  // ---- x of every token, loaded before any weight load ----
+  // the device's sigmoid table, 16 bytes per thread
+  static_assert(kSigTable * 2 == 16 * kResThreads, "one 16-byte piece of the sigmoid table per thread");
+  const uint4 sigv = DOWN ? make_uint4(0, 0, 0, 0) : load_u4(make_rsrc(a.sig, kSigTable * 2), tid * 16u);
+  // wide steps: chunk pairs u = m * npr + r (chunks 2r, 2r+1 of token m),
+  // u = tid + k * kResThreads; else chunks q = m * hw + w8
+  const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(a.x, xf ? 0u : (uint32_t)M * (uint32_t)H * 2u);
   uint4 xv[kResXRegs];
-  const int nxc = M * hw;
+  if constexpr (WIDE) {
 #pragma unroll
-  for (int j = 0; j < kResXRegs; ++j) {
-    const int q = tid + j * kResThreads;
-    xv[j] = (!xf && q < nxc) ? ((const uint4*)a.x)[q] : make_uint4(0, 0, 0, 0);
+    for (int k = 0; k < kResXRegs / 2; ++k) {
+      const int u = tid + k * kResThreads;
+      const int m = u / npr, r = u - m * npr;
+      const bool live = u < M * npr;
+      const uint32_t o0 = live ? (uint32_t)(m * hw + 2 * r) * 16u : kOffNone;
+      const uint32_t o1 = (live && 2 * r + 1 < hw) ? o0 + 16u : kOffNone;
+      xv[2 * k] = load_u4(xsrc, o0);
+      xv[2 * k + 1] = load_u4(xsrc, o1);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kResXRegs; ++j) {
+      const int q = tid + j * kResThreads;
+      xv[j] = load_u4(xsrc, q < M * hw ? (uint32_t)q * 16u : kOffNone);
+    }
   }
-  // chunk q (8 consecutive values) of f32 activations: two 16-byte loads
-  auto xf_chunk = [&](int q, uint4& lo4, uint4& hi4) {
-    const uint4* xp = (const uint4*)((const float*)a.x + 8 * (size_t)q);
-    lo4 = xp[0];
-    hi4 = xp[1];
-  };
 
-  // ---- the current slot segment: tiles [t0, t1) of slot e ----
-  int v = v0;
-  int e = 0, t0 = 0, t1 = 0, nunits = 0, ua = 0, ub = 0;
-  __amdgpu_buffer_rsrc_t gsrc, usrc;
-  const float* gscale = nullptr;
-  const float* uscale = nullptr;
+  // ---- tiles of the routed slots: whole-tile ranges per work-group ----
+  const bool compact = grouped && a.num_slots <= kBitSlots;
+  int R = grouped ? a.num_slots : 1;         // routed slots
+  int v0 = 0, v1 = 0;
+  // the current round: tiles [vr0, vr1), routed slots ra .. ra+nseg-1
+  int vr0 = 0, vr1 = 0, ra = 0, nseg = 0, N = 0;
+  auto tile_split = [&]() {
+    const uint32_t T = (uint32_t)R * (uint32_t)tps;
+    auto at = [&](uint32_t b) {
+      const uint64_t n = (uint64_t)b * T;
+      return (int)(n < 0x100000000ull ? (uint32_t)n / (uint32_t)NB : n / (uint32_t)NB);
+    };
+    v0 = at(blockIdx.x);
+    v1 = at(blockIdx.x + 1);
+    vr0 = v0;                                // the first round starts the range
+  };
+  // routing bitmap held by every wave (see below); before it is known the
+  // slots are taken as all routed
+  uint32_t wbits = 0u;
+  int wpre = 0;
+  bool known = !compact;                     // slot mapping final
+  // slot of routed index r (wave-uniform, r < R)
+  auto select = [&](int r) {
+    if (!grouped) return 0;
+    if (!compact || !known) return r;
+    const uint64_t bal = __ballot(wpre <= r && r < wpre + (int)__popc(wbits));
+    const int l = (int)__builtin_ctzll(bal);
+    const uint32_t bits = (uint32_t)__builtin_amdgcn_readlane((int)wbits, l);
+    return 32 * l + nth_set_bit(bits, r - __builtin_amdgcn_readlane(wpre, l));
+  };
+  // ---- the current round: tiles [vr0, vr1), routed slots ra .. ra+nseg-1 ----
   // Unit range start of position k (0..8).  The units are cut into four equal
   // quarters, one per SIMD; quarter q goes to waves q (first on its SIMD,
   // which wins the SIMD's issue arbitration more often) and q + 4, the first
   // taking wave_share/1024.  Position k = 2*(wave % 4) + wave / 4 orders the
   // ranges by unit.
   auto bound = [&](int k) {
-    if (k >= kResWaves) return nunits;
+    if (k >= kResWaves) return N;
     const int q = k >> 1;
-    const int qa = (int)(((int64_t)q * nunits / 4) / kResU * kResU);
+    const int qa = (int)(((int64_t)q * N / 4) / kResU * kResU);
     if (!(k & 1)) return qa;
-    const int qb = q == 3 ? nunits : (int)(((int64_t)(q + 1) * nunits / 4) / kResU * kResU);
+    const int qb = q == 3 ? N : (int)(((int64_t)(q + 1) * N / 4) / kResU * kResU);
     return qa + (int)(((int64_t)(qb - qa) * a.wave_share / 1024) / kResU * kResU);
   };
   const int wpos = 2 * (wave & 3) + (wave >> 2);
-  auto open_segment = [&]() {
-    e = v / tps;
-    t0 = v - e * tps;
-    t1 = min(v1, (e + 1) * tps) - e * tps;
-    v = e * tps + t1;
+  int ua = 0, ub = 0;
+  // the round's extent and this wave's unit range (no LDS)
+  auto open_round = [&]() {
+    ra = vr0 / tps;
+    nseg = vr0 < v1 ? min(kMaxSeg, (v1 - 1) / tps - ra + 1) : 0;
+    vr1 = min(v1, (ra + nseg) * tps);
+    N = (vr1 - vr0) * S;
+    ua = bound(wpos);
+    ub = bound(wpos + 1);
+  };
+  // ---- weight load cursor: round tile lt, step ls, segment lk ----
+  auto row_off = [&](int t) {
+    const int row = t * RT + cc;
+    return (uint32_t)(row < I ? row : I - 1) * rbytes + (uint32_t)g4 * group_bytes<WL>();
+  };
+  // (an empty resource until a slot is set: every load through it returns
+  // zeros without a memory access)
+  __amdgpu_buffer_rsrc_t gsrc = make_rsrc(a.slots, 0u), usrc = make_rsrc(a.slots, 0u);
+  auto set_slot = [&](int k) {                // segment k of the round
+    const int e = select(ra + k);
     const uint8_t* slot = a.slots + (uint64_t)e * a.slot_stride;
     gsrc = make_rsrc(slot + a.gate_w_off, wbytes);
     if constexpr (DOWN) {
@@ -204,44 +270,162 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
     } else {
       usrc = make_rsrc(slot + a.up_w_off, wbytes);
     }
-    gscale = (const float*)(slot + a.gate_s_off);
-    uscale = (const float*)(slot + a.up_s_off);
-    nunits = (t1 - t0) * S;
-    ua = bound(wpos);
-    ub = bound(wpos + 1);
-  };
-
-  auto row_off = [&](int tile) {
-    const int row = tile * RT + cc;
-    return (uint32_t)(row < I ? row : I - 1) * rbytes + (uint32_t)g4 * group_bytes<WL>();
   };
   StepW<WL> rg[kResD], ru[kResD];
-  int lt = 0, ls = 0;                        // load cursor (tile, step)
+  int ls = 0, lt = 0, lk = 0;                // load cursor: step, tile in slot, segment
   uint32_t loff = 0;
+  auto seek = [&](int w) {                   // cursor to round tile w
+    const int r = (vr0 + w) / tps;
+    lk = r - ra;
+    lt = vr0 + w - r * tps;
+    set_slot(lk);
+    loff = row_off(lt);
+  };
   auto issue = [&](StepW<WL>& g, StepW<WL>& u_, bool live, uint32_t dep = 0u) {
     const uint32_t o = (live ? loff + (uint32_t)ls * step_row_bytes<WL>() : kOffNone) + dep;
     load_step<WL, VEC>(g, gsrc, o);
     load_step<WL, VEC>(u_, usrc, o);
-    // cursor step without branches, so the loads stay unconditional
+    // cursor step after the loads: next tile every S steps, next slot every
+    // tps tiles (its resources reloaded then)
     const int nls = ls + (live ? 1 : 0);
-    const bool wrap = nls == S;
-    ls = wrap ? 0 : nls;
-    lt += wrap ? 1 : 0;
-    loff = wrap ? row_off(lt) : loff;
+    if (nls == S) {
+      ls = 0;
+      if (++lt == tps) {
+        lt = 0;
+        if (++lk < nseg) set_slot(lk);
+      }
+      loff = row_off(lt);
+    } else {
+      ls = nls;
+    }
   };
   // The ring always holds D loads per array: slots past the wave's range
   // load nothing (kOffNone) and are never consumed.
   auto start_ring = [&]() {
-    lt = t0 + ua / S;
-    ls = ua % S;
-    loff = row_off(lt);
+    const int w = ua / S;
+    ls = ua - w * S;
+    if (ua < ub) seek(w);
 #pragma unroll
     for (int d = 0; d < kResD; ++d) issue(rg[d], ru[d], ua + d < ub);
+  };
+
+  // With the slot mapping known up front (a single expert, more slots than
+  // one bitmap covers) or likely to be the identity (at least as many pairs
+  // as slots), the first weights go out before the ids have arrived.
+  const bool spec = compact && P >= a.num_slots;
+  const bool early = blockIdx.y == 0 && (known || spec);
+  if (early) {
+    tile_split();
+    open_round();
+    if constexpr (RING_FIRST) start_ring();
+  }
+
+  if (tid < kResMaxTokens) {
+    s_xmax[tid] = 0;
+    s_xmin[tid] = 255;
+  }
+  if (tid == 0) s_inv = 0;
+  const int nw = (a.num_slots + 31) >> 5;
+  if (compact && tid < nw) s_bits[tid] = 0;
+  // empty pair tables of the first round: one entry per thread
+  static_assert(kMaxSeg * kResMaxTokens == kResThreads, "one pair-table entry per thread");
+  auto clear_tables = [&]() {
+    s_first[tid / kResMaxTokens][tid % kResMaxTokens] = 0x7FFFFFFF;
+    s_cnt[tid / kResMaxTokens][tid % kResMaxTokens] = 0;
+  };
+  clear_tables();
+  __syncthreads();
+
+  // ---- routed slots: bitmap, routed count R, invalid-id count ----
+  // Every wave then holds the bitmap (word l in lane l) and, per word, the
+  // routed slots before it, so that it finds the slot of a routed index or
+  // the routed index of a slot by itself, without LDS or barriers.
+  if (grouped) {
+    int inv = 0;
+    auto post = [&](int id) {
+      if (id >= 0 && id < a.num_slots) {
+        if (compact) atomicOr(&s_bits[id >> 5], 1u << (id & 31));
+      } else {
+        ++inv;
+      }
+    };
+#pragma unroll
+    for (int j = 0; j < kResIdRegs; ++j)
+      if (tid + j * kResThreads < P) post(idr[j]);
+    for (int p = tid + kResIdRegs * kResThreads; p < P; p += kResThreads) post(a.ids[p]);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && inv) atomicAdd(&s_inv, inv);
+    __syncthreads();
+    if (compact) {
+      wbits = lane < nw ? s_bits[lane] : 0u;
+      const int c = (int)__popc(wbits);
+      const int incl = wave_incl_sum(c, lane);
+      wpre = incl - c;
+      R = __builtin_amdgcn_readlane(incl, 63);
+    }
+    if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0 && a.invalid_count) *a.invalid_count = s_inv;
+  }
+  known = true;
+  // the routed index of a routed slot id (per lane; the shuffles read other
+  // lanes: every lane of the wave must be active)
+  auto rank = [&](int id) {
+    if (!compact) return id;
+    const int w = id >> 5;
+    const uint32_t bits = (uint32_t)__shfl((int)wbits, w);
+    return __shfl(wpre, w) + (int)__popc(bits & ((1u << (id & 31)) - 1u));
+  };
+
+  if (early && R != (grouped ? a.num_slots : 1)) {
+    // some slot is not routed: the weights in flight belong to the identity
+    // mapping; let them land, then start over on the routed slots
+    __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+    tile_split();
+    open_round();
+    if constexpr (RING_FIRST) start_ring();
+  } else if (!early) {
+    tile_split();
+  }
+
+  // pairs of the round's slots (into cleared tables), unit bounds, cleared
+  // fix-up slots (visible after the next barrier)
+  auto fill_round = [&]() {
+    if (!grouped) {
+      if (tid < M) {
+        s_first[0][tid] = tid;
+        s_cnt[0][tid] = 1;
+      }
+    } else {
+      // called with every lane active (rank shuffles); only the table
+      // updates depend on the lane's pair
+      auto put = [&](int p, int id) {
+        const bool valid = p < P && id >= 0 && id < a.num_slots;
+        const int k = rank(valid ? id : 0) - ra;
+        if (valid && k >= 0 && k < nseg) {
+          const int t = p / K;
+          atomicMin(&s_first[k][t], p);
+          atomicAdd(&s_cnt[k][t], 1);
+        }
+      };
+#pragma unroll
+      for (int j = 0; j < kResIdRegs; ++j) put(tid + j * kResThreads, idr[j]);
+      for (int base = kResIdRegs * kResThreads; base < P; base += kResThreads) {
+        const int p = base + tid;
+        put(p, p < P ? a.ids[p] : -1);
+      }
+    }
+    if (tid <= kResWaves) s_bound[tid] = bound(tid);
+    if (tid < kResFixSlots) s_fixcnt[tid] = 0;
+    for (int i = tid; i < kResFixSlots * res_fix_words(NT); i += kResThreads) s_fix[i] = 0;
   };
 
   // digits per value and columns per token, fixed once x has been read
   int L = 6, W = 8;
   auto etop = [&](int m) { return xf ? max((s_xmax[m] >> 23) & 0xFF, 1) : max((s_xmax[m] >> 7) & 0xFF, 1); };
+  // chunk q (8 consecutive values) of f32 activations: two 16-byte loads
+  auto xf_chunk = [&](int q, uint4& lo4, uint4& hi4) {
+    const uint4* xp = (const uint4*)((const float*)a.x + 8 * (size_t)q);
+    lo4 = xp[0];
+    hi4 = xp[1];
+  };
   // digits of chunk w8 (8 consecutive K values) of pass token tl
   auto stage_unit4 = [&](int tl, int w8, const uint4 xq, int etop1) {
     const int st = w8 >> 4, gg = (w8 >> 2) & 3, i = w8 & 3;
@@ -353,68 +537,147 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
     }
   };
 
-  // ---- the digits of the first pass, then the first segment's weights in flight ----
-  // (x is split before any weight load is issued: a load issued after the ring,
-  // such as a rematerialised x chunk, would wait for the whole ring to arrive)
-  // largest |x| and smallest non-zero exponent of each token.  When a token's
-  // chunks fill whole waves (hw % 64 == 0), each wave's 64 chunks of x
-  // register j belong to one token: the sixteen wave reductions (DPP, no
-  // branches, so the scheduler interleaves them) go to lane 0, which posts
-  // them; otherwise every lane posts its own values.
-  if (xf) {
-    // f32: a rolled loop over the chunks, wave reductions when a wave's
-    // chunks belong to one token
+
+  // ---- range of every token's x: largest |x| and smallest non-zero exponent ----
+  // (register j or pair k of a lane belongs to one token for the whole wave
+  // when a token's units fill whole waves: sixteen DPP wave reductions go to
+  // lane 0, which posts them; otherwise every lane posts its own values)
+  auto post_range = [&](int m, uint32_t mx, uint32_t mn) {
+    if (mx) atomicMax(&s_xmax[m], (int)mx);
+    if (mn < 255) atomicMin(&s_xmin[m], (int)mn);
+  };
+  auto x_range = [&]() {
+    if constexpr (XF) {
 #pragma unroll 1
-    for (int q = tid; q < (nxc + 63) / 64 * 64; q += kResThreads) {
-      uint32_t mx = 0, mn = 255;
-      if (q < nxc) {
-        uint4 xa, xb;
-        xf_chunk(q, xa, xb);
-        f32_range8(xa, xb, mx, mn);
-      }
-      if (hw % 64 == 0) {
-        mx = wave_extreme<true>(mx);
-        mn = wave_extreme<false>(mn);
-        if (lane == 0 && q < nxc) {
-          const int m = q / hw;
-          if (mx) atomicMax(&s_xmax[m], (int)mx);
-          if (mn < 255) atomicMin(&s_xmin[m], (int)mn);
+      for (int q = tid; q < (M * hw + 63) / 64 * 64; q += kResThreads) {
+        uint32_t mx = 0, mn = 255;
+        if (q < M * hw) {
+          uint4 xa, xb;
+          xf_chunk(q, xa, xb);
+          f32_range8(xa, xb, mx, mn);
         }
-      } else if (q < nxc) {
-        const int m = q / hw;
-        if (mx) atomicMax(&s_xmax[m], (int)mx);
-        if (mn < 255) atomicMin(&s_xmin[m], (int)mn);
-      }
-    }
-  } else {
-    // registers past the last chunk in every lane (j * threads >= nxc, the
-    // same for the whole work-group) are skipped; lanes past it hold zeros,
-    // whose range (0, 255) posts nothing
-#pragma unroll
-    for (int j = 0; j < kResXRegs; ++j) {
-      if (j * kResThreads < nxc) {
-        uint32_t mx, mn;
-        range8(xv[j], mx, mn);
         if (hw % 64 == 0) {
           mx = wave_extreme<true>(mx);
           mn = wave_extreme<false>(mn);
-          const int q0 = j * kResThreads + (tid & ~63);
-          if (lane == 0 && q0 < nxc) {
-            const int m = q0 / hw;
-            if (mx) atomicMax(&s_xmax[m], (int)mx);
-            if (mn < 255) atomicMin(&s_xmin[m], (int)mn);
+          if (lane == 0 && q < M * hw) post_range(q / hw, mx, mn);
+        } else if (q < M * hw) {
+          post_range(q / hw, mx, mn);
+        }
+      }
+    } else if constexpr (WIDE) {
+#pragma unroll
+      for (int k = 0; k < kResXRegs / 2; ++k) {
+        if (k * kResThreads < M * npr) {
+          uint32_t mx, mn, mx2, mn2;
+          range8(xv[2 * k], mx, mn);
+          range8(xv[2 * k + 1], mx2, mn2);
+          mx = max(mx, mx2);
+          mn = min(mn, mn2);
+          if (npr % 64 == 0) {
+            mx = wave_extreme<true>(mx);
+            mn = wave_extreme<false>(mn);
+            const int u0 = k * kResThreads + (tid & ~63);
+            if (lane == 0 && u0 < M * npr) post_range(u0 / npr, mx, mn);
+          } else {
+            const int u = tid + k * kResThreads;
+            if (u < M * npr) post_range(u / npr, mx, mn);
           }
-        } else {
-          const int q = tid + j * kResThreads;
-          if (q < nxc) {
-            const int m = q / hw;
-            if (mx) atomicMax(&s_xmax[m], (int)mx);
-            if (mn < 255) atomicMin(&s_xmin[m], (int)mn);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kResXRegs; ++j) {
+        if (j * kResThreads < M * hw) {
+          uint32_t mx, mn;
+          range8(xv[j], mx, mn);
+          if (hw % 64 == 0) {
+            mx = wave_extreme<true>(mx);
+            mn = wave_extreme<false>(mn);
+            const int q0 = j * kResThreads + (tid & ~63);
+            if (lane == 0 && q0 < M * hw) post_range(q0 / hw, mx, mn);
+          } else {
+            const int q = tid + j * kResThreads;
+            if (q < M * hw) post_range(q / hw, mx, mn);
           }
         }
       }
     }
+  };
+
+  // ---- digits of the pass's tokens [p0, p0 + ntok) ----
+  // from the registers (f32: from memory); the padding K-steps get zero digits
+  auto stage_pass = [&](int p0, int ntok) {
+    if constexpr (WIDE) {
+      // a rolled loop over the held pairs, picked by a uniform branch (one
+      // unit's temporaries at a time while x and the weight ring hold their
+      // registers); units of token m are [m * npr, (m + 1) * npr)
+#pragma unroll 1
+      for (int k = 0; k < kResXRegs / 2 && k * kResThreads < (p0 + ntok) * npr; ++k) {
+        uint4 xa = xv[0], xb = xv[1];
+        if (k == 1) {
+          xa = xv[2];
+          xb = xv[3];
+        } else if (k == 2) {
+          xa = xv[4];
+          xb = xv[5];
+        } else if (k == 3) {
+          xa = xv[6];
+          xb = xv[7];
+        }
+        const int u = tid + k * kResThreads;
+        const int m = u / npr;
+        if (m >= p0 && m < p0 + ntok) stage_pair(m - p0, u - m * npr, xa, xb, etop(m));
+      }
+      const int padp = S * 16 - npr;
+#pragma unroll 1
+      for (int u = tid; u < ntok * padp; u += kResThreads)
+        stage_pair(u % ntok, npr + u / ntok, make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), 1);
+    } else {
+      if (xf) {
+#pragma unroll 1
+        for (int q = tid; q < ntok * hw; q += kResThreads) {
+          const int tl = q / hw;
+          uint4 xa, xb;
+          xf_chunk((p0 + tl) * hw + q - tl * hw, xa, xb);
+          stage_unitf(tl, q - tl * hw, xa, xb, etop(p0 + tl));
+        }
+      } else {
+#pragma unroll 1
+        for (int j = 0; j < kResXRegs && j * kResThreads < (p0 + ntok) * hw; ++j) {
+          uint4 xq = xv[0];
+          if (j == 1) xq = xv[1];
+          else if (j == 2) xq = xv[2];
+          else if (j == 3) xq = xv[3];
+          else if (j == 4) xq = xv[4];
+          else if (j == 5) xq = xv[5];
+          else if (j == 6) xq = xv[6];
+          else if (j == 7) xq = xv[7];
+          const int q = tid + j * kResThreads;
+          const int m = q / hw;
+          if (m >= p0 && m < p0 + ntok) stage_unit(m - p0, q - m * hw, xq, etop(m));
+        }
+      }
+      const int padw = S * 16 - hw;
+#pragma unroll 1
+      for (int u = tid; u < ntok * padw; u += kResThreads) {
+        if (xf)
+          stage_unitf(u % ntok, hw + u / ntok, make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), 1);
+        else
+          stage_unit(u % ntok, hw + u / ntok, make_uint4(0, 0, 0, 0), 1);
+      }
+    }
+  };
+
+  // ---- prologue: first round's slots, its weights in flight, digits ----
+  // pass = blockIdx.y: the tokens [pass * tpp, (pass + 1) * tpp) of a call
+  // with more tokens than one pass holds (launched with as many y slices as
+  // six-digit tokens would need; a slice with nothing to do exits here)
+  const int pass = blockIdx.y;
+  if (pass == 0 && !early) {
+    open_round();
+    if constexpr (RING_FIRST) start_ring();
   }
+  x_range();
   __syncthreads();
   {
     int l = 4;
@@ -423,84 +686,18 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
   }
   W = L == 4 ? 4 : 8;
   const int tpp = 16 * NT / W;                              // tokens per pass
-  const int npass = (M + tpp - 1) / tpp;
-  if constexpr (WIDE) {
-    // wide steps: unit pairs (16 values, one dword of every plane and digit
-    // column) over the whole padded K range, so the padding gets zero digits
-    const int ntok = min(M, tpp);
-    const int npair = S * 16;
-    // up to four pairs per thread and pass of this loop, their loads issued
-    // together (one round trip instead of four)
-    constexpr int kPairs = 4;
-#pragma unroll 1
-    for (int u0 = tid; u0 < ntok * npair; u0 += kPairs * kResThreads) {
-      uint4 xa[kPairs], xb[kPairs];
-#pragma unroll
-      for (int k = 0; k < kPairs; ++k) {
-        const int u = u0 + k * kResThreads;
-        const int m = u / npair, w8 = 2 * (u - m * npair);
-        const bool live = u < ntok * npair;
-        xa[k] = (live && w8 < hw) ? ((const uint4*)a.x)[m * hw + w8] : make_uint4(0, 0, 0, 0);
-        xb[k] = (live && w8 + 1 < hw) ? ((const uint4*)a.x)[m * hw + w8 + 1] : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int k = 0; k < kPairs; ++k) {
-        const int u = u0 + k * kResThreads;
-        if (u < ntok * npair) {
-          const int m = u / npair;
-          stage_pair(m, u - m * npair, xa[k], xb[k], etop(m));
-        }
-      }
-    }
-  } else {
-    const int ntok = min(M, tpp);
-    // a rolled loop that reads x again (cache hits: no weight load is in
-    // flight yet), the next chunk's load in flight: the launch's setup runs
-    // once per work-group, so its straight-line code is fetched cold
-    const int nq = ntok * hw;
-    int q = tid;
-    uint4 xq = (!xf && q < nq) ? ((const uint4*)a.x)[q] : make_uint4(0, 0, 0, 0);
-    if (xf) {
-#pragma unroll 1
-      for (; q < nq; q += kResThreads) {
-        uint4 xa, xb;
-        xf_chunk(q, xa, xb);
-        const int m = q / hw;
-        stage_unitf(m, q - m * hw, xa, xb, etop(m));
-      }
-    } else if (W == 4) {
-#pragma unroll 1
-      for (; q < nq; q += kResThreads) {
-        const int qn = q + kResThreads;
-        const uint4 xn = qn < nq ? ((const uint4*)a.x)[qn] : make_uint4(0, 0, 0, 0);
-        const int m = q / hw;
-        stage_unit4(m, q - m * hw, xq, etop(m));
-        xq = xn;
-      }
-    } else {
-#pragma unroll 1
-      for (; q < nq; q += kResThreads) {
-        const int qn = q + kResThreads;
-        const uint4 xn = qn < nq ? ((const uint4*)a.x)[qn] : make_uint4(0, 0, 0, 0);
-        const int m = q / hw;
-        stage_unit8(m, q - m * hw, xq, etop(m));
-        xq = xn;
-      }
-    }
-    // zero digits for the padding steps
-    const int padw = S * 16 - hw;
-    for (int u = tid; u < ntok * padw; u += kResThreads) {
-      if (xf)
-        stage_unitf(u % ntok, hw + u / ntok, make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), 1);
-      else
-        stage_unit(u % ntok, hw + u / ntok, make_uint4(0, 0, 0, 0), 1);
-    }
+  const int tp0 = pass * tpp;                               // first token of the pass
+  if (tp0 >= M) return;
+  const int tp1 = min(M, tp0 + tpp);                        // end token
+  if (pass > 0) {
+    open_round();
+    if constexpr (RING_FIRST) start_ring();
   }
-  open_segment();
-  start_ring();
-  // the sigmoid table while the first weights are on their way
-  if constexpr (!DOWN)
-    for (int i = tid; i < kSigTable; i += kResThreads) s_sig[i] = sigmoid_bf16(sig_table_bits(i));
+  stage_pass(tp0, tp1 - tp0);
+  if constexpr (!RING_FIRST) start_ring();
+  fill_round();
+  if constexpr (!DOWN) *(uint4*)(s_sig + 8 * tid) = sigv;
+  __syncthreads();
 
   // exact (row, token) sum of the four digit columns of a lane quad: lane j
   // of the quad receives row 4*g4 + j (transposing quad reduction)
@@ -520,12 +717,7 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
   for (int j = 0; j < kResU; ++j) rdo[j] = res_chunk(g4, cc, j) * 16;
 
-  for (int pass = 0;;) {
-    const int tp0 = pass * tpp;                             // first token of the pass
-    const int tp1 = min(M, tp0 + tpp);                      // end token
-    const int pend = tp1 * K;                               // end pair
-    int next_pair = tp0 * K;
-    bool first_group = true;
+  {
     // the pass token of this lane's quad in each column tile, and its exponent
     int ltok[NT], lxm[NT];
     bool lok[NT];
@@ -535,101 +727,25 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
       lok[n] = (W == 4 || (cc & 4) == 0) && ltok[n] < tp1 - tp0;
       lxm[n] = lok[n] ? s_xmax[tp0 + ltok[n]] : 0;
     }
-    for (;;) {
-      __syncthreads();  // previous group done with the fix-up slots, s_bound and s_pairs; digits visible
-      if (tid < kResFixSlots) s_fixcnt[tid] = 0;
-      if (tid <= kResWaves) s_bound[tid] = bound(tid);
-      for (int i = tid; i < kResFixSlots * res_fix_words(NT); i += kResThreads) s_fix[i] = 0;
 
-      // ---- next group of up to kResMaxPairs pairs of the pass routed to slot e ----
-      int count, more;
-      if (!grouped) {
-        count = min(kResMaxPairs, pend - next_pair);
-        more = next_pair + count < pend;
-        if (tid < count) {
-          s_pairs[tid] = next_pair + tid;
-          s_ptok[tid] = next_pair + tid - tp0;               // K == 1
-        }
-        __syncthreads();  // s_pairs, s_bound and the cleared fix-up slots visible
-      } else {
-        // block-wide scan of ids[next_pair..pend) in aligned windows of
-        // kResThreads (the first kResIdRegs from registers); stops once a
-        // further match proves there is another group
-        int found = 0;
-        int base = next_pair & ~(kResThreads - 1);
-        more = 0;
-        for (;;) {
-          const int p = base + tid;
-          const int k = base / kResThreads;
-          int id;
-          if (k < kResIdRegs) {
-            id = k == 0 ? idr[0] : k == 1 ? idr[1] : k == 2 ? idr[2] : idr[3];
-          } else {
-            id = p < P ? a.ids[p] : -1;
-            // This load completes after the ring issued before it in any
-            // case.  Waiting here, on this path alone, keeps the compiler
-            // from placing a wait for every load in flight (the whole ring)
-            // on the register path too, where the merged id is used.
-            __builtin_amdgcn_s_waitcnt(kWaitVmem0);
-          }
-          const bool m = id == e && p >= next_pair && p < pend;
-          const uint64_t bal = __ballot(m);
-          if (lane == 0) s_wcnt[wave] = __popcll(bal);
-          __syncthreads();
-          int before = found, total = found;
-#pragma unroll
-          for (int w = 0; w < kResWaves; ++w) {
-            const int c = s_wcnt[w];
-            if (w < wave) before += c;
-            total += c;
-          }
-          before += __popcll(bal & below);
-          if (m && before < kResMaxPairs) {
-            s_pairs[before] = p;
-            s_ptok[before] = p / K - tp0;
-          }
-          found = total;
-          base += kResThreads;
-          if (found > kResMaxPairs) more = 1;
-          __syncthreads();  // s_wcnt reused; s_pairs visible
-          if (more || base >= pend) break;
-        }
-        count = min(found, kResMaxPairs);
-      }
-      if (count <= 0) break;
-      next_pair = s_pairs[count - 1] + 1;
-      // the group's pairs and their pass tokens, uniform: held in scalar registers
-      int gpair[kResMaxPairs], gtok[kResMaxPairs];
-#pragma unroll
-      for (int q = 0; q < kResMaxPairs; ++q) {
-        gpair[q] = __builtin_amdgcn_readfirstlane(q < count ? s_pairs[q] : 0);
-        gtok[q] = __builtin_amdgcn_readfirstlane(q < count ? s_ptok[q] : -1);
-      }
-      // the pair of this lane's token in each column tile when it has exactly
-      // one in the group (-1: none); several pairs of one token take the loop
-      int mypair[NT];
-      bool multi = false;
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        int mp = -1;
-        for (int q = 0; q < count; ++q)
-          if (gtok[q] == ltok[n]) mp = mp == -1 ? gpair[q] : -2;   // -2: two or more
-        mypair[n] = mp;
-        multi = multi || __ballot(lok[n] && mp == -2) != 0;
-      }
-      if (!first_group) start_ring();
-      first_group = false;
-
+    for (;;) {                               // rounds
       int u = ua;
       while (u < ub) {
         // one portion: the rest of the current tile inside [u, ub)
-        const int tile = t0 + u / S;
-        const int sa = u % S;
-        const int pe = min(ub, (u / S + 1) * S);              // portion end (unit)
+        const int w = u / S;                                  // round tile
+        const int sa = u - w * S;
+        const int pe = min(ub, (w + 1) * S);                  // portion end (unit)
+        const int v = vr0 + w;
+        const int rr = v / tps;
+        const int k = rr - ra;                                // segment
+        const int e = select(rr);
+        const uint8_t* slot = a.slots + (uint64_t)e * a.slot_stride;
+        const float* gscale = (const float*)(slot + a.gate_s_off);
+        const float* uscale = (const float*)(slot + a.up_s_off);
         // the row scales this lane may finish with, loaded ahead of the
         // portion's weight loads: loads complete in order, so a scale load
         // issued at the finish would wait for every weight load in flight
-        const int row = tile * RT + 4 * g4 + qj;
+        const int row = (v - rr * tps) * RT + 4 * g4 + qj;
         const float gsc = gscale[min(row, I - 1)];
         const float usc = DOWN ? gscale[min(row + 16, I - 1)] : uscale[min(row, I - 1)];
         float gscr = 0.0f, uscr = 0.0f;
@@ -696,12 +812,12 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
         bool finish = (sa == 0 && se == S);
         if (!finish) {
           // contributors of this tile: ranges that meet its units, by position
-          const int tu0 = (tile - t0) * S, tu1 = tu0 + S;
+          const int tu0 = w * S, tu1 = tu0 + S;
           int first = -1, ncontrib = 0;
-          for (int k = 0; k < kResWaves; ++k) {
-            const int qa = s_bound[k], qb = s_bound[k + 1];
+          for (int kk = 0; kk < kResWaves; ++kk) {
+            const int qa = s_bound[kk], qb = s_bound[kk + 1];
             if (qa < qb && qa < tu1 && qb > tu0) {
-              if (first < 0) first = k;
+              if (first < 0) first = kk;
               ++ncontrib;
             }
           }
@@ -808,57 +924,74 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
                 if (a.up_probe) a.up_probe[o] = up;
               }
             };
-            if (!multi) {
-              if (ok && mypair[n] >= 0) store(mypair[n]);
-            } else {
-              for (int q = 0; q < count; ++q)
-                if (ok && gtok[q] == tl) store(gpair[q]);
+            if (ok) {
+              const int tg = tp0 + tl;                        // token of the call
+              const int cnt = s_cnt[k][tg];
+              const int p1 = s_first[k][tg];
+              if (cnt > 0) store(p1);
+              // a token routed to this slot more than once (duplicate ids)
+              if (cnt > 1)
+                for (int jj = 0; jj < K; ++jj) {
+                  const int p = tg * K + jj;
+                  if (p != p1 && a.ids[p] == e) store(p);
+                }
             }
           }
         }
       }
-      if (!more) break;
+      // ---- next round of this pass ----
+      if (vr1 >= v1) break;
+      __syncthreads();                       // every wave done with the round's tables
+      vr0 = vr1;
+      open_round();
+      clear_tables();
+      __syncthreads();
+      start_ring();
+      fill_round();
+      __syncthreads();
     }
 
-    // ---- next segment, or the next pass from the first segment ----
-    if (v < v1) {
-      open_segment();
-      start_ring();
-      continue;
-    }
-    if (++pass >= npass) break;
-    __syncthreads();  // every wave is done with the previous pass's digits
-    if constexpr (WIDE) {
-      const int p0 = pass * tpp;
-      const int ntok = min(M, p0 + tpp) - p0;
-      const int npair = S * 16;
-#pragma unroll 1
-      for (int u = tid; u < ntok * npair; u += kResThreads) {
-        const int tl = u / npair, r = u - tl * npair;
-        const int w8 = 2 * r;
-        const uint64_t xr = (uint64_t)(p0 + tl) * hw;
-        const uint4 xa = w8 < hw ? ((const uint4*)a.x)[xr + w8] : make_uint4(0, 0, 0, 0);
-        const uint4 xb = w8 + 1 < hw ? ((const uint4*)a.x)[xr + w8 + 1] : make_uint4(0, 0, 0, 0);
-        stage_pair(tl, r, xa, xb, etop(p0 + tl));
-      }
-    } else {
-      const int p0 = pass * tpp;
-      const int ntok = min(M, p0 + tpp) - p0;
-      for (int u = tid; u < ntok * S * 16; u += kResThreads) {
-        const int tl = u % ntok, w8 = u / ntok;
-        if (xf) {
-          uint4 xa = make_uint4(0, 0, 0, 0), xb = make_uint4(0, 0, 0, 0);
-          if (w8 < hw) xf_chunk((p0 + tl) * hw + w8, xa, xb);
-          stage_unitf(tl, w8, xa, xb, etop(p0 + tl));
-        } else {
-          const uint4 xq = w8 < hw ? ((const uint4*)a.x)[(uint64_t)(p0 + tl) * hw + w8] : make_uint4(0, 0, 0, 0);
-          stage_unit(tl, w8, xq, etop(p0 + tl));
+  }
+
+  // ---- pairs with invalid ids get zero outputs: pairs b, b + NB, ... here ----
+  if (grouped && pass == 0) {
+    const int nmine = P > (int)blockIdx.x ? (P - (int)blockIdx.x + NB - 1) / NB : 0;
+    for (int base = 0; base < nmine; base += kResThreads) {
+      __syncthreads();
+      if (tid == 0) s_ninv = 0;
+      __syncthreads();
+      const int i = base + tid;
+      const int p = (int)blockIdx.x + i * NB;
+      const bool bad = i < nmine && (a.ids[p] < 0 || a.ids[p] >= a.num_slots);
+      int at = -1;
+      if (bad) at = atomicAdd(&s_ninv, 1);
+      if (bad && at < kInvBatch) s_invl[at] = p;
+      __syncthreads();
+      const int nl = min(s_ninv, kInvBatch);
+      for (int q = 0; q < nl; ++q) {
+        const int pq = s_invl[q];
+        for (int r = tid; r < I; r += kResThreads) {
+          const uint64_t o = (uint64_t)pq * I + r;
+          if (xf)
+            ((float*)a.out)[o] = 0.0f;
+          else
+            a.out[o] = 0;
+          if (a.gate_probe) a.gate_probe[o] = 0.0f;
+          if (a.up_probe) a.up_probe[o] = 0.0f;
         }
       }
+      // past the batch: each finder fills its own pair
+      if (bad && at >= kInvBatch)
+        for (int r = 0; r < I; ++r) {
+          const uint64_t o = (uint64_t)p * I + r;
+          if (xf)
+            ((float*)a.out)[o] = 0.0f;
+          else
+            a.out[o] = 0;
+          if (a.gate_probe) a.gate_probe[o] = 0.0f;
+          if (a.up_probe) a.up_probe[o] = 0.0f;
+        }
     }
-    v = v0;
-    open_segment();
-    start_ring();
   }
 }
 
@@ -876,9 +1009,10 @@ constexpr int kWaveShare2 = 547;
 // most of a CU's 160 KiB).
 template <int NT, bool VEC, bool DOWN, bool Q8, bool XF>
 int resident_blocks(int device) {
-  static int cached[64] = {0};
+  // per-device cache; concurrent first calls compute the same value
+  static std::atomic<int> cached[64];
   if (device < 0 || device >= 64) device = 0;
-  if (!cached[device]) {
+  if (!cached[device].load(std::memory_order_relaxed)) {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0)
       cus = 256;
@@ -886,9 +1020,9 @@ int resident_blocks(int device) {
             &per_cu, reinterpret_cast<const void*>(&resident_kernel<NT, VEC, DOWN, Q8, XF>), kResThreads, 0) != hipSuccess ||
         per_cu <= 0)
       per_cu = 1;
-    cached[device] = cus * per_cu;
+    cached[device].store(cus * per_cu, std::memory_order_relaxed);
   }
-  return cached[device];
+  return cached[device].load(std::memory_order_relaxed);
 }
 
 template <int NT, bool VEC, bool DOWN, bool Q8, bool XF>
@@ -899,8 +1033,10 @@ hipError_t launch_resident_t(GateUpParams& p, hipStream_t stream) {
   const int tiles = p.num_slots * ((p.I + rt - 1) / rt);
   int nb = resident_blocks<NT, VEC, DOWN, Q8, XF>(device);
   if (nb > tiles) nb = tiles;
+  // y slices: the passes six-digit tokens would need (2 * NT per pass)
+  const int slices = (p.M + 2 * NT - 1) / (2 * NT);
   void* args[] = {&p};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&resident_kernel<NT, VEC, DOWN, Q8, XF>), dim3((unsigned)nb),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&resident_kernel<NT, VEC, DOWN, Q8, XF>), dim3((unsigned)nb, (unsigned)slices),
                          dim3(kResThreads), args, 0, stream);
 }
 
@@ -924,7 +1060,9 @@ bool resident_fits(int M, int H, bool q8, bool xf) {
   if (M < 1 || M > kResMaxTokens) return false;
   const int nt = res_tiles(M);
   const bool wide = res_wide(nt, q8, xf);
-  return (int64_t)M * (H / 8) <= (int64_t)kResXRegs * kResThreads &&
+  // x of every token in registers: chunks, or chunk pairs with wide steps
+  const int64_t xunits = wide ? (int64_t)M * ((H / 8 + 1) / 2) * 2 : (int64_t)M * (H / 8);
+  return xunits <= (int64_t)kResXRegs * kResThreads &&
          (int64_t)res_steps(H, wide ? 256 : 128) * res_step_bytes(nt, wide ? 4 : 2) +
                  (int64_t)kResFixSlots * res_fix_words(nt) * 8 <=
              (int64_t)kResLds;
@@ -933,14 +1071,16 @@ bool resident_fits(int M, int H, bool q8, bool xf) {
 hipError_t launch_resident(GateUpParams p, hipStream_t stream) {
   const int nt = res_tiles(p.M);
   p.steps = res_steps(p.H, res_wide(nt, p.q8 != 0, p.xf32 != 0) ? 256 : 128);
-  p.G = kResMaxPairs;
   p.wave_share = res_tiles(p.M) == 1 ? kWaveShare1 : kWaveShare2;
   return p.xf32 ? launch_resident_x<true>(p, stream) : launch_resident_x<false>(p, stream);
 }
 
 hipError_t launch_gate_up(const GateUpParams& p, int tokens_per_slot, hipStream_t stream) {
-  return resident_fits(tokens_per_slot, p.H, p.q8 != 0, p.xf32 != 0) ? launch_resident(p, stream)
-                                                         : launch_batch(p, tokens_per_slot, stream);
+  GateUpParams q = p;
+  const hipError_t e = sigmoid_table(&q.sig);
+  if (e != hipSuccess) return e;
+  return resident_fits(tokens_per_slot, q.H, q.q8 != 0, q.xf32 != 0) ? launch_resident(q, stream)
+                                                         : launch_batch(q, tokens_per_slot, stream);
 }
 
 hipError_t launch_down(const GateUpParams& p, int pairs_per_slot, hipStream_t stream) {
