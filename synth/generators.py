@@ -19,9 +19,9 @@ from the slot base): ``[gate words | up words | gate scales | up scales]``
 back to back, padded to a multiple of 4096 bytes.  Gate and up words are
 little-endian uint32 ``[I][H/8]``; scales are little-endian float32 ``[I]``.
 
-x values are standard normal float32 samples truncated toward zero to bf16
-(the upper 16 bits), which keeps the generator free of the rounding rule under
-test while giving the same N(0,1) distribution at bf16 resolution.
+x values are standard normal float32 samples rounded to nearest-even bf16 by
+torch's CPU conversion (a library routine, so the generator holds none of the
+arithmetic under test).
 """
 
 from __future__ import annotations
@@ -197,9 +197,12 @@ def fill_slot(
 
 
 def bf16_normal(rng: np.random.Generator, shape) -> np.ndarray:
-    """N(0,1) float32 samples truncated to bf16; returns uint16 bit patterns."""
+    """N(0,1) float32 samples rounded to nearest-even bf16 (torch's CPU
+    conversion); returns uint16 bit patterns."""
+    import torch
     f = rng.standard_normal(size=shape, dtype=np.float32)
-    return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    b = torch.from_numpy(np.ascontiguousarray(f)).to(torch.bfloat16)
+    return b.view(torch.int16).numpy().view(np.uint16).copy()
 
 
 def f32_normal(rng: np.random.Generator, shape) -> np.ndarray:
