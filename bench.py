@@ -58,13 +58,17 @@ SEEDS = {"pool": SEED, "expert_pool": SEED + 1000, "f32_x": SEED + 2000, "q8_poo
          "decode_routing": SEED + 4000, "ep_routing": SEED + 5000, "large": 105, "routed": 104}
 
 
+# the sources of the gate/up and down kernels and their launchers (a change in
+# any of them invalidates stored counters and parity statistics)
+KERNEL_SOURCES = ["q4moe_device.h", "q4moe_launch.h", "q4moe_resident.hip", "q4moe_batch.hip", "q4moe_sigmoid.hip"]
+
+
 def kernel_sha() -> str:
-    """sha256 over every kernel source (a change anywhere invalidates stored counters)."""
+    """sha256 over the kernel sources."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
