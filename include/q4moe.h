@@ -148,6 +148,30 @@ int q4_expert_gate_up_grouped_probe(const void *slots_base, uint64_t slot_stride
                                     void *workspace, size_t workspace_bytes,
                                     q4_stream_t stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the grouped
+ * call of q4_expert_gate_up_grouped, same arguments, kernels and results, with
+ * the workspace replaced by a static scratch array the library holds on each
+ * GPU (256 bytes per device, kept until the process ends; its address is
+ * resolved on the first call on each device).  No device memory is allocated
+ * or freed by the call.
+ *   invalid_count  device int32, 4-byte aligned, or NULL: receives the number
+ *                  of ids outside [0, num_slots) (a device-to-device copy on
+ *                  `stream` after the kernels).
+ * A call whose workspace need (q4_grouped_workspace_bytes) exceeds the scratch
+ * is rejected with Q4_ERR_UNSUPPORTED.  All calls on one GPU share its
+ * scratch, which keeps the last call's contents: calls that overlap in time
+ * on one GPU (other streams, other threads) race and must be serialised by
+ * the caller.
+ */
+int q4_expert_gate_up_grouped_noalloc(const void *slots_base, uint64_t slot_stride,
+                                      int64_t num_slots, const q4_slot_layout *layout,
+                                      const void *x_bf16, int64_t M,
+                                      const int32_t *slot_ids, int64_t K,
+                                      int64_t H, int64_t I, void *out_bf16,
+                                      int32_t *invalid_count, q4_stream_t stream);
+
 /* Host-only argument checks of the two calls (no device access, nothing
  * enqueued): the same validation the entry points run first.  Pointers are
  * only tested for NULL and alignment. */

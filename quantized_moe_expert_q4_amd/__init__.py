@@ -22,6 +22,7 @@ from ._lib import (  # noqa: F401
     grouped_workspace_bytes,
     expert_gate_up,
     expert_gate_up_grouped,
+    expert_gate_up_grouped_noalloc,
     validate_gate_up,
     validate_grouped,
     expert_down,

@@ -71,6 +71,8 @@ _SIGNATURES = {
                                                  _P, _P, _SZ, _P]),
     "q4_expert_gate_up_grouped_probe": (ctypes.c_int, [_P, _U64, _I64, _LAYOUT, _P, _I64, _P, _I64, _I64,
                                                        _I64, _P, _P, _P, _P, _SZ, _P]),
+    "q4_expert_gate_up_grouped_noalloc": (ctypes.c_int, [_P, _U64, _I64, _LAYOUT, _P, _I64, _P, _I64, _I64,
+                                                         _I64, _P, _P, _P]),
     "q4_validate_gate_up": (ctypes.c_int, [_P, _LAYOUT, _P, _I64, _I64, _I64, _P]),
     "q4_validate_grouped": (ctypes.c_int, [_P, _U64, _I64, _LAYOUT, _P, _I64, _P, _I64, _I64, _I64, _P, _P,
                                            _SZ]),
@@ -301,6 +303,22 @@ def expert_gate_up_grouped(slots_base, slot_stride: int, num_slots: int, layout,
         st = fn(_ptr(slots_base), slot_stride, num_slots, ctypes.byref(lay), _ptr(x), M, _ptr(slot_ids), K, H, I,
                 _ptr(out), _ptr(gate_probe), _ptr(up_probe), _ptr(workspace), workspace_bytes, _stream(stream))
     _check(st)
+
+
+def expert_gate_up_grouped_noalloc(slots_base, slot_stride: int, num_slots: int, layout, x, M: int, slot_ids,
+                                   K: int, H: int, I: int, out, invalid_count=None, stream=None) -> None:
+    """Enqueue the grouped call on the library's static scratch (see
+    q4_expert_gate_up_grouped_noalloc in include/q4moe.h): no workspace, no
+    device allocation; ``invalid_count`` (int32 device tensor or None)
+    receives the number of out-of-range ids."""
+    lib = load()
+    _args(_slots_spec("slots_base", slots_base, num_slots, slot_stride, layout), ("x", x, "bfloat16", M * H),
+          ("slot_ids", slot_ids, "int32", M * K), ("out", out, "bfloat16", M * K * I),
+          ("invalid_count", invalid_count, "int32", 1))
+    lay = layout_c(layout)
+    _check(lib.q4_expert_gate_up_grouped_noalloc(_ptr(slots_base), slot_stride, num_slots, ctypes.byref(lay), _ptr(x),
+                                                 M, _ptr(slot_ids), K, H, I, _ptr(out), _ptr(invalid_count),
+                                                 _stream(stream)))
 
 
 def validate_gate_up(slot, layout, x, M: int, H: int, I: int, out, fmt: str = "q4", xdtype: str = "bf16") -> int:

@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libq4moe.so")
 
-SOURCES = ["q4moe_resident.hip", "q4moe_batch.hip", "q4moe_stream.hip", "q4moe_sigmoid.hip", "q4moe_abi.cpp"]
+SOURCES = ["q4moe_resident.hip", "q4moe_batch.hip", "q4moe_stream.hip", "q4moe_sigmoid.hip", "q4moe_noalloc.hip",
+           "q4moe_abi.cpp"]
 
 FLAGS = [
     "--offload-arch=gfx950",

@@ -292,6 +292,35 @@ int q4_expert_gate_up_grouped(const void* slots_base, uint64_t slot_stride, int6
                      nullptr, workspace, workspace_bytes, stream);
 }
 
+int q4_expert_gate_up_grouped_noalloc(const void* slots_base, uint64_t slot_stride, int64_t num_slots,
+                                      const q4_slot_layout* layout, const void* x_bf16, int64_t M,
+                                      const int32_t* slot_ids, int64_t K, int64_t H, int64_t I, void* out_bf16,
+                                      int32_t* invalid_count, q4_stream_t stream) {
+  // the grouped call's workspace, here the library's static scratch
+  const size_t need = q4_grouped_workspace_bytes(M, K, num_slots);
+  if (need > q4::static_scratch_bytes())
+    return fail(Q4_ERR_UNSUPPORTED, "the call needs " + std::to_string(need) +
+                                        " bytes of workspace, more than the library's static scratch of " +
+                                        std::to_string(q4::static_scratch_bytes()));
+  if (invalid_count && !aligned(invalid_count, 4))
+    return fail(Q4_ERR_ALIGNMENT, "invalid_count must be 4-byte aligned");
+  // host-side checks first: a rejected call touches no device state
+  int rc = check_grouped(0u, slots_base, slot_stride, num_slots, layout, x_bf16, M, slot_ids, K, H, I, out_bf16,
+                         nullptr, nullptr, reinterpret_cast<void*>(uintptr_t(256)), q4::static_scratch_bytes());
+  if (rc) return rc;
+  void* ws = nullptr;
+  hipError_t e = q4::static_scratch(&ws);
+  if (e != hipSuccess)
+    return fail(Q4_ERR_HIP, std::string("static scratch unavailable: ") + hipGetErrorString(e));
+  rc = run_grouped(0u, slots_base, slot_stride, num_slots, layout, x_bf16, M, slot_ids, K, H, I, out_bf16, nullptr,
+                   nullptr, ws, q4::static_scratch_bytes(), stream);
+  if (rc || !invalid_count) return rc;
+  e = hipMemcpyAsync(invalid_count, ws, sizeof(int32_t), hipMemcpyDeviceToDevice,
+                     reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(Q4_ERR_HIP, std::string("invalid-id count copy failed: ") + hipGetErrorString(e));
+  return ok();
+}
+
 int q4_expert_gate_up_grouped_probe(const void* slots_base, uint64_t slot_stride, int64_t num_slots,
                                     const q4_slot_layout* layout, const void* x_bf16, int64_t M,
                                     const int32_t* slot_ids, int64_t K, int64_t H, int64_t I, void* out_bf16,

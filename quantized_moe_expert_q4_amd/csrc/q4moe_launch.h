@@ -34,6 +34,11 @@ struct GateUpParams {
 // (kSigTable entries, see q4moe_device.h), built on first use.
 hipError_t sigmoid_table(const uint16_t** table);
 
+// The library's static device scratch on the current device (q4moe_noalloc.hip):
+// its device address, resolved on first use per device, and its size.
+hipError_t static_scratch(void** ptr);
+size_t static_scratch_bytes();
+
 // Resident-digits kernel for token groups of at most two (decode widths):
 // true when the whole-K digits of `M_per_slot` tokens fit its LDS buffer.
 bool resident_fits(int M_per_slot, int H, bool q8, bool xf32);

@@ -159,6 +159,21 @@ def test_entry_points_reject_before_touching_the_device():
     assert ei.value.status == q4.Q4_ERR_RANGE
 
 
+def test_noalloc_entry_point_rejects_before_touching_the_device():
+    # sizes beyond the grouped limits, a misaligned count output and invalid
+    # slots are rejected on the host before the static scratch is resolved
+    with pytest.raises(q4.Q4Error) as ei:
+        q4.expert_gate_up_grouped_noalloc(SLOT, 12599296, 64, _lay(), X, 9000, IDS, 8, 4096, 1536, OUT, stream=0)
+    assert ei.value.status == q4.Q4_ERR_UNSUPPORTED and "routed pairs" in str(ei.value)
+    lib = q4.load()
+    st = lib.q4_expert_gate_up_grouped_noalloc(SLOT, 12599296, 64, ctypes.byref(q4._lib.layout_c(_lay())), X, 1,
+                                               IDS, 8, 4096, 1536, OUT, WS + 2, 0)
+    assert st == q4.Q4_ERR_ALIGNMENT and "invalid_count" in q4.last_error()
+    with pytest.raises(q4.Q4Error) as ei:
+        q4.expert_gate_up_grouped_noalloc(SLOT, 4096, 1, _lay(), X, 1, IDS, 1, 4096, 1536, OUT, stream=0)
+    assert ei.value.status == q4.Q4_ERR_RANGE
+
+
 # ---- down projection and whole expert (page 52 DOWN_SOURCE / validateCall) ----
 
 def _down(**kw):
