@@ -291,9 +291,10 @@ def leg(nbytes: float, sec: float, per, workload: str, kernel: str, rows: float 
     return d
 
 
-STREAM_VARIANTS = [("tile_w8_d1", 0, 8, 1), ("tile_w8_d2", 0, 8, 2), ("tile_w8_d4", 0, 8, 4),
-                   ("linear_w8_d2", 1, 8, 2), ("tile_w16_d1", 0, 16, 1), ("tile_w16_d2", 0, 16, 2),
-                   ("tile_w16_d4", 0, 16, 4)]
+STREAM_VARIANTS = [("tile_w8_d2", 0, 8, 2), ("tile_w8_d4", 0, 8, 4), ("line_w8_d1", 3, 8, 1),
+                   ("line_w8_d2", 3, 8, 2), ("linear_w8_d2", 1, 8, 2), ("tile_nt_w8_d2", 4, 8, 2),
+                   ("line_nt_w8_d1", 7, 8, 1), ("line_nt_w8_d2", 7, 8, 2), ("line_nt_w8_d4", 7, 8, 4),
+                   ("linear_nt_w8_d2", 5, 8, 2), ("line_nt_w16_d2", 7, 16, 2)]
 
 
 def stream_ceiling(pool, steps: int, warmup: int):
@@ -314,7 +315,9 @@ def stream_ceiling(pool, steps: int, warmup: int):
     best = max(res, key=res.get)
     return {"best_GBps": res[best], "best_variant": best, "variants_GBps": res, "bytes_per_launch": nbytes,
             "kernel": "q4::stream_read_kernel: the pool's gate and up weights read once, no arithmetic "
-                      "(tile = the gate/up kernels' 16-row x 128-byte steps; linear = lane-linear 1 KiB runs; "
+                      "(tile = 16-row x 128-byte steps, 4 lanes per row; line = the same with 8 lanes per row, whole "
+                      "128-byte lines per load instruction; linear = lane-linear 1 KiB runs; nt = non-temporal load "
+                      "hint; "
                       "w = waves per CU, d = steps in flight per wave; median of 3 repetitions)"}
 
 

@@ -511,7 +511,13 @@ const char *q4_last_error(void);
  * and up weights), each byte once, with no arithmetic.
  *   pattern 0  the gate/up kernels' weight access: 16-row tiles, 128 bytes of
  *              each row per step, 32 bytes per lane;
- *   pattern 1  the same bytes per step as two lane-linear 1 KiB runs.
+ *   pattern 1  the same bytes per step as two lane-linear 1 KiB runs;
+ *   pattern 2  16-row tiles, 128 bytes of each row per step, lane l's two
+ *              16-byte loads at (l / 16) * 16 and 64 + (l / 16) * 16: each
+ *              load instruction covers one 64-byte half of every row's 128;
+ *   pattern 3  16-row tiles, 128 bytes of each row per step, 8 lanes per row:
+ *              each load instruction covers whole 128-byte lines of 8 rows;
+ *   pattern+4  the same with the non-temporal load hint (bytes read once).
  *   waves      8 or 16 waves per work-group (one work-group per CU);
  *   depth      steps in flight per wave: 1, 2 or 4.
  *   sink       device, one 4-byte word; written only on a data value that

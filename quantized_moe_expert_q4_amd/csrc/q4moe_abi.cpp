@@ -749,7 +749,10 @@ int q4_stream_read(const void* slots_base, uint64_t slot_stride, int64_t num_slo
   const uint64_t len = (uint64_t)rows * (uint64_t)row_bytes;
   if (offset_a > slot_stride || len > slot_stride - offset_a || offset_b > slot_stride || len > slot_stride - offset_b)
     return fail(Q4_ERR_RANGE, "an array exceeds the slot stride");
-  if (pattern != 0 && pattern != 1) return fail(Q4_ERR_INVALID_ARGUMENT, "pattern must be 0 (row tiles) or 1 (linear)");
+  if (pattern < 0 || pattern > 7)
+    return fail(Q4_ERR_INVALID_ARGUMENT,
+                "pattern must be 0 (row tiles), 1 (linear), 2 (half-line row tiles) or 3 (whole-line row tiles), "
+                "plus 4 for non-temporal loads");
   if ((waves != 8 && waves != 16) || (depth != 1 && depth != 2 && depth != 4))
     return fail(Q4_ERR_UNSUPPORTED, "waves must be 8 or 16 and depth 1, 2 or 4");
   q4::StreamParams p{};

@@ -215,16 +215,20 @@ constexpr uint32_t kOffNone = 0x80000000u;
 // lgkmcnt 15).
 constexpr int kWaitVmem0 = 0x0F70;
 
-template <bool VEC>
+// Cache-policy operand of the buffer loads: 0 (default) or kLoadNT, the
+// non-temporal hint for bytes that are read once.
+constexpr int kLoadNT = 2;
+
+template <bool VEC, int AUX = 0>
 __device__ __forceinline__ v4u load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   if constexpr (VEC) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX);
   } else {
     v4u v;
-    v.x = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
-    v.y = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off + 4, 0, 0);
-    v.z = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off + 8, 0, 0);
-    v.w = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off + 12, 0, 0);
+    v.x = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, AUX);
+    v.y = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off + 4, 0, AUX);
+    v.z = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off + 8, 0, AUX);
+    v.w = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off + 12, 0, AUX);
     return v;
   }
 }
@@ -286,6 +290,53 @@ template <bool Q8, bool VEC>
 __device__ __forceinline__ void load_step(StepW<Q8>& w, __amdgpu_buffer_rsrc_t r, uint32_t off) {
   w.a = load16<VEC>(r, off);
   if constexpr (Q8) w.b = load16<VEC>(r, off + 16u);
+}
+
+// ---- whole-line weight loads (32 bytes per lane and step) ----
+// One K-step of a 16-row tile is 16 rows x 128 bytes.  Loaded with 8 lanes
+// per row, every load instruction covers whole 128-byte lines (with the
+// non-temporal hint this streams ~14% faster than 4 lanes per row on
+// MI355X): lane L receives bytes 16 (L % 8) .. +16 of tile rows L / 8 (.a)
+// and 8 + L / 8 (.b).  line_to_tile then moves them across lanes to the
+// layout the splits take, lane 16 g + r holding bytes 32 g .. 32 g + 32 of
+// row r (.a the first 16): one DPP swap of odd and even lanes, a select and
+// one ds_bpermute per dword.
+template <bool VEC>
+__device__ __forceinline__ void load_line(StepW<true>& w, __amdgpu_buffer_rsrc_t r, uint32_t off_a, uint32_t off_b) {
+  w.a = load16<VEC, kLoadNT>(r, off_a);
+  w.b = load16<VEC, kLoadNT>(r, off_b);
+}
+
+struct LineLanes {
+  int addr_a, addr_b;  // ds_bpermute byte addresses of the lane's sources
+  bool even;
+};
+
+__device__ __forceinline__ LineLanes line_lanes(int lane) {
+  const int g = lane >> 4, r = lane & 15;
+  // piece 2g (.a) / 2g+1 (.b) of row r: rows 0..7 come from .a of lane
+  // 8r + piece, rows 8..15 from .b of lane 8(r-8) + piece, staged at the
+  // neighbour lane (piece ^ 1) by the swap
+  LineLanes l;
+  l.addr_a = 4 * (8 * (r & 7) + 2 * g + (r >> 3));
+  l.addr_b = 4 * (8 * (r & 7) + 2 * g + 1 - (r >> 3));
+  l.even = (lane & 1) == 0;
+  return l;
+}
+
+__device__ __forceinline__ void line_to_tile(StepW<true>& w, const LineLanes& l) {
+  v4u na, nb;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    // .b of the neighbour lane (quad_perm 1,0,3,2)
+    const int bs = __builtin_amdgcn_mov_dpp((int)w.b[k], 0xB1, 0xF, 0xF, true);
+    const int xa = l.even ? (int)w.a[k] : bs;
+    const int xb = l.even ? bs : (int)w.a[k];
+    na[k] = (uint32_t)__builtin_amdgcn_ds_bpermute(l.addr_a, xa);
+    nb[k] = (uint32_t)__builtin_amdgcn_ds_bpermute(l.addr_b, xb);
+  }
+  w.a = na;
+  w.b = nb;
 }
 
 __device__ __forceinline__ void split_step(const StepW<false>& w, v4i& ev, v4i& od) { split_weights(w.a, ev, od); }

@@ -128,6 +128,7 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
   constexpr int kResD = res_depth(NT, Q8, XF);
   constexpr bool WIDE = res_wide(NT, Q8, XF);
   constexpr bool WL = Q8 || WIDE;            // 32 bytes per lane and step
+  constexpr bool LINE = WL;                  // weights loaded in whole lines (load_line)
   constexpr int NPL = WIDE ? 4 : 2;          // operand planes per step
   constexpr bool xf = XF;
   // x held in registers from the start and the first weights in flight
@@ -251,10 +252,14 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
     ub = bound(wpos + 1);
   };
   // ---- weight load cursor: round tile lt, step ls, segment lk ----
-  auto row_off = [&](int t) {
-    const int row = t * RT + cc;
-    return (uint32_t)(row < I ? row : I - 1) * rbytes + (uint32_t)g4 * group_bytes<WL>();
+  // 32-byte steps are loaded in whole 128-byte lines (load_line): lane L
+  // reads rows L / 8 and 8 + L / 8 of the tile; else lane 16 g + r reads row r
+  auto row_off = [&](int t, int part) {
+    const int row = LINE ? t * RT + 8 * part + (lane >> 3) : t * RT + cc;
+    const uint32_t col = LINE ? 16u * (uint32_t)(lane & 7) : (uint32_t)g4 * group_bytes<WL>();
+    return (uint32_t)(row < I ? row : I - 1) * rbytes + col;
   };
+  const LineLanes lines = line_lanes(lane);
   // (an empty resource until a slot is set: every load through it returns
   // zeros without a memory access)
   __amdgpu_buffer_rsrc_t gsrc = make_rsrc(a.slots, 0u), usrc = make_rsrc(a.slots, 0u);
@@ -273,18 +278,26 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
   };
   StepW<WL> rg[kResD], ru[kResD];
   int ls = 0, lt = 0, lk = 0;                // load cursor: step, tile in slot, segment
-  uint32_t loff = 0;
+  uint32_t loff = 0, loff2 = 0;              // the lane's row offsets in the tile
   auto seek = [&](int w) {                   // cursor to round tile w
     const int r = (vr0 + w) / tps;
     lk = r - ra;
     lt = vr0 + w - r * tps;
     set_slot(lk);
-    loff = row_off(lt);
+    loff = row_off(lt, 0);
+    loff2 = row_off(lt, 1);
   };
   auto issue = [&](StepW<WL>& g, StepW<WL>& u_, bool live, uint32_t dep = 0u) {
-    const uint32_t o = (live ? loff + (uint32_t)ls * step_row_bytes<WL>() : kOffNone) + dep;
-    load_step<WL, VEC>(g, gsrc, o);
-    load_step<WL, VEC>(u_, usrc, o);
+    const uint32_t so = (uint32_t)ls * step_row_bytes<WL>();
+    const uint32_t o = (live ? loff + so : kOffNone) + dep;
+    if constexpr (LINE) {
+      const uint32_t o2 = (live ? loff2 + so : kOffNone) + dep;
+      load_line<VEC>(g, gsrc, o, o2);
+      load_line<VEC>(u_, usrc, o, o2);
+    } else {
+      load_step<WL, VEC>(g, gsrc, o);
+      load_step<WL, VEC>(u_, usrc, o);
+    }
     // cursor step after the loads: next tile every S steps, next slot every
     // tps tiles (its resources reloaded then)
     const int nls = ls + (live ? 1 : 0);
@@ -294,7 +307,8 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
         lt = 0;
         if (++lk < nseg) set_slot(lk);
       }
-      loff = row_off(lt);
+      loff = row_off(lt, 0);
+      loff2 = row_off(lt, 1);
     } else {
       ls = nls;
     }
@@ -761,6 +775,10 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
           for (int j = 0; j < kResU; ++j) {
             const int d = j % kResD;                          // ring slot of step s + j
             v4i pg[NPL], pu[NPL];
+            if constexpr (LINE) {
+              line_to_tile(rg[d], lines);
+              line_to_tile(ru[d], lines);
+            }
             if constexpr (WIDE) {
               split_planes(rg[d].a, rg[d].b, pg);
               split_planes(ru[d].a, ru[d].b, pu);

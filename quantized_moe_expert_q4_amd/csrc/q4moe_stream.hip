@@ -10,7 +10,14 @@
 //  * TILE: lane l of a wave reads 32 bytes of row 16t + l % 16 at byte
 //    (l / 16) * 32 + 128 s of the row, from each array (four 16-byte loads);
 //  * LINEAR: the same 2 KiB of each array per unit, read as two lane-linear
-//    1 KiB runs of the tile's contiguous bytes.
+//    1 KiB runs of the tile's contiguous bytes;
+//  * HALF: as TILE, but lane l's two 16-byte loads take bytes (l / 16) * 16
+//    and 64 + (l / 16) * 16 of the row's 128 bytes, so that each load
+//    instruction covers one whole 64-byte half of every row's 128 bytes;
+//  * LINE: 8 lanes per row, so that each load instruction covers whole
+//    128-byte lines: lane l's two loads take bytes 16 (l % 8) of rows
+//    l / 8 and 8 + l / 8 of the tile.
+// Each pattern also runs with the non-temporal load hint.
 // One persistent work-group of WAVES waves per CU; work-group b takes the
 // tiles [bT/NB, (b+1)T/NB) and its waves split the (tile, step) units into
 // contiguous ranges, each with D units of loads in flight in a register ring.
@@ -28,7 +35,7 @@ struct Ring {
   v4u a0, a1, b0, b1;
 };
 
-template <int WAVES, int D, bool LINEAR>
+template <int WAVES, int D, int PAT, int AUX>
 __global__ __launch_bounds__(WAVES * 64) void stream_read_kernel(const StreamParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -55,18 +62,22 @@ __global__ __launch_bounds__(WAVES * 64) void stream_read_kernel(const StreamPar
   seek();
   auto issue = [&](Ring& r, uint32_t dep) {
     uint32_t off;
-    if (LINEAR) {
+    if (PAT == 1) {
       off = (uint32_t)ct * 16u * p.row_bytes + (uint32_t)cs * 2048u + (uint32_t)lane * 16u;
+    } else if (PAT == 3) {
+      const int row = ct * 16 + (lane >> 3);
+      off = (uint32_t)min(row, p.rows - 1) * p.row_bytes + (uint32_t)(lane & 7) * 16u + (uint32_t)cs * 128u;
     } else {
       const int row = ct * 16 + (lane & 15);
-      off = (uint32_t)min(row, p.rows - 1) * p.row_bytes + (uint32_t)(lane >> 4) * 32u + (uint32_t)cs * 128u;
+      off = (uint32_t)min(row, p.rows - 1) * p.row_bytes + (uint32_t)(lane >> 4) * (PAT == 2 ? 16u : 32u) +
+            (uint32_t)cs * 128u;
     }
     off = (left > 0 ? off : kOffNone) + dep;                   // past the range: zeros, no access
-    const uint32_t second = LINEAR ? 1024u : 16u;
-    r.a0 = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)off, 0, 0);
-    r.a1 = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(off + second), 0, 0);
-    r.b0 = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)off, 0, 0);
-    r.b1 = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)(off + second), 0, 0);
+    const uint32_t second = PAT == 1 ? 1024u : (PAT == 2 ? 64u : (PAT == 3 ? 8u * p.row_bytes : 16u));
+    r.a0 = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)off, 0, AUX);
+    r.a1 = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(off + second), 0, AUX);
+    r.b0 = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)off, 0, AUX);
+    r.b1 = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)(off + second), 0, AUX);
     if (left > 0) {
       --left;
       if (++cs == S) {
@@ -101,7 +112,7 @@ __global__ __launch_bounds__(WAVES * 64) void stream_read_kernel(const StreamPar
   if (acc == 0x9E3779B9u) p.sink[0] = acc + (uint32_t)lane;
 }
 
-template <int WAVES, int D, bool LINEAR>
+template <int WAVES, int D, int PAT, int AUX>
 hipError_t launch_t(const StreamParams& p, hipStream_t stream) {
   int device = 0, cus = 0;
   if (hipGetDevice(&device) != hipSuccess) device = 0;
@@ -112,15 +123,25 @@ hipError_t launch_t(const StreamParams& p, hipStream_t stream) {
   void* args[] = {&q};
   // dynamic LDS the kernel does not use, so that one work-group runs per CU,
   // as for the gate/up kernels
-  return hipLaunchKernel(reinterpret_cast<const void*>(&stream_read_kernel<WAVES, D, LINEAR>), dim3((unsigned)nb),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&stream_read_kernel<WAVES, D, PAT, AUX>), dim3((unsigned)nb),
                          dim3(WAVES * 64), args, 96 * 1024, stream);
 }
 
 }  // namespace
 
+template <int WAVES, int D, int AUX>
+hipError_t launch_wda(const StreamParams& p, int pattern, hipStream_t stream) {
+  if (pattern == 1) return launch_t<WAVES, D, 1, AUX>(p, stream);
+  if (pattern == 2) return launch_t<WAVES, D, 2, AUX>(p, stream);
+  if (pattern == 3) return launch_t<WAVES, D, 3, AUX>(p, stream);
+  return launch_t<WAVES, D, 0, AUX>(p, stream);
+}
+
+// pattern bit 2: the non-temporal load hint
 template <int WAVES, int D>
 hipError_t launch_wd(const StreamParams& p, int pattern, hipStream_t stream) {
-  return pattern == 1 ? launch_t<WAVES, D, true>(p, stream) : launch_t<WAVES, D, false>(p, stream);
+  return (pattern & 4) ? launch_wda<WAVES, D, kLoadNT>(p, pattern & 3, stream)
+                       : launch_wda<WAVES, D, 0>(p, pattern & 3, stream);
 }
 
 hipError_t launch_stream_read(const StreamParams& p, int pattern, int waves, int depth, hipStream_t stream) {

@@ -303,7 +303,7 @@ def test_stream_read_rejects_invalid_arguments_on_the_host():
     lib = q4.load()
     cases = [
         (dict(row_bytes=100), q4.Q4_ERR_INVALID_ARGUMENT),
-        (dict(pattern=2), q4.Q4_ERR_INVALID_ARGUMENT),
+        (dict(pattern=8), q4.Q4_ERR_INVALID_ARGUMENT),
         (dict(waves=4), q4.Q4_ERR_UNSUPPORTED),
         (dict(depth=8), q4.Q4_ERR_UNSUPPORTED),
         (dict(offset_a=8), q4.Q4_ERR_ALIGNMENT),
