@@ -156,6 +156,13 @@ __device__ __forceinline__ uint16_t swiglu_tail_tab(float gate, float up, const 
   return bf16_rne(siluT * uT);
 }
 
+// The 32-bit value of another lane of the same quad: DPP quad permute CTRL
+// (0xB1: lane l ^ 1, 0x4E: lane l ^ 2).
+template <int CTRL>
+__device__ __forceinline__ int quad_dpp(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
+}
+
 // The value held by lane l ^ 1 (or l ^ 2) of the same lane quad, through a
 // DPP quad permute (no LDS round trip).
 template <int X>

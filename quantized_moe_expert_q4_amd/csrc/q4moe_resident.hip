@@ -48,12 +48,14 @@ namespace {
 constexpr int kResWaves = 8;
 constexpr int kResThreads = kResWaves * 64;
 #ifndef Q4_RES_DEPTH
-#define Q4_RES_DEPTH 4
+#define Q4_RES_DEPTH 2
 #endif
-// K-steps of weights in flight per wave (1, 2 or 4): two for int8 weights
-// with f32 activations at two column tiles (four would spill), else four.
+// K-steps of weights in flight per wave (1, 2 or 4).  With whole-line loads
+// a step leaves the ring as soon as it has arrived (take), so two steps in
+// flight per wave keep the CU's reads going; four measured no faster at one
+// column tile and ~1.5% slower at two (register pressure).
 __host__ __device__ constexpr int res_depth(int nt, bool q8, bool xf) {
-  return (q8 && xf && nt == 2 && Q4_RES_DEPTH > 2) ? 2 : Q4_RES_DEPTH;
+  return (void)nt, (void)q8, (void)xf, Q4_RES_DEPTH;
 }
 // K-steps per pass of the step loop: the B-fragment swizzle repeats every
 // four steps, so four steps per pass keep its offsets fixed.
@@ -158,6 +160,16 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const uint32_t rbytes = row_bytes<Q8>(H);  // bytes of one weight row
   const uint32_t wbytes = (uint32_t)((uint64_t)I * rbytes);
   unsigned long long* const s_fix = (unsigned long long*)(s_lds + S * sbytes);
+  // the routed outputs, [P][I] elements of esz bytes (under 2^31 bytes: the
+  // launcher sends larger calls to the batch kernel)
+  const uint32_t esz = xf ? 4u : 2u;
+  const __amdgpu_buffer_rsrc_t osrc = make_rsrc(a.out, (uint32_t)P * (uint32_t)I * esz);
+  auto out_store = [&](uint32_t v, uint32_t off) {
+    if (xf)
+      __builtin_amdgcn_raw_buffer_store_b32(v, osrc, (int)off, 0, 0);
+    else
+      __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, osrc, (int)off, 0, 0);
+  };
 
   // ---- routing ids, the sigmoid table and x, loaded before anything waits ----
   // (unconditional buffer loads: lanes past the data read zeros without a
@@ -311,6 +323,25 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
       loff2 = row_off(lt, 1);
     } else {
       ls = nls;
+    }
+  };
+  // Whole-line loads: the next step's weights, moved out of their ring slot
+  // into the tile layout (line_to_tile), and the slot refilled at once with
+  // the step D further on (live: inside the wave's range), so that D steps
+  // stay in flight while a step is split and multiplied.  The refill's
+  // offset passes through an empty asm that takes the moved bytes, so the
+  // loads are issued after the moves have read the slot and land in the
+  // slot's own registers.
+  StepW<WL> sg, su;
+  auto take = [&](int slot, bool live) {
+    if constexpr (LINE) {
+      sg = rg[slot];
+      su = ru[slot];
+      line_to_tile(sg, lines);
+      line_to_tile(su, lines);
+      uint32_t dep = 0u;
+      asm volatile("" : "+v"(dep) : "v"(sg.a), "v"(sg.b), "v"(su.a), "v"(su.b));
+      issue(rg[slot], ru[slot], live, dep);
     }
   };
   // The ring always holds D loads per array: slots past the wave's range
@@ -712,18 +743,27 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
   fill_round();
   if constexpr (!DOWN) *(uint4*)(s_sig + 8 * tid) = sigv;
   __syncthreads();
+  // whole-line loads: the first step's weights out of the ring (each later
+  // step is taken one step ahead, in the step loop)
+  if constexpr (LINE) take(0, ua + kResD < ub);
 
   // exact (row, token) sum of the four digit columns of a lane quad: lane j
-  // of the quad receives row 4*g4 + j (transposing quad reduction)
+  // of the quad receives row 4*g4 + j.  A 4x4 transpose of the quad's int32
+  // digit sums (lane bit 1 exchanged with register bit 1, then bit 0 with
+  // bit 0, each a DPP quad permute and a select) leaves the lane with the
+  // four digit sums of its row, combined as d0 + d1 2^8 + d2 2^16 + d3 2^24.
   const int qj = cc & 3;
+  const bool qb1 = (qj & 2) != 0, qb0 = (qj & 1) != 0;
   auto quad_row_sum = [&](const v4i acc) {
-    const int64_t w0 = (int64_t)acc[0] << (8 * qj), w1 = (int64_t)acc[1] << (8 * qj);
-    const int64_t w2 = (int64_t)acc[2] << (8 * qj), w3 = (int64_t)acc[3] << (8 * qj);
-    const bool up2 = (qj & 2) != 0;
-    const int64_t r0 = quad_xor<2>(up2 ? w0 : w2), r1 = quad_xor<2>(up2 ? w1 : w3);
-    const int64_t k0 = (up2 ? w2 : w0) + r0, k1 = (up2 ? w3 : w1) + r1;  // rows (qj&2), (qj&2)+1
-    const int64_t r = quad_xor<1>((qj & 1) ? k0 : k1);
-    return ((qj & 1) ? k1 : k0) + r;
+    const int x0 = quad_dpp<0x4E>(acc[2]), x1 = quad_dpp<0x4E>(acc[3]);
+    const int y0 = quad_dpp<0x4E>(acc[0]), y1 = quad_dpp<0x4E>(acc[1]);
+    const int t0 = qb1 ? x0 : acc[0], t1 = qb1 ? x1 : acc[1];
+    const int t2 = qb1 ? acc[2] : y0, t3 = qb1 ? acc[3] : y1;
+    const int p0 = quad_dpp<0xB1>(t0), p1 = quad_dpp<0xB1>(t1);
+    const int p2 = quad_dpp<0xB1>(t2), p3 = quad_dpp<0xB1>(t3);
+    const int d0 = qb0 ? p1 : t0, d1 = qb0 ? t1 : p0;
+    const int d2 = qb0 ? p3 : t2, d3 = qb0 ? t3 : p2;
+    return (int64_t)d0 + ((int64_t)d1 << 8) + ((int64_t)d2 << 16) + ((int64_t)d3 << 24);
   };
   // this lane's B-fragment chunk for steps 0..3 mod 4
   static_assert(kResU % kResD == 0, "the step loop's pass covers whole turns of the ring");
@@ -742,6 +782,21 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
       lxm[n] = lok[n] ? s_xmax[tp0 + ltok[n]] : 0;
     }
 
+    // Output buffer: the outputs of this wave's last finished tiles, written
+    // together once the tiles cover whole 128-byte lines of the output rows
+    // (kOB tiles), at the end of the wave's range, or at a slot's last tile.
+    // Written one tile at a time, the 32-byte pieces of a line reach the
+    // cache tens of microseconds apart and go to HBM as partial lines, which
+    // costs the weight stream ~5% at eight tokens.
+    constexpr int kOB = (int)(128 / (XF ? 4 : 2)) / RT > 0 ? (int)(128 / (XF ? 4 : 2)) / RT : 1;
+    uint32_t obv[kOB][NT], obo[kOB][NT], obv2[kOB][NT], obo2[kOB][NT];
+#pragma unroll
+    for (int q = 0; q < kOB; ++q)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        obv[q][n] = obv2[q][n] = 0u;
+        obo[q][n] = obo2[q][n] = kOffNone;
+      }
     for (;;) {                               // rounds
       int u = ua;
       while (u < ub) {
@@ -762,6 +817,15 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
         const int row = (v - rr * tps) * RT + 4 * g4 + qj;
         const float gsc = gscale[min(row, I - 1)];
         const float usc = DOWN ? gscale[min(row + 16, I - 1)] : uscale[min(row, I - 1)];
+        // the routed pairs of this lane's (slot, token) items, read before the
+        // steps (LDS latency off the finish)
+        int pcnt[NT], pfirst[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          const int tg = min(tp0 + ltok[n], kResMaxTokens - 1);
+          pcnt[n] = s_cnt[k][tg];
+          pfirst[n] = s_first[k][tg];
+        }
         float gscr = 0.0f, uscr = 0.0f;
         v4i accg[NT], accu[NT];
 #pragma unroll
@@ -776,29 +840,38 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
             const int d = j % kResD;                          // ring slot of step s + j
             v4i pg[NPL], pu[NPL];
             if constexpr (LINE) {
-              line_to_tile(rg[d], lines);
-              line_to_tile(ru[d], lines);
-            }
-            if constexpr (WIDE) {
-              split_planes(rg[d].a, rg[d].b, pg);
-              split_planes(ru[d].a, ru[d].b, pu);
+              // this step's weights were moved out of the ring one step ago
+              if constexpr (WIDE) {
+                split_planes(sg.a, sg.b, pg);
+                split_planes(su.a, su.b, pu);
+              } else {
+                split_step(sg, pg[0], pg[1]);
+                split_step(su, pu[0], pu[1]);
+              }
+              // the next step's slot: moved out and refilled at once
+              take((j + 1) % kResD, u + j + 1 + kResD < ub);
             } else {
-              split_step(rg[d], pg[0], pg[1]);
-              split_step(ru[d], pu[0], pu[1]);
-            }
-            // The slot's registers are free once split: refill it before the
-            // multiply.  The refill's offset passes through an empty asm that
-            // takes the split planes, so the loads are issued after the split
-            // has read the slot and can land in the slot's own registers.
-            // Otherwise the compiler issues them early into other registers
-            // and, at the loop's back edge, copies every slot back, waiting
-            // for all loads in flight each pass.
-            uint32_t dep = 0u;
-            if constexpr (!XF) {
+              if constexpr (WIDE) {
+                split_planes(rg[d].a, rg[d].b, pg);
+                split_planes(ru[d].a, ru[d].b, pu);
+              } else {
+                split_step(rg[d], pg[0], pg[1]);
+                split_step(ru[d], pu[0], pu[1]);
+              }
+              // The slot's registers are free once split: refill it before the
+              // multiply.  The refill's offset passes through an empty asm that
+              // takes the split planes, so the loads are issued after the split
+              // has read the slot and can land in the slot's own registers.
+              // Otherwise the compiler issues them early into other registers
+              // and, at the loop's back edge, copies every slot back, waiting
+              // for all loads in flight each pass.
+              uint32_t dep = 0u;
+              if constexpr (!XF) {
 #pragma unroll
-              for (int pl = 0; pl < NPL; ++pl) asm volatile("" : "+v"(dep) : "v"(pg[pl]), "v"(pu[pl]));
+                for (int pl = 0; pl < NPL; ++pl) asm volatile("" : "+v"(dep) : "v"(pg[pl]), "v"(pu[pl]));
+              }
+              issue(rg[d], ru[d], u + j + kResD < ub, dep);
             }
-            issue(rg[d], ru[d], u + j + kResD < ub, dep);
             const uint8_t* bp = s_lds + (s + j) * sbytes + rdo[j];
             v4i bq[NPL][NT];
 #pragma unroll
@@ -860,6 +933,19 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
             finish = true;
           }
         }
+        // Outputs go out as buffer stores, the same stores on every portion:
+        // an item with nothing to store (a portion that does not finish its
+        // tile, a lane without a routed pair) stores at an offset past the
+        // buffer, which drops the write.  The portion's memory operations are
+        // then the same on every path and the wait counts of the weight loads
+        // stay exact.  Optional stores (probes, duplicate ids) wait for every
+        // memory operation before going on.
+        uint32_t st_off[NT], st_off2[NT], st_val[NT], st_val2[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          st_off[n] = st_off2[n] = kOffNone;
+          st_val[n] = st_val2[n] = 0u;
+        }
         if (finish) {
           // ---- (row, token) sums, F32 rounding, SwiGLU tail, routed stores ----
 #pragma unroll
@@ -915,46 +1001,100 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
                 if constexpr (!DOWN) ov = swiglu_tail_tab(gate, up, s_sig);
               }
             }
-            // results of this (row, token) for routed pair `pair`
-            auto store = [&](int pair) {
+            // probes and duplicate pairs: global stores (optional path)
+            auto store = [&](int pair, bool out_too) {
               const uint64_t o = (uint64_t)pair * I + row;
               float* const outf = (float*)a.out;
               if constexpr (DOWN) {
                 // rows `row` and `row + 16`, each its own output
-                if (xf)
-                  outf[o] = gate;
-                else
-                  a.out[o] = bf16_rne(gate);
+                if (out_too) {
+                  if (xf)
+                    outf[o] = gate;
+                  else
+                    a.out[o] = bf16_rne(gate);
+                }
                 if (a.gate_probe) a.gate_probe[o] = gate;
                 if (row + 16 < I) {
-                  if (xf)
-                    outf[o + 16] = up;
-                  else
-                    a.out[o + 16] = bf16_rne(up);
+                  if (out_too) {
+                    if (xf)
+                      outf[o + 16] = up;
+                    else
+                      a.out[o + 16] = bf16_rne(up);
+                  }
                   if (a.gate_probe) a.gate_probe[o + 16] = up;
                 }
               } else {
-                if (xf)
-                  outf[o] = ovf;
-                else
-                  a.out[o] = ov;
+                if (out_too) {
+                  if (xf)
+                    outf[o] = ovf;
+                  else
+                    a.out[o] = ov;
+                }
                 if (a.gate_probe) a.gate_probe[o] = gate;
                 if (a.up_probe) a.up_probe[o] = up;
               }
             };
             if (ok) {
               const int tg = tp0 + tl;                        // token of the call
-              const int cnt = s_cnt[k][tg];
-              const int p1 = s_first[k][tg];
-              if (cnt > 0) store(p1);
-              // a token routed to this slot more than once (duplicate ids)
-              if (cnt > 1)
-                for (int jj = 0; jj < K; ++jj) {
-                  const int p = tg * K + jj;
-                  if (p != p1 && a.ids[p] == e) store(p);
+              const int cnt = pcnt[n];
+              const int p1 = pfirst[n];
+              if (cnt > 0) {
+                const uint32_t o = (uint32_t)p1 * (uint32_t)I + (uint32_t)row;
+                if constexpr (DOWN) {
+                  st_off[n] = o * esz;
+                  st_val[n] = xf ? __float_as_uint(gate) : (uint32_t)bf16_rne(gate);
+                  if (row + 16 < I) {
+                    st_off2[n] = (o + 16u) * esz;
+                    st_val2[n] = xf ? __float_as_uint(up) : (uint32_t)bf16_rne(up);
+                  }
+                } else {
+                  st_off[n] = o * esz;
+                  st_val[n] = xf ? __float_as_uint(ovf) : (uint32_t)ov;
                 }
+              }
+              if ((cnt > 0 && (a.gate_probe || a.up_probe)) || cnt > 1) {
+                if (cnt > 0) store(p1, false);
+                // a token routed to this slot more than once (duplicate ids)
+                if (cnt > 1)
+                  for (int jj = 0; jj < K; ++jj) {
+                    const int p = tg * K + jj;
+                    if (p != p1 && a.ids[p] == e) store(p, true);
+                  }
+                __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+              }
             }
           }
+        }
+        if (finish) {
+#pragma unroll
+          for (int q = kOB - 1; q > 0; --q)
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+              obv[q][n] = obv[q - 1][n];
+              obo[q][n] = obo[q - 1][n];
+              obv2[q][n] = obv2[q - 1][n];
+              obo2[q][n] = obo2[q - 1][n];
+            }
+#pragma unroll
+          for (int n = 0; n < NT; ++n) {
+            obv[0][n] = st_val[n];
+            obo[0][n] = st_off[n];
+            obv2[0][n] = st_val2[n];
+            obo2[0][n] = st_off2[n];
+          }
+        }
+        // wave-uniform: the tile ends a line group or a slot, or the wave's
+        // range ends here
+        const int tis = v - rr * tps;                         // tile in its slot
+        if (pe >= ub || (finish && (((tis + 1) * RT) % (RT * kOB) == 0 || tis + 1 == tps))) {
+#pragma unroll
+          for (int q = 0; q < kOB; ++q)
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+              out_store(obv[q][n], obo[q][n]);
+              if constexpr (DOWN) out_store(obv2[q][n], obo2[q][n]);
+              obo[q][n] = obo2[q][n] = kOffNone;
+            }
         }
       }
       // ---- next round of this pass ----
@@ -967,6 +1107,7 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
       start_ring();
       fill_round();
       __syncthreads();
+      if constexpr (LINE) take(0, ua + kResD < ub);
     }
 
   }
@@ -1093,17 +1234,24 @@ hipError_t launch_resident(GateUpParams p, hipStream_t stream) {
   return p.xf32 ? launch_resident_x<true>(p, stream) : launch_resident_x<false>(p, stream);
 }
 
+// The resident kernel addresses its outputs with 32-bit buffer offsets.
+static bool resident_out_fits(const GateUpParams& p) {
+  return (uint64_t)p.M * (uint64_t)p.K * (uint64_t)p.I * (p.xf32 ? 4u : 2u) < 0x80000000ull;
+}
+
 hipError_t launch_gate_up(const GateUpParams& p, int tokens_per_slot, hipStream_t stream) {
   GateUpParams q = p;
   const hipError_t e = sigmoid_table(&q.sig);
   if (e != hipSuccess) return e;
-  return resident_fits(tokens_per_slot, q.H, q.q8 != 0, q.xf32 != 0) ? launch_resident(q, stream)
-                                                         : launch_batch(q, tokens_per_slot, stream);
+  return resident_fits(tokens_per_slot, q.H, q.q8 != 0, q.xf32 != 0) && resident_out_fits(q)
+             ? launch_resident(q, stream)
+             : launch_batch(q, tokens_per_slot, stream);
 }
 
 hipError_t launch_down(const GateUpParams& p, int pairs_per_slot, hipStream_t stream) {
-  return resident_fits(p.M, p.H, p.q8 != 0, p.xf32 != 0) ? launch_resident(p, stream)
-                                                          : launch_batch(p, pairs_per_slot, stream);
+  return resident_fits(p.M, p.H, p.q8 != 0, p.xf32 != 0) && resident_out_fits(p)
+             ? launch_resident(p, stream)
+             : launch_batch(p, pairs_per_slot, stream);
 }
 
 }  // namespace q4
