@@ -156,6 +156,13 @@ __device__ __forceinline__ uint16_t swiglu_tail_tab(float gate, float up, const 
   return bf16_rne(siluT * uT);
 }
 
+// An empty asm that takes and gives back the four words of v: keeps the
+// compiler from merging selects between held registers into an indexed
+// load, which would move the registers to scratch memory.
+__device__ __forceinline__ void opaque4(uint4& v) {
+  asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+}
+
 // The 32-bit value of another lane of the same quad: DPP quad permute CTRL
 // (0xB1: lane l ^ 1, 0x4E: lane l ^ 2).
 template <int CTRL>
@@ -351,41 +358,39 @@ __device__ __forceinline__ void split_step(const StepW<true>& w, v4i& ev, v4i& o
 
 // ---- wide K-steps of packed nibbles (256 weights per row and step) ----
 // A lane holds eight words (64 nibbles, K = base + 8w + p) of its k-group and
-// feeds four MFMAs per step, one per plane: plane 0 takes nibbles p = 0, 4 of
-// each word, plane 1 p = 2, 6, plane 2 p = 1, 5, plane 3 p = 3, 7; dword i of
-// a plane holds (word 2i, first p), (2i, second p), (2i+1, first), (2i+1,
-// second), each as the int8 16*(q-8).  Rows are then read 128 bytes per step.
+// feeds four MFMAs per step, one per plane.  Word w gives two operand dwords,
+// its even nibbles (p = 0, 2, 4, 6 as bytes 0..3) and its odd ones (p = 1, 3,
+// 5, 7), each nibble as the int8 16*(q-8): plane 0 holds the even dwords of
+// words 0..3 (dword i from word i), plane 1 their odd dwords, planes 2 and 3
+// the same for words 4..7.  Three operations per word.
 __device__ __forceinline__ void split_planes(const v4u a, const v4u b, v4i (&pl)[4]) {
   const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    // bytes 0, 2 (nibbles p = 0, 1, 4, 5) and bytes 1, 3 (p = 2, 3, 6, 7) of words 2i, 2i+1
-    // (the zero-point xor is folded into each mask: one 3-input op per plane)
-    const uint32_t e = perm(w[2 * i + 1], w[2 * i], 0x06040200u);
-    const uint32_t o = perm(w[2 * i + 1], w[2 * i], 0x07050301u);
-    pl[0][i] = (int)(((e << 4) ^ 0x88888880u) & 0xF0F0F0F0u);   // p = 0, 4
-    pl[2][i] = (int)((e ^ 0x88888888u) & 0xF0F0F0F0u);          // p = 1, 5
-    pl[1][i] = (int)(((o << 4) ^ 0x88888880u) & 0xF0F0F0F0u);   // p = 2, 6
-    pl[3][i] = (int)((o ^ 0x88888888u) & 0xF0F0F0F0u);          // p = 3, 7
+    // the zero-point xor is folded into each mask (one 3-input op per dword)
+    pl[0][i] = (int)(((w[i] << 4) ^ 0x88888880u) & 0xF0F0F0F0u);       // p = 0, 2, 4, 6
+    pl[1][i] = (int)((w[i] ^ 0x88888888u) & 0xF0F0F0F0u);              // p = 1, 3, 5, 7
+    pl[2][i] = (int)(((w[4 + i] << 4) ^ 0x88888880u) & 0xF0F0F0F0u);
+    pl[3][i] = (int)((w[4 + i] ^ 0x88888888u) & 0xF0F0F0F0u);
   }
 }
 
-// Plane dwords of one digit word pair: v0[p] / v1[p] hold four digits (bytes
-// 0..3) of position p of words 2i and 2i+1; d[j][s] receives digit s of
-// plane j's positions in the operand order of split_planes.
-__device__ __forceinline__ void plane_words4(const uint32_t (&v0)[8], const uint32_t (&v1)[8], uint32_t (&d)[4][4]) {
-  constexpr int pa[4] = {0, 2, 1, 3};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int a = pa[j], b = pa[j] + 4;
-    // [a0 b0 a1 b1] and [a2 b2 a3 b3] of each word, then digits across words
-    const uint32_t t01 = perm(v0[b], v0[a], 0x05010400u), t23 = perm(v0[b], v0[a], 0x07030602u);
-    const uint32_t u01 = perm(v1[b], v1[a], 0x05010400u), u23 = perm(v1[b], v1[a], 0x07030602u);
-    d[j][0] = perm(u01, t01, 0x05040100u);
-    d[j][1] = perm(u01, t01, 0x07060302u);
-    d[j][2] = perm(u23, t23, 0x05040100u);
-    d[j][3] = perm(u23, t23, 0x07060302u);
-  }
+// 4x4 byte transpose: o[s] = byte s of a, b, c, d as bytes 0..3.
+__device__ __forceinline__ void transpose4(uint32_t a, uint32_t b, uint32_t c, uint32_t d, uint32_t (&o)[4]) {
+  const uint32_t ab01 = perm(b, a, 0x05010400u), ab23 = perm(b, a, 0x07030602u);  // [a0 b0 a1 b1], [a2 b2 a3 b3]
+  const uint32_t cd01 = perm(d, c, 0x05010400u), cd23 = perm(d, c, 0x07030602u);
+  o[0] = perm(cd01, ab01, 0x05040100u);
+  o[1] = perm(cd01, ab01, 0x07060302u);
+  o[2] = perm(cd23, ab23, 0x05040100u);
+  o[3] = perm(cd23, ab23, 0x07060302u);
+}
+
+// Digit dwords of one word in the operand order of split_planes: v[p] holds
+// four digits (bytes 0..3) of the activation at position p of the word;
+// ev[s] / od[s] receive digit s of positions 0, 2, 4, 6 / 1, 3, 5, 7.
+__device__ __forceinline__ void plane_digits4(const uint32_t (&v)[8], uint32_t (&ev)[4], uint32_t (&od)[4]) {
+  transpose4(v[0], v[2], v[4], v[6], ev);
+  transpose4(v[1], v[3], v[5], v[7], od);
 }
 
 // Byte transpose of eight digit words: lo[p]/hi[p] hold digits 0..3 / 4..5 of

@@ -532,56 +532,61 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
       stage_unit8(tl, w8, xq, etop1);
   };
   // wide steps: digits of unit pair r (units 2r, 2r+1: words 2i, 2i+1 of k-group
-  // g of step st) of pass token tl, one dword per plane and digit column
+  // g of step st) of pass token tl, in the operand order of split_planes:
+  // word 2i + h goes to planes 2(i/2) (even positions) and 2(i/2) + 1 (odd),
+  // dword 2(i%2) + h of each 16-byte chunk
   auto stage_pair = [&](int tl, int r, const uint4 xa, const uint4 xb, int etop1) {
     const int st = r >> 4, gg = (r >> 2) & 3, i = r & 3;
-    uint8_t* base = s_lds + st * sbytes + 4 * i;
-    auto put = [&](int j, int col, uint32_t v) {
-      *(uint32_t*)(base + (j * NT + (col >> 4)) * 1024 + res_chunk(gg, col & 15, st) * 16) = v;
+    const int pe = 2 * (i >> 1);
+    uint8_t* base = s_lds + st * sbytes + 8 * (i & 1);
+    auto put = [&](int j, int h, int col, uint32_t v) {
+      *(uint32_t*)(base + 4 * h + (j * NT + (col >> 4)) * 1024 + res_chunk(gg, col & 15, st) * 16) = v;
     };
-    const uint32_t xs[2][8] = {{xa.x & 0xFFFFu, xa.x >> 16, xa.y & 0xFFFFu, xa.y >> 16, xa.z & 0xFFFFu, xa.z >> 16,
-                                xa.w & 0xFFFFu, xa.w >> 16},
-                               {xb.x & 0xFFFFu, xb.x >> 16, xb.y & 0xFFFFu, xb.y >> 16, xb.z & 0xFFFFu, xb.z >> 16,
-                                xb.w & 0xFFFFu, xb.w >> 16}};
-    uint32_t v0[8], v1[8], d[4][4];
-    if (W == 4) {
+    auto word = [&](int h, const uint4 xq) {
+      const uint32_t xs[8] = {xq.x & 0xFFFFu, xq.x >> 16, xq.y & 0xFFFFu, xq.y >> 16,
+                              xq.z & 0xFFFFu, xq.z >> 16, xq.w & 0xFFFFu, xq.w >> 16};
+      uint32_t v[8], ev[4], od[4];
+      if (W == 4) {
 #pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        v0[p] = x_digits4(xs[0][p], etop1);
-        v1[p] = x_digits4(xs[1][p], etop1);
+        for (int p = 0; p < 8; ++p) v[p] = x_digits4(xs[p], etop1);
+        plane_digits4(v, ev, od);
+#pragma unroll
+        for (int sd = 0; sd < 4; ++sd) {
+          put(pe, h, tl * 4 + sd, ev[sd]);
+          put(pe + 1, h, tl * 4 + sd, od[sd]);
+        }
+      } else {
+        // six digits: columns [d0 d1 d2 0 d3 d4 d5 0]
+        uint32_t hv[8], eh[4], oh[4];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          const uint64_t z = x_digits(xs[p], etop1);
+          v[p] = (uint32_t)z;
+          hv[p] = (uint32_t)(z >> 32);
+        }
+        plane_digits4(v, ev, od);
+        plane_digits4(hv, eh, oh);
+        put(pe, h, tl * 8 + 0, ev[0]);
+        put(pe, h, tl * 8 + 1, ev[1]);
+        put(pe, h, tl * 8 + 2, ev[2]);
+        put(pe, h, tl * 8 + 3, 0u);
+        put(pe, h, tl * 8 + 4, ev[3]);
+        put(pe, h, tl * 8 + 5, eh[0]);
+        put(pe, h, tl * 8 + 6, eh[1]);
+        put(pe, h, tl * 8 + 7, 0u);
+        put(pe + 1, h, tl * 8 + 0, od[0]);
+        put(pe + 1, h, tl * 8 + 1, od[1]);
+        put(pe + 1, h, tl * 8 + 2, od[2]);
+        put(pe + 1, h, tl * 8 + 3, 0u);
+        put(pe + 1, h, tl * 8 + 4, od[3]);
+        put(pe + 1, h, tl * 8 + 5, oh[0]);
+        put(pe + 1, h, tl * 8 + 6, oh[1]);
+        put(pe + 1, h, tl * 8 + 7, 0u);
       }
-      plane_words4(v0, v1, d);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int sd = 0; sd < 4; ++sd) put(j, tl * 4 + sd, d[j][sd]);
-      return;
-    }
-    // six digits: columns [d0 d1 d2 0 d3 d4 d5 0]
-    uint32_t h0[8], h1[8], e[4][4];
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const uint64_t z0 = x_digits(xs[0][p], etop1), z1 = x_digits(xs[1][p], etop1);
-      v0[p] = (uint32_t)z0;
-      h0[p] = (uint32_t)(z0 >> 32);
-      v1[p] = (uint32_t)z1;
-      h1[p] = (uint32_t)(z1 >> 32);
-    }
-    plane_words4(v0, v1, d);
-    plane_words4(h0, h1, e);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      put(j, tl * 8 + 0, d[j][0]);
-      put(j, tl * 8 + 1, d[j][1]);
-      put(j, tl * 8 + 2, d[j][2]);
-      put(j, tl * 8 + 3, 0u);
-      put(j, tl * 8 + 4, d[j][3]);
-      put(j, tl * 8 + 5, e[j][0]);
-      put(j, tl * 8 + 6, e[j][1]);
-      put(j, tl * 8 + 7, 0u);
-    }
+    };
+    word(0, xa);
+    word(1, xb);
   };
-
 
   // ---- range of every token's x: largest |x| and smallest non-zero exponent ----
   // (register j or pair k of a lane belongs to one token for the whole wave
@@ -658,16 +663,24 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
       // registers); units of token m are [m * npr, (m + 1) * npr)
 #pragma unroll 1
       for (int k = 0; k < kResXRegs / 2 && k * kResThreads < (p0 + ntok) * npr; ++k) {
+        // (an empty asm in each branch keeps the branches: merged into an
+        // indexed load, x would move to scratch memory)
         uint4 xa = xv[0], xb = xv[1];
         if (k == 1) {
           xa = xv[2];
           xb = xv[3];
+          opaque4(xa);
+          opaque4(xb);
         } else if (k == 2) {
           xa = xv[4];
           xb = xv[5];
+          opaque4(xa);
+          opaque4(xb);
         } else if (k == 3) {
           xa = xv[6];
           xb = xv[7];
+          opaque4(xa);
+          opaque4(xb);
         }
         const int u = tid + k * kResThreads;
         const int m = u / npr;
