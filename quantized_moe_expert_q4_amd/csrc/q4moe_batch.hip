@@ -38,6 +38,8 @@ constexpr int kBatWaves = 16;
 constexpr int kBatThreads = kBatWaves * 64;
 constexpr int kBatBuf = 72 * 1024;        // one of two digit buffers
 constexpr int kEpStride = 52;             // int32 row stride of a wave's 16 x C epilogue matrix
+constexpr int kBatBitSlots = 2048;        // slots a routing bitmap covers
+constexpr int kBatBitWords = kBatBitSlots / 32;
 
 static_assert(kBatWaves * 16 * kEpStride * 4 <= kBatBuf, "epilogue matrices fit one digit buffer");
 
@@ -76,6 +78,8 @@ void batch_kernel(const GateUpParams a) {
   __shared__ int s_xmin[G];                  // smallest non-zero exponent field of each token
   __shared__ int s_wcnt[kBatWaves];
   __shared__ int s_invalid;
+  __shared__ uint32_t s_bits[kBatBitWords];  // routed slots
+  __shared__ int s_bpre[kBatBitWords + 1];   // routed slots before each word, and in all
   __shared__ __attribute__((aligned(16))) uint16_t s_sig[kSigTable];  // bf16 sigmoid of the tabulated gT
 
   const int tid = threadIdx.x;
@@ -89,9 +93,7 @@ void batch_kernel(const GateUpParams a) {
   const int S = a.steps;                     // K-steps per tile, even
   constexpr int RT = DOWN ? 32 : 16;         // rows per tile
   const int tps = (I + RT - 1) / RT;
-  const int T = a.num_slots * tps;
   const int NB = gridDim.x;
-  const int v0 = (int)((int64_t)blockIdx.x * T / NB), v1 = (int)((int64_t)(blockIdx.x + 1) * T / NB);
   const uint32_t rbytes = row_bytes<Q8>(H);  // bytes of one weight row
   const uint32_t wbytes = (uint32_t)((uint64_t)I * rbytes);
 
@@ -124,12 +126,58 @@ void batch_kernel(const GateUpParams a) {
     if (tid == 0 && a.invalid_count) *a.invalid_count = s_invalid;
   }
 
+  // ---- routed slots: a grouped call over at most kBatBitSlots slots cuts
+  // only the tiles of the slots its ids name (T = routed slots x tiles per
+  // slot) into whole-tile ranges; the bitmap of routed slots and its word
+  // prefix counts stay in LDS ----
+  const bool compact = grouped && a.num_slots <= kBatBitSlots;
+  int R = grouped ? a.num_slots : 1;
+  if (compact) {
+    const int nw = (a.num_slots + 31) >> 5;
+    if (tid < kBatBitWords) s_bits[tid] = 0u;
+    __syncthreads();
+    for (int p = tid; p < P; p += kBatThreads) {
+      const int id = a.ids[p];
+      if (id >= 0 && id < a.num_slots) atomicOr(&s_bits[id >> 5], 1u << (id & 31));
+    }
+    __syncthreads();
+    // routed slots before word l, by wave 0
+    if (wave == 0) {
+      const int c = lane < nw ? (int)__popc(s_bits[lane]) : 0;
+      int incl = c;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(incl, d);
+        if (lane >= d) incl += o;
+      }
+      s_bpre[lane] = incl - c;
+      if (lane == 63) s_bpre[64] = incl;
+    }
+    __syncthreads();
+    R = s_bpre[64];
+  }
+  // slot of routed index r (wave-uniform): the word whose prefix brackets r,
+  // then the bit within it (LDS reads only, once per slot segment)
+  auto select = [&](int r) {
+    if (!compact) return r;
+    int lo = 0;
+#pragma unroll
+    for (int step = 32; step > 0; step >>= 1)
+      if (s_bpre[lo + step] <= r) lo += step;
+    uint32_t bits = s_bits[lo];
+    for (int j = r - s_bpre[lo]; j > 0; --j) bits &= bits - 1u;
+    return 32 * lo + (int)__builtin_ctz(bits);
+  };
+  const int T = R * tps;
+  const int v0 = (int)((int64_t)blockIdx.x * T / NB), v1 = (int)((int64_t)(blockIdx.x + 1) * T / NB);
+
   int v = v0;
   while (v < v1) {
-    const int e = v / tps;
-    const int t0 = v - e * tps;
-    const int t1 = min(v1, (e + 1) * tps) - e * tps;
-    v = e * tps + t1;
+    const int ri = v / tps;                            // routed index of the slot
+    const int t0 = v - ri * tps;
+    const int t1 = min(v1, (ri + 1) * tps) - ri * tps;
+    v = ri * tps + t1;
+    const int e = select(ri);
     const uint8_t* slot = a.slots + (uint64_t)e * a.slot_stride;
     const __amdgpu_buffer_rsrc_t gsrc = make_rsrc(slot + a.gate_w_off, wbytes);
     // DOWN: rows 16..31 of each tile are the same matrix 16 rows further on
