@@ -74,6 +74,7 @@ void batch_kernel(const GateUpParams a) {
   constexpr int G = (16 * NT) / 4;
   __shared__ __attribute__((aligned(16))) uint8_t s_buf[2 * kBatBuf];  // two digit buffers, or one spanning both
   __shared__ int s_pairs[G];
+  __shared__ int s_tok[G];                   // token (x row) of each pair of the group
   __shared__ int s_xmax[G];
   __shared__ int s_xmin[G];                  // smallest non-zero exponent field of each token
   __shared__ int s_wcnt[kBatWaves];
@@ -234,6 +235,8 @@ void batch_kernel(const GateUpParams a) {
         count = min(found, G);
       }
       if (count <= 0) break;
+      if (tid < count) s_tok[tid] = s_pairs[tid] / a.K;
+      __syncthreads();
       const int nbatch = (t1 - t0 + kBatWaves - 1) / kBatWaves;
 
       const int nxu = count * (H / 8);                 // 16-byte units of x, token-major
@@ -272,10 +275,10 @@ void batch_kernel(const GateUpParams a) {
         if (u < nxu) {
           const int w8 = u - ti * (H / 8);
           if (xf) {
-            const uint4* xp = (const uint4*)((const float*)a.x + (uint64_t)(s_pairs[ti] / a.K) * H + 8 * w8);
+            const uint4* xp = (const uint4*)((const float*)a.x + (uint64_t)s_tok[ti] * H + 8 * w8);
             f32_range8(xp[0], xp[1], mx, mn);
           } else {
-            const uint4 xq = *(const uint4*)(a.x + (uint64_t)(s_pairs[ti] / a.K) * H + 8 * w8);
+            const uint4 xq = *(const uint4*)(a.x + (uint64_t)s_tok[ti] * H + 8 * w8);
             range8(xq, mx, mn);
           }
         }
@@ -362,22 +365,29 @@ void batch_kernel(const GateUpParams a) {
       auto stage = [&](int c, uint8_t* buf) {
         const int k0c = c * spc * 128;
         const int n8 = min(spc, S - c * spc) * 16;
+        // unit u = w8 * count + ti, stepped by kBatThreads without dividing
+        const int qd = kBatThreads / count, rd = kBatThreads - qd * count;
+        int ti = tid % count, w8 = tid / count;
         for (int u = tid; u < count * n8; u += kBatThreads) {
-          const int ti = u % count;
-          const int w8 = u / count;
           const int k0 = k0c + 8 * w8;
           if (xf) {
             uint4 xa = make_uint4(0, 0, 0, 0), xb = make_uint4(0, 0, 0, 0);
             if (k0 < H) {
-              const uint4* xp = (const uint4*)((const float*)a.x + (uint64_t)(s_pairs[ti] / a.K) * H + k0);
+              const uint4* xp = (const uint4*)((const float*)a.x + (uint64_t)s_tok[ti] * H + k0);
               xa = xp[0];
               xb = xp[1];
             }
             stage_unitf(buf, ti, w8, xa, xb);
           } else {
             uint4 xq = make_uint4(0, 0, 0, 0);
-            if (k0 < H) xq = *(const uint4*)(a.x + (uint64_t)(s_pairs[ti] / a.K) * H + k0);
+            if (k0 < H) xq = *(const uint4*)(a.x + (uint64_t)s_tok[ti] * H + k0);
             stage_unit(buf, ti, w8, xq);
+          }
+          ti += rd;
+          w8 += qd;
+          if (ti >= count) {
+            ti -= count;
+            ++w8;
           }
         }
         // x was loaded after the weights in flight and is used up here, so
@@ -449,15 +459,7 @@ void batch_kernel(const GateUpParams a) {
           if (active) {
             const int j = cc & 3;
             const int row = tile * RT + 4 * g4 + j;
-            auto quad_row_sum = [&](const v4i acc) {
-              const int64_t w0 = (int64_t)acc[0] << (8 * j), w1 = (int64_t)acc[1] << (8 * j);
-              const int64_t w2 = (int64_t)acc[2] << (8 * j), w3 = (int64_t)acc[3] << (8 * j);
-              const bool up2 = (j & 2) != 0;
-              const int64_t r0 = __shfl_xor(up2 ? w0 : w2, 2), r1 = __shfl_xor(up2 ? w1 : w3, 2);
-              const int64_t k0 = (up2 ? w2 : w0) + r0, k1 = (up2 ? w3 : w1) + r1;   // rows (j&2), (j&2)+1
-              const int64_t r = __shfl_xor((j & 1) ? k0 : k1, 1);
-              return ((j & 1) ? k1 : k0) + r;
-            };
+            auto quad_row_sum = [&](const v4i acc) { return quad_digit_sum(acc, j); };
 #pragma unroll
             for (int n = 0; n < NT; ++n) {
               if (n < ntiles) {
@@ -466,18 +468,18 @@ void batch_kernel(const GateUpParams a) {
                 const int64_t vu = quad_row_sum(accu[n]);
                 if (ti < count && row < I) {
                   const int e2 = sum_exponent(s_xmax[ti]) + 16 + weight_exp_shift<Q8>();
-                  const float gate = round_scaled(vg >> 24, vg & 0xFFFFFF, e2, gscale[row]);
+                  const float gate = round_scaled53(vg, e2, gscale[row]);
                   const uint64_t o = (uint64_t)s_pairs[ti] * I + row;
                   if constexpr (DOWN) {
                     a.out[o] = bf16_rne(gate);
                     if (a.gate_probe) a.gate_probe[o] = gate;
                     if (row + 16 < I) {
-                      const float r16 = round_scaled(vu >> 24, vu & 0xFFFFFF, e2, gscale[row + 16]);
+                      const float r16 = round_scaled53(vu, e2, gscale[row + 16]);
                       a.out[o + 16] = bf16_rne(r16);
                       if (a.gate_probe) a.gate_probe[o + 16] = r16;
                     }
                   } else {
-                    const float up = round_scaled(vu >> 24, vu & 0xFFFFFF, e2, uscale[row]);
+                    const float up = round_scaled53(vu, e2, uscale[row]);
                     a.out[o] = swiglu_tail_tab(gate, up, s_sig);
                     if (a.gate_probe) a.gate_probe[o] = gate;
                     if (a.up_probe) a.up_probe[o] = up;

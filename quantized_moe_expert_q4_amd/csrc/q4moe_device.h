@@ -170,15 +170,24 @@ __device__ __forceinline__ int quad_dpp(int v) {
   return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
 }
 
-// The value held by lane l ^ 1 (or l ^ 2) of the same lane quad, through a
-// DPP quad permute (no LDS round trip).
-template <int X>
-__device__ __forceinline__ int64_t quad_xor(int64_t v) {
-  static_assert(X == 1 || X == 2, "quad lane xor");
-  constexpr int ctrl = X == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, ctrl, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)((uint64_t)v >> 32), ctrl, 0xF, 0xF, false);
-  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+// Exact (row, token) sum of the four digit columns of a lane quad of an MFMA
+// 16x16 int32 result (lane 16g + c holds rows 4g..4g+3 of column c; columns
+// 4t..4t+3 are digits 0..3 of token t): lane j = c % 4 of the quad receives
+// row 4g + j, d0 + d1 2^8 + d2 2^16 + d3 2^24.  A 4x4 transpose of the
+// quad's int32 values (lane bit 1 exchanged with register bit 1, then bit 0
+// with bit 0, each a DPP quad permute and a select) leaves the lane with the
+// four digit sums of its row.
+__device__ __forceinline__ int64_t quad_digit_sum(const v4i acc, int j) {
+  const bool b1 = (j & 2) != 0, b0 = (j & 1) != 0;
+  const int x0 = quad_dpp<0x4E>(acc[2]), x1 = quad_dpp<0x4E>(acc[3]);
+  const int y0 = quad_dpp<0x4E>(acc[0]), y1 = quad_dpp<0x4E>(acc[1]);
+  const int t0 = b1 ? x0 : acc[0], t1 = b1 ? x1 : acc[1];
+  const int t2 = b1 ? acc[2] : y0, t3 = b1 ? acc[3] : y1;
+  const int p0 = quad_dpp<0xB1>(t0), p1 = quad_dpp<0xB1>(t1);
+  const int p2 = quad_dpp<0xB1>(t2), p3 = quad_dpp<0xB1>(t3);
+  const int d0 = b0 ? p1 : t0, d1 = b0 ? t1 : p0;
+  const int d2 = b0 ? p3 : t2, d3 = b0 ? t3 : p2;
+  return (int64_t)d0 + ((int64_t)d1 << 8) + ((int64_t)d2 << 16) + ((int64_t)d3 << 24);
 }
 
 // Largest (MAX) or smallest value of v over the 64 lanes of a wave, returned

@@ -760,24 +760,10 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
   // step is taken one step ahead, in the step loop)
   if constexpr (LINE) take(0, ua + kResD < ub);
 
-  // exact (row, token) sum of the four digit columns of a lane quad: lane j
-  // of the quad receives row 4*g4 + j.  A 4x4 transpose of the quad's int32
-  // digit sums (lane bit 1 exchanged with register bit 1, then bit 0 with
-  // bit 0, each a DPP quad permute and a select) leaves the lane with the
-  // four digit sums of its row, combined as d0 + d1 2^8 + d2 2^16 + d3 2^24.
+  // exact (row, token) sums of the four digit columns of each lane quad:
+  // lane j of the quad receives row 4*g4 + j
   const int qj = cc & 3;
-  const bool qb1 = (qj & 2) != 0, qb0 = (qj & 1) != 0;
-  auto quad_row_sum = [&](const v4i acc) {
-    const int x0 = quad_dpp<0x4E>(acc[2]), x1 = quad_dpp<0x4E>(acc[3]);
-    const int y0 = quad_dpp<0x4E>(acc[0]), y1 = quad_dpp<0x4E>(acc[1]);
-    const int t0 = qb1 ? x0 : acc[0], t1 = qb1 ? x1 : acc[1];
-    const int t2 = qb1 ? acc[2] : y0, t3 = qb1 ? acc[3] : y1;
-    const int p0 = quad_dpp<0xB1>(t0), p1 = quad_dpp<0xB1>(t1);
-    const int p2 = quad_dpp<0xB1>(t2), p3 = quad_dpp<0xB1>(t3);
-    const int d0 = qb0 ? p1 : t0, d1 = qb0 ? t1 : p0;
-    const int d2 = qb0 ? p3 : t2, d3 = qb0 ? t3 : p2;
-    return (int64_t)d0 + ((int64_t)d1 << 8) + ((int64_t)d2 << 16) + ((int64_t)d3 << 24);
-  };
+  auto quad_row_sum = [&](const v4i acc) { return quad_digit_sum(acc, qj); };
   // this lane's B-fragment chunk for steps 0..3 mod 4
   static_assert(kResU % kResD == 0, "the step loop's pass covers whole turns of the ring");
   int rdo[kResU];
