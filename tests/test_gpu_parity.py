@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_helpers import check_parity, run_grouped, run_single, say
+from tests.gpu_helpers import check_parity, run_grouped, run_single, say, t1_violations
 
 pytestmark = pytest.mark.gpu
 
@@ -174,9 +174,49 @@ def test_wide_exponent_range_within_certified_bound():
     bound = 8 * H * np.exp2(etop1 - 173)[:, None] * gs[None, :]
     err = np.abs(g.astype(np.float64) - gr.astype(np.float64))
     ok = err <= 1e-5 * np.abs(gr) + 1e-6 + bound * (1 + 1e-6) + np.abs(gr) * 2.0 ** -23
-    say(f"[wide exponents] max err/bound = {float(np.max(err / (bound + 1e-300))):.3g}")
+    t1 = t1_violations(g, gr)
+    say(f"[wide exponents] max err/bound = {float(np.max(err / (bound + 1e-300))):.3g}; "
+        f"T1 violations {t1}/{g.size}")
     assert ok.all()
+    # on these inputs (random exponents, no cancellation built in) the
+    # rounded small entries stay inside plain T1 as well
+    assert t1 == 0
     assert np.array_equal(g[0].view(np.uint32), gr[0].view(np.uint32))
+
+
+def test_entries_below_the_exact_window_follow_the_stated_bound():
+    """The limit of the exact window, shown on purpose.  A token with one
+    entry of 2^40 and the rest near 2^-10 spans 50 binades; its entries more
+    than 38 binades below the largest are rounded to the 2^(e_top - 38) grid
+    (those more than 46 below, as here, to zero).  Rows whose weight at the
+    huge entry is zero (nibble 8) then lose their whole true sum: the result
+    stays within the stated bound but T1 does not hold for them.  The
+    ordinary token next to it stays bit-exact."""
+    H, I, M = 512, 32, 2
+    rng = np.random.default_rng(21)
+    lay = synth.contiguous_layout(H, I)
+    slot = synth.fill_slot(rng, H, I, lay)
+    words = np.frombuffer(slot, "<u4").copy()
+    for off in (lay.gate_weight_offset, lay.up_weight_offset):
+        rows = words[off // 4: off // 4 + I * H // 8].reshape(I, H // 8)
+        rows[:, 0] = (rows[:, 0] & ~np.uint32(0xF)) | np.uint32(8)     # weight 0 at k = 0
+    slot = words.view(np.uint8)
+    x = synth.bf16_normal(rng, (M, H))
+    small = (np.exp2(rng.uniform(-12, -8, H)) * np.where(rng.random(H) < 0.5, -1.0, 1.0)).astype(np.float32)
+    x[1] = (small.view(np.uint32) >> 16).astype(np.uint16)
+    x[1, 0] = (127 + 40) << 7                                         # 2^40
+    out, g, u = run_single(slot, lay, x, H, I)
+    gr, ur, orf = oracle.expert_gate_up(slot, lay, x, H, I)
+    gs = np.frombuffer(slot, "<f4", I, lay.gate_scale_offset).astype(np.float64)
+    etop1 = np.maximum((np.max(x & 0x7FFF, axis=1) >> 7) & 0xFF, 1).astype(np.float64)
+    bound = 8 * H * np.exp2(etop1 - 173)[:, None] * gs[None, :]
+    err = np.abs(g.astype(np.float64) - gr.astype(np.float64))
+    t1 = t1_violations(g[1], gr[1])
+    say(f"[below the window] token 1: max err {float(err[1].max()):.3g}, bound {float(bound[1].max()):.3g}, "
+        f"T1 violations {t1}/{I}")
+    assert (err <= bound * (1 + 1e-6) + np.abs(gr) * 2.0 ** -23 + 1e-30).all()
+    assert np.array_equal(g[0].view(np.uint32), gr[0].view(np.uint32))
+    assert np.array_equal(u[0].view(np.uint32), ur[0].view(np.uint32))
 
 
 def test_nonfinite_token_gives_nan_rows_only():
