@@ -289,7 +289,13 @@ def exact_dots(w: np.ndarray, xbits: np.ndarray, xdtype: str = "bf16") -> Tuple[
 
 
 def scaled_f32(nums: List[List[int]], exps: List[int], scales: np.ndarray) -> np.ndarray:
-    """``RN_f32(S[i][m] * scale[i])`` for every row and token -> ``[M, I]``."""
+    """``RN_f32(S[i][m] * scale[i])`` for every row and token -> ``[M, I]``.
+
+    The scale is one F32 multiply after the reduction (page 52,
+    ``GATE_UP_SOURCE``), so a zero result has the sign of that IEEE product:
+    an exact-zero sum (``+0``, the sum starts from ``+0``) gives the scale's
+    sign, a non-zero sum times a signed zero scale gives the sign of the two
+    factors together."""
     I = len(nums)
     M = len(exps)
     out = np.empty((M, I), dtype=np.float32)
@@ -297,7 +303,7 @@ def scaled_f32(nums: List[List[int]], exps: List[int], scales: np.ndarray) -> np
         s = float(scales[i])
         sn, se = f32_parts(s)
         for m in range(M):
-            out[m, i] = f32_round_dyadic(nums[i][m] * sn, exps[m] + se, zero_sign=s)
+            out[m, i] = f32_round_dyadic(nums[i][m] * sn, exps[m] + se, zero_sign=s if nums[i][m] >= 0 else -s)
     return out
 
 

@@ -553,7 +553,8 @@ __device__ __forceinline__ int sum_exponent_f32(uint32_t xmax_bits) {
 // exactly, with integer arithmetic: the eight-digit sums have up to 88
 // significant bits, so the product with the scale's 24-bit significand
 // (up to 112 bits) is formed in two 64-bit words and rounded from its top
-// 64 bits and a sticky bit.  An exact zero takes the sign of the scale.
+// 64 bits and a sticky bit.  A zero result has the sign of the IEEE product:
+// the scale's for a zero sum, that of the two factors for a zero scale.
 __device__ float round_scaled_wide(int64_t hi, int64_t lo, int e2, float s) {
   // V = hi * 2^32 + lo as a sign and a 128-bit magnitude (vh:vl)
   const int64_t lo_hi = lo >> 32;                       // arithmetic: floor(lo / 2^32)
@@ -586,7 +587,7 @@ __device__ float round_scaled_wide(int64_t hi, int64_t lo, int e2, float s) {
   uint64_t nl = p0 + (p1 << 32);
   const uint64_t c = nl < p0 ? 1u : 0u;
   const uint64_t nh = (p1 >> 32) + p2 + c;
-  if ((nh | nl) == 0) return __uint_as_float(sb & 0x80000000u);   // exact zero: sign of the scale
+  if ((nh | nl) == 0) return __uint_as_float(neg ? 0x80000000u : 0u);   // V = 0 (neg: the scale's sign) or s = 0
   // top 64 bits T of N (its most significant bit at bit 63) and a sticky bit
   int msb;
   uint64_t T;

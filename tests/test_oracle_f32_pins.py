@@ -64,6 +64,33 @@ def test_f32_bruteforce_exact_rationals(seed):
             assert _bits(u[m, i]) == _bits(nearest_f32(su * Fraction(float(us[i])))) or (su == 0 and u[m, i] == 0)
 
 
+def test_f32_subnormal_tokens_bruteforce():
+    # f32 tokens of subnormals, alone and next to the smallest normal
+    # exponent, scaled up so that the F32 results stay normal
+    rng = np.random.default_rng(740)
+    H, I, M = 32, 4, 3
+    gn, un = rng.integers(0, 16, (I, H)), rng.integers(0, 16, (I, H))
+    gs = (rng.uniform(0.5, 2.0, I) * 2.0 ** 120).astype(np.float32)
+    us = (rng.uniform(0.5, 2.0, I) * 2.0 ** 120).astype(np.float32)
+    lay = synth.contiguous_layout(H, I)
+    gw, uw = synth.pack_nibbles(gn), synth.pack_nibbles(un)
+    slot = synth.write_slot(lay, H, I, gw, uw, gs, us)
+    bits = rng.integers(1, 1 << 23, (M, H)).astype(np.uint32) | (rng.integers(0, 2, (M, H)).astype(np.uint32) << 31)
+    bits[1, ::2] |= np.uint32(1 << 23)                # exponent field 1 (2**-126)
+    bits[2] = 0
+    bits[2, 3] = 0x00000003
+    x = bits.view(np.float32)
+    g, u, _ = oracle.expert_gate_up(slot, lay, x, H, I, xdtype="f32")
+    for m in range(M):
+        xv = [Fraction(float(v)) for v in x[m]]
+        for i in range(I):
+            sg = sum((unpack_nibble(gw, i, k) - 8) * xv[k] for k in range(H))
+            su = sum((unpack_nibble(uw, i, k) - 8) * xv[k] for k in range(H))
+            assert _bits(g[m, i]) == _bits(nearest_f32(sg * Fraction(float(gs[i])))) or (sg == 0 and g[m, i] == 0)
+            assert _bits(u[m, i]) == _bits(nearest_f32(su * Fraction(float(us[i])))) or (su == 0 and u[m, i] == 0)
+    assert np.all(np.abs(g[g != 0]) >= 2.0 ** -126)
+
+
 def test_f32_tail_against_rational_steps_and_closed_forms():
     rng = np.random.default_rng(73)
     g = np.concatenate([rng.standard_normal(400) * 4, rng.standard_normal(100) * 40,

@@ -221,6 +221,33 @@ def test_bruteforce_exact_rationals(seed):
             assert _bits(u[m, i]) == _bits(wu) or (su == 0 and u[m, i] == 0.0)
 
 
+def test_subnormal_tokens_bruteforce():
+    # tokens made of subnormal bf16 values, alone and next to the smallest
+    # normal exponent, with scales that keep the F32 results normal: an
+    # exponent slip at the subnormal boundary changes the result by 2x
+    rng = np.random.default_rng(140)
+    H, I, M = 64, 5, 3
+    gn, un = rng.integers(0, 16, (I, H)), rng.integers(0, 16, (I, H))
+    gs = (rng.uniform(0.5, 2.0, I) * 2.0 ** 110).astype(np.float32)
+    us = (rng.uniform(0.5, 2.0, I) * 2.0 ** 110).astype(np.float32)
+    gw, uw = synth.pack_nibbles(gn), synth.pack_nibbles(un)
+    lay, slot = _slot(H, I, gw, uw, gs, us)
+    sign = (rng.integers(0, 2, (M, H)) << 15).astype(np.uint16)
+    x = (rng.integers(1, 0x80, (M, H)).astype(np.uint16) | sign)   # exponent field 0
+    x[1, ::2] |= np.uint16(1 << 7)                                  # exponent field 1 (2**-126)
+    x[2] = 0
+    x[2, 7] = 0x0005
+    g, u, _ = oracle.expert_gate_up(slot, lay, x, H, I)
+    for m in range(M):
+        xv = [bf16_value(int(b)) for b in x[m]]
+        for i in range(I):
+            sg = sum((unpack_nibble(gw, i, k) - 8) * xv[k] for k in range(H))
+            su = sum((unpack_nibble(uw, i, k) - 8) * xv[k] for k in range(H))
+            assert _bits(g[m, i]) == _bits(nearest_f32(sg * Fraction(float(gs[i])))) or (sg == 0 and g[m, i] == 0)
+            assert _bits(u[m, i]) == _bits(nearest_f32(su * Fraction(float(us[i])))) or (su == 0 and u[m, i] == 0)
+    assert np.all(np.abs(g[g != 0]) >= 2.0 ** -126)
+
+
 # --------------------------------------------------------------------------
 # Invariants
 # --------------------------------------------------------------------------
@@ -274,6 +301,55 @@ def test_general_scale_factor_within_one_rounding():
     # (S * RN(s*c)) vs c * RN(S*s): both within ~2 ulps of S*s*c
     ratio = np.float64(g2) / (np.float64(g) * c)
     assert np.all(np.abs(ratio - 1.0) < 4 * 2.0 ** -24)
+
+
+def test_negated_scales_negate_gate_and_up_bit_for_bit():
+    # RN(-v) = -RN(v), and a zero result takes the sign of the IEEE product
+    rng, lay, slot, x, H, I = _random_expert(27)
+    x[0] = 0                                           # exact-zero sums: +0 * s
+    g, u, _ = oracle.expert_gate_up(slot, lay, x, H, I)
+    g2, u2, _ = oracle.expert_gate_up(_with_scales(slot, lay, I, -1.0, -1.0), lay, x, H, I)
+    assert np.array_equal(_bits(g2), _bits(-g)) and np.array_equal(_bits(u2), _bits(-u))
+    assert np.all(_bits(g2[0]) == 0x80000000)
+
+
+_F32_OVERFLOW = Fraction(2) ** 128 - Fraction(2) ** 103     # fmax + half an ulp: ties go to infinity
+
+
+def _ieee_scaled(S, s):
+    """F32 value of ``S * s`` for an exact sum ``S`` and an F32 scale ``s``:
+    zeros from numpy's float32 multiply (which fixes their sign), infinities
+    beyond the overflow threshold, else the nearest float32."""
+    if S == 0 or s == 0:
+        return np.float32(np.sign(float(S))) * np.float32(s)
+    v = S * Fraction(float(s))
+    if abs(v) >= _F32_OVERFLOW:
+        return np.float32(math.copysign(math.inf, v))
+    r = nearest_f32(v)
+    return np.float32(math.copysign(0.0, v)) if r == 0 else r
+
+
+def test_signed_zero_subnormal_and_huge_scales():
+    H, I, M = 64, 10, 4
+    rng = np.random.default_rng(28)
+    gn = rng.integers(0, 16, (I, H))
+    un = rng.integers(0, 16, (I, H))
+    gs = np.array([0.0, -0.0, 1e-45, -3e-39, 2.0 ** -126, 1e38, -1e38, 0.75, -0.01, 3.4e38], dtype=np.float32)
+    us = gs[::-1].copy()
+    gw, uw = synth.pack_nibbles(gn), synth.pack_nibbles(un)
+    lay, slot = _slot(H, I, gw, uw, gs, us)
+    x = synth.bf16_normal(rng, (M, H))
+    x[1] = 0                                           # exact-zero sums
+    x[2, :8] = 0x7149                                  # ~1e30: products far beyond F32
+    g, u, _ = oracle.expert_gate_up(slot, lay, x, H, I)
+    for m in range(M):
+        xv = [bf16_value(int(b)) for b in x[m]]
+        for i in range(I):
+            sg = sum((unpack_nibble(gw, i, k) - 8) * xv[k] for k in range(H))
+            su = sum((unpack_nibble(uw, i, k) - 8) * xv[k] for k in range(H))
+            assert _bits(g[m, i]) == _bits(_ieee_scaled(sg, gs[i])), (m, i)
+            assert _bits(u[m, i]) == _bits(_ieee_scaled(su, us[i])), (m, i)
+    assert np.any(np.isinf(g)) and np.any(_bits(g) == 0x80000000) and np.any((_bits(g) & 0x7F800000) == 0)
 
 
 def test_negated_input_negates_gate_and_up():
