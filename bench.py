@@ -60,7 +60,8 @@ SEEDS = {"pool": SEED, "expert_pool": SEED + 1000, "f32_x": SEED + 2000, "q8_poo
 
 # the sources of the gate/up and down kernels and their launchers (a change in
 # any of them invalidates stored counters and parity statistics)
-KERNEL_SOURCES = ["q4moe_device.h", "q4moe_launch.h", "q4moe_resident.hip", "q4moe_batch.hip", "q4moe_sigmoid.hip"]
+KERNEL_SOURCES = ["q4moe_device.h", "q4moe_launch.h", "q4moe_resident.hip", "q4moe_batch.hip", "q4moe_chunked.hip",
+                  "q4moe_sigmoid.hip"]
 
 
 def kernel_sha() -> str:
@@ -95,15 +96,20 @@ def down_bytes_per_slot(H_: int = H, I_: int = I) -> int:
     return H_ * I_ // 2 + 4 * H_
 
 
-def kernel_label(M: int, H_: int) -> str:
+def kernel_label(M: int, H_: int, per_slot: int = None) -> str:
     """The gate/up kernel the library launches for a call whose slots see up
-    to M tokens (the selection rule of q4moe_resident.hip: resident digits for
-    up to eight tokens when their digits fit LDS, else the K-chunked batch
-    kernel)."""
+    to M tokens, `per_slot` routed pairs per slot on average (grouped calls;
+    None for a single expert): the selection rule of q4moe_resident.hip --
+    resident digits for up to eight tokens when their digits fit LDS, else the
+    chunked kernel for a few rows per slot, else the batch kernel."""
     nt = 1 if M <= 2 else 2
     steps = ((H_ + 255) // 256 + 3) // 4 * 4
     fits = M <= 8 and M * ((H_ // 8 + 1) // 2) * 2 <= 8 * 512 and steps * 4096 * nt + 7 * nt * 1024 <= 144 * 1024
-    return "q4::resident_kernel" if fits else "q4::batch_kernel"
+    if fits:
+        return "q4::resident_kernel"
+    if (per_slot if per_slot is not None else M) <= (6 if per_slot is not None else 8):
+        return "q4::chunked_kernel"
+    return "q4::batch_kernel"
 
 
 def large_shape_host(M: int):
@@ -485,7 +491,7 @@ def large_legs(args, legs, shapes):
             pool.bytes_per_step(), sec, per,
             f"H={LARGE_H} I={LARGE_I}, M={M} (x with 1% of entries at +-9984), {LARGE_SLOTS}-slot cold pool "
             f"({pool.bytes_per_step() / 1e9:.3f} GB per step), one grouped launch per step",
-            kernel_label(M, LARGE_H), rows=M * LARGE_SLOTS * LARGE_I)
+            kernel_label(M, LARGE_H, per_slot=M), rows=M * LARGE_SLOTS * LARGE_I)
         del pool
         torch.cuda.empty_cache()
 
@@ -504,7 +510,7 @@ def routed_legs(args, legs, shapes):
         nb = touched * weight_bytes_per_slot(c.H, c.I)
         shapes["routed_step_m32_top8"] = leg(
             nb, sec, per, f"{c.num_slots} experts of H={c.H} I={c.I}, M={c.M} tokens, top-{c.K} routing ({touched} "
-            f"slots touched, {nb / 1e9:.3f} GB per step), one grouped launch per step", kernel_label(c.M, c.H),
+            f"slots touched, {nb / 1e9:.3f} GB per step), one grouped launch per step", kernel_label(c.M, c.H, per_slot=-(-c.M * c.K // c.num_slots)),
             rows=c.M * c.K * c.I)
     if "ep_share" in legs:
         # one GPU's share of the routed step under 8-way expert parallelism: 8
@@ -524,7 +530,7 @@ def routed_legs(args, legs, shapes):
             nb, sec / n, [p / n for p in per],
             f"one GPU's expert-parallel share of the routed step: 32 routed token rows (K=1) over 8 local "
             f"experts of H={c.H} I={c.I} ({nb / 1e6:.1f} MB per step; {n} steps on rotating slots of the "
-            f"{c.num_slots}-slot pool, captured in one HIP graph)", kernel_label(32, c.H), rows=32 * c.I,
+            f"{c.num_slots}-slot pool, captured in one HIP graph)", kernel_label(32, c.H, per_slot=-(-32 // c.num_slots)), rows=32 * c.I,
             us_per_step=round(sec / n * 1e6, 2))
     del pool
     torch.cuda.empty_cache()
@@ -542,14 +548,14 @@ def expert_legs(args, legs, shapes):
         shapes["down_pool_m1"] = leg(
             nb, sec, per, f"down projection H={H} I={I}, one token's mid row per slot on a {EXPERT_SLOTS}-slot cold "
             f"pool of whole-expert slots ({nb / 1e9:.3f} GB of down weights+scales per step), one grouped launch",
-            "q4::batch_kernel (down mode)", rows=EXPERT_SLOTS * H)
+            "q4::chunked_kernel (down mode)", rows=EXPERT_SLOTS * H)
     if "forward" in legs:
         sec, per = timed(pool.forward_fn(), args.steps, args.warmup)
         nb = EXPERT_SLOTS * (weight_bytes_per_slot() + down_bytes_per_slot())
         shapes["forward_pool_m1"] = leg(
             nb, sec, per, f"whole expert (gate/up+SwiGLU then down) H={H} I={I}, one token routed to every slot of "
             f"a {EXPERT_SLOTS}-slot cold pool ({nb / 1e9:.3f} GB per step), two launches per step",
-            "q4::resident_kernel then q4::batch_kernel (down mode)")
+            "q4::resident_kernel then q4::chunked_kernel (down mode)")
     del pool
     torch.cuda.empty_cache()
 

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libq4moe.so")
 
-SOURCES = ["q4moe_resident.hip", "q4moe_batch.hip", "q4moe_stream.hip", "q4moe_sigmoid.hip", "q4moe_noalloc.hip",
+SOURCES = ["q4moe_resident.hip", "q4moe_batch.hip", "q4moe_chunked.hip", "q4moe_stream.hip", "q4moe_sigmoid.hip", "q4moe_noalloc.hip",
            "q4moe_abi.cpp"]
 
 FLAGS = [

@@ -1,0 +1,920 @@
+// Q4 gate/up + SwiGLU (and the down projection) for routed calls with a few
+// tokens per slot whose digits do not all fit LDS for the launch: the routed
+// step of a mixture-of-experts layer, the down projection of one routed row
+// per slot, one GPU's share of expert-parallel routing.
+//
+// Arithmetic: GATE_UP_SOURCE and DOWN_SOURCE of the @mlx-bun/inference 1.0.0
+// diff, page 52 (kernels/glm52/streamed-experts.ts), made exact as in
+// q4moe_device.h.
+//
+// The weight stream is the resident kernel's: 16-row tiles, wide K-steps of
+// 256 packed nibbles per row loaded in whole 128-byte lines with the
+// non-temporal hint and moved to the operand layout by a lane shuffle, D steps
+// in flight per wave in a register ring that takes each step one step ahead.
+// What differs is where the activation digits come from:
+//  * One persistent 8-wave work-group per CU takes an even share of the
+//    (slot, pass, tile) units: a slot with c routed pairs takes ceil(c/G)
+//    passes over its tiles (G = 7 pairs at two column tiles, 4 at one).  It walks its share in segments (one
+//    pass over at most kChSegTiles tiles of one slot), each in token groups:
+//    as many of the pass's pairs as fit 16*NT digit columns, four per row or
+//    eight for a row whose values need six digits.
+//  * A group's digits are split from x into LDS per K-chunk, double buffered
+//    (once for the whole K when it fits both buffers).
+//  * A segment's tiles are cut into rounds of at most kChRoundTiles tiles.
+//    The (round, chunk) elements of a group form one stream that every wave
+//    walks in the same order; in each element a wave takes the same fraction
+//    of the round's tiles (its (tile, K-step) units, in whole passes of the
+//    step loop: a SIMD's quarter, the first wave of the SIMD a little more
+//    than half of it), so it meets at most kChMaxT tiles of a round and keeps
+//    their sums in registers from chunk to chunk.  A tile met by several waves
+//    collects their exact quad sums in an LDS fix-up slot (LDS atomics); the
+//    last contributor finishes it.
+//  * The digits of element k+1 are staged while element k is multiplied: a
+//    wave's share is cut into one 32-byte piece of x per lane per pass of the
+//    step loop, loaded at a pass's last step and split into LDS one pass
+//    later, so the waits for x never cover the weight loads in flight.  One
+//    barrier per element.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <atomic>
+
+#include "q4moe_device.h"
+#include "q4moe_launch.h"
+
+namespace q4 {
+
+namespace {
+
+constexpr int kChWaves = 8;
+constexpr int kChThreads = kChWaves * 64;
+constexpr int kChBuf = 64 * 1024;          // one of the two digit buffers
+constexpr int kChU = 2;                    // K-steps per pass of the step loop
+constexpr int kChD = 2;                    // K-steps in flight per wave
+constexpr int kChRoundTiles = 14;          // tiles per round
+constexpr int kChMaxT = 3;                 // tiles one wave meets in a round
+constexpr int kChSegTiles = 48;            // tiles per segment (row scales held in LDS)
+constexpr int kChFixSlots = kChWaves - 1;
+constexpr int kChCntSlots = 2048;          // slots whose passes are held in LDS
+constexpr int kChIdRegs = 4;               // routing ids held per thread (2048 pairs)
+constexpr int kChCntWords = kChCntSlots / 32;
+constexpr int kChInvBatch = 64;            // invalid pairs zero-filled per batch
+
+// A wave's share of a round's units: the first wave of SIMD q takes the
+// fraction [q/4, q/4 + share/4096) of the round's tiles, the second wave the
+// rest of the quarter, share in [kChShareMin, kChShareMax] (the first wave of a
+// SIMD wins its issue arbitration more often).  With at most kChRoundTiles
+// tiles a share spans under two tiles, so it meets at most kChMaxT tiles.
+constexpr int kChShareMin = 439, kChShareMax = 585;
+static_assert(kChShareMax * kChRoundTiles < 2 * 4096 && (1024 - kChShareMin) * kChRoundTiles < 2 * 4096,
+              "a wave's share of a round meets at most kChMaxT tiles");
+
+// One wide K-step of digits: [plane 4][column tile n][k-group g 4][16 x 16
+// bytes]; the 16-byte chunk of column c sits at position c ^ 4g of its
+// k-group row (the sixteen lanes of a k-group read sixteen distinct chunks).
+__host__ __device__ constexpr int ch_step_bytes(int nt) { return 4 * nt * 1024; }
+__host__ __device__ constexpr int ch_chunk(int g, int c) { return g * 16 + (c ^ (4 * g)); }
+// One fix-up slot: int64 [tile][gate, up][lane] (quad sums).
+__host__ __device__ constexpr int ch_fix_words(int nt) { return nt * 2 * 64; }
+// Wide K-steps per tile, padded to whole passes of the step loop (a padding
+// step meets zero digits).
+__host__ __device__ constexpr int ch_steps(int H) { return ((H + 255) / 256 + kChU - 1) / kChU * kChU; }
+// K-steps per chunk: the whole K when it fits both buffers, else what fits one.
+__host__ __device__ constexpr int ch_chunk_steps(int nt, int S) {
+  return S * ch_step_bytes(nt) <= 2 * kChBuf ? S : kChBuf / ch_step_bytes(nt) / kChU * kChU;
+}
+
+}  // namespace
+
+// DOWN: the down projection (one matrix of a.I rows over a.H inputs; a tile is
+// 32 rows, its first 16 taking the gate role and the next 16 the up role,
+// each output rounded to bf16 on its own) instead of gate/up + SwiGLU.
+// WHOLE: the whole K's digits fit both buffers (one chunk), as the launcher
+// decides from H and NT.
+template <int NT, bool VEC, bool DOWN, bool WHOLE>
+__global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void chunked_kernel(const GateUpParams a) {
+  // pairs per pass: what fits 16*NT digit columns at four per row, with room
+  // for one row of eight at two column tiles (a pass then needs a second
+  // group only when two of its rows need six digits)
+  constexpr int G = NT == 2 ? 7 : 4;
+  constexpr int RT = DOWN ? 32 : 16;         // rows per tile
+  constexpr int sbytes = ch_step_bytes(NT);
+  __shared__ __attribute__((aligned(16))) uint8_t s_dig[2 * kChBuf];
+  __shared__ unsigned long long s_fix[kChFixSlots * ch_fix_words(NT)];
+  __shared__ int s_fixcnt[kChFixSlots];
+  __shared__ __attribute__((aligned(16))) uint16_t s_sig[DOWN ? 8 : kSigTable];
+  __shared__ float s_gsc[kChSegTiles * RT];   // row scales of the segment (DOWN: the down scales)
+  __shared__ float s_usc[DOWN ? 1 : kChSegTiles * RT];
+  __shared__ uint8_t s_pass[kChCntSlots];     // passes of each slot
+  __shared__ int s_ppre[kChCntWords + 1];     // passes of the slots before each 32-slot word, and in all
+  __shared__ int s_pairs[G];
+  __shared__ int s_tok[G];                   // x row of each pair of the group
+  __shared__ int s_xmax[G];
+  __shared__ int s_xmin[G];                  // smallest non-zero exponent field of each row
+  __shared__ int s_col[G];                   // first digit column of each row
+  __shared__ int s_wid[G];                   // digit columns of each row: 4, or 8 for six digits
+  __shared__ int s_quad[4 * NT];             // row of each 4-column quad; + 64 for the high quad of an 8-column row
+  __shared__ int s_wcnt[kChWaves];
+  __shared__ int s_inv;
+  __shared__ int s_ninv;
+  __shared__ int s_invl[kChInvBatch];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g4 = lane >> 4, cc = lane & 15;
+  const int qj = cc & 3;
+  const int H = a.H, I = a.I, K = a.K;
+  const int P = a.M * K;
+  const bool grouped = a.ids != nullptr;
+  const int S = a.steps;                     // wide K-steps per tile, a multiple of 4
+  const int Sc = WHOLE ? S : ch_chunk_steps(NT, S);
+  const int nch = WHOLE ? 1 : (S + Sc - 1) / Sc;
+  const int tps = (I + RT - 1) / RT;         // tiles per slot
+  const int NB = gridDim.x;
+  const uint32_t rbytes = (uint32_t)(H / 2);
+  const uint32_t wbytes = (uint32_t)((uint64_t)I * rbytes);
+  const int hw = H / 8;                      // 8-value units of one row of x
+
+  // ---- the sigmoid table, fix-up slots, routed slots, invalid ids ----
+  if constexpr (!DOWN) {
+    static_assert(kSigTable * 2 == 16 * kChThreads, "one 16-byte piece of the sigmoid table per thread");
+    *(uint4*)(s_sig + 8 * tid) = load_u4(make_rsrc(a.sig, kSigTable * 2), tid * 16u);
+  }
+  if (tid == 0) s_inv = 0;
+  if (tid < kChFixSlots) s_fixcnt[tid] = 0;
+  for (int i = tid; i < kChFixSlots * ch_fix_words(NT); i += kChThreads) s_fix[i] = 0;
+  // Work is cut by cost: a slot with c routed pairs takes ceil(c / G) passes
+  // over its tiles (pass g: its pairs g*G .. g*G + G - 1 in id order), and
+  // the (slot, pass, tile) units are split evenly over the work-groups, so a
+  // slot that many tokens chose spreads over more work-groups instead of
+  // lengthening the launch.  The passes are held for up to kChCntSlots slots,
+  // fewer than 65536 pairs and at most 255 passes a slot; otherwise every
+  // slot takes one pass, its pairs in as many groups as they need.
+  // The ids of the first kChIdRegs * kChThreads pairs stay in registers for
+  // the group scans.
+  const __amdgpu_buffer_rsrc_t idsrc = make_rsrc(a.ids, grouped ? (uint32_t)P * 4u : 0u);
+  int idr[kChIdRegs];
+#pragma unroll
+  for (int j = 0; j < kChIdRegs; ++j) {
+    const int p = tid + j * kChThreads;
+    const int id = (int)__builtin_amdgcn_raw_buffer_load_b32(idsrc, p * 4, 0, 0);
+    idr[j] = p < P ? id : -1;
+  }
+  // id of pair p = tid + j * kChThreads (a select over the held registers:
+  // indexed, they would move to scratch memory)
+  static_assert(kChIdRegs == 4, "id_at selects among four registers");
+  auto id_at = [&](int j, int p) {
+    if (j >= kChIdRegs) return p < P ? a.ids[p] : -1;
+    const int lo = j & 1 ? idr[1] : idr[0], hi = j & 1 ? idr[3] : idr[2];
+    return j & 2 ? hi : lo;
+  };
+  // pair counts per slot, in the digit buffer (free until the first group)
+  uint32_t* const cnt = (uint32_t*)s_dig;
+  const bool counting = grouped && a.num_slots <= kChCntSlots && P < 65536;
+  if (counting)
+    for (int i = tid; i < kChCntSlots; i += kChThreads) cnt[i] = 0u;
+  __syncthreads();
+  if (grouped) {
+    int inv = 0;
+    for (int j = 0; j * kChThreads < P; ++j) {
+      const int p = tid + j * kChThreads;
+      const int id = id_at(j, p);
+      if (p >= P) continue;
+      if (id >= 0 && id < a.num_slots) {
+        if (counting) atomicAdd(&cnt[id], 1u);
+      } else {
+        ++inv;
+      }
+    }
+    if (blockIdx.x == 0 && inv) atomicAdd(&s_inv, inv);
+  }
+  __syncthreads();
+  auto passes = [&](int c) { return (c + G - 1) / G; };
+  if (counting && wave == 0) {
+    // passes of the 32 slots of word `lane` (one byte each), then their prefix
+    // over words; a slot with more than 255 passes turns the counts off
+    int c = 0, big = 0;
+    for (int j = 0; j < 32; ++j) {
+      const int sl = 32 * lane + j;
+      const int ps = sl < a.num_slots ? passes((int)cnt[sl]) : 0;
+      big |= ps > 255;
+      s_pass[sl] = (uint8_t)ps;
+      c += ps;
+    }
+    int incl = c;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d);
+      if (lane >= d) incl += o;
+    }
+    s_ppre[lane] = incl - c;
+    if (lane == 63) s_ppre[64] = __any(big) ? -1 : incl;
+  }
+  if (grouped && blockIdx.x == 0 && tid == 0 && a.invalid_count) *a.invalid_count = s_inv;
+  __syncthreads();
+  const bool counted = counting && s_ppre[64] >= 0;
+  // passes in all: counted slots, one per slot, or the single slot's tokens
+  const int npass = counted ? s_ppre[64] : (grouped ? a.num_slots : passes(a.M));
+  // slot and pass of pass index pv (wave-uniform)
+  auto decode = [&](int pv, int& e, int& g) {
+    if (!grouped) {
+      e = 0;
+      g = pv;
+      return;
+    }
+    if (!counted) {
+      e = pv;
+      g = 0;
+      return;
+    }
+    int lo = 0;
+#pragma unroll
+    for (int step = 32; step > 0; step >>= 1)
+      if (s_ppre[lo + step] <= pv) lo += step;
+    int rem = pv - s_ppre[lo];
+    for (int sl = 32 * lo;; ++sl) {
+      const int ps = s_pass[sl];
+      if (rem < ps) {
+        e = sl;
+        g = rem;
+        return;
+      }
+      rem -= ps;
+    }
+  };
+  const int T = npass * tps;
+  const int v0 = (int)((int64_t)blockIdx.x * T / NB), v1 = (int)((int64_t)(blockIdx.x + 1) * T / NB);
+
+  // ---- per-lane constants ----
+  const LineLanes lines = line_lanes(lane);
+  const int rdo = ch_chunk(g4, cc) * 16;               // this lane's B-fragment chunk
+  // this wave's position in unit order (pos = 2 * SIMD + second wave) and the
+  // start of its share, in 1/4096 of a round's tiles
+  const int pos = 2 * (wave & 3) + (wave >> 2);
+  const int share = min(max(a.wave_share, kChShareMin), kChShareMax);
+  auto xfrac = [&](int k) { return k >= kChWaves ? 4096 : (k >> 1) * 1024 + ((k & 1) ? share : 0); };
+  // first and last tile that position k's share meets in a round of nt tiles
+  auto tile_lo = [&](int k, int nt) { return xfrac(k) * nt / 4096; };
+  auto tile_hi = [&](int k, int nt) { return min(xfrac(k + 1) * nt / 4096, nt - 1); };
+  // unit at which position k's share starts in an element of nt tiles and
+  // scc steps: the same tile fraction in every chunk, whole passes
+  auto unit_at = [&](int k, int nt, int scc) {
+    const int num = xfrac(k) * nt;
+    const int t = num / 4096;
+    return t * scc + ((num - t * 4096) * scc / 4096) / kChU * kChU;
+  };
+  // whole-line loads: lane L reads rows L / 8 and 8 + L / 8 of the tile
+  auto row_off = [&](int t, int part) {
+    const int row = t * RT + 8 * part + (lane >> 3);
+    return (uint32_t)(row < I ? row : I - 1) * rbytes + 16u * (uint32_t)(lane & 7);
+  };
+
+  // digits of x pair r (8-value units 2r, 2r+1: words 2i, 2i+1 of k-group gg
+  // of chunk step st) of group row tl, in the operand order of split_planes:
+  // word 2i + h goes to planes 2(i/2) (even positions) and 2(i/2) + 1 (odd),
+  // dword 2(i%2) + h of each 16-byte chunk
+  auto stage_pair = [&](uint8_t* buf, int W, int col0, int st, int gg, int i, const uint4 xa, const uint4 xb,
+                        int etop1) {
+    const int pe = 2 * (i >> 1);
+    uint8_t* base = buf + st * sbytes + 8 * (i & 1);
+    auto put = [&](int j, int h, int col, uint32_t v) {
+      *(uint32_t*)(base + 4 * h + (j * NT + (col >> 4)) * 1024 + ch_chunk(gg, col & 15) * 16) = v;
+    };
+    auto word = [&](int h, const uint4 xq) {
+      const uint32_t xs[8] = {xq.x & 0xFFFFu, xq.x >> 16, xq.y & 0xFFFFu, xq.y >> 16,
+                              xq.z & 0xFFFFu, xq.z >> 16, xq.w & 0xFFFFu, xq.w >> 16};
+      uint32_t v[8], ev[4], od[4];
+      if (W == 4) {
+#pragma unroll
+        for (int p = 0; p < 8; ++p) v[p] = x_digits4(xs[p], etop1);
+        plane_digits4(v, ev, od);
+#pragma unroll
+        for (int sd = 0; sd < 4; ++sd) {
+          put(pe, h, col0 + sd, ev[sd]);
+          put(pe + 1, h, col0 + sd, od[sd]);
+        }
+      } else {
+        // six digits: columns [d0 d1 d2 0 d3 d4 d5 0]
+        uint32_t hv[8], eh[4], oh[4];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          const uint64_t z = x_digits(xs[p], etop1);
+          v[p] = (uint32_t)z;
+          hv[p] = (uint32_t)(z >> 32);
+        }
+        plane_digits4(v, ev, od);
+        plane_digits4(hv, eh, oh);
+        const uint32_t e8[8] = {ev[0], ev[1], ev[2], 0u, ev[3], eh[0], eh[1], 0u};
+        const uint32_t o8[8] = {od[0], od[1], od[2], 0u, od[3], oh[0], oh[1], 0u};
+#pragma unroll
+        for (int sd = 0; sd < 8; ++sd) {
+          put(pe, h, col0 + sd, e8[sd]);
+          put(pe + 1, h, col0 + sd, o8[sd]);
+        }
+      }
+    };
+    word(0, xa);
+    word(1, xb);
+  };
+
+  // ---- segments: one pass over at most kChSegTiles tiles of one slot ----
+  int v = v0;
+  while (v < v1) {
+    const int pv = v / tps;                            // pass index
+    const int t0 = v - pv * tps;
+    const int t1 = min(min(v1 - pv * tps, tps), t0 + kChSegTiles);
+    v = pv * tps + t1;
+    int e, g;
+    decode(pv, e, g);
+    const uint8_t* slot = a.slots + (uint64_t)e * a.slot_stride;
+    const __amdgpu_buffer_rsrc_t gsrc = make_rsrc(slot + a.gate_w_off, wbytes);
+    // DOWN: rows 16..31 of each tile are the same matrix 16 rows further on
+    // (loads past its end return zeros, for rows that are never stored)
+    const uint32_t skip = 16u * rbytes;
+    const __amdgpu_buffer_rsrc_t usrc =
+        DOWN ? make_rsrc(slot + a.gate_w_off + skip, wbytes > skip ? wbytes - skip : 0u)
+             : make_rsrc(slot + a.up_w_off, wbytes);
+    const float* gscale = (const float*)(slot + a.gate_s_off);
+    const float* uscale = (const float*)(slot + a.up_s_off);
+    const int nseg = t1 - t0;
+    // the pass's pairs: indices [ilo, ihi) of the slot's pairs in id order
+    const int ilo = counted || !grouped ? g * G : 0;
+    const int ihi = counted || !grouped ? ilo + G : 0x7FFFFFFF;
+
+    // ---- the segment's stream of (round, chunk) elements ----
+    // With the whole K in LDS (one chunk) the segment is one round whose
+    // tiles each wave finishes as it completes them; else rounds of at most
+    // kChRoundTiles tiles whose sums stay in registers from chunk to chunk.
+    const int nr = WHOLE ? 1 : (nseg + kChRoundTiles - 1) / kChRoundTiles;
+    const int nelem = nr * nch;
+    auto round_at = [&](int r) { return t0 + (r * nseg) / nr; };  // first tile of round r (in the slot)
+    // element k: its round's first tile and tile count, its chunk's steps,
+    // and this wave's unit range [ua, ub) in (tile, step) order
+    auto elem = [&](int k, int& ta, int& nt, int& scc, int& s0, int& ua, int& ub) {
+      const int r = k / nch, c = k - r * nch;
+      ta = round_at(r);
+      nt = round_at(r + 1) - ta;
+      s0 = c * Sc;
+      scc = min(Sc, S - s0);
+      ua = unit_at(pos, nt, scc);
+      ub = unit_at(pos + 1, nt, scc);
+    };
+
+    // ---- weight load cursor: element ck, unit cu of [.., cub) ----
+    int left = 0;                                      // units this wave has yet to load
+    int ck = 0, cu = 0, cub = 0, cscc = 1, cs0 = 0, lt = 0, lsc = 0;
+    uint32_t loff = 0, loff2 = 0;
+    auto seek = [&]() {                                // to the first unit of element ck or later
+      while (ck < nelem) {
+        int ta, nt, ua, ub;
+        elem(ck, ta, nt, cscc, cs0, ua, ub);
+        if (ua < ub) {
+          cu = ua;
+          cub = ub;
+          lt = ta + ua / cscc;
+          lsc = ua - (ua / cscc) * cscc;
+          loff = row_off(lt, 0);
+          loff2 = row_off(lt, 1);
+          return;
+        }
+        ++ck;
+      }
+    };
+    // always four loads per call (offsets past the weights once this wave's
+    // units are all issued), so that the compiler's wait counts stay exact
+    auto issue = [&](StepW<true>& gw, StepW<true>& uw, uint32_t dep) {
+      const bool live = left > 0;
+      const uint32_t so = (uint32_t)(cs0 + lsc) * 128u;
+      const uint32_t o = (live ? loff + so : kOffNone) + dep;
+      const uint32_t o2 = (live ? loff2 + so : kOffNone) + dep;
+      load_line<VEC>(gw, gsrc, o, o2);
+      load_line<VEC>(uw, usrc, o, o2);
+      if (live) {
+        --left;
+        if (++cu == cub) {
+          ++ck;
+          seek();
+        } else if (++lsc == cscc) {
+          lsc = 0;
+          ++lt;
+          loff = row_off(lt, 0);
+          loff2 = row_off(lt, 1);
+        }
+      }
+    };
+    StepW<true> rg[kChD], ru[kChD], sg, su;
+    // the next unit's weights, moved out of their ring slot into the tile
+    // layout, and the slot refilled at once (see the resident kernel)
+    auto take = [&](int sl) {
+      sg = rg[sl];
+      su = ru[sl];
+      line_to_tile(sg, lines);
+      line_to_tile(su, lines);
+      uint32_t dep = 0u;
+      asm volatile("" : "+v"(dep) : "v"(sg.a), "v"(sg.b), "v"(su.a), "v"(su.b));
+      issue(rg[sl], ru[sl], dep);
+    };
+    // the stream from its start: the first weights go out before the group's
+    // pairs, ranges and digits are known (the addresses depend on none of them)
+    auto stream_start = [&]() {
+      left = 0;
+      for (int k = 0; k < nelem; ++k) {
+        int ta, nt, scc, s0, ua, ub;
+        elem(k, ta, nt, scc, s0, ua, ub);
+        left += ub - ua;
+      }
+      ck = 0;
+      seek();
+#pragma unroll
+      for (int d = 0; d < kChD; ++d) issue(rg[d], ru[d], 0u);
+    };
+    stream_start();
+
+    int done = 0;                                      // pairs of the pass already processed
+    for (;;) {
+      __syncthreads();  // the previous group is done with the group tables and digits
+      if (tid < G) {
+        s_xmax[tid] = 0;
+        s_xmin[tid] = 255;
+      }
+      // ---- next group: the pass's pairs [start, start + G) ----
+      const int start = ilo + done;
+      const int stop = min(ihi, start + G);
+      int count, more;
+      if (!grouped) {
+        count = max(0, min(stop, P) - start);
+        more = start + count < min(ihi, P);
+        if (tid < count) s_pairs[tid] = start + tid;
+        __syncthreads();
+      } else {
+        // block-wide scan of the ids in windows of kChThreads, counting the
+        // slot's pairs in id order; stops once it has seen past `stop`.  Ids
+        // held in registers and ids read from memory take separate loops (one
+        // merged loop would wait for every load in flight at each compare).
+        int found = 0;
+        auto window = [&](int base, bool m) {
+          const uint64_t bal = __ballot(m);
+          if (lane == 0) s_wcnt[wave] = __popcll(bal);
+          __syncthreads();
+          int before = found;
+#pragma unroll 1
+          for (int w = 0; w < wave; ++w) before += s_wcnt[w];
+          int total = found;
+#pragma unroll 1
+          for (int w = 0; w < kChWaves; ++w) total += s_wcnt[w];
+          before += __popcll(bal & ((1ull << lane) - 1ull));
+          if (m && before >= start && before < stop) s_pairs[before - start] = base + tid;
+          found = total;
+          __syncthreads();  // s_wcnt reused; s_pairs visible
+          return found > stop;
+        };
+#pragma unroll
+        for (int j = 0; j < kChIdRegs; ++j)
+          if (j * kChThreads < P && !(j > 0 && found > stop))
+            if (window(j * kChThreads, idr[j] == e)) break;
+        if (found <= stop)
+          for (int base = kChIdRegs * kChThreads; base < P; base += kChThreads)
+            if (window(base, base + tid < P && a.ids[base + tid] == e)) break;
+        count = max(0, min(found, stop) - start);
+        more = start + count < min(ihi, found);
+      }
+      if (count <= 0) break;
+      if (tid < count) s_tok[tid] = s_pairs[tid] / K;
+      __syncthreads();
+
+      // ---- range of each row of the group: largest |x|, smallest exponent ----
+      {
+        const int nxu = count * hw;
+        for (int u0 = 0; u0 < nxu; u0 += kChThreads) {
+          const int u = u0 + tid;
+          const int ti = min(u, nxu - 1) / hw;
+          uint32_t mx = 0, mn = 255;
+          if (u < nxu) {
+            const uint4 xq = *(const uint4*)(a.x + (uint64_t)s_tok[ti] * H + 8 * (u - ti * hw));
+            range8(xq, mx, mn);
+          }
+          if (__shfl(ti, 0) == __shfl(ti, 63)) {
+            mx = wave_extreme<true>(mx);
+            mn = wave_extreme<false>(mn);
+            if (lane == 0 && mx) atomicMax(&s_xmax[ti], (int)mx);
+            if (lane == 0 && mn < 255) atomicMin(&s_xmin[ti], (int)mn);
+          } else {
+            if (mx) atomicMax(&s_xmax[ti], (int)mx);
+            if (mn < 255) atomicMin(&s_xmin[ti], (int)mn);
+          }
+        }
+      }
+      // row scales of the segment
+      for (int i = tid; i < nseg * RT; i += kChThreads) {
+        const int row = t0 * RT + i;
+        s_gsc[i] = row < I ? gscale[row] : 0.0f;
+        if constexpr (!DOWN) s_usc[i] = row < I ? uscale[row] : 0.0f;
+      }
+      __syncthreads();
+      // Digit columns: four per row when all its values lie within 22
+      // binades of its largest, else eight ([d0 d1 d2 0 d3 d4 d5 0]).  Eight-
+      // column rows take the first 8-aligned columns, four-column rows the
+      // rest; the group is the longest run of its pairs that fits 16*NT
+      // columns (the rest go to the next group).
+      int n8 = 0, n4 = 0, fit = 0;
+      for (int ti = 0; ti < count; ++ti) {
+        const int w8 = digits_for(s_xmax[ti], s_xmin[ti]) == 4 ? 0 : 1;
+        if (8 * (n8 + w8) + 4 * (n4 + 1 - w8) > 16 * NT) break;
+        n8 += w8;
+        n4 += 1 - w8;
+        ++fit;
+      }
+      n8 = __builtin_amdgcn_readfirstlane(n8);
+      fit = __builtin_amdgcn_readfirstlane(fit);
+      if (fit < count) {
+        count = fit;
+        more = 1;
+      }
+      if (tid < 4 * NT) s_quad[tid] = -1;
+      __syncthreads();
+      if (tid < count) {
+        int r8 = 0, r4 = 0;
+        for (int ti = 0; ti < tid; ++ti) {
+          if (digits_for(s_xmax[ti], s_xmin[ti]) == 4)
+            ++r4;
+          else
+            ++r8;
+        }
+        const bool wide = digits_for(s_xmax[tid], s_xmin[tid]) != 4;
+        const int col0 = wide ? 8 * r8 : 8 * n8 + 4 * r4;
+        s_col[tid] = col0;
+        s_wid[tid] = wide ? 8 : 4;
+        s_quad[col0 / 4] = tid;
+        if (wide) s_quad[col0 / 4 + 1] = tid + 64;
+      }
+      __syncthreads();
+
+      // x pair xp of chunk c (pairs ordered (step, pair in step, row): xp =
+      // (st * 16 + r16) * count + tl) of the group, at K index k0 of the row;
+      // units past the row's end (padding steps) are loaded from its start
+      // and replaced by zeros when they are split, not here (a write to the
+      // loads' registers would have to wait for them at once)
+      auto pair_k = [&](int c, int pp) { return (c * Sc + (pp >> 4)) * 256 + 16 * (pp & 15); };
+      auto load_pair = [&](int c, int pp, int tl, uint4& xa, uint4& xb) {
+        const int k0 = pair_k(c, pp);
+        const uint16_t* row = a.x + (uint64_t)s_tok[tl] * H;
+        xa = *(const uint4*)(row + (k0 < H ? k0 : 0));
+        xb = *(const uint4*)(row + (k0 + 8 < H ? k0 + 8 : 0));
+      };
+      auto put_pair = [&](uint8_t* buf, int c, int pp, int tl, uint4 xa, uint4 xb) {
+        const int k0 = pair_k(c, pp);
+        if (k0 >= H) xa = make_uint4(0, 0, 0, 0);
+        if (k0 + 8 >= H) xb = make_uint4(0, 0, 0, 0);
+        const int r16 = pp & 15;
+        stage_pair(buf, s_wid[tl], s_col[tl], pp >> 4, r16 >> 2, r16 & 3, xa, xb, max((s_xmax[tl] >> 7) & 0xFF, 1));
+      };
+      // chunk 0 of the group, by every thread
+      {
+        const int xp0 = count * min(Sc, S) * 16;
+        for (int xp = tid; xp < xp0; xp += kChThreads) {
+          const int pp = xp / count, tl = xp - pp * count;
+          uint4 xa, xb;
+          load_pair(0, pp, tl, xa, xb);
+          put_pair(s_dig, 0, pp, tl, xa, xb);
+        }
+      }
+      __syncthreads();
+      take(0);
+
+      // ---- a finished tile (tseg of the segment) with its sums in ag/au:
+      // fix-up with the other `ncon` contributors (slot `first`), then the
+      // (row, pair) sums, F32 rounding, SwiGLU tail and stores ----
+      auto finish_tile = [&](int tseg, int first, int ncon, const v4i* ag, const v4i* au) {
+        int64_t gq[NT], uq[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          gq[n] = quad_digit_sum(ag[n], qj);
+          uq[n] = quad_digit_sum(au[n], qj);
+        }
+        if (ncon > 1) {
+          // first < kChFixSlots: a shared tile is the last one its first
+          // contributor meets, and a later position meets it too
+          unsigned long long* fx = s_fix + first * ch_fix_words(NT) + lane;
+#pragma unroll
+          for (int n = 0; n < NT; ++n) {
+            atomicAdd(&fx[(2 * n) * 64], (unsigned long long)gq[n]);
+            atomicAdd(&fx[(2 * n + 1) * 64], (unsigned long long)uq[n]);
+          }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+          int prev = 0;
+          if (lane == 0) prev = atomicAdd(&s_fixcnt[first], 1);
+          prev = __shfl(prev, 0);
+          if (prev != ncon - 1) return;
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+#pragma unroll
+          for (int n = 0; n < NT; ++n) {
+            gq[n] = (int64_t)fx[(2 * n) * 64];
+            uq[n] = (int64_t)fx[(2 * n + 1) * 64];
+            fx[(2 * n) * 64] = 0;
+            fx[(2 * n + 1) * 64] = 0;
+          }
+          if (lane == 0) s_fixcnt[first] = 0;
+        }
+        const int row = (t0 + tseg) * RT + 4 * g4 + qj;
+        const int si = tseg * RT + 4 * g4 + qj;        // scale index in the segment
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          // the row of this lane's quad; an 8-column row's quads are [d0 d1
+          // d2 0] and [d3 d4 d5 0], the high half of the sum from the next quad
+          const int qv = s_quad[4 * n + (cc >> 2)];
+          const int64_t gx = __shfl_xor(gq[n], 4), ux = __shfl_xor(uq[n], 4);
+          if (qv < 0 || qv >= 64 || row >= I) continue;
+          const int tq = qv;
+          const bool w8 = s_wid[tq] == 8;
+          const int xm = s_xmax[tq];
+          const float gs = s_gsc[si];
+          const float us = DOWN ? s_gsc[si + 16] : s_usc[si];
+          float gate, up;
+          if (!w8) {
+            const int e2 = sum_exponent(xm) + 16;
+            gate = round_scaled53(gq[n], e2, gs);
+            up = round_scaled53(uq[n], e2, us);
+          } else {
+            const int e2 = sum_exponent(xm);
+            gate = round_scaled(gx, gq[n], e2, gs);
+            up = round_scaled(ux, uq[n], e2, us);
+          }
+          if (xm >= 0x7F80) {
+            gate = __builtin_nanf("");
+            up = __builtin_nanf("");
+          }
+          const uint64_t o = (uint64_t)s_pairs[tq] * I + row;
+          if constexpr (DOWN) {
+            a.out[o] = bf16_rne(gate);
+            if (a.gate_probe) a.gate_probe[o] = gate;
+            if (row + 16 < I) {
+              a.out[o + 16] = bf16_rne(up);
+              if (a.gate_probe) a.gate_probe[o + 16] = up;
+            }
+          } else {
+            a.out[o] = swiglu_tail_tab(gate, up, s_sig);
+            if (a.gate_probe) a.gate_probe[o] = gate;
+            if (a.up_probe) a.up_probe[o] = up;
+          }
+        }
+      };
+      // one pass of the step loop (kChU steps) into ag/au, B fragments of
+      // chunk steps sl.. of digit buffer buf; `slice` runs after the take of
+      // the pass's last step
+      auto steps = [&](const uint8_t* buf, int sl, v4i* ag, v4i* au, auto&& slice) {
+#pragma unroll
+        for (int jj = 0; jj < kChU; ++jj) {
+          v4i pg[4], pu[4];
+          split_planes(sg.a, sg.b, pg);
+          split_planes(su.a, su.b, pu);
+          take((jj + 1) % kChD);
+          if (jj == kChU - 1) slice();
+          const uint8_t* bp = buf + (sl + jj) * sbytes + rdo;
+          v4i bq[4][NT];
+#pragma unroll
+          for (int pl = 0; pl < 4; ++pl)
+#pragma unroll
+            for (int n = 0; n < NT; ++n) bq[pl][n] = *(const v4i*)(bp + (pl * NT + n) * 1024);
+#pragma unroll
+          for (int pl = 0; pl < 4; ++pl)
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+              ag[n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pg[pl], bq[pl][n], ag[n], 0, 0, 0);
+              au[n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pu[pl], bq[pl][n], au[n], 0, 0, 0);
+            }
+        }
+      };
+
+      if constexpr (WHOLE) {
+        // ---- the whole K in LDS: portions (the rest of a tile inside this
+        // wave's range), each tile finished as its last step is done ----
+        int ta, nt, scc, s0, ua, ub;
+        elem(0, ta, nt, scc, s0, ua, ub);
+        int u = ua;
+        while (u < ub) {
+          const int w = u / S;                         // tile of the segment
+          const int pe = min(ub, (w + 1) * S);
+          const bool full = u == w * S && pe == (w + 1) * S;
+          v4i ag[NT], au[NT];
+#pragma unroll
+          for (int n = 0; n < NT; ++n) {
+            ag[n] = v4i{0, 0, 0, 0};
+            au[n] = v4i{0, 0, 0, 0};
+          }
+          for (; u < pe; u += kChU) steps(s_dig, u - w * S, ag, au, [] {});
+          // contributors: the positions whose ranges meet the tile
+          int first = pos, ncon = 1;
+          if (!full) {
+            first = -1;
+            ncon = 0;
+            for (int k = 0; k < kChWaves; ++k) {
+              const int b0 = unit_at(k, nseg, S), b1 = unit_at(k + 1, nseg, S);
+              if (b0 < b1 && b0 < (w + 1) * S && b1 > w * S) {
+                if (first < 0) first = k;
+                ++ncon;
+              }
+            }
+          }
+          finish_tile(w, first, ncon, ag, au);
+        }
+      } else {
+        v4i accg[kChMaxT][NT], accu[kChMaxT][NT];
+        const int qd = 64 / count, rd = 64 - qd * count;  // one slice: 64 pairs further on
+        for (int k = 0; k < nelem; ++k) {
+          int ta, nt, scc, s0, ua, ub;
+          elem(k, ta, nt, scc, s0, ua, ub);
+          const int c = k - (k / nch) * nch;
+          const int tf = tile_lo(pos, nt);            // first tile this wave meets in the round
+          if (c == 0) {
+#pragma unroll
+            for (int j = 0; j < kChMaxT; ++j)
+#pragma unroll
+              for (int n = 0; n < NT; ++n) {
+                accg[j][n] = v4i{0, 0, 0, 0};
+                accu[j][n] = v4i{0, 0, 0, 0};
+              }
+          }
+          const uint8_t* buf = s_dig + (k & 1) * kChBuf;
+          // this wave's share of element k+1's digits: pairs [xp, xe) of
+          // chunk c1, one slice (64 pairs, one per lane) per pass of the step
+          // loop
+          const bool stg = k + 1 < nelem;
+          const int c1 = c + 1 == nch ? 0 : c + 1;
+          uint8_t* sbuf = s_dig + ((k + 1) & 1) * kChBuf;
+          const int xpn = stg ? count * min(Sc, S - c1 * Sc) * 16 : 0;
+          int xp = wave * xpn / kChWaves + lane;
+          const int xe = (wave + 1) * xpn / kChWaves;
+          int pp = xp / count, tl = xp - pp * count;
+          auto slice_next = [&]() {
+            xp += 64;
+            pp += qd;
+            tl += rd;
+            if (tl >= count) {
+              tl -= count;
+              ++pp;
+            }
+          };
+          // A slice's x is loaded after the take at a pass's last step and
+          // split into LDS at the same point of the next pass: the take there
+          // has waited for every weight load issued before the x loads, so the
+          // wait for x covers nothing still in flight for the ring.
+          uint4 xa = make_uint4(0, 0, 0, 0), xb = make_uint4(0, 0, 0, 0);
+          int ppp = 0, tlp = 0;                        // the pending slice's pair
+          bool pend = false;
+          auto slice = [&]() {
+            if (pend) put_pair(sbuf, c1, ppp, tlp, xa, xb);
+            pend = xp < xe;
+            if (pend) {
+              load_pair(c1, pp, tl, xa, xb);
+              ppp = pp;
+              tlp = tl;
+              slice_next();
+            }
+          };
+#pragma unroll
+          for (int j = 0; j < kChMaxT; ++j) {
+            const int tile = tf + j;                   // tile of the round
+            const int pa = max(ua, tile * scc), pb = min(ub, (tile + 1) * scc);
+            for (int u = pa; u < pb; u += kChU) steps(buf, u - tile * scc, accg[j], accu[j], slice);
+          }
+          if (pend) put_pair(sbuf, c1, ppp, tlp, xa, xb);
+          // the rest of this wave's share (rounds too short for all its slices)
+          while (xp < xe) {
+            load_pair(c1, pp, tl, xa, xb);
+            put_pair(sbuf, c1, pp, tl, xa, xb);
+            slice_next();
+          }
+          __syncthreads();  // element k's digits read, element k+1's staged
+          if (c != nch - 1) continue;
+          // ---- the round's tiles this wave met ----
+          const int tl_last = tile_hi(pos, nt);
+#pragma unroll
+          for (int j = 0; j < kChMaxT; ++j) {
+            const int tile = tf + j;
+            if (tile > tl_last) continue;
+            int first = -1, ncon = 0;
+            for (int kk = 0; kk < kChWaves; ++kk) {
+              if (tile_lo(kk, nt) <= tile && tile <= tile_hi(kk, nt)) {
+                if (first < 0) first = kk;
+                ++ncon;
+              }
+            }
+            finish_tile(ta - t0 + tile, first, ncon, accg[j], accu[j]);
+          }
+        }
+      }
+      done += count;
+      if (!more) break;
+      stream_start();                                  // the next group streams the segment again
+    }
+  }
+
+  // ---- pairs with invalid ids get zero outputs: pairs b, b + NB, ... here ----
+  if (grouped) {
+    const int nmine = P > (int)blockIdx.x ? (P - (int)blockIdx.x + NB - 1) / NB : 0;
+    for (int base = 0; base < nmine; base += kChThreads) {
+      __syncthreads();
+      if (tid == 0) s_ninv = 0;
+      __syncthreads();
+      const int i = base + tid;
+      const int p = (int)blockIdx.x + i * NB;
+      const bool bad = i < nmine && (a.ids[p] < 0 || a.ids[p] >= a.num_slots);
+      int at = -1;
+      if (bad) at = atomicAdd(&s_ninv, 1);
+      if (bad && at < kChInvBatch) s_invl[at] = p;
+      __syncthreads();
+      const int nl = min(s_ninv, kChInvBatch);
+      for (int q = 0; q < nl; ++q) {
+        const int pq = s_invl[q];
+        for (int r = tid; r < I; r += kChThreads) {
+          const uint64_t o = (uint64_t)pq * I + r;
+          a.out[o] = 0;
+          if (a.gate_probe) a.gate_probe[o] = 0.0f;
+          if (a.up_probe) a.up_probe[o] = 0.0f;
+        }
+      }
+      // past the batch: each finder fills its own pair
+      if (bad && at >= kChInvBatch)
+        for (int r = 0; r < I; ++r) {
+          const uint64_t o = (uint64_t)p * I + r;
+          a.out[o] = 0;
+          if (a.gate_probe) a.gate_probe[o] = 0.0f;
+          if (a.up_probe) a.up_probe[o] = 0.0f;
+        }
+    }
+  }
+}
+
+// ---- host side ----
+
+namespace {
+
+template <int NT, bool VEC, bool DOWN, bool WHOLE>
+int chunked_blocks(int device) {
+  // per-device cache; concurrent first calls compute the same value
+  static std::atomic<int> cached[64];
+  if (device < 0 || device >= 64) device = 0;
+  if (!cached[device].load(std::memory_order_relaxed)) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0)
+      cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(&chunked_kernel<NT, VEC, DOWN, WHOLE>), kChThreads, 0) != hipSuccess ||
+        per_cu <= 0)
+      per_cu = 1;
+    cached[device].store(cus * per_cu, std::memory_order_relaxed);
+  }
+  return cached[device].load(std::memory_order_relaxed);
+}
+
+template <int NT, bool VEC, bool DOWN, bool WHOLE>
+hipError_t launch_chunked_t(GateUpParams& p, hipStream_t stream) {
+  int device = 0;
+  if (hipGetDevice(&device) != hipSuccess) device = 0;
+  const int rt = DOWN ? 32 : 16;
+  const int tiles = p.num_slots * ((p.I + rt - 1) / rt);
+  int nb = chunked_blocks<NT, VEC, DOWN, WHOLE>(device);
+  if (nb > tiles) nb = tiles;
+  void* args[] = {&p};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&chunked_kernel<NT, VEC, DOWN, WHOLE>), dim3((unsigned)nb),
+                         dim3(kChThreads), args, 0, stream);
+}
+
+template <int NT, bool DOWN>
+hipError_t launch_chunked_n(GateUpParams& p, hipStream_t stream) {
+  const bool vec = (p.H / 2) % 16 == 0;
+  const bool whole = ch_chunk_steps(NT, p.steps) == p.steps;
+  if (whole)
+    return vec ? launch_chunked_t<NT, true, DOWN, true>(p, stream) : launch_chunked_t<NT, false, DOWN, true>(p, stream);
+  return vec ? launch_chunked_t<NT, true, DOWN, false>(p, stream) : launch_chunked_t<NT, false, DOWN, false>(p, stream);
+}
+
+template <bool DOWN>
+hipError_t launch_chunked_d(GateUpParams& p, int nt, hipStream_t stream) {
+  return nt == 1 ? launch_chunked_n<1, DOWN>(p, stream) : launch_chunked_n<2, DOWN>(p, stream);
+}
+
+}  // namespace
+
+int chunked_tiles(const GateUpParams& p) {
+  if (p.q8 || p.xf32) return 0;
+  // single expert: its tokens; grouped: the routed pairs per slot on average
+  // (over all slots: routing often touches a few), two column tiles except
+  // for a down projection of one row per slot
+  if (!p.ids) return p.M <= 2 ? 1 : (p.M <= 8 ? 2 : 0);
+  const int64_t pairs = (int64_t)p.M * p.K;
+  const int64_t per_slot = (pairs + p.num_slots - 1) / p.num_slots;
+  if (per_slot > 6) return 0;
+  return p.down && per_slot <= 1 ? 1 : 2;
+}
+
+hipError_t launch_chunked(GateUpParams p, int nt, hipStream_t stream) {
+  p.steps = ch_steps(p.H);
+  // a SIMD's first-wave share, 1/1024 of the SIMD's quarter (as measured for
+  // the resident kernel's loop, which this kernel's step loop matches)
+  p.wave_share = nt == 1 ? 577 : 547;
+  return p.down ? launch_chunked_d<true>(p, nt, stream) : launch_chunked_d<false>(p, nt, stream);
+}
+
+}  // namespace q4

@@ -47,6 +47,12 @@ hipError_t launch_resident(GateUpParams p, hipStream_t stream);
 // Batch kernel for any width (digits staged per K-chunk).
 hipError_t launch_batch(GateUpParams p, int tokens_per_slot, hipStream_t stream);
 
+// Chunked kernel for bf16 activations and Q4 weights with a few rows per
+// slot: the column tiles (1 or 2) it would take for this call, or 0 when the
+// call is outside its range; and its launch.
+int chunked_tiles(const GateUpParams& p);
+hipError_t launch_chunked(GateUpParams p, int nt, hipStream_t stream);
+
 // Pick and launch the kernel for a call whose slots see at most
 // `tokens_per_slot` tokens (more are processed in further token groups).
 hipError_t launch_gate_up(const GateUpParams& p, int tokens_per_slot, hipStream_t stream);

@@ -1242,15 +1242,15 @@ hipError_t launch_gate_up(const GateUpParams& p, int tokens_per_slot, hipStream_
   GateUpParams q = p;
   const hipError_t e = sigmoid_table(&q.sig);
   if (e != hipSuccess) return e;
-  return resident_fits(tokens_per_slot, q.H, q.q8 != 0, q.xf32 != 0) && resident_out_fits(q)
-             ? launch_resident(q, stream)
-             : launch_batch(q, tokens_per_slot, stream);
+  if (resident_fits(tokens_per_slot, q.H, q.q8 != 0, q.xf32 != 0) && resident_out_fits(q)) return launch_resident(q, stream);
+  const int nt = chunked_tiles(q);
+  return nt ? launch_chunked(q, nt, stream) : launch_batch(q, tokens_per_slot, stream);
 }
 
 hipError_t launch_down(const GateUpParams& p, int pairs_per_slot, hipStream_t stream) {
-  return resident_fits(p.M, p.H, p.q8 != 0, p.xf32 != 0) && resident_out_fits(p)
-             ? launch_resident(p, stream)
-             : launch_batch(p, pairs_per_slot, stream);
+  if (resident_fits(p.M, p.H, p.q8 != 0, p.xf32 != 0) && resident_out_fits(p)) return launch_resident(p, stream);
+  const int nt = chunked_tiles(p);
+  return nt ? launch_chunked(p, nt, stream) : launch_batch(p, pairs_per_slot, stream);
 }
 
 }  // namespace q4

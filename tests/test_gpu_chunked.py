@@ -1,0 +1,142 @@
+"""GPU parity of the chunked kernel (routed calls with a few rows per slot
+whose digits do not all fit LDS for the launch) against the oracle.
+
+Grouped calls with bf16 activations and Q4 weights go to this kernel when
+the resident kernel cannot hold their rows and the routed pairs per slot
+average at most six (two column tiles; one for a down projection of one row
+per slot); single-expert calls of up to eight tokens that the resident
+kernel cannot hold go there too.  The shapes below reach: one and two column
+tiles; the whole K in LDS and K cut into two-buffer chunks (with a short last
+chunk and padding steps); several rounds per segment and several segments
+per work-group; slots with more pairs than one pass holds (work cut by
+cost); calls over more slots than the pass counts cover; rounds of a few
+tiles shared by many waves through the fix-up slots; four- and six-digit rows
+in one group; invalid and duplicate ids; rows whose bytes are not 16-byte
+aligned; ragged tiles; and the down projection, single and grouped.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import quantized_moe_expert_q4_amd as q4
+from tests.gpu_helpers import (check_down_parity, check_parity, run_down_grouped, run_down_single, run_grouped,
+                               run_single, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    q4.load()   # raises if the HIP library is missing: there is no fallback
+    yield
+
+
+def _pool(rng, E, H, I, down=False):
+    lay = synth.expert_layout(H, I) if down else synth.contiguous_layout(H, I)
+    slots = np.zeros((E, lay.slot_bytes), np.uint8)
+    for e in range(E):
+        synth.fill_slot(rng, H, I, lay, out=slots[e])
+    return lay, slots
+
+
+def _wide(x, rows):
+    """Rows given a 9984 entry next to a 2^-25 one: six digits per value."""
+    x = x.copy()
+    for t in rows:
+        x[t, 5] = 0x461C
+        x[t, 6] = 0x3300
+    return x
+
+
+# (E, H, I, M, K, wide rows, label)
+GROUPED = [
+    (24, 2048, 520, 12, 2, (), "one column tile, ragged tiles, tiny ranges (fix-ups)"),
+    (8, 6144, 2048, 32, 1, (), "two column tiles, four pairs per slot, K in three chunks"),
+    (16, 4104, 200, 20, 3, (), "rows not 16-byte aligned, padding steps, short last chunk"),
+    (8, 3072, 256, 10, 4, (1, 7), "six-digit groups: several groups per slot"),
+    (40, 512, 2048, 40, 5, (), "several rounds per segment"),
+    (160, 512, 2048, 160, 1, (), "several segments per work-group, one pair per slot"),
+    (2100, 256, 16, 20, 2, (), "more slots than the pair counts cover"),
+]
+
+
+@pytest.mark.parametrize("E,H,I,M,K,wide,label", GROUPED, ids=[g[-1] for g in GROUPED])
+def test_chunked_grouped(E, H, I, M, K, wide, label):
+    rng = np.random.default_rng(E * 1000 + H + I + M + K)
+    lay, slots = _pool(rng, E, H, I)
+    x = _wide(synth.bf16_normal(rng, (M, H)), wide)
+    ids = synth.top_k_routing(rng, M, K, E)
+    say(f"[chunked grouped E={E} H={H} I={I} M={M} K={K} wide={list(wide)}]")
+    (out, g, u), invalid = run_grouped(slots, lay, x, ids, H, I)
+    gr, ur, orf, bad = oracle.expert_gate_up_grouped(slots, lay.slot_bytes, E, lay, x, ids, H, I)
+    assert invalid == bad == 0
+    check_parity(out, g, u, gr, ur, orf, f"chunked grouped {label}")
+
+
+def test_chunked_skewed_routing_invalid_and_duplicate_ids():
+    """Most pairs on two slots (several groups there), unrouted slots, a token
+    routed twice to one slot, and ids outside [0, E)."""
+    E, H, I, M, K = 16, 1536, 96, 24, 3
+    rng = np.random.default_rng(4242)
+    lay, slots = _pool(rng, E, H, I)
+    x = synth.bf16_normal(rng, (M, H))
+    ids = np.where(rng.random((M, K)) < 0.7, rng.integers(3, 5, (M, K)), rng.integers(0, E, (M, K))).astype(np.int32)
+    ids[2, 0] = ids[2, 1] = 4
+    ids[5, 2] = E
+    ids[9, 0] = -1
+    ids[23, 1] = 1 << 30
+    say(f"[chunked skewed E={E} H={H} I={I} M={M} K={K}]")
+    (out, g, u), invalid = run_grouped(slots, lay, x, ids, H, I)
+    gr, ur, orf, bad = oracle.expert_gate_up_grouped(slots, lay.slot_bytes, E, lay, x, ids, H, I)
+    assert bad == 3 and invalid == 3
+    check_parity(out, g, u, gr, ur, orf, "chunked skewed routing")
+
+
+@pytest.mark.parametrize("H,I,M,wide", [(7168, 512, 3, True), (16384, 64, 5, False), (12288, 48, 8, False)])
+def test_chunked_single_expert(H, I, M, wide):
+    """Single-expert calls of up to eight tokens whose digits exceed the
+    resident kernel's LDS."""
+    rng = np.random.default_rng(H + I + M)
+    lay = synth.contiguous_layout(H, I)
+    slot = synth.fill_slot(rng, H, I, lay)
+    x = _wide(synth.bf16_normal(rng, (M, H)), (0,) if wide else ())
+    say(f"[chunked single H={H} I={I} M={M} wide={wide}]")
+    out, g, u = run_single(slot, lay, x, H, I)
+    gr, ur, orf = oracle.expert_gate_up(slot, lay, x, H, I)
+    check_parity(out, g, u, gr, ur, orf, f"chunked single H={H} I={I} M={M}")
+
+
+@pytest.mark.parametrize("E,H,I,wide", [(20, 4096, 1536, False), (12, 520, 2048, True), (40, 264, 8192, False)])
+def test_chunked_down_grouped(E, H, I, wide):
+    """The grouped down projection with one routed row per slot (the down
+    step of one token routed to E experts): H output rows, I inputs."""
+    rng = np.random.default_rng(E + H + I)
+    lay, slots = _pool(rng, E, H, I, down=True)
+    ids = np.arange(E, dtype=np.int32).reshape(1, E)
+    mid = synth.bf16_normal(rng, (1, E, I))
+    if wide:
+        mid[0, 3, 5] = 0x461C
+        mid[0, 3, 6] = 0x3300
+    say(f"[chunked down grouped E={E} H={H} I={I}]")
+    (out, d), invalid = run_down_grouped(slots, lay, mid, ids, H, I)
+    d_ref, o_ref, bad = oracle.expert_down_grouped(slots, lay.slot_bytes, E, lay, mid, ids, H, I)
+    assert invalid == bad == 0
+    check_down_parity(out, d, d_ref, o_ref, f"chunked down grouped E={E} H={H} I={I}")
+
+
+def test_chunked_down_single():
+    """A single-slot down call whose reduction is too long for the resident
+    kernel's LDS."""
+    H, I, M = 72, 16384, 5
+    rng = np.random.default_rng(515)
+    lay = synth.expert_layout(H, I)
+    slot = synth.fill_slot(rng, H, I, lay)
+    mid = synth.bf16_normal(rng, (M, I))
+    say(f"[chunked down single H={H} I={I} M={M}]")
+    out, d = run_down_single(slot, lay, mid, H, I)
+    d_ref, o_ref = oracle.expert_down(slot, lay, mid, H, I)
+    check_down_parity(out, d, d_ref, o_ref, "chunked down single")
