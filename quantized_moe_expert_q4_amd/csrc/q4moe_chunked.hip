@@ -257,12 +257,21 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   // first and last tile that position k's share meets in a round of nt tiles
   auto tile_lo = [&](int k, int nt) { return xfrac(k) * nt / 4096; };
   auto tile_hi = [&](int k, int nt) { return min(xfrac(k + 1) * nt / 4096, nt - 1); };
-  // unit at which position k's share starts in an element of nt tiles and
-  // scc steps: the same tile fraction in every chunk, whole passes
-  auto unit_at = [&](int k, int nt, int scc) {
+  // where position k's share starts in an element of nt tiles and scc
+  // steps: tile t, step s (the same tile fraction in every chunk, whole
+  // passes), and as a unit index; shifts only, no division (the cursor runs
+  // between weight loads, where a division's scratch registers would have to
+  // wait for loads in flight)
+  auto unit_pos = [&](int k, int nt, int scc, int& t, int& s) {
     const int num = xfrac(k) * nt;
-    const int t = num / 4096;
-    return t * scc + ((num - t * 4096) * scc / 4096) / kChU * kChU;
+    t = num >> 12;
+    s = (((num & 4095) * scc) >> 12) & ~(kChU - 1);
+  };
+  static_assert(kChU == 2, "passes of two steps: unit_pos rounds down to even steps");
+  auto unit_at = [&](int k, int nt, int scc) {
+    int t, s;
+    unit_pos(k, nt, scc, t, s);
+    return t * scc + s;
   };
   // whole-line loads: lane L reads rows L / 8 and 8 + L / 8 of the tile
   auto row_off = [&](int t, int part) {
@@ -347,12 +356,15 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     // tiles each wave finishes as it completes them; else rounds of at most
     // kChRoundTiles tiles whose sums stay in registers from chunk to chunk.
     const int nr = WHOLE ? 1 : (nseg + kChRoundTiles - 1) / kChRoundTiles;
-    const int nelem = nr * nch;
-    auto round_at = [&](int r) { return t0 + (r * nseg) / nr; };  // first tile of round r (in the slot)
-    // element k: its round's first tile and tile count, its chunk's steps,
+    // first tile of round r (in the slot): rounds of near-equal size
+    static_assert(kChSegTiles <= 4 * kChRoundTiles, "at most four rounds per segment");
+    auto round_at = [&](int r) {
+      const int q = r * nseg;
+      return t0 + (nr == 1 ? q : nr == 2 ? q >> 1 : nr == 3 ? q / 3 : q >> 2);
+    };
+    // element (r, c): round r's first tile and tile count, chunk c's steps,
     // and this wave's unit range [ua, ub) in (tile, step) order
-    auto elem = [&](int k, int& ta, int& nt, int& scc, int& s0, int& ua, int& ub) {
-      const int r = k / nch, c = k - r * nch;
+    auto elem = [&](int r, int c, int& ta, int& nt, int& scc, int& s0, int& ua, int& ub) {
       ta = round_at(r);
       nt = round_at(r + 1) - ta;
       s0 = c * Sc;
@@ -361,24 +373,32 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
       ub = unit_at(pos + 1, nt, scc);
     };
 
-    // ---- weight load cursor: element ck, unit cu of [.., cub) ----
+    // ---- weight load cursor: element (cr, cch), unit cu of [.., cub) ----
     int left = 0;                                      // units this wave has yet to load
-    int ck = 0, cu = 0, cub = 0, cscc = 1, cs0 = 0, lt = 0, lsc = 0;
+    int cr = 0, cch = 0, cu = 0, cub = 0, cscc = 1, cs0 = 0, lt = 0, lsc = 0;
     uint32_t loff = 0, loff2 = 0;
-    auto seek = [&]() {                                // to the first unit of element ck or later
-      while (ck < nelem) {
+    auto next_elem = [&]() {
+      if (++cch == nch) {
+        cch = 0;
+        ++cr;
+      }
+    };
+    auto seek = [&]() {                                // to the first unit of element (cr, cch) or later
+      while (cr < nr) {
         int ta, nt, ua, ub;
-        elem(ck, ta, nt, cscc, cs0, ua, ub);
+        elem(cr, cch, ta, nt, cscc, cs0, ua, ub);
         if (ua < ub) {
+          int t, st;
+          unit_pos(pos, nt, cscc, t, st);
           cu = ua;
           cub = ub;
-          lt = ta + ua / cscc;
-          lsc = ua - (ua / cscc) * cscc;
+          lt = ta + t;
+          lsc = st;
           loff = row_off(lt, 0);
           loff2 = row_off(lt, 1);
           return;
         }
-        ++ck;
+        next_elem();
       }
     };
     // always four loads per call (offsets past the weights once this wave's
@@ -393,7 +413,7 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
       if (live) {
         --left;
         if (++cu == cub) {
-          ++ck;
+          next_elem();
           seek();
         } else if (++lsc == cscc) {
           lsc = 0;
@@ -419,12 +439,14 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     // pairs, ranges and digits are known (the addresses depend on none of them)
     auto stream_start = [&]() {
       left = 0;
-      for (int k = 0; k < nelem; ++k) {
-        int ta, nt, scc, s0, ua, ub;
-        elem(k, ta, nt, scc, s0, ua, ub);
-        left += ub - ua;
-      }
-      ck = 0;
+      for (int r = 0; r < nr; ++r)
+        for (int c = 0; c < nch; ++c) {
+          int ta, nt, scc, s0, ua, ub;
+          elem(r, c, ta, nt, scc, s0, ua, ub);
+          left += ub - ua;
+        }
+      cr = 0;
+      cch = 0;
       seek();
 #pragma unroll
       for (int d = 0; d < kChD; ++d) issue(rg[d], ru[d], 0u);
@@ -690,10 +712,10 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         // ---- the whole K in LDS: portions (the rest of a tile inside this
         // wave's range), each tile finished as its last step is done ----
         int ta, nt, scc, s0, ua, ub;
-        elem(0, ta, nt, scc, s0, ua, ub);
-        int u = ua;
-        while (u < ub) {
-          const int w = u / S;                         // tile of the segment
+        elem(0, 0, ta, nt, scc, s0, ua, ub);
+        int w, st0;                                    // tile of the segment, and the step the range starts at
+        unit_pos(pos, nseg, S, w, st0);
+        for (int u = ua; u < ub; ++w) {
           const int pe = min(ub, (w + 1) * S);
           const bool full = u == w * S && pe == (w + 1) * S;
           v4i ag[NT], au[NT];
@@ -721,10 +743,11 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
       } else {
         v4i accg[kChMaxT][NT], accu[kChMaxT][NT];
         const int qd = 64 / count, rd = 64 - qd * count;  // one slice: 64 pairs further on
-        for (int k = 0; k < nelem; ++k) {
+        for (int r = 0; r < nr; ++r)
+        for (int c = 0; c < nch; ++c) {
+          const int k = r * nch + c;                   // element index: digit buffer k % 2
           int ta, nt, scc, s0, ua, ub;
-          elem(k, ta, nt, scc, s0, ua, ub);
-          const int c = k - (k / nch) * nch;
+          elem(r, c, ta, nt, scc, s0, ua, ub);
           const int tf = tile_lo(pos, nt);            // first tile this wave meets in the round
           if (c == 0) {
 #pragma unroll
@@ -739,7 +762,7 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
           // this wave's share of element k+1's digits: pairs [xp, xe) of
           // chunk c1, one slice (64 pairs, one per lane) per pass of the step
           // loop
-          const bool stg = k + 1 < nelem;
+          const bool stg = k + 1 < nr * nch;
           const int c1 = c + 1 == nch ? 0 : c + 1;
           uint8_t* sbuf = s_dig + ((k + 1) & 1) * kChBuf;
           const int xpn = stg ? count * min(Sc, S - c1 * Sc) * 16 : 0;
