@@ -59,6 +59,7 @@ constexpr int kChCntSlots = 2048;          // slots whose passes are held in LDS
 constexpr int kChIdRegs = 4;               // routing ids held per thread (2048 pairs)
 constexpr int kChCntWords = kChCntSlots / 32;
 constexpr int kChInvBatch = 64;            // invalid pairs zero-filled per batch
+constexpr int kChSegCost = 64;             // a segment's set-up cost, in K-steps of one tile
 
 // A wave's share of a round's units: the first wave of SIMD q takes the
 // fraction [q/4, q/4 + share/4096) of the round's tiles, the second wave the
@@ -243,8 +244,19 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
       rem -= ps;
     }
   };
-  const int T = npass * tps;
-  const int v0 = (int)((int64_t)blockIdx.x * T / NB), v1 = (int)((int64_t)(blockIdx.x + 1) * T / NB);
+  // Work-groups take even shares of a cost axis on which each pass is a
+  // set-up block of a.seg_cost followed by its tiles at S each (in K-steps of
+  // one tile): a share that reaches into another pass (one more segment set-
+  // up) takes that many fewer tiles.  Tile j of pass p starts at p * pc +
+  // seg_cost + j * S and goes to the work-group whose share holds its start.
+  const int64_t pc = (int64_t)tps * S + a.seg_cost;
+  const int64_t C = (int64_t)npass * pc;
+  auto tile_of = [&](int64_t c) {
+    const int64_t p = c / pc;
+    const int64_t r = c - p * pc - a.seg_cost;
+    return (int)(p * tps + (r > 0 ? (r + S - 1) / S : 0));
+  };
+  const int v0 = tile_of((int64_t)blockIdx.x * C / NB), v1 = tile_of((int64_t)(blockIdx.x + 1) * C / NB);
 
   // ---- per-lane constants ----
   const LineLanes lines = line_lanes(lane);
@@ -374,7 +386,6 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     };
 
     // ---- weight load cursor: element (cr, cch), unit cu of [.., cub) ----
-    int left = 0;                                      // units this wave has yet to load
     int cr = 0, cch = 0, cu = 0, cub = 0, cscc = 1, cs0 = 0, lt = 0, lsc = 0;
     uint32_t loff = 0, loff2 = 0;
     auto next_elem = [&]() {
@@ -402,16 +413,16 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
       }
     };
     // always four loads per call (offsets past the weights once this wave's
-    // units are all issued), so that the compiler's wait counts stay exact
+    // units are all issued: the cursor is past the last element), so that the
+    // compiler's wait counts stay exact
     auto issue = [&](StepW<true>& gw, StepW<true>& uw, uint32_t dep) {
-      const bool live = left > 0;
+      const bool live = cr < nr;
       const uint32_t so = (uint32_t)(cs0 + lsc) * 128u;
       const uint32_t o = (live ? loff + so : kOffNone) + dep;
       const uint32_t o2 = (live ? loff2 + so : kOffNone) + dep;
       load_line<VEC>(gw, gsrc, o, o2);
       load_line<VEC>(uw, usrc, o, o2);
       if (live) {
-        --left;
         if (++cu == cub) {
           next_elem();
           seek();
@@ -438,13 +449,6 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     // the stream from its start: the first weights go out before the group's
     // pairs, ranges and digits are known (the addresses depend on none of them)
     auto stream_start = [&]() {
-      left = 0;
-      for (int r = 0; r < nr; ++r)
-        for (int c = 0; c < nch; ++c) {
-          int ta, nt, scc, s0, ua, ub;
-          elem(r, c, ta, nt, scc, s0, ua, ub);
-          left += ub - ua;
-        }
       cr = 0;
       cch = 0;
       seek();
@@ -456,10 +460,6 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     int done = 0;                                      // pairs of the pass already processed
     for (;;) {
       __syncthreads();  // the previous group is done with the group tables and digits
-      if (tid < G) {
-        s_xmax[tid] = 0;
-        s_xmin[tid] = 255;
-      }
       // ---- next group: the pass's pairs [start, start + G) ----
       const int start = ilo + done;
       const int stop = min(ihi, start + G);
@@ -502,29 +502,35 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         more = start + count < min(ihi, found);
       }
       if (count <= 0) break;
-      if (tid < count) s_tok[tid] = s_pairs[tid] / K;
-      __syncthreads();
 
-      // ---- range of each row of the group: largest |x|, smallest exponent ----
-      {
-        const int nxu = count * hw;
-        for (int u0 = 0; u0 < nxu; u0 += kChThreads) {
-          const int u = u0 + tid;
-          const int ti = min(u, nxu - 1) / hw;
-          uint32_t mx = 0, mn = 255;
-          if (u < nxu) {
-            const uint4 xq = *(const uint4*)(a.x + (uint64_t)s_tok[ti] * H + 8 * (u - ti * hw));
-            range8(xq, mx, mn);
-          }
-          if (__shfl(ti, 0) == __shfl(ti, 63)) {
-            mx = wave_extreme<true>(mx);
-            mn = wave_extreme<false>(mn);
-            if (lane == 0 && mx) atomicMax(&s_xmax[ti], (int)mx);
-            if (lane == 0 && mn < 255) atomicMin(&s_xmin[ti], (int)mn);
-          } else {
-            if (mx) atomicMax(&s_xmax[ti], (int)mx);
-            if (mn < 255) atomicMin(&s_xmin[ti], (int)mn);
-          }
+      // ---- range of each row of the group (row `wave`, G < kChWaves):
+      // largest |x|, smallest exponent; four loads in flight per lane ----
+      static_assert(G <= kChWaves, "one wave per row of a group");
+      if (wave < count) {
+        const int tok = __builtin_amdgcn_readfirstlane(s_pairs[wave] / K);
+        const uint4* row = (const uint4*)(a.x + (uint64_t)tok * H);
+        uint32_t mx = 0, mn = 255;
+        auto acc = [&](const uint4 xq) {
+          uint32_t m1, n1;
+          range8(xq, m1, n1);
+          mx = max(mx, m1);
+          mn = min(mn, n1);
+        };
+        int u = lane;
+        for (; u + 192 < hw; u += 256) {
+          const uint4 q0 = row[u], q1 = row[u + 64], q2 = row[u + 128], q3 = row[u + 192];
+          acc(q0);
+          acc(q1);
+          acc(q2);
+          acc(q3);
+        }
+        for (; u < hw; u += 64) acc(row[u]);
+        mx = wave_extreme<true>(mx);
+        mn = wave_extreme<false>(mn);
+        if (lane == 0) {
+          s_tok[wave] = tok;
+          s_xmax[wave] = (int)mx;
+          s_xmin[wave] = (int)mn;
         }
       }
       // row scales of the segment
@@ -538,37 +544,40 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
       // binades of its largest, else eight ([d0 d1 d2 0 d3 d4 d5 0]).  Eight-
       // column rows take the first 8-aligned columns, four-column rows the
       // rest; the group is the longest run of its pairs that fits 16*NT
-      // columns (the rest go to the next group).
+      // columns (the rest go to the next group).  Every thread works out the
+      // same layout; row ti's thread and quad q's thread store it.
       int n8 = 0, n4 = 0, fit = 0;
+      uint32_t wmask = 0;                              // rows of eight columns
       for (int ti = 0; ti < count; ++ti) {
         const int w8 = digits_for(s_xmax[ti], s_xmin[ti]) == 4 ? 0 : 1;
         if (8 * (n8 + w8) + 4 * (n4 + 1 - w8) > 16 * NT) break;
         n8 += w8;
         n4 += 1 - w8;
+        wmask |= (uint32_t)w8 << ti;
         ++fit;
       }
       n8 = __builtin_amdgcn_readfirstlane(n8);
       fit = __builtin_amdgcn_readfirstlane(fit);
+      wmask = __builtin_amdgcn_readfirstlane(wmask);
       if (fit < count) {
         count = fit;
         more = 1;
       }
-      if (tid < 4 * NT) s_quad[tid] = -1;
-      __syncthreads();
-      if (tid < count) {
-        int r8 = 0, r4 = 0;
-        for (int ti = 0; ti < tid; ++ti) {
-          if (digits_for(s_xmax[ti], s_xmin[ti]) == 4)
-            ++r4;
-          else
-            ++r8;
+      {
+        int r8 = 0, r4 = 0, myq = -1;
+        for (int ti = 0; ti < count; ++ti) {
+          const bool wide = (wmask >> ti) & 1u;
+          const int q0 = wide ? 2 * r8 : 2 * n8 + r4;  // first quad of the row
+          if (tid == ti) {
+            s_col[ti] = 4 * q0;
+            s_wid[ti] = wide ? 8 : 4;
+          }
+          if (tid == q0) myq = ti;
+          if (wide && tid == q0 + 1) myq = ti + 64;
+          r8 += wide ? 1 : 0;
+          r4 += wide ? 0 : 1;
         }
-        const bool wide = digits_for(s_xmax[tid], s_xmin[tid]) != 4;
-        const int col0 = wide ? 8 * r8 : 8 * n8 + 4 * r4;
-        s_col[tid] = col0;
-        s_wid[tid] = wide ? 8 : 4;
-        s_quad[col0 / 4] = tid;
-        if (wide) s_quad[col0 / 4 + 1] = tid + 64;
+        if (tid < 4 * NT) s_quad[tid] = myq;
       }
       __syncthreads();
 
@@ -937,6 +946,9 @@ hipError_t launch_chunked(GateUpParams p, int nt, hipStream_t stream) {
   // a SIMD's first-wave share, 1/1024 of the SIMD's quarter (as measured for
   // the resident kernel's loop, which this kernel's step loop matches)
   p.wave_share = nt == 1 ? 577 : 547;
+  // a segment's set-up (id scan, row ranges, first digits, the first weights'
+  // latency) takes about as long as this many K-steps of one tile
+  p.seg_cost = kChSegCost;
   return p.down ? launch_chunked_d<true>(p, nt, stream) : launch_chunked_d<false>(p, nt, stream);
 }
 

@@ -28,6 +28,7 @@ struct GateUpParams {
   int q8;                    // 1: signed int8 weights [rows][H] (else packed nibbles [rows][H/8] words)
   int xf32;                  // 1: x and out are float32 (else bf16); probes unchanged
   const uint16_t* sig;       // set by the launchers: the device's bf16 sigmoid table (sigmoid_table)
+  int seg_cost;              // set by launch_chunked: a segment's set-up cost, in K-steps of one tile
 };
 
 // The bf16 sigmoid table of the SwiGLU tail on the current device
