@@ -7,8 +7,10 @@ One step is one grouped call routing the token to every slot of the pool: the
 routing, activation split, weight stream, exact accumulation, scale and
 SwiGLU tail of every slot, in one launch.  ``value`` is algorithmic weight
 bytes (packed gate and up nibbles plus their F32 row scales) per second, the
-median of five repetitions of ``--steps`` timed steps; ``m8`` is the same pool
-with eight tokens on every slot (the verify width).
+median of five repetitions of ``--steps`` timed steps (after SETTLE_S seconds
+of untimed steps, in which the GPU's clocks settle, and ``--warmup`` untimed
+steps); ``m8`` is the same pool with eight tokens on every slot (the verify
+width).
 
 ``shapes`` holds the other measured workloads, each the median of five
 repetitions: single-expert launches and top-8 decode steps captured in HIP
@@ -48,6 +50,7 @@ DISTINCT_CONTENTS = 8
 H, I = 4096, 1536
 SEED = 102
 REPS = 5
+SETTLE_S = 0.3      # seconds of untimed steps before each leg is timed (see settle)
 CSRC = os.path.join(ROOT, "quantized_moe_expert_q4_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_pool.json")
 PARITY_FILE = os.path.join(ROOT, "profiles", "parity_stats.json")
@@ -232,6 +235,20 @@ class Pool:
         return step
 
 
+def settle(step):
+    """Untimed steps for SETTLE_S seconds of wall time: the GPU's clocks ramp
+    up over tens of milliseconds of load (a leg's repetitions kept speeding up
+    without this), so each leg's first repetition starts from the steady
+    state a serving loop runs at."""
+    import time
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < SETTLE_S:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+
+
 def time_steps(step, steps: int, warmup: int):
     """Seconds for `steps` calls of step() on the current stream (HIP events on
     that stream, which is the one the library launches on)."""
@@ -251,7 +268,9 @@ def time_steps(step, steps: int, warmup: int):
 
 
 def timed(step, steps: int, warmup: int, reps: int = REPS):
-    """Median over `reps` repetitions of the mean seconds per step."""
+    """Median over `reps` repetitions of the mean seconds per step (after the
+    clock-settling steps, then `warmup` untimed steps)."""
+    settle(step)
     per = [time_steps(step, steps, warmup if r == 0 else 1) / steps for r in range(reps)]
     return statistics.median(per), per
 
@@ -271,6 +290,7 @@ def graph_timed(calls, reps: int = REPS, replays: int = 5):
     torch.cuda.synchronize()
     g.replay()
     torch.cuda.synchronize()
+    settle(g.replay)
     stream = torch.cuda.current_stream()
     per = []
     for _ in range(reps):
@@ -669,7 +689,8 @@ def main():
         "config": {"workload": f"expert gate/up+SwiGLU, H={H} I={I}, M={M}, {POOL_SLOTS}-slot cold pool "
                                f"({bytes_step / 1e9:.3f} GB of weights+scales per step), one grouped launch per step",
                    "H": H, "I": I, "M": M, "slots": POOL_SLOTS, "bytes_per_step": bytes_step,
-                   "repetitions": REPS, "statistic": "median of the repetitions' mean step time"},
+                   "repetitions": REPS, "statistic": "median of the repetitions' mean step time",
+                   "clock_settle_s": SETTLE_S},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "rows_per_s": round(M * POOL_SLOTS * I / sec, 1),
         "reps_GBps": [round(bytes_step / p / 1e9, 1) for p in per],

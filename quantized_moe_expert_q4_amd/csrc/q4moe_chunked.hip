@@ -59,7 +59,8 @@ constexpr int kChCntSlots = 2048;          // slots whose passes are held in LDS
 constexpr int kChIdRegs = 4;               // routing ids held per thread (2048 pairs)
 constexpr int kChCntWords = kChCntSlots / 32;
 constexpr int kChInvBatch = 64;            // invalid pairs zero-filled per batch
-constexpr int kChSegCost = 64;             // a segment's set-up cost, in K-steps of one tile
+constexpr int kChSegCost = 128;            // a segment's set-up cost, in K-steps of a one-pair tile
+constexpr int kChTileBase = 24;            // a tile of n pairs costs (kChTileBase + n) / (kChTileBase + 1) one-pair tiles
 
 // A wave's share of a round's units: the first wave of SIMD q takes the
 // fraction [q/4, q/4 + share/4096) of the round's tiles, the second wave the
@@ -108,6 +109,7 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   __shared__ float s_usc[DOWN ? 1 : kChSegTiles * RT];
   __shared__ uint8_t s_pass[kChCntSlots];     // passes of each slot
   __shared__ int s_ppre[kChCntWords + 1];     // passes of the slots before each 32-slot word, and in all
+  __shared__ long long s_cpre[kChCntWords + 1];  // cost of the slots before each word, and in all
   __shared__ int s_pairs[G];
   __shared__ int s_tok[G];                   // x row of each pair of the group
   __shared__ int s_xmax[G];
@@ -192,25 +194,44 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   }
   __syncthreads();
   auto passes = [&](int c) { return (c + G - 1) / G; };
+  // Cost units: a tile of a pass of n pairs costs S * (kChTileBase + n)
+  // (staging and finishing grow with the pairs), a segment's set-up
+  // segu; a slot with c pairs in ps passes costs ps * segu + ts * (ps *
+  // kChTileBase + c).
+  const int64_t ts = (int64_t)tps * S;
+  const int64_t segu = (int64_t)a.seg_cost * (kChTileBase + 1);
   if (counting && wave == 0) {
-    // passes of the 32 slots of word `lane` (one byte each), then their prefix
-    // over words; a slot with more than 255 passes turns the counts off
+    // passes and cost of the 32 slots of word `lane` (passes one byte each),
+    // then their prefixes over words; a slot with more than 255 passes turns
+    // the counts off
     int c = 0, big = 0;
+    long long cw = 0;
     for (int j = 0; j < 32; ++j) {
       const int sl = 32 * lane + j;
-      const int ps = sl < a.num_slots ? passes((int)cnt[sl]) : 0;
+      const int n = sl < a.num_slots ? (int)cnt[sl] : 0;
+      const int ps = passes(n);
       big |= ps > 255;
       s_pass[sl] = (uint8_t)ps;
       c += ps;
+      cw += ps * segu + ts * ((int64_t)ps * kChTileBase + n);
     }
     int incl = c;
+    long long cincl = cw;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
       const int o = __shfl_up(incl, d);
-      if (lane >= d) incl += o;
+      const long long co = __shfl_up(cincl, d);
+      if (lane >= d) {
+        incl += o;
+        cincl += co;
+      }
     }
     s_ppre[lane] = incl - c;
-    if (lane == 63) s_ppre[64] = __any(big) ? -1 : incl;
+    s_cpre[lane] = cincl - cw;
+    if (lane == 63) {
+      s_ppre[64] = __any(big) ? -1 : incl;
+      s_cpre[64] = cincl;
+    }
   }
   if (grouped && blockIdx.x == 0 && tid == 0 && a.invalid_count) *a.invalid_count = s_inv;
   __syncthreads();
@@ -245,18 +266,41 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     }
   };
   // Work-groups take even shares of a cost axis on which each pass is a
-  // set-up block of a.seg_cost followed by its tiles at S each (in K-steps of
-  // one tile): a share that reaches into another pass (one more segment set-
-  // up) takes that many fewer tiles.  Tile j of pass p starts at p * pc +
-  // seg_cost + j * S and goes to the work-group whose share holds its start.
-  const int64_t pc = (int64_t)tps * S + a.seg_cost;
-  const int64_t C = (int64_t)npass * pc;
-  auto tile_of = [&](int64_t c) {
-    const int64_t p = c / pc;
-    const int64_t r = c - p * pc - a.seg_cost;
-    return (int)(p * tps + (r > 0 ? (r + S - 1) / S : 0));
+  // set-up block (segu) followed by its tiles: a share that reaches into
+  // another pass (one more segment set-up) takes fewer tiles, and tiles of
+  // passes with more pairs count for more.  Tile j of a pass goes to the
+  // work-group whose share holds its start.  Without counts every pass is
+  // costed as one of G pairs.
+  auto tile_at = [&](int64_t rem, int pv, int n) {   // rem: cost into pass pv of n pairs
+    const int64_t r = rem - segu, tc = (int64_t)S * (kChTileBase + n);
+    return pv * tps + (r > 0 ? (int)((r + tc - 1) / tc) : 0);
   };
-  const int v0 = tile_of((int64_t)blockIdx.x * C / NB), v1 = tile_of((int64_t)(blockIdx.x + 1) * C / NB);
+  auto locate = [&](int64_t c) {
+    if (!counted) {
+      const int64_t pc = segu + ts * (kChTileBase + G);
+      const int64_t p = c / pc;
+      return tile_at(c - p * pc, (int)p, G);
+    }
+    if (c >= s_cpre[64]) return npass * tps;
+    int lo = 0;                                   // the last word starting at or before c
+#pragma unroll
+    for (int step = 32; step > 0; step >>= 1)
+      if (s_cpre[lo + step] <= c) lo += step;
+    int64_t rem = c - s_cpre[lo];
+    int pv = s_ppre[lo];
+    for (int sl = 32 * lo;; ++sl) {                // the word's cost range holds c
+      const int ps = s_pass[sl], n = (int)cnt[sl];
+      for (int g = 0; g < ps; ++g) {
+        const int cg = min(G, n - g * G);
+        const int64_t pcost = segu + ts * (kChTileBase + cg);
+        if (rem < pcost) return tile_at(rem, pv + g, cg);
+        rem -= pcost;
+      }
+      pv += ps;
+    }
+  };
+  const int64_t C = counted ? s_cpre[64] : (int64_t)npass * (segu + ts * (kChTileBase + G));
+  const int v0 = locate((int64_t)blockIdx.x * C / NB), v1 = locate((int64_t)(blockIdx.x + 1) * C / NB);
 
   // ---- per-lane constants ----
   const LineLanes lines = line_lanes(lane);
@@ -291,52 +335,72 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     return (uint32_t)(row < I ? row : I - 1) * rbytes + 16u * (uint32_t)(lane & 7);
   };
 
-  // digits of x pair r (8-value units 2r, 2r+1: words 2i, 2i+1 of k-group gg
-  // of chunk step st) of group row tl, in the operand order of split_planes:
-  // word 2i + h goes to planes 2(i/2) (even positions) and 2(i/2) + 1 (odd),
-  // dword 2(i%2) + h of each 16-byte chunk
-  auto stage_pair = [&](uint8_t* buf, int W, int col0, int st, int gg, int i, const uint4 xa, const uint4 xb,
-                        int etop1) {
-    const int pe = 2 * (i >> 1);
-    uint8_t* base = buf + st * sbytes + 8 * (i & 1);
-    auto put = [&](int j, int h, int col, uint32_t v) {
-      *(uint32_t*)(base + 4 * h + (j * NT + (col >> 4)) * 1024 + ch_chunk(gg, col & 15) * 16) = v;
+  // Digits of one quad of x: 32 consecutive values of a group row (its 8-
+  // value words j = 0..3, starting at value 32 qg of chunk step st, qg =
+  // 2 k-group + q) in the operand order of split_planes.  Word j is dword j
+  // of the 16-byte chunks of planes 2q (its even positions) and 2q + 1 (odd)
+  // in the row's digit columns, so the quad fills whole chunks: one 16-byte
+  // store per (column, plane), at fixed offsets from the row's first chunk
+  // (columns col0 .. col0 + 3 of a four-column row lie in one 4-aligned
+  // group, which the k-group's swizzle keeps together; an eight-column row
+  // has two such groups).
+  auto stage_quad = [&](uint8_t* buf, int W, int col0, int st, int qg, const uint4 (&xq)[4], int etop1) {
+    const int gg = qg >> 1, q = qg & 1;
+    const int bp = (col0 & 15) ^ (4 * gg);           // chunk position of column col0
+    uint8_t* const b0 = buf + st * sbytes + (2 * q * NT + (col0 >> 4)) * 1024 + gg * 256 + bp * 16;
+    auto vals = [&](const uint4 w, int par, uint32_t (&xs)[4]) {
+      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xs[e] = par ? u[e] >> 16 : u[e] & 0xFFFFu;
     };
-    auto word = [&](int h, const uint4 xq) {
-      const uint32_t xs[8] = {xq.x & 0xFFFFu, xq.x >> 16, xq.y & 0xFFFFu, xq.y >> 16,
-                              xq.z & 0xFFFFu, xq.z >> 16, xq.w & 0xFFFFu, xq.w >> 16};
-      uint32_t v[8], ev[4], od[4];
-      if (W == 4) {
+    if (W == 4) {
 #pragma unroll
-        for (int p = 0; p < 8; ++p) v[p] = x_digits4(xs[p], etop1);
-        plane_digits4(v, ev, od);
+      for (int par = 0; par < 2; ++par) {
+        uint32_t d[4][4];                              // [word][digit]
 #pragma unroll
-        for (int sd = 0; sd < 4; ++sd) {
-          put(pe, h, col0 + sd, ev[sd]);
-          put(pe + 1, h, col0 + sd, od[sd]);
+        for (int wj = 0; wj < 4; ++wj) {
+          uint32_t xs[4], v[4];
+          vals(xq[wj], par, xs);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = x_digits4(xs[e], etop1);
+          transpose4(v[0], v[1], v[2], v[3], d[wj]);
         }
-      } else {
-        // six digits: columns [d0 d1 d2 0 d3 d4 d5 0]
-        uint32_t hv[8], eh[4], oh[4];
 #pragma unroll
-        for (int p = 0; p < 8; ++p) {
-          const uint64_t z = x_digits(xs[p], etop1);
-          v[p] = (uint32_t)z;
-          hv[p] = (uint32_t)(z >> 32);
-        }
-        plane_digits4(v, ev, od);
-        plane_digits4(hv, eh, oh);
-        const uint32_t e8[8] = {ev[0], ev[1], ev[2], 0u, ev[3], eh[0], eh[1], 0u};
-        const uint32_t o8[8] = {od[0], od[1], od[2], 0u, od[3], oh[0], oh[1], 0u};
-#pragma unroll
-        for (int sd = 0; sd < 8; ++sd) {
-          put(pe, h, col0 + sd, e8[sd]);
-          put(pe + 1, h, col0 + sd, o8[sd]);
-        }
+        for (int sd = 0; sd < 4; ++sd)
+          *(uint4*)(b0 + par * NT * 1024 + 16 * sd) = make_uint4(d[0][sd], d[1][sd], d[2][sd], d[3][sd]);
       }
-    };
-    word(0, xa);
-    word(1, xb);
+    } else {
+      // six digits: columns [d0 d1 d2 0 d3 d4 d5 0], the second group of
+      // four at chunk position bp ^ 4
+      uint8_t* const b1 = b0 + ((bp ^ 4) - bp) * 16;
+#pragma unroll
+      for (int par = 0; par < 2; ++par) {
+        uint32_t dl[4][4], dh[4][4];
+#pragma unroll
+        for (int wj = 0; wj < 4; ++wj) {
+          uint32_t xs[4], lo[4], hi[4];
+          vals(xq[wj], par, xs);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint64_t z = x_digits_nb(xs[e], etop1);
+            lo[e] = (uint32_t)z;
+            hi[e] = (uint32_t)(z >> 32);
+          }
+          transpose4(lo[0], lo[1], lo[2], lo[3], dl[wj]);
+          transpose4(hi[0], hi[1], hi[2], hi[3], dh[wj]);
+        }
+        uint8_t* const p0 = b0 + par * NT * 1024;
+        uint8_t* const p1 = b1 + par * NT * 1024;
+#pragma unroll
+        for (int sd = 0; sd < 3; ++sd) *(uint4*)(p0 + 16 * sd) = make_uint4(dl[0][sd], dl[1][sd], dl[2][sd], dl[3][sd]);
+        *(uint4*)(p0 + 48) = make_uint4(0, 0, 0, 0);
+        *(uint4*)(p1) = make_uint4(dl[0][3], dl[1][3], dl[2][3], dl[3][3]);
+#pragma unroll
+        for (int sd = 0; sd < 2; ++sd)
+          *(uint4*)(p1 + 16 + 16 * sd) = make_uint4(dh[0][sd], dh[1][sd], dh[2][sd], dh[3][sd]);
+        *(uint4*)(p1 + 48) = make_uint4(0, 0, 0, 0);
+      }
+    }
   };
 
   // ---- segments: one pass over at most kChSegTiles tiles of one slot ----
@@ -581,33 +645,34 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
       }
       __syncthreads();
 
-      // x pair xp of chunk c (pairs ordered (step, pair in step, row): xp =
-      // (st * 16 + r16) * count + tl) of the group, at K index k0 of the row;
-      // units past the row's end (padding steps) are loaded from its start
-      // and replaced by zeros when they are split, not here (a write to the
-      // loads' registers would have to wait for them at once)
-      auto pair_k = [&](int c, int pp) { return (c * Sc + (pp >> 4)) * 256 + 16 * (pp & 15); };
-      auto load_pair = [&](int c, int pp, int tl, uint4& xa, uint4& xb) {
-        const int k0 = pair_k(c, pp);
+      // Quad xs of chunk c: quads in row-major order (xs = tl * nq + r for
+      // nq quads per row in the chunk, r = 8 st + qg), so that a wave's
+      // quads mostly share a row (and its digit width); at K index k0 of the
+      // row.  Words past the row's end (padding steps) are loaded from its
+      // start and replaced by zeros when they are split, not here (a write to
+      // the loads' registers would have to wait for them at once).
+      auto quad_k = [&](int c, int r) { return c * Sc * 256 + 32 * r; };
+      auto load_quad = [&](int c, int r, int tl, uint4 (&xq)[4]) {
+        const int k0 = quad_k(c, r);
         const uint16_t* row = a.x + (uint64_t)s_tok[tl] * H;
-        xa = *(const uint4*)(row + (k0 < H ? k0 : 0));
-        xb = *(const uint4*)(row + (k0 + 8 < H ? k0 + 8 : 0));
+#pragma unroll
+        for (int wj = 0; wj < 4; ++wj) xq[wj] = *(const uint4*)(row + (k0 + 8 * wj < H ? k0 + 8 * wj : 0));
       };
-      auto put_pair = [&](uint8_t* buf, int c, int pp, int tl, uint4 xa, uint4 xb) {
-        const int k0 = pair_k(c, pp);
-        if (k0 >= H) xa = make_uint4(0, 0, 0, 0);
-        if (k0 + 8 >= H) xb = make_uint4(0, 0, 0, 0);
-        const int r16 = pp & 15;
-        stage_pair(buf, s_wid[tl], s_col[tl], pp >> 4, r16 >> 2, r16 & 3, xa, xb, max((s_xmax[tl] >> 7) & 0xFF, 1));
+      auto put_quad = [&](uint8_t* buf, int c, int r, int tl, uint4 (&xq)[4]) {
+        const int k0 = quad_k(c, r);
+#pragma unroll
+        for (int wj = 0; wj < 4; ++wj)
+          if (k0 + 8 * wj >= H) xq[wj] = make_uint4(0, 0, 0, 0);
+        stage_quad(buf, s_wid[tl], s_col[tl], r >> 3, r & 7, xq, max((s_xmax[tl] >> 7) & 0xFF, 1));
       };
       // chunk 0 of the group, by every thread
       {
-        const int xp0 = count * min(Sc, S) * 16;
-        for (int xp = tid; xp < xp0; xp += kChThreads) {
-          const int pp = xp / count, tl = xp - pp * count;
-          uint4 xa, xb;
-          load_pair(0, pp, tl, xa, xb);
-          put_pair(s_dig, 0, pp, tl, xa, xb);
+        const int nq0 = min(Sc, S) * 8;
+        for (int xs = tid; xs < count * nq0; xs += kChThreads) {
+          const int tl = xs / nq0, r = xs - tl * nq0;
+          uint4 xq[4];
+          load_quad(0, r, tl, xq);
+          put_quad(s_dig, 0, r, tl, xq);
         }
       }
       __syncthreads();
@@ -751,7 +816,6 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         }
       } else {
         v4i accg[kChMaxT][NT], accu[kChMaxT][NT];
-        const int qd = 64 / count, rd = 64 - qd * count;  // one slice: 64 pairs further on
         for (int r = 0; r < nr; ++r)
         for (int c = 0; c < nch; ++c) {
           const int k = r * nch + c;                   // element index: digit buffer k % 2
@@ -768,40 +832,31 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
               }
           }
           const uint8_t* buf = s_dig + (k & 1) * kChBuf;
-          // this wave's share of element k+1's digits: pairs [xp, xe) of
-          // chunk c1, one slice (64 pairs, one per lane) per pass of the step
+          // this wave's share of element k+1's digits: quads [xs, xe) of
+          // chunk c1, one slice (64 quads, one per lane) per pass of the step
           // loop
           const bool stg = k + 1 < nr * nch;
           const int c1 = c + 1 == nch ? 0 : c + 1;
           uint8_t* sbuf = s_dig + ((k + 1) & 1) * kChBuf;
-          const int xpn = stg ? count * min(Sc, S - c1 * Sc) * 16 : 0;
-          int xp = wave * xpn / kChWaves + lane;
+          const int nq1 = min(Sc, S - c1 * Sc) * 8;   // quads per row in chunk c1
+          const int xpn = stg ? count * nq1 : 0;
+          int xs = wave * xpn / kChWaves + lane;
           const int xe = (wave + 1) * xpn / kChWaves;
-          int pp = xp / count, tl = xp - pp * count;
-          auto slice_next = [&]() {
-            xp += 64;
-            pp += qd;
-            tl += rd;
-            if (tl >= count) {
-              tl -= count;
-              ++pp;
-            }
-          };
           // A slice's x is loaded after the take at a pass's last step and
           // split into LDS at the same point of the next pass: the take there
           // has waited for every weight load issued before the x loads, so the
           // wait for x covers nothing still in flight for the ring.
-          uint4 xa = make_uint4(0, 0, 0, 0), xb = make_uint4(0, 0, 0, 0);
-          int ppp = 0, tlp = 0;                        // the pending slice's pair
+          uint4 xq[4] = {};
+          int rp = 0, tlp = 0;                         // the pending slice's quad
           bool pend = false;
           auto slice = [&]() {
-            if (pend) put_pair(sbuf, c1, ppp, tlp, xa, xb);
-            pend = xp < xe;
+            if (pend) put_quad(sbuf, c1, rp, tlp, xq);
+            pend = xs < xe;
             if (pend) {
-              load_pair(c1, pp, tl, xa, xb);
-              ppp = pp;
-              tlp = tl;
-              slice_next();
+              tlp = xs / nq1;
+              rp = xs - tlp * nq1;
+              load_quad(c1, rp, tlp, xq);
+              xs += 64;
             }
           };
 #pragma unroll
@@ -810,12 +865,14 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             const int pa = max(ua, tile * scc), pb = min(ub, (tile + 1) * scc);
             for (int u = pa; u < pb; u += kChU) steps(buf, u - tile * scc, accg[j], accu[j], slice);
           }
-          if (pend) put_pair(sbuf, c1, ppp, tlp, xa, xb);
+          if (pend) put_quad(sbuf, c1, rp, tlp, xq);
           // the rest of this wave's share (rounds too short for all its slices)
-          while (xp < xe) {
-            load_pair(c1, pp, tl, xa, xb);
-            put_pair(sbuf, c1, pp, tl, xa, xb);
-            slice_next();
+          while (xs < xe) {
+            tlp = xs / nq1;
+            rp = xs - tlp * nq1;
+            load_quad(c1, rp, tlp, xq);
+            put_quad(sbuf, c1, rp, tlp, xq);
+            xs += 64;
           }
           __syncthreads();  // element k's digits read, element k+1's staged
           if (c != nch - 1) continue;

@@ -40,6 +40,22 @@ __device__ __forceinline__ uint64_t x_digits(uint32_t b, int etop1) {
   return ((uint64_t)X + C) ^ C;
 }
 
+// The digits of x_digits without branches (for code that runs them between
+// matrix-core operations): the magnitude is shifted 8 bits further than X
+// needs (a shift below zero leaves nothing: the value is then under half a
+// unit of X) and rounded half up by those 8 bits, which gives X for every
+// shift x_digits takes.
+__device__ __forceinline__ uint64_t x_digits_nb(uint32_t b, int etop1) {
+  const uint32_t E = (b >> 7) & 0xFFu;
+  const uint64_t mag = (b & 0x7Fu) | (E ? 0x80u : 0u);
+  const int s8 = (int)(E ? E : 1u) - etop1 + kFracBits + 8;  // at most kFracBits + 8
+  const uint64_t Xs = s8 >= 0 ? mag << (s8 & 63) : 0ull;
+  const uint64_t Xm = (Xs + 0x80u) >> 8;
+  const uint64_t X = (b & 0x8000u) ? 0ull - Xm : Xm;
+  const uint64_t C = 0x808080808080ull;
+  return (X + C) ^ C;
+}
+
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
   const uint32_t u = __float_as_uint(f);
   if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)(((u >> 16) & 0x8000u) | 0x7FC0u);
