@@ -200,21 +200,34 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   // kChTileBase + c).
   const int64_t ts = (int64_t)tps * S;
   const int64_t segu = (int64_t)a.seg_cost * (kChTileBase + 1);
+  auto slot_cost = [&](int ps, int n) { return ps * segu + ts * ((int64_t)ps * kChTileBase + n); };
   if (counting && wave == 0) {
-    // passes and cost of the 32 slots of word `lane` (passes one byte each),
-    // then their prefixes over words; a slot with more than 255 passes turns
-    // the counts off
-    int c = 0, big = 0;
-    long long cw = 0;
-    for (int j = 0; j < 32; ++j) {
-      const int sl = 32 * lane + j;
+    // passes (one byte each) and cost of every slot, two 32-slot words per
+    // step (lane j: slot 64 i + j), each word's totals parked in s_ppre and
+    // s_cpre; then their prefixes over words.  A slot with more than 255
+    // passes turns the counts off.
+    const int nw = (a.num_slots + 31) >> 5;
+    int big = 0;
+    for (int i = 0; 2 * i < nw; ++i) {
+      const int sl = 64 * i + lane;
       const int n = sl < a.num_slots ? (int)cnt[sl] : 0;
       const int ps = passes(n);
       big |= ps > 255;
       s_pass[sl] = (uint8_t)ps;
-      c += ps;
-      cw += ps * segu + ts * ((int64_t)ps * kChTileBase + n);
+      int pw = ps;
+      long long cw = slot_cost(ps, n);
+#pragma unroll
+      for (int d = 1; d < 32; d <<= 1) {
+        pw += __shfl_xor(pw, d);
+        cw += __shfl_xor(cw, d);
+      }
+      if ((lane & 31) == 0 && 2 * i + (lane >> 5) < nw) {
+        s_ppre[2 * i + (lane >> 5)] = pw;
+        s_cpre[2 * i + (lane >> 5)] = cw;
+      }
     }
+    const int c = lane < nw ? s_ppre[lane] : 0;
+    const long long cw = lane < nw ? s_cpre[lane] : 0;
     int incl = c;
     long long cincl = cw;
 #pragma unroll
@@ -254,16 +267,19 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
     for (int step = 32; step > 0; step >>= 1)
       if (s_ppre[lo + step] <= pv) lo += step;
-    int rem = pv - s_ppre[lo];
-    for (int sl = 32 * lo;; ++sl) {
-      const int ps = s_pass[sl];
-      if (rem < ps) {
-        e = sl;
-        g = rem;
-        return;
-      }
-      rem -= ps;
+    // the word's slots one per lane (both half-waves alike): the first whose
+    // inclusive pass count exceeds pv's place in the word
+    const int rem = pv - s_ppre[lo];
+    const int ps = s_pass[32 * lo + (lane & 31)];
+    int incl = ps;
+#pragma unroll
+    for (int d = 1; d < 32; d <<= 1) {
+      const int o = __shfl_up(incl, d, 32);
+      if ((lane & 31) >= d) incl += o;
     }
+    const int k = __builtin_ctzll(__ballot(incl > rem) & 0xFFFFFFFFull);
+    e = 32 * lo + k;
+    g = __builtin_amdgcn_readfirstlane(rem - (__shfl(incl, k) - __shfl(ps, k)));
   };
   // Work-groups take even shares of a cost axis on which each pass is a
   // set-up block (segu) followed by its tiles: a share that reaches into
@@ -286,21 +302,36 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
     for (int step = 32; step > 0; step >>= 1)
       if (s_cpre[lo + step] <= c) lo += step;
+    // the word's slots one per lane (both half-waves alike): the first whose
+    // inclusive cost exceeds c's place in the word (the word's range holds c)
     int64_t rem = c - s_cpre[lo];
-    int pv = s_ppre[lo];
-    for (int sl = 32 * lo;; ++sl) {                // the word's cost range holds c
-      const int ps = s_pass[sl], n = (int)cnt[sl];
-      for (int g = 0; g < ps; ++g) {
-        const int cg = min(G, n - g * G);
-        const int64_t pcost = segu + ts * (kChTileBase + cg);
-        if (rem < pcost) return tile_at(rem, pv + g, cg);
-        rem -= pcost;
+    const int sl = 32 * lo + (lane & 31);
+    const int ps = s_pass[sl], n = (int)cnt[sl];
+    int pincl = ps;
+    long long cincl = slot_cost(ps, n);
+#pragma unroll
+    for (int d = 1; d < 32; d <<= 1) {
+      const int po = __shfl_up(pincl, d, 32);
+      const long long co = __shfl_up(cincl, d, 32);
+      if ((lane & 31) >= d) {
+        pincl += po;
+        cincl += co;
       }
-      pv += ps;
+    }
+    const int k = __builtin_ctzll(__ballot(cincl > rem) & 0xFFFFFFFFull);
+    const int psk = __shfl(ps, k), nk = __shfl(n, k);
+    rem -= __shfl(cincl, k) - slot_cost(psk, nk);
+    const int pv = s_ppre[lo] + __shfl(pincl, k) - psk;
+    for (int g = 0;; ++g) {                        // the slot's pass that holds c
+      const int cg = min(G, nk - g * G);
+      const int64_t pcost = segu + ts * (kChTileBase + cg);
+      if (rem < pcost || g == psk - 1) return tile_at(rem, pv + g, cg);
+      rem -= pcost;
     }
   };
   const int64_t C = counted ? s_cpre[64] : (int64_t)npass * (segu + ts * (kChTileBase + G));
-  const int v0 = locate((int64_t)blockIdx.x * C / NB), v1 = locate((int64_t)(blockIdx.x + 1) * C / NB);
+  const int v0 = __builtin_amdgcn_readfirstlane(locate((int64_t)blockIdx.x * C / NB));
+  const int v1 = __builtin_amdgcn_readfirstlane(locate((int64_t)(blockIdx.x + 1) * C / NB));
 
   // ---- per-lane constants ----
   const LineLanes lines = line_lanes(lane);
