@@ -59,7 +59,6 @@ constexpr int kChCntSlots = 2048;          // slots whose passes are held in LDS
 constexpr int kChIdRegs = 4;               // routing ids held per thread (2048 pairs)
 constexpr int kChCntWords = kChCntSlots / 32;
 constexpr int kChInvBatch = 64;            // invalid pairs zero-filled per batch
-constexpr int kChSegCost = 128;            // a segment's set-up cost, in K-steps of a one-pair tile
 constexpr int kChTileBase = 24;            // a tile of n pairs costs (kChTileBase + n) / (kChTileBase + 1) one-pair tiles
 
 // A wave's share of a round's units: the first wave of SIMD q takes the
@@ -1035,8 +1034,11 @@ hipError_t launch_chunked(GateUpParams p, int nt, hipStream_t stream) {
   // the resident kernel's loop, which this kernel's step loop matches)
   p.wave_share = nt == 1 ? 577 : 547;
   // a segment's set-up (id scan, row ranges, first digits, the first weights'
-  // latency) takes about as long as this many K-steps of one tile
-  p.seg_cost = kChSegCost;
+  // latency), in K-steps of a one-pair tile: a fixed part and one that grows
+  // with the row length (the range pass reads whole rows); fitted to interleaved
+  // runs of the down projection (6 steps: 64 best of 0..128), the routed step
+  // (24: 128 of 96..192) and the large shape at four tokens (28: 192 of 96..192)
+  p.seg_cost = 40 + 4 * p.steps;
   return p.down ? launch_chunked_d<true>(p, nt, stream) : launch_chunked_d<false>(p, nt, stream);
 }
 
