@@ -262,10 +262,8 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
       g = 0;
       return;
     }
-    int lo = 0;
-#pragma unroll
-    for (int step = 32; step > 0; step >>= 1)
-      if (s_ppre[lo + step] <= pv) lo += step;
+    // the last word starting at or before pv (word prefixes one per lane)
+    const int lo = __popcll(__ballot(s_ppre[lane] <= pv)) - 1;
     // the word's slots one per lane (both half-waves alike): the first whose
     // inclusive pass count exceeds pv's place in the word
     const int rem = pv - s_ppre[lo];
@@ -286,21 +284,33 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   // passes with more pairs count for more.  Tile j of a pass goes to the
   // work-group whose share holds its start.  Without counts every pass is
   // costed as one of G pairs.
+  // ceil(x / d) and floor(x / d) for 0 <= x < 2^50, 0 < d < 2^31: a double
+  // quotient corrected by one step either way (no 64-bit division)
+  auto ceil_div = [&](int64_t x, int64_t d) {
+    int64_t q = (int64_t)((double)x / (double)d);
+    if (q * d < x) ++q;
+    if (q > 0 && (q - 1) * d >= x) --q;
+    return q;
+  };
+  auto floor_div = [&](int64_t x, int64_t d) {
+    int64_t q = (int64_t)((double)x / (double)d);
+    if (q * d > x) --q;
+    if ((q + 1) * d <= x) ++q;
+    return q;
+  };
   auto tile_at = [&](int64_t rem, int pv, int n) {   // rem: cost into pass pv of n pairs
     const int64_t r = rem - segu, tc = (int64_t)S * (kChTileBase + n);
-    return pv * tps + (r > 0 ? (int)((r + tc - 1) / tc) : 0);
+    return pv * tps + (r > 0 ? (int)ceil_div(r, tc) : 0);
   };
   auto locate = [&](int64_t c) {
     if (!counted) {
       const int64_t pc = segu + ts * (kChTileBase + G);
-      const int64_t p = c / pc;
+      const int64_t p = floor_div(c, pc);
       return tile_at(c - p * pc, (int)p, G);
     }
     if (c >= s_cpre[64]) return npass * tps;
-    int lo = 0;                                   // the last word starting at or before c
-#pragma unroll
-    for (int step = 32; step > 0; step >>= 1)
-      if (s_cpre[lo + step] <= c) lo += step;
+    // the last word starting at or before c (word prefixes one per lane)
+    const int lo = __popcll(__ballot(s_cpre[lane] <= c)) - 1;
     // the word's slots one per lane (both half-waves alike): the first whose
     // inclusive cost exceeds c's place in the word (the word's range holds c)
     int64_t rem = c - s_cpre[lo];
@@ -329,8 +339,8 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     }
   };
   const int64_t C = counted ? s_cpre[64] : (int64_t)npass * (segu + ts * (kChTileBase + G));
-  const int v0 = __builtin_amdgcn_readfirstlane(locate((int64_t)blockIdx.x * C / NB));
-  const int v1 = __builtin_amdgcn_readfirstlane(locate((int64_t)(blockIdx.x + 1) * C / NB));
+  const int v0 = __builtin_amdgcn_readfirstlane(locate(floor_div((int64_t)blockIdx.x * C, NB)));
+  const int v1 = __builtin_amdgcn_readfirstlane(locate(floor_div((int64_t)(blockIdx.x + 1) * C, NB)));
 
   // ---- per-lane constants ----
   const LineLanes lines = line_lanes(lane);
