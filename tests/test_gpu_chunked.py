@@ -96,6 +96,25 @@ def test_chunked_skewed_routing_invalid_and_duplicate_ids():
     check_parity(out, g, u, gr, ur, orf, "chunked skewed routing")
 
 
+def test_chunked_invalid_ids_before_and_past_the_id_registers():
+    """Invalid ids among the first 2048 pairs (marked at the start from the ids
+    held in registers) and past them (read again at the end): 2400 pairs of
+    400 tokens over 600 slots, four per slot on average."""
+    E, H, I, M, K = 600, 512, 48, 400, 6
+    rng = np.random.default_rng(6006)
+    lay, slots = _pool(rng, E, H, I)
+    x = synth.bf16_normal(rng, (M, H))
+    ids = synth.top_k_routing(rng, M, K, E)
+    flat = ids.reshape(-1)
+    for p, v in [(0, -1), (7, E), (511, -9), (1024, E + 1), (2047, -1), (2048, E), (2222, -3), (2399, 1 << 24)]:
+        flat[p] = v
+    say(f"[chunked invalid ids E={E} H={H} I={I} M={M} K={K}]")
+    (out, g, u), invalid = run_grouped(slots, lay, x, ids, H, I)
+    gr, ur, orf, bad = oracle.expert_gate_up_grouped(slots, lay.slot_bytes, E, lay, x, ids, H, I)
+    assert bad == 8 and invalid == 8
+    check_parity(out, g, u, gr, ur, orf, "chunked invalid ids before and past the id registers")
+
+
 @pytest.mark.parametrize("H,I,M,wide", [(7168, 512, 3, True), (16384, 64, 5, False), (12288, 48, 8, False)])
 def test_chunked_single_expert(H, I, M, wide):
     """Single-expert calls of up to eight tokens whose digits exceed the

@@ -119,6 +119,22 @@ def test_decode_duplicates_and_invalid_ids():
     _check(slots, lay, x, ids, H, I, "decode duplicates and invalid ids")
 
 
+def test_invalid_ids_before_and_past_the_id_registers():
+    """Invalid ids among the first 2048 pairs (marked at the start from the
+    ids held in registers) and past them (read again at the end), in one call
+    of eight tokens: every such pair is zero and counted."""
+    E, M, K, H, I = 300, 8, 300, 256, 16
+    rng = np.random.default_rng(2048)
+    lay, slots = _pool(rng, E, H, I)
+    x = synth.bf16_normal(rng, (M, H))
+    ids = np.stack([rng.permutation(E)[:K] for _ in range(M)]).astype(np.int32)
+    flat = ids.reshape(-1)
+    for p, v in [(0, -1), (5, E), (511, -7), (512, E + 3), (2047, -1), (2048, E), (2300, -2), (2399, 1 << 20)]:
+        flat[p] = v
+    say("[invalid ids before and past the id registers]")
+    _check(slots, lay, x, ids, H, I, "invalid ids before and past the id registers")
+
+
 @pytest.mark.parametrize("M", [2, 5])
 def test_token_routed_three_times_to_one_slot(M):
     """A token routed an odd number (3) of times to one slot while every other
