@@ -648,40 +648,38 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
       // binades of its largest, else eight ([d0 d1 d2 0 d3 d4 d5 0]).  Eight-
       // column rows take the first 8-aligned columns, four-column rows the
       // rest; the group is the longest run of its pairs that fits 16*NT
-      // columns (the rest go to the next group).  Every thread works out the
-      // same layout; row ti's thread and quad q's thread store it.
-      int n8 = 0, n4 = 0, fit = 0;
-      uint32_t wmask = 0;                              // rows of eight columns
-      for (int ti = 0; ti < count; ++ti) {
-        const int w8 = digits_for(s_xmax[ti], s_xmin[ti]) == 4 ? 0 : 1;
-        if (8 * (n8 + w8) + 4 * (n4 + 1 - w8) > 16 * NT) break;
-        n8 += w8;
-        n4 += 1 - w8;
-        wmask |= (uint32_t)w8 << ti;
-        ++fit;
-      }
-      n8 = __builtin_amdgcn_readfirstlane(n8);
-      fit = __builtin_amdgcn_readfirstlane(fit);
-      wmask = __builtin_amdgcn_readfirstlane(wmask);
+      // columns (the rest go to the next group).  Lane ti of every wave reads
+      // row ti's range, a ballot gives the eight-column rows, and row ti's
+      // thread and quad q's thread store the layout.
+      const bool w8l = lane < count && digits_for(s_xmax[lane], s_xmin[lane]) != 4;
+      const uint32_t wall = (uint32_t)__ballot(w8l);   // rows of eight columns (G <= 32)
+      // rows 0..ti take 4 (ti + 1) + 4 (eight-column rows among them) columns
+      const bool okl = lane < count && 4 * (lane + 1) + 4 * __popc(wall & ((2u << lane) - 1u)) <= 16 * NT;
+      const int fit = __builtin_amdgcn_readfirstlane(__popcll(__ballot(okl)));  // a prefix of the rows
+      const uint32_t wmask = __builtin_amdgcn_readfirstlane(wall & ((1u << fit) - 1u));
+      const int n8 = __builtin_amdgcn_readfirstlane(__popc(wmask));
       if (fit < count) {
         count = fit;
         more = 1;
       }
-      {
-        int r8 = 0, r4 = 0, myq = -1;
-        for (int ti = 0; ti < count; ++ti) {
-          const bool wide = (wmask >> ti) & 1u;
-          const int q0 = wide ? 2 * r8 : 2 * n8 + r4;  // first quad of the row
-          if (tid == ti) {
-            s_col[ti] = 4 * q0;
-            s_wid[ti] = wide ? 8 : 4;
-          }
-          if (tid == q0) myq = ti;
-          if (wide && tid == q0 + 1) myq = ti + 64;
-          r8 += wide ? 1 : 0;
-          r4 += wide ? 0 : 1;
-        }
-        if (tid < 4 * NT) s_quad[tid] = myq;
+      auto nth_row = [&](uint32_t w, int j) {          // the j-th set bit of w
+        for (int k = 0; k < j; ++k) w &= w - 1u;
+        return (int)__builtin_ctz(w);
+      };
+      if (tid < count) {
+        const bool wide = (wmask >> tid) & 1u;
+        const int b8 = __popc(wmask & ((1u << tid) - 1u));
+        const int q0 = wide ? 2 * b8 : 2 * n8 + (tid - b8);  // first quad of the row
+        s_col[tid] = 4 * q0;
+        s_wid[tid] = wide ? 8 : 4;
+      }
+      if (tid < 4 * NT) {
+        int myq = -1;
+        if (tid < 2 * n8)
+          myq = nth_row(wmask, tid >> 1) + ((tid & 1) ? 64 : 0);
+        else if (tid - 2 * n8 < count - n8)
+          myq = nth_row(~wmask & ((1u << count) - 1u), tid - 2 * n8);
+        s_quad[tid] = myq;
       }
       __syncthreads();
 
