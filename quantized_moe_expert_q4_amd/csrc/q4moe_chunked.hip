@@ -240,8 +240,9 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     }
     s_ppre[lane] = incl - c;
     s_cpre[lane] = cincl - cw;
+    const bool anybig = __any(big);                // (a vote of every lane of the wave)
     if (lane == 63) {
-      s_ppre[64] = __any(big) ? -1 : incl;
+      s_ppre[64] = anybig ? -1 : incl;
       s_cpre[64] = cincl;
     }
   }

@@ -96,6 +96,23 @@ def test_chunked_skewed_routing_invalid_and_duplicate_ids():
     check_parity(out, g, u, gr, ur, orf, "chunked skewed routing")
 
 
+def test_chunked_slot_with_more_passes_than_counted():
+    """1800 of 2400 pairs on one slot (more than 255 passes of 7): the pass
+    counts are turned off, every slot takes one pass and the hot slot's pairs
+    run in 258 token groups over its tiles."""
+    E, H, I, M, K = 400, 256, 16, 300, 8
+    rng = np.random.default_rng(1800)
+    lay, slots = _pool(rng, E, H, I)
+    x = synth.bf16_normal(rng, (M, H))
+    ids = rng.integers(1, E, size=(M, K)).astype(np.int32)
+    ids[:, :6] = 0
+    say(f"[chunked hot slot E={E} H={H} I={I} M={M} K={K}]")
+    (out, g, u), invalid = run_grouped(slots, lay, x, ids, H, I)
+    gr, ur, orf, bad = oracle.expert_gate_up_grouped(slots, lay.slot_bytes, E, lay, x, ids, H, I)
+    assert invalid == bad == 0
+    check_parity(out, g, u, gr, ur, orf, "chunked slot with more passes than counted")
+
+
 def test_chunked_invalid_ids_before_and_past_the_id_registers():
     """Invalid ids among the first 2048 pairs (marked at the start from the ids
     held in registers) and past them (read again at the end): 2400 pairs of
