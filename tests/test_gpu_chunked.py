@@ -113,6 +113,56 @@ def test_chunked_slot_with_more_passes_than_counted():
     check_parity(out, g, u, gr, ur, orf, "chunked slot with more passes than counted")
 
 
+@pytest.mark.parametrize("hot", [1785, 1786])
+def test_chunked_pass_count_limit(hot):
+    """A slot with 1785 pairs (255 passes of 7, the most one byte of the pass
+    table holds: counted) or 1786 (256 passes: the counts are turned off)."""
+    E, H, I, M, K = 300, 256, 16, 300, 6
+    rng = np.random.default_rng(hot)
+    lay, slots = _pool(rng, E, H, I)
+    x = synth.bf16_normal(rng, (M, H))
+    ids = rng.integers(1, E, size=(M, K)).astype(np.int32)
+    flat = ids.reshape(-1)
+    flat[:hot] = 0
+    say(f"[chunked pass count limit: {hot} pairs on one slot]")
+    (out, g, u), invalid = run_grouped(slots, lay, x, ids, H, I)
+    gr, ur, orf, bad = oracle.expert_gate_up_grouped(slots, lay.slot_bytes, E, lay, x, ids, H, I)
+    assert invalid == bad == 0
+    check_parity(out, g, u, gr, ur, orf, f"chunked pass count limit {hot}")
+
+
+@pytest.mark.parametrize("E", [2048, 2049])
+def test_chunked_slot_count_limit(E):
+    """Sparse routing over 2048 slots (the most the pass table covers) and over
+    2049 (one pass per slot, no counts)."""
+    H, I, M, K = 256, 16, 40, 8
+    rng = np.random.default_rng(E)
+    lay, slots = _pool(rng, E, H, I)
+    x = synth.bf16_normal(rng, (M, H))
+    ids = synth.top_k_routing(rng, M, K, E)
+    ids[0, 0] = E - 1
+    say(f"[chunked slot count limit E={E}]")
+    (out, g, u), invalid = run_grouped(slots, lay, x, ids, H, I)
+    gr, ur, orf, bad = oracle.expert_gate_up_grouped(slots, lay.slot_bytes, E, lay, x, ids, H, I)
+    assert invalid == bad == 0
+    check_parity(out, g, u, gr, ur, orf, f"chunked slot count limit E={E}")
+
+
+def test_chunked_all_ids_invalid():
+    """Every id out of range: no slot is streamed, every pair is zero and counted."""
+    E, H, I, M, K = 16, 512, 48, 20, 4
+    rng = np.random.default_rng(404)
+    lay, slots = _pool(rng, E, H, I)
+    x = synth.bf16_normal(rng, (M, H))
+    ids = np.where(rng.random((M, K)) < 0.5, -1 - rng.integers(0, 5, (M, K)), E + rng.integers(0, 5, (M, K)))
+    ids = ids.astype(np.int32)
+    say(f"[chunked all ids invalid E={E} M={M} K={K}]")
+    (out, g, u), invalid = run_grouped(slots, lay, x, ids, H, I)
+    gr, ur, orf, bad = oracle.expert_gate_up_grouped(slots, lay.slot_bytes, E, lay, x, ids, H, I)
+    assert invalid == bad == M * K
+    check_parity(out, g, u, gr, ur, orf, "chunked all ids invalid")
+
+
 def test_chunked_invalid_ids_before_and_past_the_id_registers():
     """Invalid ids among the first 2048 pairs (marked at the start from the ids
     held in registers) and past them (read again at the end): 2400 pairs of
