@@ -80,7 +80,11 @@ def _tokens(rng, M, H, wide, xdtype):
 # (H, I, M, wide): resident kernel with one and two column tiles, four and six
 # digits, and the batch kernel
 CASES = [(256, 72, 1, False), (2048, 72, 2, True), (1024, 96, 8, False), (4096, 80, 8, True),
-         (264, 100, 16, False), (512, 64, 24, True)]
+         (264, 100, 16, False), (512, 64, 24, True),
+         # digits beyond the resident kernel's LDS: the chunked kernel (q4/bf16); the
+         # six-digit token (the last) is not the 2^90 one (token 2), whose entries
+         # all lie within 38 binades of its largest
+         (12288, 80, 4, True), (12288, 80, 5, False)]
 
 
 @pytest.mark.parametrize("H,I,M,wide", CASES)
@@ -115,7 +119,8 @@ def test_gate_up_scales(H, I, M, wide, fmt, xdtype):
     assert np.any(np.asarray(gr).view(np.uint32) == 0x80000000), label
 
 
-DOWN_CASES = [(256, 128, 1, False), (520, 264, 3, True), (128, 1024, 8, False), (264, 512, 17, True)]
+DOWN_CASES = [(256, 128, 1, False), (520, 264, 3, True), (128, 1024, 8, False), (264, 512, 17, True),
+              (72, 16384, 5, True)]    # a reduction beyond the resident kernel's LDS: the chunked kernel
 
 
 @pytest.mark.parametrize("H,I,M,wide", DOWN_CASES)
