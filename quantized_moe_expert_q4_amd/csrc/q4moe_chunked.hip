@@ -12,11 +12,13 @@
 // non-temporal hint and moved to the operand layout by a lane shuffle, D steps
 // in flight per wave in a register ring that takes each step one step ahead.
 // What differs is where the activation digits come from:
-//  * One persistent 8-wave work-group per CU takes an even share of the
-//    (slot, pass, tile) units: a slot with c routed pairs takes ceil(c/G)
-//    passes over its tiles (G = 7 pairs at two column tiles, 4 at one).  It walks its share in segments (one
-//    pass over at most kChSegTiles tiles of one slot), each in token groups:
-//    as many of the pass's pairs as fit 16*NT digit columns, four per row or
+//  * One persistent 8-wave work-group per CU takes an even share of the cost
+//    of the (slot, pass, tile) units: a slot with c routed pairs takes
+//    ceil(c/G) passes over its tiles (G = 7 pairs at two column tiles, 4 at
+//    one); a tile counts for more in a pass of more pairs, and each pass adds
+//    a segment set-up.  A work-group walks its share in segments (one pass
+//    over at most kChSegTiles tiles of one slot), each in token groups: as
+//    many of the pass's pairs as fit 16*NT digit columns, four per row or
 //    eight for a row whose values need six digits.
 //  * A group's digits are split from x into LDS per K-chunk, double buffered
 //    (once for the whole K when it fits both buffers).
@@ -30,10 +32,10 @@
 //    collects their exact quad sums in an LDS fix-up slot (LDS atomics); the
 //    last contributor finishes it.
 //  * The digits of element k+1 are staged while element k is multiplied: a
-//    wave's share is cut into one 32-byte piece of x per lane per pass of the
-//    step loop, loaded at a pass's last step and split into LDS one pass
-//    later, so the waits for x never cover the weight loads in flight.  One
-//    barrier per element.
+//    wave's share is cut into quads (32 values of one row, 64 bytes of x) at
+//    one per lane per pass of the step loop, loaded at a pass's last step and
+//    split into whole 16-byte LDS chunks one pass later, so the waits for x
+//    never cover the weight loads in flight.  One barrier per element.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -129,7 +131,7 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   const int H = a.H, I = a.I, K = a.K;
   const int P = a.M * K;
   const bool grouped = a.ids != nullptr;
-  const int S = a.steps;                     // wide K-steps per tile, a multiple of 4
+  const int S = a.steps;                     // wide K-steps per tile, a multiple of kChU
   const int Sc = WHOLE ? S : ch_chunk_steps(NT, S);
   const int nch = WHOLE ? 1 : (S + Sc - 1) / Sc;
   const int tps = (I + RT - 1) / RT;         // tiles per slot
@@ -148,11 +150,12 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   for (int i = tid; i < kChFixSlots * ch_fix_words(NT); i += kChThreads) s_fix[i] = 0;
   // Work is cut by cost: a slot with c routed pairs takes ceil(c / G) passes
   // over its tiles (pass g: its pairs g*G .. g*G + G - 1 in id order), and
-  // the (slot, pass, tile) units are split evenly over the work-groups, so a
-  // slot that many tokens chose spreads over more work-groups instead of
-  // lengthening the launch.  The passes are held for up to kChCntSlots slots,
-  // fewer than 65536 pairs and at most 255 passes a slot; otherwise every
-  // slot takes one pass, its pairs in as many groups as they need.
+  // the cost of the (slot, pass, tile) units is split evenly over the
+  // work-groups, so a slot that many tokens chose spreads over more
+  // work-groups instead of lengthening the launch.  The passes are held for
+  // up to kChCntSlots slots, fewer than 65536 pairs and at most 255 passes a
+  // slot; otherwise every slot takes one pass, its pairs in as many groups as
+  // they need.
   // The ids of the first kChIdRegs * kChThreads pairs stay in registers for
   // the group scans.
   const __amdgpu_buffer_rsrc_t idsrc = make_rsrc(a.ids, grouped ? (uint32_t)P * 4u : 0u);
