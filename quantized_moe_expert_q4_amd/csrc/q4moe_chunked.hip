@@ -192,7 +192,7 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         ++inv;
       }
     }
-    if (blockIdx.x == 0 && inv) atomicAdd(&s_inv, inv);
+    if (inv) atomicAdd(&s_inv, inv);               // every work-group: the call's invalid ids
   }
   __syncthreads();
   auto passes = [&](int c) { return (c + G - 1) / G; };
@@ -941,8 +941,9 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     }
   }
 
-  // ---- pairs with invalid ids get zero outputs: pairs b, b + NB, ... here ----
-  if (grouped) {
+  // ---- pairs with invalid ids get zero outputs: pairs b, b + NB, ... here
+  // (skipped, with its barriers and id reloads, when the call has none) ----
+  if (grouped && s_inv > 0) {
     const int nmine = P > (int)blockIdx.x ? (P - (int)blockIdx.x + NB - 1) / NB : 0;
     for (int base = 0; base < nmine; base += kChThreads) {
       __syncthreads();

@@ -398,7 +398,7 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
     for (int j = 0; j < kResIdRegs; ++j)
       if (tid + j * kResThreads < P) post(idr[j]);
     for (int p = tid + kResIdRegs * kResThreads; p < P; p += kResThreads) post(a.ids[p]);
-    if (blockIdx.x == 0 && blockIdx.y == 0 && inv) atomicAdd(&s_inv, inv);
+    if (inv) atomicAdd(&s_inv, inv);                 // every work-group: the call's invalid ids
     __syncthreads();
     if (compact) {
       wbits = lane < nw ? s_bits[lane] : 0u;
@@ -1111,8 +1111,9 @@ __global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2, 
 
   }
 
-  // ---- pairs with invalid ids get zero outputs: pairs b, b + NB, ... here ----
-  if (grouped && pass == 0) {
+  // ---- pairs with invalid ids get zero outputs: pairs b, b + NB, ... here
+  // (skipped, with its barriers and id reloads, when the call has none) ----
+  if (grouped && pass == 0 && s_inv > 0) {
     const int nmine = P > (int)blockIdx.x ? (P - (int)blockIdx.x + NB - 1) / NB : 0;
     for (int base = 0; base < nmine; base += kResThreads) {
       __syncthreads();

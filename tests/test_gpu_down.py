@@ -16,7 +16,7 @@ import oracle
 import synth
 import quantized_moe_expert_q4_amd as q4
 from quantized_moe_expert_q4_amd.device import aligned_empty, bf16_bits, upload_bf16_bits, upload_slots
-from tests.gpu_helpers import check_down_parity, run_down_grouped, run_down_single, say
+from tests.gpu_helpers import check_down_parity, poisoned, run_down_grouped, run_down_single, say
 
 pytestmark = pytest.mark.gpu
 
@@ -62,8 +62,8 @@ def _forward(c):
     M = c.x.shape[0]
     slot = upload_slots(c.slots[:1])
     x = upload_bf16_bits(c.x)
-    mid = torch.empty((M, c.I), dtype=torch.bfloat16, device="cuda")
-    out = torch.empty((M, c.H), dtype=torch.bfloat16, device="cuda")
+    mid = poisoned((M, c.I), torch.bfloat16)
+    out = poisoned((M, c.H), torch.bfloat16)
     q4.expert_forward(slot, c.layout, x, M, c.H, c.I, mid, out)
     torch.cuda.synchronize()
     return bf16_bits(mid), bf16_bits(out)
@@ -104,8 +104,8 @@ def _forward_grouped(c, slots=None):
         slots = upload_slots(c.slots)
     x = upload_bf16_bits(c.x)
     idt = torch.from_numpy(np.ascontiguousarray(c.ids, dtype=np.int32)).cuda()
-    mid = torch.empty((M, K, c.I), dtype=torch.bfloat16, device="cuda")
-    out = torch.empty((M, K, c.H), dtype=torch.bfloat16, device="cuda")
+    mid = poisoned((M, K, c.I), torch.bfloat16)
+    out = poisoned((M, K, c.H), torch.bfloat16)
     wsb = q4.grouped_workspace_bytes(M, K, c.num_slots)
     ws = aligned_empty(wsb, 256)
     q4.expert_forward_grouped(slots, c.slot_stride, c.num_slots, c.layout, x, M, idt, K, c.H, c.I, mid, out, ws,

@@ -15,7 +15,7 @@ import oracle
 import synth
 import quantized_moe_expert_q4_amd as q4
 from quantized_moe_expert_q4_amd.device import aligned_empty, upload_slots
-from tests.gpu_helpers import say
+from tests.gpu_helpers import poisoned, say
 
 pytestmark = pytest.mark.gpu
 
@@ -42,9 +42,9 @@ def _dev(x):
 def _single(slot_np, lay, x, H, I, fmt="q4", label=""):
     M = x.shape[0]
     slot = upload_slots(slot_np.reshape(1, -1))
-    out = torch.empty((M, I), dtype=torch.float32, device="cuda")
-    g = torch.empty((M, I), dtype=torch.float32, device="cuda")
-    u = torch.empty((M, I), dtype=torch.float32, device="cuda")
+    out = poisoned((M, I), torch.float32)
+    g = poisoned((M, I), torch.float32)
+    u = poisoned((M, I), torch.float32)
     q4.expert_gate_up(slot, lay, _dev(x), M, H, I, out, g, u, fmt=fmt, xdtype="f32")
     torch.cuda.synchronize()
     o, g, u = out.cpu().numpy(), g.cpu().numpy(), u.cpu().numpy()
@@ -114,9 +114,9 @@ def test_f32_grouped_edges():
     M, K = ids.shape
     slots = upload_slots(c.slots)
     idt = torch.from_numpy(ids).cuda()
-    out = torch.empty((M, K, c.I), dtype=torch.float32, device="cuda")
-    g = torch.empty((M, K, c.I), dtype=torch.float32, device="cuda")
-    u = torch.empty((M, K, c.I), dtype=torch.float32, device="cuda")
+    out = poisoned((M, K, c.I), torch.float32)
+    g = poisoned((M, K, c.I), torch.float32)
+    u = poisoned((M, K, c.I), torch.float32)
     wsb = q4.grouped_workspace_bytes(M, K, c.num_slots)
     ws = aligned_empty(wsb, 256)
     q4.expert_gate_up_grouped(slots, c.slot_stride, c.num_slots, c.layout, _dev(x), M, idt, K, c.H, c.I, out, ws,
@@ -137,12 +137,12 @@ def test_f32_down_and_whole_expert(fmt):
         slot_np = synth.fill_slot(rng, H, I, lay, fmt=fmt)
         slot = upload_slots(slot_np.reshape(1, -1))
         mid = synth.f32_normal(rng, (M, I))
-        out = torch.empty((M, H), dtype=torch.float32, device="cuda")
-        d = torch.empty((M, H), dtype=torch.float32, device="cuda")
+        out = poisoned((M, H), torch.float32)
+        d = poisoned((M, H), torch.float32)
         q4.expert_down(slot, lay, _dev(mid), M, H, I, out, d, fmt=fmt, xdtype="f32")
         x = synth.f32_normal(rng, (M, H))
-        midg = torch.empty((M, I), dtype=torch.float32, device="cuda")
-        outg = torch.empty((M, H), dtype=torch.float32, device="cuda")
+        midg = poisoned((M, I), torch.float32)
+        outg = poisoned((M, H), torch.float32)
         q4.expert_forward(slot, lay, _dev(x), M, H, I, midg, outg, fmt=fmt, xdtype="f32")
         torch.cuda.synchronize()
         d_ref, o_ref = oracle.expert_down(slot_np, lay, mid, H, I, fmt=fmt, xdtype="f32")
@@ -159,8 +159,8 @@ def test_f32_forward_grouped():
     M, K = c.ids.shape
     slots = upload_slots(c.slots)
     idt = torch.from_numpy(np.ascontiguousarray(c.ids, np.int32)).cuda()
-    mid = torch.empty((M, K, c.I), dtype=torch.float32, device="cuda")
-    out = torch.empty((M, K, c.H), dtype=torch.float32, device="cuda")
+    mid = poisoned((M, K, c.I), torch.float32)
+    out = poisoned((M, K, c.H), torch.float32)
     wsb = q4.grouped_workspace_bytes(M, K, c.num_slots)
     ws = aligned_empty(wsb, 256)
     q4.expert_forward_grouped(slots, c.slot_stride, c.num_slots, c.layout, _dev(x), M, idt, K, c.H, c.I, mid, out,

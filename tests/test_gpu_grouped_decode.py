@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_helpers import check_parity, run_grouped, say
+from tests.gpu_helpers import check_parity, poisoned, run_grouped, say
 
 pytestmark = pytest.mark.gpu
 
@@ -55,9 +55,9 @@ def test_benchmark_pool_full_size(M):
     x = x8[:M]
     ids = np.tile(np.arange(E, dtype=np.int32), (M, 1))
     say(f"[benchmark pool M={M}] {E} slots H={H} I={I}")
-    out = torch.empty((M, E, I), dtype=torch.bfloat16, device="cuda")
-    g = torch.empty((M, E, I), dtype=torch.float32, device="cuda")
-    u = torch.empty((M, E, I), dtype=torch.float32, device="cuda")
+    out = poisoned((M, E, I), torch.bfloat16)
+    g = poisoned((M, E, I), torch.float32)
+    u = poisoned((M, E, I), torch.float32)
     wsb = q4.grouped_workspace_bytes(M, E, E)
     ws = aligned_empty(wsb, 256)
     ws.fill_(0xAB)

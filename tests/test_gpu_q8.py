@@ -12,7 +12,7 @@ import oracle
 import synth
 import quantized_moe_expert_q4_amd as q4
 from quantized_moe_expert_q4_amd.device import aligned_empty, bf16_bits, upload_bf16_bits, upload_slots
-from tests.gpu_helpers import (check_down_parity, check_parity, run_down_grouped, run_down_single, run_grouped,
+from tests.gpu_helpers import (check_down_parity, check_parity, poisoned, run_down_grouped, run_down_single, run_grouped,
                                run_single, say)
 
 pytestmark = pytest.mark.gpu
@@ -96,8 +96,8 @@ def test_q8_forward_grouped(M, K, E):
     slots = upload_slots(c.slots)
     x = upload_bf16_bits(c.x)
     idt = torch.from_numpy(np.ascontiguousarray(c.ids, dtype=np.int32)).cuda()
-    mid = torch.empty((Mk, Kk, c.I), dtype=torch.bfloat16, device="cuda")
-    out = torch.empty((Mk, Kk, c.H), dtype=torch.bfloat16, device="cuda")
+    mid = poisoned((Mk, Kk, c.I), torch.bfloat16)
+    out = poisoned((Mk, Kk, c.H), torch.bfloat16)
     wsb = q4.grouped_workspace_bytes(Mk, Kk, c.num_slots)
     ws = aligned_empty(wsb, 256)
     q4.expert_forward_grouped(slots, c.slot_stride, c.num_slots, c.layout, x, Mk, idt, Kk, c.H, c.I, mid, out, ws,
@@ -115,8 +115,8 @@ def test_q8_forward_single_and_down_grouped():
     say("[q8 forward cfg3]")
     slot = upload_slots(c.slots[:1])
     x = upload_bf16_bits(c.x)
-    mid = torch.empty((8, c.I), dtype=torch.bfloat16, device="cuda")
-    out = torch.empty((8, c.H), dtype=torch.bfloat16, device="cuda")
+    mid = poisoned((8, c.I), torch.bfloat16)
+    out = poisoned((8, c.H), torch.bfloat16)
     q4.expert_forward(slot, c.layout, x, 8, c.H, c.I, mid, out, fmt="q8")
     torch.cuda.synchronize()
     mid_ref, out_ref = oracle.expert_forward(c.slots[0], c.layout, c.x, c.H, c.I, fmt="q8")

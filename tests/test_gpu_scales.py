@@ -19,7 +19,7 @@ import oracle
 import synth
 import quantized_moe_expert_q4_amd as q4
 from quantized_moe_expert_q4_amd.device import upload_slots
-from tests.gpu_helpers import run_down_single, run_single, say
+from tests.gpu_helpers import poisoned, run_down_single, run_single, say
 
 pytestmark = pytest.mark.gpu
 
@@ -105,9 +105,9 @@ def test_gate_up_scales(H, I, M, wide, fmt, xdtype):
     else:
         dev = upload_slots(slot.reshape(1, -1))
         xt = torch.from_numpy(np.ascontiguousarray(x, np.float32)).cuda()
-        o = torch.empty((M, I), dtype=torch.float32, device="cuda")
-        gt = torch.empty((M, I), dtype=torch.float32, device="cuda")
-        ut = torch.empty((M, I), dtype=torch.float32, device="cuda")
+        o = poisoned((M, I), torch.float32)
+        gt = poisoned((M, I), torch.float32)
+        ut = poisoned((M, I), torch.float32)
         q4.expert_gate_up(dev, lay, xt, M, H, I, o, gt, ut, fmt=fmt, xdtype="f32")
         torch.cuda.synchronize()
         out, g, u = o.cpu().numpy(), gt.cpu().numpy(), ut.cpu().numpy()
@@ -140,8 +140,8 @@ def test_down_scales(H, I, M, wide, xdtype):
     else:
         dev = upload_slots(slot.reshape(1, -1))
         mt = torch.from_numpy(np.ascontiguousarray(mid, np.float32)).cuda()
-        o = torch.empty((M, H), dtype=torch.float32, device="cuda")
-        dt = torch.empty((M, H), dtype=torch.float32, device="cuda")
+        o = poisoned((M, H), torch.float32)
+        dt = poisoned((M, H), torch.float32)
         q4.expert_down(dev, lay, mt, M, H, I, o, dt, xdtype="f32")
         torch.cuda.synchronize()
         out, d = o.cpu().numpy(), dt.cpu().numpy()
