@@ -32,14 +32,16 @@
 //    collects their exact quad sums in an LDS fix-up slot (LDS atomics); the
 //    last contributor finishes it.
 //  * The digits of element k+1 are staged while element k is multiplied: a
-//    wave's share is cut into quads (32 values of one row, 64 bytes of x) at
-//    one per lane per pass of the step loop, loaded at a pass's last step and
-//    split into whole 16-byte LDS chunks one pass later, so the waits for x
-//    never cover the weight loads in flight.  One barrier per element.
+//    wave's share is cut into quads (32 values of one row, 64 bytes of x),
+//    or half quads when there are too few quads for every lane, at one per
+//    lane per pass of the step loop, loaded at a pass's last step and split
+//    into LDS chunks one pass later, so the waits for x never cover the
+//    weight loads in flight.  One barrier per element.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "q4moe_device.h"
 #include "q4moe_launch.h"
@@ -387,11 +389,22 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   // store per (column, plane), at fixed offsets from the row's first chunk
   // (columns col0 .. col0 + 3 of a four-column row lie in one 4-aligned
   // group, which the k-group's swizzle keeps together; an eight-column row
-  // has two such groups).
-  auto stage_quad = [&](uint8_t* buf, int W, int col0, int st, int qg, const uint4 (&xq)[4], int etop1) {
+  // has two such groups).  A piece of NWD = 2 words is half h of a quad
+  // (words 2h, 2h + 1): the same stores, 8 bytes each, at byte 8h of every
+  // chunk.
+  auto stage_piece = [&](auto nwd, uint8_t* buf, int W, int col0, int st, int qg, int h, const uint4 (&xq)[4],
+                         int etop1) {
+    constexpr int NWD = decltype(nwd)::value;
     const int gg = qg >> 1, q = qg & 1;
     const int bp = (col0 & 15) ^ (4 * gg);           // chunk position of column col0
-    uint8_t* const b0 = buf + st * sbytes + (2 * q * NT + (col0 >> 4)) * 1024 + gg * 256 + bp * 16;
+    uint8_t* const b0 = buf + st * sbytes + (2 * q * NT + (col0 >> 4)) * 1024 + gg * 256 + bp * 16 + 8 * h;
+    // one piece's digit sd of every word: a 16-byte (or 8-byte) store
+    auto put = [&](uint8_t* at, uint32_t d0, uint32_t d1, uint32_t d2, uint32_t d3) {
+      if constexpr (NWD == 4)
+        *(uint4*)at = make_uint4(d0, d1, d2, d3);
+      else
+        *(uint2*)at = make_uint2(d0, d1);
+    };
     auto vals = [&](const uint4 w, int par, uint32_t (&xs)[4]) {
       const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -400,9 +413,9 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     if (W == 4) {
 #pragma unroll
       for (int par = 0; par < 2; ++par) {
-        uint32_t d[4][4];                              // [word][digit]
+        uint32_t d[4][4] = {};                         // [word][digit]
 #pragma unroll
-        for (int wj = 0; wj < 4; ++wj) {
+        for (int wj = 0; wj < NWD; ++wj) {
           uint32_t xs[4], v[4];
           vals(xq[wj], par, xs);
 #pragma unroll
@@ -410,8 +423,7 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
           transpose4(v[0], v[1], v[2], v[3], d[wj]);
         }
 #pragma unroll
-        for (int sd = 0; sd < 4; ++sd)
-          *(uint4*)(b0 + par * NT * 1024 + 16 * sd) = make_uint4(d[0][sd], d[1][sd], d[2][sd], d[3][sd]);
+        for (int sd = 0; sd < 4; ++sd) put(b0 + par * NT * 1024 + 16 * sd, d[0][sd], d[1][sd], d[2][sd], d[3][sd]);
       }
     } else {
       // six digits: columns [d0 d1 d2 0 d3 d4 d5 0], the second group of
@@ -419,9 +431,9 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
       uint8_t* const b1 = b0 + ((bp ^ 4) - bp) * 16;
 #pragma unroll
       for (int par = 0; par < 2; ++par) {
-        uint32_t dl[4][4], dh[4][4];
+        uint32_t dl[4][4] = {}, dh[4][4] = {};
 #pragma unroll
-        for (int wj = 0; wj < 4; ++wj) {
+        for (int wj = 0; wj < NWD; ++wj) {
           uint32_t xs[4], lo[4], hi[4];
           vals(xq[wj], par, xs);
 #pragma unroll
@@ -436,13 +448,12 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         uint8_t* const p0 = b0 + par * NT * 1024;
         uint8_t* const p1 = b1 + par * NT * 1024;
 #pragma unroll
-        for (int sd = 0; sd < 3; ++sd) *(uint4*)(p0 + 16 * sd) = make_uint4(dl[0][sd], dl[1][sd], dl[2][sd], dl[3][sd]);
-        *(uint4*)(p0 + 48) = make_uint4(0, 0, 0, 0);
-        *(uint4*)(p1) = make_uint4(dl[0][3], dl[1][3], dl[2][3], dl[3][3]);
+        for (int sd = 0; sd < 3; ++sd) put(p0 + 16 * sd, dl[0][sd], dl[1][sd], dl[2][sd], dl[3][sd]);
+        put(p0 + 48, 0, 0, 0, 0);
+        put(p1, dl[0][3], dl[1][3], dl[2][3], dl[3][3]);
 #pragma unroll
-        for (int sd = 0; sd < 2; ++sd)
-          *(uint4*)(p1 + 16 + 16 * sd) = make_uint4(dh[0][sd], dh[1][sd], dh[2][sd], dh[3][sd]);
-        *(uint4*)(p1 + 48) = make_uint4(0, 0, 0, 0);
+        for (int sd = 0; sd < 2; ++sd) put(p1 + 16 + 16 * sd, dh[0][sd], dh[1][sd], dh[2][sd], dh[3][sd]);
+        put(p1 + 48, 0, 0, 0, 0);
       }
     }
   };
@@ -687,34 +698,45 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
       }
       __syncthreads();
 
-      // Quad xs of chunk c: quads in row-major order (xs = tl * nq + r for
-      // nq quads per row in the chunk, r = 8 st + qg), so that a wave's
-      // quads mostly share a row (and its digit width); at K index k0 of the
-      // row.  Words past the row's end (padding steps) are loaded from its
+      // Piece xs of chunk c: pieces in row-major order (xs = tl * np + p for
+      // np pieces per row in the chunk), so that a wave's pieces mostly share
+      // a row (and its digit width).  A piece is a quad (hs = 0: p = r = 8 st
+      // + qg) or, when a chunk has too few quads for every lane of the work-
+      // group, half a quad (hs = 1: p = 2 r + h), which halves each lane's
+      // split.  Words past the row's end (padding steps) are loaded from its
       // start and replaced by zeros when they are split, not here (a write to
       // the loads' registers would have to wait for them at once).
-      auto quad_k = [&](int c, int r) { return c * Sc * 256 + 32 * r; };
-      auto load_quad = [&](int c, int r, int tl, uint4 (&xq)[4]) {
-        const int k0 = quad_k(c, r);
+      auto piece_k = [&](int c, int p, int hs) { return c * Sc * 256 + (p << (5 - hs)); };
+      auto load_piece = [&](int c, int p, int hs, int tl, uint4 (&xq)[4]) {
+        const int k0 = piece_k(c, p, hs);
         const uint16_t* row = a.x + (uint64_t)s_tok[tl] * H;
 #pragma unroll
-        for (int wj = 0; wj < 4; ++wj) xq[wj] = *(const uint4*)(row + (k0 + 8 * wj < H ? k0 + 8 * wj : 0));
+        for (int wj = 0; wj < 4; ++wj)
+          if (wj < (4 >> hs)) xq[wj] = *(const uint4*)(row + (k0 + 8 * wj < H ? k0 + 8 * wj : 0));
       };
-      auto put_quad = [&](uint8_t* buf, int c, int r, int tl, uint4 (&xq)[4]) {
-        const int k0 = quad_k(c, r);
+      auto put_piece = [&](uint8_t* buf, int c, int p, int hs, int tl, uint4 (&xq)[4]) {
+        const int k0 = piece_k(c, p, hs);
 #pragma unroll
         for (int wj = 0; wj < 4; ++wj)
           if (k0 + 8 * wj >= H) xq[wj] = make_uint4(0, 0, 0, 0);
-        stage_quad(buf, s_wid[tl], s_col[tl], r >> 3, r & 7, xq, max((s_xmax[tl] >> 7) & 0xFF, 1));
+        const int r = p >> hs, etop1 = max((s_xmax[tl] >> 7) & 0xFF, 1);
+        if (hs)
+          stage_piece(std::integral_constant<int, 2>(), buf, s_wid[tl], s_col[tl], r >> 3, r & 7, p & 1, xq, etop1);
+        else
+          stage_piece(std::integral_constant<int, 4>(), buf, s_wid[tl], s_col[tl], r >> 3, r & 7, 0, xq, etop1);
       };
+      // half-quad pieces when a chunk of nq quads per row has at most one
+      // quad for every two threads
+      auto piece_shift = [&](int nq) { return count * nq * 2 <= kChThreads ? 1 : 0; };
       // chunk 0 of the group, by every thread
       {
-        const int nq0 = min(Sc, S) * 8;
-        for (int xs = tid; xs < count * nq0; xs += kChThreads) {
-          const int tl = xs / nq0, r = xs - tl * nq0;
+        const int hs0 = piece_shift(min(Sc, S) * 8);
+        const int np0 = (min(Sc, S) * 8) << hs0;
+        for (int xs = tid; xs < count * np0; xs += kChThreads) {
+          const int tl = xs / np0, pc = xs - tl * np0;
           uint4 xq[4];
-          load_quad(0, r, tl, xq);
-          put_quad(s_dig, 0, r, tl, xq);
+          load_piece(0, pc, hs0, tl, xq);
+          put_piece(s_dig, 0, pc, hs0, tl, xq);
         }
       }
       __syncthreads();
@@ -874,13 +896,14 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
               }
           }
           const uint8_t* buf = s_dig + (k & 1) * kChBuf;
-          // this wave's share of element k+1's digits: quads [xs, xe) of
-          // chunk c1, one slice (64 quads, one per lane) per pass of the step
+          // this wave's share of element k+1's digits: pieces [xs, xe) of
+          // chunk c1, one slice (64 pieces, one per lane) per pass of the step
           // loop
           const bool stg = k + 1 < nr * nch;
           const int c1 = c + 1 == nch ? 0 : c + 1;
           uint8_t* sbuf = s_dig + ((k + 1) & 1) * kChBuf;
-          const int nq1 = min(Sc, S - c1 * Sc) * 8;   // quads per row in chunk c1
+          const int hs1 = piece_shift(min(Sc, S - c1 * Sc) * 8);
+          const int nq1 = (min(Sc, S - c1 * Sc) * 8) << hs1;  // pieces per row in chunk c1
           const int xpn = stg ? count * nq1 : 0;
           int xs = wave * xpn / kChWaves + lane;
           const int xe = (wave + 1) * xpn / kChWaves;
@@ -889,15 +912,15 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
           // has waited for every weight load issued before the x loads, so the
           // wait for x covers nothing still in flight for the ring.
           uint4 xq[4] = {};
-          int rp = 0, tlp = 0;                         // the pending slice's quad
+          int rp = 0, tlp = 0;                         // the pending slice's piece
           bool pend = false;
           auto slice = [&]() {
-            if (pend) put_quad(sbuf, c1, rp, tlp, xq);
+            if (pend) put_piece(sbuf, c1, rp, hs1, tlp, xq);
             pend = xs < xe;
             if (pend) {
               tlp = xs / nq1;
               rp = xs - tlp * nq1;
-              load_quad(c1, rp, tlp, xq);
+              load_piece(c1, rp, hs1, tlp, xq);
               xs += 64;
             }
           };
@@ -907,13 +930,13 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             const int pa = max(ua, tile * scc), pb = min(ub, (tile + 1) * scc);
             for (int u = pa; u < pb; u += kChU) steps(buf, u - tile * scc, accg[j], accu[j], slice);
           }
-          if (pend) put_quad(sbuf, c1, rp, tlp, xq);
+          if (pend) put_piece(sbuf, c1, rp, hs1, tlp, xq);
           // the rest of this wave's share (rounds too short for all its slices)
           while (xs < xe) {
             tlp = xs / nq1;
             rp = xs - tlp * nq1;
-            load_quad(c1, rp, tlp, xq);
-            put_quad(sbuf, c1, rp, tlp, xq);
+            load_piece(c1, rp, hs1, tlp, xq);
+            put_piece(sbuf, c1, rp, hs1, tlp, xq);
             xs += 64;
           }
           __syncthreads();  // element k's digits read, element k+1's staged
