@@ -182,14 +182,15 @@ def test_chunked_invalid_ids_before_and_past_the_id_registers():
     check_parity(out, g, u, gr, ur, orf, "chunked invalid ids before and past the id registers")
 
 
-@pytest.mark.parametrize("H,I,M,wide", [(7168, 512, 3, True), (16384, 64, 5, False), (12288, 48, 8, False)])
+@pytest.mark.parametrize("H,I,M,wide", [(7168, 512, 3, True), (16384, 64, 5, False), (12288, 48, 8, False),
+                                         (7168, 264, 8, "all")])
 def test_chunked_single_expert(H, I, M, wide):
     """Single-expert calls of up to eight tokens whose digits exceed the
-    resident kernel's LDS."""
+    resident kernel's LDS (eight six-digit tokens: two groups per pass)."""
     rng = np.random.default_rng(H + I + M)
     lay = synth.contiguous_layout(H, I)
     slot = synth.fill_slot(rng, H, I, lay)
-    x = _wide(synth.bf16_normal(rng, (M, H)), (0,) if wide else ())
+    x = _wide(synth.bf16_normal(rng, (M, H)), tuple(range(M)) if wide == "all" else ((0,) if wide else ()))
     say(f"[chunked single H={H} I={I} M={M} wide={wide}]")
     out, g, u = run_single(slot, lay, x, H, I)
     gr, ur, orf = oracle.expert_gate_up(slot, lay, x, H, I)
