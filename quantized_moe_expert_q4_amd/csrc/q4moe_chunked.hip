@@ -17,7 +17,8 @@
 //    ceil(c/G) passes over its tiles (G = 7 pairs at two column tiles, 4 at
 //    one); a tile counts for more in a pass of more pairs, and each pass adds
 //    a segment set-up.  A work-group walks its share in segments (one pass
-//    over at most kChSegTiles tiles of one slot), each in token groups: as
+//    over at most 48 tiles of one slot, 64 for a down projection whose K
+//    fits LDS), each in token groups: as
 //    many of the pass's pairs as fit 16*NT digit columns, four per row or
 //    eight for a row whose values need six digits.
 //  * A group's digits are split from x into LDS per K-chunk, double buffered
@@ -58,6 +59,7 @@ constexpr int kChD = 2;                    // K-steps in flight per wave
 constexpr int kChRoundTiles = 14;          // tiles per round
 constexpr int kChMaxT = 3;                 // tiles one wave meets in a round
 constexpr int kChSegTiles = 48;            // tiles per segment (row scales held in LDS)
+constexpr int kChSegTilesDown = 64;        // the same for the down projection with the whole K in LDS
 constexpr int kChFixSlots = kChWaves - 1;
 constexpr int kChCntSlots = 2048;          // slots whose passes are held in LDS
 constexpr int kChIdRegs = 4;               // routing ids held per thread (2048 pairs)
@@ -108,8 +110,11 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   __shared__ unsigned long long s_fix[kChFixSlots * ch_fix_words(NT)];
   __shared__ int s_fixcnt[kChFixSlots];
   __shared__ __attribute__((aligned(16))) uint16_t s_sig[DOWN ? 8 : kSigTable];
-  __shared__ float s_gsc[kChSegTiles * RT];   // row scales of the segment (DOWN: the down scales)
-  __shared__ float s_usc[DOWN ? 1 : kChSegTiles * RT];
+  // tiles per segment: a down projection whose K fits LDS has no rounds and
+  // one matrix of scales, and takes longer segments (fewer set-ups)
+  constexpr int SEGT = DOWN && WHOLE ? kChSegTilesDown : kChSegTiles;
+  __shared__ float s_gsc[SEGT * RT];          // row scales of the segment (DOWN: the down scales)
+  __shared__ float s_usc[DOWN ? 1 : SEGT * RT];
   __shared__ uint8_t s_pass[kChCntSlots];     // passes of each slot
   __shared__ int s_ppre[kChCntWords + 1];     // passes of the slots before each 32-slot word, and in all
   __shared__ long long s_cpre[kChCntWords + 1];  // cost of the slots before each word, and in all
@@ -458,12 +463,12 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     }
   };
 
-  // ---- segments: one pass over at most kChSegTiles tiles of one slot ----
+  // ---- segments: one pass over at most SEGT tiles of one slot ----
   int v = v0;
   while (v < v1) {
     const int pv = v / tps;                            // pass index
     const int t0 = v - pv * tps;
-    const int t1 = min(min(v1 - pv * tps, tps), t0 + kChSegTiles);
+    const int t1 = min(min(v1 - pv * tps, tps), t0 + SEGT);
     v = pv * tps + t1;
     int e, g;
     decode(pv, e, g);
@@ -488,7 +493,7 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     // kChRoundTiles tiles whose sums stay in registers from chunk to chunk.
     const int nr = WHOLE ? 1 : (nseg + kChRoundTiles - 1) / kChRoundTiles;
     // first tile of round r (in the slot): rounds of near-equal size
-    static_assert(kChSegTiles <= 4 * kChRoundTiles, "at most four rounds per segment");
+    static_assert(WHOLE || SEGT <= 4 * kChRoundTiles, "at most four rounds per segment");
     auto round_at = [&](int r) {
       const int q = r * nseg;
       return t0 + (nr == 1 ? q : nr == 2 ? q >> 1 : nr == 3 ? q / 3 : q >> 2);

@@ -197,10 +197,13 @@ def test_chunked_single_expert(H, I, M, wide):
     check_parity(out, g, u, gr, ur, orf, f"chunked single H={H} I={I} M={M}")
 
 
-@pytest.mark.parametrize("E,H,I,wide", [(20, 4096, 1536, False), (12, 520, 2048, True), (40, 264, 8192, False)])
+@pytest.mark.parametrize("E,H,I,wide", [(20, 4096, 1536, False), (12, 520, 2048, True), (40, 264, 8192, False),
+                                        (120, 4096, 64, True)])
 def test_chunked_down_grouped(E, H, I, wide):
     """The grouped down projection with one routed row per slot (the down
-    step of one token routed to E experts): H output rows, I inputs."""
+    step of one token routed to E experts): H output rows, I inputs.  The
+    last case gives each work-group about 60 tiles: segments longer than
+    the 48 tiles of gate/up calls."""
     rng = np.random.default_rng(E + H + I)
     lay, slots = _pool(rng, E, H, I, down=True)
     ids = np.arange(E, dtype=np.int32).reshape(1, E)
