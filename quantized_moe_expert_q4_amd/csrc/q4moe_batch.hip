@@ -40,6 +40,7 @@ constexpr int kBatBuf = 72 * 1024;        // one of two digit buffers
 constexpr int kEpStride = 52;             // int32 row stride of a wave's 16 x C epilogue matrix
 constexpr int kBatBitSlots = 2048;        // slots a routing bitmap covers
 constexpr int kBatBitWords = kBatBitSlots / 32;
+constexpr int kBatInvBatch = 64;          // invalid pairs zero-filled per batch
 
 static_assert(kBatWaves * 16 * kEpStride * 4 <= kBatBuf, "epilogue matrices fit one digit buffer");
 
@@ -79,6 +80,8 @@ void batch_kernel(const GateUpParams a) {
   __shared__ int s_xmin[G];                  // smallest non-zero exponent field of each token
   __shared__ int s_wcnt[kBatWaves];
   __shared__ int s_invalid;
+  __shared__ int s_ninv;
+  __shared__ int s_invl[kBatInvBatch];
   __shared__ uint32_t s_bits[kBatBitWords];  // routed slots
   __shared__ int s_bpre[kBatBitWords + 1];   // routed slots before each word, and in all
   __shared__ __attribute__((aligned(16))) uint16_t s_sig[kSigTable];  // bf16 sigmoid of the tabulated gT
@@ -102,27 +105,36 @@ void batch_kernel(const GateUpParams a) {
   if constexpr (!DOWN)
     if (tid < kSigTable / 8) *(uint4*)(s_sig + 8 * tid) = ((const uint4*)a.sig)[tid];
 
-  // ---- invalid routing ids (grouped): zero-filled by work-group 0 ----
+  // ---- invalid routing ids (grouped): counted and zero-filled by work-group
+  // 0, a batch of them at a time with every thread on a row range ----
   if (grouped && blockIdx.x == 0) {
+    auto zero = [&](uint64_t o) {
+      if (xf)
+        ((float*)a.out)[o] = 0.0f;
+      else
+        a.out[o] = 0;
+      if (a.gate_probe) a.gate_probe[o] = 0.0f;
+      if (a.up_probe) a.up_probe[o] = 0.0f;
+    };
     if (tid == 0) s_invalid = 0;
-    __syncthreads();
-    int cnt = 0;
-    for (int p = tid; p < P; p += kBatThreads) {
-      const int e = a.ids[p];
-      if (e < 0 || e >= a.num_slots) {
-        ++cnt;
-        for (int r = 0; r < I; ++r) {
-          const uint64_t o = (uint64_t)p * I + r;
-          if (xf)
-            ((float*)a.out)[o] = 0.0f;
-          else
-            a.out[o] = 0;
-          if (a.gate_probe) a.gate_probe[o] = 0.0f;
-          if (a.up_probe) a.up_probe[o] = 0.0f;
-        }
-      }
+    for (int base = 0; base < P; base += kBatThreads) {
+      __syncthreads();
+      if (tid == 0) s_ninv = 0;
+      __syncthreads();
+      const int p = base + tid;
+      const bool bad = p < P && (a.ids[p] < 0 || a.ids[p] >= a.num_slots);
+      int at = -1;
+      if (bad) at = atomicAdd(&s_ninv, 1);
+      if (bad && at < kBatInvBatch) s_invl[at] = p;
+      __syncthreads();
+      const int nl = min(s_ninv, kBatInvBatch);
+      if (tid == 0) s_invalid += s_ninv;
+      for (int q = 0; q < nl; ++q)
+        for (int r = tid; r < I; r += kBatThreads) zero((uint64_t)s_invl[q] * I + r);
+      // past the batch: each finder fills its own pair
+      if (bad && at >= kBatInvBatch)
+        for (int r = 0; r < I; ++r) zero((uint64_t)p * I + r);
     }
-    if (cnt) atomicAdd(&s_invalid, cnt);
     __syncthreads();
     if (tid == 0 && a.invalid_count) *a.invalid_count = s_invalid;
   }

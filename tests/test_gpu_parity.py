@@ -132,6 +132,27 @@ def test_grouped_edge_cases():
     check_parity(out, g, u, gr, ur, orf, "grouped edge cases")
 
 
+def test_grouped_many_invalid_ids_batch_kernel():
+    """Hundreds of invalid ids on one work-group of the batch kernel (two
+    slots of one 16-row tile each: two work-groups), past one zero-fill batch
+    of 64 pairs: every invalid pair's outputs are zeros, the count is exact."""
+    H, I, E, M, K = 256, 16, 2, 500, 4
+    rng = np.random.default_rng(78)
+    lay = synth.contiguous_layout(H, I)
+    slots = np.zeros((E, lay.slot_bytes), np.uint8)
+    for e in range(E):
+        synth.fill_slot(rng, H, I, lay, out=slots[e])
+    x = synth.bf16_normal(rng, (M, H))
+    ids = rng.integers(0, E, (M, K)).astype(np.int32)
+    bad_mask = rng.random((M, K)) < 0.5
+    ids[bad_mask] = np.where(rng.random(int(bad_mask.sum())) < 0.5, -1, E + 7).astype(np.int32)
+    say(f"[grouped many invalid ids: {int(bad_mask.sum())} of {M * K}]")
+    (out, g, u), invalid = run_grouped(slots, lay, x, ids, H, I)
+    gr, ur, orf, bad = oracle.expert_gate_up_grouped(slots, lay.slot_bytes, E, lay, x, ids, H, I)
+    assert bad == invalid == int(bad_mask.sum())
+    check_parity(out, g, u, gr, ur, orf, "grouped many invalid ids")
+
+
 def test_field_order_and_padding_in_slot():
     """Fields in another order with gaps: only the offsets matter."""
     H, I, M = 384, 24, 3
