@@ -313,17 +313,29 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     const int64_t r = rem - segu, tc = (int64_t)S * (kChTileBase + n);
     return pv * tps + (r > 0 ? (int)ceil_div(r, tc) : 0);
   };
-  auto locate = [&](int64_t c) {
+  // Both boundaries of this work-group's share at once: lanes 0..31 locate
+  // cut c0 and lanes 32..63 cut c1, each half-wave scanning its own word (the
+  // second locate no longer waits for the first).  A cut at or past the
+  // total cost is the end; it is located as the last cost unit first, so
+  // that every lane's scan and pass loop see a slot that holds its cut.
+  auto locate2 = [&](int64_t c0, int64_t c1) {
+    const bool hi = lane >= 32;
+    const int64_t cut = hi ? c1 : c0;
     if (!counted) {
       const int64_t pc = segu + ts * (kChTileBase + G);
-      const int64_t p = floor_div(c, pc);
-      return tile_at(c - p * pc, (int)p, G);
+      const int64_t p = floor_div(cut, pc);
+      return tile_at(cut - p * pc, (int)p, G);
     }
-    if (c >= s_cpre[64]) return npass * tps;
-    // the last word starting at or before c (word prefixes one per lane)
-    const int lo = __popcll(__ballot(s_cpre[lane] <= c)) - 1;
-    // the word's slots one per lane (both half-waves alike): the first whose
-    // inclusive cost exceeds c's place in the word (the word's range holds c)
+    const int64_t total = s_cpre[64];
+    if (total == 0) return npass * tps;
+    const int64_t d0 = min(c0, total - 1), d1 = min(c1, total - 1);
+    const int64_t c = hi ? d1 : d0;
+    // the last word starting at or before each cut (word prefixes one per lane)
+    const long long wp = s_cpre[lane];
+    const uint64_t b0 = __ballot(wp <= d0), b1 = __ballot(wp <= d1);
+    const int lo = (int)__popcll(hi ? b1 : b0) - 1;
+    // the word's slots one per lane of the half-wave: the first whose
+    // inclusive cost exceeds the cut's place in the word
     int64_t rem = c - s_cpre[lo];
     const int sl = 32 * lo + (lane & 31);
     const int ps = s_pass[sl], n = (int)cnt[sl];
@@ -338,20 +350,24 @@ __global__ __launch_bounds__(kChThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         cincl += co;
       }
     }
-    const int k = __builtin_ctzll(__ballot(cincl > rem) & 0xFFFFFFFFull);
+    const uint64_t m = __ballot(cincl > rem);
+    const int k = hi ? 32 + __builtin_ctzll(m >> 32) : __builtin_ctzll(m & 0xFFFFFFFFull);
     const int psk = __shfl(ps, k), nk = __shfl(n, k);
     rem -= __shfl(cincl, k) - slot_cost(psk, nk);
     const int pv = s_ppre[lo] + __shfl(pincl, k) - psk;
-    for (int g = 0;; ++g) {                        // the slot's pass that holds c
-      const int cg = min(G, nk - g * G);
+    int g = 0, cg = min(G, nk);
+    for (;; ++g) {                                 // the slot's pass that holds the cut
+      cg = min(G, nk - g * G);
       const int64_t pcost = segu + ts * (kChTileBase + cg);
-      if (rem < pcost || g == psk - 1) return tile_at(rem, pv + g, cg);
+      if (rem < pcost || g == psk - 1) break;
       rem -= pcost;
     }
+    return cut >= total ? npass * tps : tile_at(rem, pv + g, cg);
   };
   const int64_t C = counted ? s_cpre[64] : (int64_t)npass * (segu + ts * (kChTileBase + G));
-  const int v0 = __builtin_amdgcn_readfirstlane(locate(floor_div((int64_t)blockIdx.x * C, NB)));
-  const int v1 = __builtin_amdgcn_readfirstlane(locate(floor_div((int64_t)(blockIdx.x + 1) * C, NB)));
+  const int vv = locate2(floor_div((int64_t)blockIdx.x * C, NB), floor_div((int64_t)(blockIdx.x + 1) * C, NB));
+  const int v1 = min(__builtin_amdgcn_readlane(vv, 32), npass * tps);
+  const int v0 = min(__builtin_amdgcn_readlane(vv, 0), v1);
 
   // ---- per-lane constants ----
   const LineLanes lines = line_lanes(lane);
