@@ -65,7 +65,7 @@ constexpr int kChCntSlots = 2048;          // slots whose passes are held in LDS
 constexpr int kChIdRegs = 4;               // routing ids held per thread (2048 pairs)
 constexpr int kChCntWords = kChCntSlots / 32;
 constexpr int kChInvBatch = 64;            // invalid pairs zero-filled per batch
-constexpr int kChTileBase = 24;            // a tile of n pairs costs (kChTileBase + n) / (kChTileBase + 1) one-pair tiles
+constexpr int kChTileBase = 16;            // a tile of n pairs costs (kChTileBase + n) / (kChTileBase + 1) one-pair tiles
 
 // A wave's share of a round's units: the first wave of SIMD q takes the
 // fraction [q/4, q/4 + share/4096) of the round's tiles, the second wave the
