@@ -1087,10 +1087,10 @@ int chunked_tiles(const GateUpParams& p) {
 
 hipError_t launch_chunked(GateUpParams p, int nt, hipStream_t stream) {
   p.steps = ch_steps(p.H);
-  // a SIMD's first-wave share, 1/1024 of the SIMD's quarter: one column tile
-  // as measured for the resident kernel's loop, which this kernel's step loop
-  // matches; two as measured here (512 and 547 were slower on the routed step)
-  p.wave_share = nt == 1 ? 577 : 580;
+  // a SIMD's first-wave share, 1/1024 of the SIMD's quarter, as measured on
+  // this kernel: one column tile 550 (490, 520, 577 and 585 slower on the down
+  // projection), two 580 (512 and 547 slower on the routed step)
+  p.wave_share = nt == 1 ? 550 : 580;
   // a segment's set-up (id scan, row ranges, first digits, the first weights'
   // latency), in K-steps of a one-pair tile: a fixed part and one that grows
   // with the row length (the range pass reads whole rows); fitted to interleaved
